@@ -1,0 +1,245 @@
+"""Benchmark of the tensor-parallel MLP shard step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gpt2s]
+
+One step is the whole hot path of a workload: for every shard the column-
+parallel fc1 forward with fused bias + GeLU, the row-parallel fc2 partial, the
+sum over shards, the fc2 dgrad with the fused GeLU derivative, both wgrads with
+bias gradients, the fc1 dgrad and the sum of the dX partials. The step is
+captured once into a HIP graph and replayed; inputs are resident in HBM before
+timing starts.
+
+Prints one JSON line: TFLOP/s of the GEMM work (2*M*N*K per product, all
+shards) over the wall time of whole steps, the fraction of the MI355X bf16
+dense matrix-core peak, a roofline record for the dominant kernel (its own
+duration measured with HIP events on its stream) and the float64 CPU oracle
+timed on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s + % bf16 MFMA peak, TP-MLP shard fwd+bwd, 1×MI355X"
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2s")
+    ap.add_argument("--extra", default="gpt175b",
+                    help="comma-separated workloads also timed and reported under 'extra'")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--only-call", default=None,
+                    help="profiling aid: launch only this call of shard 0 --steps times")
+    return ap.parse_args()
+
+
+def shard_calls(step, i=0):
+    """The per-shard calls of the MLP step as (name, thunk, gemm flops, kernels)."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    cfg, o, inp = step.cfg, step.out, step.inp
+    T, h, F = cfg.T, cfg.h, cfg.F
+    A_i, B_i = step._col("A", i, F), step._row("B", i, F)
+    a_i = step._col("a", i, F) if cfg.has_bias else None
+    f = 2 * T * h * F
+    return [
+        ("fc1_fwd", lambda: L.tp_column_linear_fwd(inp["X"], A_i, a_i, o[f"Y_{i}"], o[f"U_{i}"],
+                                                   act="gelu"), f),
+        ("fc2_fwd", lambda: L.tp_row_linear_fwd_partial(o[f"Y_{i}"], B_i, o[f"Zp_{i}"]), f),
+        ("fc2_dgrad", lambda: L.tp_linear_bwd_dgrad(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"],
+                                                    act="gelu"), f),
+        ("fc2_wgrad", lambda: L.tp_linear_bwd_wgrad(o[f"Y_{i}"], inp["dZ"], o[f"dB_{i}"],
+                                                    o.get("db"), workspace=step.workspace), f),
+        ("fc1_dgrad", lambda: L.tp_linear_bwd_dgrad(o[f"dU_{i}"], A_i, None, o[f"dXp_{i}"],
+                                                    act="none"), f),
+        ("fc1_wgrad", lambda: L.tp_linear_bwd_wgrad(inp["X"], o[f"dU_{i}"], o[f"dA_{i}"],
+                                                    o.get(f"da_{i}"), workspace=step.workspace),
+         f),
+    ]
+
+
+def time_call(fn, reps):
+    """Average duration (ms) of one call, HIP events on the stream it launches on."""
+    import torch
+    s = torch.cuda.current_stream()
+    for _ in range(3):
+        fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(s)
+    for _ in range(reps):
+        fn()
+    e1.record(s)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def time_steps(step, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(s)
+    for _ in range(steps):
+        step.run()
+    e1.record(s)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall / steps * 1e3, e0.elapsed_time(e1) / steps
+
+
+def run_workload(name, steps, warmup):
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    from tp_inputs import get_config, make_inputs
+    cfg = get_config(name)
+    log(f"[bench] {name}: drawing inputs (T={cfg.T} h={cfg.h} p={cfg.p})")
+    inputs = make_inputs(cfg)
+    step = ShardStep(cfg, inputs, "cuda:0")
+    step.capture()
+    log(f"[bench] {name}: graph captured; timing {steps} steps after {warmup} warm-up")
+    wall_ms, ev_ms = time_steps(step, steps, warmup)
+    flops = cfg.gemm_flops()
+    tflops = flops / (wall_ms * 1e-3) / 1e12
+    return cfg, inputs, step, wall_ms, ev_ms, flops, tflops
+
+
+def cpu_baseline(cfg, inputs, seconds):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads", 1) for d in threadpool_info()
+                       if d.get("user_api") == "blas"), default=1)
+    except Exception:  # threadpoolctl missing: report the affinity mask size
+        threads = len(os.sched_getaffinity(0))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.run_config(cfg, inputs)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    return {
+        "value": cfg.gemm_flops() * reps / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{cfg.name}: the whole fwd+bwd step (T={cfg.T}, h={cfg.h}, all {cfg.p} "
+                   f"shards) in float64 numpy, {reps} run(s) in {el:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the shards of a workload run serially on "
+              f"cuda:0 and are summed locally; --gpus {args.gpus} is not supported.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+
+    if args.only_call:
+        from tensor_transformer_layer_fwd_amd.shard import ShardStep
+        from tp_inputs import get_config, make_inputs
+        cfg = get_config(args.workload)
+        step = ShardStep(cfg, make_inputs(cfg), "cuda:0")
+        step.run_eager()
+        calls = {n: (fn, f) for n, fn, f in shard_calls(step)}
+        fn, f = calls[args.only_call]
+        ms = time_call(fn, args.steps)
+        log(f"[bench] {args.workload} {args.only_call}: {ms * 1e3:.2f} us/launch, "
+            f"{f / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+        print(json.dumps({"workload": args.workload, "call": args.only_call,
+                          "us_per_launch": ms * 1e3, "tflops": f / (ms * 1e-3) / 1e12}))
+        return
+
+    cfg, inputs, step, wall_ms, ev_ms, flops, tflops = run_workload(
+        args.workload, args.steps, args.warmup)
+    log(f"[bench] {cfg.name}: {wall_ms * 1e3:.1f} us/step (events {ev_ms * 1e3:.1f}), "
+        f"{tflops:.1f} TFLOP/s = {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
+
+    # per-call durations of shard 0 (events on the launch stream)
+    kernels = {}
+    for name, fn, f in shard_calls(step):
+        ms = time_call(fn, args.kernel_reps)
+        kernels[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+    gemm_sum_us = sum(v["us"] for v in kernels.values()) * len(cfg.shards)
+    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    dom_flops = 2 * cfg.T * cfg.h * cfg.F
+    dom_tf = dom_flops / (kernels[dom]["us"] * 1e-6) / 1e12
+    log(f"[bench] per-call: {json.dumps(kernels)}")
+
+    extra = {}
+    for name in [w for w in args.extra.split(",") if w and w != args.workload]:
+        c2, _, s2, w2, e2, f2, t2 = run_workload(name, max(5, args.steps // 5), 3)
+        k2 = {}
+        for n, fn, f in shard_calls(s2):
+            ms = time_call(fn, 5)
+            k2[n] = {"us": round(ms * 1e3, 1), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        extra[name] = {"tflops": round(t2, 1), "frac_of_peak": round(t2 / PEAK_BF16_TFLOPS, 4),
+                       "ms_per_step": round(w2, 4), "gemm_gflop": round(f2 / 1e9, 2),
+                       "per_call": k2}
+        log(f"[bench] {name}: {w2 * 1e3:.1f} us/step, {t2:.1f} TFLOP/s; per-call {k2}")
+        del s2
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the float64 oracle on the host for ~{args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(cfg, inputs, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "frac_of_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+        "config": {"workload": f"{cfg.name}: GPT-2-small TP=2 MLP shard step, fwd+bwd, "
+                               f"tokens={cfg.T} (micro-batch {cfg.micro_batch} x seq {cfg.seq}), "
+                               f"h={cfg.h}, p={cfg.p} shards run serially",
+                   "tokens": cfg.T, "h": cfg.h, "p": cfg.p, "ffn_shard": cfg.F,
+                   "gemm_gflop_per_step": round(flops / 1e9, 2)},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+        "per_call_shard0": kernels,
+        "gemm_calls_sum_us": round(gemm_sum_us, 1),
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,202 @@
+/*
+ * tp_mlp.h - C ABI of the tensor-parallel Transformer MLP / attention-projection
+ * shard on one MI355X (gfx950).
+ *
+ * What is computed (page "Megatron", zzmblog.top):
+ *   - section "Tensor Parallelism", subsection "mathematical principles": the
+ *     first MLP weight A (h x 4h) is split by output columns, A = [A_1 .. A_p],
+ *     so Y = [X A_1, .., X A_p] needs no exchange because X is replicated; the
+ *     second weight B (4h x h) is split by input rows, B = [B_1; ..; B_p], so
+ *     Z = Y_1 B_1 + .. + Y_p B_p, a sum over shards (an All-Reduce across GPUs).
+ *   - section "Transformer-layer tensor parallelism": the attention QKV
+ *     projection and the first MLP linear are column-split, the attention output
+ *     projection and the second MLP linear are row-split.
+ *   - the training-script listing on the same page sets activation_func "gelu";
+ *     the tanh form of GeLU is used.
+ * The backward products (dgrad, wgrad, bias gradients) are not on the pages;
+ * they are the textbook derivatives of the forward definitions.
+ *
+ * One call computes one shard step. On one GPU the p shards of a layer run one
+ * after another and tp_reduce_partials stands in for the All-Reduce.
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major. "ld" is the row stride in elements (>= the row
+ *     width). Weights are stored [in, out]: A_i is h x n, B_i is k x h.
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *     never allocates or frees memory and keeps no pointer after returning;
+ *     scratch memory (split-K partials, column-sum partials) is the caller's
+ *     workspace, sized by tp_linear_bwd_wgrad_workspace_size.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *     Outputs are valid after the caller synchronises with that stream.
+ *   - dtype TP_BF16: operands are bf16, products accumulate in fp32; outputs
+ *     are rounded to bf16 with round-to-nearest-even (NaN stays NaN) unless the
+ *     call says fp32. dtype TP_F32: fp32 throughout.
+ *   - Errors: arguments are validated on the host before anything is launched.
+ *     A bad argument returns a negative tp_status and launches nothing. A failed
+ *     launch returns TP_ERR_HIP; tp_last_hip_error() gives the hipError_t (kept
+ *     per thread). Faults during execution surface at the caller's stream
+ *     synchronisation. Nothing throws across this interface.
+ *   - Sizes: every dimension must be >= 1 and < 2^31; any ld >= width is
+ *     accepted. Pointers need only the alignment of their element type; 16-byte
+ *     aligned pointers with ld a multiple of 8 take the vector-load path.
+ *   - Results are deterministic: the same call on the same inputs gives the same
+ *     bits (fixed summation orders, no floating-point atomics).
+ *   - Calls are reentrant and hold no state beyond the loaded code object.
+ */
+#ifndef TP_MLP_H
+#define TP_MLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TP_OK = 0,
+  TP_ERR_NULL = -1,      /* a required pointer is NULL */
+  TP_ERR_SHAPE = -2,     /* a dimension < 1 or >= 2^31, an ld below the row width, p out of range */
+  TP_ERR_DTYPE = -3,     /* unknown dtype or unsupported dtype combination */
+  TP_ERR_ACT = -4,       /* unknown activation */
+  TP_ERR_WORKSPACE = -5, /* workspace smaller than tp_linear_bwd_wgrad_workspace_size */
+  TP_ERR_HIP = -6        /* a HIP launch failed; see tp_last_hip_error() */
+} tp_status;
+
+typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
+
+/*
+ * Column-parallel forward of shard i ("Megatron" page, "Tensor Parallelism /
+ * mathematical principles", the column split Y = [X A_1, .., X A_p]; applied to
+ * MLP fc1 and to the QKV projection per "Transformer-layer tensor parallelism").
+ *
+ *   U_i = X A_i + bias_i          (T x n; bias broadcast over rows)
+ *   Y_i = act(U_i)                (T x n)
+ *
+ * X      [T, h], ld_x, dtype dt        replicated input
+ * A_i    [h, n], ld_a, dtype dt        column shard of the weight (may be a view
+ *                                      of the unsharded [h, p*n] weight)
+ * bias_i [n], dtype dt, or NULL        column shard of the bias
+ * Y_i    [T, n], ld_y, dtype dt        output
+ * U_i    [T, n], ld_y, dtype dt, or NULL   pre-activation, saved for the
+ *                                      backward; required when act != NONE
+ *                                      (with act == NONE it receives Y_i's values)
+ */
+int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, void* Y_i,
+                         void* U_i, int64_t T, int64_t h, int64_t n, int64_t ld_x,
+                         int64_t ld_a, int64_t ld_y, int dt, int act, hipStream_t stream);
+
+/*
+ * Row-parallel forward partial of shard i ("Megatron" page, "Tensor
+ * Parallelism / mathematical principles", one term Y_i B_i of
+ * Z = Y_1 B_1 + .. + Y_p B_p; MLP fc2 and the attention output projection).
+ *
+ *   Zp_i = Y_i B_i                (T x h, fp32, no bias: the bias is added once
+ *                                  after the sum, in tp_reduce_partials)
+ *
+ * Y_i  [T, k], ld_y, dtype dt
+ * B_i  [k, h], ld_b, dtype dt          row shard of the weight (may be a view of
+ *                                      the unsharded [p*k, h] weight)
+ * Zp_i [T, h], ld_z, fp32
+ */
+int tp_row_linear_fwd_partial(const void* Y_i, const void* B_i, float* Zp_i, int64_t T,
+                              int64_t k, int64_t h, int64_t ld_y, int64_t ld_b,
+                              int64_t ld_z, int dt, hipStream_t stream);
+
+/*
+ * Input gradient (dgrad) of Out = act(In W) for a weight stored [k, n]
+ * (derivative of the forward definitions above; not on the pages).
+ *
+ *   dIn = (dOut W^T) * act'(U)     elementwise with the saved pre-activation U
+ *   dIn = dOut W^T                 when act == NONE (U ignored, may be NULL)
+ *
+ * Row-parallel layer: dOut = dZ, W = B_i, U = U_i, act = GELU -> dU_i (out_dt = dt).
+ * Column-parallel layer: dOut = dU_i, W = A_i, act = NONE -> partial dX_i
+ * (out_dt = TP_F32), summed over shards by tp_reduce_partials.
+ *
+ * dOut [T, n], ld_dout, dtype dt
+ * W    [k, n], ld_w, dtype dt
+ * U    [T, k], ld_u, dtype dt (required when act != NONE)
+ * dIn  [T, k], ld_din, dtype out_dt (TP_F32, or dt)
+ */
+int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act, void* dIn,
+                        int64_t T, int64_t k, int64_t n, int64_t ld_dout, int64_t ld_w,
+                        int64_t ld_u, int64_t ld_din, int dt, int out_dt,
+                        hipStream_t stream);
+
+/*
+ * Weight and bias gradients (wgrad) of Out = In W + c for a weight stored
+ * [k, n] (derivative of the forward definitions; not on the pages).
+ *
+ *   dW    (+)= In^T dOut           (k x n, fp32)
+ *   dbias (+)= sum over the T rows of dOut   (n, fp32; skipped when NULL)
+ *
+ * With accumulate != 0 both are added to the values already in dW / dbias;
+ * otherwise they are overwritten.
+ *
+ * In   [T, k], ld_in, dtype dt
+ * dOut [T, n], ld_dout, dtype dt
+ * dW   [k, n], ld_dw, fp32
+ * workspace: device scratch of at least tp_linear_bwd_wgrad_workspace_size()
+ *            bytes for the same (T, k, n, dt); may be NULL when that size is 0.
+ *            Its contents on entry are ignored. One workspace must not be
+ *            shared by calls that may run at the same time.
+ */
+int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbias, int64_t T,
+                        int64_t k, int64_t n, int64_t ld_in, int64_t ld_dout, int64_t ld_dw,
+                        int accumulate, int dt, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/* Scratch bytes tp_linear_bwd_wgrad needs for (T, k, n, dt); pure host function. */
+int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
+                                       size_t* bytes);
+
+/*
+ * Sum over shards, the one-GPU stand-in for the All-Reduce ("Megatron" page,
+ * "Tensor Parallelism / mathematical principles": the row-split partials Y_i B_i
+ * are summed across GPUs; "Transformer-layer tensor parallelism": one such sum
+ * after the attention output projection and one after the MLP).
+ *
+ *   out = partials[0] + partials[1] + .. + partials[p-1] + bias
+ *
+ * summed in fp32 in the order i = 0 .. p-1, the bias (if any) added last, then
+ * rounded once to out_dt. Also used for the backward sum of the partial dX_i.
+ *
+ * partials  HOST array of p DEVICE pointers, each [T, h] fp32 with row stride ld_p
+ * p         1 .. 16
+ * bias      [h], dtype out_dt, or NULL
+ * out       [T, h], ld_out, dtype out_dt; may alias partials[0] when
+ *           out_dt == TP_F32 and ld_out == ld_p
+ */
+int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
+                       int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, int out_dt,
+                       hipStream_t stream);
+
+/*
+ * Standalone bias + activation pass: Y = act(U + bias), elementwise.
+ * The fused epilogue of tp_column_linear_fwd does the same work inside the
+ * GEMM; this call exists to measure the pass on its own (it is HBM-bound).
+ *
+ * U    [T, n], ld_u, dtype in_dt
+ * bias [n], dtype in_dt, or NULL
+ * Y    [T, n], ld_y, dtype out_dt
+ * act  TP_ACT_GELU_TANH or TP_ACT_NONE (then Y = U + bias)
+ */
+int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, int64_t ld_u,
+                int64_t ld_y, int in_dt, int out_dt, int act, hipStream_t stream);
+
+/* Human-readable name of a tp_status value (never NULL). */
+const char* tp_status_string(int status);
+
+/* hipError_t of the last TP_ERR_HIP returned on the calling thread (0 if none). */
+int tp_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP_MLP_H */

@@ -1,0 +1,23 @@
+"""MI355X-native tensor-parallel Transformer MLP / attention-projection shard.
+
+The arithmetic lives in libtpmlp.so (hand-written HIP for gfx950, C ABI in
+include/tp_mlp.h); this package is its Python binding and a step driver.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    TP_ACT_GELU_TANH,
+    TP_ACT_NONE,
+    TP_BF16,
+    TP_F32,
+    TPError,
+    lib,
+    tp_bias_act,
+    tp_column_linear_fwd,
+    tp_last_hip_error,
+    tp_linear_bwd_dgrad,
+    tp_linear_bwd_wgrad,
+    tp_linear_bwd_wgrad_workspace_size,
+    tp_reduce_partials,
+    tp_row_linear_fwd_partial,
+    tp_status_string,
+)

@@ -1,0 +1,187 @@
+"""ctypes binding of libtpmlp.so (include/tp_mlp.h). Argument marshalling only:
+every step of the shard runs in the library's HIP kernels.
+
+Two layers:
+  - ``lib()`` returns the loaded ``ctypes.CDLL`` with typed signatures;
+  - the ``tp_*`` functions below take torch tensors that already live on the
+    GPU, derive sizes and row strides from them, call the entry point of the
+    same name on the current torch stream and raise ``TPError`` on a non-zero
+    status.
+There is no fallback: if the library is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
+
+TP_OK = 0
+TP_F32, TP_BF16 = 0, 1
+TP_ACT_NONE, TP_ACT_GELU_TANH = 0, 1
+STATUS = {0: "TP_OK", -1: "TP_ERR_NULL", -2: "TP_ERR_SHAPE", -3: "TP_ERR_DTYPE",
+          -4: "TP_ERR_ACT", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP"}
+
+# Every function declared in include/tp_mlp.h, with its ctypes signature.
+_vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+SIGNATURES = {
+    "tp_column_linear_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                    _int, _int, _vp]),
+    "tp_row_linear_fwd_partial": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                                         _vp]),
+    "tp_linear_bwd_dgrad": (_int, [_vp, _vp, _vp, _int, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                   _i64, _int, _int, _vp]),
+    "tp_linear_bwd_wgrad": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                                   _int, _vp, _sz, _vp]),
+    "tp_linear_bwd_wgrad_workspace_size": (_int, [_i64, _i64, _i64, _int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_reduce_partials": (_int, [ctypes.POINTER(ctypes.c_void_p), _int, _vp, _vp, _i64, _i64, _i64,
+                                  _i64, _int, _vp]),
+    "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "tp_status_string": (ctypes.c_char_p, [_int]),
+    "tp_last_hip_error": (_int, []),
+}
+
+_LIB = None
+
+
+class TPError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        detail = ""
+        if status == -6:
+            detail = f" (hipError_t {lib().tp_last_hip_error()})"
+        super().__init__(f"{fn} returned {status} {STATUS.get(status, '?')}{detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtpmlp.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is None:
+        # torch ships its own HIP runtime (same SONAME as the system one); load
+        # it first so that this library binds to it and shares torch's streams
+        import torch  # noqa: F401
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m tensor_transformer_layer_fwd_amd.build` (no fallback path exists)")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _check(fn: str, status: int) -> None:
+    if status != TP_OK:
+        raise TPError(fn, status)
+
+
+# --------------------------------------------------------------------------- #
+# torch-tensor conveniences (device memory and streams come from torch)       #
+# --------------------------------------------------------------------------- #
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    if t.dtype == torch.float32:
+        return TP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ld(t) -> int:
+    """Row stride of a 2-D row-major view (unit stride along columns)."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
+        raise ValueError("expected a 2-D tensor with unit column stride")
+    return int(t.stride(0)) if t.shape[0] > 1 else int(max(t.stride(0), t.shape[1]))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _act(act) -> int:
+    if act in (None, "none", TP_ACT_NONE):
+        return TP_ACT_NONE
+    if act in ("gelu", "gelu_tanh", TP_ACT_GELU_TANH):
+        return TP_ACT_GELU_TANH
+    raise ValueError(f"unknown activation {act!r}")
+
+
+def tp_column_linear_fwd(X, A_i, bias_i, Y_i, U_i=None, act="gelu", stream=None):
+    T, h = X.shape
+    n = A_i.shape[1]
+    if U_i is not None and _ld(U_i) != _ld(Y_i):
+        raise ValueError("U_i and Y_i must share a row stride")
+    _check("tp_column_linear_fwd", lib().tp_column_linear_fwd(
+        _ptr(X), _ptr(A_i), _ptr(bias_i), _ptr(Y_i), _ptr(U_i), T, h, n, _ld(X), _ld(A_i),
+        _ld(Y_i), _dt(X), _act(act), _stream(stream)))
+
+
+def tp_row_linear_fwd_partial(Y_i, B_i, Zp_i, stream=None):
+    T, k = Y_i.shape
+    h = B_i.shape[1]
+    _check("tp_row_linear_fwd_partial", lib().tp_row_linear_fwd_partial(
+        _ptr(Y_i), _ptr(B_i), _ptr(Zp_i), T, k, h, _ld(Y_i), _ld(B_i), _ld(Zp_i), _dt(Y_i),
+        _stream(stream)))
+
+
+def tp_linear_bwd_dgrad(dOut, W, U, dIn, act="none", stream=None):
+    T, n = dOut.shape
+    k = W.shape[0]
+    ld_u = _ld(U) if U is not None else k
+    _check("tp_linear_bwd_dgrad", lib().tp_linear_bwd_dgrad(
+        _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(dIn), T, k, n, _ld(dOut), _ld(W), ld_u,
+        _ld(dIn), _dt(dOut), _dt(dIn), _stream(stream)))
+
+
+def tp_linear_bwd_wgrad_workspace_size(T: int, k: int, n: int, dt: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_linear_bwd_wgrad_workspace_size",
+           lib().tp_linear_bwd_wgrad_workspace_size(T, k, n, dt, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_linear_bwd_wgrad(In, dOut, dW, dbias=None, accumulate=False, workspace=None,
+                        stream=None):
+    T, k = In.shape
+    n = dOut.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tp_linear_bwd_wgrad", lib().tp_linear_bwd_wgrad(
+        _ptr(In), _ptr(dOut), _ptr(dW), _ptr(dbias), T, k, n, _ld(In), _ld(dOut), _ld(dW),
+        int(bool(accumulate)), _dt(In), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_reduce_partials(partials, bias, out, stream=None):
+    p = len(partials)
+    T, h = partials[0].shape
+    ld_p = _ld(partials[0])
+    for P in partials:
+        if tuple(P.shape) != (T, h) or _ld(P) != ld_p:
+            raise ValueError("partials must share shape and row stride")
+    arr = (ctypes.c_void_p * p)(*[P.data_ptr() for P in partials])
+    _check("tp_reduce_partials", lib().tp_reduce_partials(
+        arr, p, _ptr(bias), _ptr(out), T, h, ld_p, _ld(out), _dt(out), _stream(stream)))
+
+
+def tp_bias_act(U, bias, Y, act="gelu", stream=None):
+    T, n = U.shape
+    _check("tp_bias_act", lib().tp_bias_act(
+        _ptr(U), _ptr(bias), _ptr(Y), T, n, _ld(U), _ld(Y), _dt(U), _dt(Y), _act(act),
+        _stream(stream)))
+
+
+def tp_status_string(status: int) -> str:
+    return lib().tp_status_string(status).decode()
+
+
+def tp_last_hip_error() -> int:
+    return int(lib().tp_last_hip_error())

@@ -1,0 +1,211 @@
+// HBM-bound passes of the shard step:
+//   - split-K fix-up: sum the fp32 K-slice partials in slice order, apply the
+//     epilogue (used by the wgrad GEMM when its output has too few tiles);
+//   - column sums (bias gradients), two deterministic passes;
+//   - the sum over shards that stands in for the All-Reduce;
+//   - a standalone bias + activation pass.
+#include <hip/hip_runtime.h>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace tpmlp {
+namespace {
+
+__global__ __launch_bounds__(256) void splitk_fixup_kernel(GemmParams p) {
+  const int64_t total = p.M * p.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    float v = 0.0f;
+    for (int z = 0; z < p.splitk; ++z) v += p.ws[z * total + e];
+    const int64_t row = e / p.N, col = e - row * p.N;
+    epilogue_elem(p, row, col, v, 1);
+  }
+}
+
+// Pass 1: block (cb, chunk) sums rows [chunk*R, chunk*R + R) of 128 columns.
+// Thread (cx, ry) owns columns 2cx, 2cx+1 and rows ry, ry+4, ...; the four
+// row-groups are then added in order through LDS.
+__global__ __launch_bounds__(256) void colsum_pass1_kernel(ColsumParams p, int nchunks) {
+  __shared__ float part[4][128];
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 128 + cx * 2;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kColsumRows;
+  const int64_t t1 = min(p.T, t0 + kColsumRows);
+  float s0 = 0.0f, s1 = 0.0f;
+  for (int64_t t = t0 + ry; t < t1; t += 4) {
+    const int64_t o = t * p.ld + c;
+    if (c < p.N) s0 += load_elem(p.src, o, p.src_bf16);
+    if (c + 1 < p.N) s1 += load_elem(p.src, o + 1, p.src_bf16);
+  }
+  part[ry][cx * 2] = s0;
+  part[ry][cx * 2 + 1] = s1;
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int64_t cc = static_cast<int64_t>(blockIdx.x) * 128 + threadIdx.x;
+    if (cc < p.N) {
+      float v = ((part[0][threadIdx.x] + part[1][threadIdx.x]) + part[2][threadIdx.x]) +
+                part[3][threadIdx.x];
+      if (nchunks == 1) {
+        p.dbias[cc] = p.accumulate ? p.dbias[cc] + v : v;
+      } else {
+        p.ws[static_cast<int64_t>(blockIdx.y) * p.N + cc] = v;
+      }
+    }
+  }
+}
+
+// Pass 2: dbias[c] (+)= sum over chunks, in chunk order.
+__global__ __launch_bounds__(256) void colsum_pass2_kernel(ColsumParams p, int nchunks) {
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= p.N) return;
+  float v = 0.0f;
+  for (int i = 0; i < nchunks; ++i) v += p.ws[static_cast<int64_t>(i) * p.N + c];
+  p.dbias[c] = p.accumulate ? p.dbias[c] + v : v;
+}
+
+// out = ((parts[0] + parts[1]) + ...) + bias, rounded once. Vector path: four
+// consecutive columns per thread.
+__global__ __launch_bounds__(256) void reduce_vec4_kernel(ReduceParams p) {
+  const int64_t nq = p.N >> 2;
+  const int64_t total = p.T * nq;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    const int64_t t = e / nq, c = (e - t * nq) << 2;
+    const int64_t ip = t * p.ldp + c;
+    float4 s = *reinterpret_cast<const float4*>(p.parts[0] + ip);
+    for (int i = 1; i < p.p; ++i) {
+      const float4 v = *reinterpret_cast<const float4*>(p.parts[i] + ip);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    if (p.bias) {
+      const int bb = p.out_bf16;
+      s.x += load_elem(p.bias, c, bb);
+      s.y += load_elem(p.bias, c + 1, bb);
+      s.z += load_elem(p.bias, c + 2, bb);
+      s.w += load_elem(p.bias, c + 3, bb);
+    }
+    const int64_t io = t * p.ldo + c;
+    if (p.out_bf16) {
+      uint2 o;
+      o.x = pack_bf16x2(s.x, s.y);
+      o.y = pack_bf16x2(s.z, s.w);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + io) = o;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + io) = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void reduce_scalar_kernel(ReduceParams p) {
+  const int64_t total = p.T * p.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    const int64_t t = e / p.N, c = e - t * p.N;
+    float s = p.parts[0][t * p.ldp + c];
+    for (int i = 1; i < p.p; ++i) s += p.parts[i][t * p.ldp + c];
+    if (p.bias) s += load_elem(p.bias, c, p.out_bf16);
+    store_elem(p.out, t * p.ldo + c, s, p.out_bf16);
+  }
+}
+
+__global__ __launch_bounds__(256) void bias_act_kernel(BiasActParams p) {
+  const int64_t total = p.T * p.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    const int64_t t = e / p.N, c = e - t * p.N;
+    float u = p.u_f32 ? static_cast<const float*>(p.u)[t * p.ldu + c]
+                      : load_elem(p.u, t * p.ldu + c, p.in_bf16);
+    if (p.bias) u += load_elem(p.bias, c, p.in_bf16);
+    store_elem(p.y, t * p.ldy + c, apply_act(p.act, u), p.out_bf16);
+  }
+}
+
+// Vector path of bias_act: fp32 U, bf16 Y, four columns per thread.
+__global__ __launch_bounds__(256) void bias_act_vec4_kernel(BiasActParams p) {
+  const int64_t nq = p.N >> 2;
+  const int64_t total = p.T * nq;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    const int64_t t = e / nq, c = (e - t * nq) << 2;
+    float4 u = *reinterpret_cast<const float4*>(static_cast<const float*>(p.u) + t * p.ldu + c);
+    if (p.bias) {
+      u.x += load_elem(p.bias, c, p.in_bf16);
+      u.y += load_elem(p.bias, c + 1, p.in_bf16);
+      u.z += load_elem(p.bias, c + 2, p.in_bf16);
+      u.w += load_elem(p.bias, c + 3, p.in_bf16);
+    }
+    uint2 o;
+    o.x = pack_bf16x2(apply_act(p.act, u.x), apply_act(p.act, u.y));
+    o.y = pack_bf16x2(apply_act(p.act, u.z), apply_act(p.act, u.w));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.y) + t * p.ldy + c) = o;
+  }
+}
+
+unsigned grid_for(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  const int64_t cap = 256 * 16;  // enough workgroups to cover every CU many times
+  if (g > cap) g = cap;
+  if (g < 1) g = 1;
+  return static_cast<unsigned>(g);
+}
+
+}  // namespace
+
+size_t colsum_workspace_bytes(int64_t T, int64_t N) {
+  const int64_t nchunks = (T + kColsumRows - 1) / kColsumRows;
+  return nchunks > 1 ? static_cast<size_t>(nchunks * N) * sizeof(float) : 0;
+}
+
+hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(splitk_fixup_kernel, dim3(grid_for(p.M * p.N, 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_colsum(const ColsumParams& p, hipStream_t s) {
+  const int64_t nchunks = (p.T + kColsumRows - 1) / kColsumRows;
+  const int64_t cblocks = (p.N + 127) / 128;
+  if (nchunks > 65535) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(colsum_pass1_kernel,
+                     dim3(static_cast<unsigned>(cblocks), static_cast<unsigned>(nchunks)),
+                     dim3(256), 0, s, p, static_cast<int>(nchunks));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || nchunks == 1) return e;
+  hipLaunchKernelGGL(colsum_pass2_kernel, dim3(static_cast<unsigned>((p.N + 255) / 256)),
+                     dim3(256), 0, s, p, static_cast<int>(nchunks));
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
+  bool vec = (p.N % 4 == 0) && (p.ldp % 4 == 0) && (p.ldo % 4 == 0);
+  for (int i = 0; i < p.p; ++i) vec = vec && (reinterpret_cast<uintptr_t>(p.parts[i]) % 16 == 0);
+  vec = vec && (reinterpret_cast<uintptr_t>(p.out) % (p.out_bf16 ? 8 : 16) == 0);
+  if (vec)
+    hipLaunchKernelGGL(reduce_vec4_kernel, dim3(grid_for(p.T * (p.N / 4), 256)), dim3(256), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL(reduce_scalar_kernel, dim3(grid_for(p.T * p.N, 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s) {
+  const bool vec = p.u_f32 && p.out_bf16 && (p.N % 4 == 0) && (p.ldu % 4 == 0) &&
+                   (p.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(p.u) % 16 == 0) &&
+                   (reinterpret_cast<uintptr_t>(p.y) % 8 == 0);
+  if (vec)
+    hipLaunchKernelGGL(bias_act_vec4_kernel, dim3(grid_for(p.T * (p.N / 4), 256)), dim3(256), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL(bias_act_kernel, dim3(grid_for(p.T * p.N, 256)), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

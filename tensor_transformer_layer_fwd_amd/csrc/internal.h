@@ -1,0 +1,90 @@
+// Internal interface between the C ABI (tp_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+enum Epilogue : int {
+  EPI_STORE = 0,     // C (+)= acc
+  EPI_BIAS_ACT = 1,  // U = acc + bias; C = act(U); C2 = U (if C2)
+  EPI_DACT = 2,      // C = acc * act'(Uin)
+};
+
+enum Act : int { ACT_NONE = 0, ACT_GELU = 1 };
+
+// One GEMM C[M,N] = op(A)[M,K] * op(B)[K,N] with a fused epilogue.
+//   a_kcontig: A stored [M,K] (true) or [K,M] (false), row stride lda
+//   b_kcontig: B stored [N,K] (true) or [K,N] (false), row stride ldb
+struct GemmParams {
+  const void* a;
+  const void* b;
+  void* c;         // output [M,N], ldc; fp32 or bf16 (out_bf16)
+  void* c2;        // EPI_BIAS_ACT: pre-activation output, ldc (same dtype as c); may be null
+  const void* bias;  // EPI_BIAS_ACT: [N], dtype of the operands; may be null
+  const void* u;     // EPI_DACT: saved pre-activation [M,N], ldu, dtype of the operands
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc, ldu;
+  int epi, act;
+  int out_bf16;    // output dtype of c / c2
+  int accumulate;  // EPI_STORE with fp32 output: C += acc
+  // split-K: grid slice z covers K range [z*k_chunk, min(K,(z+1)*k_chunk)) and
+  // writes raw fp32 partials to ws + z*M*N (row stride N); the fix-up kernel
+  // then applies the epilogue.
+  int splitk;
+  int64_t k_chunk;
+  float* ws;
+  int a_kcontig, b_kcontig;
+};
+
+// Column-sum (bias gradient) request: dbias[n] (+)= sum_t src[t, n].
+struct ColsumParams {
+  const void* src;
+  int64_t T, N, ld;
+  int src_bf16;
+  float* dbias;
+  int accumulate;
+  float* ws;  // partial sums [nchunks, N]
+};
+
+constexpr int kColsumRows = 128;  // rows summed per block in the first pass
+
+// Reduction over shards.
+constexpr int kMaxPartials = 16;
+struct ReduceParams {
+  const float* parts[kMaxPartials];
+  int p;
+  const void* bias;
+  void* out;
+  int64_t T, N, ldp, ldo;
+  int out_bf16;
+};
+
+struct BiasActParams {
+  const void* u;
+  const void* bias;
+  void* y;
+  int64_t T, N, ldu, ldy;
+  int in_bf16, u_f32, out_bf16, act;
+};
+
+// Split-K choice shared by the workspace-size query and the launcher.
+struct SplitPlan {
+  int tile;     // tile configuration index
+  int splitk;   // >= 1
+  int64_t k_chunk;
+};
+
+SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split);
+size_t colsum_workspace_bytes(int64_t T, int64_t N);
+
+hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
+hipError_t launch_gemm_f32(const GemmParams& p, hipStream_t s);
+hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s);
+hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
+hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s);
+
+}  // namespace tpmlp

@@ -1,0 +1,262 @@
+// The C ABI: host-side validation, then dispatch to the kernels. Every check
+// runs before the first HIP call, so a rejected call launches nothing.
+#include <hip/hip_runtime.h>
+
+#include "../../include/tp_mlp.h"
+#include "internal.h"
+
+using namespace tpmlp;
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool dim_ok(int64_t d) { return d >= 1 && d <= kMaxDim; }
+bool dtype_ok(int dt) { return dt == TP_F32 || dt == TP_BF16; }
+bool act_ok(int a) { return a == TP_ACT_NONE || a == TP_ACT_GELU_TANH; }
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return TP_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return TP_ERR_HIP;
+}
+
+int run_gemm(GemmParams& p, int dt, bool allow_split, size_t ws_bytes, hipStream_t s) {
+  if (dt == TP_F32) {
+    p.splitk = 1;
+    p.k_chunk = p.K;
+    return hip_status(launch_gemm_f32(p, s));
+  }
+  const SplitPlan plan = plan_gemm_bf16(p.M, p.N, p.K, allow_split);
+  p.splitk = plan.splitk;
+  p.k_chunk = plan.k_chunk;
+  if (plan.splitk > 1) {
+    const size_t need = static_cast<size_t>(plan.splitk) * p.M * p.N * sizeof(float);
+    if (!p.ws || ws_bytes < need) return TP_ERR_WORKSPACE;
+    hipError_t e = launch_gemm_bf16(p, plan, s);
+    if (e != hipSuccess) return hip_status(e);
+    return hip_status(launch_splitk_fixup(p, s));
+  }
+  return hip_status(launch_gemm_bf16(p, plan, s));
+}
+
+size_t wgrad_split_bytes(int64_t T, int64_t k, int64_t n, int dt) {
+  if (dt != TP_BF16) return 0;
+  const SplitPlan plan = plan_gemm_bf16(k, n, T, true);
+  if (plan.splitk <= 1) return 0;
+  // keep the column-sum partials 256-byte aligned behind the split-K partials
+  const size_t b = static_cast<size_t>(plan.splitk) * k * n * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, void* Y_i,
+                         void* U_i, int64_t T, int64_t h, int64_t n, int64_t ld_x,
+                         int64_t ld_a, int64_t ld_y, int dt, int act, hipStream_t stream) {
+  if (!X || !A_i || !Y_i) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (act != TP_ACT_NONE && !U_i) return TP_ERR_NULL;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_x < h || ld_a < n || ld_y < n) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = X;
+  p.b = A_i;
+  p.c = Y_i;
+  p.c2 = U_i;
+  p.bias = bias_i;
+  p.M = T;
+  p.N = n;
+  p.K = h;
+  p.lda = ld_x;
+  p.ldb = ld_a;
+  p.ldc = ld_y;
+  p.epi = EPI_BIAS_ACT;
+  p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
+  p.out_bf16 = dt == TP_BF16;
+  p.a_kcontig = 1;  // X [T, h]
+  p.b_kcontig = 0;  // A_i [h, n]
+  return run_gemm(p, dt, false, 0, stream);
+}
+
+int tp_row_linear_fwd_partial(const void* Y_i, const void* B_i, float* Zp_i, int64_t T,
+                              int64_t k, int64_t h, int64_t ld_y, int64_t ld_b,
+                              int64_t ld_z, int dt, hipStream_t stream) {
+  if (!Y_i || !B_i || !Zp_i) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(h)) return TP_ERR_SHAPE;
+  if (ld_y < k || ld_b < h || ld_z < h) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = Y_i;
+  p.b = B_i;
+  p.c = Zp_i;
+  p.M = T;
+  p.N = h;
+  p.K = k;
+  p.lda = ld_y;
+  p.ldb = ld_b;
+  p.ldc = ld_z;
+  p.epi = EPI_STORE;
+  p.out_bf16 = 0;
+  p.a_kcontig = 1;  // Y_i [T, k]
+  p.b_kcontig = 0;  // B_i [k, h]
+  return run_gemm(p, dt, false, 0, stream);
+}
+
+int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act, void* dIn,
+                        int64_t T, int64_t k, int64_t n, int64_t ld_dout, int64_t ld_w,
+                        int64_t ld_u, int64_t ld_din, int dt, int out_dt,
+                        hipStream_t stream) {
+  if (!dOut || !W || !dIn) return TP_ERR_NULL;
+  if (!dtype_ok(dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (dt == TP_F32 && out_dt != TP_F32) return TP_ERR_DTYPE;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (act != TP_ACT_NONE && !U) return TP_ERR_NULL;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_dout < n || ld_w < n || ld_din < k) return TP_ERR_SHAPE;
+  if (act != TP_ACT_NONE && ld_u < k) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = dOut;
+  p.b = W;
+  p.c = dIn;
+  p.u = U;
+  p.M = T;
+  p.N = k;
+  p.K = n;
+  p.lda = ld_dout;
+  p.ldb = ld_w;
+  p.ldc = ld_din;
+  p.ldu = ld_u;
+  p.epi = act != TP_ACT_NONE ? EPI_DACT : EPI_STORE;
+  p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
+  p.out_bf16 = out_dt == TP_BF16;
+  p.a_kcontig = 1;  // dOut [T, n]
+  p.b_kcontig = 1;  // W [k, n] read as W^T: K (= n) contiguous
+  return run_gemm(p, dt, false, 0, stream);
+}
+
+int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
+                                       size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  *bytes = wgrad_split_bytes(T, k, n, dt) + colsum_workspace_bytes(T, n);
+  return TP_OK;
+}
+
+int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbias, int64_t T,
+                        int64_t k, int64_t n, int64_t ld_in, int64_t ld_dout, int64_t ld_dw,
+                        int accumulate, int dt, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!In || !dOut || !dW) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_in < k || ld_dout < n || ld_dw < n) return TP_ERR_SHAPE;
+  const size_t split_bytes = wgrad_split_bytes(T, k, n, dt);
+  const size_t cs_bytes = dbias ? colsum_workspace_bytes(T, n) : 0;
+  if (split_bytes + cs_bytes > 0 && (!workspace || workspace_bytes < split_bytes + cs_bytes))
+    return TP_ERR_WORKSPACE;
+  GemmParams p{};
+  p.a = In;
+  p.b = dOut;
+  p.c = dW;
+  p.M = k;
+  p.N = n;
+  p.K = T;
+  p.lda = ld_in;
+  p.ldb = ld_dout;
+  p.ldc = ld_dw;
+  p.epi = EPI_STORE;
+  p.out_bf16 = 0;
+  p.accumulate = accumulate != 0;
+  p.ws = static_cast<float*>(workspace);
+  p.a_kcontig = 0;  // In [T, k] read as In^T: M (= k) contiguous
+  p.b_kcontig = 0;  // dOut [T, n]: N contiguous
+  int st = run_gemm(p, dt, true, split_bytes, stream);
+  if (st != TP_OK || !dbias) return st;
+  ColsumParams c{};
+  c.src = dOut;
+  c.T = T;
+  c.N = n;
+  c.ld = ld_dout;
+  c.src_bf16 = dt == TP_BF16;
+  c.dbias = dbias;
+  c.accumulate = accumulate != 0;
+  c.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes);
+  return hip_status(launch_colsum(c, stream));
+}
+
+int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
+                       int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, int out_dt,
+                       hipStream_t stream) {
+  if (!partials || !out) return TP_ERR_NULL;
+  if (p < 1 || p > kMaxPartials) return TP_ERR_SHAPE;
+  for (int i = 0; i < p; ++i)
+    if (!partials[i]) return TP_ERR_NULL;
+  if (!dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h)) return TP_ERR_SHAPE;
+  if (ld_p < h || ld_out < h) return TP_ERR_SHAPE;
+  ReduceParams r{};
+  for (int i = 0; i < p; ++i) r.parts[i] = partials[i];
+  r.p = p;
+  r.bias = bias;
+  r.out = out;
+  r.T = T;
+  r.N = h;
+  r.ldp = ld_p;
+  r.ldo = ld_out;
+  r.out_bf16 = out_dt == TP_BF16;
+  return hip_status(launch_reduce(r, stream));
+}
+
+int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, int64_t ld_u,
+                int64_t ld_y, int in_dt, int out_dt, int act, hipStream_t stream) {
+  if (!U || !Y) return TP_ERR_NULL;
+  if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (!dim_ok(T) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_u < n || ld_y < n) return TP_ERR_SHAPE;
+  BiasActParams b{};
+  b.u = U;
+  b.bias = bias;
+  b.y = Y;
+  b.T = T;
+  b.N = n;
+  b.ldu = ld_u;
+  b.ldy = ld_y;
+  b.in_bf16 = in_dt == TP_BF16;
+  b.u_f32 = in_dt == TP_F32;
+  b.out_bf16 = out_dt == TP_BF16;
+  b.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
+  return hip_status(launch_bias_act(b, stream));
+}
+
+const char* tp_status_string(int status) {
+  switch (status) {
+    case TP_OK:
+      return "TP_OK";
+    case TP_ERR_NULL:
+      return "TP_ERR_NULL: a required pointer is NULL";
+    case TP_ERR_SHAPE:
+      return "TP_ERR_SHAPE: bad dimension, leading dimension or shard count";
+    case TP_ERR_DTYPE:
+      return "TP_ERR_DTYPE: unknown or unsupported dtype";
+    case TP_ERR_ACT:
+      return "TP_ERR_ACT: unknown activation";
+    case TP_ERR_WORKSPACE:
+      return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_HIP:
+      return "TP_ERR_HIP: a HIP launch failed";
+    default:
+      return "unknown tp_status";
+  }
+}
+
+int tp_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

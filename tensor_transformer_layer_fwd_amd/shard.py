@@ -1,0 +1,189 @@
+"""One forward + backward step of a tensor-parallel shard workload on one GPU.
+
+The sequence follows the "Megatron" page (zzmblog.top), "Tensor Parallelism":
+per shard i the column-parallel linear (fc1: U_i = X A_i + a_i, Y_i = GeLU(U_i);
+QKV_i = X W_i) and the row-parallel partial (fc2: Zp_i = Y_i B_i; output
+projection: C_i O_i), then the sum over shards that replaces the All-Reduce.
+The backward (not on the pages; derivatives of the same definitions) runs the
+row-parallel dgrad with the GeLU derivative, both wgrads with bias gradients,
+the column-parallel dgrad to a partial dX_i, and the sum of the partials.
+
+All p shards of a workload run one after another on the same device and
+stream; the shards' weights are column / row views of the unsharded tensors
+(no copies). torch provides device memory and streams only; every arithmetic
+step is a call into libtpmlp.so.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+def to_device(host_tensor, device) -> torch.Tensor:
+    """Upload a tp_inputs HostTensor (raw bf16 bits or fp32) unchanged."""
+    raw = host_tensor.raw
+    if host_tensor.dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(raw).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(raw, dtype=np.float32))
+    return t.to(device)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class ShardStep:
+    """Device buffers of one workload and the calls of one fwd+bwd step."""
+
+    def __init__(self, cfg, inputs: dict, device="cuda"):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+        self.tp_dt = L.TP_BF16 if cfg.dtype == "bf16" else L.TP_F32
+        self.inp = {k: to_device(v, self.device) for k, v in inputs.items()}
+        self.out = {}
+        self._graph = None
+        T, h = cfg.T, cfg.h
+        f32 = dict(device=self.device, dtype=torch.float32)
+        act = dict(device=self.device, dtype=self.dt)
+        shards = cfg.shards
+        ws = 0
+        if cfg.mlp:
+            F = cfg.F
+            for i in shards:
+                self.out[f"U_{i}"] = torch.empty(T, F, **act)
+                self.out[f"Y_{i}"] = torch.empty(T, F, **act)
+                self.out[f"Zp_{i}"] = torch.empty(T, h, **f32)
+                self.out[f"dU_{i}"] = torch.empty(T, F, **act)
+                self.out[f"dB_{i}"] = torch.empty(F, h, **f32)
+                self.out[f"dA_{i}"] = torch.empty(h, F, **f32)
+                self.out[f"dXp_{i}"] = torch.empty(T, h, **f32)
+                if cfg.has_bias:
+                    self.out[f"da_{i}"] = torch.empty(F, **f32)
+            if cfg.has_bias:
+                self.out["db"] = torch.empty(h, **f32)
+            if len(shards) == cfg.p:
+                self.out["Z"] = torch.empty(T, h, **act)
+                self.out["dX"] = torch.empty(T, h, **act)
+            ws = max(ws, L.tp_linear_bwd_wgrad_workspace_size(T, F, h, self.tp_dt),
+                     L.tp_linear_bwd_wgrad_workspace_size(T, h, F, self.tp_dt))
+        if cfg.attn:
+            Q, O = cfg.Q, cfg.O
+            for i in shards:
+                self.out[f"QKV_{i}"] = torch.empty(T, Q, **act)
+                self.out[f"Zpa_{i}"] = torch.empty(T, h, **f32)
+                self.out[f"dC_{i}"] = torch.empty(T, O, **act)
+                self.out[f"dOw_{i}"] = torch.empty(O, h, **f32)
+                self.out[f"dW_{i}"] = torch.empty(h, Q, **f32)
+                self.out[f"dXqp_{i}"] = torch.empty(T, h, **f32)
+            if len(shards) == cfg.p:
+                self.out["Za"] = torch.empty(T, h, **act)
+                self.out["dXq"] = torch.empty(T, h, **act)
+            ws = max(ws, L.tp_linear_bwd_wgrad_workspace_size(T, O, h, self.tp_dt),
+                     L.tp_linear_bwd_wgrad_workspace_size(T, h, Q, self.tp_dt))
+        # one scratch buffer, shared by the wgrad calls (they run in order on one stream)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+
+    # ------------------------------------------------------------------ views
+    def _col(self, name, i, width):
+        t = self.inp[name]
+        if not self.cfg.full_weights and name in ("A", "a"):
+            return t
+        return t[..., i * width:(i + 1) * width]
+
+    def _row(self, name, i, width):
+        t = self.inp[name]
+        if not self.cfg.full_weights and name == "B":
+            return t
+        return t[i * width:(i + 1) * width]
+
+    # ------------------------------------------------------------------ step
+    def mlp_forward(self):
+        cfg, o, inp = self.cfg, self.out, self.inp
+        F = cfg.F
+        for i in cfg.shards:
+            a_i = self._col("a", i, F) if cfg.has_bias else None
+            L.tp_column_linear_fwd(inp["X"], self._col("A", i, F), a_i, o[f"Y_{i}"], o[f"U_{i}"],
+                                   act="gelu")
+            L.tp_row_linear_fwd_partial(o[f"Y_{i}"], self._row("B", i, F), o[f"Zp_{i}"])
+        if "Z" in o:
+            L.tp_reduce_partials([o[f"Zp_{i}"] for i in cfg.shards],
+                                 inp["b"] if cfg.has_bias else None, o["Z"])
+
+    def mlp_backward(self):
+        cfg, o, inp = self.cfg, self.out, self.inp
+        F = cfg.F
+        for n, i in enumerate(cfg.shards):
+            B_i, A_i = self._row("B", i, F), self._col("A", i, F)
+            L.tp_linear_bwd_dgrad(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"], act="gelu")
+            L.tp_linear_bwd_wgrad(o[f"Y_{i}"], inp["dZ"], o[f"dB_{i}"],
+                                  o["db"] if (cfg.has_bias and n == 0) else None,
+                                  workspace=self.workspace)
+            L.tp_linear_bwd_dgrad(o[f"dU_{i}"], A_i, None, o[f"dXp_{i}"], act="none")
+            L.tp_linear_bwd_wgrad(inp["X"], o[f"dU_{i}"], o[f"dA_{i}"],
+                                  o.get(f"da_{i}"), workspace=self.workspace)
+        if "dX" in o:
+            L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])
+
+    def attn_forward(self):
+        cfg, o, inp = self.cfg, self.out, self.inp
+        Q, O = cfg.Q, cfg.O
+        for i in cfg.shards:
+            L.tp_column_linear_fwd(inp["X"], self._col("W", i, Q), None, o[f"QKV_{i}"], None,
+                                   act="none")
+            L.tp_row_linear_fwd_partial(self._col("C", i, O), self._row("Ow", i, O),
+                                        o[f"Zpa_{i}"])
+        if "Za" in o:
+            L.tp_reduce_partials([o[f"Zpa_{i}"] for i in cfg.shards], None, o["Za"])
+
+    def attn_backward(self):
+        cfg, o, inp = self.cfg, self.out, self.inp
+        Q, O = cfg.Q, cfg.O
+        for i in cfg.shards:
+            Ow_i, W_i = self._row("Ow", i, O), self._col("W", i, Q)
+            C_i, dQKV_i = self._col("C", i, O), self._col("dQKV", i, Q)
+            L.tp_linear_bwd_dgrad(inp["dZa"], Ow_i, None, o[f"dC_{i}"], act="none")
+            L.tp_linear_bwd_wgrad(C_i, inp["dZa"], o[f"dOw_{i}"], None, workspace=self.workspace)
+            L.tp_linear_bwd_dgrad(dQKV_i, W_i, None, o[f"dXqp_{i}"], act="none")
+            L.tp_linear_bwd_wgrad(inp["X"], dQKV_i, o[f"dW_{i}"], None, workspace=self.workspace)
+        if "dXq" in o:
+            L.tp_reduce_partials([o[f"dXqp_{i}"] for i in cfg.shards], None, o["dXq"])
+
+    def run_eager(self):
+        """Enqueue one fwd+bwd step on the current stream."""
+        if self.cfg.attn:
+            self.attn_forward()
+        if self.cfg.mlp:
+            self.mlp_forward()
+        if self.cfg.attn:
+            self.attn_backward()
+        if self.cfg.mlp:
+            self.mlp_backward()
+
+    def capture(self):
+        """Record one step into a HIP graph (launch overhead off the host path)."""
+        s = torch.cuda.Stream(device=self.device)
+        s.wait_stream(torch.cuda.current_stream(self.device))
+        with torch.cuda.stream(s):
+            self.run_eager()  # warm-up outside the graph
+        torch.cuda.current_stream(self.device).wait_stream(s)
+        torch.cuda.synchronize(self.device)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run_eager()
+        self._graph = g
+        return g
+
+    def run(self):
+        if self._graph is not None:
+            self._graph.replay()
+        else:
+            self.run_eager()
+
+    def results(self) -> dict:
+        """All outputs as float64 numpy arrays (names as in the oracle)."""
+        torch.cuda.synchronize(self.device)
+        return {k: to_f64(v) for k, v in self.out.items()}

@@ -16,3 +16,12 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _library_built():
+    """Build libtpmlp.so once if it is missing (an existing build is used as is)."""
+    from tensor_transformer_layer_fwd_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from tensor_transformer_layer_fwd_amd import build
+        build.build()

@@ -1,0 +1,118 @@
+"""Host-side checks of the C ABI (CPU only: no kernel is launched).
+
+The library must load without a GPU, export every function include/tp_mlp.h
+declares, and reject bad arguments with the documented status before making
+any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tensor_transformer_layer_fwd_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp_mlp.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(tp_\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.lib()
+
+
+def test_header_and_binding_agree():
+    names = declared_functions()
+    assert "tp_column_linear_fwd" in names and "tp_reduce_partials" in names
+    assert set(names) == set(L.SIGNATURES), set(names) ^ set(L.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for code, name in L.STATUS.items():
+        assert L.tp_status_string(code).startswith(name)
+    assert L.tp_status_string(12345) == "unknown tp_status"
+    assert L.tp_last_hip_error() == 0
+
+
+def test_workspace_size_query(lib):
+    n = L.tp_linear_bwd_wgrad_workspace_size(4096, 1536, 768, L.TP_BF16)
+    assert n > 0 and n % 4 == 0
+    # fp32 needs only the column-sum partials: ceil(T/128) * n floats
+    assert L.tp_linear_bwd_wgrad_workspace_size(512, 24, 12, L.TP_F32) == 4 * 12 * 4
+    assert L.tp_linear_bwd_wgrad_workspace_size(100, 24, 12, L.TP_F32) == 0
+    out = ctypes.c_size_t(7)
+    assert lib.tp_linear_bwd_wgrad_workspace_size(0, 5, 5, L.TP_BF16, ctypes.byref(out)) == -2
+    assert lib.tp_linear_bwd_wgrad_workspace_size(5, 5, 5, 7, ctypes.byref(out)) == -3
+    assert lib.tp_linear_bwd_wgrad_workspace_size(5, 5, 5, 1, None) == -1
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation
+
+
+def test_column_fwd_validation(lib):
+    f = lib.tp_column_linear_fwd
+    ok = dict(X=FAKE, A=FAKE, b=None, Y=FAKE, U=FAKE, T=8, h=4, n=4, ldx=4, lda=4, ldy=4,
+              dt=1, act=1)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["X"], a["A"], a["b"], a["Y"], a["U"], a["T"], a["h"], a["n"], a["ldx"],
+                 a["lda"], a["ldy"], a["dt"], a["act"], None)
+
+    assert call(X=None) == -1
+    assert call(Y=None) == -1
+    assert call(U=None) == -1            # GeLU needs the pre-activation buffer
+    assert call(dt=2) == -3
+    assert call(act=9) == -4
+    assert call(T=0) == -2
+    assert call(n=-1) == -2
+    assert call(h=1 << 31) == -2
+    assert call(ldx=3) == -2
+    assert call(lda=3) == -2
+    assert call(ldy=3) == -2
+
+
+def test_other_entry_points_validation(lib):
+    assert lib.tp_row_linear_fwd_partial(FAKE, FAKE, None, 8, 4, 4, 4, 4, 4, 1, None) == -1
+    assert lib.tp_row_linear_fwd_partial(FAKE, FAKE, FAKE, 8, 4, 4, 3, 4, 4, 1, None) == -2
+    assert lib.tp_row_linear_fwd_partial(FAKE, FAKE, FAKE, 8, 4, 4, 4, 4, 4, 5, None) == -3
+    d = lib.tp_linear_bwd_dgrad
+    assert d(FAKE, FAKE, None, 1, FAKE, 8, 4, 4, 4, 4, 4, 4, 1, 1, None) == -1  # GeLU needs U
+    assert d(FAKE, FAKE, FAKE, 3, FAKE, 8, 4, 4, 4, 4, 4, 4, 1, 1, None) == -4
+    assert d(FAKE, FAKE, FAKE, 1, FAKE, 8, 4, 4, 4, 4, 4, 4, 0, 1, None) == -3  # f32 in, bf16 out
+    assert d(FAKE, FAKE, FAKE, 1, FAKE, 8, 4, 4, 4, 4, 3, 4, 1, 1, None) == -2  # ld_u < k
+    assert d(FAKE, FAKE, None, 0, FAKE, 8, 4, 4, 4, 3, 4, 4, 1, 0, None) == -2  # ld_w < n
+    w = lib.tp_linear_bwd_wgrad
+    assert w(FAKE, FAKE, None, None, 8, 4, 4, 4, 4, 4, 0, 1, None, 0, None) == -1
+    assert w(FAKE, FAKE, FAKE, None, 8, 4, 4, 4, 4, 3, 0, 1, None, 0, None) == -2
+    # a shape that needs split-K partials, with no workspace
+    need = L.tp_linear_bwd_wgrad_workspace_size(4096, 256, 256, L.TP_BF16)
+    assert need > 0
+    assert w(FAKE, FAKE, FAKE, None, 4096, 256, 256, 256, 256, 256, 0, 1, None, 0, None) == -5
+    assert w(FAKE, FAKE, FAKE, None, 4096, 256, 256, 256, 256, 256, 0, 1, FAKE, 64, None) == -5
+    # bias gradient over more than one row chunk needs the column-sum partials
+    assert w(FAKE, FAKE, FAKE, FAKE, 1000, 4, 4, 4, 4, 4, 0, 0, None, 0, None) == -5
+    r = lib.tp_reduce_partials
+    arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
+    assert r(None, 2, None, FAKE, 8, 4, 4, 4, 1, None) == -1
+    assert r(arr, 0, None, FAKE, 8, 4, 4, 4, 1, None) == -2
+    assert r(arr, 17, None, FAKE, 8, 4, 4, 4, 1, None) == -2
+    assert r(arr, 2, None, FAKE, 8, 4, 3, 4, 1, None) == -2
+    assert r(arr, 2, None, FAKE, 8, 4, 4, 4, 2, None) == -3
+    arr0 = (ctypes.c_void_p * 2)(0x1000, None)
+    assert r(arr0, 2, None, FAKE, 8, 4, 4, 4, 1, None) == -1
+    b = lib.tp_bias_act
+    assert b(FAKE, None, None, 8, 4, 4, 4, 0, 1, 1, None) == -1
+    assert b(FAKE, None, FAKE, 8, 4, 4, 4, 0, 1, 5, None) == -4
+    assert b(FAKE, None, FAKE, 8, 4, 3, 4, 0, 1, 1, None) == -2
