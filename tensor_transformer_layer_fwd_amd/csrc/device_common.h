@@ -43,10 +43,10 @@ __device__ __forceinline__ float gelu_tanh(float x) {
 
 // d/dx of gelu_tanh. With g = 1/(1 + exp(-2s)):
 //   gelu'(x) = g + x * 2 g (1 - g) * s'(x),  s'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2).
-// For |x| >= 10, g is 0 or 1 to fp32 precision; x is clamped there so that the
-// cubic cannot overflow (the result is then 0 or 1 up to ~1e-35).
+// For |x| >= 1e4, g is exactly 0 or 1 in fp32, so g (1 - g) = 0 and the result
+// is g; x is clamped there only so that x^2 stays finite (no 0 * inf).
 __device__ __forceinline__ float gelu_tanh_grad(float x) {
-  float xc = fminf(fmaxf(x, -10.0f), 10.0f);
+  float xc = fminf(fmaxf(x, -1.0e4f), 1.0e4f);
   float x2 = xc * xc;
   float s = kSqrt2OverPi * fmaf(kGeluCubic * xc, x2, xc);
   float g = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * s));
@@ -91,6 +91,85 @@ __device__ __forceinline__ void epilogue_elem(const GemmParams& p, int64_t row, 
   } else {
     if (p.accumulate && !p.out_bf16) v += static_cast<const float*>(p.c)[o];
     store_elem(p.c, o, v, p.out_bf16);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Vector epilogue: 8 consecutive outputs (row, col .. col+7) of a bf16-operand
+// GEMM, with 16-byte loads and stores. Valid when epilogue_vec_ok(p) holds and
+// col is a multiple of 8 with col + 8 <= N.
+// --------------------------------------------------------------------------
+__device__ __forceinline__ bool aligned16(const void* ptr) {
+  return (reinterpret_cast<uintptr_t>(ptr) & 15) == 0;
+}
+
+__device__ __forceinline__ bool epilogue_vec_ok(const GemmParams& p) {
+  return aligned16(p.c) && (p.ldc & 7) == 0 && (!p.c2 || aligned16(p.c2)) &&
+         (!p.bias || aligned16(p.bias)) && (!p.u || (aligned16(p.u) && (p.ldu & 7) == 0));
+}
+
+typedef uint32_t ep_u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load8_bf16(const void* base, int64_t off, float v[8]) {
+  const ep_u32x4 w = *reinterpret_cast<const ep_u32x4*>(static_cast<const uint16_t*>(base) + off);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+  }
+}
+
+__device__ __forceinline__ void load8_f32(const void* base, int64_t off, float v[8]) {
+  const float* s = static_cast<const float*>(base) + off;
+  const f32x4_t a = *reinterpret_cast<const f32x4_t*>(s);
+  const f32x4_t b = *reinterpret_cast<const f32x4_t*>(s + 4);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = a[q];
+    v[q + 4] = b[q];
+  }
+}
+
+__device__ __forceinline__ void store8(void* base, int64_t off, const float v[8], int is_bf16) {
+  if (is_bf16) {
+    *reinterpret_cast<ep_u32x4*>(static_cast<uint16_t*>(base) + off) =
+        ep_u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                 pack_bf16x2(v[6], v[7])};
+  } else {
+    float* d = static_cast<float*>(base) + off;
+    *reinterpret_cast<f32x4_t*>(d) = f32x4_t{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<f32x4_t*>(d + 4) = f32x4_t{v[4], v[5], v[6], v[7]};
+  }
+}
+
+__device__ __forceinline__ void epilogue_vec8(const GemmParams& p, int64_t row, int64_t col,
+                                              float v[8]) {
+  const int64_t o = row * p.ldc + col;
+  if (p.epi == EPI_BIAS_ACT) {
+    if (p.bias) {
+      float b[8];
+      load8_bf16(p.bias, col, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += b[q];
+    }
+    if (p.c2) store8(p.c2, o, v, p.out_bf16);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] = apply_act(p.act, v[q]);
+    store8(p.c, o, v, p.out_bf16);
+  } else if (p.epi == EPI_DACT) {
+    float u[8];
+    load8_bf16(p.u, row * p.ldu + col, u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] *= apply_act_grad(p.act, u[q]);
+    store8(p.c, o, v, p.out_bf16);
+  } else {
+    if (p.accumulate && !p.out_bf16) {
+      float c[8];
+      load8_f32(p.c, o, c);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += c[q];
+    }
+    store8(p.c, o, v, p.out_bf16);
   }
 }
 

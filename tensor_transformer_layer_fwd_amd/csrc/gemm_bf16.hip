@@ -24,6 +24,8 @@
 // in groups of 8 tile-rows so that neighbours share operand tiles in L2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -31,6 +33,11 @@ namespace tpmlp {
 namespace {
 
 constexpr int KT = 64;  // K-tile (elements), one 128-byte LDS row
+
+// Staging registers are native vectors (not HIP's union-based uint4), so the
+// optimiser keeps them in VGPRs.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * KT + (((chunk ^ row ^ (row >> 3)) & 7) << 3);
@@ -45,7 +52,7 @@ template <int ROWS, int NT, bool CHECK>
 struct LoadKContig {
   static constexpr int NV = ROWS * (KT / 8) / NT;  // 16-byte vectors per thread
   static_assert(NV >= 1 && NV * NT == ROWS * (KT / 8), "tile/threads mismatch");
-  uint4 v[NV];
+  u32x4 v[NV];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld,
                                        int64_t r0, int64_t rows_total, int64_t k0,
@@ -56,18 +63,16 @@ struct LoadKContig {
       const int r = idx >> 3, ch = idx & 7;
       const int64_t gr = r0 + r, gk = k0 + ch * 8;
       if (!CHECK) {
-        v[i] = *reinterpret_cast<const uint4*>(base + gr * ld + gk);
+        v[i] = *reinterpret_cast<const u32x4*>(base + gr * ld + gk);
       } else if (gr < rows_total && gk + 8 <= kend && vec_ok) {
-        v[i] = *reinterpret_cast<const uint4*>(base + gr * ld + gk);
+        v[i] = *reinterpret_cast<const u32x4*>(base + gr * ld + gk);
       } else {
-        uint16_t e[8];
+        uint32_t e[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          e[j] = (gr < rows_total && gk + j < kend) ? base[gr * ld + gk + j] : uint16_t(0);
-        v[i].x = e[0] | (uint32_t(e[1]) << 16);
-        v[i].y = e[2] | (uint32_t(e[3]) << 16);
-        v[i].z = e[4] | (uint32_t(e[5]) << 16);
-        v[i].w = e[6] | (uint32_t(e[7]) << 16);
+          e[j] = (gr < rows_total && gk + j < kend) ? base[gr * ld + gk + j] : 0u;
+        v[i] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                     e[6] | (e[7] << 16)};
       }
     }
   }
@@ -77,14 +82,14 @@ struct LoadKContig {
     for (int i = 0; i < NV; ++i) {
       const int idx = tid + i * NT;
       const int r = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<uint4*>(lds + swz(r, ch)) = v[i];
+      *reinterpret_cast<u32x4*>(lds + swz(r, ch)) = v[i];
     }
   }
 };
 
-// 16-bit element q of a uint4.
-__device__ __forceinline__ uint32_t elem16(const uint4& v, int q) {
-  const uint32_t w = (q >> 1) == 0 ? v.x : (q >> 1) == 1 ? v.y : (q >> 1) == 2 ? v.z : v.w;
+// 16-bit element q (a compile-time constant after unrolling) of a u32x4.
+__device__ __forceinline__ uint32_t elem16(const u32x4& v, int q) {
+  const uint32_t w = v[q >> 1];
   return (q & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
@@ -98,7 +103,7 @@ struct LoadMNContig {
   static constexpr int RB = ROWS / 8;                        // 8-wide blocks along M/N
   static_assert(KB == 2 || KB == 4 || KB == 8, "unsupported K block");
   static_assert(NB >= 1 && NB * KB * 8 * NT == ROWS * KT, "tile/threads mismatch");
-  uint4 v[NB][KB];
+  u32x4 v[NB][KB];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ base, int64_t ld,
                                        int64_t r0, int64_t rows_total, int64_t k0,
@@ -112,18 +117,16 @@ struct LoadMNContig {
       for (int j = 0; j < KB; ++j) {
         const int64_t gk = k0 + kb * KB + j;
         if (!CHECK) {
-          v[b][j] = *reinterpret_cast<const uint4*>(base + gk * ld + gr);
+          v[b][j] = *reinterpret_cast<const u32x4*>(base + gk * ld + gr);
         } else if (gk < kend && gr + 8 <= rows_total && vec_ok) {
-          v[b][j] = *reinterpret_cast<const uint4*>(base + gk * ld + gr);
+          v[b][j] = *reinterpret_cast<const u32x4*>(base + gk * ld + gr);
         } else {
-          uint16_t e[8];
+          uint32_t e[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q)
-            e[q] = (gk < kend && gr + q < rows_total) ? base[gk * ld + gr + q] : uint16_t(0);
-          v[b][j].x = e[0] | (uint32_t(e[1]) << 16);
-          v[b][j].y = e[2] | (uint32_t(e[3]) << 16);
-          v[b][j].z = e[4] | (uint32_t(e[5]) << 16);
-          v[b][j].w = e[6] | (uint32_t(e[7]) << 16);
+            e[q] = (gk < kend && gr + q < rows_total) ? base[gk * ld + gr + q] : 0u;
+          v[b][j] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
+                          e[6] | (e[7] << 16)};
         }
       }
     }
@@ -141,23 +144,37 @@ struct LoadMNContig {
         const int r = rb * 8 + q;
         uint16_t* dst = lds + swz(r, kk >> 3) + (kk & 7);
         if constexpr (KB == 8) {
-          uint4 o;
-          o.x = elem16(v[b][0], q) | (elem16(v[b][1], q) << 16);
-          o.y = elem16(v[b][2], q) | (elem16(v[b][3], q) << 16);
-          o.z = elem16(v[b][4], q) | (elem16(v[b][5], q) << 16);
-          o.w = elem16(v[b][6], q) | (elem16(v[b][7], q) << 16);
-          *reinterpret_cast<uint4*>(dst) = o;
+          *reinterpret_cast<u32x4*>(dst) =
+              u32x4{elem16(v[b][0], q) | (elem16(v[b][1], q) << 16),
+                    elem16(v[b][2], q) | (elem16(v[b][3], q) << 16),
+                    elem16(v[b][4], q) | (elem16(v[b][5], q) << 16),
+                    elem16(v[b][6], q) | (elem16(v[b][7], q) << 16)};
         } else if constexpr (KB == 4) {
-          uint2 o;
-          o.x = elem16(v[b][0], q) | (elem16(v[b][1], q) << 16);
-          o.y = elem16(v[b][2], q) | (elem16(v[b][3], q) << 16);
-          *reinterpret_cast<uint2*>(dst) = o;
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{elem16(v[b][0], q) | (elem16(v[b][1], q) << 16),
+                    elem16(v[b][2], q) | (elem16(v[b][3], q) << 16)};
         } else {
           *reinterpret_cast<uint32_t*>(dst) = elem16(v[b][0], q) | (elem16(v[b][1], q) << 16);
         }
       }
     }
   }
+};
+
+// Calls f(std::integral_constant<int, I>) for I = I0 .. END-1, so that the
+// body indexes register arrays with compile-time constants only.
+template <int I0, int END>
+struct StaticFor {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f(std::integral_constant<int, I0>{});
+    StaticFor<I0 + 1, END>::run(f);
+  }
+};
+template <int END>
+struct StaticFor<END, END> {
+  template <class F>
+  __device__ __forceinline__ static void run(F&&) {}
 };
 
 template <bool KCONTIG, int ROWS, int NT, bool CHECK>
@@ -214,9 +231,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
   if (nk > 0) {
     la.load(A, p.lda, m0, p.M, kbeg, kend, a_vec, tid);
@@ -260,34 +275,66 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
     __syncthreads();
   }
 
-  // ---- epilogue. 32x32 accumulator layout: lane holds column (lane & 31) and,
-  // in register r, row 8*(r/4) + 4*(lane/32) + r%4.
-  const int64_t rbase = m0 + wm * WTM + 4 * (lane >> 5);
-  const int64_t cbase = n0 + wn * WTN + (lane & 31);
-  if (p.splitk > 1) {
-    float* ws = p.ws + static_cast<int64_t>(z) * p.M * p.N;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int64_t row = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-          const int64_t col = cbase + j * 32;
-          if (!CHECK || (row < p.M && col < p.N)) ws[row * p.N + col] = acc[i][j][r];
-        }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
+  // ---- epilogue through LDS. Each wave owns 32 x EP floats of the (now free)
+  // operand LDS. For every 32-row band i of its wave tile it writes the
+  // accumulators there in the 32x32 MFMA layout (lane holds column lane & 31;
+  // register r holds row 8*(r/4) + 4*(lane/32) + r%4), then reads them back as
+  // 8 consecutive columns per lane and finishes them with 16-byte accesses.
+  constexpr int EP = WTN + 4;       // padded row pitch (floats)
+  constexpr int LPR = WTN / 8;      // lanes per tile row on the way out
+  constexpr int RPP = 64 / LPR;     // tile rows per pass
+  static_assert(WM * WN * 32 * EP * 4 <= sizeof(smem), "epilogue LDS");
+  static_assert(32 % RPP == 0, "rows per pass");
+  float* ep = reinterpret_cast<float*>(&smem[0][0]) + wave * 32 * EP;
+  const int er = lane / LPR, ec = (lane % LPR) * 8;
+  const bool split = p.splitk > 1;
+  float* ws = split ? p.ws + static_cast<int64_t>(z) * p.M * p.N : nullptr;
+  const bool out_vec =
+      split ? ((reinterpret_cast<uintptr_t>(p.ws) & 15) == 0 && (p.N & 7) == 0)
+            : epilogue_vec_ok(p);
+  StaticFor<0, FM>::run([&](auto band) {
+    constexpr int i = decltype(band)::value;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = rbase + i * 32 + (r >> 2) * 8 + (r & 3);
-        const int64_t col = cbase + j * 32;
-        if (!CHECK || (row < p.M && col < p.N)) epilogue_elem(p, row, col, acc[i][j][r], 1);
+      for (int r = 0; r < 16; ++r)
+        ep[((r >> 2) * 8 + 4 * (lane >> 5) + (r & 3)) * EP + j * 32 + (lane & 31)] = acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int pass = 0; pass < 32 / RPP; ++pass) {
+      const int lr = pass * RPP + er;
+      const float* src = ep + lr * EP + ec;
+      float v[8];
+      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
+      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = lo[q];
+        v[q + 4] = hi[q];
       }
+      const int64_t row = m0 + wm * WTM + i * 32 + lr;
+      const int64_t col = n0 + wn * WTN + ec;
+      const bool full = !CHECK || (row < p.M && col + 8 <= p.N);
+      if (split) {
+        if (full && out_vec) {
+          float* d = ws + row * p.N + col;
+          *reinterpret_cast<f32x4_t*>(d) = lo;
+          *reinterpret_cast<f32x4_t*>(d + 4) = hi;
+        } else if (row < p.M) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q)
+            if (col + q < p.N) ws[row * p.N + col + q] = v[q];
+        }
+      } else if (full && out_vec) {
+        epilogue_vec8(p, row, col, v);
+      } else if (row < p.M) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+          if (col + q < p.N) epilogue_elem(p, row, col + q, v[q], 1);
+      }
+    }
+    __syncthreads();
+  });
 }
 
 // ---------------------------------------------------------------------------

@@ -213,7 +213,14 @@ def test_reduce_partials(dev, out_dt, p, T, h):
     tp.tp_reduce_partials(views, upload(biasr, out_dt, dev), out.view)
     torch.cuda.synchronize()
     ref = oracle.reduce_partials([x.astype(np.float64) for x in parts], bias)
-    assert err(out.value(), ref) <= (TOL["bf16"] if out_dt == "bf16" else 1e-6)
+    got = out.value()
+    if out_dt == "bf16":
+        assert err(got, ref) <= TOL["bf16"]
+    else:
+        # p fp32 additions (bias included), each with relative error <= 2^-24:
+        # |got - exact| <= p * 2^-24 * (sum_i |part_i| + |bias|) elementwise
+        mag = sum(np.abs(x.astype(np.float64)) for x in parts) + np.abs(bias)[None, :]
+        assert np.all(np.abs(got - ref) <= p * 2.0 ** -24 * mag * 1.0001)
 
 
 def test_reduce_partials_order_and_rounding(dev):
@@ -265,7 +272,9 @@ def test_gelu_extremes(dev):
     torch.cuda.synchronize()
     xs = x[0].astype(np.float64)
     np.testing.assert_array_equal(U.cpu().numpy()[0], x[0])
-    np.testing.assert_allclose(Y.cpu().numpy()[0], oracle.gelu_tanh(xs), rtol=2e-6, atol=1e-37)
+    # the oracle's tanh form cancels (1 + tanh(s) = 0 in float64) for x below
+    # about -8, where the true values are below 1e-30: absolute floor 1e-30
+    np.testing.assert_allclose(Y.cpu().numpy()[0], oracle.gelu_tanh(xs), rtol=2e-6, atol=1e-30)
     np.testing.assert_allclose(dU.cpu().numpy()[0], oracle.gelu_tanh_grad(xs), rtol=2e-6,
                                atol=1e-30)
     xn = np.array([[1.0, np.nan, 2.0]], np.float32)
