@@ -48,7 +48,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--only-call", default=None,
-                    help="profiling aid: launch only this call of shard 0 --steps times")
+                    help="profiling aid: comma-separated calls of shard 0, each launched "
+                         "--steps times")
     return ap.parse_args()
 
 
@@ -168,12 +169,13 @@ def main():
         step = ShardStep(cfg, make_inputs(cfg), "cuda:0")
         step.run_eager()
         calls = {n: (fn, f) for n, fn, f in shard_calls(step)}
-        fn, f = calls[args.only_call]
-        ms = time_call(fn, args.steps)
-        log(f"[bench] {args.workload} {args.only_call}: {ms * 1e3:.2f} us/launch, "
-            f"{f / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
-        print(json.dumps({"workload": args.workload, "call": args.only_call,
-                          "us_per_launch": ms * 1e3, "tflops": f / (ms * 1e-3) / 1e12}))
+        for name in args.only_call.split(","):
+            fn, f = calls[name]
+            ms = time_call(fn, args.steps)
+            log(f"[bench] {args.workload} {name}: {ms * 1e3:.2f} us/launch, "
+                f"{f / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+            print(json.dumps({"workload": args.workload, "call": name,
+                              "us_per_launch": ms * 1e3, "tflops": f / (ms * 1e-3) / 1e12}))
         return
 
     cfg, inputs, step, wall_ms, ev_ms, flops, tflops = run_workload(

@@ -189,6 +189,19 @@ int tp_reduce_partials(const float* const* partials, int p, const void* bias, vo
 int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, int64_t ld_u,
                 int64_t ld_y, int in_dt, int out_dt, int act, hipStream_t stream);
 
+/*
+ * Which GEMM kernel configuration the library uses for a bf16 product
+ * C[M,N] = op(A)[M,K] op(B)[K,N] of this shape (pure host function, for
+ * tuning and tests). allow_split != 0 for the weight-gradient products, which
+ * may split K. Writes the tile id (0: general kernel, any shape; 10: 256x256,
+ * 11: 256x128, 12: 128x256, 13: 128x128 pipelined kernels, used when M and N
+ * are multiples of the tile, K of 64 and both operands are 16-byte aligned
+ * with row strides a multiple of 8), the number of K slices, and the K extent
+ * of each slice. Any output pointer may be NULL.
+ */
+int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, int* splitk,
+                 int64_t* k_chunk);
+
 /* Human-readable name of a tp_status value (never NULL). */
 const char* tp_status_string(int status);
 

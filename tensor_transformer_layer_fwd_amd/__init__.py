@@ -13,6 +13,7 @@ from ._lib import (  # noqa: F401
     lib,
     tp_bias_act,
     tp_column_linear_fwd,
+    tp_gemm_plan,
     tp_last_hip_error,
     tp_linear_bwd_dgrad,
     tp_linear_bwd_wgrad,

@@ -38,6 +38,8 @@ SIGNATURES = {
     "tp_reduce_partials": (_int, [ctypes.POINTER(ctypes.c_void_p), _int, _vp, _vp, _i64, _i64, _i64,
                                   _i64, _int, _vp]),
     "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
+    "tp_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(ctypes.c_int),
+                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_hip_error": (_int, []),
 }
@@ -177,6 +179,14 @@ def tp_bias_act(U, bias, Y, act="gelu", stream=None):
     _check("tp_bias_act", lib().tp_bias_act(
         _ptr(U), _ptr(bias), _ptr(Y), T, n, _ld(U), _ld(Y), _dt(U), _dt(Y), _act(act),
         _stream(stream)))
+
+
+def tp_gemm_plan(M: int, N: int, K: int, allow_split: bool = False):
+    """(tile id, K slices, K per slice) the library uses for a bf16 product."""
+    t, sk, kc = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int64(0)
+    _check("tp_gemm_plan", lib().tp_gemm_plan(M, N, K, int(bool(allow_split)), ctypes.byref(t),
+                                               ctypes.byref(sk), ctypes.byref(kc)))
+    return int(t.value), int(sk.value), int(kc.value)
 
 
 def tp_status_string(status: int) -> str:

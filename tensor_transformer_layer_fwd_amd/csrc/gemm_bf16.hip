@@ -338,16 +338,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Tile configurations and dispatch
+// Launch
 // ---------------------------------------------------------------------------
-struct TileCfg {
-  int bm, bn;
-};
-constexpr TileCfg kTiles[] = {
-    {128, 128},  // 0: 4 waves (2x2), wave tile 64x64
-    {256, 256},  // 1: 8 waves (2x4), wave tile 128x64
-};
-
 template <int BM, int BN, int WM, int WN, bool AK, bool BKC>
 hipError_t launch_cfg(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
   const int64_t tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
@@ -366,47 +358,15 @@ hipError_t launch_cfg(const GemmParams& p, const SplitPlan& plan, hipStream_t s)
 
 template <bool AK, bool BKC>
 hipError_t launch_layout(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
-  switch (plan.tile) {
-    case 1:
-      return launch_cfg<256, 256, 2, 4, AK, BKC>(p, plan, s);
-    default:
-      return launch_cfg<128, 128, 2, 2, AK, BKC>(p, plan, s);
-  }
+  return launch_cfg<128, 128, 2, 2, AK, BKC>(p, plan, s);
 }
 
 }  // namespace
 
-SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
-  constexpr int kCUs = 256;
-  SplitPlan pl{0, 1, K};
-  const int64_t t256 = ((M + 255) / 256) * ((N + 255) / 256);
-  if (t256 >= kCUs && M % 256 == 0 && N % 256 == 0) pl.tile = 1;
-  const TileCfg tc = kTiles[pl.tile];
-  const int64_t tiles = ((M + tc.bm - 1) / tc.bm) * ((N + tc.bn - 1) / tc.bn);
-  if (allow_split && tiles < kCUs) {
-    // Split K so that the grid covers the CUs about once, keeping at least
-    // 4 K-tiles per split.
-    int64_t want = (kCUs + tiles - 1) / tiles;
-    int64_t max_split = K / (4 * KT);
-    int64_t s = want < max_split ? want : max_split;
-    if (s > 1) {
-      int64_t chunk = (K + s - 1) / s;
-      chunk = (chunk + KT - 1) / KT * KT;
-      pl.splitk = static_cast<int>((K + chunk - 1) / chunk);
-      pl.k_chunk = chunk;
-      if (pl.splitk <= 1) {
-        pl.splitk = 1;
-        pl.k_chunk = K;
-      }
-    }
-  }
-  return pl;
-}
-
-hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
-  if (p.a_kcontig && !p.b_kcontig) return launch_layout<true, false>(p, plan, s);   // NN
-  if (p.a_kcontig && p.b_kcontig) return launch_layout<true, true>(p, plan, s);     // NT
-  if (!p.a_kcontig && !p.b_kcontig) return launch_layout<false, false>(p, plan, s); // TN
+hipError_t launch_gemm_bf16_general(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+  if (p.a_kcontig && !p.b_kcontig) return launch_layout<true, false>(p, plan, s);    // NN
+  if (p.a_kcontig && p.b_kcontig) return launch_layout<true, true>(p, plan, s);      // NT
+  if (!p.a_kcontig && !p.b_kcontig) return launch_layout<false, false>(p, plan, s);  // TN
   return hipErrorInvalidValue;
 }
 

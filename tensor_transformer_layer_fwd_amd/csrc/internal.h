@@ -70,9 +70,22 @@ struct BiasActParams {
   int in_bf16, u_f32, out_bf16, act;
 };
 
-// Split-K choice shared by the workspace-size query and the launcher.
+// bf16 GEMM kernels. The pipelined kernel needs M and N to be multiples of
+// its tile, K of 64 and 16-byte aligned operands; the general kernel takes
+// any shape, stride and alignment.
+enum TileId : int {
+  kGeneral128x128 = 0,  // general kernel, 128x128 tile
+  kGeneral256x256 = 1,  // general kernel, 256x256 tile
+  kPipe256x256 = 10,
+  kPipe256x128 = 11,
+  kPipe128x256 = 12,
+  kPipe128x128 = 13,
+};
+
+// Tile and split-K choice. It depends on the shape only, so the workspace-size
+// query and the launch always agree; k_chunk is a multiple of 64.
 struct SplitPlan {
-  int tile;     // tile configuration index
+  int tile;     // TileId for aligned operands
   int splitk;   // >= 1
   int64_t k_chunk;
 };
@@ -80,7 +93,11 @@ struct SplitPlan {
 SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split);
 size_t colsum_workspace_bytes(int64_t T, int64_t N);
 
+// Launch per plan: the planned pipelined tile when the operands allow it,
+// otherwise the general kernel with the same split.
 hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
+hipError_t launch_gemm_bf16_general(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
+hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s);
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);

@@ -236,6 +236,16 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
   return hip_status(launch_bias_act(b, stream));
 }
 
+int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, int* splitk,
+                 int64_t* k_chunk) {
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return TP_ERR_SHAPE;
+  const SplitPlan plan = plan_gemm_bf16(M, N, K, allow_split != 0);
+  if (tile) *tile = plan.tile;
+  if (splitk) *splitk = plan.splitk;
+  if (k_chunk) *k_chunk = plan.k_chunk;
+  return TP_OK;
+}
+
 const char* tp_status_string(int status) {
   switch (status) {
     case TP_OK:

@@ -116,3 +116,23 @@ def test_other_entry_points_validation(lib):
     assert b(FAKE, None, None, 8, 4, 4, 4, 0, 1, 1, None) == -1
     assert b(FAKE, None, FAKE, 8, 4, 4, 4, 0, 1, 5, None) == -4
     assert b(FAKE, None, FAKE, 8, 4, 3, 4, 0, 1, 1, None) == -2
+
+
+def test_gemm_plan_query(lib):
+    # the workloads' products all land on the pipelined kernels
+    for M, N, K in [(4096, 1536, 768), (4096, 768, 1536), (2048, 6144, 12288),
+                    (2048, 12288, 6144), (6144, 1024, 256)]:
+        tile, sk, kc = L.tp_gemm_plan(M, N, K)
+        assert tile in (10, 11, 12, 13) and sk == 1 and kc == K
+    tile, sk, kc = L.tp_gemm_plan(768, 1536, 4096, allow_split=True)
+    assert tile >= 10 and sk >= 1 and kc * sk == 4096 and kc % 64 == 0
+    # ragged shapes use the general kernel
+    assert L.tp_gemm_plan(680, 1536, 768)[0] == 0
+    assert L.tp_gemm_plan(4096, 1536, 700)[0] == 0
+    # the plan never splits without permission and agrees with the workspace size
+    for M, N, K in [(768, 1536, 4096), (256, 256, 4096), (1536, 768, 4096)]:
+        tile, sk, kc = L.tp_gemm_plan(M, N, K, allow_split=True)
+        ws = L.tp_linear_bwd_wgrad_workspace_size(K, M, N, L.TP_BF16)
+        assert ws >= (sk * M * N * 4 if sk > 1 else 0)
+        assert L.tp_gemm_plan(M, N, K, allow_split=False)[1] == 1
+    assert lib.tp_gemm_plan(0, 5, 5, 0, None, None, None) == -2

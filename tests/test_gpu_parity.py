@@ -417,3 +417,81 @@ def test_determinism_and_graph_replay(dev):
             np.testing.assert_array_equal(first[k], got[k], err_msg=f"replay {rep}: {k}")
         # eager work between replays
         torch.randn(1000, device=dev).sum().item()
+
+
+# --------------------------------------------------------------------------- #
+# every pipelined tile configuration, in every operand layout                  #
+# --------------------------------------------------------------------------- #
+_CAND = sorted(((M, N, K) for M in (128, 256, 384, 512, 768, 1024, 1536, 2048, 4096)
+                for N in (128, 256, 384, 512, 768, 1024, 1536, 2048, 4096)
+                for K in (256, 512, 1024, 2048, 4096)), key=lambda s: s[0] * s[1] * s[2])
+
+
+def _shape_for(tile, allow_split, want_split):
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    for M, N, K in _CAND:
+        t, sk, _ = L.tp_gemm_plan(M, N, K, allow_split)
+        if t == tile and (sk > 1) == want_split:
+            return M, N, K
+    return None
+
+
+@pytest.mark.parametrize("tile", [10, 11, 12, 13])
+@pytest.mark.parametrize("op", ["fwd_gelu", "row_partial", "dgrad_gelu", "dgrad_f32", "wgrad",
+                                "wgrad_split"])
+def test_pipelined_tiles(dev, tile, op):
+    import tensor_transformer_layer_fwd_amd as tp
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    split = op == "wgrad_split"
+    shape = _shape_for(tile, op.startswith("wgrad"), split)
+    if shape is None:
+        pytest.skip(f"no candidate shape plans to tile {tile} for {op}")
+    M, N, K = shape
+    _say(f"pipelined tile={tile} op={op} M={M} N={N} K={K}")
+    rng = np.random.default_rng(tile * 100 + len(op))
+    dt = "bf16"
+    if op in ("fwd_gelu", "row_partial"):
+        X, Xr = rand(rng, (M, K), 1.0, dt)
+        W, Wr = rand(rng, (K, N), 0.05, dt)
+        if op == "fwd_gelu":
+            b, br = rand(rng, (N,), 0.1, dt)
+            Y, U = torch.empty(M, N, dtype=torch.bfloat16, device=dev), \
+                torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            tp.tp_column_linear_fwd(upload(Xr, dt, dev), upload(Wr, dt, dev), upload(br, dt, dev),
+                                    Y, U, act="gelu")
+            torch.cuda.synchronize()
+            U_ref, Y_ref = oracle.column_linear_fwd(X, W, b, "gelu")
+            assert err(Y.float().cpu().numpy(), Y_ref) <= TOL[dt]
+            assert err(U.float().cpu().numpy(), U_ref) <= TOL[dt]
+        else:
+            Z = torch.empty(M, N, device=dev)
+            tp.tp_row_linear_fwd_partial(upload(Xr, dt, dev), upload(Wr, dt, dev), Z)
+            torch.cuda.synchronize()
+            assert err(Z.cpu().numpy(), oracle.row_linear_fwd_partial(X, W)) <= 1e-5
+    elif op.startswith("dgrad"):
+        dO, dOr = rand(rng, (M, K), 1.0, dt)
+        W, Wr = rand(rng, (N, K), 0.05, dt)
+        if op == "dgrad_gelu":
+            U, Ur = rand(rng, (M, N), 1.5, dt)
+            dI = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            tp.tp_linear_bwd_dgrad(upload(dOr, dt, dev), upload(Wr, dt, dev), upload(Ur, dt, dev),
+                                   dI, act="gelu")
+            torch.cuda.synchronize()
+            assert err(dI.float().cpu().numpy(), oracle.linear_bwd_dgrad(dO, W, U, "gelu")) <= TOL[dt]
+        else:
+            dI = torch.empty(M, N, device=dev)
+            tp.tp_linear_bwd_dgrad(upload(dOr, dt, dev), upload(Wr, dt, dev), None, dI)
+            torch.cuda.synchronize()
+            assert err(dI.cpu().numpy(), oracle.linear_bwd_dgrad(dO, W)) <= 1e-5
+    else:
+        In, Inr = rand(rng, (K, M), 1.0, dt)
+        dO, dOr = rand(rng, (K, N), 1.0, dt)
+        dW = torch.empty(M, N, device=dev)
+        db = torch.empty(N, device=dev)
+        ws = torch.empty(max(16, L.tp_linear_bwd_wgrad_workspace_size(K, M, N, L.TP_BF16)),
+                         dtype=torch.uint8, device=dev)
+        tp.tp_linear_bwd_wgrad(upload(Inr, dt, dev), upload(dOr, dt, dev), dW, db, workspace=ws)
+        torch.cuda.synchronize()
+        rw, rb = oracle.linear_bwd_wgrad(In, dO)
+        assert err(dW.cpu().numpy(), rw) <= 1e-5
+        assert err(db.cpu().numpy(), rb) <= 1e-5
