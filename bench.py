@@ -78,16 +78,23 @@ def shard_calls(step, i=0):
 
 
 def time_call(fn, reps):
-    """Average duration (ms) of one call, HIP events on the stream it launches on."""
+    """Average device duration (ms) of one call: `reps` back-to-back calls are
+    captured into a HIP graph (so host launch cost is off the timed path) and
+    the replay is timed with HIP events on the stream it runs on."""
     import torch
-    s = torch.cuda.current_stream()
-    for _ in range(3):
+    for _ in range(2):
         fn()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(s)
-    for _ in range(reps):
-        fn()
+    g.replay()
     e1.record(s)
     e1.synchronize()
     return e0.elapsed_time(e1) / reps

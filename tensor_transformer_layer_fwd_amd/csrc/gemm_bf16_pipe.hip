@@ -34,6 +34,7 @@ namespace tpmlp {
 namespace {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <int J, int BYTES>
 __device__ __forceinline__ uint8_t* stage_buf() {
@@ -170,7 +171,7 @@ struct Operand {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC>
+template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -284,86 +285,153 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   wait_vmcnt<0>();
   block_sync();
 
-  // ---- epilogue through LDS (per-wave regions inside the stage buffers)
+  // ---- epilogue through LDS (per-wave regions inside the stage buffers).
+  // For each 32-row band of its wave tile a wave writes the accumulators to
+  // LDS in the 32x32 MFMA layout (lane holds column lane & 31; register r holds
+  // row 8*(r/4) + 4*(lane/32) + r%4) and reads them back as 8 consecutive
+  // columns per lane, which it finishes with 16-byte stores. A lane's columns
+  // are the same in every pass, so the bias is loaded once; the saved
+  // pre-activation U of the whole wave tile is loaded before the first store.
+  // (On gfx9 loads and stores share one counter: a load issued after stores
+  // could only be waited for together with them.)
   constexpr int EP = WTN + 4;
   constexpr int REGION = 32 * EP * 4;
   constexpr int WPS = SB / REGION;  // wave regions per stage
   static_assert(WPS >= 1 && WPS * S >= NW, "epilogue LDS");
   constexpr int VPR = WTN / 8;      // 8-column vectors per tile row
-  static_assert((32 * VPR) % 64 == 0, "epilogue passes");
+  static_assert(64 % VPR == 0 && WTN <= 64, "epilogue lanes / registers");
+  constexpr int RPP = 64 / VPR;     // tile rows per pass
+  constexpr int PASSES = 32 / RPP;
   const int ws_idx = wave / WPS;
   uint8_t* base = ws_idx == 0 ? stage_buf<0, SB>()
                 : ws_idx == 1 ? stage_buf<1, SB>()
                 : ws_idx == 2 ? stage_buf<2, SB>()
                               : stage_buf<(S > 3 ? 3 : 2), SB>();
-  float* ep = reinterpret_cast<float*>(base + (wave % WPS) * REGION);
-  const bool split = p.splitk > 1;
-  float* wsz = split ? p.ws + static_cast<int64_t>(z) * p.M * p.N : nullptr;
-  const bool out_vec = split ? ((reinterpret_cast<uintptr_t>(p.ws) & 15) == 0 && (p.N & 7) == 0)
-                             : epilogue_vec_ok(p);
+  const float* ep = reinterpret_cast<const float*>(base + (wave % WPS) * REGION);
+  const int lr0 = lane / VPR, ec = (lane % VPR) * 8;
+  const int64_t col = n0 + wn * WTN + ec;
+  const int64_t row0 = m0 + wm * WTM + lr0;
+  // fp32 output: C, or this K slice's partial sums (row stride N) when split
+  float* const cf = EK == kEpiF32 ? (p.splitk > 1 ? p.ws + static_cast<int64_t>(z) * p.M * p.N
+                                                   : static_cast<float*>(p.c))
+                                  : nullptr;
+  const int64_t ldc = (EK == kEpiF32 && p.splitk > 1) ? p.N : p.ldc;
+
+  float bias8[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) bias8[q] = 0.0f;
+  if (EK == kEpiBiasGelu && p.bias) load8_bf16(p.bias, col, bias8);
+  // U of band i+1 is loaded before the stores of band i (two register sets)
+  u32x4_t upre[2][PASSES];
+  const uint16_t* Ug = static_cast<const uint16_t*>(p.u);
+  auto load_u = [&](int i, u32x4_t(&d)[PASSES]) {
+#pragma unroll
+    for (int ps = 0; ps < PASSES; ++ps)
+      d[ps] = *reinterpret_cast<const u32x4_t*>(Ug + (row0 + i * 32 + ps * RPP) * p.ldu + col);
+  };
+  if (EK == kEpiDGelu) load_u(0, upre[0]);
+
+  // This wave's LDS region is written and read only by this wave, and LDS
+  // executes one wave's operations in order, so no barrier is needed between
+  // the bands. The LDS accesses are inline assembly: the compiler would
+  // otherwise guard them against the earlier copies into the same buffers with
+  // a full vector-memory wait, which also waits for the stores of the previous
+  // pass.
+  const uint32_t ep_w = lds_addr(reinterpret_cast<const uint8_t*>(ep)) +
+                        (4 * (lane >> 5) * EP + (lane & 31)) * 4;
+  const uint32_t ep_r = lds_addr(reinterpret_cast<const uint8_t*>(ep)) + (lr0 * EP + ec) * 4;
   Unroll<0, FM>::run([&](auto band) {
     constexpr int i = decltype(band)::value;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ep[((r >> 2) * 8 + 4 * (lane >> 5) + (r & 3)) * EP + j * 32 + (lane & 31)] = acc[i][j][r];
-    block_sync();
-#pragma unroll
-    for (int pass = 0; pass < 32 * VPR / 64; ++pass) {
-      const int v = pass * 64 + lane;
-      const int lr = v / VPR, ec = (v % VPR) * 8;
-      const float* src = ep + lr * EP + ec;
-      const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src);
-      const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(src + 4);
-      float vals[8];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        vals[q] = lo[q];
-        vals[q + 4] = hi[q];
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t a = ep_w + (((r >> 2) * 8 + (r & 3)) * EP + j * 32) * 4;
+        asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(acc[i][j][r]) : "memory");
       }
-      const int64_t row = m0 + wm * WTM + i * 32 + lr;
-      const int64_t col = n0 + wn * WTN + ec;
-      if (split) {
-        if (out_vec) {
-          float* d = wsz + row * p.N + col;
-          *reinterpret_cast<f32x4_t*>(d) = lo;
-          *reinterpret_cast<f32x4_t*>(d + 4) = hi;
-        } else {
+    if (EK == kEpiDGelu && i + 1 < FM) load_u(i + 1, upre[(i + 1) & 1]);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) wsz[row * p.N + col + q] = vals[q];
-        }
-      } else if (out_vec) {
-        epilogue_vec8(p, row, col, vals);
+    for (int ps = 0; ps < PASSES; ++ps) {
+      const uint32_t a = ep_r + ps * RPP * EP * 4;
+      f32x4_t lo, hi;
+      asm volatile("ds_read_b128 %0, %1" : "=v"(lo) : "v"(a) : "memory");
+      asm volatile("ds_read_b128 %0, %1" : "=v"(hi) : "v"(a + 16) : "memory");
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi)::"memory");
+      const int64_t row = row0 + i * 32 + ps * RPP;
+      if constexpr (EK == kEpiF32) {
+        float* d = cf + row * ldc + col;
+        *reinterpret_cast<f32x4_t*>(d) = lo;
+        *reinterpret_cast<f32x4_t*>(d + 4) = hi;
       } else {
+        float v[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) epilogue_elem(p, row, col + q, vals[q], 1);
+        for (int q = 0; q < 4; ++q) {
+          v[q] = lo[q];
+          v[q + 4] = hi[q];
+        }
+        const int64_t o = row * p.ldc + col;
+        if constexpr (EK == kEpiBiasGelu) {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] += bias8[q];
+          store8(p.c2, o, v, 1);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] = gelu_tanh(v[q]);
+        } else if constexpr (EK == kEpiDGelu) {
+          const u32x4_t w = upre[i & 1][ps];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            v[2 * q] *= gelu_tanh_grad(__uint_as_float(w[q] << 16));
+            v[2 * q + 1] *= gelu_tanh_grad(__uint_as_float(w[q] & 0xffff0000u));
+          }
+        }
+        store8(p.c, o, v, 1);
       }
     }
-    block_sync();
   });
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC>
-hipError_t launch_pipe_cfg(const GemmParams& p, int splitk, hipStream_t s) {
+hipError_t launch_pipe_cfg(const GemmParams& p, int splitk, int ek, hipStream_t s) {
   const int64_t tiles = (p.M / BM) * (p.N / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC>),
-                     dim3(static_cast<unsigned>(tiles), static_cast<unsigned>(splitk)),
-                     dim3(WM * WN * 64), 0, s, p);
+  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splitk));
+  const dim3 block(WM * WN * 64);
+  switch (ek) {
+    case kEpiF32:
+      hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiF32>), grid,
+                         block, 0, s, p);
+      break;
+    case kEpiBF16:
+      if constexpr (AK)
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiBF16>),
+                           grid, block, 0, s, p);
+      break;
+    case kEpiBiasGelu:
+      if constexpr (AK && !BKC)
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiBiasGelu>),
+                           grid, block, 0, s, p);
+      break;
+    case kEpiDGelu:
+      if constexpr (AK && BKC)
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiDGelu>),
+                           grid, block, 0, s, p);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <bool AK, bool BKC>
-hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, int ek, hipStream_t s) {
   switch (plan.tile) {
     case kPipe256x256:
-      return launch_pipe_cfg<256, 256, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, s);
+      return launch_pipe_cfg<256, 256, 2, 4, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     case kPipe256x128:
-      return launch_pipe_cfg<256, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, s);
+      return launch_pipe_cfg<256, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     case kPipe128x256:
-      return launch_pipe_cfg<128, 256, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, s);
+      return launch_pipe_cfg<128, 256, 2, 4, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     case kPipe128x128:
-      return launch_pipe_cfg<128, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, s);
+      return launch_pipe_cfg<128, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -371,10 +439,39 @@ hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, hipStr
 
 }  // namespace
 
-hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
-  if (p.a_kcontig && !p.b_kcontig) return launch_pipe_layout<true, false>(p, plan, s);    // NN
-  if (p.a_kcontig && p.b_kcontig) return launch_pipe_layout<true, true>(p, plan, s);      // NT
-  if (!p.a_kcontig && !p.b_kcontig) return launch_pipe_layout<false, false>(p, plan, s);  // TN
+int pipe_epilogue_kind(const GemmParams& p) {
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (p.splitk > 1) {
+    return (p.epi == EPI_STORE && a16(p.ws) && p.N % 8 == 0) ? kEpiF32 : kEpiNone;
+  }
+  if (!a16(p.c) || p.ldc % 8) return kEpiNone;
+  switch (p.epi) {
+    case EPI_STORE:
+      if (p.accumulate) return kEpiNone;
+      if (!p.out_bf16) return kEpiF32;
+      return p.a_kcontig ? kEpiBF16 : kEpiNone;
+    case EPI_BIAS_ACT:
+      // with no activation, no bias and no saved pre-activation it is a plain store
+      if (p.act == ACT_NONE && !p.bias && !p.c2 && p.out_bf16 && p.a_kcontig) return kEpiBF16;
+      if (p.act == ACT_GELU && p.out_bf16 && p.c2 && a16(p.c2) && (!p.bias || a16(p.bias)) &&
+          p.a_kcontig && !p.b_kcontig)
+        return kEpiBiasGelu;
+      return kEpiNone;
+    case EPI_DACT:
+      if (p.act == ACT_GELU && p.out_bf16 && p.u && a16(p.u) && p.ldu % 8 == 0 && p.a_kcontig &&
+          p.b_kcontig)
+        return kEpiDGelu;
+      return kEpiNone;
+    default:
+      return kEpiNone;
+  }
+}
+
+hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int ek,
+                                 hipStream_t s) {
+  if (p.a_kcontig && !p.b_kcontig) return launch_pipe_layout<true, false>(p, plan, ek, s);   // NN
+  if (p.a_kcontig && p.b_kcontig) return launch_pipe_layout<true, true>(p, plan, ek, s);     // NT
+  if (!p.a_kcontig && !p.b_kcontig) return launch_pipe_layout<false, false>(p, plan, ek, s); // TN
   return hipErrorInvalidValue;
 }
 

@@ -76,10 +76,10 @@ struct BiasActParams {
 enum TileId : int {
   kGeneral128x128 = 0,  // general kernel, 128x128 tile
   kGeneral256x256 = 1,  // general kernel, 256x256 tile
-  kPipe256x256 = 10,
-  kPipe256x128 = 11,
-  kPipe128x256 = 12,
-  kPipe128x128 = 13,
+  kPipe256x256 = 10,  // 8 waves (two per SIMD), 128x64 per wave
+  kPipe256x128 = 11,  // 4 waves, 128x64 per wave
+  kPipe128x256 = 12,  // 8 waves, 64x64 per wave
+  kPipe128x128 = 13,  // 4 waves, 64x64 per wave
 };
 
 // Tile and split-K choice. It depends on the shape only, so the workspace-size
@@ -97,7 +97,14 @@ size_t colsum_workspace_bytes(int64_t T, int64_t N);
 // otherwise the general kernel with the same split.
 hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
 hipError_t launch_gemm_bf16_general(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
-hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
+// Epilogue kinds the pipelined kernel is compiled for (one kernel per kind):
+// fp32 store (or split-K partial), bf16 store, bias + GeLU saving the
+// pre-activation, and GeLU derivative from the saved pre-activation. All
+// outputs 16-byte aligned with row strides a multiple of 8.
+enum EpiKind : int { kEpiNone = -1, kEpiF32 = 0, kEpiBF16 = 1, kEpiBiasGelu = 2, kEpiDGelu = 3 };
+int pipe_epilogue_kind(const GemmParams& p);  // kEpiNone: use the general kernel
+hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int ek,
+                                 hipStream_t s);
 hipError_t launch_gemm_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s);
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);

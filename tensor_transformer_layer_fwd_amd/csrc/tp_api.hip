@@ -2,7 +2,7 @@
 // runs before the first HIP call, so a rejected call launches nothing.
 #include <hip/hip_runtime.h>
 
-#include "../../include/tp_mlp.h"
+#include "tp_mlp.h"
 #include "internal.h"
 
 using namespace tpmlp;

@@ -223,6 +223,30 @@ def test_reduce_partials(dev, out_dt, p, T, h):
         assert np.all(np.abs(got - ref) <= p * 2.0 ** -24 * mag * 1.0001)
 
 
+def test_bf16_rounding_is_rne(dev):
+    """fp32 -> bf16 on the device (one partial, bf16 output) equals round to
+    nearest even bit for bit: ties, denormals, huge values, infinities, NaN."""
+    import tensor_transformer_layer_fwd_amd as tp
+    rng = np.random.default_rng(123)
+    x = (rng.standard_normal(60000) * 10.0 ** rng.integers(-40, 38, 60000)).astype(np.float32)
+    ties = (f32_to_bf16_bits(rng.standard_normal(2000).astype(np.float32)).astype(np.uint32) << 16)
+    ties = (ties | 0x8000).view(np.float32)  # exactly half-way between two bf16 values
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1.1754942e-38, 3.4028235e38, -3.4028235e38,
+                        np.inf, -np.inf], np.float32)
+    x = np.concatenate([x, ties, special])
+    n = x.size
+    out = torch.empty(1, n, dtype=torch.bfloat16, device=dev)
+    tp.tp_reduce_partials([torch.from_numpy(x).view(1, n).to(dev)], None, out)
+    torch.cuda.synchronize()
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)[0]
+    np.testing.assert_array_equal(got, f32_to_bf16_bits(x))
+    nan = torch.full((1, 8), float("nan"), device=dev)
+    outn = torch.empty(1, 8, dtype=torch.bfloat16, device=dev)
+    tp.tp_reduce_partials([nan], None, outn)
+    torch.cuda.synchronize()
+    assert torch.isnan(outn.float()).all()
+
+
 def test_reduce_partials_order_and_rounding(dev):
     """Sum in fp32 in shard order, bias last, one rounding: reproduce it exactly."""
     import tensor_transformer_layer_fwd_amd as tp
