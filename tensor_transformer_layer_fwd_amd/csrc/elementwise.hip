@@ -24,7 +24,28 @@ __global__ __launch_bounds__(256) void splitk_fixup_kernel(GemmParams p) {
   }
 }
 
-// Pass 1: block (cb, chunk) sums rows [chunk*R, chunk*R + R) of 128 columns.
+// Vector fix-up of fp32 weight gradients: four columns per thread, the K-slice
+// partials summed in slice order, then accumulated into C if requested.
+__global__ __launch_bounds__(256) void splitk_fixup_vec4_kernel(GemmParams p) {
+  const int64_t nq = p.N >> 2;
+  const int64_t total = p.M * nq;
+  const int64_t slice = p.M * p.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    const int64_t row = e / nq, col = (e - row * nq) << 2;
+    const float* w = p.ws + row * p.N + col;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(w);
+    for (int z = 1; z < p.splitk; ++z) v += *reinterpret_cast<const f32x4_t*>(w + z * slice);
+    float* c = static_cast<float*>(p.c) + row * p.ldc + col;
+    if (p.accumulate) v += *reinterpret_cast<const f32x4_t*>(c);
+    *reinterpret_cast<f32x4_t*>(c) = v;
+  }
+}
+
+// Column sums (bias gradients) in two deterministic passes over chunks of
+// kColsumRows rows.
+// Pass 1, general path: block (cb, chunk) sums its rows of 128 columns.
 // Thread (cx, ry) owns columns 2cx, 2cx+1 and rows ry, ry+4, ...; the four
 // row-groups are then added in order through LDS.
 __global__ __launch_bounds__(256) void colsum_pass1_kernel(ColsumParams p, int nchunks) {
@@ -56,13 +77,65 @@ __global__ __launch_bounds__(256) void colsum_pass1_kernel(ColsumParams p, int n
   }
 }
 
-// Pass 2: dbias[c] (+)= sum over chunks, in chunk order.
+// Pass 1, vector path (N a multiple of 8, 16-byte aligned rows): block (cb,
+// chunk) covers 256 columns; thread (cv, rl) loads 8 columns (16 bytes of
+// bf16, or 32 of fp32) of rows rl, rl+8, .., all loads independent, and the
+// 8 row lanes are added in order through LDS.
+__global__ __launch_bounds__(256) void colsum_vec_pass1_kernel(ColsumParams p, int nchunks) {
+  __shared__ float part[8][256];
+  const int cv = threadIdx.x & 31, rl = threadIdx.x >> 5;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 256 + cv * 8;
+  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kColsumRows;
+  float s[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) s[q] = 0.0f;
+  if (c0 < p.N) {
+#pragma unroll
+    for (int j = 0; j < kColsumRows / 8; ++j) {
+      const int64_t t = t0 + rl + 8 * j;
+      if (t < p.T) {
+        float v[8];
+        if (p.src_bf16)
+          load8_bf16(p.src, t * p.ld + c0, v);
+        else
+          load8_f32(p.src, t * p.ld + c0, v);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s[q] += v[q];
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) part[rl][cv * 8 + q] = s[q];
+  __syncthreads();
+  const int64_t cc = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (cc < p.N) {
+    float v = part[0][threadIdx.x];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) v += part[r][threadIdx.x];
+    if (nchunks == 1)
+      p.dbias[cc] = p.accumulate ? p.dbias[cc] + v : v;
+    else
+      p.ws[static_cast<int64_t>(blockIdx.y) * p.N + cc] = v;
+  }
+}
+
+// Pass 2: dbias[c] (+)= sum over chunks. Each column's chunks are split over 4
+// threads (chunks i, i+4, ...; loads independent) whose sums are added in order.
 __global__ __launch_bounds__(256) void colsum_pass2_kernel(ColsumParams p, int nchunks) {
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (c >= p.N) return;
-  float v = 0.0f;
-  for (int i = 0; i < nchunks; ++i) v += p.ws[static_cast<int64_t>(i) * p.N + c];
-  p.dbias[c] = p.accumulate ? p.dbias[c] + v : v;
+  __shared__ float part[4][64];
+  const int cl = threadIdx.x & 63, pr = threadIdx.x >> 6;
+  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
+  float s = 0.0f;
+  if (c < p.N) {
+#pragma unroll 16
+    for (int i = pr; i < nchunks; i += 4) s += p.ws[static_cast<int64_t>(i) * p.N + c];
+  }
+  part[pr][cl] = s;
+  __syncthreads();
+  if (threadIdx.x < 64 && c < p.N) {
+    const float v = ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
+    p.dbias[c] = p.accumulate ? p.dbias[c] + v : v;
+  }
 }
 
 // out = ((parts[0] + parts[1]) + ...) + bias, rounded once. Vector path: four
@@ -166,20 +239,33 @@ size_t colsum_workspace_bytes(int64_t T, int64_t N) {
 }
 
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(splitk_fixup_kernel, dim3(grid_for(p.M * p.N, 256)), dim3(256), 0, s, p);
+  const bool vec = !p.out_bf16 && p.epi == EPI_STORE && p.N % 4 == 0 && p.ldc % 4 == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.ws) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(splitk_fixup_vec4_kernel, dim3(grid_for(p.M * p.N / 4, 256)), dim3(256), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL(splitk_fixup_kernel, dim3(grid_for(p.M * p.N, 256)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s) {
   const int64_t nchunks = (p.T + kColsumRows - 1) / kColsumRows;
-  const int64_t cblocks = (p.N + 127) / 128;
   if (nchunks > 65535) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(colsum_pass1_kernel,
-                     dim3(static_cast<unsigned>(cblocks), static_cast<unsigned>(nchunks)),
-                     dim3(256), 0, s, p, static_cast<int>(nchunks));
+  const bool vec = p.N % 8 == 0 && p.ld % 8 == 0 &&
+                   (reinterpret_cast<uintptr_t>(p.src) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(colsum_vec_pass1_kernel,
+                       dim3(static_cast<unsigned>((p.N + 255) / 256), static_cast<unsigned>(nchunks)),
+                       dim3(256), 0, s, p, static_cast<int>(nchunks));
+  else
+    hipLaunchKernelGGL(colsum_pass1_kernel,
+                       dim3(static_cast<unsigned>((p.N + 127) / 128), static_cast<unsigned>(nchunks)),
+                       dim3(256), 0, s, p, static_cast<int>(nchunks));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 1) return e;
-  hipLaunchKernelGGL(colsum_pass2_kernel, dim3(static_cast<unsigned>((p.N + 255) / 256)),
+  hipLaunchKernelGGL(colsum_pass2_kernel, dim3(static_cast<unsigned>((p.N + 63) / 64)),
                      dim3(256), 0, s, p, static_cast<int>(nchunks));
   return hipGetLastError();
 }

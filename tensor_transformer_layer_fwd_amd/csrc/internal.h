@@ -49,7 +49,7 @@ struct ColsumParams {
   float* ws;  // partial sums [nchunks, N]
 };
 
-constexpr int kColsumRows = 128;  // rows summed per block in the first pass
+constexpr int kColsumRows = 64;  // rows summed per block in the first pass
 
 // Reduction over shards.
 constexpr int kMaxPartials = 16;

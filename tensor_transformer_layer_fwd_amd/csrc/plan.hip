@@ -1,10 +1,10 @@
 // Host-side choice of GEMM tile and split-K, and the launch dispatch.
 //
-// The cost model counts, per CU, the matrix-core time of the tiles it runs
-// (scaled by a per-tile efficiency: larger wave tiles need less LDS traffic
-// per MFMA) plus the HBM time of the split-K partials, and takes the cheapest
-// (tile, split) pair. MI355X: 256 CUs, 4096 bf16 flop/clk/CU at 2.4 GHz,
-// 160 KiB LDS per CU.
+// The cost model counts rounds of tiles over the 256 CUs; a round costs a
+// fixed overhead (prologue, epilogue, launch) plus the tile's matrix work at a
+// per-CU rate measured for each tile configuration on MI355X (the clock runs
+// at 1.7-2.2 GHz under matrix load, below the 2.4 GHz peak). A split K adds the
+// HBM time of the fp32 partials and one fix-up launch.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -13,31 +13,29 @@ namespace tpmlp {
 namespace {
 
 constexpr int kCUs = 256;
-constexpr double kFlopPerSecPerCU = 4096.0 * 2.4e9;
+constexpr double kRoundOverheadSec = 3.0e-6;
 constexpr double kHbmBytesPerSec = 5.0e12;  // sustained, for partial traffic
 constexpr double kLaunchSec = 2.0e-6;       // one extra kernel
 
 struct PipeTile {
   TileId id;
-  int bm, bn, lds_kib;
-  double eff;
+  int bm, bn;
+  double flop_per_sec_per_cu;
 };
 constexpr PipeTile kPipeTiles[] = {
-    {kPipe256x256, 256, 256, 128, 0.85},
-    {kPipe256x128, 256, 128, 96, 0.75},
-    {kPipe128x256, 128, 256, 96, 0.75},
-    {kPipe128x128, 128, 128, 64, 0.60},
+    {kPipe256x256, 256, 256, 5.3e12},
+    {kPipe256x128, 256, 128, 4.6e12},
+    {kPipe128x256, 128, 256, 5.0e12},
+    {kPipe128x128, 128, 128, 4.0e12},
 };
 
-double cost(int64_t M, int64_t N, int64_t K, int bm, int bn, int lds_kib, double eff, int split) {
-  const int64_t tiles = (M / bm) * (N / bn) * split;
-  const int64_t per_cu = 160 / lds_kib;  // workgroups resident per CU
-  const int64_t rounds = (tiles + kCUs * per_cu - 1) / (kCUs * per_cu);
-  const int64_t busiest = rounds * per_cu < tiles ? rounds * per_cu : tiles;  // tiles on one CU
-  const double kc = static_cast<double>(K / split);
-  double t = static_cast<double>(busiest) * 2.0 * bm * bn * kc / (kFlopPerSecPerCU * eff);
-  if (split > 1) t += (split + 1.0) * M * N * 4.0 / kHbmBytesPerSec + kLaunchSec;
-  return t;
+double cost(int64_t M, int64_t N, int64_t K, const PipeTile& t, int split) {
+  const int64_t tiles = (M / t.bm) * (N / t.bn) * split;
+  const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+  const double flops = 2.0 * t.bm * t.bn * static_cast<double>(K / split);
+  double c = static_cast<double>(rounds) * (kRoundOverheadSec + flops / t.flop_per_sec_per_cu);
+  if (split > 1) c += (split + 1.0) * M * N * 4.0 / kHbmBytesPerSec + kLaunchSec;
+  return c;
 }
 
 }  // namespace
@@ -51,7 +49,7 @@ SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
     if (!k_ok || M % t.bm || N % t.bn) continue;
     for (int s : kSplits) {
       if (s > 1 && (!allow_split || K % (64 * s) || K / s < 256)) continue;
-      const double c = cost(M, N, K, t.bm, t.bn, t.lds_kib, t.eff, s);
+      const double c = cost(M, N, K, t, s);
       if (c < best_t) {
         best_t = c;
         best = SplitPlan{t.id, s, K / s};

@@ -48,9 +48,9 @@ def test_status_strings(lib):
 def test_workspace_size_query(lib):
     n = L.tp_linear_bwd_wgrad_workspace_size(4096, 1536, 768, L.TP_BF16)
     assert n > 0 and n % 4 == 0
-    # fp32 needs only the column-sum partials: ceil(T/128) * n floats
-    assert L.tp_linear_bwd_wgrad_workspace_size(512, 24, 12, L.TP_F32) == 4 * 12 * 4
-    assert L.tp_linear_bwd_wgrad_workspace_size(100, 24, 12, L.TP_F32) == 0
+    # fp32 needs only the column-sum partials: ceil(T/64) * n floats
+    assert L.tp_linear_bwd_wgrad_workspace_size(512, 24, 12, L.TP_F32) == 8 * 12 * 4
+    assert L.tp_linear_bwd_wgrad_workspace_size(64, 24, 12, L.TP_F32) == 0
     out = ctypes.c_size_t(7)
     assert lib.tp_linear_bwd_wgrad_workspace_size(0, 5, 5, L.TP_BF16, ctypes.byref(out)) == -2
     assert lib.tp_linear_bwd_wgrad_workspace_size(5, 5, 5, 7, ctypes.byref(out)) == -3
@@ -103,6 +103,7 @@ def test_other_entry_points_validation(lib):
     assert w(FAKE, FAKE, FAKE, None, 4096, 256, 256, 256, 256, 256, 0, 1, FAKE, 64, None) == -5
     # bias gradient over more than one row chunk needs the column-sum partials
     assert w(FAKE, FAKE, FAKE, FAKE, 1000, 4, 4, 4, 4, 4, 0, 0, None, 0, None) == -5
+    assert w(FAKE, FAKE, FAKE, FAKE, 65, 4, 4, 4, 4, 4, 0, 0, None, 0, None) == -5
     r = lib.tp_reduce_partials
     arr = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     assert r(None, 2, None, FAKE, 8, 4, 4, 4, 1, None) == -1
