@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--only-call", default=None,
                     help="profiling aid: comma-separated calls of shard 0, each launched "
                          "--steps times")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="profiling aid (with --only-call): also copy MIB MiB device-to-device "
+                         "three times, to scale HBM byte counters")
     return ap.parse_args()
 
 
@@ -132,6 +135,21 @@ def run_workload(name, steps, warmup):
     return cfg, inputs, step, wall_ms, ev_ms, flops, tflops
 
 
+def measured_traffic(call):
+    """HBM bytes per launch of `call` from profiles/traffic.json (two rocprofv3
+    --pmc runs, FETCH_SIZE and WRITE_SIZE, scaled by a plain copy), or None when
+    the record is for another call or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))
+        from tensor_transformer_layer_fwd_amd.prof_summary import source_hash
+        if rec.get("call") == call and rec.get("source_sha256") == source_hash():
+            return round(float(rec["traffic_bytes_per_launch"]))
+    except (OSError, ValueError, KeyError):
+        pass
+    return None
+
+
 def cpu_baseline(cfg, inputs, seconds):
     import oracle
     try:
@@ -183,6 +201,14 @@ def main():
                 f"{f / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
             print(json.dumps({"workload": args.workload, "call": name,
                               "us_per_launch": ms * 1e3, "tflops": f / (ms * 1e-3) / 1e12}))
+        if args.calibrate_copy:
+            n = args.calibrate_copy * 1024 * 1024 // 4
+            src = torch.ones(n, device="cuda:0")
+            dst = torch.empty_like(src)
+            for _ in range(3):
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            log(f"[bench] copied {args.calibrate_copy} MiB three times for counter calibration")
         return
 
     cfg, inputs, step, wall_ms, ev_ms, flops, tflops = run_workload(
@@ -190,16 +216,44 @@ def main():
     log(f"[bench] {cfg.name}: {wall_ms * 1e3:.1f} us/step (events {ev_ms * 1e3:.1f}), "
         f"{tflops:.1f} TFLOP/s = {100 * tflops / PEAK_BF16_TFLOPS:.1f}% of bf16 peak")
 
-    # per-call durations of shard 0 (events on the launch stream)
+    # per-call durations of shard 0 (HIP events on the launch stream)
     kernels = {}
     for name, fn, f in shard_calls(step):
         ms = time_call(fn, args.kernel_reps)
         kernels[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
     gemm_sum_us = sum(v["us"] for v in kernels.values()) * len(cfg.shards)
-    dom = max(kernels, key=lambda k: kernels[k]["us"])
+    # dominant kernel: the slowest call that is a single GEMM kernel (the wgrad
+    # calls also launch a split-K fix-up and the bias column sums)
+    single = [k for k in kernels if not k.endswith("wgrad")]
+    dom = max(single, key=lambda k: kernels[k]["us"])
     dom_flops = 2 * cfg.T * cfg.h * cfg.F
     dom_tf = dom_flops / (kernels[dom]["us"] * 1e-6) / 1e12
+    dom_shape = {"fc1_fwd": (cfg.T, cfg.F, cfg.h), "fc2_fwd": (cfg.T, cfg.h, cfg.F),
+                 "fc2_dgrad": (cfg.T, cfg.F, cfg.h), "fc1_dgrad": (cfg.T, cfg.h, cfg.F)}[dom]
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    dom_plan = L.tp_gemm_plan(*dom_shape)
     log(f"[bench] per-call: {json.dumps(kernels)}")
+
+    # HBM-bound passes: the sum over shards (fp32 partials -> bf16 + bias) and
+    # the standalone bias + GeLU pass (fp32 U -> bf16 Y) over one shard's [T, F]
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    o = step.out
+    parts = [o[f"Zp_{i}"] for i in cfg.shards]
+    red_bytes = len(parts) * cfg.T * cfg.h * 4 + cfg.T * cfg.h * 2 + cfg.h * 2
+    red_ms = time_call(lambda: L.tp_reduce_partials(parts, step.inp.get("b"), o["Z"]),
+                       args.kernel_reps)
+    u32 = torch.randn(cfg.T, cfg.F, device="cuda:0")
+    a32 = torch.randn(cfg.F, device="cuda:0")
+    ybf = torch.empty(cfg.T, cfg.F, dtype=torch.bfloat16, device="cuda:0")
+    gelu_bytes = cfg.T * cfg.F * (4 + 2) + cfg.F * 4
+    gelu_ms = time_call(lambda: L.tp_bias_act(u32, a32, ybf, act="gelu"), args.kernel_reps)
+    hbm = {"reduce_partials": {"GB/s": round(red_bytes / (red_ms * 1e-3) / 1e9, 1),
+                               "bytes": red_bytes, "us": round(red_ms * 1e3, 2)},
+           "bias_gelu": {"GB/s": round(gelu_bytes / (gelu_ms * 1e-3) / 1e9, 1),
+                         "bytes": gelu_bytes, "us": round(gelu_ms * 1e3, 2)},
+           "peak_GB/s": PEAK_HBM_GBS}
+    log(f"[bench] HBM passes: {json.dumps(hbm)}")
+    del u32, ybf
 
     extra = {}
     for name in [w for w in args.extra.split(",") if w and w != args.workload]:
@@ -241,9 +295,13 @@ def main():
                    "gemm_gflop_per_step": round(flops / 1e9, 2)},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(dom),
+                     "gemm": {"M": dom_shape[0], "N": dom_shape[1], "K": dom_shape[2],
+                              "tile": dom_plan[0], "us_per_launch": kernels[dom]["us"]}},
         "per_call_shard0": kernels,
         "gemm_calls_sum_us": round(gemm_sum_us, 1),
+        "hbm_passes": hbm,
         "cpu_baseline": cpu,
         "extra": extra,
     }

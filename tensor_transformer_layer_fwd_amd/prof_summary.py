@@ -1,0 +1,154 @@
+"""Summaries of rocprofv3 output for the committed profiles.
+
+    python -m tensor_transformer_layer_fwd_amd.prof_summary stats KERNEL_STATS_CSV \
+        --cmd "the profiled command" [--out profiles/NAME.txt]
+    python -m tensor_transformer_layer_fwd_amd.prof_summary traffic \
+        --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel SUBSTRING \
+        --grid GRID_SIZE --copy-mib MIB --cmd-fetch "..." --cmd-write "..." \
+        [--out profiles/traffic.json]
+    python -m tensor_transformer_layer_fwd_amd.prof_summary mfma COUNTER_CSV --cmd "..."
+
+`traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel into
+HBM bytes per launch, scaled by what the same counters read for a plain device
+copy of known size run in the same process (bench.py --calibrate-copy), and
+records a hash of the kernel sources so that bench.py reports the figure only
+while the kernels are unchanged.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import statistics
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+
+
+def source_hash() -> str:
+    """sha256 over the kernel sources and the public header."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files.append(os.path.join(os.path.dirname(PKG), "include", "tp_mlp.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _short(name: str) -> str:
+    return name.replace("tpmlp::(anonymous namespace)::", "").replace("(tpmlp::GemmParams)", "")
+
+
+def cmd_stats(a):
+    rows = list(csv.DictReader(open(a.csv)))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    lines = [f"# rocprofv3 kernel statistics", f"# command: {a.cmd}", "",
+             f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'share':>7}  kernel"]
+    for r in rows:
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:9.2f} "
+                     f"{float(r['MinNs']) / 1e3:9.2f} {float(r['MaxNs']) / 1e3:9.2f} "
+                     f"{100 * float(r['TotalDurationNs']) / total:6.2f}%  {_short(r['Kernel_Name'] if 'Kernel_Name' in r else r['Name'])}")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    print(text)
+
+
+def _per_dispatch(path):
+    d = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"], int(r["Grid_Size"]))
+        d.setdefault(key, collections.Counter())[r["Counter_Name"]] += float(r["Counter_Value"])
+    return d
+
+
+def _kernel_value(d, counter, substr, grid):
+    vals = [c[counter] for (did, name, g), c in d.items()
+            if substr in name and (grid is None or g == grid)]
+    if not vals:
+        raise SystemExit(f"no dispatch of {substr!r} (grid {grid}) in the counter file")
+    return statistics.median(vals), len(vals)
+
+
+def _copy_value(d, counter):
+    vals = [c[counter] for (did, name, g), c in d.items() if "copy" in name.lower() or
+            "elementwise" in name.lower()]
+    return max(vals) if vals else None
+
+
+def cmd_traffic(a):
+    f = _per_dispatch(a.fetch)
+    w = _per_dispatch(a.write)
+    fk, nf = _kernel_value(f, "FETCH_SIZE", a.kernel, a.grid)
+    wk, nw = _kernel_value(w, "WRITE_SIZE", a.kernel, a.grid)
+    copy_bytes = a.copy_mib * 1024 * 1024
+    fc, wc = _copy_value(f, "FETCH_SIZE"), _copy_value(w, "WRITE_SIZE")
+    f_scale = copy_bytes / (fc * 1024) if fc else 1.0
+    w_scale = copy_bytes / (wc * 1024) if wc else 1.0
+    rec = {
+        "call": a.call, "kernel": a.kernel, "grid": a.grid,
+        "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": [nf, nw],
+        "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": fc, "write_kib": wc,
+                             "fetch_scale": f_scale, "write_scale": w_scale},
+        "traffic_bytes_per_launch": fk * 1024 * f_scale + wk * 1024 * w_scale,
+        "source_sha256": source_hash(),
+        "commands": {"fetch": a.cmd_fetch, "write": a.cmd_write},
+    }
+    text = json.dumps(rec, indent=1)
+    if a.out:
+        open(a.out, "w").write(text + "\n")
+    print(text)
+
+
+def cmd_mfma(a):
+    d = _per_dispatch(a.csv)
+    lines = [f"# rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CU_CYCLES",
+             f"# command: {a.cmd}",
+             "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)", "",
+             f"{'dispatches':>10} {'mfma_busy':>9}  kernel (grid)"]
+    agg = collections.defaultdict(list)
+    for (did, name, g), c in d.items():
+        if "GRBM_GUI_ACTIVE" not in c or c["GRBM_GUI_ACTIVE"] == 0:
+            continue
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        agg[(_short(name), g)].append(busy)
+    for (name, g), v in sorted(agg.items(), key=lambda kv: -statistics.median(kv[1])):
+        lines.append(f"{len(v):10d} {100 * statistics.median(v):8.1f}%  {name} ({g})")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    print(text)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--call", required=True, help="the bench.py call the kernel belongs to")
+    t.add_argument("--grid", type=int, default=None)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    t.add_argument("--out")
+    m = sub.add_parser("mfma")
+    m.add_argument("csv")
+    m.add_argument("--cmd", required=True)
+    m.add_argument("--out")
+    a = ap.parse_args()
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)
+
+
+if __name__ == "__main__":
+    main()
