@@ -20,5 +20,6 @@ from ._lib import (  # noqa: F401
     tp_linear_bwd_wgrad_workspace_size,
     tp_reduce_partials,
     tp_row_linear_fwd_partial,
+    tp_set_gemm_override,
     tp_status_string,
 )

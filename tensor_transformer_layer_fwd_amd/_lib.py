@@ -40,6 +40,7 @@ SIGNATURES = {
     "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "tp_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(ctypes.c_int),
                             ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
+    "tp_set_gemm_override": (_int, [_int, _int]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_hip_error": (_int, []),
 }
@@ -187,6 +188,12 @@ def tp_gemm_plan(M: int, N: int, K: int, allow_split: bool = False):
     _check("tp_gemm_plan", lib().tp_gemm_plan(M, N, K, int(bool(allow_split)), ctypes.byref(t),
                                                ctypes.byref(sk), ctypes.byref(kc)))
     return int(t.value), int(sk.value), int(kc.value)
+
+
+def tp_set_gemm_override(tile: int = 0, splitk: int = 1) -> None:
+    """Force a pipelined tile (and K slices for weight gradients) on every later
+    bf16 product whose shape it supports; tile 0 restores the library's choice."""
+    _check("tp_set_gemm_override", lib().tp_set_gemm_override(int(tile), int(splitk)))
 
 
 def tp_status_string(status: int) -> str:

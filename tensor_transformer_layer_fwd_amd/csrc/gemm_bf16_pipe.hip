@@ -10,7 +10,10 @@
 //     rows at one K offset fall in distinct banks.
 //   M/N-contiguous operand (the weight in NN, both operands in TN):
 //     BK x ROWS, one ROWS*2-byte row per K; 16-byte chunks are XOR-swizzled by
-//     4*(k mod 4). Fragments are read with ds_read_b64_tr_b16, which hands each
+//     4*(k mod 4) (ROWS = 128, 256) or rotated by 4*((k/2) mod 2) (ROWS = 192,
+//     whose 384-byte rows already put odd K rows half a bank cycle apart), so
+//     that the four K rows one transposed read touches hit disjoint banks.
+//     Fragments are read with ds_read_b64_tr_b16, which hands each
 //     lane four consecutive K-values of its own column: within a 16-lane group,
 //     lane i receives element i%4 of the 8-byte words read by lanes i/4,
 //     i/4+4, i/4+8 and i/4+12. Two such reads give the 8 K-values of a
@@ -21,8 +24,13 @@
 //
 // Each stage is a separate __shared__ object so the compiler can tell the
 // stages apart and does not wait for copies into other stages before reading
-// one. The steady-state loop issues one K-tile per step with no conditionals;
-// the last steps run in a guarded tail with conservative waits.
+// one. The block synchronises once per K-tile, just before the matrix cores
+// start on the tile's last 16-wide K step: by then every wave holds that
+// step's fragments in registers, so the tile's own stage can be refilled with
+// K-tile t+S at once, and the first fragments of K-tile t+1 are read while the
+// last MFMAs of tile t run. A wave therefore never waits on LDS between
+// K-tiles, and all S stages are in flight. The steady-state loop has no
+// conditionals; the last steps run in a guarded tail with conservative waits.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -101,42 +109,70 @@ __device__ __forceinline__ int kswz(int r) {
   else return (r >> 2) & 3;
 }
 
+// M/N-contiguous tiles: physical 16-byte chunk of logical chunk c in K row k,
+// and the inverse map.
+template <int ROWS>
+__device__ __forceinline__ int mn_phys(int k, int c) {
+  if constexpr (ROWS % 128 == 0) return c ^ (4 * (k & 3));
+  else return (c + 4 * ((k >> 1) & 1)) % (ROWS / 8);
+}
+template <int ROWS>
+__device__ __forceinline__ int mn_logical(int k, int pc) {
+  if constexpr (ROWS % 128 == 0) return pc ^ (4 * (k & 3));
+  else return (pc + ROWS / 8 - 4 * ((k >> 1) & 1)) % (ROWS / 8);
+}
+
 template <bool KC, int ROWS, int BK, int NW>
 struct Operand {
   static constexpr int BYTES = ROWS * BK * 2;
-  static constexpr int NI = BYTES / 1024 / NW;  // copy instructions per wave per tile
-  static_assert(NI >= 1 && NI * 1024 * NW == BYTES, "tile / waves mismatch");
-  static_assert(KC || ROWS % 128 == 0, "M/N-contiguous tiles need 16-chunk rows");
+  // A copy instruction fills one 1 KiB window of the tile. Window q*NW + w is
+  // copied by wave w; when the windows do not divide evenly among the waves,
+  // the first EXTRA waves copy one more.
+  static constexpr int NWIN = BYTES / 1024;
+  static constexpr int NB = NWIN / NW;
+  static constexpr int EXTRA = NWIN % NW;
+  static_assert(NB >= 1 && NWIN * 1024 == BYTES, "tile / waves mismatch");
+  static_assert(KC || ROWS % 128 == 0 || ROWS == 192, "M/N-contiguous tile rows");
   static_assert(BK == 32 || BK == 64, "K tile");
 
-  const uint16_t* ptr[NI];
+  const uint16_t* ptr[NB + (EXTRA > 0)];
   int64_t adv;  // elements between consecutive K-tiles
 
   // Tile origin (row r0 of M/N, k0 of K); ld = row stride of the operand in HBM.
   __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t r0, int64_t k0,
                                        int wave, int lane) {
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      const int byte = (wave * NI + q) * 1024 + lane * 16;
+    for (int q = 0; q < NB + (EXTRA > 0); ++q) {
+      // a wave without an extra window points its extra copy at window 0 (never issued)
+      const int win = q < NB ? q * NW + wave : (wave < EXTRA ? NB * NW + wave : 0);
+      const int byte = win * 1024 + lane * 16;
       if constexpr (KC) {
         const int r = byte / (BK * 2);
         const int c = ((byte % (BK * 2)) >> 4) ^ kswz<BK>(r);
         ptr[q] = base + (r0 + r) * ld + k0 + c * 8;
       } else {
         const int k = byte / (ROWS * 2);
-        const int c = ((byte % (ROWS * 2)) >> 4) ^ (4 * (k & 3));
+        const int c = mn_logical<ROWS>(k, (byte % (ROWS * 2)) >> 4);
         ptr[q] = base + (k0 + k) * ld + r0 + c * 8;
       }
     }
     adv = KC ? BK : BK * ld;
   }
 
-  // Copy the next K-tile into the stage at lds (this operand's part of it).
+  // Copy the next K-tile into the stage at lds (this operand's part of it):
+  // the windows every wave copies, and the extra one of waves below EXTRA
+  // (`extra` must be wave-uniform).
   __device__ __forceinline__ void issue(uint8_t* lds, int wave) {
 #pragma unroll
-    for (int q = 0; q < NI; ++q) {
-      copy16_to_lds(ptr[q], lds + (wave * NI + q) * 1024);
+    for (int q = 0; q < NB; ++q) {
+      copy16_to_lds(ptr[q], lds + (q * NW + wave) * 1024);
       ptr[q] += adv;
+    }
+  }
+  __device__ __forceinline__ void issue_extra(uint8_t* lds, int wave, bool extra) {
+    if constexpr (EXTRA > 0) {
+      if (extra) copy16_to_lds(ptr[NB], lds + (NB * NW + wave) * 1024);
+      ptr[NB] += adv;
     }
   }
 
@@ -156,8 +192,9 @@ struct Operand {
       const int g = lane >> 4, s = lane & 15;
       const int mn = R0 + 16 * (g & 1) + 4 * (s & 3);
       const int kb = ks * 16 + 8 * (g >> 1) + (s >> 2);
-      const int sw = 4 * (s >> 2);  // 4 * (k & 3)
-      const uint32_t a0 = lds_addr(lds) + kb * (ROWS * 2) + (((mn >> 3) ^ sw) << 4) + (mn & 7) * 2;
+      // K rows kb and kb+4 share the chunk permutation
+      const uint32_t a0 =
+          lds_addr(lds) + kb * (ROWS * 2) + (mn_phys<ROWS>(kb, mn >> 3) << 4) + (mn & 7) * 2;
       const uint32_t a1 = a0 + 4 * (ROWS * 2);
       s16x4_t lo, hi;
       asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
@@ -181,10 +218,14 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   using OA = Operand<AK, BM, BK, NW>;
   using OB = Operand<BKC, BN, BK, NW>;
   constexpr int SB = OA::BYTES + OB::BYTES;  // bytes per stage
-  constexpr int NIT = OA::NI + OB::NI;       // copies per wave per K-tile
+  // copies per wave per K-tile: NIT, plus one for each operand with an extra
+  // window for this wave
+  constexpr int NIT = OA::NB + OB::NB;
+  static_assert(OA::EXTRA == 0 || OB::EXTRA == 0, "extra windows in one operand only");
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int wm = wave / WN, wn = wave % WN;
 
   // ---- output tile (same XCD-aware order as the general kernel)
@@ -216,69 +257,131 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x16_t{};
 
+  constexpr int NX = OA::EXTRA + OB::EXTRA;  // waves 0..NX-1 copy NIT+1 windows per K-tile
+  const bool xw = wave < NX;
   auto issue = [&](auto stage_c) {
     constexpr int J = decltype(stage_c)::value;
     uint8_t* st = stage_buf<J, SB>();
     oa.issue(st, wave);
     ob.issue(st + OA::BYTES, wave);
   };
-  // One K-tile from one stage. Fragments of K-step ks+1 are read while the
-  // matrix cores work on K-step ks.
-  auto compute = [&](auto stage_c) {
+  auto issue_extra = [&](auto stage_c) {
+    constexpr int J = decltype(stage_c)::value;
+    uint8_t* st = stage_buf<J, SB>();
+    oa.issue_extra(st, wave, xw);
+    ob.issue_extra(st + OA::BYTES, wave, xw);
+  };
+  // Wait until at most T K-tiles of this wave's copies are in flight.
+  auto wait_tiles = [&](auto tiles_c) {
+    constexpr int T = decltype(tiles_c)::value;
+    if constexpr (NX == 0) {
+      wait_vmcnt<T * NIT>();
+    } else {
+      if (xw) wait_vmcnt<T*(NIT + 1)>();
+      else wait_vmcnt<T * NIT>();
+    }
+  };
+  auto wait_after = [&](int after) {
+    if (after >= 3) wait_tiles(std::integral_constant<int, 3>{});
+    else if (after == 2) wait_tiles(std::integral_constant<int, 2>{});
+    else if (after == 1) wait_tiles(std::integral_constant<int, 1>{});
+    else wait_vmcnt<0>();
+  };
+  constexpr int KS = BK / 16;  // 16-wide K steps per K-tile
+  bf16x8_t f[2][FM + FN];      // fragments of K step ks live in f[ks & 1]
+  auto read = [&](auto stage_c, int ks, bf16x8_t(&d)[FM + FN]) {
     constexpr int J = decltype(stage_c)::value;
     const uint8_t* sa = stage_buf<J, SB>();
     const uint8_t* sb = sa + OA::BYTES;
-    bf16x8_t f[2][FM + FN];
-    auto read = [&](int ks, bf16x8_t(&d)[FM + FN]) {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) d[i] = OA::frag(sa, wm * WTM + i * 32, ks, lane);
+    for (int i = 0; i < FM; ++i) d[i] = OA::frag(sa, wm * WTM + i * 32, ks, lane);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) d[FM + j] = OB::frag(sb, wn * WTN + j * 32, ks, lane);
-    };
-    read(0, f[0]);
-    lds_fence(f[0]);
+    for (int j = 0; j < FN; ++j) d[FM + j] = OB::frag(sb, wn * WTN + j * 32, ks, lane);
+  };
+  auto mfma = [&](const bf16x8_t(&d)[FM + FN]) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      if (ks + 1 < BK / 16) read(ks + 1, f[(ks + 1) & 1]);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d[i], d[FM + j], acc[i][j], 0, 0, 0);
+  };
+  // One K-tile from stage J; its first fragments are already in f[0]. Before
+  // the last K step, sync() synchronises the block (and issues the uneven
+  // extra window copies into stage J); then the first fragments of the next
+  // K-tile (stage J+1) are read and refill() reloads the rest of stage J while
+  // the last MFMAs run. Scheduling barriers keep each K step in the order:
+  // fragment reads for the next step, the MFMAs (with the tile copies of the
+  // last step spread between them), the wait for the reads. Left alone, the
+  // compiler sinks the reads to the end of the MFMAs, where their latency
+  // shows, and bunches the copies.
+  auto tile = [&](auto stage_c, auto&& sync, auto&& refill, bool has_next) {
+    constexpr int J = decltype(stage_c)::value;
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1][i], f[ks & 1][FM + j],
-                                                              acc[i][j], 0, 0, 0);
-      if (ks + 1 < BK / 16) lds_fence(f[(ks + 1) & 1]);
+    for (int ks = 0; ks + 1 < KS; ++ks) {
+      read(stage_c, ks + 1, f[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      mfma(f[ks & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_fence(f[(ks + 1) & 1]);
     }
+    if (has_next) {
+      sync();
+      read(std::integral_constant<int, (J + 1) % S>{}, 0, f[0]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    refill();
+    mfma(f[(KS - 1) & 1]);
+#pragma unroll
+    for (int q = 0; q < NIT; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // one copy
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (has_next) lds_fence(f[0]);
   };
 
-  // ---- prologue: K-tiles 0 .. S-2 into stages 0 .. S-2
-  Unroll<0, S - 1>::run([&](auto jc) {
-    if (decltype(jc)::value < nk) issue(jc);
+  // ---- prologue: K-tiles 0 .. S-1 into all stages, first fragments of tile 0
+  Unroll<0, S>::run([&](auto jc) {
+    if (decltype(jc)::value < nk) {
+      issue(jc);
+      issue_extra(jc);
+    }
   });
+  wait_after(min(S - 1, nk - 1));
+  block_sync();
+  read(std::integral_constant<int, 0>{}, 0, f[0]);
+  lds_fence(f[0]);
 
-  // ---- steady state: every step also prefetches K-tile it+S-1
+  // ---- steady state: K-tile t refills its own stage with K-tile t+S
   int it0 = 0;
-  for (; it0 + 2 * S - 1 <= nk; it0 += S) {
+  for (; it0 + 2 * S <= nk; it0 += S) {
     Unroll<0, S>::run([&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      wait_vmcnt<(S - 2) * NIT>();
-      block_sync();
-      issue(std::integral_constant<int, (J + S - 1) % S>{});
-      compute(jc);
+      tile(
+          jc,
+          [&] {
+            wait_tiles(std::integral_constant<int, S - 2>{});
+            block_sync();
+            issue_extra(jc);
+          },
+          [&] { issue(jc); }, true);
     });
   }
   // ---- tail
   for (; it0 < nk; it0 += S) {
     Unroll<0, S>::run([&](auto jc) {
-      constexpr int J = decltype(jc)::value;
-      const int it = it0 + J;
-      if (it < nk) {
-        const int after = min(S - 2, nk - 1 - it);  // K-tiles issued after this one
-        if (after >= 2) wait_vmcnt<2 * NIT>();
-        else if (after == 1) wait_vmcnt<NIT>();
-        else wait_vmcnt<0>();
-        block_sync();
-        if (it + S - 1 < nk) issue(std::integral_constant<int, (J + S - 1) % S>{});
-        compute(jc);
+      const int t = it0 + decltype(jc)::value;
+      if (t < nk) {
+        tile(
+            jc,
+            [&] {
+              wait_after(min(S - 2, nk - 2 - t));  // K-tiles issued after tile t+1
+              block_sync();
+              if (t + S < nk) issue_extra(jc);
+            },
+            [&] {
+              if (t + S < nk) issue(jc);
+            },
+            t + 1 < nk);
       }
     });
   }
@@ -289,45 +392,53 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   // For each 32-row band of its wave tile a wave writes the accumulators to
   // LDS in the 32x32 MFMA layout (lane holds column lane & 31; register r holds
   // row 8*(r/4) + 4*(lane/32) + r%4) and reads them back as 8 consecutive
-  // columns per lane, which it finishes with 16-byte stores. A lane's columns
-  // are the same in every pass, so the bias is loaded once; the saved
-  // pre-activation U of the whole wave tile is loaded before the first store.
-  // (On gfx9 loads and stores share one counter: a load issued after stores
-  // could only be waited for together with them.)
+  // columns per lane, which it finishes with 16-byte stores. The wave tile's
+  // columns go in chunks of up to 64: a 64-wide chunk is 8 lanes wide and 8
+  // rows deep per pass, a 32-wide one 4 lanes wide and 16 rows deep. A lane's
+  // columns are the same in every band, so the bias is loaded once; the saved
+  // pre-activation U of band i+1 is loaded before the stores of band i (on
+  // gfx9 loads and stores share one counter: a load issued after stores could
+  // only be waited for together with them).
   constexpr int EP = WTN + 4;
   constexpr int REGION = 32 * EP * 4;
   constexpr int WPS = SB / REGION;  // wave regions per stage
   static_assert(WPS >= 1 && WPS * S >= NW, "epilogue LDS");
-  constexpr int VPR = WTN / 8;      // 8-column vectors per tile row
-  static_assert(64 % VPR == 0 && WTN <= 64, "epilogue lanes / registers");
-  constexpr int RPP = 64 / VPR;     // tile rows per pass
-  constexpr int PASSES = 32 / RPP;
+  constexpr int NCH = (WTN + 63) / 64;  // column chunks
+  constexpr int NPB = WTN / 16;         // passes per band, all chunks
   const int ws_idx = wave / WPS;
   uint8_t* base = ws_idx == 0 ? stage_buf<0, SB>()
                 : ws_idx == 1 ? stage_buf<1, SB>()
                 : ws_idx == 2 ? stage_buf<2, SB>()
                               : stage_buf<(S > 3 ? 3 : 2), SB>();
   const float* ep = reinterpret_cast<const float*>(base + (wave % WPS) * REGION);
-  const int lr0 = lane / VPR, ec = (lane % VPR) * 8;
-  const int64_t col = n0 + wn * WTN + ec;
-  const int64_t row0 = m0 + wm * WTM + lr0;
+  const int64_t col0 = n0 + wn * WTN;
+  const int64_t rowt = m0 + wm * WTM;
+  // chunk C = P / 4 of pass P: width, lanes per row, rows per pass, lane offsets
+  auto chunk_w = [](int C) { return WTN - 64 * C < 64 ? WTN - 64 * C : 64; };
   // fp32 output: C, or this K slice's partial sums (row stride N) when split
   float* const cf = EK == kEpiF32 ? (p.splitk > 1 ? p.ws + static_cast<int64_t>(z) * p.M * p.N
                                                    : static_cast<float*>(p.c))
                                   : nullptr;
   const int64_t ldc = (EK == kEpiF32 && p.splitk > 1) ? p.N : p.ldc;
 
-  float bias8[8];
+  float bias8[NCH][8];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) bias8[q] = 0.0f;
-  if (EK == kEpiBiasGelu && p.bias) load8_bf16(p.bias, col, bias8);
-  // U of band i+1 is loaded before the stores of band i (two register sets)
-  u32x4_t upre[2][PASSES];
+  for (int C = 0; C < NCH; ++C) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) bias8[C][q] = 0.0f;
+    const int vpr = chunk_w(C) / 8;
+    if (EK == kEpiBiasGelu && p.bias) load8_bf16(p.bias, col0 + 64 * C + (lane % vpr) * 8, bias8[C]);
+  }
+  u32x4_t upre[2][NPB];
   const uint16_t* Ug = static_cast<const uint16_t*>(p.u);
-  auto load_u = [&](int i, u32x4_t(&d)[PASSES]) {
+  auto load_u = [&](int i, u32x4_t(&d)[NPB]) {
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps)
-      d[ps] = *reinterpret_cast<const u32x4_t*>(Ug + (row0 + i * 32 + ps * RPP) * p.ldu + col);
+    for (int P = 0; P < NPB; ++P) {
+      const int C = P >> 2, ps = P & 3;
+      const int vpr = chunk_w(C) / 8, rpp = 64 / vpr;
+      const int64_t row = rowt + i * 32 + lane / vpr + ps * rpp;
+      d[P] = *reinterpret_cast<const u32x4_t*>(Ug + row * p.ldu + col0 + 64 * C + (lane % vpr) * 8);
+    }
   };
   if (EK == kEpiDGelu) load_u(0, upre[0]);
 
@@ -337,9 +448,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   // otherwise guard them against the earlier copies into the same buffers with
   // a full vector-memory wait, which also waits for the stores of the previous
   // pass.
-  const uint32_t ep_w = lds_addr(reinterpret_cast<const uint8_t*>(ep)) +
-                        (4 * (lane >> 5) * EP + (lane & 31)) * 4;
-  const uint32_t ep_r = lds_addr(reinterpret_cast<const uint8_t*>(ep)) + (lr0 * EP + ec) * 4;
+  const uint32_t ep_lds = lds_addr(reinterpret_cast<const uint8_t*>(ep));
+  const uint32_t ep_w = ep_lds + (4 * (lane >> 5) * EP + (lane & 31)) * 4;
   Unroll<0, FM>::run([&](auto band) {
     constexpr int i = decltype(band)::value;
 #pragma unroll
@@ -351,13 +461,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
       }
     if (EK == kEpiDGelu && i + 1 < FM) load_u(i + 1, upre[(i + 1) & 1]);
 #pragma unroll
-    for (int ps = 0; ps < PASSES; ++ps) {
-      const uint32_t a = ep_r + ps * RPP * EP * 4;
+    for (int P = 0; P < NPB; ++P) {
+      const int C = P >> 2, ps = P & 3;
+      const int vpr = chunk_w(C) / 8, rpp = 64 / vpr;
+      const int lr = lane / vpr + ps * rpp, ec = 64 * C + (lane % vpr) * 8;
+      const uint32_t a = ep_lds + (lr * EP + ec) * 4;
       f32x4_t lo, hi;
       asm volatile("ds_read_b128 %0, %1" : "=v"(lo) : "v"(a) : "memory");
       asm volatile("ds_read_b128 %0, %1" : "=v"(hi) : "v"(a + 16) : "memory");
       asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(lo), "+v"(hi)::"memory");
-      const int64_t row = row0 + i * 32 + ps * RPP;
+      const int64_t row = rowt + i * 32 + lr;
+      const int64_t col = col0 + ec;
       if constexpr (EK == kEpiF32) {
         float* d = cf + row * ldc + col;
         *reinterpret_cast<f32x4_t*>(d) = lo;
@@ -372,12 +486,12 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
         const int64_t o = row * p.ldc + col;
         if constexpr (EK == kEpiBiasGelu) {
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] += bias8[q];
+          for (int q = 0; q < 8; ++q) v[q] += bias8[C][q];
           store8(p.c2, o, v, 1);
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] = gelu_tanh(v[q]);
         } else if constexpr (EK == kEpiDGelu) {
-          const u32x4_t w = upre[i & 1][ps];
+          const u32x4_t w = upre[i & 1][P];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             v[2 * q] *= gelu_tanh_grad(__uint_as_float(w[q] << 16));
@@ -432,6 +546,8 @@ hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, int ek
       return launch_pipe_cfg<128, 256, 2, 4, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     case kPipe128x128:
       return launch_pipe_cfg<128, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
+    case kPipe256x192:
+      return launch_pipe_cfg<256, 192, 4, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -80,6 +80,7 @@ enum TileId : int {
   kPipe256x128 = 11,  // 4 waves, 128x64 per wave
   kPipe128x256 = 12,  // 8 waves, 64x64 per wave
   kPipe128x128 = 13,  // 4 waves, 64x64 per wave
+  kPipe256x192 = 14,  // 8 waves, 64x96 per wave
 };
 
 // Tile and split-K choice. It depends on the shape only, so the workspace-size
@@ -91,6 +92,8 @@ struct SplitPlan {
 };
 
 SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split);
+// Forced tile / split for later plans (tile 0: none); false for invalid values.
+bool set_gemm_override(int tile, int splitk);
 size_t colsum_workspace_bytes(int64_t T, int64_t N);
 
 // Launch per plan: the planned pipelined tile when the operands allow it,

@@ -3,8 +3,9 @@
 // The cost model counts rounds of tiles over the 256 CUs; a round costs a
 // fixed overhead (prologue, epilogue, launch) plus the tile's matrix work at a
 // per-CU rate measured for each tile configuration on MI355X (the clock runs
-// at 1.7-2.2 GHz under matrix load, below the 2.4 GHz peak). A split K adds the
-// HBM time of the fp32 partials and one fix-up launch.
+// at 1.8-2.2 GHz under matrix load, below the 2.4 GHz peak). A split K adds the
+// HBM time of the fp32 partials (written, then read by the fix-up) and one
+// fix-up launch.
 #include <hip/hip_runtime.h>
 
 #include "internal.h"
@@ -23,10 +24,11 @@ struct PipeTile {
   double flop_per_sec_per_cu;
 };
 constexpr PipeTile kPipeTiles[] = {
-    {kPipe256x256, 256, 256, 5.3e12},
-    {kPipe256x128, 256, 128, 4.6e12},
-    {kPipe128x256, 128, 256, 5.0e12},
+    {kPipe256x256, 256, 256, 5.0e12},
+    {kPipe256x128, 256, 128, 4.4e12},
+    {kPipe128x256, 128, 256, 4.6e12},
     {kPipe128x128, 128, 128, 4.0e12},
+    {kPipe256x192, 256, 192, 4.6e12},
 };
 
 double cost(int64_t M, int64_t N, int64_t K, const PipeTile& t, int split) {
@@ -34,13 +36,45 @@ double cost(int64_t M, int64_t N, int64_t K, const PipeTile& t, int split) {
   const int64_t rounds = (tiles + kCUs - 1) / kCUs;
   const double flops = 2.0 * t.bm * t.bn * static_cast<double>(K / split);
   double c = static_cast<double>(rounds) * (kRoundOverheadSec + flops / t.flop_per_sec_per_cu);
-  if (split > 1) c += (split + 1.0) * M * N * 4.0 / kHbmBytesPerSec + kLaunchSec;
+  // the slices write their partials and the fix-up reads them back
+  if (split > 1) c += (2.0 * split + 1.0) * M * N * 4.0 / kHbmBytesPerSec + kLaunchSec;
   return c;
 }
 
+int g_force_tile = 0;
+int g_force_split = 1;
+
+const PipeTile* find_tile(int id) {
+  for (const PipeTile& t : kPipeTiles)
+    if (t.id == id) return &t;
+  return nullptr;
+}
+
+SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split);
+
 }  // namespace
 
+bool set_gemm_override(int tile, int splitk) {
+  if ((tile != 0 && !find_tile(tile)) || splitk < 1 || splitk > 16) return false;
+  g_force_tile = tile;
+  g_force_split = splitk;
+  return true;
+}
+
 SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
+  SplitPlan plan = plan_model(M, N, K, allow_split);
+  const PipeTile* t = find_tile(g_force_tile);
+  if (t && K % 64 == 0 && M % t->bm == 0 && N % t->bn == 0) {
+    plan = SplitPlan{t->id, 1, K};
+    const int s = g_force_split;
+    if (allow_split && s > 1 && K % (64 * s) == 0) plan = SplitPlan{t->id, s, K / s};
+  }
+  return plan;
+}
+
+namespace {
+
+SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
   SplitPlan best{kGeneral128x128, 1, K};
   double best_t = 1e30;
   static const int kSplits[] = {1, 2, 3, 4, 6, 8};
@@ -72,6 +106,8 @@ SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split) {
   }
   return best;
 }
+
+}  // namespace
 
 hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
   const bool aligned = (reinterpret_cast<uintptr_t>(p.a) & 15) == 0 && (p.lda & 7) == 0 &&

@@ -246,6 +246,10 @@ int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, in
   return TP_OK;
 }
 
+int tp_set_gemm_override(int tile, int splitk) {
+  return set_gemm_override(tile, splitk) ? TP_OK : TP_ERR_SHAPE;
+}
+
 const char* tp_status_string(int status) {
   switch (status) {
     case TP_OK:

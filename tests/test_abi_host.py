@@ -124,7 +124,7 @@ def test_gemm_plan_query(lib):
     for M, N, K in [(4096, 1536, 768), (4096, 768, 1536), (2048, 6144, 12288),
                     (2048, 12288, 6144), (6144, 1024, 256)]:
         tile, sk, kc = L.tp_gemm_plan(M, N, K)
-        assert tile in (10, 11, 12, 13) and sk == 1 and kc == K
+        assert tile in (10, 11, 12, 13, 14) and sk == 1 and kc == K
     tile, sk, kc = L.tp_gemm_plan(768, 1536, 4096, allow_split=True)
     assert tile >= 10 and sk >= 1 and kc * sk == 4096 and kc % 64 == 0
     # ragged shapes use the general kernel
@@ -137,3 +137,27 @@ def test_gemm_plan_query(lib):
         assert ws >= (sk * M * N * 4 if sk > 1 else 0)
         assert L.tp_gemm_plan(M, N, K, allow_split=False)[1] == 1
     assert lib.tp_gemm_plan(0, 5, 5, 0, None, None, None) == -2
+
+
+def test_gemm_override(lib):
+    """The tuning hook forces a tile where the shape allows it, splits only
+    weight gradients, changes the workspace query with the plan and resets."""
+    try:
+        L.tp_set_gemm_override(14, 4)
+        assert L.tp_gemm_plan(1024, 384, 4096) == (14, 1, 4096)
+        assert L.tp_gemm_plan(1024, 384, 4096, allow_split=True) == (14, 4, 1024)
+        assert L.tp_linear_bwd_wgrad_workspace_size(4096, 1024, 384, L.TP_BF16) >= 4 * 1024 * 384 * 4
+        # N not a multiple of 192: the planner's own choice
+        L.tp_set_gemm_override(0)
+        own = L.tp_gemm_plan(1024, 512, 4096, allow_split=True)
+        L.tp_set_gemm_override(14, 4)
+        assert L.tp_gemm_plan(1024, 512, 4096, allow_split=True) == own
+        # split that does not divide K into multiples of 64: one slice
+        L.tp_set_gemm_override(10, 3)
+        assert L.tp_gemm_plan(512, 512, 1024, allow_split=True) == (10, 1, 1024)
+        assert lib.tp_set_gemm_override(7, 1) == -2
+        assert lib.tp_set_gemm_override(10, 0) == -2
+        assert lib.tp_set_gemm_override(10, 17) == -2
+    finally:
+        L.tp_set_gemm_override(0)
+    assert L.tp_gemm_plan(1024, 512, 4096, allow_split=True) == own

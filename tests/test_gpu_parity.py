@@ -446,32 +446,39 @@ def test_determinism_and_graph_replay(dev):
 # --------------------------------------------------------------------------- #
 # every pipelined tile configuration, in every operand layout                  #
 # --------------------------------------------------------------------------- #
-_CAND = sorted(((M, N, K) for M in (128, 256, 384, 512, 768, 1024, 1536, 2048, 4096)
-                for N in (128, 256, 384, 512, 768, 1024, 1536, 2048, 4096)
-                for K in (256, 512, 1024, 2048, 4096)), key=lambda s: s[0] * s[1] * s[2])
+_TILE_MN = {10: (256, 256), 11: (256, 128), 12: (128, 256), 13: (128, 128), 14: (256, 192)}
 
 
-def _shape_for(tile, allow_split, want_split):
-    from tensor_transformer_layer_fwd_amd import _lib as L
-    for M, N, K in _CAND:
-        t, sk, _ = L.tp_gemm_plan(M, N, K, allow_split)
-        if t == tile and (sk > 1) == want_split:
-            return M, N, K
-    return None
-
-
-@pytest.mark.parametrize("tile", [10, 11, 12, 13])
+@pytest.mark.parametrize("tile", sorted(_TILE_MN))
 @pytest.mark.parametrize("op", ["fwd_gelu", "row_partial", "dgrad_gelu", "dgrad_f32", "wgrad",
                                 "wgrad_split"])
-def test_pipelined_tiles(dev, tile, op):
+@pytest.mark.parametrize("kt", [2, 18])
+def test_pipelined_tiles(dev, tile, op, kt):
+    """Each pipelined tile forced on a grid of 8 tiles (XCD remap path), with
+    kt 32-wide K-tiles per block: 2 runs only the guarded tail, 18 the
+    steady-state loop and a 6-tile tail. The split case uses 3 K slices."""
     import tensor_transformer_layer_fwd_amd as tp
     from tensor_transformer_layer_fwd_amd import _lib as L
     split = op == "wgrad_split"
-    shape = _shape_for(tile, op.startswith("wgrad"), split)
-    if shape is None:
-        pytest.skip(f"no candidate shape plans to tile {tile} for {op}")
-    M, N, K = shape
+    bm, bn = _TILE_MN[tile]
+    M, N, K = 4 * bm, 2 * bn, 32 * kt * (3 if split else 1)
+    tp.tp_set_gemm_override(tile, 3 if split else 1)
+    try:
+        plan = L.tp_gemm_plan(M, N, K, op.startswith("wgrad"))
+    finally:
+        tp.tp_set_gemm_override(0)
+    assert plan[0] == tile and (plan[1] == 3) == split, plan
     _say(f"pipelined tile={tile} op={op} M={M} N={N} K={K}")
+    tp.tp_set_gemm_override(tile, 3 if split else 1)
+    try:
+        _run_tile_op(dev, tile, op, M, N, K)
+    finally:
+        tp.tp_set_gemm_override(0)
+
+
+def _run_tile_op(dev, tile, op, M, N, K):
+    import tensor_transformer_layer_fwd_amd as tp
+    from tensor_transformer_layer_fwd_amd import _lib as L
     rng = np.random.default_rng(tile * 100 + len(op))
     dt = "bf16"
     if op in ("fwd_gelu", "row_partial"):
