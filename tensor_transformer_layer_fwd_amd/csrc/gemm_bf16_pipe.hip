@@ -79,7 +79,6 @@ __device__ __forceinline__ void lds_fence(bf16x8_t (&f)[NF]) {
 #pragma unroll
   for (int i = 0; i < NF; ++i) asm volatile("" : "+v"(f[i]));
 }
-
 __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -214,7 +213,7 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "tile");
-  static_assert(S >= 3 && S <= 4, "stages");
+  static_assert(S >= 3 && S <= 8, "stages");
   using OA = Operand<AK, BM, BK, NW>;
   using OB = Operand<BKC, BN, BK, NW>;
   constexpr int SB = OA::BYTES + OB::BYTES;  // bytes per stage
@@ -281,11 +280,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
       else wait_vmcnt<T * NIT>();
     }
   };
-  auto wait_after = [&](int after) {
-    if (after >= 3) wait_tiles(std::integral_constant<int, 3>{});
-    else if (after == 2) wait_tiles(std::integral_constant<int, 2>{});
-    else if (after == 1) wait_tiles(std::integral_constant<int, 1>{});
-    else wait_vmcnt<0>();
+  auto wait_after = [&](int after) {  // 0 <= after < S
+    Unroll<0, S>::run([&](auto c) {
+      if (after == decltype(c)::value) wait_tiles(c);
+    });
   };
   constexpr int KS = BK / 16;  // 16-wide K steps per K-tile
   bf16x8_t f[2][FM + FN];      // fragments of K step ks live in f[ks & 1]
@@ -406,10 +404,10 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   constexpr int NCH = (WTN + 63) / 64;  // column chunks
   constexpr int NPB = WTN / 16;         // passes per band, all chunks
   const int ws_idx = wave / WPS;
-  uint8_t* base = ws_idx == 0 ? stage_buf<0, SB>()
-                : ws_idx == 1 ? stage_buf<1, SB>()
-                : ws_idx == 2 ? stage_buf<2, SB>()
-                              : stage_buf<(S > 3 ? 3 : 2), SB>();
+  uint8_t* base = stage_buf<0, SB>();
+  Unroll<1, S>::run([&](auto c) {
+    if (ws_idx == decltype(c)::value) base = stage_buf<decltype(c)::value, SB>();
+  });
   const float* ep = reinterpret_cast<const float*>(base + (wave % WPS) * REGION);
   const int64_t col0 = n0 + wn * WTN;
   const int64_t rowt = m0 + wm * WTM;
@@ -535,17 +533,24 @@ hipError_t launch_pipe_cfg(const GemmParams& p, int splitk, int ek, hipStream_t 
   return hipGetLastError();
 }
 
+// Tile configurations. With both operands K-contiguous a 32-wide K-tile is
+// copied as 64-byte row pieces, half a 128-byte line each, which the vector
+// memory path moves at about two thirds of its rate for whole lines; there the
+// 128-row tiles take 64-wide K-tiles (three stages fit in LDS).
 template <bool AK, bool BKC>
 hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, int ek, hipStream_t s) {
+  constexpr bool kNT = AK && BKC;
   switch (plan.tile) {
     case kPipe256x256:
       return launch_pipe_cfg<256, 256, 2, 4, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     case kPipe256x128:
       return launch_pipe_cfg<256, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     case kPipe128x256:
-      return launch_pipe_cfg<128, 256, 2, 4, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
+      return launch_pipe_cfg<128, 256, 2, 4, kNT ? 64 : 32, kNT ? 3 : 4, AK, BKC>(p, plan.splitk, ek,
+                                                                                 s);
     case kPipe128x128:
-      return launch_pipe_cfg<128, 128, 2, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
+      return launch_pipe_cfg<128, 128, 2, 2, kNT ? 64 : 32, kNT ? 3 : 4, AK, BKC>(p, plan.splitk, ek,
+                                                                                 s);
     case kPipe256x192:
       return launch_pipe_cfg<256, 192, 4, 2, 32, 4, AK, BKC>(p, plan.splitk, ek, s);
     default:
