@@ -6,6 +6,7 @@
 //   - a standalone bias + activation pass.
 #include <hip/hip_runtime.h>
 
+#include "colsum_device.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -77,64 +78,40 @@ __global__ __launch_bounds__(256) void colsum_pass1_kernel(ColsumParams p, int n
   }
 }
 
-// Pass 1, vector path (N a multiple of 8, 16-byte aligned rows): block (cb,
-// chunk) covers 256 columns; thread (cv, rl) loads 8 columns (16 bytes of
-// bf16, or 32 of fp32) of rows rl, rl+8, .., all loads independent, and the
-// 8 row lanes are added in order through LDS.
+// Pass 1, vector path: one unit (column block, row chunk) per block.
 __global__ __launch_bounds__(256) void colsum_vec_pass1_kernel(ColsumParams p, int nchunks) {
   __shared__ float part[8][256];
-  const int cv = threadIdx.x & 31, rl = threadIdx.x >> 5;
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * 256 + cv * 8;
-  const int64_t t0 = static_cast<int64_t>(blockIdx.y) * kColsumRows;
-  float s[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) s[q] = 0.0f;
-  if (c0 < p.N) {
-#pragma unroll
-    for (int j = 0; j < kColsumRows / 8; ++j) {
-      const int64_t t = t0 + rl + 8 * j;
-      if (t < p.T) {
-        float v[8];
-        if (p.src_bf16)
-          load8_bf16(p.src, t * p.ld + c0, v);
-        else
-          load8_f32(p.src, t * p.ld + c0, v);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) s[q] += v[q];
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) part[rl][cv * 8 + q] = s[q];
-  __syncthreads();
-  const int64_t cc = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (cc < p.N) {
-    float v = part[0][threadIdx.x];
-#pragma unroll
-    for (int r = 1; r < 8; ++r) v += part[r][threadIdx.x];
-    if (nchunks == 1)
-      p.dbias[cc] = p.accumulate ? p.dbias[cc] + v : v;
-    else
-      p.ws[static_cast<int64_t>(blockIdx.y) * p.N + cc] = v;
-  }
+  colsum_vec_unit(p, blockIdx.x, blockIdx.y, nchunks, part);
 }
 
-// Pass 2: dbias[c] (+)= sum over chunks. Each column's chunks are split over 4
-// threads (chunks i, i+4, ...; loads independent) whose sums are added in order.
+// Pass 2: one unit of 64 columns per block.
 __global__ __launch_bounds__(256) void colsum_pass2_kernel(ColsumParams p, int nchunks) {
   __shared__ float part[4][64];
-  const int cl = threadIdx.x & 63, pr = threadIdx.x >> 6;
-  const int64_t c = static_cast<int64_t>(blockIdx.x) * 64 + cl;
-  float s = 0.0f;
-  if (c < p.N) {
-#pragma unroll 16
-    for (int i = pr; i < nchunks; i += 4) s += p.ws[static_cast<int64_t>(i) * p.N + c];
+  colsum_pass2_unit(p, blockIdx.x, nchunks, part);
+}
+
+// Split-K fix-up (vector path) and column-sum pass 2 in one launch: blocks
+// below nfix run the fix-up, the rest one pass-2 unit each.
+__global__ __launch_bounds__(256) void splitk_fixup_colsum_kernel(GemmParams p, int nfix,
+                                                                  int nchunks) {
+  __shared__ float part[4][64];
+  if (static_cast<int>(blockIdx.x) >= nfix) {
+    colsum_pass2_unit(p.cs, blockIdx.x - nfix, nchunks, part);
+    return;
   }
-  part[pr][cl] = s;
-  __syncthreads();
-  if (threadIdx.x < 64 && c < p.N) {
-    const float v = ((part[0][cl] + part[1][cl]) + part[2][cl]) + part[3][cl];
-    p.dbias[c] = p.accumulate ? p.dbias[c] + v : v;
+  const int64_t nq = p.N >> 2;
+  const int64_t total = p.M * nq;
+  const int64_t slice = p.M * p.N;
+  const int64_t stride = static_cast<int64_t>(nfix) * blockDim.x;
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += stride) {
+    const int64_t row = e / nq, col = (e - row * nq) << 2;
+    const float* w = p.ws + row * p.N + col;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(w);
+    for (int z = 1; z < p.splitk; ++z) v += *reinterpret_cast<const f32x4_t*>(w + z * slice);
+    float* c = static_cast<float*>(p.c) + row * p.ldc + col;
+    if (p.accumulate) v += *reinterpret_cast<const f32x4_t*>(c);
+    *reinterpret_cast<f32x4_t*>(c) = v;
   }
 }
 
@@ -242,19 +219,41 @@ hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s) {
   const bool vec = !p.out_bf16 && p.epi == EPI_STORE && p.N % 4 == 0 && p.ldc % 4 == 0 &&
                    (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(p.ws) & 15) == 0;
+  // column sums carried by the GEMM launch: pass 2 rides along here
+  const bool pass2 = p.cs_blocks > 0 && p.cs_nchunks > 1;
+  if (vec && pass2) {
+    const unsigned nfix = grid_for(p.M * p.N / 4, 256);
+    const unsigned ncs = static_cast<unsigned>((p.cs.N + 63) / 64);
+    hipLaunchKernelGGL(splitk_fixup_colsum_kernel, dim3(nfix + ncs), dim3(256), 0, s, p,
+                       static_cast<int>(nfix), p.cs_nchunks);
+    return hipGetLastError();
+  }
   if (vec)
     hipLaunchKernelGGL(splitk_fixup_vec4_kernel, dim3(grid_for(p.M * p.N / 4, 256)), dim3(256), 0,
                        s, p);
   else
     hipLaunchKernelGGL(splitk_fixup_kernel, dim3(grid_for(p.M * p.N, 256)), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !pass2) return e;
+  return launch_colsum_pass2(p.cs, p.cs_nchunks, s);
+}
+
+int64_t colsum_chunks(const ColsumParams& p) { return (p.T + kColsumRows - 1) / kColsumRows; }
+
+bool colsum_vec_ok(const ColsumParams& p) {
+  return p.N % 8 == 0 && p.ld % 8 == 0 && (reinterpret_cast<uintptr_t>(p.src) & 15) == 0;
+}
+
+hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s) {
+  hipLaunchKernelGGL(colsum_pass2_kernel, dim3(static_cast<unsigned>((p.N + 63) / 64)), dim3(256),
+                     0, s, p, nchunks);
   return hipGetLastError();
 }
 
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s) {
-  const int64_t nchunks = (p.T + kColsumRows - 1) / kColsumRows;
+  const int64_t nchunks = colsum_chunks(p);
   if (nchunks > 65535) return hipErrorInvalidConfiguration;
-  const bool vec = p.N % 8 == 0 && p.ld % 8 == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.src) & 15) == 0;
+  const bool vec = colsum_vec_ok(p);
   if (vec)
     hipLaunchKernelGGL(colsum_vec_pass1_kernel,
                        dim3(static_cast<unsigned>((p.N + 255) / 256), static_cast<unsigned>(nchunks)),
@@ -265,9 +264,7 @@ hipError_t launch_colsum(const ColsumParams& p, hipStream_t s) {
                        dim3(256), 0, s, p, static_cast<int>(nchunks));
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || nchunks == 1) return e;
-  hipLaunchKernelGGL(colsum_pass2_kernel, dim3(static_cast<unsigned>((p.N + 63) / 64)),
-                     dim3(256), 0, s, p, static_cast<int>(nchunks));
-  return hipGetLastError();
+  return launch_colsum_pass2(p, static_cast<int>(nchunks), s);
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {

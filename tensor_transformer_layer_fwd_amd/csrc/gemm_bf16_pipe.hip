@@ -35,6 +35,7 @@
 
 #include <type_traits>
 
+#include "colsum_device.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -231,7 +232,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   const int tiles_m = static_cast<int>(p.M / BM);
   const int tiles_n = static_cast<int>(p.N / BN);
   const int ntiles = tiles_m * tiles_n;
-  int bid = blockIdx.x;
+  // One block per (K slice z, tile) in a 1-D grid, slice-major; blocks past
+  // the last slice's tiles run column-sum pass-1 units.
+  const int z = static_cast<int>(blockIdx.x) / ntiles;
+  if constexpr (EK == kEpiF32) {
+    if (z >= p.splitk) {
+      const int e = blockIdx.x - p.splitk * ntiles, ncb = static_cast<int>((p.cs.N + 255) / 256);
+      float(*part)[256] = reinterpret_cast<float(*)[256]>(stage_buf<0, SB>());
+      for (int u = e; u < p.cs_units; u += p.cs_blocks)
+        colsum_vec_unit(p.cs, u % ncb, u / ncb, p.cs_nchunks, part);
+      return;
+    }
+  }
+  int bid = static_cast<int>(blockIdx.x) - z * ntiles;
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   constexpr int G = 8;
   const int group = bid / (G * tiles_n);
@@ -241,7 +254,6 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   const int64_t m0 = static_cast<int64_t>(first_m + in_group % gs) * BM;
   const int64_t n0 = static_cast<int64_t>(in_group / gs) * BN;
 
-  const int z = blockIdx.y;
   const int64_t kbeg = static_cast<int64_t>(z) * p.k_chunk;
   const int nk = static_cast<int>((min(p.K, kbeg + p.k_chunk) - kbeg) / BK);
 
@@ -505,12 +517,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC>
 hipError_t launch_pipe_cfg(const GemmParams& p, int splitk, int ek, hipStream_t s) {
   const int64_t tiles = (p.M / BM) * (p.N / BN);
-  const dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(splitk));
+  const dim3 grid(static_cast<unsigned>(tiles * splitk));
   const dim3 block(WM * WN * 64);
   switch (ek) {
     case kEpiF32:
-      hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiF32>), grid,
-                         block, 0, s, p);
+      // column-sum blocks (if any) come last in dispatch order
+      hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiF32>),
+                         dim3(grid.x + p.cs_blocks), block, 0, s, p);
       break;
     case kEpiBF16:
       if constexpr (AK)

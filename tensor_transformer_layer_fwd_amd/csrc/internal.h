@@ -15,6 +15,18 @@ enum Epilogue : int {
 
 enum Act : int { ACT_NONE = 0, ACT_GELU = 1 };
 
+// Column-sum (bias gradient) request: dbias[n] (+)= sum_t src[t, n].
+struct ColsumParams {
+  const void* src;
+  int64_t T, N, ld;
+  int src_bf16;
+  float* dbias;
+  int accumulate;
+  float* ws;  // partial sums [nchunks, N]
+};
+
+constexpr int kColsumRows = 64;  // rows summed per block in the first pass
+
 // One GEMM C[M,N] = op(A)[M,K] * op(B)[K,N] with a fused epilogue.
 //   a_kcontig: A stored [M,K] (true) or [K,M] (false), row stride lda
 //   b_kcontig: B stored [N,K] (true) or [K,N] (false), row stride ldb
@@ -37,19 +49,14 @@ struct GemmParams {
   int64_t k_chunk;
   float* ws;
   int a_kcontig, b_kcontig;
+  // Column sums carried by this launch (weight gradients on the pipelined
+  // kernel, fp32 epilogue): cs_blocks extra blocks after all tiles run the
+  // cs_units pass-1 units of cs (cs_nchunks row chunks); the fix-up launch
+  // then runs pass 2. cs_blocks = 0: none.
+  ColsumParams cs;
+  int cs_blocks, cs_units, cs_nchunks;
 };
 
-// Column-sum (bias gradient) request: dbias[n] (+)= sum_t src[t, n].
-struct ColsumParams {
-  const void* src;
-  int64_t T, N, ld;
-  int src_bf16;
-  float* dbias;
-  int accumulate;
-  float* ws;  // partial sums [nchunks, N]
-};
-
-constexpr int kColsumRows = 64;  // rows summed per block in the first pass
 
 // Reduction over shards.
 constexpr int kMaxPartials = 16;
@@ -99,6 +106,8 @@ size_t colsum_workspace_bytes(int64_t T, int64_t N);
 // Launch per plan: the planned pipelined tile when the operands allow it,
 // otherwise the general kernel with the same split.
 hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
+// Whether launch_gemm_bf16 will run the pipelined kernel, and with which epilogue kind.
+int gemm_pipe_epilogue(const GemmParams& p, const SplitPlan& plan);  // kEpiNone: general kernel
 hipError_t launch_gemm_bf16_general(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
 // Epilogue kinds the pipelined kernel is compiled for (one kernel per kind):
 // fp32 store (or split-K partial), bf16 store, bias + GeLU saving the
@@ -111,6 +120,10 @@ hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int
 hipError_t launch_gemm_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s);
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);
+// Column-sum pass-1 units for a ColsumParams: row chunks, vector path usable.
+int64_t colsum_chunks(const ColsumParams& p);
+bool colsum_vec_ok(const ColsumParams& p);
+hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s);
 

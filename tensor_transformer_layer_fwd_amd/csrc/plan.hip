@@ -109,13 +109,16 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+int gemm_pipe_epilogue(const GemmParams& p, const SplitPlan& plan) {
   const bool aligned = (reinterpret_cast<uintptr_t>(p.a) & 15) == 0 && (p.lda & 7) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.b) & 15) == 0 && (p.ldb & 7) == 0;
-  if (plan.tile >= kPipe256x256 && aligned) {
-    const int ek = pipe_epilogue_kind(p);
-    if (ek != kEpiNone) return launch_gemm_bf16_pipe(p, plan, ek, s);
-  }
+  if (plan.tile < kPipe256x256 || !aligned) return kEpiNone;
+  return pipe_epilogue_kind(p);
+}
+
+hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+  const int ek = gemm_pipe_epilogue(p, plan);
+  if (ek != kEpiNone) return launch_gemm_bf16_pipe(p, plan, ek, s);
   return launch_gemm_bf16_general(p, plan, s);
 }
 

@@ -23,11 +23,20 @@ int hip_status(hipError_t e) {
   return TP_ERR_HIP;
 }
 
-int run_gemm(GemmParams& p, int dt, bool allow_split, size_t ws_bytes, hipStream_t s) {
+// Spare blocks of a weight-gradient GEMM that run column-sum pass-1 units.
+constexpr int kColsumBlocks = 128;
+
+// One bf16/fp32 GEMM (+ split-K fix-up). With cs (weight gradients with a
+// bias gradient), the column sums ride along with the GEMM and fix-up launches
+// when the pipelined kernel runs; otherwise they get launches of their own.
+int run_gemm(GemmParams& p, int dt, bool allow_split, size_t ws_bytes, hipStream_t s,
+             const ColsumParams* cs = nullptr) {
   if (dt == TP_F32) {
     p.splitk = 1;
     p.k_chunk = p.K;
-    return hip_status(launch_gemm_f32(p, s));
+    hipError_t e = launch_gemm_f32(p, s);
+    if (e == hipSuccess && cs) e = launch_colsum(*cs, s);
+    return hip_status(e);
   }
   const SplitPlan plan = plan_gemm_bf16(p.M, p.N, p.K, allow_split);
   p.splitk = plan.splitk;
@@ -35,11 +44,22 @@ int run_gemm(GemmParams& p, int dt, bool allow_split, size_t ws_bytes, hipStream
   if (plan.splitk > 1) {
     const size_t need = static_cast<size_t>(plan.splitk) * p.M * p.N * sizeof(float);
     if (!p.ws || ws_bytes < need) return TP_ERR_WORKSPACE;
-    hipError_t e = launch_gemm_bf16(p, plan, s);
-    if (e != hipSuccess) return hip_status(e);
-    return hip_status(launch_splitk_fixup(p, s));
   }
-  return hip_status(launch_gemm_bf16(p, plan, s));
+  const bool carry = cs && colsum_vec_ok(*cs) && gemm_pipe_epilogue(p, plan) == kEpiF32;
+  if (carry) {
+    const int64_t nchunks = colsum_chunks(*cs);
+    const int64_t units = (cs->N + 255) / 256 * nchunks;
+    p.cs = *cs;
+    p.cs_nchunks = static_cast<int>(nchunks);
+    p.cs_units = static_cast<int>(units);
+    p.cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
+  }
+  hipError_t e = launch_gemm_bf16(p, plan, s);
+  if (e == hipSuccess && plan.splitk > 1) e = launch_splitk_fixup(p, s);  // + pass 2
+  if (e == hipSuccess && carry && plan.splitk == 1 && p.cs_nchunks > 1)
+    e = launch_colsum_pass2(p.cs, p.cs_nchunks, s);
+  if (e == hipSuccess && cs && !carry) e = launch_colsum(*cs, s);
+  return hip_status(e);
 }
 
 size_t wgrad_split_bytes(int64_t T, int64_t k, int64_t n, int dt) {
@@ -177,8 +197,6 @@ int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbia
   p.ws = static_cast<float*>(workspace);
   p.a_kcontig = 0;  // In [T, k] read as In^T: M (= k) contiguous
   p.b_kcontig = 0;  // dOut [T, n]: N contiguous
-  int st = run_gemm(p, dt, true, split_bytes, stream);
-  if (st != TP_OK || !dbias) return st;
   ColsumParams c{};
   c.src = dOut;
   c.T = T;
@@ -187,8 +205,8 @@ int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbia
   c.src_bf16 = dt == TP_BF16;
   c.dbias = dbias;
   c.accumulate = accumulate != 0;
-  c.ws = reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes);
-  return hip_status(launch_colsum(c, stream));
+  c.ws = dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr;
+  return run_gemm(p, dt, true, split_bytes, stream, dbias ? &c : nullptr);
 }
 
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
