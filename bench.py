@@ -239,9 +239,17 @@ def main():
     from tensor_transformer_layer_fwd_amd import _lib as L
     o = step.out
     parts = [o[f"Zp_{i}"] for i in cfg.shards]
-    red_bytes = len(parts) * cfg.T * cfg.h * 4 + cfg.T * cfg.h * 2 + cfg.h * 2
-    red_ms = time_call(lambda: L.tp_reduce_partials(parts, step.inp.get("b"), o["Z"]),
+    z_out = o.get("Z")
+    if len(parts) < cfg.p or z_out is None:
+        # a workload that runs a subset of its shards: time the sum over all p
+        # partials with stand-in buffers of the same shape (zero-filled)
+        parts += [torch.zeros_like(parts[0]) for _ in range(cfg.p - len(parts))]
+        z_out = torch.empty(cfg.T, cfg.h, dtype=step.dt, device="cuda:0")
+    esz = z_out.element_size()
+    red_bytes = len(parts) * cfg.T * cfg.h * 4 + cfg.T * cfg.h * esz + (cfg.h * esz if cfg.has_bias else 0)
+    red_ms = time_call(lambda: L.tp_reduce_partials(parts, step.inp.get("b"), z_out),
                        args.kernel_reps)
+    del parts, z_out
     u32 = torch.randn(cfg.T, cfg.F, device="cuda:0")
     a32 = torch.randn(cfg.F, device="cuda:0")
     ybf = torch.empty(cfg.T, cfg.F, dtype=torch.bfloat16, device="cuda:0")

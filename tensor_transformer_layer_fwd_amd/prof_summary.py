@@ -41,7 +41,8 @@ def source_hash() -> str:
 
 
 def _short(name: str) -> str:
-    return name.replace("tpmlp::(anonymous namespace)::", "").replace("(tpmlp::GemmParams)", "")
+    name = name.replace("tpmlp::(anonymous namespace)::", "").replace("(tpmlp::GemmParams)", "")
+    return name if len(name) <= 120 else name[:117] + "..."
 
 
 def cmd_stats(a):
