@@ -194,17 +194,17 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
  * C[M,N] = op(A)[M,K] op(B)[K,N] of this shape (pure host function, for
  * tuning and tests). allow_split != 0 for the weight-gradient products, which
  * may split K. Writes the tile id (0: general kernel, any shape; 10: 256x256,
- * 11: 256x128, 12: 128x256, 13: 128x128, 14: 256x192 pipelined kernels, used when M and N
- * are multiples of the tile, K of 64 and both operands are 16-byte aligned
- * with row strides a multiple of 8), the number of K slices, and the K extent
- * of each slice. Any output pointer may be NULL.
+ * 11: 256x128, 12: 128x256, 13: 128x128, 14: 256x192, 15: 128x192 pipelined
+ * kernels, used when M and N are multiples of the tile, K of 64 and both
+ * operands are 16-byte aligned with row strides a multiple of 8), the number
+ * of K slices, and the K extent of each slice. Any output pointer may be NULL.
  */
 int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, int* splitk,
                  int64_t* k_chunk);
 
 /*
  * Tuning and test hook: every later bf16 product whose shape the pipelined
- * tile `tile` (10..14, as for tp_gemm_plan) supports uses that tile, and a
+ * tile `tile` (10..15, as for tp_gemm_plan) supports uses that tile, and a
  * weight-gradient product (the only kind that may split K) uses `splitk` K
  * slices when K is a multiple of 64 * splitk. tile = 0 restores the library's
  * own choice. Process-wide, and not synchronised with calls running on other

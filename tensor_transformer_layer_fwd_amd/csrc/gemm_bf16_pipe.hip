@@ -570,6 +570,9 @@ hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, int ek
                                                                                  s);
     case kPipe256x192:
       return launch_pipe_cfg<256, 192, 4, 2, 64, 2, AK, BKC>(p, plan.splitk, ek, s);
+    case kPipe128x192:
+      return launch_pipe_cfg<128, 192, 2, 2, kNT ? 64 : 32, kNT ? 3 : 4, AK, BKC>(p, plan.splitk, ek,
+                                                                                 s);
     default:
       return hipErrorInvalidValue;
   }

@@ -88,6 +88,7 @@ enum TileId : int {
   kPipe128x256 = 12,  // 8 waves, 64x64 per wave
   kPipe128x128 = 13,  // 4 waves, 64x64 per wave
   kPipe256x192 = 14,  // 8 waves, 64x96 per wave
+  kPipe128x192 = 15,  // 4 waves, 64x96 per wave
 };
 
 // Tile and split-K choice. It depends on the shape only, so the workspace-size

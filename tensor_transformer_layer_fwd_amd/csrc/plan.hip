@@ -22,13 +22,17 @@ struct PipeTile {
   TileId id;
   int bm, bn;
   double flop_per_sec_per_cu;
+  bool split_ok;  // measured competitive with split K
 };
 constexpr PipeTile kPipeTiles[] = {
-    {kPipe256x256, 256, 256, 5.0e12},
-    {kPipe256x128, 256, 128, 4.4e12},
-    {kPipe128x256, 128, 256, 4.6e12},
-    {kPipe128x128, 128, 128, 4.0e12},
-    {kPipe256x192, 256, 192, 4.6e12},
+    {kPipe256x256, 256, 256, 5.0e12, true},
+    {kPipe256x128, 256, 128, 4.4e12, true},
+    {kPipe128x256, 128, 256, 4.6e12, true},
+    {kPipe128x128, 128, 128, 4.0e12, true},
+    {kPipe256x192, 256, 192, 4.6e12, true},
+    // one wave per SIMD on a 64x96 wave tile: ahead of 128x256 on unsplit
+    // GPT-2-small products (19.3 vs 20.6 us), behind 128x128 once K is split
+    {kPipe128x192, 128, 192, 4.2e12, false},
 };
 
 double cost(int64_t M, int64_t N, int64_t K, const PipeTile& t, int split) {
@@ -82,7 +86,7 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
   for (const PipeTile& t : kPipeTiles) {
     if (!k_ok || M % t.bm || N % t.bn) continue;
     for (int s : kSplits) {
-      if (s > 1 && (!allow_split || K % (64 * s) || K / s < 256)) continue;
+      if (s > 1 && (!allow_split || !t.split_ok || K % (64 * s) || K / s < 256)) continue;
       const double c = cost(M, N, K, t, s);
       if (c < best_t) {
         best_t = c;

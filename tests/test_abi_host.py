@@ -124,7 +124,7 @@ def test_gemm_plan_query(lib):
     for M, N, K in [(4096, 1536, 768), (4096, 768, 1536), (2048, 6144, 12288),
                     (2048, 12288, 6144), (6144, 1024, 256)]:
         tile, sk, kc = L.tp_gemm_plan(M, N, K)
-        assert tile in (10, 11, 12, 13, 14) and sk == 1 and kc == K
+        assert tile in (10, 11, 12, 13, 14, 15) and sk == 1 and kc == K
     tile, sk, kc = L.tp_gemm_plan(768, 1536, 4096, allow_split=True)
     assert tile >= 10 and sk >= 1 and kc * sk == 4096 and kc % 64 == 0
     # ragged shapes use the general kernel

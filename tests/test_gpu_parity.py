@@ -446,7 +446,8 @@ def test_determinism_and_graph_replay(dev):
 # --------------------------------------------------------------------------- #
 # every pipelined tile configuration, in every operand layout                  #
 # --------------------------------------------------------------------------- #
-_TILE_MN = {10: (256, 256), 11: (256, 128), 12: (128, 256), 13: (128, 128), 14: (256, 192)}
+_TILE_MN = {10: (256, 256), 11: (256, 128), 12: (128, 256), 13: (128, 128), 14: (256, 192),
+            15: (128, 192)}
 
 
 @pytest.mark.parametrize("tile", sorted(_TILE_MN))
