@@ -452,15 +452,17 @@ _TILE_MN = {10: (256, 256), 11: (256, 128), 12: (128, 256), 13: (128, 128), 14: 
 
 @pytest.mark.parametrize("tile", sorted(_TILE_MN))
 @pytest.mark.parametrize("op", ["fwd_gelu", "row_partial", "dgrad_gelu", "dgrad_f32", "wgrad",
-                                "wgrad_split"])
+                                "wgrad_split", "wgrad_split_acc"])
 @pytest.mark.parametrize("kt", [2, 18])
 def test_pipelined_tiles(dev, tile, op, kt):
     """Each pipelined tile forced on a grid of 8 tiles (XCD remap path), with
     kt 32-wide K-tiles per block: 2 runs only the guarded tail, 18 the
-    steady-state loop and a 6-tile tail. The split case uses 3 K slices."""
+    steady-state loop and a 6-tile tail. The split cases use 3 K slices; the
+    weight gradients carry the bias column sums, once accumulating into
+    existing dW and dbias."""
     import tensor_transformer_layer_fwd_amd as tp
     from tensor_transformer_layer_fwd_amd import _lib as L
-    split = op == "wgrad_split"
+    split = op.startswith("wgrad_split")
     bm, bn = _TILE_MN[tile]
     M, N, K = 4 * bm, 2 * bn, 32 * kt * (3 if split else 1)
     tp.tp_set_gemm_override(tile, 3 if split else 1)
@@ -518,12 +520,18 @@ def _run_tile_op(dev, tile, op, M, N, K):
     else:
         In, Inr = rand(rng, (K, M), 1.0, dt)
         dO, dOr = rand(rng, (K, N), 1.0, dt)
-        dW = torch.empty(M, N, device=dev)
-        db = torch.empty(N, device=dev)
-        ws = torch.empty(max(16, L.tp_linear_bwd_wgrad_workspace_size(K, M, N, L.TP_BF16)),
-                         dtype=torch.uint8, device=dev)
-        tp.tp_linear_bwd_wgrad(upload(Inr, dt, dev), upload(dOr, dt, dev), dW, db, workspace=ws)
+        acc = op.endswith("_acc")
+        prev_w = rng.standard_normal((M, N)).astype(np.float32)
+        prev_b = rng.standard_normal(N).astype(np.float32)
+        dW = torch.from_numpy(prev_w).to(dev) if acc else torch.empty(M, N, device=dev)
+        db = torch.from_numpy(prev_b).to(dev) if acc else torch.empty(N, device=dev)
+        ws = torch.full((max(16, L.tp_linear_bwd_wgrad_workspace_size(K, M, N, L.TP_BF16)),), 255,
+                        dtype=torch.uint8, device=dev)  # garbage on entry
+        tp.tp_linear_bwd_wgrad(upload(Inr, dt, dev), upload(dOr, dt, dev), dW, db, accumulate=acc,
+                               workspace=ws)
         torch.cuda.synchronize()
         rw, rb = oracle.linear_bwd_wgrad(In, dO)
+        if acc:
+            rw, rb = rw + prev_w, rb + prev_b
         assert err(dW.cpu().numpy(), rw) <= 1e-5
         assert err(db.cpu().numpy(), rb) <= 1e-5
