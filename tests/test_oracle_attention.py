@@ -1,0 +1,110 @@
+"""Pins of the attention-core oracle (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle.attention import attention_core_fwd, split_qkv
+
+
+def _brute(QKV, batch, seq, heads, d, causal):
+    """Pure-Python loops: exp and correctly rounded sums (math.fsum)."""
+    rows = [list(map(float, r)) for r in np.asarray(QKV, dtype=np.float64)]
+    C = [[0.0] * (heads * d) for _ in range(batch * seq)]
+    lse = [[[0.0] * seq for _ in range(heads)] for _ in range(batch)]
+    for b in range(batch):
+        for h in range(heads):
+            for qi in range(seq):
+                qrow = rows[b * seq + qi][h * d:(h + 1) * d]
+                keys = range(qi + 1) if causal else range(seq)
+                sc = []
+                for ki in keys:
+                    krow = rows[b * seq + ki][heads * d + h * d:heads * d + (h + 1) * d]
+                    sc.append(math.fsum(x * y for x, y in zip(qrow, krow)) / math.sqrt(d))
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                den = math.fsum(w)
+                lse[b][h][qi] = mx + math.log(den)
+                for j in range(d):
+                    C[b * seq + qi][h * d + j] = math.fsum(
+                        wk * rows[b * seq + ki][2 * heads * d + h * d + j]
+                        for wk, ki in zip(w, keys)) / den
+    return np.array(C), np.array(lse)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_brute_force_tiny(causal):
+    rng = np.random.default_rng(5)
+    batch, seq, heads, d = 2, 5, 2, 3
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d))
+    C, lse = attention_core_fwd(QKV, batch, seq, heads, d, causal)
+    Cb, lseb = _brute(QKV, batch, seq, heads, d, causal)
+    np.testing.assert_allclose(C, Cb, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, lseb, rtol=1e-13, atol=1e-14)
+
+
+def test_zero_queries_give_prefix_means():
+    """Q = 0: all scores 0, so causal attention is the mean of V over positions
+    0..q and lse = log(q + 1)."""
+    rng = np.random.default_rng(6)
+    batch, seq, heads, d = 3, 7, 2, 4
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d))
+    QKV[:, :heads * d] = 0.0
+    C, lse = attention_core_fwd(QKV, batch, seq, heads, d)
+    _, _, v = split_qkv(QKV, batch, seq, heads, d)
+    mean = np.cumsum(v, axis=1) / np.arange(1, seq + 1)[None, :, None, None]
+    np.testing.assert_allclose(C, mean.reshape(batch * seq, heads * d), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse, np.broadcast_to(np.log(np.arange(1, seq + 1)), lse.shape),
+                               rtol=1e-13)
+
+
+def test_first_position_sees_only_itself():
+    rng = np.random.default_rng(7)
+    batch, seq, heads, d = 2, 6, 3, 8
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d)) * 3
+    C, _ = attention_core_fwd(QKV, batch, seq, heads, d)
+    _, _, v = split_qkv(QKV, batch, seq, heads, d)
+    np.testing.assert_array_equal(C.reshape(batch, seq, heads, d)[:, 0], v[:, 0])
+
+
+def test_one_hot_attention_picks_a_value_row():
+    """Each query aligned with one earlier key at a large scale: the output is
+    that key's value row (to within exp(-gap))."""
+    batch, seq, heads, d = 1, 6, 1, 6
+    rng = np.random.default_rng(8)
+    QKV = np.zeros((seq, 3 * d))
+    QKV[:, d:2 * d] = np.eye(seq, d) * 40.0      # key k = 40 e_k
+    target = [0, 0, 1, 2, 1, 4]                  # query q looks at key target[q] <= q
+    for qi, t in enumerate(target):
+        QKV[qi, :d] = np.eye(d)[t] * 40.0
+    QKV[:, 2 * d:] = rng.standard_normal((seq, d))
+    C, _ = attention_core_fwd(QKV, batch, seq, heads, d)
+    np.testing.assert_allclose(C, QKV[target, 2 * d:], rtol=0, atol=1e-12)
+
+
+def test_last_row_is_unmasked_and_sequences_are_independent():
+    rng = np.random.default_rng(9)
+    batch, seq, heads, d = 4, 9, 2, 5
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d))
+    Cc, lc = attention_core_fwd(QKV, batch, seq, heads, d, causal=True)
+    Cn, ln = attention_core_fwd(QKV, batch, seq, heads, d, causal=False)
+    last = np.arange(batch) * seq + seq - 1
+    np.testing.assert_allclose(Cc[last], Cn[last], rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(lc[:, :, -1], ln[:, :, -1], rtol=1e-14)
+    perm = np.array([2, 0, 3, 1])
+    QKVp = QKV.reshape(batch, seq, -1)[perm].reshape(batch * seq, -1)
+    Cp, lp = attention_core_fwd(QKVp, batch, seq, heads, d)
+    np.testing.assert_array_equal(Cp.reshape(batch, seq, -1), Cc.reshape(batch, seq, -1)[perm])
+    np.testing.assert_array_equal(lp, lc[perm])
+
+
+def test_weights_are_normalised():
+    """exp(score - lse) sums to one over the visible keys of every query."""
+    rng = np.random.default_rng(10)
+    batch, seq, heads, d = 2, 11, 3, 4
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d)) * 2
+    _, lse = attention_core_fwd(QKV, batch, seq, heads, d)
+    q, k, _ = split_qkv(QKV, batch, seq, heads, d)
+    s = np.einsum("bqhd,bkhd->bhqk", q, k) / math.sqrt(d)
+    w = np.exp(s - lse[..., None]) * np.tril(np.ones((seq, seq)))
+    np.testing.assert_allclose(w.sum(-1), 1.0, rtol=1e-13)
