@@ -190,6 +190,31 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
                 int64_t ld_y, int in_dt, int out_dt, int act, hipStream_t stream);
 
 /*
+ * Attention core of one shard, forward. The "Megatron" page ("Transformer-
+ * layer tensor parallelism") splits the QKV projection by output columns, so a
+ * shard holds whole heads and attends with them alone, between its QKV
+ * projection and its row-split output projection; the page's optimisation
+ * list recommends a fused attention kernel. For each of `batch` sequences of
+ * `seq` tokens (tokens sequence-major) and each of the shard's `heads` heads:
+ *
+ *   C   = softmax(Q K^T / sqrt(head_dim) [causal: position q sees keys <= q]) V
+ *   lse = log of each query's softmax normaliser (natural log)
+ *
+ * QKV   [batch*seq, 3*heads*head_dim] bf16, row stride ld_qkv: the Q, K and V
+ *       thirds, each head-major (head j at columns j*head_dim .. of its third)
+ * C     [batch*seq, heads*head_dim] bf16, row stride ld_c, head-major
+ * lse   [batch, heads, seq] fp32, or NULL
+ * causal  nonzero: mask keys after the query (a GPT decoder)
+ *
+ * bf16 only (TP_ERR_DTYPE). head_dim must be 64, QKV 16-byte aligned with
+ * ld_qkv a multiple of 8, and C 8-byte aligned with ld_c a multiple of 4
+ * (TP_ERR_SHAPE otherwise).
+ */
+int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
+                     int64_t heads, int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int causal,
+                     int dt, hipStream_t stream);
+
+/*
  * Which GEMM kernel configuration the library uses for a bf16 product
  * C[M,N] = op(A)[M,K] op(B)[K,N] of this shape (pure host function, for
  * tuning and tests). allow_split != 0 for the weight-gradient products, which

@@ -40,6 +40,8 @@ SIGNATURES = {
     "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
     "tp_gemm_plan": (_int, [_i64, _i64, _i64, _int, ctypes.POINTER(ctypes.c_int),
                             ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
+    "tp_attention_fwd": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
+                                _vp]),
     "tp_set_gemm_override": (_int, [_int, _int]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_hip_error": (_int, []),
@@ -188,6 +190,15 @@ def tp_gemm_plan(M: int, N: int, K: int, allow_split: bool = False):
     _check("tp_gemm_plan", lib().tp_gemm_plan(M, N, K, int(bool(allow_split)), ctypes.byref(t),
                                                ctypes.byref(sk), ctypes.byref(kc)))
     return int(t.value), int(sk.value), int(kc.value)
+
+
+def tp_attention_fwd(QKV, C, lse, batch: int, seq: int, heads: int, causal: bool = True,
+                     stream=None):
+    """Attention core of one shard: QKV [batch*seq, 3*heads*64] bf16 -> C
+    [batch*seq, heads*64] bf16 and lse [batch, heads, seq] fp32 (or None)."""
+    _check("tp_attention_fwd", lib().tp_attention_fwd(
+        _ptr(QKV), _ptr(C), _ptr(lse), batch, seq, heads, 64, _ld(QKV), _ld(C), int(bool(causal)),
+        _dt(QKV), _stream(stream)))
 
 
 def tp_set_gemm_override(tile: int = 0, splitk: int = 1) -> None:

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace tpmlp {
@@ -172,5 +174,20 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, int64_t row, 
     store8(p.c, o, v, p.out_bf16);
   }
 }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = I0 .. END-1.
+template <int I0, int END>
+struct Unroll {
+  template <class F>
+  __device__ __forceinline__ static void run(F&& f) {
+    f(std::integral_constant<int, I0>{});
+    Unroll<I0 + 1, END>::run(f);
+  }
+};
+template <int END>
+struct Unroll<END, END> {
+  template <class F>
+  __device__ __forceinline__ static void run(F&&) {}
+};
 
 }  // namespace tpmlp

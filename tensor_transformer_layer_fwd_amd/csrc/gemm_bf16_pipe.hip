@@ -86,20 +86,6 @@ __device__ __forceinline__ void block_sync() {
   asm volatile("" ::: "memory");
 }
 
-template <int I0, int END>
-struct Unroll {
-  template <class F>
-  __device__ __forceinline__ static void run(F&& f) {
-    f(std::integral_constant<int, I0>{});
-    Unroll<I0 + 1, END>::run(f);
-  }
-};
-template <int END>
-struct Unroll<END, END> {
-  template <class F>
-  __device__ __forceinline__ static void run(F&&) {}
-};
-
 // ---------------------------------------------------------------------------
 // Operand tiles
 // ---------------------------------------------------------------------------

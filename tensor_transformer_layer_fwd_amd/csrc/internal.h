@@ -58,6 +58,17 @@ struct GemmParams {
 };
 
 
+// Attention core of one shard (forward): QKV [batch*seq, 3*heads*64] bf16 as
+// [Q | K | V], C [batch*seq, heads*64] bf16, lse [batch, heads, seq] (or null).
+struct AttnParams {
+  const void* qkv;
+  void* c;
+  float* lse;
+  int64_t batch, seq, heads, ld_qkv, ld_c;
+  int causal;
+  float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+
 // Reduction over shards.
 constexpr int kMaxPartials = 16;
 struct ReduceParams {
@@ -127,5 +138,6 @@ bool colsum_vec_ok(const ColsumParams& p);
 hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s);
+hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s);
 
 }  // namespace tpmlp

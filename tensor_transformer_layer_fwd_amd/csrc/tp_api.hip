@@ -254,6 +254,31 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
   return hip_status(launch_bias_act(b, stream));
 }
 
+int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
+                     int64_t heads, int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int causal,
+                     int dt, hipStream_t stream) {
+  if (!QKV || !C) return TP_ERR_NULL;
+  if (dt != TP_BF16) return TP_ERR_DTYPE;
+  if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || head_dim != 64) return TP_ERR_SHAPE;
+  if (ld_qkv < 3 * heads * head_dim || ld_c < heads * head_dim) return TP_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(QKV) & 15) || (ld_qkv & 7) ||
+      (reinterpret_cast<uintptr_t>(C) & 7) || (ld_c & 3))
+    return TP_ERR_SHAPE;
+  if (batch * seq > kMaxDim) return TP_ERR_SHAPE;
+  AttnParams a{};
+  a.qkv = QKV;
+  a.c = C;
+  a.lse = lse;
+  a.batch = batch;
+  a.seq = seq;
+  a.heads = heads;
+  a.ld_qkv = ld_qkv;
+  a.ld_c = ld_c;
+  a.causal = causal != 0;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+  return hip_status(launch_attention_fwd(a, stream));
+}
+
 int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, int* splitk,
                  int64_t* k_chunk) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return TP_ERR_SHAPE;

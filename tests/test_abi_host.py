@@ -139,6 +139,29 @@ def test_gemm_plan_query(lib):
     assert lib.tp_gemm_plan(0, 5, 5, 0, None, None, None) == -2
 
 
+def test_attention_validation(lib):
+    """The attention entry point rejects bad arguments on the host, before any launch."""
+    import ctypes
+    buf = ctypes.create_string_buffer(4096 + 64)
+    base = (ctypes.addressof(buf) + 63) // 64 * 64
+    q = ctypes.c_void_p(base)
+    args = dict(batch=1, seq=4, heads=1, hd=64, ld_qkv=192, ld_c=64, causal=1, dt=L.TP_BF16)
+
+    def call(qkv=q, c=q, **kw):
+        a = dict(args, **kw)
+        return lib.tp_attention_fwd(qkv, c, None, a["batch"], a["seq"], a["heads"], a["hd"],
+                                    a["ld_qkv"], a["ld_c"], a["causal"], a["dt"], None)
+    assert call(qkv=None) == -1
+    assert call(c=None) == -1
+    assert call(dt=L.TP_F32) == -3
+    assert call(hd=32) == -2
+    assert call(seq=0) == -2
+    assert call(ld_qkv=191) == -2          # shorter than the row
+    assert call(ld_qkv=196) == -2          # not a multiple of 8
+    assert call(qkv=ctypes.c_void_p(base + 8)) == -2   # not 16-byte aligned
+    assert call(ld_c=66) == -2             # not a multiple of 4
+
+
 def test_gemm_override(lib):
     """The tuning hook forces a tile where the shape allows it, splits only
     weight gradients, changes the workspace query with the plan and resets."""

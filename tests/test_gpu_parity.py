@@ -535,3 +535,48 @@ def _run_tile_op(dev, tile, op, M, N, K):
             rw, rb = rw + prev_w, rb + prev_b
         assert err(dW.cpu().numpy(), rw) <= 1e-5
         assert err(db.cpu().numpy(), rb) <= 1e-5
+
+
+# --------------------------------------------------------------------------- #
+# attention core of one shard (forward)                                        #
+# --------------------------------------------------------------------------- #
+@pytest.mark.parametrize("batch,seq,heads,causal", [
+    (1, 1, 2, True), (1, 64, 1, True), (2, 100, 3, True), (2, 100, 3, False),
+    (3, 257, 2, True), (1, 384, 1, False),
+    (8, 512, 8, True),    # the attention-projection workload's shard: 8 x 512 tokens, 8 heads
+    (6, 1024, 4, True),   # the ~350M-layer workload's shard: 6 x 1024 tokens, 4 heads
+])
+def test_attention_fwd(dev, batch, seq, heads, causal):
+    import tensor_transformer_layer_fwd_amd as tp
+    from oracle.attention import attention_core_fwd
+    _say(f"attention batch={batch} seq={seq} heads={heads} causal={causal}")
+    rng = np.random.default_rng(batch * 1000 + seq + heads)
+    T, hd = batch * seq, heads * 64
+    QKV, QKVr = rand(rng, (T, 3 * hd), 1.0, "bf16")
+    C = Guarded(T, hd, "bf16", dev, pad=4)
+    lse = torch.full((batch * heads * seq + 8,), float("nan"), device=dev)
+    tp.tp_attention_fwd(upload(QKVr, "bf16", dev, pad=8), C.view, lse[4:4 + batch * heads * seq],
+                        batch, seq, heads, causal=causal)
+    torch.cuda.synchronize()
+    C_ref, lse_ref = attention_core_fwd(QKV, batch, seq, heads, 64, causal)
+    assert err(C.value(), C_ref) <= TOL["bf16"]
+    got = lse.cpu().numpy().astype(np.float64)
+    assert np.all(np.isnan(got[:4])) and np.all(np.isnan(got[4 + batch * heads * seq:]))
+    np.testing.assert_allclose(got[4:4 + batch * heads * seq], lse_ref.reshape(-1), rtol=0,
+                               atol=1e-4)
+
+
+def test_attention_fwd_deterministic_and_lse_optional(dev):
+    import tensor_transformer_layer_fwd_amd as tp
+    rng = np.random.default_rng(77)
+    batch, seq, heads = 2, 320, 2
+    _, QKVr = rand(rng, (batch * seq, 3 * heads * 64), 1.0, "bf16")
+    x = upload(QKVr, "bf16", dev)
+    outs = []
+    for with_lse in (True, False, True):
+        C = torch.empty(batch * seq, heads * 64, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty(batch * heads * seq, device=dev) if with_lse else None
+        tp.tp_attention_fwd(x, C, lse, batch, seq, heads)
+        outs.append(C.cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
