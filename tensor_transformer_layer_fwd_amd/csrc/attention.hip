@@ -33,9 +33,10 @@ constexpr int kStageBytes = 2 * kTileBytes;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
-template <int J>
-__device__ __forceinline__ uint8_t* attn_stage() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[kStageBytes];
+// All stages in one LDS array, so a stage is a constant offset: fragment reads
+// use the instruction's immediate offset and keep one address register each.
+__device__ __forceinline__ uint8_t* attn_lds() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[kStages * kStageBytes];
   return buf;
 }
 
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
     src[i] = qkv + (row0 + r) * p.ld_qkv + (1 + t) * hd + h * kD + c * 8;
   }
   auto issue = [&](auto stage_c, int kb) {
-    uint8_t* st = attn_stage<decltype(stage_c)::value>();
+    uint8_t* st = attn_lds() + decltype(stage_c)::value * kStageBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int w = wave * 4 + i, r = 8 * (w % 8) + lane / 8;
@@ -124,53 +125,93 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16_t o[2] = {f32x16_t{}, f32x16_t{}};
 
+  const int wq_first = qb * kQB + wave * 32;     // this wave's first query
+
+  // per-lane LDS byte addresses of the fragment reads within stage 0
+  const uint32_t lds0 = attn_lds_addr(attn_lds());
+  uint32_t ka[2][4];  // K tile: key row 32m + ql, 16-byte chunk 2ks + half
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int r = 32 * m + ql, c = 2 * ks + half;
+      ka[m][ks] = lds0 + r * 128 + ((c ^ kswz(r)) << 4);
+    }
+  uint32_t va[4][2];  // V tile, transposed reads: key rows kr and kr + 8, columns d .. d+3
+  {
+    const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const int kr = 16 * st + 4 * (g >> 1) + (sl >> 2);
+        const int d = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+        va[st][db] = lds0 + kTileBytes + kr * 128 + (((d >> 3) ^ vswz(kr)) << 4) + (d & 7) * 2;
+      }
+  }
+
   auto compute = [&](auto stage_c, int kb) {
-    const uint8_t* kt = attn_stage<decltype(stage_c)::value>();
-    const uint8_t* vt = kt + kTileBytes;
+    constexpr int SOFF = decltype(stage_c)::value * kStageBytes;
     const int k0 = kb * kKB;
     if (p.causal && k0 > wq_last) return;  // every key of the tile is masked for this wave
-    // S^T for two 32-key halves
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+    // K fragments for S^T
+    bf16x8_t kf[2][4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bf16x8_t kf[4];
-      const int r = 32 * m + ql;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int c = 2 * ks + half;
-        const uint32_t a = attn_lds_addr(kt) + r * 128 + ((c ^ kswz(r)) << 4);
-        asm volatile("ds_read_b128 %0, %1" : "=v"(kf[ks]) : "v"(a));
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(kf[ks]));
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks], qf[ks], s[m], 0, 0, 0);
-    }
-    // scale, mask, running max and sum (register r of half m: key
-    // k0 + 32m + 8*(r/4) + 4*half + r%4)
+        asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(kf[m][ks]) : "v"(ka[m][ks]), "i"(SOFF));
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(kf[m][ks]));
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[m][ks], qf[ks], s[m], 0, 0, 0);
+    // the transposed V fragments, read while the softmax arithmetic runs
+    // (not before: the K and V fragments would then be live together)
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8_t vf[4][2];  // [16-key step][32-wide d block]
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        s16x4_t lo, hi;
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(va[st][db]), "i"(SOFF));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(hi) : "v"(va[st][db]), "i"(SOFF + 8 * 128));  // key row + 8
+        vf[st][db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+    // scale and mask (register r of half m: key k0 + 32m + 8*(r/4) + 4*half + r%4);
+    // tiles wholly below the diagonal and inside the sequence need no mask
+    const bool interior = (!p.causal || k0 + kKB - 1 <= wq_first) && k0 + kKB <= seq;
     float mx = -INFINITY;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = k0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
         float v = s[m][r] * scale;
-        if (key >= seq || (p.causal && key > q)) v = -INFINITY;
+        if (!interior) {
+          const int key = k0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
+          if (key >= seq || (p.causal && key > q)) v = -INFINITY;
+        }
         s[m][r] = v;
         mx = fmaxf(mx, v);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // a row with no visible key yet
-    const float corr = exp2f(m_run - m_use);
+    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
     float sum = 0.0f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[m][r] - m_use);
+        const float e = __builtin_amdgcn_exp2f(s[m][r] - m_use);  // argument <= 0
         s[m][r] = e;
         sum += e;
       }
@@ -179,35 +220,23 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
     m_run = m_new;
 #pragma unroll
     for (int db = 0; db < 2; ++db) o[db] *= corr;
-    // O^T += V^T P^T over four 16-key steps
-    const int g = lane >> 4, sl = lane & 15;
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int st = 0; st < 4; ++st)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        f32x8_t pv;
+      for (int db = 0; db < 2; ++db) asm volatile("" : "+v"(vf[st][db]));
+    // O^T += V^T P^T over four 16-key steps (step st: half m = st/2, registers 8*(st%2) ..)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pv[e] = s[m][8 * hh + e];
-        const bf16x8_t pf = __builtin_convertvector(pv, bf16x8_t);  // round to nearest even
-        const int kr = 32 * m + 16 * hh + 4 * (g >> 1) + (sl >> 2);
-        bf16x8_t vf[2];
+    for (int st = 0; st < 4; ++st) {
+      const int m = st >> 1, hh = st & 1;
+      f32x8_t pv;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int d = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
-          const uint32_t a0 = attn_lds_addr(vt) + kr * 128 + (((d >> 3) ^ vswz(kr)) << 4) + (d & 7) * 2;
-          const uint32_t a1 = a0 + 8 * 128;  // key row kr + 8: same swizzle
-          s16x4_t lo, hi;
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
-          asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
-          vf[db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      for (int e = 0; e < 8; ++e) pv[e] = s[m][8 * hh + e];
+      const bf16x8_t pf = __builtin_convertvector(pv, bf16x8_t);  // round to nearest even
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          asm volatile("" : "+v"(vf[db]));
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[db], pf, o[db], 0, 0, 0);
-        }
-      }
+      for (int db = 0; db < 2; ++db)
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[st][db], pf, o[db], 0, 0, 0);
+    }
   };
 
   // ---- pass over the key tiles: 3 stages, two tiles in flight
