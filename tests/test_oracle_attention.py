@@ -108,3 +108,88 @@ def test_weights_are_normalised():
     s = np.einsum("bqhd,bkhd->bhqk", q, k) / math.sqrt(d)
     w = np.exp(s - lse[..., None]) * np.tril(np.ones((seq, seq)))
     np.testing.assert_allclose(w.sum(-1), 1.0, rtol=1e-13)
+
+
+from oracle.attention import attention_core_bwd  # noqa: E402
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_finite_differences(causal):
+    """<dC, dC_dir> sensitivity: d/de L(QKV + e*E) with L = <G, C(QKV)> equals
+    <dQKV, E>, checked by central differences in float64."""
+    rng = np.random.default_rng(11)
+    batch, seq, heads, d = 2, 6, 2, 4
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d))
+    G = rng.standard_normal((batch * seq, heads * d))
+    dQKV = attention_core_bwd(QKV, G, batch, seq, heads, d, causal)
+    for trial in range(4):
+        E = rng.standard_normal(QKV.shape)
+        h = 1e-5
+        lp = np.sum(G * attention_core_fwd(QKV + h * E, batch, seq, heads, d, causal)[0])
+        lm = np.sum(G * attention_core_fwd(QKV - h * E, batch, seq, heads, d, causal)[0])
+        assert abs((lp - lm) / (2 * h) - np.sum(dQKV * E)) <= 1e-7 * (1 + abs(np.sum(dQKV * E)))
+
+
+def _brute_bwd(QKV, G, batch, seq, heads, d, causal):
+    """Chain rule written out per element with pure-Python loops."""
+    X = [list(map(float, r)) for r in np.asarray(QKV, dtype=np.float64)]
+    Gl = [list(map(float, r)) for r in np.asarray(G, dtype=np.float64)]
+    out = [[0.0] * (3 * heads * d) for _ in range(batch * seq)]
+    sc = 1.0 / math.sqrt(d)
+    for b in range(batch):
+        for h in range(heads):
+            Q = [X[b * seq + t][h * d:(h + 1) * d] for t in range(seq)]
+            K = [X[b * seq + t][heads * d + h * d:heads * d + (h + 1) * d] for t in range(seq)]
+            V = [X[b * seq + t][2 * heads * d + h * d:2 * heads * d + (h + 1) * d] for t in range(seq)]
+            for qi in range(seq):
+                keys = list(range(qi + 1)) if causal else list(range(seq))
+                s = [math.fsum(a * c for a, c in zip(Q[qi], K[ki])) * sc for ki in keys]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                den = math.fsum(w)
+                pr = [x / den for x in w]
+                g = Gl[b * seq + qi][h * d:(h + 1) * d]
+                dp = [math.fsum(a * c for a, c in zip(g, V[ki])) for ki in keys]
+                dot = math.fsum(a * c for a, c in zip(pr, dp))
+                ds = [p_ * (x - dot) for p_, x in zip(pr, dp)]
+                for j in range(d):
+                    out[b * seq + qi][h * d + j] += math.fsum(
+                        x * K[ki][j] for x, ki in zip(ds, keys)) * sc
+                for x, p_, ki in zip(ds, pr, keys):
+                    for j in range(d):
+                        out[b * seq + ki][heads * d + h * d + j] += x * Q[qi][j] * sc
+                        out[b * seq + ki][2 * heads * d + h * d + j] += p_ * g[j]
+    return np.array(out)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_brute_force(causal):
+    rng = np.random.default_rng(12)
+    batch, seq, heads, d = 2, 5, 2, 3
+    QKV = rng.standard_normal((batch * seq, 3 * heads * d))
+    G = rng.standard_normal((batch * seq, heads * d))
+    np.testing.assert_allclose(attention_core_bwd(QKV, G, batch, seq, heads, d, causal),
+                               _brute_bwd(QKV, G, batch, seq, heads, d, causal),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_backward_special_cases():
+    """Q = 0 (uniform causal weights): dV[k] = sum over q >= k of dC[q]/(q+1)
+    and dK = 0 exactly. For any inputs each query's score gradient sums to
+    zero over its keys (softmax is shift-invariant), so dK sums to zero over
+    the keys of a sequence."""
+    rng = np.random.default_rng(13)
+    batch, seq, heads, d = 1, 7, 1, 4
+    QKV = rng.standard_normal((seq, 3 * d))
+    QKV[:, :d] = 0.0
+    G = rng.standard_normal((seq, d))
+    dQKV = attention_core_bwd(QKV, G, batch, seq, heads, d, True)
+    w = 1.0 / np.arange(1, seq + 1)
+    dv_ref = np.array([np.sum(G[k:] * w[k:, None], axis=0) for k in range(seq)])
+    np.testing.assert_allclose(dQKV[:, 2 * d:], dv_ref, rtol=1e-13, atol=1e-14)
+    # with Q = 0, dK = dS^T Q / sqrt(d) = 0 exactly
+    np.testing.assert_array_equal(dQKV[:, d:2 * d], 0.0)
+    # for general inputs, sum over keys of dK = (sum_k dS[q,k]) Q ... = 0
+    QKV2 = rng.standard_normal((seq, 3 * d))
+    dQKV2 = attention_core_bwd(QKV2, G, batch, seq, heads, d, True)
+    np.testing.assert_allclose(dQKV2[:, d:2 * d].sum(axis=0), 0.0, atol=1e-12)
