@@ -215,6 +215,34 @@ int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_
                      int dt, hipStream_t stream);
 
 /*
+ * Attention core of one shard, backward: the gradient of the forward above
+ * with respect to QKV, given the gradient dC of its output (in a shard this is
+ * the dgrad of the row-split output projection). With P the softmax weights,
+ * recomputed from Q, K and lse:
+ *
+ *   delta[q] = sum_d dC[q,d] C[q,d]
+ *   dV = P^T dC,  dS = P * (dC V^T - delta),  dQ = dS K / sqrt(head_dim),
+ *   dK = dS^T Q / sqrt(head_dim)
+ *
+ * QKV, C, lse, causal  exactly as passed to / written by tp_attention_fwd
+ * dC    [batch*seq, heads*head_dim] bf16, row stride ld_dc
+ * delta [batch, heads, seq] fp32 workspace owned by the caller, overwritten
+ * dQKV  [batch*seq, 3*heads*head_dim] bf16, row stride ld_dqkv, laid out like
+ *       QKV; columns 0 .. 3*heads*head_dim of every row are written. It must
+ *       not overlap any input.
+ *
+ * Each output element is computed by one thread in a fixed order (no atomics):
+ * results are bitwise reproducible. bf16 only (TP_ERR_DTYPE); lse and delta
+ * must not be NULL (TP_ERR_NULL). head_dim must be 64, QKV, C and dC 16-byte
+ * aligned with row strides a multiple of 8, dQKV 8-byte aligned with ld_dqkv a
+ * multiple of 4 (TP_ERR_SHAPE otherwise).
+ */
+int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float* lse,
+                     float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
+                     int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
+                     int64_t ld_dqkv, int causal, int dt, hipStream_t stream);
+
+/*
  * Which GEMM kernel configuration the library uses for a bf16 product
  * C[M,N] = op(A)[M,K] op(B)[K,N] of this shape (pure host function, for
  * tuning and tests). allow_split != 0 for the weight-gradient products, which

@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     TP_F32,
     TPError,
     lib,
+    tp_attention_bwd,
     tp_attention_fwd,
     tp_bias_act,
     tp_column_linear_fwd,

@@ -42,6 +42,8 @@ SIGNATURES = {
                             ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
     "tp_attention_fwd": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
                                 _vp]),
+    "tp_attention_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                _i64, _i64, _int, _int, _vp]),
     "tp_set_gemm_override": (_int, [_int, _int]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_hip_error": (_int, []),
@@ -199,6 +201,15 @@ def tp_attention_fwd(QKV, C, lse, batch: int, seq: int, heads: int, causal: bool
     _check("tp_attention_fwd", lib().tp_attention_fwd(
         _ptr(QKV), _ptr(C), _ptr(lse), batch, seq, heads, 64, _ld(QKV), _ld(C), int(bool(causal)),
         _dt(QKV), _stream(stream)))
+
+
+def tp_attention_bwd(QKV, C, dC, lse, delta, dQKV, batch: int, seq: int, heads: int,
+                     causal: bool = True, stream=None):
+    """Backward of tp_attention_fwd: dQKV (laid out like QKV) from dC, the
+    forward's C and lse; delta [batch, heads, seq] fp32 is a workspace."""
+    _check("tp_attention_bwd", lib().tp_attention_bwd(
+        _ptr(QKV), _ptr(C), _ptr(dC), _ptr(lse), _ptr(delta), _ptr(dQKV), batch, seq, heads, 64,
+        _ld(QKV), _ld(C), _ld(dC), _ld(dQKV), int(bool(causal)), _dt(QKV), _stream(stream)))
 
 
 def tp_set_gemm_override(tile: int = 0, splitk: int = 1) -> None:

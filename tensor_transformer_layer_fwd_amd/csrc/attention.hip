@@ -275,7 +275,432 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   }
 }
 
+// ===========================================================================
+// Backward. With P = softmax(S), S = Q K^T / 8 (masked), delta[q] =
+// rowsum(dC * C)[q]:  dV = P^T dC,  dP = dC V^T,  dS = P (dP - delta),
+// dQ = dS K / 8,  dK = dS^T Q / 8.  P is recomputed from the saved lse.
+// Two kernels, each owning its outputs (no atomics, so the result does not
+// depend on scheduling): one per 128-key block, walking the query tiles, for
+// dK and dV; one per 128-query block, walking the key tiles, for dQ.
+// ===========================================================================
+
+// Chunk swizzle for a [64][64] bf16 tile read both along rows (16-byte reads
+// of 32 consecutive rows) and across rows (transposed reads of rows k..k+3
+// and k+8..k+11): an XOR of the row bits found by exhaustive search over such
+// maps, conflict-free for both patterns.
+__device__ __forceinline__ int dswz(int r) {
+  return ((r >> 1) & 1) | (((r >> 2) & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2);
+}
+
+constexpr int kBStages = 3;
+// a stage: two [64][64] bf16 tiles, then (dK/dV kernel) the lse and delta of
+// the tile's 64 queries, each twice so that every wave issues one copy
+constexpr int kBStatBytes = 1024;
+constexpr int kBStageBytes = 2 * kTileBytes + kBStatBytes;
+
+__device__ __forceinline__ uint8_t* attn_bwd_lds() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[kBStages * kBStageBytes];
+  return buf;
+}
+
+// delta[b, h, q] = sum over d of dC[t, h*64 + d] * C[t, h*64 + d], t = b*seq + q
+__global__ __launch_bounds__(256) void attn_delta_kernel(AttnBwdParams p) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= p.batch * p.seq * p.heads) return;
+  const int64_t t = i / p.heads;
+  const int h = static_cast<int>(i % p.heads);
+  const uint16_t* dc = static_cast<const uint16_t*>(p.dc) + t * p.ld_dc + h * kD;
+  const uint16_t* c = static_cast<const uint16_t*>(p.c) + t * p.ld_c + h * kD;
+  float acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kD; j += 8) {
+    float a[8], v[8];
+    load8_bf16(dc, j, a);
+    load8_bf16(c, j, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(a[e], v[e], acc);
+  }
+  const int64_t b = t / p.seq, q = t % p.seq;
+  p.delta[(b * p.heads + h) * p.seq + q] = acc;
+}
+
+// Copies of a [64][64] tile (rows = tokens row0 + r0 + 0..63, clamped to the
+// sequence; 64 columns from col) into LDS at dst, swizzled with dswz: 8
+// windows of 1 KiB, window w = 8 rows; this wave copies windows w0..w0+1.
+struct TileCopy {
+  const uint16_t* src[2];
+  __device__ __forceinline__ void init(const uint16_t* base, int64_t ld, int64_t row0, int64_t col,
+                                       int w0, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * (w0 + i) + lane / 8, c = (lane % 8) ^ dswz(r);
+      src[i] = base + (row0 + r) * ld + col + c * 8;
+    }
+  }
+  // rows r0 + r; rows past seq read row seq-1 (callers mask them)
+  __device__ __forceinline__ void issue(uint8_t* dst, int64_t r0, int64_t seq, int64_t ld, int w0,
+                                        int lane) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = 8 * (w0 + i) + lane / 8;
+      const int64_t over = r0 + r - (seq - 1);
+      const uint16_t* g = src[i] + r0 * ld - (over > 0 ? over * ld : 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                       (__attribute__((address_space(3))) void*)(dst + (w0 + i) * 1024),
+                                       16, 0, 0);
+    }
+  }
+};
+
+// Per-lane LDS addresses of a tile's fragment reads, relative to the tile.
+// Row reads: row 32m + (lane & 31), chunk 2ks + lane/32. Transposed reads
+// (A operand with the permuted 16-token order of the forward): rows
+// 16st + 4*(lane/32) + (lane%16)/4 and that + 8, columns 32db + 16*((lane/16)%2)
+// + 4*(lane%4).
+__device__ __forceinline__ uint32_t row_addr(int m, int ks, int lane) {
+  const int r = 32 * m + (lane & 31), c = 2 * ks + (lane >> 5);
+  return r * 128 + ((c ^ dswz(r)) << 4);
+}
+__device__ __forceinline__ uint32_t tr_addr(int st, int db, int second, int lane) {
+  const int g = lane >> 4, sl = lane & 15;
+  const int r = 16 * st + 4 * (g >> 1) + (sl >> 2) + 8 * second;
+  const int d = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+  return r * 128 + (((d >> 3) ^ dswz(r)) << 4) + (d & 7) * 2;
+}
+
+template <int N>
+__device__ __forceinline__ void lds_tie(bf16x8_t (&f)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+
+// 32x32x16 operand from two transposed reads at LDS byte addresses a0, a1.
+__device__ __forceinline__ bf16x8_t tr_frag(uint32_t a0, uint32_t a1) {
+  s16x4_t lo, hi;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ bf16x8_t row_frag(uint32_t a) {
+  bf16x8_t f;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(f) : "v"(a));
+  return f;
+}
+
+// bf16 operand from registers 8*hh .. 8*hh+7 of an accumulator
+__device__ __forceinline__ bf16x8_t pack8(const f32x16_t& v, int hh) {
+  f32x8_t t;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) t[e] = v[8 * hh + e];
+  return __builtin_convertvector(t, bf16x8_t);
+}
+
+// ---- dK, dV: block = 128 keys of one (sequence, head), wave = 32 keys;
+// per 64-query tile: S = Q K^T and dP = dC V^T (lane = key, registers =
+// queries), P, dS, then dV^T += dC^T P and dK^T += Q^T dS.
+__global__ __launch_bounds__(256) void attn_bwd_kv_kernel(AttnBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t seq = p.seq;
+  const int nkb = static_cast<int>((seq + 127) / 128);
+  const int kb = static_cast<int>(blockIdx.x % nkb);  // the keys most queries see first
+  const int bh = static_cast<int>(blockIdx.x / nkb);
+  const int h = bh % static_cast<int>(p.heads);
+  const int64_t b = bh / p.heads;
+  const int64_t row0 = b * seq, hd = p.heads * kD;
+  const int64_t lbase = (b * p.heads + h) * seq;
+  const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
+  const uint16_t* dcp = static_cast<const uint16_t*>(p.dc);
+  const int kl = lane & 31, half = lane >> 5;
+  const int key = kb * 128 + wave * 32 + kl;
+  const int64_t krow = row0 + (key < seq ? key : seq - 1);
+
+  // K and V fragments of this wave's 32 keys (B operands: column = key)
+  bf16x8_t kf[4], vf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    kf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + krow * p.ld_qkv + hd + h * kD + 16 * ks + 8 * half);
+    vf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + krow * p.ld_qkv + 2 * hd + h * kD + 16 * ks + 8 * half);
+  }
+  attn_wait_vmcnt<0>();
+  lds_tie(kf);
+  lds_tie(vf);
+
+  // query tiles: causal rows q >= the block's first key
+  const int nqt = static_cast<int>((seq + 63) / 64);
+  const int qt0 = p.causal ? kb * 2 : 0;
+  TileCopy cq, cd;
+  cq.init(qkv, p.ld_qkv, row0, h * kD, 2 * wave, lane);       // Q tile: windows 2w, 2w+1
+  cd.init(dcp, p.ld_dc, row0, h * kD, 2 * wave, lane);        // dC tile
+  const uint32_t lds0 = attn_lds_addr(attn_bwd_lds());
+  // stats copy: waves 0 and 2 copy lse, 1 and 3 delta, of queries qt*64 + lane
+  const float* stat_src = (wave & 1 ? p.delta : p.lse) + lbase;
+  auto issue = [&](auto stage_c, int qt) {
+    uint8_t* st = attn_bwd_lds() + decltype(stage_c)::value * kBStageBytes;
+    cq.issue(st, static_cast<int64_t>(qt) * 64, seq, p.ld_qkv, 2 * wave, lane);
+    cd.issue(st + kTileBytes, static_cast<int64_t>(qt) * 64, seq, p.ld_dc, 2 * wave, lane);
+    const int64_t qq = static_cast<int64_t>(qt) * 64 + lane;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(stat_src + (qq < seq ? qq : seq - 1)),
+        (__attribute__((address_space(3))) void*)(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
+  };
+
+  f32x16_t dv[2] = {f32x16_t{}, f32x16_t{}}, dk[2] = {f32x16_t{}, f32x16_t{}};
+  const float scale = p.scale_log2;
+  const int wk_first = kb * 128 + wave * 32;  // this wave's first key
+
+  auto compute = [&](auto stage_c, int qt) {
+    constexpr int kStage = decltype(stage_c)::value;
+    const uint32_t sq = lds0 + kStage * kBStageBytes, sd = sq + kTileBytes;
+    const float* stats = reinterpret_cast<const float*>(attn_bwd_lds() + kStage * kBStageBytes + 2 * kTileBytes);
+    const int q0 = qt * 64;
+    if (p.causal && q0 + 63 < wk_first) return;  // no query of the tile sees these keys
+    // S = Q K^T, dP = dC V^T for the tile's 64 queries
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8_t qa[4], da[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        qa[ks] = row_frag(sq + row_addr(m, ks, lane));
+        da[ks] = row_frag(sd + row_addr(m, ks, lane));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_tie(qa);
+      lds_tie(da);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s[m], 0, 0, 0);
+        dp[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], dp[m], 0, 0, 0);
+      }
+    }
+    // P and dS (masked entries 0); register r of half m holds query
+    // q0 + 32m + 8*(r/4) + 4*half + r%4
+    const bool interior = (!p.causal || q0 >= wk_first + 31) && q0 + 64 <= seq;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int qi = 32 * m + 8 * j + 4 * half;
+        const float4 l4 = *reinterpret_cast<const float4*>(stats + qi);
+        const float4 d4 = *reinterpret_cast<const float4*>(stats + 64 + qi);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * j + e;
+          float pr = __builtin_amdgcn_exp2f(s[m][r] * scale - lv[e] * 1.4426950408889634f);
+          if (!interior) {
+            const int qq = q0 + qi + e;
+            if (qq >= seq || (p.causal && key > qq)) pr = 0.0f;
+          }
+          s[m][r] = pr;
+          dp[m][r] = pr * (dp[m][r] - dl[e]);
+        }
+      }
+    // dV^T += dC^T P and dK^T += Q^T dS over four 16-query steps
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int m = st >> 1, hh = st & 1;
+      const bf16x8_t pf = pack8(s[m], hh), sf = pack8(dp[m], hh);
+      bf16x8_t ta[2], tq[2];
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        ta[db] = tr_frag(sd + tr_addr(st, db, 0, lane), sd + tr_addr(st, db, 1, lane));
+        tq[db] = tr_frag(sq + tr_addr(st, db, 0, lane), sq + tr_addr(st, db, 1, lane));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_tie(ta);
+      lds_tie(tq);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], pf, dv[db], 0, 0, 0);
+        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[db], sf, dk[db], 0, 0, 0);
+      }
+    }
+  };
+
+  const int ntile = nqt - qt0;
+  Unroll<0, 2>::run([&](auto jc) {
+    if (decltype(jc)::value < ntile) issue(jc, qt0 + decltype(jc)::value);
+  });
+  for (int i0 = 0; i0 < ntile; i0 += kBStages) {
+    Unroll<0, kBStages>::run([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int i = i0 + J;
+      if (i < ntile) {
+        if (i + 1 < ntile) attn_wait_vmcnt<5>();  // tile i+1's five copies may still fly
+        else attn_wait_vmcnt<0>();
+        attn_sync();
+        if (i + 2 < ntile) issue(std::integral_constant<int, (J + 2) % kBStages>{}, qt0 + i + 2);
+        compute(jc, qt0 + i);
+      }
+    });
+  }
+
+  // dK = dK^T^T / 8, dV = dV^T^T: lane holds key `key`, d = 32db + 8*(r/4) + 4*half + r%4
+  if (key < seq) {
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + (row0 + key) * p.ld_dqkv + h * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = 32 * db + 8 * r4 + 4 * half;
+        uint2 wk, wv;
+        wk.x = pack_bf16x2(dk[db][4 * r4] * 0.125f, dk[db][4 * r4 + 1] * 0.125f);
+        wk.y = pack_bf16x2(dk[db][4 * r4 + 2] * 0.125f, dk[db][4 * r4 + 3] * 0.125f);
+        wv.x = pack_bf16x2(dv[db][4 * r4], dv[db][4 * r4 + 1]);
+        wv.y = pack_bf16x2(dv[db][4 * r4 + 2], dv[db][4 * r4 + 3]);
+        *reinterpret_cast<uint2*>(out + hd + d) = wk;
+        *reinterpret_cast<uint2*>(out + 2 * hd + d) = wv;
+      }
+  }
+}
+
+// ---- dQ: block = 128 queries, wave = 32 queries; per 64-key tile:
+// S^T = K Q^T, dP^T = V dC^T (lane = query), P^T, dS^T, dQ^T += K^T dS^T.
+__global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnBwdParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t seq = p.seq;
+  const int nqb = static_cast<int>((seq + kQB - 1) / kQB);
+  const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
+  const int bh = static_cast<int>(blockIdx.x / nqb);
+  const int h = bh % static_cast<int>(p.heads);
+  const int64_t b = bh / p.heads;
+  const int64_t row0 = b * seq, hd = p.heads * kD;
+  const int64_t lbase = (b * p.heads + h) * seq;
+  const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
+  const uint16_t* dcp = static_cast<const uint16_t*>(p.dc);
+  const int ql = lane & 31, half = lane >> 5;
+  const int q = qb * kQB + wave * 32 + ql;
+  const int64_t qrow = row0 + (q < seq ? q : seq - 1);
+  bf16x8_t qf[4], df[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    qf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + qrow * p.ld_qkv + h * kD + 16 * ks + 8 * half);
+    df[ks] = *reinterpret_cast<const bf16x8_t*>(dcp + qrow * p.ld_dc + h * kD + 16 * ks + 8 * half);
+  }
+  const float lq = p.lse[lbase + (q < seq ? q : seq - 1)] * 1.4426950408889634f;
+  const float dl = p.delta[lbase + (q < seq ? q : seq - 1)];
+  attn_wait_vmcnt<0>();
+  lds_tie(qf);
+  lds_tie(df);
+
+  const int nkt_seq = static_cast<int>((seq + 63) / 64);
+  const int qlast = min(static_cast<int>(seq) - 1, qb * kQB + kQB - 1);
+  const int nkt = p.causal ? min(nkt_seq, qlast / 64 + 1) : nkt_seq;
+  const int wq_first = qb * kQB + wave * 32, wq_last = wq_first + 31;
+  TileCopy ck, cv;
+  ck.init(qkv, p.ld_qkv, row0, hd + h * kD, 2 * wave, lane);
+  cv.init(qkv, p.ld_qkv, row0, 2 * hd + h * kD, 2 * wave, lane);
+  const uint32_t lds0 = attn_lds_addr(attn_bwd_lds());
+  auto issue = [&](auto stage_c, int kt) {
+    uint8_t* st = attn_bwd_lds() + decltype(stage_c)::value * kBStageBytes;
+    ck.issue(st, static_cast<int64_t>(kt) * 64, seq, p.ld_qkv, 2 * wave, lane);
+    cv.issue(st + kTileBytes, static_cast<int64_t>(kt) * 64, seq, p.ld_qkv, 2 * wave, lane);
+  };
+  f32x16_t dqa[2] = {f32x16_t{}, f32x16_t{}};
+  const float scale = p.scale_log2;
+
+  auto compute = [&](auto stage_c, int kt) {
+    const uint32_t sk = lds0 + decltype(stage_c)::value * kBStageBytes, sv = sk + kTileBytes;
+    const int k0 = kt * 64;
+    if (p.causal && k0 > wq_last) return;
+    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      bf16x8_t ka[4], va[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ka[ks] = row_frag(sk + row_addr(m, ks, lane));
+        va[ks] = row_frag(sv + row_addr(m, ks, lane));
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_tie(ka);
+      lds_tie(va);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s[m], 0, 0, 0);
+        dp[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp[m], 0, 0, 0);
+      }
+    }
+    const bool interior = (!p.causal || k0 + 63 <= wq_first) && k0 + 64 <= seq;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = __builtin_amdgcn_exp2f(s[m][r] * scale - lq);
+        if (!interior) {
+          const int key = k0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
+          if (key >= seq || (p.causal && key > q)) pr = 0.0f;
+        }
+        dp[m][r] = pr * (dp[m][r] - dl);
+      }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int m = st >> 1, hh = st & 1;
+      const bf16x8_t sf = pack8(dp[m], hh);
+      bf16x8_t ta[2];
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        ta[db] = tr_frag(sk + tr_addr(st, db, 0, lane), sk + tr_addr(st, db, 1, lane));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      lds_tie(ta);
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], sf, dqa[db], 0, 0, 0);
+    }
+  };
+
+  Unroll<0, 2>::run([&](auto jc) {
+    if (decltype(jc)::value < nkt) issue(jc, decltype(jc)::value);
+  });
+  for (int k0 = 0; k0 < nkt; k0 += kBStages) {
+    Unroll<0, kBStages>::run([&](auto jc) {
+      constexpr int J = decltype(jc)::value;
+      const int kt = k0 + J;
+      if (kt < nkt) {
+        if (kt + 1 < nkt) attn_wait_vmcnt<4>();
+        else attn_wait_vmcnt<0>();
+        attn_sync();
+        if (kt + 2 < nkt) issue(std::integral_constant<int, (J + 2) % kBStages>{}, kt + 2);
+        compute(jc, kt);
+      }
+    });
+  }
+
+  if (q < seq) {
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + (row0 + q) * p.ld_dqkv + h * kD;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        uint2 w;
+        w.x = pack_bf16x2(dqa[db][4 * r4] * 0.125f, dqa[db][4 * r4 + 1] * 0.125f);
+        w.y = pack_bf16x2(dqa[db][4 * r4 + 2] * 0.125f, dqa[db][4 * r4 + 3] * 0.125f);
+        *reinterpret_cast<uint2*>(out + 32 * db + 8 * r4 + 4 * half) = w;
+      }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s) {
+  const int64_t bh = p.batch * p.heads;
+  const int64_t rows = p.batch * p.seq * p.heads;
+  hipLaunchKernelGGL(attn_delta_kernel, dim3(static_cast<unsigned>((rows + 255) / 256)), dim3(256),
+                     0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(static_cast<unsigned>(bh * ((p.seq + 127) / 128))),
+                     dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(static_cast<unsigned>(bh * ((p.seq + kQB - 1) / kQB))),
+                     dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s) {
   const int64_t blocks = p.batch * p.heads * ((p.seq + kQB - 1) / kQB);

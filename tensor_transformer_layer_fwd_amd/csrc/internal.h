@@ -69,6 +69,21 @@ struct AttnParams {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
+// Attention core backward: dQKV [batch*seq, 3*heads*64] bf16 ([dQ | dK | dV])
+// from QKV, the forward output C, its gradient dC and the forward lse; delta
+// [batch, heads, seq] fp32 receives rowsum(dC * C).
+struct AttnBwdParams {
+  const void* qkv;
+  const void* c;
+  const void* dc;
+  const float* lse;
+  float* delta;
+  void* dqkv;
+  int64_t batch, seq, heads, ld_qkv, ld_c, ld_dc, ld_dqkv;
+  int causal;
+  float scale_log2;  // log2(e) / sqrt(head_dim)
+};
+
 // Reduction over shards.
 constexpr int kMaxPartials = 16;
 struct ReduceParams {
@@ -139,5 +154,6 @@ hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s);
 hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s);
+hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s);
 
 }  // namespace tpmlp

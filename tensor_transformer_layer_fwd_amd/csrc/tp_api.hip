@@ -279,6 +279,39 @@ int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_
   return hip_status(launch_attention_fwd(a, stream));
 }
 
+int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float* lse,
+                     float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
+                     int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
+                     int64_t ld_dqkv, int causal, int dt, hipStream_t stream) {
+  if (!QKV || !C || !dC || !lse || !delta || !dQKV) return TP_ERR_NULL;
+  if (dt != TP_BF16) return TP_ERR_DTYPE;
+  if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || head_dim != 64) return TP_ERR_SHAPE;
+  const int64_t hd = heads * head_dim;
+  if (ld_qkv < 3 * hd || ld_c < hd || ld_dc < hd || ld_dqkv < 3 * hd) return TP_ERR_SHAPE;
+  auto al = [](const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; };
+  if (!al(QKV, 16) || (ld_qkv & 7) || !al(C, 16) || (ld_c & 7) || !al(dC, 16) || (ld_dc & 7) ||
+      !al(dQKV, 8) || (ld_dqkv & 3) || !al(lse, 4) || !al(delta, 4))
+    return TP_ERR_SHAPE;
+  if (batch * seq > kMaxDim) return TP_ERR_SHAPE;
+  AttnBwdParams a{};
+  a.qkv = QKV;
+  a.c = C;
+  a.dc = dC;
+  a.lse = lse;
+  a.delta = delta;
+  a.dqkv = dQKV;
+  a.batch = batch;
+  a.seq = seq;
+  a.heads = heads;
+  a.ld_qkv = ld_qkv;
+  a.ld_c = ld_c;
+  a.ld_dc = ld_dc;
+  a.ld_dqkv = ld_dqkv;
+  a.causal = causal != 0;
+  a.scale_log2 = static_cast<float>(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
+  return hip_status(launch_attention_bwd(a, stream));
+}
+
 int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, int* splitk,
                  int64_t* k_chunk) {
   if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return TP_ERR_SHAPE;

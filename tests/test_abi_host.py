@@ -162,6 +162,33 @@ def test_attention_validation(lib):
     assert call(ld_c=66) == -2             # not a multiple of 4
 
 
+def test_attention_bwd_validation(lib):
+    """The attention backward rejects bad arguments on the host, before any launch."""
+    import ctypes
+    buf = ctypes.create_string_buffer(4096 + 64)
+    base = (ctypes.addressof(buf) + 63) // 64 * 64
+    q = ctypes.c_void_p(base)
+    args = dict(batch=1, seq=4, heads=1, hd=64, ld_qkv=192, ld_c=64, ld_dc=64, ld_dqkv=192,
+                causal=1, dt=L.TP_BF16)
+
+    def call(qkv=q, c=q, dc=q, lse=q, delta=q, dqkv=q, **kw):
+        a = dict(args, **kw)
+        return lib.tp_attention_bwd(qkv, c, dc, lse, delta, dqkv, a["batch"], a["seq"], a["heads"],
+                                    a["hd"], a["ld_qkv"], a["ld_c"], a["ld_dc"], a["ld_dqkv"],
+                                    a["causal"], a["dt"], None)
+    for name in ("qkv", "c", "dc", "lse", "delta", "dqkv"):
+        assert call(**{name: None}) == -1, name
+    assert call(dt=L.TP_F32) == -3
+    assert call(hd=128) == -2
+    assert call(heads=0) == -2
+    assert call(ld_dqkv=191) == -2         # shorter than the row
+    assert call(ld_dc=60) == -2            # shorter than the row
+    assert call(ld_c=68) == -2             # not a multiple of 8
+    assert call(dc=ctypes.c_void_p(base + 8)) == -2    # not 16-byte aligned
+    assert call(dqkv=ctypes.c_void_p(base + 4)) == -2  # not 8-byte aligned
+    assert call(delta=ctypes.c_void_p(base + 2)) == -2
+
+
 def test_gemm_override(lib):
     """The tuning hook forces a tile where the shape allows it, splits only
     weight gradients, changes the workspace query with the plan and resets."""

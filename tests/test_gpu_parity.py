@@ -580,3 +580,80 @@ def test_attention_fwd_deterministic_and_lse_optional(dev):
         outs.append(C.cpu())
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def _attn_bwd_case(dev, batch, seq, heads, causal, seed, from_oracle=False):
+    import tensor_transformer_layer_fwd_amd as tp
+    from oracle.attention import attention_core_bwd, attention_core_fwd
+    rng = np.random.default_rng(seed)
+    T, hd = batch * seq, heads * 64
+    QKV, QKVr = rand(rng, (T, 3 * hd), 1.0, "bf16")
+    dC, dCr = rand(rng, (T, hd), 1.0, "bf16")
+    x = upload(QKVr, "bf16", dev, pad=8)
+    n = batch * heads * seq
+    if from_oracle:
+        # the backward alone, on the oracle's forward (C rounded to bf16)
+        C_ref, lse_ref = attention_core_fwd(QKV, batch, seq, heads, 64, causal)
+        C = upload(f32_to_bf16_bits(C_ref.astype(np.float32)), "bf16", dev, pad=8)
+        lse = torch.from_numpy(lse_ref.reshape(-1).astype(np.float32)).to(dev)
+    else:
+        Cg = Guarded(T, hd, "bf16", dev, pad=8)
+        C = Cg.view
+        lse = torch.empty(n, device=dev)
+        tp.tp_attention_fwd(x, C, lse, batch, seq, heads, causal=causal)
+    delta = torch.full((n + 8,), float("nan"), device=dev)
+    dQKV = Guarded(T, 3 * hd, "bf16", dev, pad=4)
+    tp.tp_attention_bwd(x, C, upload(dCr, "bf16", dev, pad=8), lse, delta[4:4 + n], dQKV.view,
+                        batch, seq, heads, causal=causal)
+    torch.cuda.synchronize()
+    got = dQKV.value()
+    d = delta.cpu().numpy()
+    assert np.all(np.isnan(d[:4])) and np.all(np.isnan(d[4 + n:])), "delta written out of range"
+    ref = attention_core_bwd(QKV, dC, batch, seq, heads, 64, causal)
+    errs = [err(got[:, i * hd:(i + 1) * hd], ref[:, i * hd:(i + 1) * hd]) for i in range(3)]
+    _say(f"  dQ/dK/dV rel err {errs[0]:.2e} {errs[1]:.2e} {errs[2]:.2e}")
+    return errs
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch,seq,heads,causal", [
+    (1, 1, 2, True), (1, 64, 1, True), (2, 100, 3, True), (2, 100, 3, False),
+    (3, 257, 2, True), (1, 384, 1, False), (1, 130, 1, True),
+    (8, 512, 8, True),    # the attention-projection workload's shard: 8 x 512 tokens, 8 heads
+    (6, 1024, 4, True),   # the ~350M-layer workload's shard: 6 x 1024 tokens, 4 heads
+])
+def test_attention_bwd(dev, batch, seq, heads, causal):
+    """dQKV of the GPU forward -> backward chain against the oracle's gradient
+    of the same attention core (one third at a time)."""
+    _say(f"attention bwd batch={batch} seq={seq} heads={heads} causal={causal}")
+    errs = _attn_bwd_case(dev, batch, seq, heads, causal, batch * 1000 + seq + heads)
+    assert max(errs) <= TOL["bf16"], errs
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_bwd_on_oracle_forward(dev, causal):
+    """The backward fed the oracle's C and lse: its own error, apart from the forward's."""
+    _say(f"attention bwd on the oracle's forward causal={causal}")
+    errs = _attn_bwd_case(dev, 2, 200, 2, causal, 31, from_oracle=True)
+    assert max(errs) <= TOL["bf16"], errs
+
+
+@pytest.mark.gpu
+def test_attention_bwd_deterministic(dev):
+    import tensor_transformer_layer_fwd_amd as tp
+    rng = np.random.default_rng(78)
+    batch, seq, heads = 2, 320, 2
+    T, hd = batch * seq, heads * 64
+    x = upload(rand(rng, (T, 3 * hd), 1.0, "bf16")[1], "bf16", dev)
+    dC = upload(rand(rng, (T, hd), 1.0, "bf16")[1], "bf16", dev)
+    C = torch.empty(T, hd, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(batch * heads * seq, device=dev)
+    tp.tp_attention_fwd(x, C, lse, batch, seq, heads)
+    outs = []
+    for _ in range(3):
+        d = torch.empty(T, 3 * hd, dtype=torch.bfloat16, device=dev)
+        tp.tp_attention_bwd(x, C, dC, lse, torch.empty_like(lse), d, batch, seq, heads)
+        outs.append(d.cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
