@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default="gpt2s")
     ap.add_argument("--extra", default="gpt175b",
                     help="comma-separated workloads also timed and reported under 'extra'")
+    ap.add_argument("--attention", default="attn,gpt350m",
+                    help="comma-separated workloads whose shard attention core (forward and "
+                         "backward) is timed and reported under 'attention'; empty: none")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
@@ -148,6 +151,52 @@ def measured_traffic(call):
     except (OSError, ValueError, KeyError):
         pass
     return None
+
+
+def time_attention(name, reps, with_oracle):
+    """The attention core of one shard of `name` (its micro-batch x seq tokens
+    and the shard's heads of 64), causal, forward and backward, on N(0,1)
+    bf16 inputs. Flops count the unmasked half of the score matrix: 4*L^2*d/2
+    per sequence and head forward (Q K^T and P V), 2.5x that backward (five
+    products). Algorithmic bytes: every tensor read once and written once."""
+    import numpy as np
+    import torch
+    import tensor_transformer_layer_fwd_amd as tp
+    from tp_inputs import get_config
+    cfg = get_config(name)
+    b, L, H = cfg.micro_batch, cfg.seq, cfg.Q // 192
+    T, hd = b * L, H * 64
+    g = torch.Generator(device="cuda:0").manual_seed(1234)
+    x = torch.randn(T, 3 * hd, device="cuda:0", generator=g).to(torch.bfloat16)
+    dC = torch.randn(T, hd, device="cuda:0", generator=g).to(torch.bfloat16)
+    C = torch.empty(T, hd, dtype=torch.bfloat16, device="cuda:0")
+    dx = torch.empty_like(x)
+    lse = torch.empty(b * H * L, device="cuda:0")
+    delta = torch.empty_like(lse)
+    fwd_ms = time_call(lambda: tp.tp_attention_fwd(x, C, lse, b, L, H), reps)
+    bwd_ms = time_call(lambda: tp.tp_attention_bwd(x, C, dC, lse, delta, dx, b, L, H), reps)
+    f_fwd = 4.0 * b * H * L * L * 64 / 2
+    f_bwd = 2.5 * f_fwd
+    by_fwd = T * 3 * hd * 2 + T * hd * 2 + b * H * L * 4
+    by_bwd = T * 3 * hd * 2 + 2 * T * hd * 2 + b * H * L * 4 * 3 + T * 3 * hd * 2
+    rec = {"batch": b, "seq": L, "heads": H, "head_dim": 64, "causal": True}
+    for tag, ms, f, by in (("fwd", fwd_ms, f_fwd, by_fwd), ("bwd", bwd_ms, f_bwd, by_bwd)):
+        t_roof = max(f / (PEAK_BF16_TFLOPS * 1e12), by / (PEAK_HBM_GBS * 1e9))
+        rec[tag] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
+                    "gflop": round(f / 1e9, 3), "bytes": by,
+                    "roofline_us": round(t_roof * 1e6, 2),
+                    "frac_of_roofline": round(t_roof / (ms * 1e-3), 4)}
+    if with_oracle:
+        from oracle.attention import attention_core_bwd, attention_core_fwd
+        xs = x.float().cpu().numpy().astype(np.float64)
+        dcs = dC.float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        attention_core_fwd(xs, b, L, H, 64, True)
+        attention_core_bwd(xs, dcs, b, L, H, 64, True)
+        rec["cpu_oracle_fwd_bwd_ms"] = round((time.perf_counter() - t0) * 1e3, 1)
+    del x, dC, C, dx, lse, delta
+    torch.cuda.empty_cache()
+    return rec
 
 
 def cpu_baseline(cfg, inputs, seconds):
@@ -277,6 +326,11 @@ def main():
         del s2
         torch.cuda.empty_cache()
 
+    attention = {}
+    for name in [w for w in args.attention.split(",") if w]:
+        attention[name] = time_attention(name, args.kernel_reps, not args.no_cpu_baseline)
+        log(f"[bench] attention core {name}: {json.dumps(attention[name])}")
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the float64 oracle on the host for ~{args.cpu_seconds:.0f} s")
@@ -312,6 +366,7 @@ def main():
         "hbm_passes": hbm,
         "cpu_baseline": cpu,
         "extra": extra,
+        "attention": attention,
     }
     print(json.dumps(rec))
 
