@@ -312,6 +312,22 @@ def main():
     log(f"[bench] HBM passes: {json.dumps(hbm)}")
     del u32, ybf
 
+    # the same step with activation recompute: Y_i is not kept across the
+    # step but recomputed from U_i in the fc2 dgrad epilogue
+    recompute = None
+    if cfg.mlp:
+        from tensor_transformer_layer_fwd_amd.shard import ShardStep
+        rs = ShardStep(cfg, inputs, "cuda:0", recompute=True)
+        rs.capture()
+        r_ms, _ = time_steps(rs, args.steps, args.warmup)
+        esz = 2 if cfg.dtype == "bf16" else 4
+        recompute = {"ms_per_step": round(r_ms, 5), "tflops": round(flops / (r_ms * 1e-3) / 1e12, 1),
+                     "vs_stored": round(wall_ms / r_ms, 4),
+                     "activation_bytes_saved_per_shard": cfg.T * cfg.F * esz}
+        log(f"[bench] {cfg.name} with recompute: {json.dumps(recompute)}")
+        del rs
+        torch.cuda.empty_cache()
+
     extra = {}
     for name in [w for w in args.extra.split(",") if w and w != args.workload]:
         c2, _, s2, w2, e2, f2, t2 = run_workload(name, max(5, args.steps // 5), 3)
@@ -367,6 +383,7 @@ def main():
         "cpu_baseline": cpu,
         "extra": extra,
         "attention": attention,
+        "recompute": recompute,
     }
     print(json.dumps(rec))
 

@@ -129,6 +129,29 @@ int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act,
                         hipStream_t stream);
 
 /*
+ * Row-parallel dgrad with activation recompute. The "Megatron" page
+ * ("activation recomputation", under its training optimisations) trades
+ * compute for memory: activations that the forward does not keep are computed
+ * again in the backward. With this call a step keeps only the pre-activation
+ * U_i from the forward; Y_i = GeLU(U_i), which the fc2 weight gradient needs,
+ * is recomputed in the epilogue of the fc2 dgrad, which loads U_i anyway:
+ *
+ *   dU_i = (dZ B_i^T) * GeLU'(U_i)     exactly as tp_linear_bwd_dgrad
+ *   Y    = GeLU(U_i)                   from the stored (rounded) U_i
+ *
+ * Y is then the In operand of tp_linear_bwd_wgrad for B_i. Compared with the
+ * forward's Y_i it differs by the rounding of U_i to dt before the GeLU.
+ *
+ * dOut, W, U, dIn as tp_linear_bwd_dgrad with act = TP_ACT_GELU_TANH (other
+ * values: TP_ERR_ACT) and out_dt = dt
+ * Y    [T, k], ld_y, dtype dt; must not overlap U or dIn
+ */
+int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U, int act,
+                                  void* dIn, void* Y, int64_t T, int64_t k, int64_t n,
+                                  int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_din,
+                                  int64_t ld_y, int dt, hipStream_t stream);
+
+/*
  * Weight and bias gradients (wgrad) of Out = In W + c for a weight stored
  * [k, n] (derivative of the forward definitions; not on the pages).
  *

@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     tp_gemm_plan,
     tp_last_hip_error,
     tp_linear_bwd_dgrad,
+    tp_linear_bwd_dgrad_recompute,
     tp_linear_bwd_wgrad,
     tp_linear_bwd_wgrad_workspace_size,
     tp_reduce_partials,

@@ -42,6 +42,8 @@ SIGNATURES = {
                             ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int64)]),
     "tp_attention_fwd": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int, _int,
                                 _vp]),
+    "tp_linear_bwd_dgrad_recompute": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64,
+                                             _i64, _i64, _i64, _i64, _i64, _int, _vp]),
     "tp_attention_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _i64, _i64, _int, _int, _vp]),
     "tp_set_gemm_override": (_int, [_int, _int]),
@@ -148,6 +150,15 @@ def tp_linear_bwd_dgrad(dOut, W, U, dIn, act="none", stream=None):
     _check("tp_linear_bwd_dgrad", lib().tp_linear_bwd_dgrad(
         _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(dIn), T, k, n, _ld(dOut), _ld(W), ld_u,
         _ld(dIn), _dt(dOut), _dt(dIn), _stream(stream)))
+
+
+def tp_linear_bwd_dgrad_recompute(dOut, W, U, dIn, Y, act="gelu", stream=None):
+    """dIn = (dOut W^T) * act'(U) and Y = act(U) recomputed from the saved U."""
+    T, n = dOut.shape
+    k = W.shape[0]
+    _check("tp_linear_bwd_dgrad_recompute", lib().tp_linear_bwd_dgrad_recompute(
+        _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(dIn), _ptr(Y), T, k, n, _ld(dOut), _ld(W),
+        _ld(U), _ld(dIn), _ld(Y), _dt(dOut), _stream(stream)))
 
 
 def tp_linear_bwd_wgrad_workspace_size(T: int, k: int, n: int, dt: int) -> int:

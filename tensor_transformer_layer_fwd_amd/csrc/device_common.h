@@ -85,10 +85,11 @@ __device__ __forceinline__ void epilogue_elem(const GemmParams& p, int64_t row, 
   const int64_t o = row * p.ldc + col;
   if (p.epi == EPI_BIAS_ACT) {
     if (p.bias) v += load_elem(p.bias, col, in_bf16);
-    if (p.c2) store_elem(p.c2, o, v, p.out_bf16);
+    if (p.c2) store_elem(p.c2, row * p.ldc2 + col, v, p.out_bf16);
     store_elem(p.c, o, apply_act(p.act, v), p.out_bf16);
   } else if (p.epi == EPI_DACT) {
     float u = load_elem(p.u, row * p.ldu + col, in_bf16);
+    if (p.c2) store_elem(p.c2, row * p.ldc2 + col, apply_act(p.act, u), p.out_bf16);
     store_elem(p.c, o, v * apply_act_grad(p.act, u), p.out_bf16);
   } else {
     if (p.accumulate && !p.out_bf16) v += static_cast<const float*>(p.c)[o];
@@ -106,7 +107,7 @@ __device__ __forceinline__ bool aligned16(const void* ptr) {
 }
 
 __device__ __forceinline__ bool epilogue_vec_ok(const GemmParams& p) {
-  return aligned16(p.c) && (p.ldc & 7) == 0 && (!p.c2 || aligned16(p.c2)) &&
+  return aligned16(p.c) && (p.ldc & 7) == 0 && (!p.c2 || (aligned16(p.c2) && (p.ldc2 & 7) == 0)) &&
          (!p.bias || aligned16(p.bias)) && (!p.u || (aligned16(p.u) && (p.ldu & 7) == 0));
 }
 
@@ -154,13 +155,19 @@ __device__ __forceinline__ void epilogue_vec8(const GemmParams& p, int64_t row, 
 #pragma unroll
       for (int q = 0; q < 8; ++q) v[q] += b[q];
     }
-    if (p.c2) store8(p.c2, o, v, p.out_bf16);
+    if (p.c2) store8(p.c2, row * p.ldc2 + col, v, p.out_bf16);
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] = apply_act(p.act, v[q]);
     store8(p.c, o, v, p.out_bf16);
   } else if (p.epi == EPI_DACT) {
     float u[8];
     load8_bf16(p.u, row * p.ldu + col, u);
+    if (p.c2) {
+      float y[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) y[q] = apply_act(p.act, u[q]);
+      store8(p.c2, row * p.ldc2 + col, y, p.out_bf16);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) v[q] *= apply_act_grad(p.act, u[q]);
     store8(p.c, o, v, p.out_bf16);

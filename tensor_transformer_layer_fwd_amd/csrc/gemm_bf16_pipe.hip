@@ -483,16 +483,25 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
         if constexpr (EK == kEpiBiasGelu) {
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] += bias8[C][q];
-          store8(p.c2, o, v, 1);
+          store8(p.c2, row * p.ldc2 + col, v, 1);
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] = gelu_tanh(v[q]);
         } else if constexpr (EK == kEpiDGelu) {
           const u32x4_t w = upre[i & 1][P];
+          float u[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            v[2 * q] *= gelu_tanh_grad(__uint_as_float(w[q] << 16));
-            v[2 * q + 1] *= gelu_tanh_grad(__uint_as_float(w[q] & 0xffff0000u));
+            u[2 * q] = __uint_as_float(w[q] << 16);
+            u[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
           }
+          if (p.c2) {  // recompute of the activation from the saved U
+            float y[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) y[q] = gelu_tanh(u[q]);
+            store8(p.c2, row * p.ldc2 + col, y, 1);
+          }
+#pragma unroll
+          for (int q = 0; q < 8; ++q) v[q] *= gelu_tanh_grad(u[q]);
         }
         store8(p.c, o, v, 1);
       }
@@ -580,13 +589,14 @@ int pipe_epilogue_kind(const GemmParams& p) {
     case EPI_BIAS_ACT:
       // with no activation, no bias and no saved pre-activation it is a plain store
       if (p.act == ACT_NONE && !p.bias && !p.c2 && p.out_bf16 && p.a_kcontig) return kEpiBF16;
-      if (p.act == ACT_GELU && p.out_bf16 && p.c2 && a16(p.c2) && (!p.bias || a16(p.bias)) &&
+      if (p.act == ACT_GELU && p.out_bf16 && p.c2 && a16(p.c2) && p.ldc2 % 8 == 0 &&
+          (!p.bias || a16(p.bias)) &&
           p.a_kcontig && !p.b_kcontig)
         return kEpiBiasGelu;
       return kEpiNone;
     case EPI_DACT:
       if (p.act == ACT_GELU && p.out_bf16 && p.u && a16(p.u) && p.ldu % 8 == 0 && p.a_kcontig &&
-          p.b_kcontig)
+          p.b_kcontig && (!p.c2 || (a16(p.c2) && p.ldc2 % 8 == 0)))
         return kEpiDGelu;
       return kEpiNone;
     default:

@@ -10,7 +10,7 @@ namespace tpmlp {
 enum Epilogue : int {
   EPI_STORE = 0,     // C (+)= acc
   EPI_BIAS_ACT = 1,  // U = acc + bias; C = act(U); C2 = U (if C2)
-  EPI_DACT = 2,      // C = acc * act'(Uin)
+  EPI_DACT = 2,      // C = acc * act'(Uin); C2 = act(Uin) (if C2: recompute)
 };
 
 enum Act : int { ACT_NONE = 0, ACT_GELU = 1 };
@@ -34,11 +34,12 @@ struct GemmParams {
   const void* a;
   const void* b;
   void* c;         // output [M,N], ldc; fp32 or bf16 (out_bf16)
-  void* c2;        // EPI_BIAS_ACT: pre-activation output, ldc (same dtype as c); may be null
+  void* c2;        // EPI_BIAS_ACT: pre-activation U; EPI_DACT: recomputed act(Uin);
+                   // row stride ldc2, dtype of c; may be null
   const void* bias;  // EPI_BIAS_ACT: [N], dtype of the operands; may be null
   const void* u;     // EPI_DACT: saved pre-activation [M,N], ldu, dtype of the operands
   int64_t M, N, K;
-  int64_t lda, ldb, ldc, ldu;
+  int64_t lda, ldb, ldc, ldu, ldc2;
   int epi, act;
   int out_bf16;    // output dtype of c / c2
   int accumulate;  // EPI_STORE with fp32 output: C += acc

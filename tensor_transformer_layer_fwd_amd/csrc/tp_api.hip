@@ -96,6 +96,7 @@ int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, voi
   p.lda = ld_x;
   p.ldb = ld_a;
   p.ldc = ld_y;
+  p.ldc2 = ld_y;
   p.epi = EPI_BIAS_ACT;
   p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
   p.out_bf16 = dt == TP_BF16;
@@ -155,6 +156,37 @@ int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act,
   p.epi = act != TP_ACT_NONE ? EPI_DACT : EPI_STORE;
   p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
   p.out_bf16 = out_dt == TP_BF16;
+  p.a_kcontig = 1;  // dOut [T, n]
+  p.b_kcontig = 1;  // W [k, n] read as W^T: K (= n) contiguous
+  return run_gemm(p, dt, false, 0, stream);
+}
+
+int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U, int act,
+                                  void* dIn, void* Y, int64_t T, int64_t k, int64_t n,
+                                  int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_din,
+                                  int64_t ld_y, int dt, hipStream_t stream) {
+  if (!dOut || !W || !U || !dIn || !Y) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (act != TP_ACT_GELU_TANH) return TP_ERR_ACT;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_dout < n || ld_w < n || ld_din < k || ld_u < k || ld_y < k) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = dOut;
+  p.b = W;
+  p.c = dIn;
+  p.c2 = Y;
+  p.u = U;
+  p.M = T;
+  p.N = k;
+  p.K = n;
+  p.lda = ld_dout;
+  p.ldb = ld_w;
+  p.ldc = ld_din;
+  p.ldc2 = ld_y;
+  p.ldu = ld_u;
+  p.epi = EPI_DACT;
+  p.act = ACT_GELU;
+  p.out_bf16 = dt == TP_BF16;
   p.a_kcontig = 1;  // dOut [T, n]
   p.b_kcontig = 1;  // W [k, n] read as W^T: K (= n) contiguous
   return run_gemm(p, dt, false, 0, stream);

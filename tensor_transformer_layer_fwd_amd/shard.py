@@ -8,6 +8,12 @@ The backward (not on the pages; derivatives of the same definitions) runs the
 row-parallel dgrad with the GeLU derivative, both wgrads with bias gradients,
 the column-parallel dgrad to a partial dX_i, and the sum of the partials.
 
+With recompute=True the step keeps only U_i of the fc1 output across the
+step (the activation recomputation of the "Megatron" page's training
+optimisations): Y_i lives in one transient buffer that fc2's forward reads, and
+the backward recomputes it from U_i in the fc2 dgrad epilogue
+(tp_linear_bwd_dgrad_recompute) just before fc2's weight gradient reads it.
+
 All p shards of a workload run one after another on the same device and
 stream; the shards' weights are column / row views of the unsharded tensors
 (no copies). torch provides device memory and streams only; every arithmetic
@@ -38,8 +44,9 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 class ShardStep:
     """Device buffers of one workload and the calls of one fwd+bwd step."""
 
-    def __init__(self, cfg, inputs: dict, device="cuda"):
+    def __init__(self, cfg, inputs: dict, device="cuda", recompute=False):
         self.cfg = cfg
+        self.recompute = bool(recompute and cfg.mlp)
         self.device = torch.device(device)
         self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.tp_dt = L.TP_BF16 if cfg.dtype == "bf16" else L.TP_F32
@@ -55,7 +62,8 @@ class ShardStep:
             F = cfg.F
             for i in shards:
                 self.out[f"U_{i}"] = torch.empty(T, F, **act)
-                self.out[f"Y_{i}"] = torch.empty(T, F, **act)
+                if not self.recompute:
+                    self.out[f"Y_{i}"] = torch.empty(T, F, **act)
                 self.out[f"Zp_{i}"] = torch.empty(T, h, **f32)
                 self.out[f"dU_{i}"] = torch.empty(T, F, **act)
                 self.out[f"dB_{i}"] = torch.empty(F, h, **f32)
@@ -63,6 +71,9 @@ class ShardStep:
                 self.out[f"dXp_{i}"] = torch.empty(T, h, **f32)
                 if cfg.has_bias:
                     self.out[f"da_{i}"] = torch.empty(F, **f32)
+            if self.recompute:
+                # the forward's Y_i, then the backward's recomputed Y_i, shard by shard
+                self.out["Yt"] = torch.empty(T, F, **act)
             if cfg.has_bias:
                 self.out["db"] = torch.empty(h, **f32)
             if len(shards) == cfg.p:
@@ -101,14 +112,17 @@ class ShardStep:
         return t[i * width:(i + 1) * width]
 
     # ------------------------------------------------------------------ step
+    def _y(self, i):
+        return self.out["Yt"] if self.recompute else self.out[f"Y_{i}"]
+
     def mlp_forward(self):
         cfg, o, inp = self.cfg, self.out, self.inp
         F = cfg.F
         for i in cfg.shards:
             a_i = self._col("a", i, F) if cfg.has_bias else None
-            L.tp_column_linear_fwd(inp["X"], self._col("A", i, F), a_i, o[f"Y_{i}"], o[f"U_{i}"],
+            L.tp_column_linear_fwd(inp["X"], self._col("A", i, F), a_i, self._y(i), o[f"U_{i}"],
                                    act="gelu")
-            L.tp_row_linear_fwd_partial(o[f"Y_{i}"], self._row("B", i, F), o[f"Zp_{i}"])
+            L.tp_row_linear_fwd_partial(self._y(i), self._row("B", i, F), o[f"Zp_{i}"])
         if "Z" in o:
             L.tp_reduce_partials([o[f"Zp_{i}"] for i in cfg.shards],
                                  inp["b"] if cfg.has_bias else None, o["Z"])
@@ -118,8 +132,12 @@ class ShardStep:
         F = cfg.F
         for n, i in enumerate(cfg.shards):
             B_i, A_i = self._row("B", i, F), self._col("A", i, F)
-            L.tp_linear_bwd_dgrad(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"], act="gelu")
-            L.tp_linear_bwd_wgrad(o[f"Y_{i}"], inp["dZ"], o[f"dB_{i}"],
+            if self.recompute:
+                L.tp_linear_bwd_dgrad_recompute(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"],
+                                                o["Yt"])
+            else:
+                L.tp_linear_bwd_dgrad(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"], act="gelu")
+            L.tp_linear_bwd_wgrad(self._y(i), inp["dZ"], o[f"dB_{i}"],
                                   o["db"] if (cfg.has_bias and n == 0) else None,
                                   workspace=self.workspace)
             L.tp_linear_bwd_dgrad(o[f"dU_{i}"], A_i, None, o[f"dXp_{i}"], act="none")

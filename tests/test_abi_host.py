@@ -189,6 +189,28 @@ def test_attention_bwd_validation(lib):
     assert call(delta=ctypes.c_void_p(base + 2)) == -2
 
 
+def test_dgrad_recompute_validation(lib):
+    """The recompute dgrad rejects bad arguments on the host, before any launch."""
+    import ctypes
+    buf = ctypes.create_string_buffer(4096 + 64)
+    q = ctypes.c_void_p((ctypes.addressof(buf) + 63) // 64 * 64)
+    args = dict(T=4, k=8, n=8, ld_dout=8, ld_w=8, ld_u=8, ld_din=8, ld_y=8, dt=L.TP_BF16,
+                act=L.TP_ACT_GELU_TANH)
+
+    def call(u=q, y=q, **kw):
+        a = dict(args, **kw)
+        return lib.tp_linear_bwd_dgrad_recompute(q, q, u, a["act"], q, y, a["T"], a["k"], a["n"],
+                                                 a["ld_dout"], a["ld_w"], a["ld_u"], a["ld_din"],
+                                                 a["ld_y"], a["dt"], None)
+    assert call(u=None) == -1
+    assert call(y=None) == -1
+    assert call(act=L.TP_ACT_NONE) == -4
+    assert call(dt=7) == -3
+    assert call(ld_y=7) == -2
+    assert call(ld_u=7) == -2
+    assert call(k=0) == -2
+
+
 def test_gemm_override(lib):
     """The tuning hook forces a tile where the shape allows it, splits only
     weight gradients, changes the workspace query with the plan and resets."""

@@ -657,3 +657,48 @@ def test_attention_bwd_deterministic(dev):
         outs.append(d.cpu())
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("name,mb,seq", [("tiny", 8, 64), ("gpt2s", 1, 680), ("gpt350m", 1, 520)])
+def test_workload_recompute(dev, name, mb, seq):
+    """The step with activation recompute: every output the oracle defines
+    except the Y_i it no longer keeps, and the recomputed Y of the last shard
+    (left in the transient buffer) against the oracle's Y."""
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    cfg = dataclasses.replace(get_config(name), micro_batch=mb, seq=seq)
+    _say(f"workload {name} with recompute T={cfg.T}")
+    inputs = make_inputs(cfg)
+    step = ShardStep(cfg, inputs, dev, recompute=True)
+    step.run_eager()
+    got = step.results()
+    ref = oracle.run_config(cfg, inputs)
+    assert not any(k.startswith("Y_") for k in got)
+    last = cfg.shards[-1]
+    y_ref = ref[f"Y_{last}"]
+    ref = {k: v for k, v in ref.items() if not k.startswith("Y_")}
+    worst = _compare_all(cfg, got, ref, TOL[cfg.dtype])
+    e = err(got["Yt"], y_ref)
+    _say(f"  worst rel err {worst[0]:.3e} ({worst[1]}); recomputed Y {e:.3e}")
+    assert e <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("dt", DTS)
+@pytest.mark.parametrize("T,k,n", [(300, 129, 200), (512, 256, 384), (4096, 1536, 768)])
+def test_linear_bwd_dgrad_recompute(dev, dt, T, k, n):
+    """dU equals tp_linear_bwd_dgrad's bitwise; Y = GeLU(U) against the oracle's
+    GeLU of the same stored U; guards around both outputs."""
+    import tensor_transformer_layer_fwd_amd as tp
+    rng = np.random.default_rng(T + k + n)
+    dZ, dZr = rand(rng, (T, n), 1.0, dt)
+    B, Br = rand(rng, (k, n), 0.05, dt)
+    U, Ur = rand(rng, (T, k), 2.0, dt)
+    dZd, Bd, Ud = upload(dZr, dt, dev, pad=8), upload(Br, dt, dev), upload(Ur, dt, dev, pad=16)
+    dU = Guarded(T, k, dt, dev, pad=8)
+    Y = Guarded(T, k, dt, dev, pad=24)
+    tp.tp_linear_bwd_dgrad_recompute(dZd, Bd, Ud, dU.view, Y.view)
+    dU2 = torch.empty(T, k, dtype=dU.tdt, device=dev)
+    tp.tp_linear_bwd_dgrad(dZd, Bd, Ud, dU2, act="gelu")
+    torch.cuda.synchronize()
+    assert torch.equal(dU.view, dU2)
+    assert err(dU.value(), oracle.linear_bwd_dgrad(dZ, B, U, "gelu")) <= TOL[dt]
+    assert err(Y.value(), oracle.gelu_tanh(U)) <= TOL[dt]
