@@ -69,6 +69,9 @@ typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 
 typedef enum { TP_ACT_NONE = 0, TP_ACT_GELU_TANH = 1 } tp_act;
 
+/* FP8 code formats (OCP 8-bit floats): E4M3 (largest finite 448), E5M2 (57344) */
+typedef enum { TP_FP8_E4M3 = 0, TP_FP8_E5M2 = 1 } tp_fp8_format;
+
 /*
  * Column-parallel forward of shard i ("Megatron" page, "Tensor Parallelism /
  * mathematical principles", the column split Y = [X A_1, .., X A_p]; applied to
@@ -264,6 +267,88 @@ int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float
                      float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
                      int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
                      int64_t ld_dqkv, int causal, int dt, hipStream_t stream);
+
+/*
+ * FP8 variant of the shard GEMMs. The "Megatron" page ("mixed-precision
+ * training") trains in FP8 besides FP16/BF16, and the "Megatron-LM
+ * quick-start" page ("performance optimisation") recommends it; neither fixes
+ * the format or the scaling. Here: OCP E4M3 for weights and activations,
+ * E4M3 or E5M2 for gradients, each tensor with its own current scale
+ * s = fmax / amax(tensor). The GEMMs run on gfx950's FP8 matrix cores
+ * (v_mfma_f32_32x32x64_f8f6f4, fp32 accumulation) and multiply the
+ * accumulators by the two 1/s factors before their epilogue. Both operands of
+ * every FP8 product are K-contiguous codes, so the quantiser writes X or X^T
+ * as each product needs it.
+ *
+ * Shapes: every M, N and K of an FP8 product must be a multiple of 128, the
+ * code operands 16-byte aligned with row strides (ld, in codes = bytes) a
+ * multiple of 16 (TP_ERR_SHAPE otherwise). Scale factors are device fp32
+ * scalars written by tp_fp8_quantize.
+ */
+
+/* Bytes of workspace tp_fp8_quantize needs (per-block maxima; 4 KiB). */
+int tp_fp8_quantize_workspace_size(int64_t rows, int64_t cols, size_t* bytes);
+
+/*
+ * Per-tensor current scaling of X [rows, cols] (ld_x, dtype dt):
+ *   s = fmax / max|X| in fp32 (1 when X is all zeros),
+ *   code = nearest value of `fmt`, ties to even, of clamp(x * s, -fmax, fmax),
+ *   scale_inv[0] = 1 / s (device fp32 scalar, for the GEMMs).
+ * Q receives the codes of X ([rows, cols], ld_q >= cols) or, with transpose,
+ * of X^T ([cols, rows], ld_q >= rows). The maximum is order-independent, so
+ * the result is reproducible. X must hold finite values. Two launches.
+ */
+int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt, int fmt,
+                    int transpose, void* Q, int64_t ld_q, float* scale_inv, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP8 column-parallel forward: Y_i = act(X A_i + a_i) with U_i saved, as
+ * tp_column_linear_fwd, from Xq = codes of X [T, h] (E4M3) and Atq = codes of
+ * A_i^T [n, h] (E4M3, quantised with transpose). Y_i, U_i and bias_i bf16.
+ * act TP_ACT_NONE requires bias_i and U_i NULL (a plain bf16 store).
+ */
+int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
+                             const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
+                             int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
+                             int64_t ld_y, int act, hipStream_t stream);
+
+/*
+ * FP8 row-parallel forward partial: Zp_i = Y_i B_i (fp32 [T, h]) from
+ * Yq = codes of Y_i [T, k] (E4M3) and Btq = codes of B_i^T [h, k] (E4M3).
+ */
+int tp_fp8_row_linear_fwd_partial(const void* Yq, const void* Btq, const float* y_scale_inv,
+                                  const float* b_scale_inv, float* Zp_i, int64_t T, int64_t k,
+                                  int64_t h, int64_t ld_y, int64_t ld_bt, int64_t ld_z,
+                                  hipStream_t stream);
+
+/*
+ * FP8 dgrad: dIn = (dOut W^T) [* act'(U)] as tp_linear_bwd_dgrad, from
+ * dOutq = codes of dOut [T, n] (dout_fmt) and Wq = codes of the weight as
+ * stored, [k, n] (E4M3). act TP_ACT_GELU_TANH needs U (bf16 [T, k]) and
+ * out_dt TP_BF16; act NONE writes dIn in out_dt (TP_F32 for a dX partial).
+ */
+int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
+                            const float* w_scale_inv, int dout_fmt, const void* U, int act,
+                            void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
+                            int64_t ld_w, int64_t ld_u, int64_t ld_din, int out_dt,
+                            hipStream_t stream);
+
+/* Workspace bytes of tp_fp8_linear_bwd_wgrad (split-K partials and bias sums). */
+int tp_fp8_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, size_t* bytes);
+
+/*
+ * FP8 wgrad: dW = In^T dOut (fp32 [k, n], overwritten) from Intq = codes of
+ * In^T [k, T] (E4M3) and dOuttq = codes of dOut^T [n, T] (dout_fmt), both
+ * quantised with transpose. K = T may be split, with partials in the
+ * workspace and a fixed-order fix-up. With dbias non-NULL, dbias = column sums
+ * of the unquantised dOut (bf16 [T, n], ld_dout), as tp_linear_bwd_wgrad.
+ */
+int tp_fp8_linear_bwd_wgrad(const void* Intq, const void* dOuttq, const float* in_scale_inv,
+                            const float* dout_scale_inv, int dout_fmt, float* dW,
+                            const void* dOut, float* dbias, int64_t T, int64_t k, int64_t n,
+                            int64_t ld_int, int64_t ld_doutt, int64_t ld_dw, int64_t ld_dout,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Which GEMM kernel configuration the library uses for a bf16 product

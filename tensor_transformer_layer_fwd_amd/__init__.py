@@ -14,6 +14,15 @@ from ._lib import (  # noqa: F401
     tp_attention_bwd,
     tp_attention_fwd,
     tp_bias_act,
+    TP_FP8_E4M3,
+    TP_FP8_E5M2,
+    tp_fp8_column_linear_fwd,
+    tp_fp8_linear_bwd_dgrad,
+    tp_fp8_linear_bwd_wgrad,
+    tp_fp8_linear_bwd_wgrad_workspace_size,
+    tp_fp8_quantize,
+    tp_fp8_quantize_workspace_size,
+    tp_fp8_row_linear_fwd_partial,
     tp_column_linear_fwd,
     tp_gemm_plan,
     tp_last_hip_error,

@@ -44,6 +44,19 @@ SIGNATURES = {
                                 _vp]),
     "tp_linear_bwd_dgrad_recompute": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64,
                                              _i64, _i64, _i64, _i64, _i64, _int, _vp]),
+    "tp_fp8_quantize_workspace_size": (_int, [_i64, _i64, ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_fp8_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _int, _int, _vp, _i64, _vp, _vp,
+                               ctypes.c_size_t, _vp]),
+    "tp_fp8_column_linear_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                        _i64, _i64, _i64, _int, _vp]),
+    "tp_fp8_row_linear_fwd_partial": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                                             _i64, _i64, _vp]),
+    "tp_fp8_linear_bwd_dgrad": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _int, _vp, _i64, _i64,
+                                       _i64, _i64, _i64, _i64, _i64, _int, _vp]),
+    "tp_fp8_linear_bwd_wgrad_workspace_size": (_int, [_i64, _i64, _i64,
+                                                      ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_fp8_linear_bwd_wgrad": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _vp, _vp, _i64, _i64,
+                                       _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_size_t, _vp]),
     "tp_attention_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _i64, _i64, _int, _int, _vp]),
     "tp_set_gemm_override": (_int, [_int, _int]),
@@ -221,6 +234,73 @@ def tp_attention_bwd(QKV, C, dC, lse, delta, dQKV, batch: int, seq: int, heads: 
     _check("tp_attention_bwd", lib().tp_attention_bwd(
         _ptr(QKV), _ptr(C), _ptr(dC), _ptr(lse), _ptr(delta), _ptr(dQKV), batch, seq, heads, 64,
         _ld(QKV), _ld(C), _ld(dC), _ld(dQKV), int(bool(causal)), _dt(QKV), _stream(stream)))
+
+
+TP_FP8_E4M3, TP_FP8_E5M2 = 0, 1
+
+
+def _fmt(fmt) -> int:
+    return {"e4m3": TP_FP8_E4M3, "e5m2": TP_FP8_E5M2, 0: 0, 1: 1}[fmt]
+
+
+def tp_fp8_quantize_workspace_size(rows: int, cols: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_fp8_quantize_workspace_size",
+           lib().tp_fp8_quantize_workspace_size(rows, cols, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_fp8_quantize(X, Q, scale_inv, workspace, fmt="e4m3", transpose=False, stream=None):
+    """Codes of X (or X^T) into the uint8 tensor Q; scale_inv (fp32 [1]) = 1/s."""
+    rows, cols = X.shape
+    _check("tp_fp8_quantize", lib().tp_fp8_quantize(
+        _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), int(bool(transpose)), _ptr(Q), _ld(Q),
+        _ptr(scale_inv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def tp_fp8_column_linear_fwd(Xq, Atq, x_si, a_si, bias, Y, U, act="gelu", stream=None):
+    T, h = Xq.shape
+    n = Atq.shape[0]
+    _check("tp_fp8_column_linear_fwd", lib().tp_fp8_column_linear_fwd(
+        _ptr(Xq), _ptr(Atq), _ptr(x_si), _ptr(a_si), _ptr(bias), _ptr(Y), _ptr(U), T, h, n,
+        _ld(Xq), _ld(Atq), _ld(Y), _act(act), _stream(stream)))
+
+
+def tp_fp8_row_linear_fwd_partial(Yq, Btq, y_si, b_si, Zp, stream=None):
+    T, k = Yq.shape
+    h = Btq.shape[0]
+    _check("tp_fp8_row_linear_fwd_partial", lib().tp_fp8_row_linear_fwd_partial(
+        _ptr(Yq), _ptr(Btq), _ptr(y_si), _ptr(b_si), _ptr(Zp), T, k, h, _ld(Yq), _ld(Btq),
+        _ld(Zp), _stream(stream)))
+
+
+def tp_fp8_linear_bwd_dgrad(dOutq, Wq, d_si, w_si, dIn, U=None, act="none", dout_fmt="e5m2",
+                            stream=None):
+    T, n = dOutq.shape
+    k = Wq.shape[0]
+    ld_u = _ld(U) if U is not None else k
+    _check("tp_fp8_linear_bwd_dgrad", lib().tp_fp8_linear_bwd_dgrad(
+        _ptr(dOutq), _ptr(Wq), _ptr(d_si), _ptr(w_si), _fmt(dout_fmt), _ptr(U), _act(act),
+        _ptr(dIn), T, k, n, _ld(dOutq), _ld(Wq), ld_u, _ld(dIn), _dt(dIn), _stream(stream)))
+
+
+def tp_fp8_linear_bwd_wgrad_workspace_size(T: int, k: int, n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_fp8_linear_bwd_wgrad_workspace_size",
+           lib().tp_fp8_linear_bwd_wgrad_workspace_size(T, k, n, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_fp8_linear_bwd_wgrad(Intq, dOuttq, in_si, d_si, dW, dOut=None, dbias=None,
+                            dout_fmt="e5m2", workspace=None, stream=None):
+    k, T = Intq.shape
+    n = dOuttq.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tp_fp8_linear_bwd_wgrad", lib().tp_fp8_linear_bwd_wgrad(
+        _ptr(Intq), _ptr(dOuttq), _ptr(in_si), _ptr(d_si), _fmt(dout_fmt), _ptr(dW), _ptr(dOut),
+        _ptr(dbias), T, k, n, _ld(Intq), _ld(dOuttq), _ld(dW),
+        _ld(dOut) if dOut is not None else n, _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def tp_set_gemm_override(tile: int = 0, splitk: int = 1) -> None:

@@ -44,6 +44,8 @@ namespace {
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 template <int J, int BYTES>
 __device__ __forceinline__ uint8_t* stage_buf() {
@@ -51,7 +53,7 @@ __device__ __forceinline__ uint8_t* stage_buf() {
   return buf;
 }
 
-__device__ __forceinline__ void copy16_to_lds(const uint16_t* g, uint8_t* lds) {
+__device__ __forceinline__ void copy16_to_lds(const void* g, uint8_t* lds) {
   // address-space casts (global = 1, LDS = 3) need C-style casts
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                    (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
@@ -74,8 +76,8 @@ __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
 
 // Wait for this wave's outstanding LDS reads; the fragments pass through the
 // statement so that no instruction reading them is scheduled before the wait.
-template <int NF>
-__device__ __forceinline__ void lds_fence(bf16x8_t (&f)[NF]) {
+template <typename FT, int NF>
+__device__ __forceinline__ void lds_fence(FT (&f)[NF]) {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
   for (int i = 0; i < NF; ++i) asm volatile("" : "+v"(f[i]));
@@ -191,18 +193,76 @@ struct Operand {
   }
 };
 
+// FP8 operand, K-contiguous codes: a K-tile is 128 codes, one 128-byte line
+// per row, swizzled like the 64-wide bf16 K-tile (same bytes per row). A
+// v_mfma_f32_32x32x64_f8f6f4 operand is 32 bytes per lane: row R0 + lane%32,
+// K bytes 64*ks + 32*(lane/32) .. +31, read as two 16-byte chunks. Which K a
+// byte position feeds inside the instruction does not matter: A and B use the
+// same positions, and a dot product is invariant under a common permutation
+// of K.
+template <int ROWS, int NW>
+struct OperandF8 {
+  static constexpr int BK = 128;
+  static constexpr int BYTES = ROWS * BK;
+  static constexpr int NWIN = BYTES / 1024;
+  static constexpr int NB = NWIN / NW;
+  static constexpr int EXTRA = NWIN % NW;
+  static_assert(NB >= 1 && NWIN * 1024 == BYTES, "tile / waves mismatch");
+
+  const uint8_t* ptr[NB + (EXTRA > 0)];
+
+  __device__ __forceinline__ void init(const uint8_t* base, int64_t ld, int64_t r0, int64_t k0,
+                                       int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < NB + (EXTRA > 0); ++q) {
+      const int win = q < NB ? q * NW + wave : (wave < EXTRA ? NB * NW + wave : 0);
+      const int byte = win * 1024 + lane * 16;
+      const int r = byte / BK;
+      const int c = ((byte % BK) >> 4) ^ kswz<64>(r);
+      ptr[q] = base + (r0 + r) * ld + k0 + c * 16;
+    }
+  }
+  __device__ __forceinline__ void issue(uint8_t* lds, int wave) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      copy16_to_lds(ptr[q], lds + (q * NW + wave) * 1024);
+      ptr[q] += BK;
+    }
+  }
+  __device__ __forceinline__ void issue_extra(uint8_t* lds, int wave, bool extra) {
+    if constexpr (EXTRA > 0) {
+      if (extra) copy16_to_lds(ptr[NB], lds + (NB * NW + wave) * 1024);
+      ptr[NB] += BK;
+    }
+  }
+  __device__ __forceinline__ static i32x8_t frag(const uint8_t* lds, int R0, int ks, int lane) {
+    const int r = R0 + (lane & 31);
+    const int c = 4 * ks + 2 * (lane >> 5);
+    const uint32_t row = lds_addr(lds) + r * BK;
+    const uint32_t a0 = row + ((c ^ kswz<64>(r)) << 4), a1 = row + (((c + 1) ^ kswz<64>(r)) << 4);
+    i32x4_t lo, hi;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(lo) : "v"(a0));
+    asm volatile("ds_read_b128 %0, %1" : "=v"(hi) : "v"(a1));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK>
+// F8 = 0: bf16 operands; F8 = 1 + fmt_a + 2 * fmt_b: FP8 codes (both operands
+// K-contiguous, BK = 128 codes), fmt 0 = E4M3, 1 = E5M2.
+template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams p) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
   static_assert(FM * 32 * WM == BM && FN * 32 * WN == BN, "tile");
   static_assert(S >= 2 && S <= 8, "stages");
-  using OA = Operand<AK, BM, BK, NW>;
-  using OB = Operand<BKC, BN, BK, NW>;
+  static_assert(F8 == 0 || (AK && BKC && BK == 128), "FP8: K-contiguous operands, 128-code K-tiles");
+  using OA = std::conditional_t<(F8 > 0), OperandF8<BM, NW>, Operand<AK, BM, BK, NW>>;
+  using OB = std::conditional_t<(F8 > 0), OperandF8<BN, NW>, Operand<BKC, BN, BK, NW>>;
+  using FragT = std::conditional_t<(F8 > 0), i32x8_t, bf16x8_t>;
   constexpr int SB = OA::BYTES + OB::BYTES;  // bytes per stage
   // copies per wave per K-tile: NIT, plus one for each operand with an extra
   // window for this wave
@@ -245,8 +305,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 
   OA oa;
   OB ob;
-  oa.init(static_cast<const uint16_t*>(p.a), p.lda, m0, kbeg, wave, lane);
-  ob.init(static_cast<const uint16_t*>(p.b), p.ldb, n0, kbeg, wave, lane);
+  if constexpr (F8 > 0) {
+    oa.init(static_cast<const uint8_t*>(p.a), p.lda, m0, kbeg, wave, lane);
+    ob.init(static_cast<const uint8_t*>(p.b), p.ldb, n0, kbeg, wave, lane);
+  } else {
+    oa.init(static_cast<const uint16_t*>(p.a), p.lda, m0, kbeg, wave, lane);
+    ob.init(static_cast<const uint16_t*>(p.b), p.ldb, n0, kbeg, wave, lane);
+  }
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -283,9 +348,9 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
       if (after == decltype(c)::value) wait_tiles(c);
     });
   };
-  constexpr int KS = BK / 16;  // 16-wide K steps per K-tile
-  bf16x8_t f[2][FM + FN];      // fragments of K step ks live in f[ks & 1]
-  auto read = [&](auto stage_c, int ks, bf16x8_t(&d)[FM + FN]) {
+  constexpr int KS = F8 > 0 ? BK / 64 : BK / 16;  // MFMA K steps per K-tile
+  FragT f[2][FM + FN];         // fragments of K step ks live in f[ks & 1]
+  auto read = [&](auto stage_c, int ks, FragT(&d)[FM + FN]) {
     constexpr int J = decltype(stage_c)::value;
     const uint8_t* sa = stage_buf<J, SB>();
     const uint8_t* sb = sa + OA::BYTES;
@@ -294,12 +359,19 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 #pragma unroll
     for (int j = 0; j < FN; ++j) d[FM + j] = OB::frag(sb, wn * WTN + j * 32, ks, lane);
   };
-  auto mfma = [&](const bf16x8_t(&d)[FM + FN]) {
+  auto mfma = [&](const FragT(&d)[FM + FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d[i], d[FM + j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (F8 > 0) {
+          // operand formats are immediates; scales 0 select the unscaled instruction
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              d[i], d[FM + j], acc[i][j], (F8 - 1) & 1, (F8 - 1) >> 1, 0, 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d[i], d[FM + j], acc[i][j], 0, 0, 0);
+        }
+      }
   };
   // One K-tile from stage J; its first fragments are already in f[0]. Before
   // the last K step, sync() synchronises the block (and issues the uneven
@@ -383,6 +455,13 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   }
   wait_vmcnt<0>();
   block_sync();
+  if constexpr (F8 > 0) {  // dequantisation: 1/sa * 1/sb
+    const float sc = p.sa_inv[0] * p.sb_inv[0];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] *= sc;
+  }
 
   // ---- epilogue through LDS (per-wave regions inside the stage buffers).
   // For each 32-row band of its wave tile a wave writes the accumulators to
@@ -509,7 +588,21 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   });
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC>
+// Epilogue kinds instantiated per layout (bf16) or operand formats (FP8):
+// bf16 NN carries fc1's bias + GeLU, NT the dgrads, TN the weight gradients;
+// FP8 E4M3 x E4M3 every kind, E5M2 x E4M3 (data gradients) the dgrad kinds,
+// E4M3 x E5M2 (weight gradients) the fp32 store.
+template <bool AK, bool BKC, int F8>
+constexpr bool epi_instantiated(int ek) {
+  if constexpr (F8 == 0) {
+    return ek == kEpiF32 || (ek == kEpiBF16 && AK) || (ek == kEpiBiasGelu && AK && !BKC) ||
+           (ek == kEpiDGelu && AK && BKC);
+  } else {
+    return F8 == 1 || ek == kEpiF32 || (F8 == 2 && (ek == kEpiBF16 || ek == kEpiDGelu));
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int F8 = 0>
 hipError_t launch_pipe_cfg(const GemmParams& p, int splitk, int ek, hipStream_t s) {
   const int64_t tiles = (p.M / BM) * (p.N / BN);
   const dim3 grid(static_cast<unsigned>(tiles * splitk));
@@ -517,23 +610,30 @@ hipError_t launch_pipe_cfg(const GemmParams& p, int splitk, int ek, hipStream_t 
   switch (ek) {
     case kEpiF32:
       // column-sum blocks (if any) come last in dispatch order
-      hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiF32>),
+      hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiF32, F8>),
                          dim3(grid.x + p.cs_blocks), block, 0, s, p);
       break;
     case kEpiBF16:
-      if constexpr (AK)
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiBF16>),
+      if constexpr (epi_instantiated<AK, BKC, F8>(kEpiBF16))
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiBF16, F8>),
                            grid, block, 0, s, p);
+      else
+        return hipErrorInvalidValue;
       break;
     case kEpiBiasGelu:
-      if constexpr (AK && !BKC)
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiBiasGelu>),
-                           grid, block, 0, s, p);
+      if constexpr (epi_instantiated<AK, BKC, F8>(kEpiBiasGelu))
+        hipLaunchKernelGGL(
+            (gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiBiasGelu, F8>), grid,
+            block, 0, s, p);
+      else
+        return hipErrorInvalidValue;
       break;
     case kEpiDGelu:
-      if constexpr (AK && BKC)
-        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiDGelu>),
+      if constexpr (epi_instantiated<AK, BKC, F8>(kEpiDGelu))
+        hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, BK, S, AK, BKC, kEpiDGelu, F8>),
                            grid, block, 0, s, p);
+      else
+        return hipErrorInvalidValue;
       break;
     default:
       return hipErrorInvalidValue;
@@ -573,7 +673,68 @@ hipError_t launch_pipe_layout(const GemmParams& p, const SplitPlan& plan, int ek
   }
 }
 
+// FP8 tiles: 128-code (one line) K-tiles; three stages where they fit in LDS.
+template <int F8>
+hipError_t launch_fp8_tile(const GemmParams& p, const SplitPlan& plan, int ek, hipStream_t s) {
+  switch (plan.tile) {
+    case kPipe128x256:
+      return launch_pipe_cfg<128, 256, 2, 4, 128, 3, true, true, F8>(p, plan.splitk, ek, s);
+    case kPipe128x128:
+      return launch_pipe_cfg<128, 128, 2, 2, 128, 3, true, true, F8>(p, plan.splitk, ek, s);
+    case kPipe256x192:
+      return launch_pipe_cfg<256, 192, 4, 2, 128, 2, true, true, F8>(p, plan.splitk, ek, s);
+    case kPipe128x192:
+      return launch_pipe_cfg<128, 192, 2, 2, 128, 3, true, true, F8>(p, plan.splitk, ek, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+// Epilogue of an FP8 product; kEpiNone when the pipelined kernel cannot run it
+// (there is no general FP8 kernel: the API rejects such calls).
+int fp8_epilogue_kind(const GemmParams& p) {
+  auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+  if (p.splitk > 1)
+    return (p.epi == EPI_STORE && a16(p.ws) && p.N % 8 == 0) ? kEpiF32 : kEpiNone;
+  if (!a16(p.c) || p.ldc % 8) return kEpiNone;
+  switch (p.epi) {
+    case EPI_STORE:
+      if (p.accumulate) return kEpiNone;
+      return p.out_bf16 ? kEpiBF16 : kEpiF32;
+    case EPI_BIAS_ACT:
+      if (p.act == ACT_NONE && !p.bias && !p.c2) return p.out_bf16 ? kEpiBF16 : kEpiF32;
+      if (p.act == ACT_GELU && p.out_bf16 && p.c2 && a16(p.c2) && p.ldc2 % 8 == 0 &&
+          (!p.bias || a16(p.bias)))
+        return kEpiBiasGelu;
+      return kEpiNone;
+    case EPI_DACT:
+      if (p.act == ACT_GELU && p.out_bf16 && p.u && a16(p.u) && p.ldu % 8 == 0 &&
+          (!p.c2 || (a16(p.c2) && p.ldc2 % 8 == 0)))
+        return kEpiDGelu;
+      return kEpiNone;
+    default:
+      return kEpiNone;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gemm_fp8(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+  const int ek = fp8_epilogue_kind(p);
+  if (ek == kEpiNone) return hipErrorInvalidValue;
+  switch (p.f8) {
+    case 1:
+      return launch_fp8_tile<1>(p, plan, ek, s);
+    case 2:
+      return launch_fp8_tile<2>(p, plan, ek, s);
+    case 3:
+      return launch_fp8_tile<3>(p, plan, ek, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+int fp8_pipe_epilogue(const GemmParams& p) { return fp8_epilogue_kind(p); }
 
 int pipe_epilogue_kind(const GemmParams& p) {
   auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };

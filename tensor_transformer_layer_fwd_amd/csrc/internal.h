@@ -56,8 +56,34 @@ struct GemmParams {
   // then runs pass 2. cs_blocks = 0: none.
   ColsumParams cs;
   int cs_blocks, cs_units, cs_nchunks;
+  // FP8 operands (both K-contiguous codes): f8 = 0 for bf16, else
+  // 1 + fmt_a + 2 * fmt_b (fmt 0: E4M3, 1: E5M2); the accumulators are
+  // multiplied by sa_inv[0] * sb_inv[0] before the epilogue.
+  int f8;
+  const float* sa_inv;
+  const float* sb_inv;
 };
 
+
+// FP8 quantisation of X [rows, cols] (ld_x, bf16 or fp32) into codes Q
+// (ld_q; [cols, rows] when transpose) with per-tensor scaling; scale_inv
+// receives 1/s; partial holds kFp8AmaxBlocks floats of per-block maxima.
+constexpr int kFp8AmaxBlocks = 1024;
+struct Fp8QuantParams {
+  const void* x;
+  int64_t rows, cols, ld_x;
+  int x_bf16;
+  int fmt;  // 0: E4M3, 1: E5M2
+  int transpose;
+  uint8_t* q;
+  int64_t ld_q;
+  float* scale_inv;
+  float* partial;
+  int nblk;              // set by the launcher
+  int vec_in, vec_out;   // 16-byte input loads / 8- or 16-byte code stores allowed
+};
+int fp8_amax_blocks(int64_t rows, int64_t cols);
+hipError_t launch_fp8_quantize(Fp8QuantParams p, hipStream_t s);
 
 // Attention core of one shard (forward): QKV [batch*seq, 3*heads*64] bf16 as
 // [Q | K | V], C [batch*seq, heads*64] bf16, lse [batch, heads, seq] (or null).
@@ -127,6 +153,10 @@ struct SplitPlan {
 };
 
 SplitPlan plan_gemm_bf16(int64_t M, int64_t N, int64_t K, bool allow_split);
+// FP8 products: M, N multiples of 128, K of 128 (k_chunk too); tile 0 if none fits.
+SplitPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split);
+hipError_t launch_gemm_fp8(const GemmParams& p, const SplitPlan& plan, hipStream_t s);
+int fp8_pipe_epilogue(const GemmParams& p);  // kEpiNone: not supported
 // Forced tile / split for later plans (tile 0: none); false for invalid values.
 bool set_gemm_override(int tile, int splitk);
 size_t colsum_workspace_bytes(int64_t T, int64_t N);

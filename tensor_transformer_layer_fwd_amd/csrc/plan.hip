@@ -113,6 +113,39 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
 
 }  // namespace
 
+namespace {
+const TileId kF8Tiles[] = {kPipe256x192, kPipe128x256, kPipe128x192, kPipe128x128};
+}  // namespace
+
+SplitPlan plan_gemm_fp8(int64_t M, int64_t N, int64_t K, bool allow_split) {
+  // the bf16 cost model at twice the per-CU matrix rate, over the FP8 tiles
+  static const int kSplits[] = {1, 2, 3, 4, 6, 8};
+  SplitPlan best{0, 1, K};
+  double best_t = 1e30;
+  if (K % 128) return best;
+  for (TileId id : kF8Tiles) {  // a forced tile, where it fits
+    const PipeTile* t = find_tile(id);
+    if (id != g_force_tile || M % t->bm || N % t->bn) continue;
+    const int sp = g_force_split;
+    if (allow_split && sp > 1 && K % (128 * sp) == 0) return SplitPlan{id, sp, K / sp};
+    return SplitPlan{id, 1, K};
+  }
+  for (TileId id : kF8Tiles) {
+    PipeTile t = *find_tile(id);
+    if (M % t.bm || N % t.bn) continue;
+    t.flop_per_sec_per_cu *= 2.0;
+    for (int sp : kSplits) {
+      if (sp > 1 && (!allow_split || !t.split_ok || K % (128 * sp) || K / sp < 512)) continue;
+      const double c = cost(M, N, K, t, sp);
+      if (c < best_t) {
+        best_t = c;
+        best = SplitPlan{t.id, sp, K / sp};
+      }
+    }
+  }
+  return best;
+}
+
 int gemm_pipe_epilogue(const GemmParams& p, const SplitPlan& plan) {
   const bool aligned = (reinterpret_cast<uintptr_t>(p.a) & 15) == 0 && (p.lda & 7) == 0 &&
                        (reinterpret_cast<uintptr_t>(p.b) & 15) == 0 && (p.ldb & 7) == 0;

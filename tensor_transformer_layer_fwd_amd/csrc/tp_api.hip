@@ -62,6 +62,53 @@ int run_gemm(GemmParams& p, int dt, bool allow_split, size_t ws_bytes, hipStream
   return hip_status(e);
 }
 
+// One FP8 GEMM (+ split-K fix-up, + carried column sums). Every check runs
+// before the first launch: a shape the FP8 tiles do not cover, or an epilogue
+// the FP8 kernel does not have, returns TP_ERR_SHAPE.
+int run_gemm_fp8(GemmParams& p, bool allow_split, size_t ws_bytes, hipStream_t s,
+                 const ColsumParams* cs = nullptr) {
+  const SplitPlan plan = plan_gemm_fp8(p.M, p.N, p.K, allow_split);
+  if (plan.tile == 0) return TP_ERR_SHAPE;
+  p.splitk = plan.splitk;
+  p.k_chunk = plan.k_chunk;
+  if (plan.splitk > 1) {
+    const size_t need = static_cast<size_t>(plan.splitk) * p.M * p.N * sizeof(float);
+    if (!p.ws || ws_bytes < need) return TP_ERR_WORKSPACE;
+  }
+  if (fp8_pipe_epilogue(p) == kEpiNone) return TP_ERR_SHAPE;
+  const bool carry = cs && colsum_vec_ok(*cs) && fp8_pipe_epilogue(p) == kEpiF32;
+  if (carry) {
+    const int64_t nchunks = colsum_chunks(*cs);
+    const int64_t units = (cs->N + 255) / 256 * nchunks;
+    p.cs = *cs;
+    p.cs_nchunks = static_cast<int>(nchunks);
+    p.cs_units = static_cast<int>(units);
+    p.cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
+  }
+  hipError_t e = launch_gemm_fp8(p, plan, s);
+  if (e == hipSuccess && plan.splitk > 1) e = launch_splitk_fixup(p, s);
+  if (e == hipSuccess && carry && plan.splitk == 1 && p.cs_nchunks > 1)
+    e = launch_colsum_pass2(p.cs, p.cs_nchunks, s);
+  if (e == hipSuccess && cs && !carry) e = launch_colsum(*cs, s);
+  return hip_status(e);
+}
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+bool fmt_ok(int f) { return f == TP_FP8_E4M3 || f == TP_FP8_E5M2; }
+
+// FP8 operand codes: 16-byte aligned rows of at least K codes, stride a
+// multiple of 16 bytes.
+bool fp8_operand_ok(const void* q, int64_t ld, int64_t K) {
+  return aligned(q, 16) && ld % 16 == 0 && ld >= K;
+}
+
+size_t fp8_wgrad_split_bytes(int64_t T, int64_t k, int64_t n) {
+  const SplitPlan plan = plan_gemm_fp8(k, n, T, true);
+  if (plan.splitk <= 1) return 0;
+  const size_t b = static_cast<size_t>(plan.splitk) * k * n * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
 size_t wgrad_split_bytes(int64_t T, int64_t k, int64_t n, int dt) {
   if (dt != TP_BF16) return 0;
   const SplitPlan plan = plan_gemm_bf16(k, n, T, true);
@@ -342,6 +389,184 @@ int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float
   a.causal = causal != 0;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
   return hip_status(launch_attention_bwd(a, stream));
+}
+
+int tp_fp8_quantize_workspace_size(int64_t rows, int64_t cols, size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (!dim_ok(rows) || !dim_ok(cols)) return TP_ERR_SHAPE;
+  *bytes = kFp8AmaxBlocks * sizeof(float);
+  return TP_OK;
+}
+
+int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt, int fmt,
+                    int transpose, void* Q, int64_t ld_q, float* scale_inv, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !Q || !scale_inv) return TP_ERR_NULL;
+  if (!dtype_ok(dt) || !fmt_ok(fmt)) return TP_ERR_DTYPE;
+  if (!dim_ok(rows) || !dim_ok(cols) || rows * cols > (int64_t(1) << 40)) return TP_ERR_SHAPE;
+  if (ld_x < cols || ld_q < (transpose ? rows : cols)) return TP_ERR_SHAPE;
+  if (!aligned(scale_inv, 4) || !aligned(X, dt == TP_BF16 ? 2 : 4)) return TP_ERR_SHAPE;
+  if (!workspace || workspace_bytes < kFp8AmaxBlocks * sizeof(float) || !aligned(workspace, 4))
+    return TP_ERR_WORKSPACE;
+  Fp8QuantParams q{};
+  q.x = X;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld_x = ld_x;
+  q.x_bf16 = dt == TP_BF16;
+  q.fmt = fmt;
+  q.transpose = transpose != 0;
+  q.q = static_cast<uint8_t*>(Q);
+  q.ld_q = ld_q;
+  q.scale_inv = scale_inv;
+  q.partial = static_cast<float*>(workspace);
+  q.vec_in = aligned(X, 16) && ld_x % (dt == TP_BF16 ? 8 : 4) == 0;
+  q.vec_out = q.transpose ? (aligned(Q, 16) && ld_q % 16 == 0) : (aligned(Q, 8) && ld_q % 8 == 0);
+  return hip_status(launch_fp8_quantize(q, stream));
+}
+
+int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
+                             const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
+                             int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
+                             int64_t ld_y, int act, hipStream_t stream) {
+  if (!Xq || !Atq || !x_scale_inv || !a_scale_inv || !Y_i) return TP_ERR_NULL;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (act != TP_ACT_NONE && !U_i) return TP_ERR_NULL;
+  if (act == TP_ACT_NONE && (bias_i || U_i)) return TP_ERR_ACT;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(n) || ld_y < n) return TP_ERR_SHAPE;
+  if (!fp8_operand_ok(Xq, ld_x, h) || !fp8_operand_ok(Atq, ld_at, h)) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = Xq;
+  p.b = Atq;
+  p.c = Y_i;
+  p.c2 = U_i;
+  p.bias = bias_i;
+  p.M = T;
+  p.N = n;
+  p.K = h;
+  p.lda = ld_x;
+  p.ldb = ld_at;
+  p.ldc = ld_y;
+  p.ldc2 = ld_y;
+  p.epi = EPI_BIAS_ACT;
+  p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
+  p.out_bf16 = 1;
+  p.a_kcontig = p.b_kcontig = 1;
+  p.f8 = 1;  // E4M3 x E4M3
+  p.sa_inv = x_scale_inv;
+  p.sb_inv = a_scale_inv;
+  return run_gemm_fp8(p, false, 0, stream);
+}
+
+int tp_fp8_row_linear_fwd_partial(const void* Yq, const void* Btq, const float* y_scale_inv,
+                                  const float* b_scale_inv, float* Zp_i, int64_t T, int64_t k,
+                                  int64_t h, int64_t ld_y, int64_t ld_bt, int64_t ld_z,
+                                  hipStream_t stream) {
+  if (!Yq || !Btq || !y_scale_inv || !b_scale_inv || !Zp_i) return TP_ERR_NULL;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(h) || ld_z < h) return TP_ERR_SHAPE;
+  if (!fp8_operand_ok(Yq, ld_y, k) || !fp8_operand_ok(Btq, ld_bt, k)) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = Yq;
+  p.b = Btq;
+  p.c = Zp_i;
+  p.M = T;
+  p.N = h;
+  p.K = k;
+  p.lda = ld_y;
+  p.ldb = ld_bt;
+  p.ldc = ld_z;
+  p.epi = EPI_STORE;
+  p.out_bf16 = 0;
+  p.a_kcontig = p.b_kcontig = 1;
+  p.f8 = 1;
+  p.sa_inv = y_scale_inv;
+  p.sb_inv = b_scale_inv;
+  return run_gemm_fp8(p, false, 0, stream);
+}
+
+int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
+                            const float* w_scale_inv, int dout_fmt, const void* U, int act,
+                            void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
+                            int64_t ld_w, int64_t ld_u, int64_t ld_din, int out_dt,
+                            hipStream_t stream) {
+  if (!dOutq || !Wq || !dout_scale_inv || !w_scale_inv || !dIn) return TP_ERR_NULL;
+  if (!fmt_ok(dout_fmt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (act != TP_ACT_NONE && !U) return TP_ERR_NULL;
+  if (act != TP_ACT_NONE && out_dt != TP_BF16) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n) || ld_din < k) return TP_ERR_SHAPE;
+  if (act != TP_ACT_NONE && ld_u < k) return TP_ERR_SHAPE;
+  if (!fp8_operand_ok(dOutq, ld_dout, n) || !fp8_operand_ok(Wq, ld_w, n)) return TP_ERR_SHAPE;
+  GemmParams p{};
+  p.a = dOutq;
+  p.b = Wq;
+  p.c = dIn;
+  p.u = U;
+  p.M = T;
+  p.N = k;
+  p.K = n;
+  p.lda = ld_dout;
+  p.ldb = ld_w;
+  p.ldc = ld_din;
+  p.ldu = ld_u;
+  p.epi = act != TP_ACT_NONE ? EPI_DACT : EPI_STORE;
+  p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
+  p.out_bf16 = out_dt == TP_BF16;
+  p.a_kcontig = p.b_kcontig = 1;
+  p.f8 = 1 + dout_fmt;  // dOut in dout_fmt, W in E4M3
+  p.sa_inv = dout_scale_inv;
+  p.sb_inv = w_scale_inv;
+  return run_gemm_fp8(p, false, 0, stream);
+}
+
+int tp_fp8_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  *bytes = fp8_wgrad_split_bytes(T, k, n) + colsum_workspace_bytes(T, n);
+  return TP_OK;
+}
+
+int tp_fp8_linear_bwd_wgrad(const void* Intq, const void* dOuttq, const float* in_scale_inv,
+                            const float* dout_scale_inv, int dout_fmt, float* dW,
+                            const void* dOut, float* dbias, int64_t T, int64_t k, int64_t n,
+                            int64_t ld_int, int64_t ld_doutt, int64_t ld_dw, int64_t ld_dout,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!Intq || !dOuttq || !in_scale_inv || !dout_scale_inv || !dW) return TP_ERR_NULL;
+  if (dbias && !dOut) return TP_ERR_NULL;
+  if (!fmt_ok(dout_fmt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n) || ld_dw < n) return TP_ERR_SHAPE;
+  if (dbias && ld_dout < n) return TP_ERR_SHAPE;
+  if (!fp8_operand_ok(Intq, ld_int, T) || !fp8_operand_ok(dOuttq, ld_doutt, T)) return TP_ERR_SHAPE;
+  const size_t split_bytes = fp8_wgrad_split_bytes(T, k, n);
+  const size_t cs_bytes = dbias ? colsum_workspace_bytes(T, n) : 0;
+  if (split_bytes + cs_bytes > 0 && (!workspace || workspace_bytes < split_bytes + cs_bytes))
+    return TP_ERR_WORKSPACE;
+  GemmParams p{};
+  p.a = Intq;
+  p.b = dOuttq;
+  p.c = dW;
+  p.M = k;
+  p.N = n;
+  p.K = T;
+  p.lda = ld_int;
+  p.ldb = ld_doutt;
+  p.ldc = ld_dw;
+  p.epi = EPI_STORE;
+  p.out_bf16 = 0;
+  p.ws = static_cast<float*>(workspace);
+  p.a_kcontig = p.b_kcontig = 1;
+  p.f8 = 1 + 2 * dout_fmt;  // In^T in E4M3, dOut^T in dout_fmt
+  p.sa_inv = in_scale_inv;
+  p.sb_inv = dout_scale_inv;
+  ColsumParams c{};
+  c.src = dOut;
+  c.T = T;
+  c.N = n;
+  c.ld = ld_dout;
+  c.src_bf16 = 1;
+  c.dbias = dbias;
+  c.ws = dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr;
+  return run_gemm_fp8(p, true, split_bytes, stream, dbias ? &c : nullptr);
 }
 
 int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, int* splitk,

@@ -211,6 +211,48 @@ def test_dgrad_recompute_validation(lib):
     assert call(k=0) == -2
 
 
+def test_fp8_validation(lib):
+    """The FP8 entry points reject bad arguments on the host, before any launch."""
+    import ctypes
+    buf = ctypes.create_string_buffer(8192 + 256)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    q = ctypes.c_void_p(base)
+    ws = ctypes.c_size_t(0)
+    assert lib.tp_fp8_quantize_workspace_size(4, 4, ctypes.byref(ws)) == 0 and ws.value == 4096
+    wsp = ctypes.c_void_p(base)
+
+    def quant(x=q, Q=q, si=q, rows=4, cols=8, ld_x=8, dt=L.TP_BF16, fmt=0, tr=0, ld_q=8,
+              wsb=4096):
+        return lib.tp_fp8_quantize(x, rows, cols, ld_x, dt, fmt, tr, Q, ld_q, si, wsp, wsb, None)
+    assert quant(x=None) == -1 and quant(Q=None) == -1 and quant(si=None) == -1
+    assert quant(fmt=2) == -3 and quant(dt=5) == -3
+    assert quant(ld_x=7) == -2 and quant(ld_q=7) == -2
+    assert quant(tr=1, ld_q=3) == -2          # X^T rows are 4 codes
+    assert quant(wsb=4092) == -5
+
+    def col(M=256, N=256, K=256, lda=256, ldb=256, act=L.TP_ACT_GELU_TANH, U=q, bias=None):
+        return lib.tp_fp8_column_linear_fwd(q, q, q, q, bias, q, U, M, K, N, lda, ldb, N, act, None)
+    assert col(U=None) == -1
+    assert col(act=L.TP_ACT_NONE, U=None, bias=q) == -4   # no bias without the activation
+    assert col(K=200, lda=256, ldb=256) == -2             # K not a multiple of 128
+    assert col(M=200) == -2                                # M not a multiple of 128
+    assert col(lda=264) == -2                              # code stride not a multiple of 16
+
+    def dgrad(fmt=1, act=L.TP_ACT_GELU_TANH, out_dt=L.TP_BF16, U=q):
+        return lib.tp_fp8_linear_bwd_dgrad(q, q, q, q, fmt, U, act, q, 256, 256, 256, 256, 256,
+                                           256, 256, out_dt, None)
+    assert dgrad(fmt=3) == -3
+    assert dgrad(out_dt=L.TP_F32) == -3                    # the GeLU' epilogue writes bf16
+    assert dgrad(U=None) == -1
+
+    def wgrad(T=256, dbias=None, dout=None, wsb=0):
+        return lib.tp_fp8_linear_bwd_wgrad(q, q, q, q, 1, q, dout, dbias, T, 256, 256, T, T, 256,
+                                           256, None, wsb, None)
+    assert wgrad(dbias=q) == -1                            # bias gradient needs the bf16 dOut
+    assert wgrad(T=64) == -2
+    assert L.tp_fp8_linear_bwd_wgrad_workspace_size(4096, 256, 256) >= 0
+
+
 def test_gemm_override(lib):
     """The tuning hook forces a tile where the shape allows it, splits only
     weight gradients, changes the workspace query with the plan and resets."""
