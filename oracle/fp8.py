@@ -127,3 +127,78 @@ def fp8_linear(qa, qb, fmt_a, fmt_b, sinv_a, sinv_b, bias=None, act="none", U=No
     if act == "gelu":
         return gelu_tanh(C), C
     return C
+
+
+def round_bf16(x) -> np.ndarray:
+    """x rounded to fp32 (nearest even), then to bf16 (nearest even on the
+    upper 16 bits): the storage of the recipe's bf16 intermediates."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def tp_mlp_fp8(X, A, a, B, b, dZ, p, shards=None, weights_are_shards=False, grad_fmt=E5M2):
+    """One fwd+bwd step of the MLP shard with every product in FP8: weights and
+    activations in E4M3, gradients in grad_fmt, each operand quantised from its
+    stored value (inputs as given; U_i, Y_i, dU_i rounded to bf16, the storage
+    precision of the bf16 path) with its own current scale, in the layout its
+    product reads (K-contiguous). Bias gradients are column sums of the stored
+    gradients. Outputs are named as in oracle.tp_mlp."""
+    shards = tuple(range(p)) if shards is None else tuple(shards)
+    g = grad_fmt
+    X = np.asarray(X, np.float64)
+    dZ = np.asarray(dZ, np.float64)
+    qX, _, sX = quantize(X, E4M3)
+    qXt, _, sXt = quantize(X, E4M3, transpose=True)
+    qD, _, sD = quantize(dZ, g)
+    qDt, _, sDt = quantize(dZ, g, transpose=True)
+    out, Zp, dXp = {}, [], []
+    F = np.asarray(A).shape[1] if weights_are_shards else np.asarray(A).shape[1] // p
+    for i in shards:
+        if weights_are_shards:
+            A_i, B_i, a_i = A, B, a
+        else:
+            A_i, B_i = A[:, i * F:(i + 1) * F], B[i * F:(i + 1) * F]
+            a_i = None if a is None else a[i * F:(i + 1) * F]
+        qAt, _, sAt = quantize(A_i, E4M3, transpose=True)
+        Y, U = fp8_linear(qX, qAt, E4M3, E4M3, sX, sAt, bias=a_i, act="gelu")
+        U16, Y16 = round_bf16(U), round_bf16(Y)
+        qY, _, sY = quantize(Y16, E4M3)
+        qBt, _, sBt = quantize(B_i, E4M3, transpose=True)
+        Zp_i = fp8_linear(qY, qBt, E4M3, E4M3, sY, sBt)
+        qB, _, sB = quantize(B_i, E4M3)
+        dU = fp8_linear(qD, qB, g, E4M3, sD, sB, act="dgelu", U=U16)
+        dU16 = round_bf16(dU)
+        qYt, _, sYt = quantize(Y16, E4M3, transpose=True)
+        dB = fp8_linear(qYt, qDt, E4M3, g, sYt, sDt)
+        qdU, _, sdU = quantize(dU16, g)
+        qA, _, sA = quantize(A_i, E4M3)
+        dXp_i = fp8_linear(qdU, qA, g, E4M3, sdU, sA)
+        qdUt, _, sdUt = quantize(dU16, g, transpose=True)
+        dA = fp8_linear(qXt, qdUt, E4M3, g, sXt, sdUt)
+        out.update({f"U_{i}": U, f"Y_{i}": Y, f"Zp_{i}": Zp_i, f"dU_{i}": dU,
+                    f"dB_{i}": dB, f"dA_{i}": dA, f"dXp_{i}": dXp_i})
+        if a is not None:
+            out[f"da_{i}"] = dU16.sum(axis=0)
+        Zp.append(Zp_i)
+        dXp.append(dXp_i)
+    if b is not None:
+        out["db"] = dZ.sum(axis=0)
+    if len(shards) == p:
+        Z = Zp[0].copy()
+        for z in Zp[1:]:
+            Z = Z + z
+        out["Z"] = Z + (0.0 if b is None else np.asarray(b, np.float64)[None, :])
+        dX = dXp[0].copy()
+        for d in dXp[1:]:
+            dX = dX + d
+        out["dX"] = dX
+    return out
+
+
+def run_config_fp8(cfg, inputs, grad_fmt=E5M2) -> dict:
+    """tp_mlp_fp8 on a workload's inputs (MLP workloads)."""
+    g = {k: v.f64() for k, v in inputs.items()}
+    return tp_mlp_fp8(g["X"], g["A"], g.get("a"), g["B"], g.get("b"), g["dZ"], cfg.p,
+                      cfg.shards, weights_are_shards=not cfg.full_weights, grad_fmt=grad_fmt)

@@ -133,3 +133,35 @@ def test_linear_epilogues_closed_forms():
     # a large positive bias makes GeLU the identity; U is the biased product
     Y, U = F.fp8_linear(qa, qb, 0, 0, ia, ib, bias=np.full(5, 50.0), act="gelu")
     assert np.allclose(U, C + 50.0) and np.allclose(Y, U, rtol=1e-12)
+
+
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(21)
+    x = np.concatenate([rng.standard_normal(50000) * 10.0 ** rng.integers(-6, 6, 50000),
+                        [0.0, -0.0, 1.0, 65504.0, 1e-40]])
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(F.round_bf16(x), ref)
+
+
+@pytest.mark.parametrize("grad_fmt", [F.E4M3, F.E5M2])
+def test_fp8_step_within_quantisation_error_of_exact_step(grad_fmt):
+    """The FP8 step approximates the exact step: every output within the error
+    that 3-bit (2-bit) significands allow (about 2^-4 (2^-3) per element,
+    averaging down in the products), and visibly different from it (so the
+    quantisation really took place). A transposed operand, a wrong shard or a
+    misapplied scale gives errors of order one."""
+    import dataclasses
+    import oracle
+    from tp_inputs import get_config, make_inputs
+    cfg = dataclasses.replace(get_config("gpt2s"), micro_batch=1, seq=256, h=256)
+    inputs = make_inputs(cfg)
+    exact = oracle.run_config(cfg, inputs)
+    got = F.run_config_fp8(cfg, inputs, grad_fmt)
+    assert set(got) == set(exact)
+    bound = 0.12 if grad_fmt == F.E5M2 else 0.08
+    for k in exact:
+        if k == "db":
+            assert np.array_equal(got[k], exact[k])   # from the unquantised dZ
+            continue
+        e = oracle.rel_fro(got[k], exact[k])
+        assert 1e-3 < e < bound, (k, e)
