@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 METRIC = "TFLOP/s + % bf16 MFMA peak, TP-MLP shard fwd+bwd, 1×MI355X"
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 flop/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2  # dense FP8 matrix-core peak, twice bf16
 
 
 def log(msg):
@@ -226,6 +227,7 @@ def cpu_baseline(cfg, inputs, seconds):
 
 def main():
     args = parse()
+    from tp_inputs import get_config, make_inputs
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the shards of a workload run serially on "
               f"cuda:0 and are summed locally; --gpus {args.gpus} is not supported.",
@@ -328,6 +330,25 @@ def main():
         del rs
         torch.cuda.empty_cache()
 
+    # the same MLP step with every product in FP8 (E4M3 / E5M2, per-tensor
+    # current scaling, quantisation passes inside the timed step)
+    fp8 = {}
+    for name in [args.workload] + [w for w in args.extra.split(",") if w and w != args.workload]:
+        c8 = get_config(name)
+        if not (c8.mlp and not c8.attn and c8.dtype == "bf16"):
+            continue
+        from tensor_transformer_layer_fwd_amd.shard import ShardStep
+        s8 = ShardStep(c8, inputs if name == args.workload else make_inputs(c8), "cuda:0",
+                       fp8=True)
+        s8.capture()
+        f_ms, _ = time_steps(s8, max(5, args.steps // 5), 3)
+        tf8 = c8.gemm_flops() / (f_ms * 1e-3) / 1e12
+        fp8[name] = {"ms_per_step": round(f_ms, 5), "tflops": round(tf8, 1),
+                     "frac_of_fp8_peak": round(tf8 / PEAK_FP8_TFLOPS, 4)}
+        log(f"[bench] {name} FP8 step: {json.dumps(fp8[name])}")
+        del s8
+        torch.cuda.empty_cache()
+
     extra = {}
     for name in [w for w in args.extra.split(",") if w and w != args.workload]:
         c2, _, s2, w2, e2, f2, t2 = run_workload(name, max(5, args.steps // 5), 3)
@@ -384,6 +405,7 @@ def main():
         "extra": extra,
         "attention": attention,
         "recompute": recompute,
+        "fp8": fp8,
     }
     print(json.dumps(rec))
 

@@ -14,6 +14,12 @@ optimisations): Y_i lives in one transient buffer that fc2's forward reads, and
 the backward recomputes it from U_i in the fc2 dgrad epilogue
 (tp_linear_bwd_dgrad_recompute) just before fc2's weight gradient reads it.
 
+With fp8=True every MLP product runs on the FP8 matrix cores: each operand
+is quantised (tp_fp8_quantize, per-tensor current scaling) from its stored
+value into the K-contiguous layout its product reads; weights and activations
+in E4M3, gradients in E5M2. Bias gradients are column sums of the stored
+gradients.
+
 All p shards of a workload run one after another on the same device and
 stream; the shards' weights are column / row views of the unsharded tensors
 (no copies). torch provides device memory and streams only; every arithmetic
@@ -44,9 +50,12 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 class ShardStep:
     """Device buffers of one workload and the calls of one fwd+bwd step."""
 
-    def __init__(self, cfg, inputs: dict, device="cuda", recompute=False):
+    def __init__(self, cfg, inputs: dict, device="cuda", recompute=False, fp8=False):
         self.cfg = cfg
         self.recompute = bool(recompute and cfg.mlp)
+        self.fp8 = bool(fp8 and cfg.mlp)
+        if self.fp8 and (recompute or cfg.dtype != "bf16" or cfg.attn):
+            raise ValueError("the FP8 step covers bf16 MLP workloads without recompute")
         self.device = torch.device(device)
         self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.tp_dt = L.TP_BF16 if cfg.dtype == "bf16" else L.TP_F32
@@ -95,8 +104,69 @@ class ShardStep:
                 self.out["dXq"] = torch.empty(T, h, **act)
             ws = max(ws, L.tp_linear_bwd_wgrad_workspace_size(T, O, h, self.tp_dt),
                      L.tp_linear_bwd_wgrad_workspace_size(T, h, Q, self.tp_dt))
+        if self.fp8:
+            ws = max(ws, self._fp8_buffers())
         # one scratch buffer, shared by the wgrad calls (they run in order on one stream)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
+
+    def _fp8_buffers(self):
+        """Code buffers of the FP8 step: the shared operands (X, X^T, dZ, dZ^T)
+        and one set per product operand, reused shard after shard; one fp32
+        1/s per buffer. Returns the wgrad workspace size."""
+        T, h, F = self.cfg.T, self.cfg.h, self.cfg.F
+        u8 = dict(device=self.device, dtype=torch.uint8)
+        shapes = {"X": (T, h), "Xt": (h, T), "dZ": (T, h), "dZt": (h, T), "At": (F, h),
+                  "A": (h, F), "Bt": (h, F), "B": (F, h), "Y": (T, F), "Yt": (F, T),
+                  "dU": (T, F), "dUt": (F, T)}
+        self.q = {k: torch.empty(*v, **u8) for k, v in shapes.items()}
+        self.qs = {k: torch.empty(1, device=self.device) for k in shapes}
+        self.qws = torch.empty(L.tp_fp8_quantize_workspace_size(T, h), **u8)
+        return max(L.tp_fp8_linear_bwd_wgrad_workspace_size(T, F, h),
+                   L.tp_fp8_linear_bwd_wgrad_workspace_size(T, h, F))
+
+    def _quant(self, src, name, fmt="e4m3", transpose=False):
+        L.tp_fp8_quantize(src, self.q[name], self.qs[name], self.qws, fmt=fmt,
+                          transpose=transpose)
+        return self.q[name], self.qs[name]
+
+    def mlp_forward_fp8(self):
+        cfg, o, inp = self.cfg, self.out, self.inp
+        F = cfg.F
+        Xq, sX = self._quant(inp["X"], "X")
+        for i in cfg.shards:
+            a_i = self._col("a", i, F) if cfg.has_bias else None
+            Atq, sA = self._quant(self._col("A", i, F), "At", transpose=True)
+            L.tp_fp8_column_linear_fwd(Xq, Atq, sX, sA, a_i, o[f"Y_{i}"], o[f"U_{i}"])
+            Yq, sY = self._quant(o[f"Y_{i}"], "Y")
+            Btq, sB = self._quant(self._row("B", i, F), "Bt", transpose=True)
+            L.tp_fp8_row_linear_fwd_partial(Yq, Btq, sY, sB, o[f"Zp_{i}"])
+        if "Z" in o:
+            L.tp_reduce_partials([o[f"Zp_{i}"] for i in cfg.shards],
+                                 inp["b"] if cfg.has_bias else None, o["Z"])
+
+    def mlp_backward_fp8(self):
+        cfg, o, inp = self.cfg, self.out, self.inp
+        F, g = cfg.F, "e5m2"
+        dZq, sD = self._quant(inp["dZ"], "dZ", g)
+        dZtq, sDt = self._quant(inp["dZ"], "dZt", g, transpose=True)
+        Xtq, sXt = self._quant(inp["X"], "Xt", transpose=True)
+        for n, i in enumerate(cfg.shards):
+            Bq, sB = self._quant(self._row("B", i, F), "B")
+            L.tp_fp8_linear_bwd_dgrad(dZq, Bq, sD, sB, o[f"dU_{i}"], U=o[f"U_{i}"], act="gelu",
+                                      dout_fmt=g)
+            Ytq, sYt = self._quant(o[f"Y_{i}"], "Yt", transpose=True)
+            L.tp_fp8_linear_bwd_wgrad(Ytq, dZtq, sYt, sDt, o[f"dB_{i}"], dOut=inp["dZ"],
+                                      dbias=o["db"] if (cfg.has_bias and n == 0) else None,
+                                      dout_fmt=g, workspace=self.workspace)
+            dUq, sdU = self._quant(o[f"dU_{i}"], "dU", g)
+            Aq, sA = self._quant(self._col("A", i, F), "A")
+            L.tp_fp8_linear_bwd_dgrad(dUq, Aq, sdU, sA, o[f"dXp_{i}"], act="none", dout_fmt=g)
+            dUtq, sdUt = self._quant(o[f"dU_{i}"], "dUt", g, transpose=True)
+            L.tp_fp8_linear_bwd_wgrad(Xtq, dUtq, sXt, sdUt, o[f"dA_{i}"], dOut=o[f"dU_{i}"],
+                                      dbias=o.get(f"da_{i}"), dout_fmt=g,
+                                      workspace=self.workspace)
+        if "dX" in o:
+            L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])
 
     # ------------------------------------------------------------------ views
     def _col(self, name, i, width):
@@ -175,11 +245,11 @@ class ShardStep:
         if self.cfg.attn:
             self.attn_forward()
         if self.cfg.mlp:
-            self.mlp_forward()
+            self.mlp_forward_fp8() if self.fp8 else self.mlp_forward()
         if self.cfg.attn:
             self.attn_backward()
         if self.cfg.mlp:
-            self.mlp_backward()
+            self.mlp_backward_fp8() if self.fp8 else self.mlp_backward()
 
     def capture(self):
         """Record one step into a HIP graph (launch overhead off the host path)."""

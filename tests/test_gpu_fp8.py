@@ -280,3 +280,47 @@ def test_fp8_deterministic(dev):
         outs.append(dW.cpu())
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("name,mb,seq", [("gpt2s", 1, 640), ("gpt2s", 2, 512),
+                                         ("gpt175b", 1, 256)])
+def test_workload_fp8_step(dev, name, mb, seq):
+    """The whole MLP step in FP8 against the oracle's FP8 step (every output).
+    Both quantise the same stored values; the intermediates U_i, Y_i, dU_i
+    differ only where fp32 and float64 round to different bf16 neighbours,
+    and a code then flips only where an FP8 boundary lies between them, so
+    the outputs stay within the bf16 bar."""
+    import dataclasses
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    from tp_inputs import get_config, make_inputs
+    cfg = dataclasses.replace(get_config(name), micro_batch=mb, seq=seq)
+    if name == "gpt175b":
+        cfg = dataclasses.replace(cfg, h=1024)
+    _say(f"fp8 step {name} T={cfg.T} h={cfg.h}")
+    inputs = make_inputs(cfg)
+    step = ShardStep(cfg, inputs, dev, fp8=True)
+    step.run_eager()
+    got = step.results()
+    ref = F.run_config_fp8(cfg, inputs)
+    worst = (0.0, None)
+    for k, r in ref.items():
+        e = _err(got[k], r)
+        worst = max(worst, (e, k))
+        assert e <= TOL["bf16"], (k, e)
+    _say(f"  worst {worst[0]:.2e} ({worst[1]})")
+
+
+def test_fp8_step_graph_replay(dev):
+    """The FP8 step captured into a HIP graph replays bitwise like the eager step."""
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    from tp_inputs import get_config, make_inputs
+    cfg = get_config("gpt2s")
+    step = ShardStep(cfg, make_inputs(cfg), dev, fp8=True)
+    step.run_eager()
+    eager = {k: v.clone() for k, v in step.out.items()}
+    step.capture()
+    for _ in range(3):
+        step.run()
+        torch.cuda.synchronize()
+        for k, v in step.out.items():
+            assert torch.equal(v, eager[k]), k
