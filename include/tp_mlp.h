@@ -303,6 +303,17 @@ int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int
                     size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Both layouts at once: the codes of X into Q ([rows, cols], ld_q >= cols) and
+ * of X^T into Qt ([cols, rows], ld_qt >= rows), with one scale, from one read
+ * of X (two launches in all). The codes equal those of two tp_fp8_quantize
+ * calls.
+ */
+int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt,
+                         int fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
+                         float* scale_inv, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * FP8 column-parallel forward: Y_i = act(X A_i + a_i) with U_i saved, as
  * tp_column_linear_fwd, from Xq = codes of X [T, h] (E4M3) and Atq = codes of
  * A_i^T [n, h] (E4M3, quantised with transpose). Y_i, U_i and bias_i bf16.

@@ -21,6 +21,7 @@ from ._lib import (  # noqa: F401
     tp_fp8_linear_bwd_wgrad,
     tp_fp8_linear_bwd_wgrad_workspace_size,
     tp_fp8_quantize,
+    tp_fp8_quantize_both,
     tp_fp8_quantize_workspace_size,
     tp_fp8_row_linear_fwd_partial,
     tp_column_linear_fwd,

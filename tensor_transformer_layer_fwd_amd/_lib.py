@@ -47,6 +47,8 @@ SIGNATURES = {
     "tp_fp8_quantize_workspace_size": (_int, [_i64, _i64, ctypes.POINTER(ctypes.c_size_t)]),
     "tp_fp8_quantize": (_int, [_vp, _i64, _i64, _i64, _int, _int, _int, _vp, _i64, _vp, _vp,
                                ctypes.c_size_t, _vp]),
+    "tp_fp8_quantize_both": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64,
+                                    _vp, _vp, ctypes.c_size_t, _vp]),
     "tp_fp8_column_linear_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                         _i64, _i64, _i64, _int, _vp]),
     "tp_fp8_row_linear_fwd_partial": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -255,6 +257,15 @@ def tp_fp8_quantize(X, Q, scale_inv, workspace, fmt="e4m3", transpose=False, str
     rows, cols = X.shape
     _check("tp_fp8_quantize", lib().tp_fp8_quantize(
         _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), int(bool(transpose)), _ptr(Q), _ld(Q),
+        _ptr(scale_inv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
+
+
+def tp_fp8_quantize_both(X, Q, Qt, scale_inv, workspace, fmt="e4m3", stream=None):
+    """Codes of X into Q and of X^T into Qt from one read; scale_inv = 1/s."""
+    rows, cols = X.shape
+    _check("tp_fp8_quantize_both", lib().tp_fp8_quantize_both(
+        _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), _ptr(Q), _ld(Q), _ptr(Qt), _ld(Qt),
         _ptr(scale_inv), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
 

@@ -138,6 +138,17 @@ __global__ __launch_bounds__(kThreads) void fp8_cast_t_kernel(Fp8QuantParams p) 
     w.z = cvt4(v + 8, s, fmax, p.fmt);
     w.w = cvt4(v + 12, s, fmax, p.fmt);
     *reinterpret_cast<uint4*>(tile + lr * kTStride + lc) = w;
+    if (p.q_rows && row < p.rows) {  // the codes of X itself, from the same read
+      const int64_t c = c0 + lc;
+      uint8_t* qr = p.q_rows + row * p.ld_q_rows + c;
+      if (p.vec_rows && c + 16 <= p.cols) {
+        *reinterpret_cast<uint4*>(qr) = w;
+      } else {
+        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+        for (int e = 0; e < 16 && c + e < p.cols; ++e)
+          qr[e] = static_cast<uint8_t>((ww[e / 4] >> (8 * (e % 4))) & 0xff);
+      }
+    }
     __syncthreads();
     // output row c = c0 + lr of Q, entries r0 + lc .. r0 + lc + 15
     const int64_t qrow = c0 + lr, qc = r0 + lc;

@@ -81,6 +81,10 @@ struct Fp8QuantParams {
   float* partial;
   int nblk;              // set by the launcher
   int vec_in, vec_out;   // 16-byte input loads / 8- or 16-byte code stores allowed
+  // with transpose: also the codes of X itself ([rows, cols], ld_q_rows), or null
+  uint8_t* q_rows;
+  int64_t ld_q_rows;
+  int vec_rows;          // 16-byte stores into q_rows allowed
 };
 int fp8_amax_blocks(int64_t rows, int64_t cols);
 hipError_t launch_fp8_quantize(Fp8QuantParams p, hipStream_t s);

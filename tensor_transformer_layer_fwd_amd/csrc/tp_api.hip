@@ -425,6 +425,37 @@ int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int
   return hip_status(launch_fp8_quantize(q, stream));
 }
 
+int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt,
+                         int fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
+                         float* scale_inv, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!X || !Q || !Qt || !scale_inv) return TP_ERR_NULL;
+  if (!dtype_ok(dt) || !fmt_ok(fmt)) return TP_ERR_DTYPE;
+  if (!dim_ok(rows) || !dim_ok(cols) || rows * cols > (int64_t(1) << 40)) return TP_ERR_SHAPE;
+  if (ld_x < cols || ld_q < cols || ld_qt < rows) return TP_ERR_SHAPE;
+  if (!aligned(scale_inv, 4) || !aligned(X, dt == TP_BF16 ? 2 : 4)) return TP_ERR_SHAPE;
+  if (!workspace || workspace_bytes < kFp8AmaxBlocks * sizeof(float) || !aligned(workspace, 4))
+    return TP_ERR_WORKSPACE;
+  Fp8QuantParams q{};
+  q.x = X;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld_x = ld_x;
+  q.x_bf16 = dt == TP_BF16;
+  q.fmt = fmt;
+  q.transpose = 1;
+  q.q = static_cast<uint8_t*>(Qt);
+  q.ld_q = ld_qt;
+  q.q_rows = static_cast<uint8_t*>(Q);
+  q.ld_q_rows = ld_q;
+  q.scale_inv = scale_inv;
+  q.partial = static_cast<float*>(workspace);
+  q.vec_in = aligned(X, 16) && ld_x % (dt == TP_BF16 ? 8 : 4) == 0;
+  q.vec_out = aligned(Qt, 16) && ld_qt % 16 == 0;
+  q.vec_rows = aligned(Q, 16) && ld_q % 16 == 0;
+  return hip_status(launch_fp8_quantize(q, stream));
+}
+
 int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
                              const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
                              int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,

@@ -110,60 +110,63 @@ class ShardStep:
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
 
     def _fp8_buffers(self):
-        """Code buffers of the FP8 step: the shared operands (X, X^T, dZ, dZ^T)
-        and one set per product operand, reused shard after shard; one fp32
-        1/s per buffer. Returns the wgrad workspace size."""
+        """Code buffers of the FP8 step, each with its fp32 1/s: X and dZ in
+        both layouts; per shard the weights A_i and B_i and the activation Y_i
+        in both layouts (written in the forward, read by both passes); dU_i in
+        both layouts, reused shard after shard. Returns the wgrad workspace
+        size."""
         T, h, F = self.cfg.T, self.cfg.h, self.cfg.F
         u8 = dict(device=self.device, dtype=torch.uint8)
-        shapes = {"X": (T, h), "Xt": (h, T), "dZ": (T, h), "dZt": (h, T), "At": (F, h),
-                  "A": (h, F), "Bt": (h, F), "B": (F, h), "Y": (T, F), "Yt": (F, T),
-                  "dU": (T, F), "dUt": (F, T)}
+        shapes = {"X": (T, h), "Xt": (h, T), "dZ": (T, h), "dZt": (h, T), "dU": (T, F),
+                  "dUt": (F, T)}
+        for i in self.cfg.shards:
+            shapes.update({f"At{i}": (F, h), f"A{i}": (h, F), f"Bt{i}": (h, F), f"B{i}": (F, h),
+                           f"Y{i}": (T, F), f"Yt{i}": (F, T)})
         self.q = {k: torch.empty(*v, **u8) for k, v in shapes.items()}
         self.qs = {k: torch.empty(1, device=self.device) for k in shapes}
         self.qws = torch.empty(L.tp_fp8_quantize_workspace_size(T, h), **u8)
         return max(L.tp_fp8_linear_bwd_wgrad_workspace_size(T, F, h),
                    L.tp_fp8_linear_bwd_wgrad_workspace_size(T, h, F))
 
-    def _quant(self, src, name, fmt="e4m3", transpose=False):
-        L.tp_fp8_quantize(src, self.q[name], self.qs[name], self.qws, fmt=fmt,
-                          transpose=transpose)
-        return self.q[name], self.qs[name]
+    def _quant2(self, src, name, tname, fmt="e4m3"):
+        """Codes of src into q[name] and of src^T into q[tname] (one scale)."""
+        L.tp_fp8_quantize_both(src, self.q[name], self.q[tname], self.qs[name], self.qws,
+                               fmt=fmt)
+        self.qs[tname] = self.qs[name]
 
     def mlp_forward_fp8(self):
-        cfg, o, inp = self.cfg, self.out, self.inp
+        cfg, o, inp, q, qs = self.cfg, self.out, self.inp, self.q, self.qs
         F = cfg.F
-        Xq, sX = self._quant(inp["X"], "X")
+        self._quant2(inp["X"], "X", "Xt")
         for i in cfg.shards:
             a_i = self._col("a", i, F) if cfg.has_bias else None
-            Atq, sA = self._quant(self._col("A", i, F), "At", transpose=True)
-            L.tp_fp8_column_linear_fwd(Xq, Atq, sX, sA, a_i, o[f"Y_{i}"], o[f"U_{i}"])
-            Yq, sY = self._quant(o[f"Y_{i}"], "Y")
-            Btq, sB = self._quant(self._row("B", i, F), "Bt", transpose=True)
-            L.tp_fp8_row_linear_fwd_partial(Yq, Btq, sY, sB, o[f"Zp_{i}"])
+            self._quant2(self._col("A", i, F), f"A{i}", f"At{i}")
+            L.tp_fp8_column_linear_fwd(q["X"], q[f"At{i}"], qs["X"], qs[f"At{i}"], a_i,
+                                       o[f"Y_{i}"], o[f"U_{i}"])
+            self._quant2(o[f"Y_{i}"], f"Y{i}", f"Yt{i}")
+            self._quant2(self._row("B", i, F), f"B{i}", f"Bt{i}")
+            L.tp_fp8_row_linear_fwd_partial(q[f"Y{i}"], q[f"Bt{i}"], qs[f"Y{i}"], qs[f"Bt{i}"],
+                                            o[f"Zp_{i}"])
         if "Z" in o:
             L.tp_reduce_partials([o[f"Zp_{i}"] for i in cfg.shards],
                                  inp["b"] if cfg.has_bias else None, o["Z"])
 
     def mlp_backward_fp8(self):
-        cfg, o, inp = self.cfg, self.out, self.inp
-        F, g = cfg.F, "e5m2"
-        dZq, sD = self._quant(inp["dZ"], "dZ", g)
-        dZtq, sDt = self._quant(inp["dZ"], "dZt", g, transpose=True)
-        Xtq, sXt = self._quant(inp["X"], "Xt", transpose=True)
+        cfg, o, inp, q, qs = self.cfg, self.out, self.inp, self.q, self.qs
+        g = "e5m2"
+        self._quant2(inp["dZ"], "dZ", "dZt", g)
         for n, i in enumerate(cfg.shards):
-            Bq, sB = self._quant(self._row("B", i, F), "B")
-            L.tp_fp8_linear_bwd_dgrad(dZq, Bq, sD, sB, o[f"dU_{i}"], U=o[f"U_{i}"], act="gelu",
-                                      dout_fmt=g)
-            Ytq, sYt = self._quant(o[f"Y_{i}"], "Yt", transpose=True)
-            L.tp_fp8_linear_bwd_wgrad(Ytq, dZtq, sYt, sDt, o[f"dB_{i}"], dOut=inp["dZ"],
+            L.tp_fp8_linear_bwd_dgrad(q["dZ"], q[f"B{i}"], qs["dZ"], qs[f"B{i}"], o[f"dU_{i}"],
+                                      U=o[f"U_{i}"], act="gelu", dout_fmt=g)
+            L.tp_fp8_linear_bwd_wgrad(q[f"Yt{i}"], q["dZt"], qs[f"Yt{i}"], qs["dZt"],
+                                      o[f"dB_{i}"], dOut=inp["dZ"],
                                       dbias=o["db"] if (cfg.has_bias and n == 0) else None,
                                       dout_fmt=g, workspace=self.workspace)
-            dUq, sdU = self._quant(o[f"dU_{i}"], "dU", g)
-            Aq, sA = self._quant(self._col("A", i, F), "A")
-            L.tp_fp8_linear_bwd_dgrad(dUq, Aq, sdU, sA, o[f"dXp_{i}"], act="none", dout_fmt=g)
-            dUtq, sdUt = self._quant(o[f"dU_{i}"], "dUt", g, transpose=True)
-            L.tp_fp8_linear_bwd_wgrad(Xtq, dUtq, sXt, sdUt, o[f"dA_{i}"], dOut=o[f"dU_{i}"],
-                                      dbias=o.get(f"da_{i}"), dout_fmt=g,
+            self._quant2(o[f"dU_{i}"], "dU", "dUt", g)
+            L.tp_fp8_linear_bwd_dgrad(q["dU"], q[f"A{i}"], qs["dU"], qs[f"A{i}"], o[f"dXp_{i}"],
+                                      act="none", dout_fmt=g)
+            L.tp_fp8_linear_bwd_wgrad(q["Xt"], q["dUt"], qs["Xt"], qs["dUt"], o[f"dA_{i}"],
+                                      dOut=o[f"dU_{i}"], dbias=o.get(f"da_{i}"), dout_fmt=g,
                                       workspace=self.workspace)
         if "dX" in o:
             L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])

@@ -324,3 +324,22 @@ def test_fp8_step_graph_replay(dev):
         torch.cuda.synchronize()
         for k, v in step.out.items():
             assert torch.equal(v, eager[k]), k
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,cols", [(37, 53), (300, 1000), (768, 4096)])
+def test_quantize_both_equals_two_calls(dev, fmt, rows, cols):
+    """Both layouts from one read: the codes of each layout and the scale
+    equal the oracle's (as for the single-layout calls)."""
+    import tensor_transformer_layer_fwd_amd as tp
+    rng = np.random.default_rng(rows + cols + len(fmt))
+    Xf, bits = rand_bf16(rng, (rows, cols), 1.5)
+    X = to_dev_bf16(bits, dev, pad=8)
+    Q, Qt = Codes(rows, cols, dev, pad=16), Codes(cols, rows, dev, pad=16)
+    si = torch.full((1,), float("nan"), device=dev)
+    ws = torch.empty(tp.tp_fp8_quantize_workspace_size(rows, cols), dtype=torch.uint8, device=dev)
+    tp.tp_fp8_quantize_both(X, Q.view, Qt.view, si, ws, fmt=fmt)
+    torch.cuda.synchronize()
+    q_ref, _, sinv = F.quantize(Xf, FMT[fmt])
+    assert np.array_equal(Q.value(), q_ref) and np.array_equal(Qt.value(), q_ref.T)
+    assert si.item() == float(sinv)
