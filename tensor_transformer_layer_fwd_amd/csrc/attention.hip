@@ -35,8 +35,9 @@ typedef float f32x8_t __attribute__((ext_vector_type(8)));
 
 // All stages in one LDS array, so a stage is a constant offset: fragment reads
 // use the instruction's immediate offset and keep one address register each.
+template <int BYTES = kStages * kStageBytes>
 __device__ __forceinline__ uint8_t* attn_lds() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[BYTES];
   return buf;
 }
 
@@ -63,9 +64,22 @@ __device__ __forceinline__ void attn_sync() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
+// KG key groups: with KG = 2 a block has 8 waves; waves w and w + 4 take the
+// same 32 queries and alternate key tiles (group g the tiles KG*i + g, from the
+// g-th tile of each stage), and merge their running statistics and outputs
+// through LDS at the end. That halves the serial chain of a long causal row
+// and puts two waves on each SIMD when a shard has only one wave per SIMD's
+// worth of queries, so one wave's softmax runs beside the other's MFMAs.
+template <int KG>
+__global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
+  constexpr int kSet = KG * kStageBytes;  // bytes of one stage: KG (K, V) tile pairs
+  // stages: 3 of one pair, or 2 of two pairs (every fragment read keeps its
+  // stage offset within the 16-bit immediate)
+  constexpr int NS = KG == 2 ? 2 : kStages;
+  constexpr int kLds = NS * kSet;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qw = wave & 3, grp = wave >> 2;  // query sub-block, key group
   const int nqb = static_cast<int>((p.seq + kQB - 1) / kQB);
   // the longest causal rows first: query blocks in decreasing order
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
@@ -79,7 +93,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept for the whole pass
   const int ql = lane & 31, half = lane >> 5;
-  const int q = qb * kQB + wave * 32 + ql;
+  const int q = qb * kQB + qw * 32 + ql;
   const int64_t qrow = row0 + (q < seq ? q : seq - 1);
   bf16x8_t qf[4];
 #pragma unroll
@@ -90,25 +104,29 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qf[ks]));
 
-  // ---- tile copies: 16 windows of 1 KiB per stage (8 of K, 8 of V), four
-  // per wave; window w covers rows 8*(w%8) .. +7 of its tile, lane L copies
-  // row 8*(w%8) + L/8, physical chunk L%8.
+  // ---- tile copies: 16 windows of 1 KiB per (K, V) pair (8 of K, 8 of V),
+  // KG pairs per stage, four windows per wave; window w is pair w/16 of the
+  // stage, tile (w/8)%2 (K or V), rows 8*(w%8) .. +7; lane L copies row
+  // 8*(w%8) + L/8, physical chunk L%8.
   const uint16_t* src[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int w = wave * 4 + i, t = w / 8, r = 8 * (w % 8) + lane / 8, pc = lane % 8;
+    const int w = wave * 4 + i, t = (w / 8) % 2, r = 8 * (w % 8) + lane / 8, pc = lane % 8;
     const int c = pc ^ (t == 0 ? kswz(r) : vswz(r));
     src[i] = qkv + (row0 + r) * p.ld_qkv + (1 + t) * hd + h * kD + c * 8;
   }
-  auto issue = [&](auto stage_c, int kb) {
-    uint8_t* st = attn_lds() + decltype(stage_c)::value * kStageBytes;
+  // stage of key tiles KG*kp .. KG*kp + KG-1; a tile past the last one is
+  // still copied (its rows clamp to the sequence's last) so that every wave
+  // issues the same number of copies, and is never used
+  auto issue = [&](auto stage_c, int kp) {
+    uint8_t* st = attn_lds<kLds>() + decltype(stage_c)::value * kSet;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int w = wave * 4 + i, r = 8 * (w % 8) + lane / 8;
+      const int64_t kb = static_cast<int64_t>(kp) * KG + w / 16;
       // keys past the sequence read its last row (they are masked)
-      const int64_t over = static_cast<int64_t>(kb) * kKB + r - (seq - 1);
-      const uint16_t* g = src[i] + static_cast<int64_t>(kb) * kKB * p.ld_qkv -
-                          (over > 0 ? over * p.ld_qkv : 0);
+      const int64_t over = kb * kKB + r - (seq - 1);
+      const uint16_t* g = src[i] + kb * kKB * p.ld_qkv - (over > 0 ? over * p.ld_qkv : 0);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
                                        (__attribute__((address_space(3))) void*)(st + w * 1024),
                                        16, 0, 0);
@@ -119,16 +137,17 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   const int nkb_seq = static_cast<int>((seq + kKB - 1) / kKB);
   const int qlast = min(static_cast<int>(seq) - 1, qb * kQB + kQB - 1);
   const int nkb = p.causal ? min(nkb_seq, qlast / kKB + 1) : nkb_seq;
-  const int wq_last = qb * kQB + wave * 32 + 31;  // this wave's last query
+  const int wq_last = qb * kQB + qw * 32 + 31;  // this wave's last query
 
   const float scale = p.scale_log2;  // log2(e) / sqrt(64)
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16_t o[2] = {f32x16_t{}, f32x16_t{}};
 
-  const int wq_first = qb * kQB + wave * 32;     // this wave's first query
+  const int wq_first = qb * kQB + qw * 32;     // this wave's first query
 
-  // per-lane LDS byte addresses of the fragment reads within stage 0
-  const uint32_t lds0 = attn_lds_addr(attn_lds());
+  // per-lane LDS byte addresses of the fragment reads within stage 0 (this
+  // key group's tile pair)
+  const uint32_t lds0 = attn_lds_addr(attn_lds<kLds>()) + grp * kStageBytes;
   uint32_t ka[2][4];  // K tile: key row 32m + ql, 16-byte chunk 2ks + half
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -151,9 +170,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
   }
 
   auto compute = [&](auto stage_c, int kb) {
-    constexpr int SOFF = decltype(stage_c)::value * kStageBytes;
+    constexpr int SOFF = decltype(stage_c)::value * kSet;
     const int k0 = kb * kKB;
-    if (p.causal && k0 > wq_last) return;  // every key of the tile is masked for this wave
+    if (kb >= nkb || (p.causal && k0 > wq_last)) return;  // no visible key in the tile
     // K fragments for S^T
     bf16x8_t kf[2][4];
 #pragma unroll
@@ -239,22 +258,53 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnParams p) {
     }
   };
 
-  // ---- pass over the key tiles: 3 stages, two tiles in flight
-  Unroll<0, 2>::run([&](auto jc) {
-    if (decltype(jc)::value < nkb) issue(jc, decltype(jc)::value);
+  // ---- pass over the key tiles: NS stages of KG tiles, NS-1 in flight
+  const int nkp = (nkb + KG - 1) / KG;
+  Unroll<0, NS - 1>::run([&](auto jc) {
+    if (decltype(jc)::value < nkp) issue(jc, decltype(jc)::value);
   });
-  for (int kb0 = 0; kb0 < nkb; kb0 += kStages) {
-    Unroll<0, kStages>::run([&](auto jc) {
+  for (int kp0 = 0; kp0 < nkp; kp0 += NS) {
+    Unroll<0, NS>::run([&](auto jc) {
       constexpr int J = decltype(jc)::value;
-      const int kb = kb0 + J;
-      if (kb < nkb) {
-        if (kb + 1 < nkb) attn_wait_vmcnt<4>();  // tile kb+1's copies may still fly
-        else attn_wait_vmcnt<0>();
-        attn_sync();  // tile kb landed for every wave; stage (kb+2)%3 is free
-        if (kb + 2 < nkb) issue(std::integral_constant<int, (J + 2) % kStages>{}, kb + 2);
-        compute(jc, kb);
+      const int kp = kp0 + J;
+      if (kp < nkp) {
+        if constexpr (NS == 3) {
+          if (kp + 1 < nkp) attn_wait_vmcnt<4>();  // stage kp+1's copies may still fly
+          else attn_wait_vmcnt<0>();
+        } else {
+          attn_wait_vmcnt<0>();
+        }
+        attn_sync();  // stage kp landed for every wave; stage (kp+NS-1)%NS is free
+        if (kp + NS - 1 < nkp) issue(std::integral_constant<int, (J + NS - 1) % NS>{}, kp + NS - 1);
+        compute(jc, kp * KG + grp);
       }
     });
+  }
+  if constexpr (KG == 2) {
+    // merge the key groups: group 1 leaves (m, l, O^T) in LDS, group 0 folds
+    // them into its own; lane data at float index (wave%4 * 34 + j) * 64 + lane
+    attn_sync();  // every wave is done with the stages
+    float* x = reinterpret_cast<float*>(attn_lds<kLds>()) + qw * 34 * 64 + lane;
+    if (grp == 1) {
+      x[0] = m_run;
+      x[64] = l_run;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(2 + 16 * db + r) * 64] = o[db][r];
+    }
+    attn_sync();
+    if (grp == 1) return;
+    const float m1 = x[0], l1 = x[64];
+    const float m_new = fmaxf(m_run, m1);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    const float c0 = __builtin_amdgcn_exp2f(m_run - m_use), c1 = __builtin_amdgcn_exp2f(m1 - m_use);
+    l_run = l_run * c0 + l1 * c1;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * c0 + x[(2 + 16 * db + r) * 64] * c1;
   }
 
   // ---- output: lane holds query q and d = 32*db + 8*(r/4) + 4*half + r%4
@@ -705,7 +755,11 @@ hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s) {
 hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s) {
   const int64_t blocks = p.batch * p.heads * ((p.seq + kQB - 1) / kQB);
   if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL(attn_fwd_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+  // two key groups per block while the grid leaves SIMDs with one wave
+  if (blocks < 2 * 256)
+    hipLaunchKernelGGL(attn_fwd_kernel<2>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

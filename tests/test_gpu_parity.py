@@ -545,6 +545,8 @@ def _run_tile_op(dev, tile, op, M, N, K):
     (3, 257, 2, True), (1, 384, 1, False),
     (8, 512, 8, True),    # the attention-projection workload's shard: 8 x 512 tokens, 8 heads
     (6, 1024, 4, True),   # the ~350M-layer workload's shard: 6 x 1024 tokens, 4 heads
+    (2, 1024, 32, True),  # 512 query blocks: one key group per block
+    (4, 200, 80, False),  # 640 query blocks, ragged
 ])
 def test_attention_fwd(dev, batch, seq, heads, causal):
     import tensor_transformer_layer_fwd_amd as tp
