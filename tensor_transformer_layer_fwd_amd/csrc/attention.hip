@@ -348,8 +348,9 @@ constexpr int kBStages = 3;
 constexpr int kBStatBytes = 1024;
 constexpr int kBStageBytes = 2 * kTileBytes + kBStatBytes;
 
+template <int BYTES>
 __device__ __forceinline__ uint8_t* attn_bwd_lds() {
-  __shared__ __attribute__((aligned(1024))) uint8_t buf[kBStages * kBStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[BYTES];
   return buf;
 }
 
@@ -424,19 +425,43 @@ __device__ __forceinline__ void lds_tie(bf16x8_t (&f)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
 }
 
-// 32x32x16 operand from two transposed reads at LDS byte addresses a0, a1.
+// 32x32x16 operand from two transposed reads at LDS byte addresses a0 + OFF,
+// a1 + OFF (OFF: a stage's constant offset, in the instruction's immediate).
+template <int OFF>
 __device__ __forceinline__ bf16x8_t tr_frag(uint32_t a0, uint32_t a1) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
   s16x4_t lo, hi;
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a0));
-  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(hi) : "v"(a1));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(lo) : "v"(a0), "i"(OFF));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(hi) : "v"(a1), "i"(OFF));
   return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
+template <int OFF>
 __device__ __forceinline__ bf16x8_t row_frag(uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "16-bit LDS offset");
   bf16x8_t f;
-  asm volatile("ds_read_b128 %0, %1" : "=v"(f) : "v"(a));
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(f) : "v"(a), "i"(OFF));
   return f;
 }
+
+// Per-lane fragment addresses of one tile set (relative addresses + base):
+// row reads ra[m][ks], transposed reads tr0 / tr1[st][db] (rows r and r + 8).
+struct FragAddr {
+  uint32_t ra[2][4], tr0[4][2], tr1[4][2];
+  __device__ __forceinline__ void init(uint32_t base, int lane) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) ra[m][ks] = base + row_addr(m, ks, lane);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        tr0[st][db] = base + tr_addr(st, db, 0, lane);
+        tr1[st][db] = base + tr_addr(st, db, 1, lane);
+      }
+  }
+};
 
 // bf16 operand from registers 8*hh .. 8*hh+7 of an accumulator
 __device__ __forceinline__ bf16x8_t pack8(const f32x16_t& v, int hh) {
@@ -446,12 +471,20 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t& v, int hh) {
   return __builtin_convertvector(t, bf16x8_t);
 }
 
-// ---- dK, dV: block = 128 keys of one (sequence, head), wave = 32 keys;
-// per 64-query tile: S = Q K^T and dP = dC V^T (lane = key, registers =
-// queries), P, dS, then dV^T += dC^T P and dK^T += Q^T dS.
-__global__ __launch_bounds__(256) void attn_bwd_kv_kernel(AttnBwdParams p) {
+// ---- dK, dV: block = 128 keys of one (sequence, head), 4 waves of 32 keys
+// per query group; with QG = 2 groups, waves w and w + 4 hold the same keys and
+// alternate query tiles, and add their dK, dV through LDS at the end (in a
+// fixed order). Per 64-query tile and 32-query half m: S = Q K^T and
+// dP = dC V^T (lane = key, registers = queries), P, dS, then dV^T += dC^T P
+// and dK^T += Q^T dS.
+template <int QG>
+__global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) {
+  constexpr int kSet = QG * kBStageBytes;  // one stage: QG query tiles (Q, dC, stats)
+  constexpr int NS = QG == 2 ? 2 : kBStages;
+  constexpr int kLds = NS * kSet;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = wave & 3, grp = wave >> 2;
   const int64_t seq = p.seq;
   const int nkb = static_cast<int>((seq + 127) / 128);
   const int kb = static_cast<int>(blockIdx.x % nkb);  // the keys most queries see first
@@ -463,7 +496,7 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(AttnBwdParams p) {
   const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
   const uint16_t* dcp = static_cast<const uint16_t*>(p.dc);
   const int kl = lane & 31, half = lane >> 5;
-  const int key = kb * 128 + wave * 32 + kl;
+  const int key = kb * 128 + kw * 32 + kl;
   const int64_t krow = row0 + (key < seq ? key : seq - 1);
 
   // K and V fragments of this wave's 32 keys (B operands: column = key)
@@ -477,59 +510,61 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(AttnBwdParams p) {
   lds_tie(kf);
   lds_tie(vf);
 
-  // query tiles: causal rows q >= the block's first key
+  // query tiles: causal rows q >= the block's first key; group g takes tiles
+  // qt0 + QG*i + g from slot g of stage i
   const int nqt = static_cast<int>((seq + 63) / 64);
   const int qt0 = p.causal ? kb * 2 : 0;
+  const int nst = (nqt - qt0 + QG - 1) / QG;
   TileCopy cq, cd;
-  cq.init(qkv, p.ld_qkv, row0, h * kD, 2 * wave, lane);       // Q tile: windows 2w, 2w+1
-  cd.init(dcp, p.ld_dc, row0, h * kD, 2 * wave, lane);        // dC tile
-  const uint32_t lds0 = attn_lds_addr(attn_bwd_lds());
-  // stats copy: waves 0 and 2 copy lse, 1 and 3 delta, of queries qt*64 + lane
-  const float* stat_src = (wave & 1 ? p.delta : p.lse) + lbase;
-  auto issue = [&](auto stage_c, int qt) {
-    uint8_t* st = attn_bwd_lds() + decltype(stage_c)::value * kBStageBytes;
-    cq.issue(st, static_cast<int64_t>(qt) * 64, seq, p.ld_qkv, 2 * wave, lane);
-    cd.issue(st + kTileBytes, static_cast<int64_t>(qt) * 64, seq, p.ld_dc, 2 * wave, lane);
-    const int64_t qq = static_cast<int64_t>(qt) * 64 + lane;
+  cq.init(qkv, p.ld_qkv, row0, h * kD, 2 * kw, lane);  // Q tile: windows 2kw, 2kw+1
+  cd.init(dcp, p.ld_dc, row0, h * kD, 2 * kw, lane);   // dC tile
+  uint8_t* const lds = attn_bwd_lds<kLds>();
+  FragAddr fa;
+  fa.init(attn_lds_addr(lds) + grp * kBStageBytes, lane);
+  // stats copy: waves 0 and 2 of a group copy lse, 1 and 3 delta, of queries
+  // qt*64 + lane (a tile past the last one is copied clamped and never used)
+  const float* stat_src = (kw & 1 ? p.delta : p.lse) + lbase;
+  auto issue = [&](auto stage_c, int si) {
+    uint8_t* st = lds + decltype(stage_c)::value * kSet + grp * kBStageBytes;
+    const int64_t q0 = static_cast<int64_t>(qt0 + si * QG + grp) * 64;
+    cq.issue(st, q0, seq, p.ld_qkv, 2 * kw, lane);
+    cd.issue(st + kTileBytes, q0, seq, p.ld_dc, 2 * kw, lane);
+    const int64_t qq = q0 + lane;
     __builtin_amdgcn_global_load_lds(
         (const __attribute__((address_space(1))) void*)(stat_src + (qq < seq ? qq : seq - 1)),
-        (__attribute__((address_space(3))) void*)(st + 2 * kTileBytes + wave * 256), 4, 0, 0);
+        (__attribute__((address_space(3))) void*)(st + 2 * kTileBytes + kw * 256), 4, 0, 0);
   };
 
   f32x16_t dv[2] = {f32x16_t{}, f32x16_t{}}, dk[2] = {f32x16_t{}, f32x16_t{}};
   const float scale = p.scale_log2;
-  const int wk_first = kb * 128 + wave * 32;  // this wave's first key
+  const int wk_first = kb * 128 + kw * 32;  // this wave's first key
 
   auto compute = [&](auto stage_c, int qt) {
-    constexpr int kStage = decltype(stage_c)::value;
-    const uint32_t sq = lds0 + kStage * kBStageBytes, sd = sq + kTileBytes;
-    const float* stats = reinterpret_cast<const float*>(attn_bwd_lds() + kStage * kBStageBytes + 2 * kTileBytes);
+    constexpr int SO = decltype(stage_c)::value * kSet;
+    const float* stats = reinterpret_cast<const float*>(lds + SO + grp * kBStageBytes + 2 * kTileBytes);
     const int q0 = qt * 64;
-    if (p.causal && q0 + 63 < wk_first) return;  // no query of the tile sees these keys
-    // S = Q K^T, dP = dC V^T for the tile's 64 queries
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+    if (qt >= nqt || (p.causal && q0 + 63 < wk_first)) return;  // no query sees these keys
+    const bool interior = (!p.causal || q0 >= wk_first + 31) && q0 + 64 <= seq;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
+      // S and dP for queries q0 + 32m .. +31 (register r: query
+      // q0 + 32m + 8*(r/4) + 4*half + r%4)
       bf16x8_t qa[4], da[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        qa[ks] = row_frag(sq + row_addr(m, ks, lane));
-        da[ks] = row_frag(sd + row_addr(m, ks, lane));
+        qa[ks] = row_frag<SO>(fa.ra[m][ks]);
+        da[ks] = row_frag<SO + kTileBytes>(fa.ra[m][ks]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_tie(qa);
       lds_tie(da);
+      f32x16_t sv = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], s[m], 0, 0, 0);
-        dp[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], dp[m], 0, 0, 0);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], sv, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], dp, 0, 0, 0);
       }
-    }
-    // P and dS (masked entries 0); register r of half m holds query
-    // q0 + 32m + 8*(r/4) + 4*half + r%4
-    const bool interior = (!p.causal || q0 >= wk_first + 31) && q0 + 64 <= seq;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
+      // P and dS (masked entries 0)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int qi = 32 * m + 8 * j + 4 * half;
@@ -539,53 +574,80 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(AttnBwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * j + e;
-          float pr = __builtin_amdgcn_exp2f(s[m][r] * scale - lv[e] * 1.4426950408889634f);
+          float pr = __builtin_amdgcn_exp2f(sv[r] * scale - lv[e] * 1.4426950408889634f);
           if (!interior) {
             const int qq = q0 + qi + e;
             if (qq >= seq || (p.causal && key > qq)) pr = 0.0f;
           }
-          s[m][r] = pr;
-          dp[m][r] = pr * (dp[m][r] - dl[e]);
+          sv[r] = pr;
+          dp[r] = pr * (dp[r] - dl[e]);
         }
       }
-    // dV^T += dC^T P and dK^T += Q^T dS over four 16-query steps
+      // dV^T += dC^T P and dK^T += Q^T dS over the half's two 16-query steps
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int m = st >> 1, hh = st & 1;
-      const bf16x8_t pf = pack8(s[m], hh), sf = pack8(dp[m], hh);
-      bf16x8_t ta[2], tq[2];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int st = 2 * m + hh;
+        const bf16x8_t pf = pack8(sv, hh), sf = pack8(dp, hh);
+        bf16x8_t ta[2], tq[2];
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        ta[db] = tr_frag(sd + tr_addr(st, db, 0, lane), sd + tr_addr(st, db, 1, lane));
-        tq[db] = tr_frag(sq + tr_addr(st, db, 0, lane), sq + tr_addr(st, db, 1, lane));
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      lds_tie(ta);
-      lds_tie(tq);
+        for (int db = 0; db < 2; ++db) {
+          ta[db] = tr_frag<SO + kTileBytes>(fa.tr0[st][db], fa.tr1[st][db]);
+          tq[db] = tr_frag<SO>(fa.tr0[st][db], fa.tr1[st][db]);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_tie(ta);
+        lds_tie(tq);
 #pragma unroll
-      for (int db = 0; db < 2; ++db) {
-        dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], pf, dv[db], 0, 0, 0);
-        dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[db], sf, dk[db], 0, 0, 0);
+        for (int db = 0; db < 2; ++db) {
+          dv[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], pf, dv[db], 0, 0, 0);
+          dk[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tq[db], sf, dk[db], 0, 0, 0);
+        }
       }
     }
   };
 
-  const int ntile = nqt - qt0;
-  Unroll<0, 2>::run([&](auto jc) {
-    if (decltype(jc)::value < ntile) issue(jc, qt0 + decltype(jc)::value);
+  Unroll<0, NS - 1>::run([&](auto jc) {
+    if (decltype(jc)::value < nst) issue(jc, decltype(jc)::value);
   });
-  for (int i0 = 0; i0 < ntile; i0 += kBStages) {
-    Unroll<0, kBStages>::run([&](auto jc) {
+  for (int i0 = 0; i0 < nst; i0 += NS) {
+    Unroll<0, NS>::run([&](auto jc) {
       constexpr int J = decltype(jc)::value;
-      const int i = i0 + J;
-      if (i < ntile) {
-        if (i + 1 < ntile) attn_wait_vmcnt<5>();  // tile i+1's five copies may still fly
-        else attn_wait_vmcnt<0>();
+      const int si = i0 + J;
+      if (si < nst) {
+        if constexpr (NS == 3) {
+          if (si + 1 < nst) attn_wait_vmcnt<5>();  // stage si+1's five copies may still fly
+          else attn_wait_vmcnt<0>();
+        } else {
+          attn_wait_vmcnt<0>();
+        }
         attn_sync();
-        if (i + 2 < ntile) issue(std::integral_constant<int, (J + 2) % kBStages>{}, qt0 + i + 2);
-        compute(jc, qt0 + i);
+        if (si + NS - 1 < nst) issue(std::integral_constant<int, (J + NS - 1) % NS>{}, si + NS - 1);
+        compute(jc, qt0 + si * QG + grp);
       }
     });
+  }
+  if constexpr (QG == 2) {
+    // group 0 adds group 1's sums (64 floats per lane at (kw*64 + j)*64 + lane)
+    attn_sync();
+    float* x = reinterpret_cast<float*>(lds) + kw * 64 * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          x[(16 * db + r) * 64] = dv[db][r];
+          x[(32 + 16 * db + r) * 64] = dk[db][r];
+        }
+    }
+    attn_sync();
+    if (grp == 1) return;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dv[db][r] += x[(16 * db + r) * 64];
+        dk[db][r] += x[(32 + 16 * db + r) * 64];
+      }
   }
 
   // dK = dK^T^T / 8, dV = dV^T^T: lane holds key `key`, d = 32db + 8*(r/4) + 4*half + r%4
@@ -607,11 +669,19 @@ __global__ __launch_bounds__(256) void attn_bwd_kv_kernel(AttnBwdParams p) {
   }
 }
 
-// ---- dQ: block = 128 queries, wave = 32 queries; per 64-key tile:
+// ---- dQ: block = 128 queries, 4 waves of 32 queries per key group; with
+// KG = 2 groups, waves w and w + 4 hold the same queries, alternate key tiles
+// and add their dQ through LDS at the end. Per 64-key tile and 32-key half m:
 // S^T = K Q^T, dP^T = V dC^T (lane = query), P^T, dS^T, dQ^T += K^T dS^T.
-__global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnBwdParams p) {
+template <int KG>
+__global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
+  constexpr int kPair = 2 * kTileBytes;  // one K and one V tile
+  constexpr int kSet = KG * kPair;
+  constexpr int NS = KG == 2 ? 2 : kBStages;
+  constexpr int kLds = NS * kSet;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int qw = wave & 3, grp = wave >> 2;
   const int64_t seq = p.seq;
   const int nqb = static_cast<int>((seq + kQB - 1) / kQB);
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
@@ -623,7 +693,7 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnBwdParams p) {
   const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
   const uint16_t* dcp = static_cast<const uint16_t*>(p.dc);
   const int ql = lane & 31, half = lane >> 5;
-  const int q = qb * kQB + wave * 32 + ql;
+  const int q = qb * kQB + qw * 32 + ql;
   const int64_t qrow = row0 + (q < seq ? q : seq - 1);
   bf16x8_t qf[4], df[4];
 #pragma unroll
@@ -640,84 +710,107 @@ __global__ __launch_bounds__(256) void attn_bwd_q_kernel(AttnBwdParams p) {
   const int nkt_seq = static_cast<int>((seq + 63) / 64);
   const int qlast = min(static_cast<int>(seq) - 1, qb * kQB + kQB - 1);
   const int nkt = p.causal ? min(nkt_seq, qlast / 64 + 1) : nkt_seq;
-  const int wq_first = qb * kQB + wave * 32, wq_last = wq_first + 31;
+  const int nst = (nkt + KG - 1) / KG;
+  const int wq_first = qb * kQB + qw * 32, wq_last = wq_first + 31;
   TileCopy ck, cv;
-  ck.init(qkv, p.ld_qkv, row0, hd + h * kD, 2 * wave, lane);
-  cv.init(qkv, p.ld_qkv, row0, 2 * hd + h * kD, 2 * wave, lane);
-  const uint32_t lds0 = attn_lds_addr(attn_bwd_lds());
-  auto issue = [&](auto stage_c, int kt) {
-    uint8_t* st = attn_bwd_lds() + decltype(stage_c)::value * kBStageBytes;
-    ck.issue(st, static_cast<int64_t>(kt) * 64, seq, p.ld_qkv, 2 * wave, lane);
-    cv.issue(st + kTileBytes, static_cast<int64_t>(kt) * 64, seq, p.ld_qkv, 2 * wave, lane);
+  ck.init(qkv, p.ld_qkv, row0, hd + h * kD, 2 * qw, lane);
+  cv.init(qkv, p.ld_qkv, row0, 2 * hd + h * kD, 2 * qw, lane);
+  uint8_t* const lds = attn_bwd_lds<kLds>();
+  FragAddr fa;
+  fa.init(attn_lds_addr(lds) + grp * kPair, lane);
+  // stage si holds key tiles KG*si .. KG*si + KG-1 (one past the last is
+  // copied clamped and never used)
+  auto issue = [&](auto stage_c, int si) {
+    uint8_t* st = lds + decltype(stage_c)::value * kSet + grp * kPair;
+    const int64_t k0 = static_cast<int64_t>(si * KG + grp) * 64;
+    ck.issue(st, k0, seq, p.ld_qkv, 2 * qw, lane);
+    cv.issue(st + kTileBytes, k0, seq, p.ld_qkv, 2 * qw, lane);
   };
   f32x16_t dqa[2] = {f32x16_t{}, f32x16_t{}};
   const float scale = p.scale_log2;
 
   auto compute = [&](auto stage_c, int kt) {
-    const uint32_t sk = lds0 + decltype(stage_c)::value * kBStageBytes, sv = sk + kTileBytes;
+    constexpr int SO = decltype(stage_c)::value * kSet;
     const int k0 = kt * 64;
-    if (p.causal && k0 > wq_last) return;
-    f32x16_t s[2] = {f32x16_t{}, f32x16_t{}}, dp[2] = {f32x16_t{}, f32x16_t{}};
+    if (kt >= nkt || (p.causal && k0 > wq_last)) return;
+    const bool interior = (!p.causal || k0 + 63 <= wq_first) && k0 + 64 <= seq;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       bf16x8_t ka[4], va[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        ka[ks] = row_frag(sk + row_addr(m, ks, lane));
-        va[ks] = row_frag(sv + row_addr(m, ks, lane));
+        ka[ks] = row_frag<SO>(fa.ra[m][ks]);
+        va[ks] = row_frag<SO + kTileBytes>(fa.ra[m][ks]);
       }
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       lds_tie(ka);
       lds_tie(va);
+      f32x16_t sv = f32x16_t{}, dp = f32x16_t{};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        s[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], s[m], 0, 0, 0);
-        dp[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp[m], 0, 0, 0);
+        sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
       }
-    }
-    const bool interior = (!p.causal || k0 + 63 <= wq_first) && k0 + 64 <= seq;
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(s[m][r] * scale - lq);
+        float pr = __builtin_amdgcn_exp2f(sv[r] * scale - lq);
         if (!interior) {
           const int key = k0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
           if (key >= seq || (p.causal && key > q)) pr = 0.0f;
         }
-        dp[m][r] = pr * (dp[m][r] - dl);
+        dp[r] = pr * (dp[r] - dl);
       }
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int m = st >> 1, hh = st & 1;
-      const bf16x8_t sf = pack8(dp[m], hh);
-      bf16x8_t ta[2];
+      for (int hh = 0; hh < 2; ++hh) {
+        const int st = 2 * m + hh;
+        const bf16x8_t sf = pack8(dp, hh);
+        bf16x8_t ta[2];
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-        ta[db] = tr_frag(sk + tr_addr(st, db, 0, lane), sk + tr_addr(st, db, 1, lane));
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      lds_tie(ta);
+        for (int db = 0; db < 2; ++db) ta[db] = tr_frag<SO>(fa.tr0[st][db], fa.tr1[st][db]);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_tie(ta);
 #pragma unroll
-      for (int db = 0; db < 2; ++db)
-        dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], sf, dqa[db], 0, 0, 0);
+        for (int db = 0; db < 2; ++db)
+          dqa[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[db], sf, dqa[db], 0, 0, 0);
+      }
     }
   };
 
-  Unroll<0, 2>::run([&](auto jc) {
-    if (decltype(jc)::value < nkt) issue(jc, decltype(jc)::value);
+  Unroll<0, NS - 1>::run([&](auto jc) {
+    if (decltype(jc)::value < nst) issue(jc, decltype(jc)::value);
   });
-  for (int k0 = 0; k0 < nkt; k0 += kBStages) {
-    Unroll<0, kBStages>::run([&](auto jc) {
+  for (int i0 = 0; i0 < nst; i0 += NS) {
+    Unroll<0, NS>::run([&](auto jc) {
       constexpr int J = decltype(jc)::value;
-      const int kt = k0 + J;
-      if (kt < nkt) {
-        if (kt + 1 < nkt) attn_wait_vmcnt<4>();
-        else attn_wait_vmcnt<0>();
+      const int si = i0 + J;
+      if (si < nst) {
+        if constexpr (NS == 3) {
+          if (si + 1 < nst) attn_wait_vmcnt<4>();
+          else attn_wait_vmcnt<0>();
+        } else {
+          attn_wait_vmcnt<0>();
+        }
         attn_sync();
-        if (kt + 2 < nkt) issue(std::integral_constant<int, (J + 2) % kBStages>{}, kt + 2);
-        compute(jc, kt);
+        if (si + NS - 1 < nst) issue(std::integral_constant<int, (J + NS - 1) % NS>{}, si + NS - 1);
+        compute(jc, si * KG + grp);
       }
     });
+  }
+  if constexpr (KG == 2) {
+    attn_sync();
+    float* x = reinterpret_cast<float*>(lds) + qw * 32 * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[(16 * db + r) * 64] = dqa[db][r];
+    }
+    attn_sync();
+    if (grp == 1) return;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dqa[db][r] += x[(16 * db + r) * 64];
   }
 
   if (q < seq) {
@@ -743,12 +836,22 @@ hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s) {
                      0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_kv_kernel, dim3(static_cast<unsigned>(bh * ((p.seq + 127) / 128))),
-                     dim3(256), 0, s, p);
+  // two query (key) groups per block while the grid leaves SIMDs with one wave
+  const int64_t kv_blocks = bh * ((p.seq + 127) / 128), q_blocks = bh * ((p.seq + kQB - 1) / kQB);
+  if (kv_blocks < 2 * 256)
+    hipLaunchKernelGGL(attn_bwd_kv_kernel<2>, dim3(static_cast<unsigned>(kv_blocks)), dim3(512), 0,
+                       s, p);
+  else
+    hipLaunchKernelGGL(attn_bwd_kv_kernel<1>, dim3(static_cast<unsigned>(kv_blocks)), dim3(256), 0,
+                       s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_bwd_q_kernel, dim3(static_cast<unsigned>(bh * ((p.seq + kQB - 1) / kQB))),
-                     dim3(256), 0, s, p);
+  if (q_blocks < 2 * 256)
+    hipLaunchKernelGGL(attn_bwd_q_kernel<2>, dim3(static_cast<unsigned>(q_blocks)), dim3(512), 0, s,
+                       p);
+  else
+    hipLaunchKernelGGL(attn_bwd_q_kernel<1>, dim3(static_cast<unsigned>(q_blocks)), dim3(256), 0, s,
+                       p);
   return hipGetLastError();
 }
 

@@ -623,6 +623,8 @@ def _attn_bwd_case(dev, batch, seq, heads, causal, seed, from_oracle=False):
     (3, 257, 2, True), (1, 384, 1, False), (1, 130, 1, True),
     (8, 512, 8, True),    # the attention-projection workload's shard: 8 x 512 tokens, 8 heads
     (6, 1024, 4, True),   # the ~350M-layer workload's shard: 6 x 1024 tokens, 4 heads
+    (2, 1024, 32, True),  # 512 key and query blocks: one group per block
+    (4, 200, 80, False),  # 640 blocks, ragged
 ])
 def test_attention_bwd(dev, batch, seq, heads, causal):
     """dQKV of the GPU forward -> backward chain against the oracle's gradient
