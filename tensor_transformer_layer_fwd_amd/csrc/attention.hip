@@ -65,18 +65,18 @@ __device__ __forceinline__ void attn_sync() {
 }
 
 // KG key groups: with KG = 2 a block has 8 waves; waves w and w + 4 take the
-// same 32 queries and alternate key tiles (group g the tiles KG*i + g, from the
-// g-th tile of each stage), and merge their running statistics and outputs
+// same 32 queries and alternate key tiles (group g the tiles KG*i + g, through
+// a 3-stage ring of its own), and merge their running statistics and outputs
 // through LDS at the end. That halves the serial chain of a long causal row
 // and puts two waves on each SIMD when a shard has only one wave per SIMD's
 // worth of queries, so one wave's softmax runs beside the other's MFMAs.
 template <int KG>
 __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
-  constexpr int kSet = KG * kStageBytes;  // bytes of one stage: KG (K, V) tile pairs
-  // stages: 3 of one pair, or 2 of two pairs (every fragment read keeps its
-  // stage offset within the 16-bit immediate)
-  constexpr int NS = KG == 2 ? 2 : kStages;
-  constexpr int kLds = NS * kSet;
+  // one 3-stage ring of (K, V) tile pairs per key group, so that every stage
+  // offset a fragment read adds fits the instruction's 16-bit immediate
+  constexpr int NS = kStages;
+  constexpr int kRing = NS * kStageBytes;
+  constexpr int kLds = KG * kRing;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qw = wave & 3, grp = wave >> 2;  // query sub-block, key group
@@ -105,8 +105,8 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
   for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qf[ks]));
 
   // ---- tile copies: 16 windows of 1 KiB per (K, V) pair (8 of K, 8 of V),
-  // KG pairs per stage, four windows per wave; window w is pair w/16 of the
-  // stage, tile (w/8)%2 (K or V), rows 8*(w%8) .. +7; lane L copies row
+  // KG pairs per stage, four windows per wave; window w goes to group w/16's
+  // ring, tile (w/8)%2 (K or V), rows 8*(w%8) .. +7; lane L copies row
   // 8*(w%8) + L/8, physical chunk L%8.
   const uint16_t* src[4];
 #pragma unroll
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
   // still copied (its rows clamp to the sequence's last) so that every wave
   // issues the same number of copies, and is never used
   auto issue = [&](auto stage_c, int kp) {
-    uint8_t* st = attn_lds<kLds>() + decltype(stage_c)::value * kSet;
+    uint8_t* st = attn_lds<kLds>() + decltype(stage_c)::value * kStageBytes;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int w = wave * 4 + i, r = 8 * (w % 8) + lane / 8;
@@ -127,9 +127,10 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
       // keys past the sequence read its last row (they are masked)
       const int64_t over = kb * kKB + r - (seq - 1);
       const uint16_t* g = src[i] + kb * kKB * p.ld_qkv - (over > 0 ? over * p.ld_qkv : 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
-                                       (__attribute__((address_space(3))) void*)(st + w * 1024),
-                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)g,
+          (__attribute__((address_space(3))) void*)(st + (w / 16) * kRing + (w % 16) * 1024), 16,
+          0, 0);
     }
   };
 
@@ -147,7 +148,7 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
 
   // per-lane LDS byte addresses of the fragment reads within stage 0 (this
   // key group's tile pair)
-  const uint32_t lds0 = attn_lds_addr(attn_lds<kLds>()) + grp * kStageBytes;
+  const uint32_t lds0 = attn_lds_addr(attn_lds<kLds>()) + grp * kRing;
   uint32_t ka[2][4];  // K tile: key row 32m + ql, 16-byte chunk 2ks + half
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
   }
 
   auto compute = [&](auto stage_c, int kb) {
-    constexpr int SOFF = decltype(stage_c)::value * kSet;
+    constexpr int SOFF = decltype(stage_c)::value * kStageBytes;
     const int k0 = kb * kKB;
     if (kb >= nkb || (p.causal && k0 > wq_last)) return;  // no visible key in the tile
     // K fragments for S^T
@@ -479,9 +480,11 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t& v, int hh) {
 // and dK^T += Q^T dS.
 template <int QG>
 __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) {
-  constexpr int kSet = QG * kBStageBytes;  // one stage: QG query tiles (Q, dC, stats)
-  constexpr int NS = QG == 2 ? 2 : kBStages;
-  constexpr int kLds = NS * kSet;
+  // one 3-stage ring of query tiles (Q, dC, stats) per group: every stage
+  // offset fits the 16-bit immediate of the fragment reads
+  constexpr int NS = kBStages;
+  constexpr int kRing = NS * kBStageBytes;
+  constexpr int kLds = QG * kRing;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kw = wave & 3, grp = wave >> 2;
@@ -520,12 +523,12 @@ __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) 
   cd.init(dcp, p.ld_dc, row0, h * kD, 2 * kw, lane);   // dC tile
   uint8_t* const lds = attn_bwd_lds<kLds>();
   FragAddr fa;
-  fa.init(attn_lds_addr(lds) + grp * kBStageBytes, lane);
+  fa.init(attn_lds_addr(lds) + grp * kRing, lane);
   // stats copy: waves 0 and 2 of a group copy lse, 1 and 3 delta, of queries
   // qt*64 + lane (a tile past the last one is copied clamped and never used)
   const float* stat_src = (kw & 1 ? p.delta : p.lse) + lbase;
   auto issue = [&](auto stage_c, int si) {
-    uint8_t* st = lds + decltype(stage_c)::value * kSet + grp * kBStageBytes;
+    uint8_t* st = lds + grp * kRing + decltype(stage_c)::value * kBStageBytes;
     const int64_t q0 = static_cast<int64_t>(qt0 + si * QG + grp) * 64;
     cq.issue(st, q0, seq, p.ld_qkv, 2 * kw, lane);
     cd.issue(st + kTileBytes, q0, seq, p.ld_dc, 2 * kw, lane);
@@ -540,8 +543,8 @@ __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) 
   const int wk_first = kb * 128 + kw * 32;  // this wave's first key
 
   auto compute = [&](auto stage_c, int qt) {
-    constexpr int SO = decltype(stage_c)::value * kSet;
-    const float* stats = reinterpret_cast<const float*>(lds + SO + grp * kBStageBytes + 2 * kTileBytes);
+    constexpr int SO = decltype(stage_c)::value * kBStageBytes;
+    const float* stats = reinterpret_cast<const float*>(lds + grp * kRing + SO + 2 * kTileBytes);
     const int q0 = qt * 64;
     if (qt >= nqt || (p.causal && q0 + 63 < wk_first)) return;  // no query sees these keys
     const bool interior = (!p.causal || q0 >= wk_first + 31) && q0 + 64 <= seq;
@@ -676,9 +679,9 @@ __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) 
 template <int KG>
 __global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
   constexpr int kPair = 2 * kTileBytes;  // one K and one V tile
-  constexpr int kSet = KG * kPair;
-  constexpr int NS = KG == 2 ? 2 : kBStages;
-  constexpr int kLds = NS * kSet;
+  constexpr int NS = kBStages;            // a 3-stage ring of pairs per group
+  constexpr int kRing = NS * kPair;
+  constexpr int kLds = KG * kRing;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int qw = wave & 3, grp = wave >> 2;
@@ -717,11 +720,11 @@ __global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
   cv.init(qkv, p.ld_qkv, row0, 2 * hd + h * kD, 2 * qw, lane);
   uint8_t* const lds = attn_bwd_lds<kLds>();
   FragAddr fa;
-  fa.init(attn_lds_addr(lds) + grp * kPair, lane);
+  fa.init(attn_lds_addr(lds) + grp * kRing, lane);
   // stage si holds key tiles KG*si .. KG*si + KG-1 (one past the last is
   // copied clamped and never used)
   auto issue = [&](auto stage_c, int si) {
-    uint8_t* st = lds + decltype(stage_c)::value * kSet + grp * kPair;
+    uint8_t* st = lds + grp * kRing + decltype(stage_c)::value * kPair;
     const int64_t k0 = static_cast<int64_t>(si * KG + grp) * 64;
     ck.issue(st, k0, seq, p.ld_qkv, 2 * qw, lane);
     cv.issue(st + kTileBytes, k0, seq, p.ld_qkv, 2 * qw, lane);
@@ -730,7 +733,7 @@ __global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
   const float scale = p.scale_log2;
 
   auto compute = [&](auto stage_c, int kt) {
-    constexpr int SO = decltype(stage_c)::value * kSet;
+    constexpr int SO = decltype(stage_c)::value * kPair;
     const int k0 = kt * 64;
     if (kt >= nkt || (p.causal && k0 > wq_last)) return;
     const bool interior = (!p.causal || k0 + 63 <= wq_first) && k0 + 64 <= seq;
