@@ -275,3 +275,17 @@ def test_gemm_override(lib):
     finally:
         L.tp_set_gemm_override(0)
     assert L.tp_gemm_plan(1024, 512, 4096, allow_split=True) == own
+
+
+def test_valid_call_without_a_device_reports_hip_error(lib):
+    """With no GPU present, a call that passes validation reports TP_ERR_HIP
+    (and the hipError_t) instead of crashing. Skipped wherever a device
+    exists: the pointers here are host memory."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present; this case is for hosts without one")
+    buf = ctypes.create_string_buffer(4096)
+    x = ctypes.c_void_p(ctypes.addressof(buf))
+    assert lib.tp_bias_act(x, None, x, 8, 8, 8, 8, 1, 1, 1, None) == -6
+    assert L.tp_last_hip_error() != 0
+    assert "TP_ERR_HIP" in L.tp_status_string(-6)
