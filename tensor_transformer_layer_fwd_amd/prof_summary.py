@@ -11,7 +11,7 @@
 `traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel into
 HBM bytes per launch, scaled by what the same counters read for a plain device
 copy of known size run in the same process (bench.py --calibrate-copy), and
-records a hash of the kernel sources so that bench.py reports the figure only
+records a hash of the pipelined GEMM sources so that bench.py reports the figure only
 while the kernels are unchanged.
 """
 from __future__ import annotations
@@ -27,11 +27,17 @@ import statistics
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 
+# Sources of the pipelined bf16 GEMM kernels and of their tile choice: the
+# kernels whose HBM traffic profiles/traffic.json records.
+GEMM_SOURCES = ("gemm_bf16_pipe.hip", "device_common.h", "internal.h", "colsum_device.h",
+                "plan.hip")
+
+
 def source_hash() -> str:
-    """sha256 over the kernel sources and the public header."""
+    """sha256 over the pipelined GEMM sources and the public header."""
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
-    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc))
+    files = [os.path.join(csrc, f) for f in GEMM_SOURCES]
     files.append(os.path.join(os.path.dirname(PKG), "include", "tp_mlp.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
