@@ -84,6 +84,19 @@ def shard_calls(step, i=0):
     ]
 
 
+def gemm_call_bytes(cfg, name):
+    """Algorithmic HBM bytes of one single-GEMM call of the bf16 MLP step: every
+    operand read once, every output written once (bf16 activations, fp32
+    partials)."""
+    T, h, F, e = cfg.T, cfg.h, cfg.F, 2
+    return {
+        "fc1_fwd": T * h * e + h * F * e + (F * e if cfg.has_bias else 0) + 2 * T * F * e,
+        "fc2_fwd": T * F * e + F * h * e + T * h * 4,
+        "fc2_dgrad": T * h * e + F * h * e + 2 * T * F * e,
+        "fc1_dgrad": T * F * e + h * F * e + T * h * 4,
+    }[name]
+
+
 def time_call(fn, reps):
     """Average device duration (ms) of one call: `reps` back-to-back calls are
     captured into a HIP graph (so host launch cost is off the timed path) and
@@ -278,7 +291,12 @@ def main():
     single = [k for k in kernels if not k.endswith("wgrad")]
     dom = max(single, key=lambda k: kernels[k]["us"])
     dom_flops = 2 * cfg.T * cfg.h * cfg.F
-    dom_tf = dom_flops / (kernels[dom]["us"] * 1e-6) / 1e12
+    dom_bytes = gemm_call_bytes(cfg, dom)
+    dom_s = kernels[dom]["us"] * 1e-6
+    dom_tf = dom_flops / dom_s / 1e12
+    dom_gbs = dom_bytes / dom_s / 1e9
+    # the roof that takes longer at peak bounds the kernel
+    hbm_bound = dom_bytes / (PEAK_HBM_GBS * 1e9) > dom_flops / (PEAK_BF16_TFLOPS * 1e12)
     dom_shape = {"fc1_fwd": (cfg.T, cfg.F, cfg.h), "fc2_fwd": (cfg.T, cfg.h, cfg.F),
                  "fc2_dgrad": (cfg.T, cfg.F, cfg.h), "fc1_dgrad": (cfg.T, cfg.h, cfg.F)}[dom]
     from tensor_transformer_layer_fwd_amd import _lib as L
@@ -392,10 +410,16 @@ def main():
                                f"h={cfg.h}, p={cfg.p} shards run serially",
                    "tokens": cfg.T, "h": cfg.h, "p": cfg.p, "ffn_shard": cfg.F,
                    "gemm_gflop_per_step": round(flops / 1e9, 2)},
-        "roofline": {"bound": "mfma", "kernel": dom, "achieved": round(dom_tf, 1),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"bound": "hbm" if hbm_bound else "mfma", "kernel": dom,
+                     "achieved": round(dom_gbs if hbm_bound else dom_tf, 1),
+                     "peak": PEAK_HBM_GBS if hbm_bound else PEAK_BF16_TFLOPS,
+                     "unit": "GB/s" if hbm_bound else "TFLOP/s",
+                     "frac": round(dom_gbs / PEAK_HBM_GBS if hbm_bound
+                                   else dom_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(dom),
+                     "algorithmic_bytes": dom_bytes, "gemm_flops": dom_flops,
+                     "tflops": round(dom_tf, 1),
+                     "mfma_frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
                      "gemm": {"M": dom_shape[0], "N": dom_shape[1], "K": dom_shape[2],
                               "tile": dom_plan[0], "us_per_launch": kernels[dom]["us"]}},
         "per_call_shard0": kernels,
