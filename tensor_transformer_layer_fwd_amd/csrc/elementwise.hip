@@ -152,6 +152,36 @@ __global__ __launch_bounds__(256) void reduce_vec4_kernel(ReduceParams p) {
   }
 }
 
+// Eight consecutive columns per thread: two 16-byte loads per partial in
+// flight and one 16-byte bf16 store (or two fp32 ones), with 32-bit index
+// arithmetic (the host checks T * N / 8 < 2^31). Same summation order as the
+// four-column path: partials in shard order, then the bias.
+__global__ __launch_bounds__(256) void reduce_vec8_kernel(ReduceParams p) {
+  const uint32_t no = static_cast<uint32_t>(p.N >> 3);
+  const uint32_t total = static_cast<uint32_t>(p.T) * no;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const uint32_t t = e / no, c = (e - t * no) << 3;
+    const int64_t ip = static_cast<int64_t>(t) * p.ldp + c;
+    float s[8];
+    load8_f32(p.parts[0], ip, s);
+    for (int i = 1; i < p.p; ++i) {
+      float v[8];
+      load8_f32(p.parts[i], ip, v);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] += v[q];
+    }
+    if (p.bias) {
+      float b[8];
+      if (p.out_bf16) load8_bf16(p.bias, c, b);
+      else load8_f32(p.bias, c, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s[q] += b[q];
+    }
+    store8(p.out, static_cast<int64_t>(t) * p.ldo + c, s, p.out_bf16);
+  }
+}
+
 __global__ __launch_bounds__(256) void reduce_scalar_kernel(ReduceParams p) {
   const int64_t total = p.T * p.N;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
@@ -175,6 +205,29 @@ __global__ __launch_bounds__(256) void bias_act_kernel(BiasActParams p) {
                       : load_elem(p.u, t * p.ldu + c, p.in_bf16);
     if (p.bias) u += load_elem(p.bias, c, p.in_bf16);
     store_elem(p.y, t * p.ldy + c, apply_act(p.act, u), p.out_bf16);
+  }
+}
+
+// Vector path of bias_act: fp32 U, bf16 Y, eight columns per thread (two
+// 16-byte loads, one 16-byte store), 32-bit index arithmetic.
+__global__ __launch_bounds__(256) void bias_act_vec8_kernel(BiasActParams p) {
+  const uint32_t no = static_cast<uint32_t>(p.N >> 3);
+  const uint32_t total = static_cast<uint32_t>(p.T) * no;
+  const uint32_t stride = gridDim.x * blockDim.x;
+  for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
+    const uint32_t t = e / no, c = (e - t * no) << 3;
+    float u[8];
+    load8_f32(p.u, static_cast<int64_t>(t) * p.ldu + c, u);
+    if (p.bias) {
+      float b[8];
+      if (p.in_bf16) load8_bf16(p.bias, c, b);
+      else load8_f32(p.bias, c, b);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) u[q] += b[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) u[q] = apply_act(p.act, u[q]);
+    store8(p.y, static_cast<int64_t>(t) * p.ldy + c, u, 1);
   }
 }
 
@@ -268,6 +321,15 @@ hipError_t launch_colsum(const ColsumParams& p, hipStream_t s) {
 }
 
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
+  auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  bool vec8 = p.N % 8 == 0 && p.ldp % 4 == 0 && p.ldo % 8 == 0 && a16(p.out) &&
+              (!p.bias || a16(p.bias)) && p.T * (p.N / 8) < (int64_t(1) << 31);
+  for (int i = 0; i < p.p; ++i) vec8 = vec8 && a16(p.parts[i]);
+  if (vec8) {
+    hipLaunchKernelGGL(reduce_vec8_kernel, dim3(grid_for(p.T * (p.N / 8), 256)), dim3(256), 0,
+                       s, p);
+    return hipGetLastError();
+  }
   bool vec = (p.N % 4 == 0) && (p.ldp % 4 == 0) && (p.ldo % 4 == 0);
   for (int i = 0; i < p.p; ++i) vec = vec && (reinterpret_cast<uintptr_t>(p.parts[i]) % 16 == 0);
   vec = vec && (reinterpret_cast<uintptr_t>(p.out) % (p.out_bf16 ? 8 : 16) == 0);
@@ -280,6 +342,13 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
 }
 
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s) {
+  auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
+  if (p.u_f32 && p.out_bf16 && p.N % 8 == 0 && p.ldu % 4 == 0 && p.ldy % 8 == 0 && a16(p.u) &&
+      a16(p.y) && (!p.bias || a16(p.bias)) && p.T * (p.N / 8) < (int64_t(1) << 31)) {
+    hipLaunchKernelGGL(bias_act_vec8_kernel, dim3(grid_for(p.T * (p.N / 8), 256)), dim3(256), 0,
+                       s, p);
+    return hipGetLastError();
+  }
   const bool vec = p.u_f32 && p.out_bf16 && (p.N % 4 == 0) && (p.ldu % 4 == 0) &&
                    (p.ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(p.u) % 16 == 0) &&
                    (reinterpret_cast<uintptr_t>(p.y) % 8 == 0);

@@ -199,9 +199,12 @@ def test_linear_bwd_wgrad(dev, dt, T, k, n, accumulate, bias):
 @pytest.mark.parametrize("out_dt", DTS)
 @pytest.mark.parametrize("p", [1, 2, 3, 8, 16])
 @pytest.mark.parametrize("T,h", [(1, 1), (7, 13), (64, 768), (33, 1028)])
-def test_reduce_partials(dev, out_dt, p, T, h):
+@pytest.mark.parametrize("pad", [3, 8])
+def test_reduce_partials(dev, out_dt, p, T, h, pad):
+    """Output row stride h + pad: pad 8 keeps 16-byte aligned rows, which takes
+    the eight-column path where h is a multiple of 8."""
     import tensor_transformer_layer_fwd_amd as tp
-    _say(f"reduce out={out_dt} p={p} T={T} h={h}")
+    _say(f"reduce out={out_dt} p={p} T={T} h={h} pad={pad}")
     rng = np.random.default_rng(p * 100 + T + h)
     parts = [rng.standard_normal((T, h)).astype(np.float32) for _ in range(p)]
     bias, biasr = rand(rng, (h,), 0.5, out_dt)
@@ -209,7 +212,7 @@ def test_reduce_partials(dev, out_dt, p, T, h):
     for i in range(p):
         big[i, :, :h] = torch.from_numpy(parts[i])
     views = [big[i, :, :h] for i in range(p)]
-    out = Guarded(T, h, out_dt, dev)
+    out = Guarded(T, h, out_dt, dev, pad=pad)
     tp.tp_reduce_partials(views, upload(biasr, out_dt, dev), out.view)
     torch.cuda.synchronize()
     ref = oracle.reduce_partials([x.astype(np.float64) for x in parts], bias)
@@ -268,13 +271,19 @@ def test_reduce_partials_order_and_rounding(dev):
 
 @pytest.mark.parametrize("in_dt,out_dt", [("f32", "bf16"), ("bf16", "bf16"), ("f32", "f32")])
 @pytest.mark.parametrize("T,n", [(3, 5), (64, 1536), (17, 260)])
-def test_bias_act(dev, in_dt, out_dt, T, n):
+@pytest.mark.parametrize("pad,with_bias", [(3, True), (8, True), (8, False)])
+def test_bias_act(dev, in_dt, out_dt, T, n, pad, with_bias):
+    """Output row stride n + pad: pad 8 keeps 16-byte aligned rows (the
+    eight-column path for fp32 U and bf16 Y where n is a multiple of 8)."""
     import tensor_transformer_layer_fwd_amd as tp
     rng = np.random.default_rng(T * n)
     U, Ur = rand(rng, (T, n), 2.0, in_dt)
     b, br = rand(rng, (n,), 0.1, in_dt)
-    Y = Guarded(T, n, out_dt, dev)
-    tp.tp_bias_act(upload(Ur, in_dt, dev), upload(br, in_dt, dev), Y.view, act="gelu")
+    if not with_bias:
+        b = np.zeros_like(b)
+    Y = Guarded(T, n, out_dt, dev, pad=pad)
+    tp.tp_bias_act(upload(Ur, in_dt, dev), upload(br, in_dt, dev) if with_bias else None, Y.view,
+                   act="gelu")
     torch.cuda.synchronize()
     ref = oracle.gelu_tanh(U + b[None, :])
     assert err(Y.value(), ref) <= (TOL["bf16"] if out_dt == "bf16" else 1e-6)
