@@ -11,7 +11,7 @@ attention on its own Q, K and V; the result C_i feeds the row-split output
 projection. The same page's optimisation list recommends a fused
 (FlashAttention-style) attention kernel. The pages do not write the attention
 out; this is the textbook scaled dot-product attention of a GPT decoder, with
-these readings (also listed in the design doc):
+these readings:
 
   * QKV_i [T, 3*H*d] holds [Q | K | V], each third head-major: head j at
     columns j*d .. j*d+d-1 of its third;

@@ -8,7 +8,7 @@ Source: the "Megatron" page (zzmblog.top), "mixed-precision training": besides
 FP16/BF16 the framework trains in FP8 on Hopper GPUs; the "Megatron-LM
 quick-start" page (blog.gitcode.com), "performance optimisation", recommends
 mixed precision such as FP8. The pages fix neither the format nor the scaling.
-Readings (also listed in the design doc):
+Readings:
 
   * formats: the OCP 8-bit floats E4M3 (exponent bias 7, 3 mantissa bits, no
     infinities, largest finite 448) and E5M2 (bias 15, 2 mantissa bits,

@@ -22,7 +22,7 @@ The backward products are not on the pages; they are the textbook derivatives
 of the forward definitions (d(XW)/dX = dOut W^T, d(XW)/dW = X^T dOut, bias grad
 = column sum), and the GeLU derivative is the derivative of the tanh form.
 
-Readings where the pages are silent (listed in the design doc as well): rows of X are
+Readings where the pages are silent: rows of X are
 tokens; weights are stored [in, out]; shards are contiguous equal blocks; GeLU is
 the tanh form with constants sqrt(2/pi) and 0.044715 (Hendrycks & Gimpel); the
 row-parallel bias is added once, after the sum over shards.
