@@ -84,6 +84,24 @@ def shard_calls(step, i=0):
     ]
 
 
+def layer_bwd_calls(step, i=0):
+    """Both gradients of each MLP layer of shard i in one tp_linear_bwd call, as
+    the step runs them: (name, thunk, gemm flops)."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    cfg, o, inp = step.cfg, step.out, step.inp
+    F = cfg.F
+    A_i, B_i = step._col("A", i, F), step._row("B", i, F)
+    f = 4 * cfg.T * cfg.h * F
+    return [
+        ("fc2_bwd", lambda: L.tp_linear_bwd(inp["dZ"], B_i, o[f"U_{i}"], o[f"Y_{i}"], o[f"dU_{i}"],
+                                            o[f"dB_{i}"], o.get("db"), act="gelu",
+                                            workspace=step.workspace), f),
+        ("fc1_bwd", lambda: L.tp_linear_bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"],
+                                            o[f"dA_{i}"], o.get(f"da_{i}"), act="none",
+                                            workspace=step.workspace), f),
+    ]
+
+
 def gemm_call_bytes(cfg, name):
     """Algorithmic HBM bytes of one single-GEMM call of the bf16 MLP step: every
     operand read once, every output written once (bf16 activations, fp32
@@ -286,6 +304,11 @@ def main():
         ms = time_call(fn, args.kernel_reps)
         kernels[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
     gemm_sum_us = sum(v["us"] for v in kernels.values()) * len(cfg.shards)
+    # each layer's two gradients as the step runs them: one tp_linear_bwd call
+    layer_bwd = {}
+    for name, fn, f in layer_bwd_calls(step):
+        ms = time_call(fn, args.kernel_reps)
+        layer_bwd[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
     # dominant kernel: the slowest call that is a single GEMM kernel (the wgrad
     # calls also launch a split-K fix-up and the bias column sums)
     single = [k for k in kernels if not k.endswith("wgrad")]
@@ -424,6 +447,7 @@ def main():
                               "tile": dom_plan[0], "us_per_launch": kernels[dom]["us"]}},
         "per_call_shard0": kernels,
         "gemm_calls_sum_us": round(gemm_sum_us, 1),
+        "layer_bwd_shard0": layer_bwd,
         "hbm_passes": hbm,
         "cpu_baseline": cpu,
         "extra": extra,

@@ -182,6 +182,40 @@ int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
                                        size_t* bytes);
 
 /*
+ * The whole backward of one linear layer of the shard, the data gradient and
+ * the weight gradient of the same forward product (derivatives of the
+ * column- and row-parallel products of the "Megatron" page, "Tensor
+ * Parallelism / mathematical principles"; the pages do not write the backward
+ * out):
+ *
+ *   dIn   = (dOut W^T) [* act'(U)]    as tp_linear_bwd_dgrad
+ *   dW    (+)= In^T dOut, dbias (+)= column sums of dOut
+ *                                     as tp_linear_bwd_wgrad
+ *
+ * Same arguments, layouts, dtypes and results as those two calls made one
+ * after the other with the same values (dIn to within the rounding of its
+ * own call, bitwise; dW and dbias to within fp32 summation order: the K slices
+ * of the weight gradient may differ). For bf16 operands whose products both
+ * fit one of the pipelined tiles 128x192, 128x128 or 256x192 (16-byte aligned
+ * operands, row strides a multiple of 8, T a multiple of 64, k and n tile
+ * multiples), both products run in one launch, the weight gradient's blocks
+ * first, which saves one kernel's start and drain; otherwise the two calls
+ * run. dIn and dW must not overlap any input. workspace: at least
+ * tp_linear_bwd_workspace_size() bytes for the same (T, k, n, dt) (a smaller
+ * one that still fits tp_linear_bwd_wgrad runs the two calls); contents on
+ * entry ignored; not shared by calls that may run at the same time. Errors as
+ * the two calls; every check of both runs before the first launch.
+ */
+int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const void* In,
+                  void* dIn, float* dW, float* dbias, int64_t T, int64_t k, int64_t n,
+                  int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_in, int64_t ld_din,
+                  int64_t ld_dw, int accumulate, int dt, int out_dt, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* Scratch bytes tp_linear_bwd needs for (T, k, n, dt); pure host function. */
+int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t* bytes);
+
+/*
  * Sum over shards, the one-GPU stand-in for the All-Reduce ("Megatron" page,
  * "Tensor Parallelism / mathematical principles": the row-split partials Y_i B_i
  * are summed across GPUs; "Transformer-layer tensor parallelism": one such sum

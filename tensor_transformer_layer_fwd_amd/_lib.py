@@ -35,6 +35,10 @@ SIGNATURES = {
                                    _int, _vp, _sz, _vp]),
     "tp_linear_bwd_wgrad_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_linear_bwd": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
+                             _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz, _vp]),
+    "tp_linear_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int,
+                                            ctypes.POINTER(ctypes.c_size_t)]),
     "tp_reduce_partials": (_int, [ctypes.POINTER(ctypes.c_void_p), _int, _vp, _vp, _i64, _i64, _i64,
                                   _i64, _int, _vp]),
     "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
@@ -191,6 +195,27 @@ def tp_linear_bwd_wgrad(In, dOut, dW, dbias=None, accumulate=False, workspace=No
     _check("tp_linear_bwd_wgrad", lib().tp_linear_bwd_wgrad(
         _ptr(In), _ptr(dOut), _ptr(dW), _ptr(dbias), T, k, n, _ld(In), _ld(dOut), _ld(dW),
         int(bool(accumulate)), _dt(In), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_linear_bwd_workspace_size(T: int, k: int, n: int, dt: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_linear_bwd_workspace_size",
+           lib().tp_linear_bwd_workspace_size(T, k, n, dt, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_linear_bwd(dOut, W, U, In, dIn, dW, dbias=None, act="none", accumulate=False,
+                  workspace=None, stream=None):
+    """Both gradients of one linear layer: dIn = (dOut W^T) [* act'(U)] and
+    dW (+)= In^T dOut, dbias (+)= column sums of dOut."""
+    T, n = dOut.shape
+    k = W.shape[0]
+    ld_u = _ld(U) if U is not None else k
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tp_linear_bwd", lib().tp_linear_bwd(
+        _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(In), _ptr(dIn), _ptr(dW), _ptr(dbias),
+        T, k, n, _ld(dOut), _ld(W), ld_u, _ld(In), _ld(dIn), _ld(dW), int(bool(accumulate)),
+        _dt(dOut), _dt(dIn), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def tp_reduce_partials(partials, bias, out, stream=None):

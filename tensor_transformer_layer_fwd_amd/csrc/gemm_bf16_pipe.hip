@@ -252,8 +252,10 @@ struct OperandF8 {
 // ---------------------------------------------------------------------------
 // F8 = 0: bf16 operands; F8 = 1 + fmt_a + 2 * fmt_b: FP8 codes (both operands
 // K-contiguous, BK = 128 codes), fmt 0 = E4M3, 1 = E5M2.
+// One block of a product: output tile (or column-sum unit) number `block` of
+// the product's 1-D grid.
 template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams p) {
+__device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int block) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -280,17 +282,17 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   const int ntiles = tiles_m * tiles_n;
   // One block per (K slice z, tile) in a 1-D grid, slice-major; blocks past
   // the last slice's tiles run column-sum pass-1 units.
-  const int z = static_cast<int>(blockIdx.x) / ntiles;
+  const int z = block / ntiles;
   if constexpr (EK == kEpiF32) {
     if (z >= p.splitk) {
-      const int e = blockIdx.x - p.splitk * ntiles, ncb = static_cast<int>((p.cs.N + 255) / 256);
+      const int e = block - p.splitk * ntiles, ncb = static_cast<int>((p.cs.N + 255) / 256);
       float(*part)[256] = reinterpret_cast<float(*)[256]>(stage_buf<0, SB>());
       for (int u = e; u < p.cs_units; u += p.cs_blocks)
         colsum_vec_unit(p.cs, u % ncb, u / ncb, p.cs_nchunks, part);
       return;
     }
   }
-  int bid = static_cast<int>(blockIdx.x) - z * ntiles;
+  int bid = block - z * ntiles;
   if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
   constexpr int G = 8;
   const int group = bid / (G * tiles_n);
@@ -588,6 +590,23 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
   });
 }
 
+template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams p) {
+  gemm_pipe_block<BM, BN, WM, WN, BK, S, AK, BKC, EK, F8>(p, static_cast<int>(blockIdx.x));
+}
+
+// The backward of one linear layer in one launch: the weight gradient (TN,
+// fp32, K slices and column-sum units as in its own launch) in blocks
+// 0 .. nblk_w-1, then the data gradient (NT, epilogue EKD). Both products use
+// the same tile, K-tile and stage count, so they share the LDS stages.
+template <int BM, int BN, int WM, int WN, int BK, int S, int EKD>
+__global__ __launch_bounds__(WM* WN * 64) void gemm_bwd_pair_kernel(GemmParams pw, GemmParams pd,
+                                                                    int nblk_w) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < nblk_w) gemm_pipe_block<BM, BN, WM, WN, BK, S, false, false, kEpiF32>(pw, b);
+  else gemm_pipe_block<BM, BN, WM, WN, BK, S, true, true, EKD>(pd, b - nblk_w);
+}
+
 // Epilogue kinds instantiated per layout (bf16) or operand formats (FP8):
 // bf16 NN carries fc1's bias + GeLU, NT the dgrads, TN the weight gradients;
 // FP8 E4M3 x E4M3 every kind, E5M2 x E4M3 (data gradients) the dgrad kinds,
@@ -717,7 +736,49 @@ int fp8_epilogue_kind(const GemmParams& p) {
   }
 }
 
+template <int BM, int BN, int WM, int WN, int BK, int S>
+hipError_t launch_pair_cfg(const GemmParams& pw, const GemmParams& pd, int ekd, hipStream_t s) {
+  const int nblk_w = static_cast<int>((pw.M / BM) * (pw.N / BN) * pw.splitk) + pw.cs_blocks;
+  const int nblk_d = static_cast<int>((pd.M / BM) * (pd.N / BN));
+  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d)), block(WM * WN * 64);
+  switch (ekd) {
+    case kEpiF32:
+      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiF32>), grid, block, 0, s,
+                         pw, pd, nblk_w);
+      break;
+    case kEpiBF16:
+      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiBF16>), grid, block, 0,
+                         s, pw, pd, nblk_w);
+      break;
+    case kEpiDGelu:
+      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiDGelu>), grid, block, 0,
+                         s, pw, pd, nblk_w);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool pair_tile_ok(int tile) {
+  return tile == kPipe128x192 || tile == kPipe128x128 || tile == kPipe256x192;
+}
+
+hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int tile, int ekd,
+                                hipStream_t s) {
+  switch (tile) {
+    case kPipe128x192:
+      return launch_pair_cfg<128, 192, 2, 2, 64, 3>(pw, pd, ekd, s);
+    case kPipe128x128:
+      return launch_pair_cfg<128, 128, 2, 2, 64, 3>(pw, pd, ekd, s);
+    case kPipe256x192:
+      return launch_pair_cfg<256, 192, 4, 2, 64, 2>(pw, pd, ekd, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_gemm_fp8(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
   const int ek = fp8_epilogue_kind(p);

@@ -179,6 +179,17 @@ enum EpiKind : int { kEpiNone = -1, kEpiF32 = 0, kEpiBF16 = 1, kEpiBiasGelu = 2,
 int pipe_epilogue_kind(const GemmParams& p);  // kEpiNone: use the general kernel
 hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int ek,
                                  hipStream_t s);
+// The backward of one linear layer in one launch: the weight gradient pw (TN,
+// fp32 epilogue, K slices and carried column-sum units set as for its own
+// launch) and then the data gradient pd (NT, epilogue kind ekd), both on
+// pipelined tile `tile`, which pair_tile_ok accepts (64-wide K-tiles in both
+// layouts). The split-K fix-up is a launch of its own.
+bool pair_tile_ok(int tile);
+hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int tile, int ekd,
+                                hipStream_t s);
+// K slices of the weight gradient paired with its data gradient on `tile`
+// (T a multiple of 64 * slices); 0 for an unknown tile.
+int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n);
 hipError_t launch_gemm_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s);
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);

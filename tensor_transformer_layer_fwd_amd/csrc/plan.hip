@@ -8,6 +8,10 @@
 // fix-up launch.
 #include <hip/hip_runtime.h>
 
+#include <functional>
+#include <queue>
+#include <vector>
+
 #include "internal.h"
 
 namespace tpmlp {
@@ -112,6 +116,44 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
 }
 
 }  // namespace
+
+int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n) {
+  const PipeTile* t = find_tile(tile);
+  if (!t) return 0;
+  if (g_force_tile != 0 && g_force_split > 1 && T % (64 * g_force_split) == 0)
+    return g_force_split;
+  // one block per CU (the paired tiles fill most of the LDS); blocks go to the
+  // CU that frees first, the weight gradient's slices first
+  const double ktile = 2.0 * t->bm * t->bn * 64.0 / t->flop_per_sec_per_cu;
+  const int64_t tiles_w = (k / t->bm) * (n / t->bn), tiles_d = (T / t->bm) * (k / t->bn);
+  int best = 0;
+  double best_c = 1e30;
+  for (int sp : {1, 2, 4, 8}) {
+    if (sp > 1 && (T % (64 * sp) || T / sp < 256)) continue;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+    for (int c = 0; c < kCUs; ++c) cu.push(0.0);
+    auto run = [&](int64_t blocks, double sec) {
+      for (int64_t b = 0; b < blocks; ++b) {
+        const double f = cu.top();
+        cu.pop();
+        cu.push(f + kRoundOverheadSec + sec);
+      }
+    };
+    run(tiles_w * sp, static_cast<double>(T / sp / 64) * ktile);
+    run(tiles_d, static_cast<double>(n / 64) * ktile);
+    double c = 0.0;
+    while (!cu.empty()) {
+      c = cu.top();
+      cu.pop();
+    }
+    if (sp > 1) c += (2.0 * sp + 1.0) * k * n * 4.0 / kHbmBytesPerSec + kLaunchSec;
+    if (c < best_c) {
+      best_c = c;
+      best = sp;
+    }
+  }
+  return best;
+}
 
 namespace {
 const TileId kF8Tiles[] = {kPipe256x192, kPipe128x256, kPipe128x192, kPipe128x128};

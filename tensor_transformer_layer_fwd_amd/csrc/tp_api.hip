@@ -118,6 +118,89 @@ size_t wgrad_split_bytes(int64_t T, int64_t k, int64_t n, int dt) {
   return (b + 255) / 256 * 256;
 }
 
+// Data gradient dIn[T,k] = dOut[T,n] W[k,n]^T (x act'(U)) as a product.
+GemmParams dgrad_params(const void* dOut, const void* W, const void* U, int act, void* dIn,
+                        int64_t T, int64_t k, int64_t n, int64_t ld_dout, int64_t ld_w,
+                        int64_t ld_u, int64_t ld_din, int out_dt) {
+  GemmParams p{};
+  p.a = dOut;
+  p.b = W;
+  p.c = dIn;
+  p.u = U;
+  p.M = T;
+  p.N = k;
+  p.K = n;
+  p.lda = ld_dout;
+  p.ldb = ld_w;
+  p.ldc = ld_din;
+  p.ldu = ld_u;
+  p.epi = act != TP_ACT_NONE ? EPI_DACT : EPI_STORE;
+  p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
+  p.out_bf16 = out_dt == TP_BF16;
+  p.a_kcontig = 1;  // dOut [T, n]
+  p.b_kcontig = 1;  // W [k, n] read as W^T: K (= n) contiguous
+  return p;
+}
+
+// Weight gradient dW[k,n] (+)= In[T,k]^T dOut[T,n] as a product, and the bias
+// gradient's column sums of dOut with their partials at cs_ws.
+GemmParams wgrad_params(const void* In, const void* dOut, float* dW, int64_t T, int64_t k,
+                        int64_t n, int64_t ld_in, int64_t ld_dout, int64_t ld_dw, int accumulate,
+                        void* ws) {
+  GemmParams p{};
+  p.a = In;
+  p.b = dOut;
+  p.c = dW;
+  p.M = k;
+  p.N = n;
+  p.K = T;
+  p.lda = ld_in;
+  p.ldb = ld_dout;
+  p.ldc = ld_dw;
+  p.epi = EPI_STORE;
+  p.out_bf16 = 0;
+  p.accumulate = accumulate != 0;
+  p.ws = static_cast<float*>(ws);
+  p.a_kcontig = 0;  // In [T, k] read as In^T: M (= k) contiguous
+  p.b_kcontig = 0;  // dOut [T, n]: N contiguous
+  return p;
+}
+
+ColsumParams bias_grad_params(const void* dOut, float* dbias, int64_t T, int64_t n,
+                              int64_t ld_dout, int dt, int accumulate, float* cs_ws) {
+  ColsumParams c{};
+  c.src = dOut;
+  c.T = T;
+  c.N = n;
+  c.ld = ld_dout;
+  c.src_bf16 = dt == TP_BF16;
+  c.dbias = dbias;
+  c.accumulate = accumulate != 0;
+  c.ws = cs_ws;
+  return c;
+}
+
+// Tile and K slices of the paired backward launch of a bf16 linear layer
+// (tile 0: the layer's products cannot pair). Shapes only, so the workspace
+// query and the call agree; operand alignment is checked at the call.
+SplitPlan pair_plan(int64_t T, int64_t k, int64_t n) {
+  const SplitPlan pd = plan_gemm_bf16(T, k, n, false);
+  if (!pair_tile_ok(pd.tile)) return SplitPlan{0, 1, T};
+  const int bm = pd.tile == kPipe256x192 ? 256 : 128;
+  const int bn = pd.tile == kPipe128x128 ? 128 : 192;
+  if (T % 64 || k % bm || n % bn) return SplitPlan{0, 1, T};
+  const int sp = plan_pair_split(pd.tile, T, k, n);
+  if (sp < 1) return SplitPlan{0, 1, T};
+  return SplitPlan{pd.tile, sp, T / sp};
+}
+
+size_t pair_split_bytes(int64_t T, int64_t k, int64_t n) {
+  const SplitPlan pl = pair_plan(T, k, n);
+  if (pl.tile == 0 || pl.splitk <= 1) return 0;
+  const size_t b = static_cast<size_t>(pl.splitk) * k * n * sizeof(float);
+  return (b + 255) / 256 * 256;
+}
+
 }  // namespace
 
 extern "C" {
@@ -188,23 +271,7 @@ int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act,
   if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
   if (ld_dout < n || ld_w < n || ld_din < k) return TP_ERR_SHAPE;
   if (act != TP_ACT_NONE && ld_u < k) return TP_ERR_SHAPE;
-  GemmParams p{};
-  p.a = dOut;
-  p.b = W;
-  p.c = dIn;
-  p.u = U;
-  p.M = T;
-  p.N = k;
-  p.K = n;
-  p.lda = ld_dout;
-  p.ldb = ld_w;
-  p.ldc = ld_din;
-  p.ldu = ld_u;
-  p.epi = act != TP_ACT_NONE ? EPI_DACT : EPI_STORE;
-  p.act = act == TP_ACT_GELU_TANH ? ACT_GELU : ACT_NONE;
-  p.out_bf16 = out_dt == TP_BF16;
-  p.a_kcontig = 1;  // dOut [T, n]
-  p.b_kcontig = 1;  // W [k, n] read as W^T: K (= n) contiguous
+  GemmParams p = dgrad_params(dOut, W, U, act, dIn, T, k, n, ld_dout, ld_w, ld_u, ld_din, out_dt);
   return run_gemm(p, dt, false, 0, stream);
 }
 
@@ -260,32 +327,85 @@ int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbia
   const size_t cs_bytes = dbias ? colsum_workspace_bytes(T, n) : 0;
   if (split_bytes + cs_bytes > 0 && (!workspace || workspace_bytes < split_bytes + cs_bytes))
     return TP_ERR_WORKSPACE;
-  GemmParams p{};
-  p.a = In;
-  p.b = dOut;
-  p.c = dW;
-  p.M = k;
-  p.N = n;
-  p.K = T;
-  p.lda = ld_in;
-  p.ldb = ld_dout;
-  p.ldc = ld_dw;
-  p.epi = EPI_STORE;
-  p.out_bf16 = 0;
-  p.accumulate = accumulate != 0;
-  p.ws = static_cast<float*>(workspace);
-  p.a_kcontig = 0;  // In [T, k] read as In^T: M (= k) contiguous
-  p.b_kcontig = 0;  // dOut [T, n]: N contiguous
-  ColsumParams c{};
-  c.src = dOut;
-  c.T = T;
-  c.N = n;
-  c.ld = ld_dout;
-  c.src_bf16 = dt == TP_BF16;
-  c.dbias = dbias;
-  c.accumulate = accumulate != 0;
-  c.ws = dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr;
+  GemmParams p = wgrad_params(In, dOut, dW, T, k, n, ld_in, ld_dout, ld_dw, accumulate, workspace);
+  ColsumParams c = bias_grad_params(
+      dOut, dbias, T, n, ld_dout, dt, accumulate,
+      dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr);
   return run_gemm(p, dt, true, split_bytes, stream, dbias ? &c : nullptr);
+}
+
+int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  size_t split = wgrad_split_bytes(T, k, n, dt);
+  if (dt == TP_BF16) {
+    const size_t pair = pair_split_bytes(T, k, n);
+    split = pair > split ? pair : split;
+  }
+  *bytes = split + colsum_workspace_bytes(T, n);
+  return TP_OK;
+}
+
+int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const void* In,
+                  void* dIn, float* dW, float* dbias, int64_t T, int64_t k, int64_t n,
+                  int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_in, int64_t ld_din,
+                  int64_t ld_dw, int accumulate, int dt, int out_dt, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  // every check of both products first
+  if (!dOut || !W || !dIn || !In || !dW) return TP_ERR_NULL;
+  if (!dtype_ok(dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (dt == TP_F32 && out_dt != TP_F32) return TP_ERR_DTYPE;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (act != TP_ACT_NONE && !U) return TP_ERR_NULL;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_dout < n || ld_w < n || ld_din < k || ld_in < k || ld_dw < n) return TP_ERR_SHAPE;
+  if (act != TP_ACT_NONE && ld_u < k) return TP_ERR_SHAPE;
+  const size_t need_split = wgrad_split_bytes(T, k, n, dt);
+  const size_t cs_bytes = dbias ? colsum_workspace_bytes(T, n) : 0;
+  if (need_split + cs_bytes > 0 && (!workspace || workspace_bytes < need_split + cs_bytes))
+    return TP_ERR_WORKSPACE;
+
+  if (dt == TP_BF16) {
+    const SplitPlan pl = pair_plan(T, k, n);
+    const size_t split_bytes = pl.splitk > 1 ? pair_split_bytes(T, k, n) : 0;
+    GemmParams pd = dgrad_params(dOut, W, U, act, dIn, T, k, n, ld_dout, ld_w, ld_u, ld_din, out_dt);
+    GemmParams pw = wgrad_params(In, dOut, dW, T, k, n, ld_in, ld_dout, ld_dw, accumulate, workspace);
+    ColsumParams c = bias_grad_params(
+        dOut, dbias, T, n, ld_dout, dt, accumulate,
+        dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr);
+    const SplitPlan plan_d = plan_gemm_bf16(T, k, n, false);
+    pd.splitk = 1;
+    pd.k_chunk = n;
+    pw.splitk = pl.splitk;
+    pw.k_chunk = pl.k_chunk;
+    const int ekd = pl.tile ? gemm_pipe_epilogue(pd, plan_d) : kEpiNone;
+    const bool ok = pl.tile != 0 && ekd != kEpiNone && gemm_pipe_epilogue(pw, pl) == kEpiF32 &&
+                    (!dbias || colsum_vec_ok(c)) &&
+                    (split_bytes + cs_bytes == 0 ||
+                     (workspace && workspace_bytes >= split_bytes + cs_bytes));
+    if (ok) {
+      if (dbias) {
+        const int64_t nchunks = colsum_chunks(c);
+        const int64_t units = (n + 255) / 256 * nchunks;
+        pw.cs = c;
+        pw.cs_nchunks = static_cast<int>(nchunks);
+        pw.cs_units = static_cast<int>(units);
+        pw.cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
+      }
+      hipError_t e = launch_gemm_bwd_pair(pw, pd, pl.tile, ekd, stream);
+      if (e == hipSuccess && pl.splitk > 1) e = launch_splitk_fixup(pw, stream);  // + pass 2
+      if (e == hipSuccess && dbias && pl.splitk == 1 && pw.cs_nchunks > 1)
+        e = launch_colsum_pass2(pw.cs, pw.cs_nchunks, stream);
+      return hip_status(e);
+    }
+  }
+  // the two products one after the other
+  const int r = tp_linear_bwd_dgrad(dOut, W, U, act, dIn, T, k, n, ld_dout, ld_w, ld_u, ld_din,
+                                    dt, out_dt, stream);
+  if (r != TP_OK) return r;
+  return tp_linear_bwd_wgrad(In, dOut, dW, dbias, T, k, n, ld_in, ld_dout, ld_dw, accumulate, dt,
+                             workspace, workspace_bytes, stream);
 }
 
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,

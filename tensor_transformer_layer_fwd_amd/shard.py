@@ -6,7 +6,10 @@ QKV_i = X W_i) and the row-parallel partial (fc2: Zp_i = Y_i B_i; output
 projection: C_i O_i), then the sum over shards that replaces the All-Reduce.
 The backward (not on the pages; derivatives of the same definitions) runs the
 row-parallel dgrad with the GeLU derivative, both wgrads with bias gradients,
-the column-parallel dgrad to a partial dX_i, and the sum of the partials.
+the column-parallel dgrad to a partial dX_i, and the sum of the partials. Each
+layer's two gradients go through one tp_linear_bwd call (one launch where the
+shapes allow), or with fused_bwd=False through tp_linear_bwd_dgrad and
+tp_linear_bwd_wgrad.
 
 With recompute=True the step keeps only U_i of the fc1 output across the
 step (the activation recomputation of the "Megatron" page's training
@@ -50,8 +53,11 @@ def to_f64(t: torch.Tensor) -> np.ndarray:
 class ShardStep:
     """Device buffers of one workload and the calls of one fwd+bwd step."""
 
-    def __init__(self, cfg, inputs: dict, device="cuda", recompute=False, fp8=False):
+    def __init__(self, cfg, inputs: dict, device="cuda", recompute=False, fp8=False,
+                 fused_bwd=True):
         self.cfg = cfg
+        # both gradients of a layer in one call (tp_linear_bwd) or as two calls
+        self.fused_bwd = bool(fused_bwd)
         self.recompute = bool(recompute and cfg.mlp)
         self.fp8 = bool(fp8 and cfg.mlp)
         if self.fp8 and (recompute or cfg.dtype != "bf16" or cfg.attn):
@@ -88,8 +94,8 @@ class ShardStep:
             if len(shards) == cfg.p:
                 self.out["Z"] = torch.empty(T, h, **act)
                 self.out["dX"] = torch.empty(T, h, **act)
-            ws = max(ws, L.tp_linear_bwd_wgrad_workspace_size(T, F, h, self.tp_dt),
-                     L.tp_linear_bwd_wgrad_workspace_size(T, h, F, self.tp_dt))
+            ws = max(ws, L.tp_linear_bwd_workspace_size(T, F, h, self.tp_dt),
+                     L.tp_linear_bwd_workspace_size(T, h, F, self.tp_dt))
         if cfg.attn:
             Q, O = cfg.Q, cfg.O
             for i in shards:
@@ -102,8 +108,8 @@ class ShardStep:
             if len(shards) == cfg.p:
                 self.out["Za"] = torch.empty(T, h, **act)
                 self.out["dXq"] = torch.empty(T, h, **act)
-            ws = max(ws, L.tp_linear_bwd_wgrad_workspace_size(T, O, h, self.tp_dt),
-                     L.tp_linear_bwd_wgrad_workspace_size(T, h, Q, self.tp_dt))
+            ws = max(ws, L.tp_linear_bwd_workspace_size(T, O, h, self.tp_dt),
+                     L.tp_linear_bwd_workspace_size(T, h, Q, self.tp_dt))
         if self.fp8:
             ws = max(ws, self._fp8_buffers())
         # one scratch buffer, shared by the wgrad calls (they run in order on one stream)
@@ -185,6 +191,14 @@ class ShardStep:
         return t[i * width:(i + 1) * width]
 
     # ------------------------------------------------------------------ step
+    def _bwd(self, dOut, W, U, In, dIn, dW, dbias, act):
+        """Data and weight gradients of one linear layer."""
+        if self.fused_bwd:
+            L.tp_linear_bwd(dOut, W, U, In, dIn, dW, dbias, act=act, workspace=self.workspace)
+        else:
+            L.tp_linear_bwd_dgrad(dOut, W, U, dIn, act=act)
+            L.tp_linear_bwd_wgrad(In, dOut, dW, dbias, workspace=self.workspace)
+
     def _y(self, i):
         return self.out["Yt"] if self.recompute else self.out[f"Y_{i}"]
 
@@ -205,17 +219,18 @@ class ShardStep:
         F = cfg.F
         for n, i in enumerate(cfg.shards):
             B_i, A_i = self._row("B", i, F), self._col("A", i, F)
+            db = o["db"] if (cfg.has_bias and n == 0) else None
             if self.recompute:
+                # the weight gradient reads the Y_i the dgrad epilogue recomputes
                 L.tp_linear_bwd_dgrad_recompute(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"],
                                                 o["Yt"])
+                L.tp_linear_bwd_wgrad(self._y(i), inp["dZ"], o[f"dB_{i}"], db,
+                                      workspace=self.workspace)
             else:
-                L.tp_linear_bwd_dgrad(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"], act="gelu")
-            L.tp_linear_bwd_wgrad(self._y(i), inp["dZ"], o[f"dB_{i}"],
-                                  o["db"] if (cfg.has_bias and n == 0) else None,
-                                  workspace=self.workspace)
-            L.tp_linear_bwd_dgrad(o[f"dU_{i}"], A_i, None, o[f"dXp_{i}"], act="none")
-            L.tp_linear_bwd_wgrad(inp["X"], o[f"dU_{i}"], o[f"dA_{i}"],
-                                  o.get(f"da_{i}"), workspace=self.workspace)
+                self._bwd(inp["dZ"], B_i, o[f"U_{i}"], self._y(i), o[f"dU_{i}"], o[f"dB_{i}"],
+                          db, "gelu")
+            self._bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"], o[f"dA_{i}"],
+                      o.get(f"da_{i}"), "none")
         if "dX" in o:
             L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])
 
@@ -236,10 +251,8 @@ class ShardStep:
         for i in cfg.shards:
             Ow_i, W_i = self._row("Ow", i, O), self._col("W", i, Q)
             C_i, dQKV_i = self._col("C", i, O), self._col("dQKV", i, Q)
-            L.tp_linear_bwd_dgrad(inp["dZa"], Ow_i, None, o[f"dC_{i}"], act="none")
-            L.tp_linear_bwd_wgrad(C_i, inp["dZa"], o[f"dOw_{i}"], None, workspace=self.workspace)
-            L.tp_linear_bwd_dgrad(dQKV_i, W_i, None, o[f"dXqp_{i}"], act="none")
-            L.tp_linear_bwd_wgrad(inp["X"], dQKV_i, o[f"dW_{i}"], None, workspace=self.workspace)
+            self._bwd(inp["dZa"], Ow_i, None, C_i, o[f"dC_{i}"], o[f"dOw_{i}"], None, "none")
+            self._bwd(dQKV_i, W_i, None, inp["X"], o[f"dXqp_{i}"], o[f"dW_{i}"], None, "none")
         if "dXq" in o:
             L.tp_reduce_partials([o[f"dXqp_{i}"] for i in cfg.shards], None, o["dXq"])
 

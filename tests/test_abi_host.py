@@ -139,6 +139,38 @@ def test_gemm_plan_query(lib):
     assert lib.tp_gemm_plan(0, 5, 5, 0, None, None, None) == -2
 
 
+def test_linear_bwd_validation(lib):
+    """tp_linear_bwd runs every check of both gradients before any launch."""
+    f = lib.tp_linear_bwd
+    # dOut W U act In dIn dW dbias T k n ld_dout ld_w ld_u ld_in ld_din ld_dw acc dt out_dt ws bytes s
+    ok = [FAKE, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, 8, 4, 4, 4, 4, 4, 4, 4, 4, 0, 1, 1, None, 0,
+          None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a4=None) == -1                   # In
+    assert call(a6=None) == -1                   # dW
+    assert call(a2=None) == -1                   # GeLU needs U
+    assert call(a3=3) == -4
+    assert call(a18=0, a19=1) == -3              # fp32 operands, bf16 dIn
+    assert call(a18=7) == -3
+    assert call(a13=3) == -2                     # ld_u < k
+    assert call(a14=3) == -2                     # ld_in < k
+    assert call(a16=3) == -2                     # ld_dw < n
+    assert call(a8=0) == -2
+    # a weight gradient that splits K needs the workspace
+    big = dict(a8=4096, a9=256, a10=256, a11=256, a12=256, a13=256, a14=256, a15=256, a16=256)
+    assert call(**big) == -5
+    assert call(**big, a20=FAKE, a21=64) == -5
+    # the workspace query covers both gradients' own needs
+    for T, k, n in [(4096, 1536, 768), (4096, 768, 1536), (2048, 6144, 12288), (300, 129, 200)]:
+        both = L.tp_linear_bwd_workspace_size(T, k, n, L.TP_BF16)
+        assert both >= L.tp_linear_bwd_wgrad_workspace_size(T, k, n, L.TP_BF16)
+
+
 def test_attention_validation(lib):
     """The attention entry point rejects bad arguments on the host, before any launch."""
     import ctypes

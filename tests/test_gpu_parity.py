@@ -424,6 +424,31 @@ def test_workload_full_size_sampled(dev, name):
         assert np.all(np.isfinite(v)), k
 
 
+@pytest.mark.parametrize("name", ["gpt2s", "gpt350m"])
+def test_fused_backward_step_matches_two_calls(dev, name):
+    """The step with each layer's gradients in one tp_linear_bwd call equals the
+    step with separate dgrad and wgrad calls: data gradients and forward outputs
+    bitwise, weight and bias gradients within fp32 summation order (their K
+    slices may differ)."""
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    cfg = get_config(name)
+    _say(f"fused vs two-call backward {name} T={cfg.T}")
+    inputs = make_inputs(cfg)
+    two = ShardStep(cfg, inputs, dev, fused_bwd=False)
+    two.run_eager()
+    want = two.results()
+    del two
+    step = ShardStep(cfg, inputs, dev)
+    step.run_eager()
+    got = step.results()
+    for key in want:
+        if key[:2] in ("dA", "dB", "dW") or key[:3] in ("dOw",) or key in ("db",) or \
+                key.startswith("da_"):
+            assert err(got[key], want[key]) <= 1e-6, key
+        else:
+            np.testing.assert_array_equal(got[key], want[key], err_msg=key)
+
+
 def test_determinism_and_graph_replay(dev):
     """Two eager runs are bitwise equal; graph replays (with eager work and
     synchronisations between them) equal the eager result bitwise."""
@@ -544,6 +569,101 @@ def _run_tile_op(dev, tile, op, M, N, K):
             rw, rb = rw + prev_w, rb + prev_b
         assert err(dW.cpu().numpy(), rw) <= 1e-5
         assert err(db.cpu().numpy(), rb) <= 1e-5
+
+
+# --------------------------------------------------------------------------- #
+# the backward of one linear layer in one call (tp_linear_bwd)                 #
+# --------------------------------------------------------------------------- #
+# (tile id, BM, BN, paired K slices): the tiles whose data and weight gradients
+# share one launch; k is a multiple of BM and BN, n of BN
+_PAIR_TILES = [(15, 128, 192), (13, 128, 128), (14, 256, 192)]
+
+
+@pytest.mark.parametrize("tile,bm,bn", _PAIR_TILES)
+@pytest.mark.parametrize("split", [1, 2, 4])
+@pytest.mark.parametrize("kind", ["gelu_bias", "f32_out", "bf16_out_acc"])
+def test_linear_bwd_paired(dev, tile, bm, bn, split, kind):
+    """Both gradients of a layer in one launch (tile and K slices forced), against
+    the oracle; dIn bitwise equal to tp_linear_bwd_dgrad on the same tile."""
+    import tensor_transformer_layer_fwd_amd as tp
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    lcm = bm * bn // np.gcd(bm, bn)
+    T, k, n = 2 * bm * split if bm * split >= 256 else 512, lcm, 2 * bn
+    _say(f"paired bwd tile={tile} split={split} kind={kind} T={T} k={k} n={n}")
+    rng = np.random.default_rng(tile * 10 + split + len(kind))
+    dt = "bf16"
+    dO, dOr = rand(rng, (T, n), 1.0, dt)
+    W, Wr = rand(rng, (k, n), 0.05, dt)
+    In, Inr = rand(rng, (T, k), 1.0, dt)
+    act = "gelu" if kind == "gelu_bias" else "none"
+    out_dt = "f32" if kind == "f32_out" else "bf16"
+    U, Ur = rand(rng, (T, k), 1.5, dt)
+    acc = kind.endswith("_acc")
+    prev_w = rng.standard_normal((k, n)).astype(np.float32)
+    prev_b = rng.standard_normal(n).astype(np.float32)
+    dI = Guarded(T, k, out_dt, dev, pad=8)
+    dW = torch.from_numpy(prev_w).to(dev) if acc else torch.empty(k, n, device=dev)
+    db = None if kind == "f32_out" else (torch.from_numpy(prev_b).to(dev) if acc
+                                          else torch.empty(n, device=dev))
+    tp.tp_set_gemm_override(tile, split)
+    try:
+        ws = torch.full((max(16, L.tp_linear_bwd_workspace_size(T, k, n, L.TP_BF16)),), 255,
+                        dtype=torch.uint8, device=dev)  # garbage on entry
+        dOd, Wd, Ind = upload(dOr, dt, dev), upload(Wr, dt, dev), upload(Inr, dt, dev)
+        Ud = upload(Ur, dt, dev) if act == "gelu" else None
+        tp.tp_linear_bwd(dOd, Wd, Ud, Ind, dI.view, dW, db, act=act, accumulate=acc,
+                         workspace=ws)
+        dI_alone = torch.empty_like(dI.view)
+        tp.tp_linear_bwd_dgrad(dOd, Wd, Ud, dI_alone, act=act)
+        torch.cuda.synchronize()
+    finally:
+        tp.tp_set_gemm_override(0)
+    got = dI.value()
+    ref = oracle.linear_bwd_dgrad(dO, W, U if act == "gelu" else None, act)
+    assert err(got, ref) <= (TOL["bf16"] if out_dt == "bf16" else 1e-5)
+    np.testing.assert_array_equal(got, dI_alone.float().cpu().numpy().astype(np.float64))
+    rw, rb = oracle.linear_bwd_wgrad(In, dO)
+    if acc:
+        rw, rb = rw + prev_w, rb + prev_b
+    assert err(dW.cpu().numpy(), rw) <= 1e-5
+    if db is not None:
+        assert err(db.cpu().numpy(), rb) <= 1e-5
+
+
+@pytest.mark.parametrize("dt,T,k,n,ws_kind", [
+    ("f32", 300, 129, 200, "full"),    # fp32 operands: the two calls
+    ("bf16", 130, 520, 264, "full"),   # ragged against every tile
+    ("bf16", 4096, 1536, 768, "wgrad_only"),  # pairable, workspace sized for the wgrad alone
+    ("bf16", 4096, 1536, 768, "full"),  # the GPT-2-small fc2 layer, paired
+    ("bf16", 4096, 768, 1536, "full"),  # the GPT-2-small fc1 layer, paired
+])
+def test_linear_bwd_shapes(dev, dt, T, k, n, ws_kind):
+    """tp_linear_bwd on the planner's own choice, paired or as two calls, against
+    the oracle (sampled rows for the large shapes)."""
+    import tensor_transformer_layer_fwd_amd as tp
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    _say(f"linear bwd dt={dt} T={T} k={k} n={n} ws={ws_kind}")
+    rng = np.random.default_rng(T + k + n)
+    dO, dOr = rand(rng, (T, n), 1.0, dt)
+    W, Wr = rand(rng, (k, n), 0.05, dt)
+    In, Inr = rand(rng, (T, k), 1.0, dt)
+    U, Ur = rand(rng, (T, k), 1.5, dt)
+    tdt = L.TP_BF16 if dt == "bf16" else L.TP_F32
+    nbytes = (L.tp_linear_bwd_workspace_size(T, k, n, tdt) if ws_kind == "full"
+              else L.tp_linear_bwd_wgrad_workspace_size(T, k, n, tdt))
+    ws = torch.full((max(16, nbytes),), 255, dtype=torch.uint8, device=dev)
+    dI = Guarded(T, k, dt, dev, pad=8)
+    dW = torch.empty(k, n, device=dev)
+    db = torch.empty(n, device=dev)
+    tp.tp_linear_bwd(upload(dOr, dt, dev), upload(Wr, dt, dev), upload(Ur, dt, dev),
+                     upload(Inr, dt, dev), dI.view, dW, db, act="gelu", workspace=ws)
+    torch.cuda.synchronize()
+    rows = np.arange(T) if T <= 512 else np.sort(rng.choice(T, 64, replace=False))
+    ref = oracle.linear_bwd_dgrad(dO[rows], W, U[rows], "gelu")
+    assert err(dI.value()[rows], ref) <= TOL[dt]
+    rw, rb = oracle.linear_bwd_wgrad(In, dO)
+    assert err(dW.cpu().numpy(), rw) <= 1e-5
+    assert err(db.cpu().numpy(), rb) <= 1e-5
 
 
 # --------------------------------------------------------------------------- #
