@@ -216,6 +216,41 @@ int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const
 int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t* bytes);
 
 /*
+ * The backward of one shard's MLP block ("Megatron" page, "Tensor
+ * Parallelism / mathematical principles": the column-parallel fc1 with GeLU,
+ * then the row-parallel fc2; derivatives not on the pages), without the sum
+ * of the dX partials over shards (tp_reduce_partials):
+ *
+ *   fc2: dU_i = (dZ B_i^T) * GeLU'(U_i); dB_i (+)= Y_i^T dZ; db (+)= colsum(dZ)
+ *   fc1: dXp_i = dU_i A_i^T (fp32 partial); dA_i (+)= X^T dU_i;
+ *        da_i (+)= colsum(dU_i)
+ *
+ * Same results as tp_linear_bwd for fc2 (act GeLU, out dtype dt) followed by
+ * tp_linear_bwd for fc1 (act none, out TP_F32). Where both layers pair (see
+ * tp_linear_bwd) it makes two launches plus fc1's own fix-up: fc2's
+ * split-K fix-up and bias-gradient pass run in spare blocks of fc1's paired
+ * launch, on the CUs fc1's data gradient leaves while its weight gradient
+ * still runs; otherwise the two tp_linear_bwd calls run.
+ *
+ * dZ [T,h], X [T,h], A_i [h,F] (ld_a), B_i [F,h] (ld_b), U_i and Y_i [T,F]:
+ * dtype dt. dU_i [T,F] dtype dt (written, then read by fc1). dB_i [F,h]
+ * (ld_db), dA_i [h,F] (ld_da), dXp_i [T,h] (ld_dxp), db [h], da_i [F]: fp32;
+ * db and da_i nullable. No output may overlap an input or another output.
+ * workspace: at least tp_mlp_bwd_workspace_size() bytes; contents on entry
+ * ignored; not shared by calls that may run at the same time. Errors as
+ * tp_linear_bwd; every check of both layers runs before the first launch.
+ */
+int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, const void* U_i,
+               const void* Y_i, void* dU_i, float* dB_i, float* db, float* dXp_i, float* dA_i,
+               float* da_i, int64_t T, int64_t h, int64_t F, int64_t ld_dz, int64_t ld_x,
+               int64_t ld_a, int64_t ld_b, int64_t ld_u, int64_t ld_y, int64_t ld_du,
+               int64_t ld_dxp, int64_t ld_db, int64_t ld_da, int accumulate, int dt,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Scratch bytes tp_mlp_bwd needs for (T, h, F, dt); pure host function. */
+int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, int dt, size_t* bytes);
+
+/*
  * Sum over shards, the one-GPU stand-in for the All-Reduce ("Megatron" page,
  * "Tensor Parallelism / mathematical principles": the row-split partials Y_i B_i
  * are summed across GPUs; "Transformer-layer tensor parallelism": one such sum

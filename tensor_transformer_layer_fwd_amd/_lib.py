@@ -39,6 +39,11 @@ SIGNATURES = {
                              _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz, _vp]),
     "tp_linear_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                             ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_mlp_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                          _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int,
+                          _int, _vp, _sz, _vp]),
+    "tp_mlp_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int,
+                                         ctypes.POINTER(ctypes.c_size_t)]),
     "tp_reduce_partials": (_int, [ctypes.POINTER(ctypes.c_void_p), _int, _vp, _vp, _i64, _i64, _i64,
                                   _i64, _int, _vp]),
     "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
@@ -216,6 +221,27 @@ def tp_linear_bwd(dOut, W, U, In, dIn, dW, dbias=None, act="none", accumulate=Fa
         _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(In), _ptr(dIn), _ptr(dW), _ptr(dbias),
         T, k, n, _ld(dOut), _ld(W), ld_u, _ld(In), _ld(dIn), _ld(dW), int(bool(accumulate)),
         _dt(dOut), _dt(dIn), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def tp_mlp_bwd_workspace_size(T: int, h: int, F: int, dt: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_mlp_bwd_workspace_size",
+           lib().tp_mlp_bwd_workspace_size(T, h, F, dt, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_mlp_bwd(dZ, X, A_i, B_i, U_i, Y_i, dU_i, dB_i, db, dXp_i, dA_i, da_i, accumulate=False,
+               workspace=None, stream=None):
+    """The backward of one shard's MLP block: fc2's gradients with the GeLU
+    derivative, then fc1's, dXp_i the shard's fp32 dX partial."""
+    T, h = dZ.shape
+    F = B_i.shape[0]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("tp_mlp_bwd", lib().tp_mlp_bwd(
+        _ptr(dZ), _ptr(X), _ptr(A_i), _ptr(B_i), _ptr(U_i), _ptr(Y_i), _ptr(dU_i), _ptr(dB_i),
+        _ptr(db), _ptr(dXp_i), _ptr(dA_i), _ptr(da_i), T, h, F, _ld(dZ), _ld(X), _ld(A_i),
+        _ld(B_i), _ld(U_i), _ld(Y_i), _ld(dU_i), _ld(dXp_i), _ld(dB_i), _ld(dA_i),
+        int(bool(accumulate)), _dt(dZ), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def tp_reduce_partials(partials, bias, out, stream=None):

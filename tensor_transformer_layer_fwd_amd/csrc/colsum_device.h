@@ -1,8 +1,9 @@
-// Column-sum (bias-gradient) work units shared by the standalone kernels and
-// the launches they ride along with: pass 1 runs in spare blocks of the
-// weight-gradient GEMM, pass 2 in spare blocks of the split-K fix-up. Each
-// unit is the same arithmetic in every launch, so the result does not depend
-// on which launch carried it.
+// Column-sum (bias-gradient) and split-K fix-up work units shared by the
+// standalone kernels and the launches they ride along with: pass 1 runs in
+// spare blocks of the weight-gradient GEMM, pass 2 and the fix-up in spare
+// blocks of the fix-up launch or of the next layer's paired backward launch.
+// Each unit is the same arithmetic in every launch, so the result does not
+// depend on which launch carried it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -86,6 +87,26 @@ __device__ __forceinline__ void colsum_pass2_unit(const ColsumParams& p, int bx,
       const float v = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
       p.dbias[c] = p.accumulate ? p.dbias[c] + v : v;
     }
+  }
+}
+
+// Split-K fix-up, vector path (fp32 C, N and ldc multiples of 4, C and the
+// partials 16-byte aligned): C (+)= the K slices' partials summed in slice
+// order, four columns per thread. Thread `first` of `nthreads` takes every
+// nthreads-th group of four.
+__device__ __forceinline__ void splitk_fixup_vec4_unit(const GemmParams& p, int64_t first,
+                                                       int64_t nthreads) {
+  const int64_t nq = p.N >> 2;
+  const int64_t total = p.M * nq;
+  const int64_t slice = p.M * p.N;
+  for (int64_t e = first; e < total; e += nthreads) {
+    const int64_t row = e / nq, col = (e - row * nq) << 2;
+    const float* w = p.ws + row * p.N + col;
+    f32x4_t v = *reinterpret_cast<const f32x4_t*>(w);
+    for (int z = 1; z < p.splitk; ++z) v += *reinterpret_cast<const f32x4_t*>(w + z * slice);
+    float* c = static_cast<float*>(p.c) + row * p.ldc + col;
+    if (p.accumulate) v += *reinterpret_cast<const f32x4_t*>(c);
+    *reinterpret_cast<f32x4_t*>(c) = v;
   }
 }
 

@@ -28,20 +28,8 @@ __global__ __launch_bounds__(256) void splitk_fixup_kernel(GemmParams p) {
 // Vector fix-up of fp32 weight gradients: four columns per thread, the K-slice
 // partials summed in slice order, then accumulated into C if requested.
 __global__ __launch_bounds__(256) void splitk_fixup_vec4_kernel(GemmParams p) {
-  const int64_t nq = p.N >> 2;
-  const int64_t total = p.M * nq;
-  const int64_t slice = p.M * p.N;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += stride) {
-    const int64_t row = e / nq, col = (e - row * nq) << 2;
-    const float* w = p.ws + row * p.N + col;
-    f32x4_t v = *reinterpret_cast<const f32x4_t*>(w);
-    for (int z = 1; z < p.splitk; ++z) v += *reinterpret_cast<const f32x4_t*>(w + z * slice);
-    float* c = static_cast<float*>(p.c) + row * p.ldc + col;
-    if (p.accumulate) v += *reinterpret_cast<const f32x4_t*>(c);
-    *reinterpret_cast<f32x4_t*>(c) = v;
-  }
+  splitk_fixup_vec4_unit(p, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+                         static_cast<int64_t>(gridDim.x) * blockDim.x);
 }
 
 // Column sums (bias gradients) in two deterministic passes over chunks of
@@ -99,20 +87,8 @@ __global__ __launch_bounds__(256) void splitk_fixup_colsum_kernel(GemmParams p, 
     colsum_pass2_unit(p.cs, blockIdx.x - nfix, nchunks, part);
     return;
   }
-  const int64_t nq = p.N >> 2;
-  const int64_t total = p.M * nq;
-  const int64_t slice = p.M * p.N;
-  const int64_t stride = static_cast<int64_t>(nfix) * blockDim.x;
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
-       e += stride) {
-    const int64_t row = e / nq, col = (e - row * nq) << 2;
-    const float* w = p.ws + row * p.N + col;
-    f32x4_t v = *reinterpret_cast<const f32x4_t*>(w);
-    for (int z = 1; z < p.splitk; ++z) v += *reinterpret_cast<const f32x4_t*>(w + z * slice);
-    float* c = static_cast<float*>(p.c) + row * p.ldc + col;
-    if (p.accumulate) v += *reinterpret_cast<const f32x4_t*>(c);
-    *reinterpret_cast<f32x4_t*>(c) = v;
-  }
+  splitk_fixup_vec4_unit(p, static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x,
+                         static_cast<int64_t>(nfix) * blockDim.x);
 }
 
 // out = ((parts[0] + parts[1]) + ...) + bias, rounded once. Vector path: four
@@ -268,10 +244,14 @@ size_t colsum_workspace_bytes(int64_t T, int64_t N) {
   return nchunks > 1 ? static_cast<size_t>(nchunks * N) * sizeof(float) : 0;
 }
 
+bool splitk_fixup_vec_ok(const GemmParams& p) {
+  return !p.out_bf16 && p.epi == EPI_STORE && p.N % 4 == 0 && p.ldc % 4 == 0 &&
+         (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 &&
+         (reinterpret_cast<uintptr_t>(p.ws) & 15) == 0;
+}
+
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s) {
-  const bool vec = !p.out_bf16 && p.epi == EPI_STORE && p.N % 4 == 0 && p.ldc % 4 == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(p.ws) & 15) == 0;
+  const bool vec = splitk_fixup_vec_ok(p);
   // column sums carried by the GEMM launch: pass 2 rides along here
   const bool pass2 = p.cs_blocks > 0 && p.cs_nchunks > 1;
   if (vec && pass2) {

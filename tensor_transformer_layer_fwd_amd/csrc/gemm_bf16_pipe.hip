@@ -598,13 +598,30 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 // The backward of one linear layer in one launch: the weight gradient (TN,
 // fp32, K slices and column-sum units as in its own launch) in blocks
 // 0 .. nblk_w-1, then the data gradient (NT, epilogue EKD). Both products use
-// the same tile, K-tile and stage count, so they share the LDS stages.
+// the same tile, K-tile and stage count, so they share the LDS stages. The
+// last nfix_r + ncs_r blocks finish an earlier weight gradient pr on the CUs
+// the data gradient leaves while the weight gradient's longer blocks still
+// run: its split-K fix-up (vector path), then its column-sum pass-2 units.
 template <int BM, int BN, int WM, int WN, int BK, int S, int EKD>
 __global__ __launch_bounds__(WM* WN * 64) void gemm_bwd_pair_kernel(GemmParams pw, GemmParams pd,
-                                                                    int nblk_w) {
+                                                                    int nblk_w, int nblk_d,
+                                                                    GemmParams pr, int nfix_r) {
   const int b = static_cast<int>(blockIdx.x);
-  if (b < nblk_w) gemm_pipe_block<BM, BN, WM, WN, BK, S, false, false, kEpiF32>(pw, b);
-  else gemm_pipe_block<BM, BN, WM, WN, BK, S, true, true, EKD>(pd, b - nblk_w);
+  if (b < nblk_w) {
+    gemm_pipe_block<BM, BN, WM, WN, BK, S, false, false, kEpiF32>(pw, b);
+  } else if (b < nblk_w + nblk_d) {
+    gemm_pipe_block<BM, BN, WM, WN, BK, S, true, true, EKD>(pd, b - nblk_w);
+  } else {
+    const int r = b - nblk_w - nblk_d;
+    if (r < nfix_r) {
+      splitk_fixup_vec4_unit(pr, static_cast<int64_t>(r) * blockDim.x + threadIdx.x,
+                             static_cast<int64_t>(nfix_r) * blockDim.x);
+    } else {
+      constexpr int SB = (BM + BN) * BK * 2;
+      float(*part)[64] = reinterpret_cast<float(*)[64]>(stage_buf<0, SB>());
+      colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
+    }
+  }
 }
 
 // Epilogue kinds instantiated per layout (bf16) or operand formats (FP8):
@@ -737,22 +754,25 @@ int fp8_epilogue_kind(const GemmParams& p) {
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int S>
-hipError_t launch_pair_cfg(const GemmParams& pw, const GemmParams& pd, int ekd, hipStream_t s) {
+hipError_t launch_pair_cfg(const GemmParams& pw, const GemmParams& pd, int ekd,
+                           const PairRider& rd, hipStream_t s) {
   const int nblk_w = static_cast<int>((pw.M / BM) * (pw.N / BN) * pw.splitk) + pw.cs_blocks;
   const int nblk_d = static_cast<int>((pd.M / BM) * (pd.N / BN));
-  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d)), block(WM * WN * 64);
+  const GemmParams pr = rd.p ? *rd.p : GemmParams{};
+  const int nfix = rd.p ? rd.nfix : 0, ncs = rd.p ? rd.ncs : 0;
+  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs)), block(WM * WN * 64);
   switch (ekd) {
     case kEpiF32:
       hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiF32>), grid, block, 0, s,
-                         pw, pd, nblk_w);
+                         pw, pd, nblk_w, nblk_d, pr, nfix);
       break;
     case kEpiBF16:
       hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiBF16>), grid, block, 0,
-                         s, pw, pd, nblk_w);
+                         s, pw, pd, nblk_w, nblk_d, pr, nfix);
       break;
     case kEpiDGelu:
       hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiDGelu>), grid, block, 0,
-                         s, pw, pd, nblk_w);
+                         s, pw, pd, nblk_w, nblk_d, pr, nfix);
       break;
     default:
       return hipErrorInvalidValue;
@@ -767,14 +787,14 @@ bool pair_tile_ok(int tile) {
 }
 
 hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int tile, int ekd,
-                                hipStream_t s) {
+                                const PairRider& rider, hipStream_t s) {
   switch (tile) {
     case kPipe128x192:
-      return launch_pair_cfg<128, 192, 2, 2, 64, 3>(pw, pd, ekd, s);
+      return launch_pair_cfg<128, 192, 2, 2, 64, 3>(pw, pd, ekd, rider, s);
     case kPipe128x128:
-      return launch_pair_cfg<128, 128, 2, 2, 64, 3>(pw, pd, ekd, s);
+      return launch_pair_cfg<128, 128, 2, 2, 64, 3>(pw, pd, ekd, rider, s);
     case kPipe256x192:
-      return launch_pair_cfg<256, 192, 4, 2, 64, 2>(pw, pd, ekd, s);
+      return launch_pair_cfg<256, 192, 4, 2, 64, 2>(pw, pd, ekd, rider, s);
     default:
       return hipErrorInvalidValue;
   }

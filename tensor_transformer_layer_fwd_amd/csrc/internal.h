@@ -184,9 +184,17 @@ hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int
 // launch) and then the data gradient pd (NT, epilogue kind ekd), both on
 // pipelined tile `tile`, which pair_tile_ok accepts (64-wide K-tiles in both
 // layouts). The split-K fix-up is a launch of its own.
+// An earlier weight gradient finished by spare blocks of a paired launch: its
+// split-K fix-up over nfix blocks (vector path, splitk_fixup_vec_ok), then ncs
+// column-sum pass-2 units of its carried bias gradient. p NULL: none.
+struct PairRider {
+  const GemmParams* p = nullptr;
+  int nfix = 0, ncs = 0;
+};
 bool pair_tile_ok(int tile);
 hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int tile, int ekd,
-                                hipStream_t s);
+                                const PairRider& rider, hipStream_t s);
+bool splitk_fixup_vec_ok(const GemmParams& p);
 // K slices of the weight gradient paired with its data gradient on `tile`
 // (T a multiple of 64 * slices); 0 for an unknown tile.
 int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n);

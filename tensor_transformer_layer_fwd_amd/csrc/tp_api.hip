@@ -201,6 +201,94 @@ size_t pair_split_bytes(int64_t T, int64_t k, int64_t n) {
   return (b + 255) / 256 * 256;
 }
 
+// Workspace bytes of one layer's paired launch: split partials, then the
+// column-sum partials (256-byte multiples).
+size_t pair_bytes(int64_t T, int64_t k, int64_t n, bool dbias) {
+  const size_t cs = dbias ? (colsum_workspace_bytes(T, n) + 255) / 256 * 256 : 0;
+  return pair_split_bytes(T, k, n) + cs;
+}
+
+// Every argument check of one layer's data and weight gradients.
+int check_linear_bwd(const void* dOut, const void* W, const void* U, int act, const void* In,
+                     const void* dIn, const float* dW, int64_t T, int64_t k, int64_t n,
+                     int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_in, int64_t ld_din,
+                     int64_t ld_dw, int dt, int out_dt) {
+  if (!dOut || !W || !dIn || !In || !dW) return TP_ERR_NULL;
+  if (!dtype_ok(dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
+  if (dt == TP_F32 && out_dt != TP_F32) return TP_ERR_DTYPE;
+  if (!act_ok(act)) return TP_ERR_ACT;
+  if (act != TP_ACT_NONE && !U) return TP_ERR_NULL;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_dout < n || ld_w < n || ld_din < k || ld_in < k || ld_dw < n) return TP_ERR_SHAPE;
+  if (act != TP_ACT_NONE && ld_u < k) return TP_ERR_SHAPE;
+  return TP_OK;
+}
+
+// One bf16 layer's two gradients set up for a paired launch, with the weight
+// gradient's split partials at ws and its column-sum partials behind them.
+// ok is false where they cannot pair (shapes, alignment, workspace).
+struct PairSetup {
+  GemmParams pd, pw;
+  SplitPlan plan{0, 1, 0};
+  int ekd = kEpiNone;
+  bool ok = false, carry = false;
+};
+
+PairSetup setup_pair(const void* dOut, const void* W, const void* U, int act, const void* In,
+                     void* dIn, float* dW, float* dbias, int64_t T, int64_t k, int64_t n,
+                     int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_in, int64_t ld_din,
+                     int64_t ld_dw, int accumulate, int out_dt, char* ws, size_t ws_bytes) {
+  PairSetup q;
+  q.plan = pair_plan(T, k, n);
+  if (q.plan.tile == 0) return q;
+  const size_t split_bytes = pair_split_bytes(T, k, n);
+  q.pd = dgrad_params(dOut, W, U, act, dIn, T, k, n, ld_dout, ld_w, ld_u, ld_din, out_dt);
+  q.pw = wgrad_params(In, dOut, dW, T, k, n, ld_in, ld_dout, ld_dw, accumulate, ws);
+  ColsumParams c = bias_grad_params(dOut, dbias, T, n, ld_dout, TP_BF16, accumulate,
+                                    dbias ? reinterpret_cast<float*>(ws + split_bytes) : nullptr);
+  q.pd.splitk = 1;
+  q.pd.k_chunk = n;
+  q.pw.splitk = q.plan.splitk;
+  q.pw.k_chunk = q.plan.k_chunk;
+  q.ekd = gemm_pipe_epilogue(q.pd, plan_gemm_bf16(T, k, n, false));
+  const size_t need = pair_bytes(T, k, n, dbias != nullptr);
+  q.ok = q.ekd != kEpiNone && gemm_pipe_epilogue(q.pw, q.plan) == kEpiF32 &&
+         (!dbias || colsum_vec_ok(c)) && (need == 0 || (ws && ws_bytes >= need));
+  if (q.ok && dbias) {
+    const int64_t nchunks = colsum_chunks(c);
+    const int64_t units = (n + 255) / 256 * nchunks;
+    q.pw.cs = c;
+    q.pw.cs_nchunks = static_cast<int>(nchunks);
+    q.pw.cs_units = static_cast<int>(units);
+    q.pw.cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
+    q.carry = true;
+  }
+  return q;
+}
+
+// What a paired weight gradient still needs after its launch: the split-K
+// fix-up, and pass 2 of its carried column sums.
+bool pair_needs_finish(const PairSetup& q) {
+  return q.plan.splitk > 1 || (q.carry && q.pw.cs_nchunks > 1);
+}
+
+hipError_t finish_pair(const PairSetup& q, hipStream_t s) {
+  if (q.plan.splitk > 1) return launch_splitk_fixup(q.pw, s);  // + pass 2
+  if (q.carry && q.pw.cs_nchunks > 1) return launch_colsum_pass2(q.pw.cs, q.pw.cs_nchunks, s);
+  return hipSuccess;
+}
+
+// That work as spare blocks of the next paired launch (vector fix-up only).
+bool rider_for(const PairSetup& q, PairRider* r) {
+  if (!pair_needs_finish(q)) return true;
+  if (q.plan.splitk > 1 && !splitk_fixup_vec_ok(q.pw)) return false;
+  r->p = &q.pw;
+  const int64_t fix_blocks = (q.pw.M * q.pw.N / 4 + 255) / 256;  // one float4 per thread
+  r->nfix = q.plan.splitk > 1 ? static_cast<int>(fix_blocks < 256 ? fix_blocks : 256) : 0;
+  r->ncs = (q.carry && q.pw.cs_nchunks > 1) ? static_cast<int>((q.pw.cs.N + 63) / 64) : 0;
+  return true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -338,13 +426,72 @@ int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t
   if (!bytes) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
-  size_t split = wgrad_split_bytes(T, k, n, dt);
-  if (dt == TP_BF16) {
-    const size_t pair = pair_split_bytes(T, k, n);
-    split = pair > split ? pair : split;
-  }
-  *bytes = split + colsum_workspace_bytes(T, n);
+  const size_t alone = wgrad_split_bytes(T, k, n, dt) + colsum_workspace_bytes(T, n);
+  const size_t pair = dt == TP_BF16 ? pair_bytes(T, k, n, true) : 0;
+  *bytes = pair > alone ? pair : alone;
   return TP_OK;
+}
+
+int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, int dt, size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  size_t b2 = 0, b1 = 0;
+  int st = tp_linear_bwd_workspace_size(T, F, h, dt, &b2);
+  if (st == TP_OK) st = tp_linear_bwd_workspace_size(T, h, F, dt, &b1);
+  if (st != TP_OK) return st;
+  const size_t alone = b2 > b1 ? b2 : b1;
+  const size_t both = dt == TP_BF16 ? pair_bytes(T, F, h, true) + pair_bytes(T, h, F, true) : 0;
+  *bytes = both > alone ? both : alone;
+  return TP_OK;
+}
+
+int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, const void* U_i,
+               const void* Y_i, void* dU_i, float* dB_i, float* db, float* dXp_i, float* dA_i,
+               float* da_i, int64_t T, int64_t h, int64_t F, int64_t ld_dz, int64_t ld_x,
+               int64_t ld_a, int64_t ld_b, int64_t ld_u, int64_t ld_y, int64_t ld_du,
+               int64_t ld_dxp, int64_t ld_db, int64_t ld_da, int accumulate, int dt,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  // fc2 (row-parallel, GeLU before it): dOut dZ [T,h], W = B_i [F,h], In = Y_i
+  // fc1 (column-parallel): dOut dU_i [T,F], W = A_i [h,F], In = X, fp32 dX partial
+  int st = check_linear_bwd(dZ, B_i, U_i, TP_ACT_GELU_TANH, Y_i, dU_i, dB_i, T, F, h, ld_dz,
+                            ld_b, ld_u, ld_y, ld_du, ld_db, dt, dt);
+  if (st == TP_OK)
+    st = check_linear_bwd(dU_i, A_i, nullptr, TP_ACT_NONE, X, dXp_i, dA_i, T, h, F, ld_du, ld_a,
+                          h, ld_x, ld_dxp, ld_da, dt, TP_F32);
+  if (st != TP_OK) return st;
+  const size_t alone2 = wgrad_split_bytes(T, F, h, dt) + (db ? colsum_workspace_bytes(T, h) : 0);
+  const size_t alone1 = wgrad_split_bytes(T, h, F, dt) + (da_i ? colsum_workspace_bytes(T, F) : 0);
+  const size_t alone = alone2 > alone1 ? alone2 : alone1;
+  if (alone > 0 && (!workspace || workspace_bytes < alone)) return TP_ERR_WORKSPACE;
+
+  if (dt == TP_BF16) {
+    // fc2's pair first; its fix-up rides in fc1's pair, so the two layers'
+    // partials sit one after the other in the workspace
+    char* ws = static_cast<char*>(workspace);
+    const size_t b2 = pair_bytes(T, F, h, db != nullptr);
+    const PairSetup q2 = setup_pair(dZ, B_i, U_i, TP_ACT_GELU_TANH, Y_i, dU_i, dB_i, db, T, F, h,
+                                    ld_dz, ld_b, ld_u, ld_y, ld_du, ld_db, accumulate, dt, ws,
+                                    workspace_bytes);
+    const PairSetup q1 =
+        setup_pair(dU_i, A_i, nullptr, TP_ACT_NONE, X, dXp_i, dA_i, da_i, T, h, F, ld_du, ld_a, h,
+                   ld_x, ld_dxp, ld_da, accumulate, TP_F32, ws ? ws + b2 : nullptr,
+                   workspace_bytes > b2 ? workspace_bytes - b2 : 0);
+    PairRider rider;
+    if (q2.ok && q1.ok && rider_for(q2, &rider)) {
+      hipError_t e = launch_gemm_bwd_pair(q2.pw, q2.pd, q2.plan.tile, q2.ekd, PairRider{}, stream);
+      if (e == hipSuccess)
+        e = launch_gemm_bwd_pair(q1.pw, q1.pd, q1.plan.tile, q1.ekd, rider, stream);
+      if (e == hipSuccess) e = finish_pair(q1, stream);
+      return hip_status(e);
+    }
+  }
+  // the two layers one after the other
+  st = tp_linear_bwd(dZ, B_i, U_i, TP_ACT_GELU_TANH, Y_i, dU_i, dB_i, db, T, F, h, ld_dz, ld_b,
+                     ld_u, ld_y, ld_du, ld_db, accumulate, dt, dt, workspace, workspace_bytes,
+                     stream);
+  if (st != TP_OK) return st;
+  return tp_linear_bwd(dU_i, A_i, nullptr, TP_ACT_NONE, X, dXp_i, dA_i, da_i, T, h, F, ld_du, ld_a,
+                       h, ld_x, ld_dxp, ld_da, accumulate, dt, TP_F32, workspace, workspace_bytes,
+                       stream);
 }
 
 int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const void* In,
@@ -353,50 +500,21 @@ int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const
                   int64_t ld_dw, int accumulate, int dt, int out_dt, void* workspace,
                   size_t workspace_bytes, hipStream_t stream) {
   // every check of both products first
-  if (!dOut || !W || !dIn || !In || !dW) return TP_ERR_NULL;
-  if (!dtype_ok(dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
-  if (dt == TP_F32 && out_dt != TP_F32) return TP_ERR_DTYPE;
-  if (!act_ok(act)) return TP_ERR_ACT;
-  if (act != TP_ACT_NONE && !U) return TP_ERR_NULL;
-  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
-  if (ld_dout < n || ld_w < n || ld_din < k || ld_in < k || ld_dw < n) return TP_ERR_SHAPE;
-  if (act != TP_ACT_NONE && ld_u < k) return TP_ERR_SHAPE;
+  const int st = check_linear_bwd(dOut, W, U, act, In, dIn, dW, T, k, n, ld_dout, ld_w, ld_u,
+                                  ld_in, ld_din, ld_dw, dt, out_dt);
+  if (st != TP_OK) return st;
   const size_t need_split = wgrad_split_bytes(T, k, n, dt);
   const size_t cs_bytes = dbias ? colsum_workspace_bytes(T, n) : 0;
   if (need_split + cs_bytes > 0 && (!workspace || workspace_bytes < need_split + cs_bytes))
     return TP_ERR_WORKSPACE;
 
   if (dt == TP_BF16) {
-    const SplitPlan pl = pair_plan(T, k, n);
-    const size_t split_bytes = pl.splitk > 1 ? pair_split_bytes(T, k, n) : 0;
-    GemmParams pd = dgrad_params(dOut, W, U, act, dIn, T, k, n, ld_dout, ld_w, ld_u, ld_din, out_dt);
-    GemmParams pw = wgrad_params(In, dOut, dW, T, k, n, ld_in, ld_dout, ld_dw, accumulate, workspace);
-    ColsumParams c = bias_grad_params(
-        dOut, dbias, T, n, ld_dout, dt, accumulate,
-        dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr);
-    const SplitPlan plan_d = plan_gemm_bf16(T, k, n, false);
-    pd.splitk = 1;
-    pd.k_chunk = n;
-    pw.splitk = pl.splitk;
-    pw.k_chunk = pl.k_chunk;
-    const int ekd = pl.tile ? gemm_pipe_epilogue(pd, plan_d) : kEpiNone;
-    const bool ok = pl.tile != 0 && ekd != kEpiNone && gemm_pipe_epilogue(pw, pl) == kEpiF32 &&
-                    (!dbias || colsum_vec_ok(c)) &&
-                    (split_bytes + cs_bytes == 0 ||
-                     (workspace && workspace_bytes >= split_bytes + cs_bytes));
-    if (ok) {
-      if (dbias) {
-        const int64_t nchunks = colsum_chunks(c);
-        const int64_t units = (n + 255) / 256 * nchunks;
-        pw.cs = c;
-        pw.cs_nchunks = static_cast<int>(nchunks);
-        pw.cs_units = static_cast<int>(units);
-        pw.cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
-      }
-      hipError_t e = launch_gemm_bwd_pair(pw, pd, pl.tile, ekd, stream);
-      if (e == hipSuccess && pl.splitk > 1) e = launch_splitk_fixup(pw, stream);  // + pass 2
-      if (e == hipSuccess && dbias && pl.splitk == 1 && pw.cs_nchunks > 1)
-        e = launch_colsum_pass2(pw.cs, pw.cs_nchunks, stream);
+    const PairSetup q = setup_pair(dOut, W, U, act, In, dIn, dW, dbias, T, k, n, ld_dout, ld_w,
+                                   ld_u, ld_in, ld_din, ld_dw, accumulate, out_dt,
+                                   static_cast<char*>(workspace), workspace_bytes);
+    if (q.ok) {
+      hipError_t e = launch_gemm_bwd_pair(q.pw, q.pd, q.plan.tile, q.ekd, PairRider{}, stream);
+      if (e == hipSuccess) e = finish_pair(q, stream);
       return hip_status(e);
     }
   }

@@ -6,10 +6,11 @@ QKV_i = X W_i) and the row-parallel partial (fc2: Zp_i = Y_i B_i; output
 projection: C_i O_i), then the sum over shards that replaces the All-Reduce.
 The backward (not on the pages; derivatives of the same definitions) runs the
 row-parallel dgrad with the GeLU derivative, both wgrads with bias gradients,
-the column-parallel dgrad to a partial dX_i, and the sum of the partials. Each
-layer's two gradients go through one tp_linear_bwd call (one launch where the
-shapes allow), or with fused_bwd=False through tp_linear_bwd_dgrad and
-tp_linear_bwd_wgrad.
+the column-parallel dgrad to a partial dX_i, and the sum of the partials. A
+shard's MLP backward is one tp_mlp_bwd call (two launches where the shapes
+allow, fc2's fix-up riding in fc1's) and each attention projection's two
+gradients one tp_linear_bwd call; with fused_bwd=False every product is a
+tp_linear_bwd_dgrad or tp_linear_bwd_wgrad call of its own.
 
 With recompute=True the step keeps only U_i of the fc1 output across the
 step (the activation recomputation of the "Megatron" page's training
@@ -94,8 +95,7 @@ class ShardStep:
             if len(shards) == cfg.p:
                 self.out["Z"] = torch.empty(T, h, **act)
                 self.out["dX"] = torch.empty(T, h, **act)
-            ws = max(ws, L.tp_linear_bwd_workspace_size(T, F, h, self.tp_dt),
-                     L.tp_linear_bwd_workspace_size(T, h, F, self.tp_dt))
+            ws = max(ws, L.tp_mlp_bwd_workspace_size(T, h, F, self.tp_dt))
         if cfg.attn:
             Q, O = cfg.Q, cfg.O
             for i in shards:
@@ -220,7 +220,12 @@ class ShardStep:
         for n, i in enumerate(cfg.shards):
             B_i, A_i = self._row("B", i, F), self._col("A", i, F)
             db = o["db"] if (cfg.has_bias and n == 0) else None
-            if self.recompute:
+            if self.fused_bwd and not self.recompute:
+                # both layers in one call: fc2's fix-up rides in fc1's launch
+                L.tp_mlp_bwd(inp["dZ"], inp["X"], A_i, B_i, o[f"U_{i}"], self._y(i), o[f"dU_{i}"],
+                             o[f"dB_{i}"], db, o[f"dXp_{i}"], o[f"dA_{i}"], o.get(f"da_{i}"),
+                             workspace=self.workspace)
+            elif self.recompute:
                 # the weight gradient reads the Y_i the dgrad epilogue recomputes
                 L.tp_linear_bwd_dgrad_recompute(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"],
                                                 o["Yt"])
@@ -229,8 +234,9 @@ class ShardStep:
             else:
                 self._bwd(inp["dZ"], B_i, o[f"U_{i}"], self._y(i), o[f"dU_{i}"], o[f"dB_{i}"],
                           db, "gelu")
-            self._bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"], o[f"dA_{i}"],
-                      o.get(f"da_{i}"), "none")
+            if not self.fused_bwd or self.recompute:
+                self._bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"], o[f"dA_{i}"],
+                          o.get(f"da_{i}"), "none")
         if "dX" in o:
             L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])
 

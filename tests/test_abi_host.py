@@ -171,6 +171,33 @@ def test_linear_bwd_validation(lib):
         assert both >= L.tp_linear_bwd_wgrad_workspace_size(T, k, n, L.TP_BF16)
 
 
+def test_mlp_bwd_validation(lib):
+    """tp_mlp_bwd checks both layers before any launch; its workspace covers
+    each layer's own call."""
+    f = lib.tp_mlp_bwd
+    # dZ X A B U Y dU dB db dXp dA da T h F ld_dz ld_x ld_a ld_b ld_u ld_y ld_du ld_dxp ld_db ld_da
+    # acc dt ws bytes stream
+    ok = [FAKE] * 6 + [FAKE, FAKE, None, FAKE, FAKE, None, 8, 4, 8, 4, 4, 8, 4, 8, 8, 8, 4, 4, 8,
+                       0, 1, None, 0, None]
+
+    def call(**kw):
+        a = list(ok)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return f(*a)
+    assert call(a4=None) == -1   # U (GeLU)
+    assert call(a5=None) == -1   # Y
+    assert call(a10=None) == -1  # dA
+    assert call(a26=5) == -3
+    assert call(a17=4) == -2     # ld_a < F
+    assert call(a24=4) == -2     # ld_da < F
+    assert call(a12=0) == -2
+    for T, h, F in [(4096, 768, 1536), (6144, 1024, 1024), (2048, 12288, 6144), (300, 129, 200)]:
+        both = L.tp_mlp_bwd_workspace_size(T, h, F, L.TP_BF16)
+        assert both >= L.tp_linear_bwd_workspace_size(T, F, h, L.TP_BF16)
+        assert both >= L.tp_linear_bwd_workspace_size(T, h, F, L.TP_BF16)
+
+
 def test_attention_validation(lib):
     """The attention entry point rejects bad arguments on the host, before any launch."""
     import ctypes

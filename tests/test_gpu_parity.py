@@ -666,6 +666,56 @@ def test_linear_bwd_shapes(dev, dt, T, k, n, ws_kind):
     assert err(db.cpu().numpy(), rb) <= 1e-5
 
 
+@pytest.mark.parametrize("T,h,F,acc,bias", [
+    (4096, 768, 1536, False, True),   # the GPT-2-small shard: both layers paired, fc2's
+                                      # fix-up riding in fc1's launch
+    (1024, 768, 1536, True, True),    # accumulating into existing gradients
+    (6144, 1024, 1024, False, False),  # the ~350M shard's MLP, no bias
+    (300, 129, 200, False, True),     # ragged: the two layers one after the other
+])
+def test_mlp_bwd(dev, T, h, F, acc, bias):
+    """The backward of one shard's MLP block against the oracle's chain
+    (sampled token rows of the data gradients on the large shapes)."""
+    import tensor_transformer_layer_fwd_amd as tp
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    _say(f"mlp bwd T={T} h={h} F={F} acc={acc} bias={bias}")
+    rng = np.random.default_rng(T + h + F + acc)
+    dt = "bf16"
+    dZ, dZr = rand(rng, (T, h), 1.0, dt)
+    X, Xr = rand(rng, (T, h), 1.0, dt)
+    A, Ar = rand(rng, (h, F), 0.02, dt)
+    B, Br = rand(rng, (F, h), 0.02, dt)
+    U, Ur = rand(rng, (T, F), 1.0, dt)
+    Y, Yr = rand(rng, (T, F), 1.0, dt)
+    prev = {k: rng.standard_normal(s).astype(np.float32)
+            for k, s in (("dB", (F, h)), ("dA", (h, F)), ("db", (h,)), ("da", (F,)))}
+    out = {}
+    for k, shp in (("dB", (F, h)), ("dA", (h, F)), ("db", (h,)), ("da", (F,))):
+        out[k] = torch.from_numpy(prev[k]).to(dev) if acc else torch.empty(*shp, device=dev)
+    dU = torch.empty(T, F, dtype=torch.bfloat16, device=dev)
+    dXp = torch.empty(T, h, device=dev)
+    ws = torch.full((max(16, L.tp_mlp_bwd_workspace_size(T, h, F, L.TP_BF16)),), 255,
+                    dtype=torch.uint8, device=dev)
+    tp.tp_mlp_bwd(upload(dZr, dt, dev), upload(Xr, dt, dev), upload(Ar, dt, dev),
+                  upload(Br, dt, dev), upload(Ur, dt, dev), upload(Yr, dt, dev), dU, out["dB"],
+                  out["db"] if bias else None, dXp, out["dA"], out["da"] if bias else None,
+                  accumulate=acc, workspace=ws)
+    torch.cuda.synchronize()
+    dU_ref = oracle.linear_bwd_dgrad(dZ, B, U, "gelu")
+    dB_ref, db_ref = oracle.linear_bwd_wgrad(Y, dZ)
+    dA_ref, da_ref = oracle.linear_bwd_wgrad(X, dU_ref)
+    rows = np.arange(T) if T <= 512 else np.sort(rng.choice(T, 64, replace=False))
+    dXp_ref = oracle.linear_bwd_dgrad(dU_ref[rows], A)
+    assert err(dU.float().cpu().numpy()[rows], dU_ref[rows]) <= TOL[dt]
+    assert err(dXp.cpu().numpy()[rows], dXp_ref) <= TOL[dt]
+    got = {k: v.cpu().numpy().astype(np.float64) for k, v in out.items()}
+    ref = {"dB": dB_ref, "dA": dA_ref, "db": db_ref, "da": da_ref}
+    for k in ("dB", "dA") + (("db", "da") if bias else ()):
+        want = ref[k] + prev[k] if acc else ref[k]
+        # dB reads only stored inputs; dA and da read the device's bf16 dU
+        assert err(got[k], want) <= (1e-5 if k in ("dB", "db") else TOL[dt]), k
+
+
 # --------------------------------------------------------------------------- #
 # attention core of one shard (forward)                                        #
 # --------------------------------------------------------------------------- #
