@@ -53,6 +53,25 @@ __device__ __forceinline__ uint8_t* stage_buf() {
   return buf;
 }
 
+// One LDS array for a launch whose blocks run products of different tiles:
+// stage J of a product with stage size SB at byte J * SB (multiples of 1 KiB).
+template <int BYTES>
+__device__ __forceinline__ uint8_t* pool_buf() {
+  __shared__ __attribute__((aligned(1024))) uint8_t buf[BYTES];
+  return buf;
+}
+
+// Stage J: its own array (POOL = 0), or inside a pool of POOL bytes.
+template <int J, int SB, int POOL>
+__device__ __forceinline__ uint8_t* stage_ptr() {
+  if constexpr (POOL == 0) {
+    return stage_buf<J, SB>();
+  } else {
+    static_assert((J + 1) * SB <= POOL && SB % 1024 == 0, "pool");
+    return pool_buf<POOL>() + J * SB;
+  }
+}
+
 __device__ __forceinline__ void copy16_to_lds(const void* g, uint8_t* lds) {
   // address-space casts (global = 1, LDS = 3) need C-style casts
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
@@ -254,7 +273,8 @@ struct OperandF8 {
 // K-contiguous, BK = 128 codes), fmt 0 = E4M3, 1 = E5M2.
 // One block of a product: output tile (or column-sum unit) number `block` of
 // the product's 1-D grid.
-template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0>
+template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0,
+          int POOL = 0>
 __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int block) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
@@ -286,7 +306,7 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   if constexpr (EK == kEpiF32) {
     if (z >= p.splitk) {
       const int e = block - p.splitk * ntiles, ncb = static_cast<int>((p.cs.N + 255) / 256);
-      float(*part)[256] = reinterpret_cast<float(*)[256]>(stage_buf<0, SB>());
+      float(*part)[256] = reinterpret_cast<float(*)[256]>(stage_ptr<0, SB, POOL>());
       for (int u = e; u < p.cs_units; u += p.cs_blocks)
         colsum_vec_unit(p.cs, u % ncb, u / ncb, p.cs_nchunks, part);
       return;
@@ -325,13 +345,13 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   const bool xw = wave < NX;
   auto issue = [&](auto stage_c) {
     constexpr int J = decltype(stage_c)::value;
-    uint8_t* st = stage_buf<J, SB>();
+    uint8_t* st = stage_ptr<J, SB, POOL>();
     oa.issue(st, wave);
     ob.issue(st + OA::BYTES, wave);
   };
   auto issue_extra = [&](auto stage_c) {
     constexpr int J = decltype(stage_c)::value;
-    uint8_t* st = stage_buf<J, SB>();
+    uint8_t* st = stage_ptr<J, SB, POOL>();
     oa.issue_extra(st, wave, xw);
     ob.issue_extra(st + OA::BYTES, wave, xw);
   };
@@ -354,7 +374,7 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   FragT f[2][FM + FN];         // fragments of K step ks live in f[ks & 1]
   auto read = [&](auto stage_c, int ks, FragT(&d)[FM + FN]) {
     constexpr int J = decltype(stage_c)::value;
-    const uint8_t* sa = stage_buf<J, SB>();
+    const uint8_t* sa = stage_ptr<J, SB, POOL>();
     const uint8_t* sb = sa + OA::BYTES;
 #pragma unroll
     for (int i = 0; i < FM; ++i) d[i] = OA::frag(sa, wm * WTM + i * 32, ks, lane);
@@ -483,9 +503,9 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   constexpr int NCH = (WTN + 63) / 64;  // column chunks
   constexpr int NPB = WTN / 16;         // passes per band, all chunks
   const int ws_idx = wave / WPS;
-  uint8_t* base = stage_buf<0, SB>();
+  uint8_t* base = stage_ptr<0, SB, POOL>();
   Unroll<1, S>::run([&](auto c) {
-    if (ws_idx == decltype(c)::value) base = stage_buf<decltype(c)::value, SB>();
+    if (ws_idx == decltype(c)::value) base = stage_ptr<decltype(c)::value, SB, POOL>();
   });
   const float* ep = reinterpret_cast<const float*>(base + (wave % WPS) * REGION);
   const int64_t col0 = n0 + wn * WTN;
@@ -596,28 +616,55 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 }
 
 // The backward of one linear layer in one launch: the weight gradient (TN,
-// fp32, K slices and column-sum units as in its own launch) in blocks
-// 0 .. nblk_w-1, then the data gradient (NT, epilogue EKD). Both products use
-// the same tile, K-tile and stage count, so they share the LDS stages. The
-// last nfix_r + ncs_r blocks finish an earlier weight gradient pr on the CUs
-// the data gradient leaves while the weight gradient's longer blocks still
-// run: its split-K fix-up (vector path), then its column-sum pass-2 units.
-template <int BM, int BN, int WM, int WN, int BK, int S, int EKD>
-__global__ __launch_bounds__(WM* WN * 64) void gemm_bwd_pair_kernel(GemmParams pw, GemmParams pd,
-                                                                    int nblk_w, int nblk_d,
-                                                                    GemmParams pr, int nfix_r) {
+// fp32, tile W = BMW x BNW with BKW-wide K-tiles in SW stages; K slices and
+// column-sum units as in its own launch) in blocks 0 .. nblk_w-1, then the
+// data gradient (NT, tile D, epilogue EKD). Both products keep their stages
+// in one LDS pool sized for the larger, so the launch needs no more LDS than
+// its larger product alone. The last nfix_r + ncs_r blocks finish an earlier
+// weight gradient pr on the CUs the data gradient leaves while the weight
+// gradient's longer blocks still run: its split-K fix-up (vector path), then
+// its column-sum pass-2 units.
+template <int BMW, int BNW, int BKW, int SW, int BMD, int BND, int BKD, int SD, int EKD>
+__global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmParams pd,
+                                                            int nblk_w, int nblk_d,
+                                                            GemmParams pr, int nfix_r) {
+  constexpr int PW = SW * (BMW + BNW) * BKW * 2, PD = SD * (BMD + BND) * BKD * 2;
+  constexpr int POOL = PW > PD ? PW : PD;
   const int b = static_cast<int>(blockIdx.x);
   if (b < nblk_w) {
-    gemm_pipe_block<BM, BN, WM, WN, BK, S, false, false, kEpiF32>(pw, b);
+    gemm_pipe_block<BMW, BNW, 2, 2, BKW, SW, false, false, kEpiF32, 0, POOL>(pw, b);
   } else if (b < nblk_w + nblk_d) {
-    gemm_pipe_block<BM, BN, WM, WN, BK, S, true, true, EKD>(pd, b - nblk_w);
+    gemm_pipe_block<BMD, BND, 2, 2, BKD, SD, true, true, EKD, 0, POOL>(pd, b - nblk_w);
   } else {
     const int r = b - nblk_w - nblk_d;
     if (r < nfix_r) {
       splitk_fixup_vec4_unit(pr, static_cast<int64_t>(r) * blockDim.x + threadIdx.x,
                              static_cast<int64_t>(nfix_r) * blockDim.x);
     } else {
-      constexpr int SB = (BM + BN) * BK * 2;
+      float(*part)[64] = reinterpret_cast<float(*)[64]>(pool_buf<POOL>());
+      colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
+    }
+  }
+}
+
+// The same for the 8-wave 256x192 tile in both products (64-wide K-tiles, two
+// stages), which share their stage arrays.
+template <int EKD>
+__global__ __launch_bounds__(512) void gemm_bwd_pair256_kernel(GemmParams pw, GemmParams pd,
+                                                               int nblk_w, int nblk_d,
+                                                               GemmParams pr, int nfix_r) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < nblk_w) {
+    gemm_pipe_block<256, 192, 4, 2, 64, 2, false, false, kEpiF32>(pw, b);
+  } else if (b < nblk_w + nblk_d) {
+    gemm_pipe_block<256, 192, 4, 2, 64, 2, true, true, EKD>(pd, b - nblk_w);
+  } else {
+    const int r = b - nblk_w - nblk_d;
+    if (r < nfix_r) {
+      splitk_fixup_vec4_unit(pr, static_cast<int64_t>(r) * blockDim.x + threadIdx.x,
+                             static_cast<int64_t>(nfix_r) * blockDim.x);
+    } else {
+      constexpr int SB = (256 + 192) * 64 * 2;
       float(*part)[64] = reinterpret_cast<float(*)[64]>(stage_buf<0, SB>());
       colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
     }
@@ -753,26 +800,58 @@ int fp8_epilogue_kind(const GemmParams& p) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int S>
+// Blocks of a product on tile BM x BN (plus its column-sum units).
+template <int BM, int BN>
+int pair_blocks(const GemmParams& p) {
+  return static_cast<int>((p.M / BM) * (p.N / BN) * p.splitk) + p.cs_blocks;
+}
+
+template <int BMW, int BNW, int BKW, int SW, int BMD, int BND, int BKD, int SD>
 hipError_t launch_pair_cfg(const GemmParams& pw, const GemmParams& pd, int ekd,
                            const PairRider& rd, hipStream_t s) {
-  const int nblk_w = static_cast<int>((pw.M / BM) * (pw.N / BN) * pw.splitk) + pw.cs_blocks;
-  const int nblk_d = static_cast<int>((pd.M / BM) * (pd.N / BN));
+  const int nblk_w = pair_blocks<BMW, BNW>(pw);
+  const int nblk_d = static_cast<int>((pd.M / BMD) * (pd.N / BND));
   const GemmParams pr = rd.p ? *rd.p : GemmParams{};
   const int nfix = rd.p ? rd.nfix : 0, ncs = rd.p ? rd.ncs : 0;
-  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs)), block(WM * WN * 64);
+  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs)), block(256);
   switch (ekd) {
     case kEpiF32:
-      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiF32>), grid, block, 0, s,
-                         pw, pd, nblk_w, nblk_d, pr, nfix);
+      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BMW, BNW, BKW, SW, BMD, BND, BKD, SD, kEpiF32>),
+                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix);
       break;
     case kEpiBF16:
-      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiBF16>), grid, block, 0,
-                         s, pw, pd, nblk_w, nblk_d, pr, nfix);
+      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BMW, BNW, BKW, SW, BMD, BND, BKD, SD, kEpiBF16>),
+                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix);
       break;
     case kEpiDGelu:
-      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BM, BN, WM, WN, BK, S, kEpiDGelu>), grid, block, 0,
-                         s, pw, pd, nblk_w, nblk_d, pr, nfix);
+      hipLaunchKernelGGL((gemm_bwd_pair_kernel<BMW, BNW, BKW, SW, BMD, BND, BKD, SD, kEpiDGelu>),
+                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pair256(const GemmParams& pw, const GemmParams& pd, int ekd, const PairRider& rd,
+                          hipStream_t s) {
+  const int nblk_w = pair_blocks<256, 192>(pw);
+  const int nblk_d = static_cast<int>((pd.M / 256) * (pd.N / 192));
+  const GemmParams pr = rd.p ? *rd.p : GemmParams{};
+  const int nfix = rd.p ? rd.nfix : 0, ncs = rd.p ? rd.ncs : 0;
+  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs)), block(512);
+  switch (ekd) {
+    case kEpiF32:
+      hipLaunchKernelGGL((gemm_bwd_pair256_kernel<kEpiF32>), grid, block, 0, s, pw, pd, nblk_w,
+                         nblk_d, pr, nfix);
+      break;
+    case kEpiBF16:
+      hipLaunchKernelGGL((gemm_bwd_pair256_kernel<kEpiBF16>), grid, block, 0, s, pw, pd, nblk_w,
+                         nblk_d, pr, nfix);
+      break;
+    case kEpiDGelu:
+      hipLaunchKernelGGL((gemm_bwd_pair256_kernel<kEpiDGelu>), grid, block, 0, s, pw, pd, nblk_w,
+                         nblk_d, pr, nfix);
       break;
     default:
       return hipErrorInvalidValue;
@@ -782,19 +861,15 @@ hipError_t launch_pair_cfg(const GemmParams& pw, const GemmParams& pd, int ekd,
 
 }  // namespace
 
-bool pair_tile_ok(int tile) {
-  return tile == kPipe128x192 || tile == kPipe128x128 || tile == kPipe256x192;
-}
-
-hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int tile, int ekd,
+hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int kind, int ekd,
                                 const PairRider& rider, hipStream_t s) {
-  switch (tile) {
-    case kPipe128x192:
-      return launch_pair_cfg<128, 192, 2, 2, 64, 3>(pw, pd, ekd, rider, s);
-    case kPipe128x128:
-      return launch_pair_cfg<128, 128, 2, 2, 64, 3>(pw, pd, ekd, rider, s);
-    case kPipe256x192:
-      return launch_pair_cfg<256, 192, 4, 2, 64, 2>(pw, pd, ekd, rider, s);
+  switch (kind) {
+    case kPairSame128x128:
+      return launch_pair_cfg<128, 128, 64, 3, 128, 128, 64, 3>(pw, pd, ekd, rider, s);
+    case kPairW128x128D128x192:
+      return launch_pair_cfg<128, 128, 32, 4, 128, 192, 64, 3>(pw, pd, ekd, rider, s);
+    case kPairSame256x192:
+      return launch_pair256(pw, pd, ekd, rider, s);
     default:
       return hipErrorInvalidValue;
   }

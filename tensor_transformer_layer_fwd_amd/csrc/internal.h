@@ -181,9 +181,9 @@ hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int
                                  hipStream_t s);
 // The backward of one linear layer in one launch: the weight gradient pw (TN,
 // fp32 epilogue, K slices and carried column-sum units set as for its own
-// launch) and then the data gradient pd (NT, epilogue kind ekd), both on
-// pipelined tile `tile`, which pair_tile_ok accepts (64-wide K-tiles in both
-// layouts). The split-K fix-up is a launch of its own.
+// launch) and then the data gradient pd (NT, epilogue kind ekd), on the tiles
+// of `kind` (below). The split-K fix-up is a launch of its own, or rides in a
+// later paired launch.
 // An earlier weight gradient finished by spare blocks of a paired launch: its
 // split-K fix-up over nfix blocks (vector path, splitk_fixup_vec_ok), then ncs
 // column-sum pass-2 units of its carried bias gradient. p NULL: none.
@@ -191,13 +191,22 @@ struct PairRider {
   const GemmParams* p = nullptr;
   int nfix = 0, ncs = 0;
 };
-bool pair_tile_ok(int tile);
-hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int tile, int ekd,
+// Tiles of a paired backward launch: the weight gradient's (TN, fp32) and the
+// data gradient's (NT), each with its own K-tile and stage count.
+enum PairKind : int {
+  kPairNone = 0,
+  kPairSame128x128 = 1,       // both 128x128, 64-wide K-tiles, 3 stages
+  kPairW128x128D128x192 = 2,  // weight 128x128 (32-wide, 4 stages), data 128x192 (64, 3)
+  kPairSame256x192 = 3,       // both 256x192, 64-wide K-tiles, 2 stages (8 waves)
+};
+// The paired launch of one bf16 layer with input width k and output width n
+// over T tokens: plan.tile holds the PairKind (kPairNone: the layer's products
+// cannot pair), plan.splitk / k_chunk the weight gradient's K slices. Shapes
+// only, so the workspace query and the call agree.
+SplitPlan plan_pair(int64_t T, int64_t k, int64_t n);
+hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int kind, int ekd,
                                 const PairRider& rider, hipStream_t s);
 bool splitk_fixup_vec_ok(const GemmParams& p);
-// K slices of the weight gradient paired with its data gradient on `tile`
-// (T a multiple of 64 * slices); 0 for an unknown tile.
-int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n);
 hipError_t launch_gemm_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_fixup(const GemmParams& p, hipStream_t s);
 hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);

@@ -117,15 +117,28 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
 
 }  // namespace
 
-int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n) {
-  const PipeTile* t = find_tile(tile);
-  if (!t) return 0;
+SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
+  const SplitPlan none{kPairNone, 1, T};
+  // the data gradient keeps its own tile; the weight gradient takes 128x128
+  // beside a 128-row data-gradient tile (faster than 128x192 in TN) and
+  // 256x192 beside 256x192
+  const SplitPlan pd = plan_gemm_bf16(T, k, n, false);
+  int kind = kPairNone;
+  TileId tw = kPipe128x128;
+  if (pd.tile == kPipe128x192) kind = kPairW128x128D128x192;
+  else if (pd.tile == kPipe128x128) kind = kPairSame128x128;
+  else if (pd.tile == kPipe256x192) kind = kPairSame256x192, tw = kPipe256x192;
+  if (kind == kPairNone) return none;
+  const PipeTile* w = find_tile(tw);
+  const PipeTile* d = find_tile(pd.tile);
+  if (T % 64 || k % w->bm || n % w->bn) return none;
   if (g_force_tile != 0 && g_force_split > 1 && T % (64 * g_force_split) == 0)
-    return g_force_split;
-  // one block per CU (the paired tiles fill most of the LDS); blocks go to the
+    return SplitPlan{kind, g_force_split, T / g_force_split};
+  // one block per CU (the pair's stages fill most of the LDS); blocks go to the
   // CU that frees first, the weight gradient's slices first
-  const double ktile = 2.0 * t->bm * t->bn * 64.0 / t->flop_per_sec_per_cu;
-  const int64_t tiles_w = (k / t->bm) * (n / t->bn), tiles_d = (T / t->bm) * (k / t->bn);
+  const double kw = 2.0 * w->bm * w->bn * 64.0 / w->flop_per_sec_per_cu;
+  const double kd = 2.0 * d->bm * d->bn * 64.0 / d->flop_per_sec_per_cu;
+  const int64_t tiles_w = (k / w->bm) * (n / w->bn), tiles_d = (T / d->bm) * (k / d->bn);
   int best = 0;
   double best_c = 1e30;
   for (int sp : {1, 2, 4, 8}) {
@@ -139,8 +152,8 @@ int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n) {
         cu.push(f + kRoundOverheadSec + sec);
       }
     };
-    run(tiles_w * sp, static_cast<double>(T / sp / 64) * ktile);
-    run(tiles_d, static_cast<double>(n / 64) * ktile);
+    run(tiles_w * sp, static_cast<double>(T / sp / 64) * kw);
+    run(tiles_d, static_cast<double>(n / 64) * kd);
     double c = 0.0;
     while (!cu.empty()) {
       c = cu.top();
@@ -152,7 +165,7 @@ int plan_pair_split(int tile, int64_t T, int64_t k, int64_t n) {
       best = sp;
     }
   }
-  return best;
+  return SplitPlan{kind, best, T / best};
 }
 
 namespace {

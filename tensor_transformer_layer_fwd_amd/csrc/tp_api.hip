@@ -180,23 +180,20 @@ ColsumParams bias_grad_params(const void* dOut, float* dbias, int64_t T, int64_t
   return c;
 }
 
-// Tile and K slices of the paired backward launch of a bf16 linear layer
-// (tile 0: the layer's products cannot pair). Shapes only, so the workspace
-// query and the call agree; operand alignment is checked at the call.
-SplitPlan pair_plan(int64_t T, int64_t k, int64_t n) {
-  const SplitPlan pd = plan_gemm_bf16(T, k, n, false);
-  if (!pair_tile_ok(pd.tile)) return SplitPlan{0, 1, T};
-  const int bm = pd.tile == kPipe256x192 ? 256 : 128;
-  const int bn = pd.tile == kPipe128x128 ? 128 : 192;
-  if (T % 64 || k % bm || n % bn) return SplitPlan{0, 1, T};
-  const int sp = plan_pair_split(pd.tile, T, k, n);
-  if (sp < 1) return SplitPlan{0, 1, T};
-  return SplitPlan{pd.tile, sp, T / sp};
+// Pair kind and K slices of the paired backward launch of a bf16 linear layer
+// (kPairNone: the layer's products cannot pair). Operand alignment is checked
+// at the call.
+SplitPlan pair_plan(int64_t T, int64_t k, int64_t n) { return plan_pair(T, k, n); }
+
+// The weight gradient's own tile in a paired launch.
+SplitPlan pair_wgrad_plan(const SplitPlan& pl) {
+  return SplitPlan{pl.tile == kPairSame256x192 ? kPipe256x192 : kPipe128x128, pl.splitk,
+                   pl.k_chunk};
 }
 
 size_t pair_split_bytes(int64_t T, int64_t k, int64_t n) {
   const SplitPlan pl = pair_plan(T, k, n);
-  if (pl.tile == 0 || pl.splitk <= 1) return 0;
+  if (pl.tile == kPairNone || pl.splitk <= 1) return 0;
   const size_t b = static_cast<size_t>(pl.splitk) * k * n * sizeof(float);
   return (b + 255) / 256 * 256;
 }
@@ -240,7 +237,7 @@ PairSetup setup_pair(const void* dOut, const void* W, const void* U, int act, co
                      int64_t ld_dw, int accumulate, int out_dt, char* ws, size_t ws_bytes) {
   PairSetup q;
   q.plan = pair_plan(T, k, n);
-  if (q.plan.tile == 0) return q;
+  if (q.plan.tile == kPairNone) return q;
   const size_t split_bytes = pair_split_bytes(T, k, n);
   q.pd = dgrad_params(dOut, W, U, act, dIn, T, k, n, ld_dout, ld_w, ld_u, ld_din, out_dt);
   q.pw = wgrad_params(In, dOut, dW, T, k, n, ld_in, ld_dout, ld_dw, accumulate, ws);
@@ -252,7 +249,7 @@ PairSetup setup_pair(const void* dOut, const void* W, const void* U, int act, co
   q.pw.k_chunk = q.plan.k_chunk;
   q.ekd = gemm_pipe_epilogue(q.pd, plan_gemm_bf16(T, k, n, false));
   const size_t need = pair_bytes(T, k, n, dbias != nullptr);
-  q.ok = q.ekd != kEpiNone && gemm_pipe_epilogue(q.pw, q.plan) == kEpiF32 &&
+  q.ok = q.ekd != kEpiNone && gemm_pipe_epilogue(q.pw, pair_wgrad_plan(q.plan)) == kEpiF32 &&
          (!dbias || colsum_vec_ok(c)) && (need == 0 || (ws && ws_bytes >= need));
   if (q.ok && dbias) {
     const int64_t nchunks = colsum_chunks(c);

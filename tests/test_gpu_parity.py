@@ -574,8 +574,9 @@ def _run_tile_op(dev, tile, op, M, N, K):
 # --------------------------------------------------------------------------- #
 # the backward of one linear layer in one call (tp_linear_bwd)                 #
 # --------------------------------------------------------------------------- #
-# (tile id, BM, BN, paired K slices): the tiles whose data and weight gradients
-# share one launch; k is a multiple of BM and BN, n of BN
+# (data-gradient tile id, BM, BN): the tiles on which a layer's data and weight
+# gradients share one launch (beside 128x192 the weight gradient takes 128x128);
+# k is a multiple of BM and BN, n of BN and 128
 _PAIR_TILES = [(15, 128, 192), (13, 128, 128), (14, 256, 192)]
 
 
