@@ -545,6 +545,16 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   // otherwise guard them against the earlier copies into the same buffers with
   // a full vector-memory wait, which also waits for the stores of the previous
   // pass.
+  // Column sums of the stored (bf16) outputs of the GeLU-derivative epilogue
+  // when cs_part is set: each lane adds its 8 columns of each chunk over the
+  // rows it stores, in band and pass order (a lane's columns are the same in
+  // every band and pass); the block then adds the lanes' sums in a fixed order.
+  constexpr bool CSUM = EK == kEpiDGelu;
+  float colacc[NCH][8];
+#pragma unroll
+  for (int C = 0; C < NCH; ++C)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) colacc[C][q] = 0.0f;
   const uint32_t ep_lds = lds_addr(reinterpret_cast<const uint8_t*>(ep));
   const uint32_t ep_w = ep_lds + (4 * (lane >> 5) * EP + (lane & 31)) * 4;
   Unroll<0, FM>::run([&](auto band) {
@@ -603,11 +613,45 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
           }
 #pragma unroll
           for (int q = 0; q < 8; ++q) v[q] *= gelu_tanh_grad(u[q]);
+          const u32x4_t wv{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+          *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.c) + o) = wv;
+          if (p.cs_part) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              colacc[C][2 * q] += __uint_as_float(wv[q] << 16);
+              colacc[C][2 * q + 1] += __uint_as_float(wv[q] & 0xffff0000u);
+            }
+          }
         }
-        store8(p.c, o, v, 1);
+        if constexpr (EK != kEpiDGelu) store8(p.c, o, v, 1);
       }
     }
   });
+  if constexpr (CSUM) {
+    if (p.cs_part) {
+      // row lanes of each wave row's sums in LDS: [WM][16][BN] floats
+      constexpr int RL = 16;
+      static_assert(WM * RL * BN * 4 <= SB, "LDS for the column sums");
+      block_sync();  // every wave is done with its epilogue region
+      float* cb = reinterpret_cast<float*>(stage_ptr<0, SB, POOL>());
+#pragma unroll
+      for (int C = 0; C < NCH; ++C) {
+        const int vpr = chunk_w(C) / 8;
+        const int cc = wn * WTN + 64 * C + (lane % vpr) * 8;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) cb[(wm * RL + lane / vpr) * BN + cc + q] = colacc[C][q];
+      }
+      block_sync();
+      for (int c = tid; c < BN; c += NW * 64) {
+        const int rpp = 64 / (chunk_w((c % WTN) / 64) / 8);  // row lanes of c's chunk
+        float v = 0.0f;
+        for (int w = 0; w < WM; ++w)
+          for (int r = 0; r < rpp; ++r) v += cb[(w * RL + r) * BN + c];
+        p.cs_part[(m0 / BM) * p.N + n0 + c] = v;
+      }
+    }
+  }
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0>
@@ -627,7 +671,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_pipe_kernel(GemmParams 
 template <int BMW, int BNW, int BKW, int SW, int BMD, int BND, int BKD, int SD, int EKD>
 __global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmParams pd,
                                                             int nblk_w, int nblk_d,
-                                                            GemmParams pr, int nfix_r) {
+                                                            GemmParams pr, int nfix_r, int ncs_r,
+                                                            ColsumParams c2, int c2_nchunks) {
   constexpr int PW = SW * (BMW + BNW) * BKW * 2, PD = SD * (BMD + BND) * BKD * 2;
   constexpr int POOL = PW > PD ? PW : PD;
   const int b = static_cast<int>(blockIdx.x);
@@ -642,7 +687,8 @@ __global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmP
                              static_cast<int64_t>(nfix_r) * blockDim.x);
     } else {
       float(*part)[64] = reinterpret_cast<float(*)[64]>(pool_buf<POOL>());
-      colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
+      if (r < nfix_r + ncs_r) colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
+      else colsum_pass2_unit(c2, r - nfix_r - ncs_r, c2_nchunks, part);
     }
   }
 }
@@ -652,7 +698,9 @@ __global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmP
 template <int EKD>
 __global__ __launch_bounds__(512) void gemm_bwd_pair256_kernel(GemmParams pw, GemmParams pd,
                                                                int nblk_w, int nblk_d,
-                                                               GemmParams pr, int nfix_r) {
+                                                               GemmParams pr, int nfix_r,
+                                                               int ncs_r, ColsumParams c2,
+                                                               int c2_nchunks) {
   const int b = static_cast<int>(blockIdx.x);
   if (b < nblk_w) {
     gemm_pipe_block<256, 192, 4, 2, 64, 2, false, false, kEpiF32>(pw, b);
@@ -666,7 +714,8 @@ __global__ __launch_bounds__(512) void gemm_bwd_pair256_kernel(GemmParams pw, Ge
     } else {
       constexpr int SB = (256 + 192) * 64 * 2;
       float(*part)[64] = reinterpret_cast<float(*)[64]>(stage_buf<0, SB>());
-      colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
+      if (r < nfix_r + ncs_r) colsum_pass2_unit(pr.cs, r - nfix_r, pr.cs_nchunks, part);
+      else colsum_pass2_unit(c2, r - nfix_r - ncs_r, c2_nchunks, part);
     }
   }
 }
@@ -813,19 +862,22 @@ hipError_t launch_pair_cfg(const GemmParams& pw, const GemmParams& pd, int ekd,
   const int nblk_d = static_cast<int>((pd.M / BMD) * (pd.N / BND));
   const GemmParams pr = rd.p ? *rd.p : GemmParams{};
   const int nfix = rd.p ? rd.nfix : 0, ncs = rd.p ? rd.ncs : 0;
-  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs)), block(256);
+  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs + rd.ncs2)), block(256);
   switch (ekd) {
     case kEpiF32:
       hipLaunchKernelGGL((gemm_bwd_pair_kernel<BMW, BNW, BKW, SW, BMD, BND, BKD, SD, kEpiF32>),
-                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix);
+                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix, ncs,
+                         rd.cs2, rd.cs2_nchunks);
       break;
     case kEpiBF16:
       hipLaunchKernelGGL((gemm_bwd_pair_kernel<BMW, BNW, BKW, SW, BMD, BND, BKD, SD, kEpiBF16>),
-                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix);
+                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix, ncs,
+                         rd.cs2, rd.cs2_nchunks);
       break;
     case kEpiDGelu:
       hipLaunchKernelGGL((gemm_bwd_pair_kernel<BMW, BNW, BKW, SW, BMD, BND, BKD, SD, kEpiDGelu>),
-                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix);
+                         grid, block, 0, s, pw, pd, nblk_w, nblk_d, pr, nfix, ncs,
+                         rd.cs2, rd.cs2_nchunks);
       break;
     default:
       return hipErrorInvalidValue;
@@ -839,19 +891,19 @@ hipError_t launch_pair256(const GemmParams& pw, const GemmParams& pd, int ekd, c
   const int nblk_d = static_cast<int>((pd.M / 256) * (pd.N / 192));
   const GemmParams pr = rd.p ? *rd.p : GemmParams{};
   const int nfix = rd.p ? rd.nfix : 0, ncs = rd.p ? rd.ncs : 0;
-  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs)), block(512);
+  const dim3 grid(static_cast<unsigned>(nblk_w + nblk_d + nfix + ncs + rd.ncs2)), block(512);
   switch (ekd) {
     case kEpiF32:
       hipLaunchKernelGGL((gemm_bwd_pair256_kernel<kEpiF32>), grid, block, 0, s, pw, pd, nblk_w,
-                         nblk_d, pr, nfix);
+                         nblk_d, pr, nfix, ncs, rd.cs2, rd.cs2_nchunks);
       break;
     case kEpiBF16:
       hipLaunchKernelGGL((gemm_bwd_pair256_kernel<kEpiBF16>), grid, block, 0, s, pw, pd, nblk_w,
-                         nblk_d, pr, nfix);
+                         nblk_d, pr, nfix, ncs, rd.cs2, rd.cs2_nchunks);
       break;
     case kEpiDGelu:
       hipLaunchKernelGGL((gemm_bwd_pair256_kernel<kEpiDGelu>), grid, block, 0, s, pw, pd, nblk_w,
-                         nblk_d, pr, nfix);
+                         nblk_d, pr, nfix, ncs, rd.cs2, rd.cs2_nchunks);
       break;
     default:
       return hipErrorInvalidValue;

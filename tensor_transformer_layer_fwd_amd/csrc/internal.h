@@ -38,6 +38,10 @@ struct GemmParams {
                    // row stride ldc2, dtype of c; may be null
   const void* bias;  // EPI_BIAS_ACT: [N], dtype of the operands; may be null
   const void* u;     // EPI_DACT: saved pre-activation [M,N], ldu, dtype of the operands
+  // EPI_DACT on the pipelined kernel, nullable: column sums of the stored
+  // (bf16) outputs over each block tile's BM rows, one row of N per tile row
+  // (row stride N): the first pass of the bias gradient of the next layer down
+  float* cs_part;
   int64_t M, N, K;
   int64_t lda, ldb, ldc, ldu, ldc2;
   int epi, act;
@@ -190,6 +194,10 @@ hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int
 struct PairRider {
   const GemmParams* p = nullptr;
   int nfix = 0, ncs = 0;
+  // pass 2 of a second bias gradient (partials in cs2.ws, cs2_nchunks rows of
+  // cs2.N) over ncs2 units
+  ColsumParams cs2{};
+  int ncs2 = 0, cs2_nchunks = 0;
 };
 // Tiles of a paired backward launch: the weight gradient's (TN, fp32) and the
 // data gradient's (NT), each with its own K-tile and stage count.
