@@ -192,10 +192,10 @@ int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
  *   dW    (+)= In^T dOut, dbias (+)= column sums of dOut
  *                                     as tp_linear_bwd_wgrad
  *
- * Same arguments, layouts, dtypes and results as those two calls made one
- * after the other with the same values (dIn to within the rounding of its
- * own call, bitwise; dW and dbias to within fp32 summation order: the K slices
- * of the weight gradient may differ). For bf16 operands whose products both
+ * Same arguments, layouts and dtypes as those two calls made one after the
+ * other. dIn is bitwise equal to tp_linear_bwd_dgrad's; dW and dbias equal
+ * tp_linear_bwd_wgrad's to within fp32 summation order (the weight gradient's
+ * tile and K slices may differ). For bf16 operands whose products both
  * fit one of the pipelined tiles 128x192, 128x128 or 256x192 (16-byte aligned
  * operands, row strides a multiple of 8, T a multiple of 64, k and n tile
  * multiples), both products run in one launch, the weight gradient's blocks
@@ -226,11 +226,15 @@ int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t
  *        da_i (+)= colsum(dU_i)
  *
  * Same results as tp_linear_bwd for fc2 (act GeLU, out dtype dt) followed by
- * tp_linear_bwd for fc1 (act none, out TP_F32). Where both layers pair (see
- * tp_linear_bwd) it makes two launches plus fc1's own fix-up: fc2's
- * split-K fix-up and bias-gradient pass run in spare blocks of fc1's paired
- * launch, on the CUs fc1's data gradient leaves while its weight gradient
- * still runs; otherwise the two tp_linear_bwd calls run.
+ * tp_linear_bwd for fc1 (act none, out TP_F32): dU_i and dXp_i bitwise, the
+ * weight and bias gradients to within fp32 summation order (da_i is summed
+ * per data-gradient tile of 128 or 256 rows, then over the tiles in order). Where both layers pair (see
+ * tp_linear_bwd) it makes two launches (plus fc1's own fix-up if fc1's
+ * weight gradient splits K): fc2's data-gradient epilogue also writes the
+ * column partial sums of dU_i, and fc2's split-K fix-up, the last pass of db
+ * and of da_i run in spare blocks of fc1's paired launch, on the CUs fc1's
+ * data gradient leaves while its weight gradient still runs; otherwise the
+ * two tp_linear_bwd calls run.
  *
  * dZ [T,h], X [T,h], A_i [h,F] (ld_a), B_i [F,h] (ld_b), U_i and Y_i [T,F]:
  * dtype dt. dU_i [T,F] dtype dt (written, then read by fc1). dB_i [F,h]

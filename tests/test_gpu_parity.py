@@ -667,19 +667,22 @@ def test_linear_bwd_shapes(dev, dt, T, k, n, ws_kind):
     assert err(db.cpu().numpy(), rb) <= 1e-5
 
 
-@pytest.mark.parametrize("T,h,F,acc,bias", [
-    (4096, 768, 1536, False, True),   # the GPT-2-small shard: both layers paired, fc2's
-                                      # fix-up riding in fc1's launch
-    (1024, 768, 1536, True, True),    # accumulating into existing gradients
-    (6144, 1024, 1024, False, False),  # the ~350M shard's MLP, no bias
-    (300, 129, 200, False, True),     # ragged: the two layers one after the other
+@pytest.mark.parametrize("T,h,F,acc,bias,tile", [
+    (4096, 768, 1536, False, True, 0),    # the GPT-2-small shard: both layers paired, fc2's
+                                          # fix-up and fc1's bias gradient riding in fc1's launch
+    (1024, 768, 1536, True, True, 0),     # accumulating into existing gradients
+    (6144, 1024, 1024, False, False, 0),  # the ~350M shard's MLP, no bias
+    (2048, 768, 1536, False, True, 14),   # 256x192 tiles (8 waves), column partials of 256 rows
+    (2048, 768, 1536, True, True, 14),
+    (300, 129, 200, False, True, 0),      # ragged: the two layers one after the other
 ])
-def test_mlp_bwd(dev, T, h, F, acc, bias):
+def test_mlp_bwd(dev, T, h, F, acc, bias, tile):
     """The backward of one shard's MLP block against the oracle's chain
-    (sampled token rows of the data gradients on the large shapes)."""
+    (sampled token rows of the data gradients on the large shapes); tile != 0
+    forces that pipelined tile on every product that fits it."""
     import tensor_transformer_layer_fwd_amd as tp
     from tensor_transformer_layer_fwd_amd import _lib as L
-    _say(f"mlp bwd T={T} h={h} F={F} acc={acc} bias={bias}")
+    _say(f"mlp bwd T={T} h={h} F={F} acc={acc} bias={bias} tile={tile}")
     rng = np.random.default_rng(T + h + F + acc)
     dt = "bf16"
     dZ, dZr = rand(rng, (T, h), 1.0, dt)
@@ -695,13 +698,17 @@ def test_mlp_bwd(dev, T, h, F, acc, bias):
         out[k] = torch.from_numpy(prev[k]).to(dev) if acc else torch.empty(*shp, device=dev)
     dU = torch.empty(T, F, dtype=torch.bfloat16, device=dev)
     dXp = torch.empty(T, h, device=dev)
-    ws = torch.full((max(16, L.tp_mlp_bwd_workspace_size(T, h, F, L.TP_BF16)),), 255,
-                    dtype=torch.uint8, device=dev)
-    tp.tp_mlp_bwd(upload(dZr, dt, dev), upload(Xr, dt, dev), upload(Ar, dt, dev),
-                  upload(Br, dt, dev), upload(Ur, dt, dev), upload(Yr, dt, dev), dU, out["dB"],
-                  out["db"] if bias else None, dXp, out["dA"], out["da"] if bias else None,
-                  accumulate=acc, workspace=ws)
-    torch.cuda.synchronize()
+    tp.tp_set_gemm_override(tile, 1)
+    try:
+        ws = torch.full((max(16, L.tp_mlp_bwd_workspace_size(T, h, F, L.TP_BF16)),), 255,
+                        dtype=torch.uint8, device=dev)
+        tp.tp_mlp_bwd(upload(dZr, dt, dev), upload(Xr, dt, dev), upload(Ar, dt, dev),
+                      upload(Br, dt, dev), upload(Ur, dt, dev), upload(Yr, dt, dev), dU,
+                      out["dB"], out["db"] if bias else None, dXp, out["dA"],
+                      out["da"] if bias else None, accumulate=acc, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        tp.tp_set_gemm_override(0)
     dU_ref = oracle.linear_bwd_dgrad(dZ, B, U, "gelu")
     dB_ref, db_ref = oracle.linear_bwd_wgrad(Y, dZ)
     dA_ref, da_ref = oracle.linear_bwd_wgrad(X, dU_ref)
