@@ -55,6 +55,10 @@ def test_workspace_size_query(lib):
     assert lib.tp_linear_bwd_wgrad_workspace_size(0, 5, 5, L.TP_BF16, ctypes.byref(out)) == -2
     assert lib.tp_linear_bwd_wgrad_workspace_size(5, 5, 5, 7, ctypes.byref(out)) == -3
     assert lib.tp_linear_bwd_wgrad_workspace_size(5, 5, 5, 1, None) == -1
+    for q in (lib.tp_linear_bwd_workspace_size, lib.tp_mlp_bwd_workspace_size):
+        assert q(0, 5, 5, L.TP_BF16, ctypes.byref(out)) == -2
+        assert q(5, 5, 5, 7, ctypes.byref(out)) == -3
+        assert q(5, 5, 5, 1, None) == -1
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation
