@@ -468,18 +468,16 @@ int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, 
     // partials sit one after the other in the workspace
     char* ws = static_cast<char*>(workspace);
     const size_t b2 = pair_bytes(T, F, h, db != nullptr);
-    const PairSetup q2 = setup_pair(dZ, B_i, U_i, TP_ACT_GELU_TANH, Y_i, dU_i, dB_i, db, T, F, h,
-                                    ld_dz, ld_b, ld_u, ld_y, ld_du, ld_db, accumulate, dt, ws,
-                                    workspace_bytes);
+    PairSetup q2 = setup_pair(dZ, B_i, U_i, TP_ACT_GELU_TANH, Y_i, dU_i, dB_i, db, T, F, h, ld_dz,
+                              ld_b, ld_u, ld_y, ld_du, ld_db, accumulate, dt, ws, workspace_bytes);
     // fc1's bias gradient da_i = column sums of dU_i: fc2's data-gradient
     // epilogue adds each block tile's rows as it stores dU_i, and the partials
     // (behind both layers' own) are added in fc1's launch
     const size_t b1 = pair_bytes(T, h, F, false);
-    PairSetup q1 =
+    const PairSetup q1 =
         setup_pair(dU_i, A_i, nullptr, TP_ACT_NONE, X, dXp_i, dA_i, nullptr, T, h, F, ld_du, ld_a,
                    h, ld_x, ld_dxp, ld_da, accumulate, TP_F32, ws ? ws + b2 : nullptr,
                    workspace_bytes > b2 ? workspace_bytes - b2 : 0);
-    PairSetup q2m = q2;
     PairRider rider;
     bool part_ok = true;
     if (da_i && q2.ok) {
@@ -488,15 +486,14 @@ int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, 
       part_ok = q2.ekd == kEpiDGelu && T % bm == 0 && ws && workspace_bytes >= b2 + b1 + part_bytes;
       if (part_ok) {
         float* part = reinterpret_cast<float*>(ws + b2 + b1);
-        q2m.pd.cs_part = part;
+        q2.pd.cs_part = part;
         rider.cs2 = bias_grad_params(dU_i, da_i, T, F, ld_du, dt, accumulate, part);
         rider.cs2_nchunks = static_cast<int>(T / bm);
         rider.ncs2 = static_cast<int>((F + 63) / 64);
       }
     }
-    if (q2.ok && q1.ok && part_ok && rider_for(q2m, &rider)) {
-      hipError_t e =
-          launch_gemm_bwd_pair(q2m.pw, q2m.pd, q2m.plan.tile, q2m.ekd, PairRider{}, stream);
+    if (q2.ok && q1.ok && part_ok && rider_for(q2, &rider)) {
+      hipError_t e = launch_gemm_bwd_pair(q2.pw, q2.pd, q2.plan.tile, q2.ekd, PairRider{}, stream);
       if (e == hipSuccess)
         e = launch_gemm_bwd_pair(q1.pw, q1.pd, q1.plan.tile, q1.ekd, rider, stream);
       if (e == hipSuccess) e = finish_pair(q1, stream);
