@@ -478,8 +478,11 @@ __device__ __forceinline__ bf16x8_t pack8(const f32x16_t& v, int hh) {
 // fixed order). Per 64-query tile and 32-query half m: S = Q K^T and
 // dP = dC V^T (lane = key, registers = queries), P, dS, then dV^T += dC^T P
 // and dK^T += Q^T dS.
-template <int QG>
-__global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) {
+// dK and dV of key block `block` (blocks key-block-major within a (batch,
+// head)); LDS: its own array, or a pool of POOL bytes shared with the dQ blocks
+// of the same launch.
+template <int QG, int POOL = 0>
+__device__ __forceinline__ void attn_bwd_kv_block(const AttnBwdParams& p, const int block) {
   // one 3-stage ring of query tiles (Q, dC, stats) per group: every stage
   // offset fits the 16-bit immediate of the fragment reads
   constexpr int NS = kBStages;
@@ -490,8 +493,8 @@ __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) 
   const int kw = wave & 3, grp = wave >> 2;
   const int64_t seq = p.seq;
   const int nkb = static_cast<int>((seq + 127) / 128);
-  const int kb = static_cast<int>(blockIdx.x % nkb);  // the keys most queries see first
-  const int bh = static_cast<int>(blockIdx.x / nkb);
+  const int kb = block % nkb;  // the keys most queries see first
+  const int bh = block / nkb;
   const int h = bh % static_cast<int>(p.heads);
   const int64_t b = bh / p.heads;
   const int64_t row0 = b * seq, hd = p.heads * kD;
@@ -521,7 +524,8 @@ __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) 
   TileCopy cq, cd;
   cq.init(qkv, p.ld_qkv, row0, h * kD, 2 * kw, lane);  // Q tile: windows 2kw, 2kw+1
   cd.init(dcp, p.ld_dc, row0, h * kD, 2 * kw, lane);   // dC tile
-  uint8_t* const lds = attn_bwd_lds<kLds>();
+  static_assert(POOL == 0 || POOL >= kLds, "LDS pool");
+  uint8_t* const lds = attn_bwd_lds<POOL ? POOL : kLds>();
   FragAddr fa;
   fa.init(attn_lds_addr(lds) + grp * kRing, lane);
   // stats copy: waves 0 and 2 of a group copy lse, 1 and 3 delta, of queries
@@ -676,8 +680,12 @@ __global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) 
 // KG = 2 groups, waves w and w + 4 hold the same queries, alternate key tiles
 // and add their dQ through LDS at the end. Per 64-key tile and 32-key half m:
 // S^T = K Q^T, dP^T = V dC^T (lane = query), P^T, dS^T, dQ^T += K^T dS^T.
-template <int KG>
-__global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
+// dQ of query block `block`; LDS as attn_bwd_kv_block. Blocks are taken
+// longest causal row first within each (batch, head), or with BYLEN across all
+// of them (every head's last query block first), which pairs the longest rows
+// with the CUs that the dK/dV blocks of the same launch free first.
+template <int KG, int POOL = 0, bool BYLEN = false>
+__device__ __forceinline__ void attn_bwd_q_block(const AttnBwdParams& p, const int block) {
   constexpr int kPair = 2 * kTileBytes;  // one K and one V tile
   constexpr int NS = kBStages;            // a 3-stage ring of pairs per group
   constexpr int kRing = NS * kPair;
@@ -687,8 +695,9 @@ __global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
   const int qw = wave & 3, grp = wave >> 2;
   const int64_t seq = p.seq;
   const int nqb = static_cast<int>((seq + kQB - 1) / kQB);
-  const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
-  const int bh = static_cast<int>(blockIdx.x / nqb);
+  const int nbh = static_cast<int>(p.batch * p.heads);
+  const int qb = nqb - 1 - (BYLEN ? block / nbh : block % nqb);
+  const int bh = BYLEN ? block % nbh : block / nqb;
   const int h = bh % static_cast<int>(p.heads);
   const int64_t b = bh / p.heads;
   const int64_t row0 = b * seq, hd = p.heads * kD;
@@ -718,7 +727,8 @@ __global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
   TileCopy ck, cv;
   ck.init(qkv, p.ld_qkv, row0, hd + h * kD, 2 * qw, lane);
   cv.init(qkv, p.ld_qkv, row0, 2 * hd + h * kD, 2 * qw, lane);
-  uint8_t* const lds = attn_bwd_lds<kLds>();
+  static_assert(POOL == 0 || POOL >= kLds, "LDS pool");
+  uint8_t* const lds = attn_bwd_lds<POOL ? POOL : kLds>();
   FragAddr fa;
   fa.init(attn_lds_addr(lds) + grp * kRing, lane);
   // stage si holds key tiles KG*si .. KG*si + KG-1 (one past the last is
@@ -830,6 +840,27 @@ __global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
   }
 }
 
+template <int QG>
+__global__ __launch_bounds__(256 * QG) void attn_bwd_kv_kernel(AttnBwdParams p) {
+  attn_bwd_kv_block<QG>(p, static_cast<int>(blockIdx.x));
+}
+
+template <int KG>
+__global__ __launch_bounds__(256 * KG) void attn_bwd_q_kernel(AttnBwdParams p) {
+  attn_bwd_q_block<KG>(p, static_cast<int>(blockIdx.x));
+}
+
+// Both passes in one launch (each reads only the inputs and delta): the dK/dV
+// blocks first, then the dQ blocks, in one LDS pool sized for the larger.
+template <int G>
+__global__ __launch_bounds__(256 * G) void attn_bwd_kvq_kernel(AttnBwdParams p, int kv_blocks) {
+  constexpr int kKv = G * kBStages * kBStageBytes, kQ = G * kBStages * 2 * kTileBytes;
+  constexpr int kPool = kKv > kQ ? kKv : kQ;
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < kv_blocks) attn_bwd_kv_block<G, kPool>(p, b);
+  else attn_bwd_q_block<G, kPool, true>(p, b - kv_blocks);
+}
+
 }  // namespace
 
 hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s) {
@@ -841,6 +872,17 @@ hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   // two query (key) groups per block while the grid leaves SIMDs with one wave
   const int64_t kv_blocks = bh * ((p.seq + 127) / 128), q_blocks = bh * ((p.seq + kQB - 1) / kQB);
+  const bool kv2 = kv_blocks < 2 * 256, q2 = q_blocks < 2 * 256;
+  if (kv2 == q2 && kv_blocks + q_blocks <= 0x7fffffff) {  // one launch for both passes
+    const unsigned grid = static_cast<unsigned>(kv_blocks + q_blocks);
+    if (kv2)
+      hipLaunchKernelGGL(attn_bwd_kvq_kernel<2>, dim3(grid), dim3(512), 0, s, p,
+                         static_cast<int>(kv_blocks));
+    else
+      hipLaunchKernelGGL(attn_bwd_kvq_kernel<1>, dim3(grid), dim3(256), 0, s, p,
+                         static_cast<int>(kv_blocks));
+    return hipGetLastError();
+  }
   if (kv_blocks < 2 * 256)
     hipLaunchKernelGGL(attn_bwd_kv_kernel<2>, dim3(static_cast<unsigned>(kv_blocks)), dim3(512), 0,
                        s, p);
