@@ -102,16 +102,45 @@ def layer_bwd_calls(step, i=0):
     ]
 
 
+def pair_calls(step, i=0):
+    """The layers of shard i whose fused backward is one paired kernel launch
+    (pairing query: paired, weight gradient not split), each timed without
+    its bias gradient, which the step adds as column partials and a short
+    second pass: (name, thunk, gemm flops, (T, k, n, pairing, splitk))."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    cfg, o, inp = step.cfg, step.out, step.inp
+    if not (cfg.mlp and step.fused_bwd and cfg.dtype == "bf16"):
+        return []
+    T, h, F = cfg.T, cfg.h, cfg.F
+    A_i, B_i = step._col("A", i, F), step._row("B", i, F)
+    f = 4 * T * h * F
+    out = []
+    for name, k, n, fn in (
+            ("fc2_bwd_pair", F, h,
+             lambda: L.tp_linear_bwd(inp["dZ"], B_i, o[f"U_{i}"], o[f"Y_{i}"], o[f"dU_{i}"],
+                                     o[f"dB_{i}"], None, act="gelu", workspace=step.workspace)),
+            ("fc1_bwd_pair", h, F,
+             lambda: L.tp_linear_bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"],
+                                     o[f"dA_{i}"], None, act="none", workspace=step.workspace))):
+        pr, sk = L.tp_linear_bwd_plan(T, k, n)
+        if pr and sk == 1:
+            out.append((name, fn, f, (T, k, n, pr, sk)))
+    return out
+
+
 def gemm_call_bytes(cfg, name):
-    """Algorithmic HBM bytes of one single-GEMM call of the bf16 MLP step: every
-    operand read once, every output written once (bf16 activations, fp32
-    partials)."""
+    """Algorithmic HBM bytes of one single-kernel call of the bf16 MLP step:
+    every operand read once, every output written once (bf16 activations, fp32
+    partials and weight gradients)."""
     T, h, F, e = cfg.T, cfg.h, cfg.F, 2
     return {
         "fc1_fwd": T * h * e + h * F * e + (F * e if cfg.has_bias else 0) + 2 * T * F * e,
         "fc2_fwd": T * F * e + F * h * e + T * h * 4,
         "fc2_dgrad": T * h * e + F * h * e + 2 * T * F * e,
         "fc1_dgrad": T * F * e + h * F * e + T * h * 4,
+        # both products of a layer: the shared dOut read once, dW in fp32
+        "fc2_bwd_pair": T * h * e + F * h * e + 3 * T * F * e + F * h * 4,
+        "fc1_bwd_pair": T * F * e + h * F * e + T * h * e + T * h * 4 + h * F * 4,
     }[name]
 
 
@@ -276,6 +305,7 @@ def main():
         step = ShardStep(cfg, make_inputs(cfg), "cuda:0")
         step.run_eager()
         calls = {n: (fn, f) for n, fn, f in shard_calls(step)}
+        calls.update({n: (fn, f) for n, fn, f, _ in pair_calls(step)})
         for name in args.only_call.split(","):
             fn, f = calls[name]
             ms = time_call(fn, args.steps)
@@ -309,21 +339,38 @@ def main():
     for name, fn, f in layer_bwd_calls(step):
         ms = time_call(fn, args.kernel_reps)
         layer_bwd[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
-    # dominant kernel: the slowest call that is a single GEMM kernel (the wgrad
-    # calls also launch a split-K fix-up and the bias column sums)
-    single = [k for k in kernels if not k.endswith("wgrad")]
+    # dominant kernel: the slowest single-kernel launch the step makes. A layer
+    # whose fused backward is one paired launch contributes that kernel; any
+    # other layer runs its data gradient as a kernel of its own (its weight
+    # gradient call also launches a split-K fix-up and the bias column sums)
+    flops_of = {name: f for name, _, f in shard_calls(step)}
+    pair_geom = {}
+    for name, fn, f, geom in pair_calls(step):
+        ms = time_call(fn, args.kernel_reps)
+        kernels[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        flops_of[name], pair_geom[name] = f, geom
+    single = ["fc1_fwd", "fc2_fwd"]
+    for layer in ("fc2", "fc1"):
+        single.append(f"{layer}_bwd_pair" if f"{layer}_bwd_pair" in pair_geom
+                      else f"{layer}_dgrad")
     dom = max(single, key=lambda k: kernels[k]["us"])
-    dom_flops = 2 * cfg.T * cfg.h * cfg.F
+    dom_flops = flops_of[dom]
     dom_bytes = gemm_call_bytes(cfg, dom)
     dom_s = kernels[dom]["us"] * 1e-6
     dom_tf = dom_flops / dom_s / 1e12
     dom_gbs = dom_bytes / dom_s / 1e9
     # the roof that takes longer at peak bounds the kernel
     hbm_bound = dom_bytes / (PEAK_HBM_GBS * 1e9) > dom_flops / (PEAK_BF16_TFLOPS * 1e12)
-    dom_shape = {"fc1_fwd": (cfg.T, cfg.F, cfg.h), "fc2_fwd": (cfg.T, cfg.h, cfg.F),
-                 "fc2_dgrad": (cfg.T, cfg.F, cfg.h), "fc1_dgrad": (cfg.T, cfg.h, cfg.F)}[dom]
     from tensor_transformer_layer_fwd_amd import _lib as L
-    dom_plan = L.tp_gemm_plan(*dom_shape)
+    if dom in pair_geom:
+        T_, k_, n_, pr_, sk_ = pair_geom[dom]
+        dom_gemm = {"T": T_, "k": k_, "n": n_, "pairing": pr_, "splitk": sk_,
+                    "us_per_launch": kernels[dom]["us"]}
+    else:
+        M_, N_, K_ = {"fc1_fwd": (cfg.T, cfg.F, cfg.h), "fc2_fwd": (cfg.T, cfg.h, cfg.F),
+                      "fc2_dgrad": (cfg.T, cfg.F, cfg.h), "fc1_dgrad": (cfg.T, cfg.h, cfg.F)}[dom]
+        dom_gemm = {"M": M_, "N": N_, "K": K_, "tile": L.tp_gemm_plan(M_, N_, K_)[0],
+                    "us_per_launch": kernels[dom]["us"]}
     log(f"[bench] per-call: {json.dumps(kernels)}")
 
     # HBM-bound passes: the sum over shards (fp32 partials -> bf16 + bias) and
@@ -443,8 +490,7 @@ def main():
                      "algorithmic_bytes": dom_bytes, "gemm_flops": dom_flops,
                      "tflops": round(dom_tf, 1),
                      "mfma_frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
-                     "gemm": {"M": dom_shape[0], "N": dom_shape[1], "K": dom_shape[2],
-                              "tile": dom_plan[0], "us_per_launch": kernels[dom]["us"]}},
+                     "gemm": dom_gemm},
         "per_call_shard0": kernels,
         "gemm_calls_sum_us": round(gemm_sum_us, 1),
         "layer_bwd_shard0": layer_bwd,

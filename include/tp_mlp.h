@@ -216,6 +216,21 @@ int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const
 int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t* bytes);
 
 /*
+ * How tp_linear_bwd runs a bf16 layer of this shape (pure host function, for
+ * tuning, tests and measurement). Writes the pairing: 0 (no paired kernel
+ * fits: the two calls run), 1 (one launch, both products on 128x128 tiles),
+ * 2 (one launch, weight gradient on 128x128 and data gradient on 128x192
+ * tiles), 3 (one launch, both on 256x192 tiles); and the weight gradient's
+ * number of K slices in that launch (1 when pairing is 0). A paired call is
+ * one kernel launch unless splitk > 1 (a fix-up launch sums the slices) or
+ * dbias is requested over more than one row block (a second pass sums the
+ * column partials). Shape only: the call pairs when its operands also meet
+ * the alignment stated for tp_linear_bwd. Returns TP_ERR_SHAPE for a
+ * dimension < 1; either output pointer may be NULL.
+ */
+int tp_linear_bwd_plan(int64_t T, int64_t k, int64_t n, int* pairing, int* splitk);
+
+/*
  * The backward of one shard's MLP block ("Megatron" page, "Tensor
  * Parallelism / mathematical principles": the column-parallel fc1 with GeLU,
  * then the row-parallel fc2; derivatives not on the pages), without the sum

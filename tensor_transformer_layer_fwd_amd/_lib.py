@@ -39,6 +39,8 @@ SIGNATURES = {
                              _i64, _i64, _i64, _i64, _i64, _int, _int, _int, _vp, _sz, _vp]),
     "tp_linear_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                             ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_linear_bwd_plan": (_int, [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int),
+                                  ctypes.POINTER(ctypes.c_int)]),
     "tp_mlp_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                           _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                           _int, _vp, _sz, _vp]),
@@ -207,6 +209,15 @@ def tp_linear_bwd_workspace_size(T: int, k: int, n: int, dt: int) -> int:
     _check("tp_linear_bwd_workspace_size",
            lib().tp_linear_bwd_workspace_size(T, k, n, dt, ctypes.byref(out)))
     return int(out.value)
+
+
+def tp_linear_bwd_plan(T: int, k: int, n: int):
+    """(pairing, K slices) of tp_linear_bwd for a bf16 layer: pairing 0 runs
+    the two products as separate calls, 1..3 in one paired launch."""
+    pr, sk = ctypes.c_int(0), ctypes.c_int(0)
+    _check("tp_linear_bwd_plan", lib().tp_linear_bwd_plan(T, k, n, ctypes.byref(pr),
+                                                           ctypes.byref(sk)))
+    return int(pr.value), int(sk.value)
 
 
 def tp_linear_bwd(dOut, W, U, In, dIn, dW, dbias=None, act="none", accumulate=False,

@@ -429,6 +429,14 @@ int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t
   return TP_OK;
 }
 
+int tp_linear_bwd_plan(int64_t T, int64_t k, int64_t n, int* pairing, int* splitk) {
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  const SplitPlan pl = pair_plan(T, k, n);
+  if (pairing) *pairing = pl.tile;
+  if (splitk) *splitk = pl.tile == kPairNone ? 1 : pl.splitk;
+  return TP_OK;
+}
+
 int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, int dt, size_t* bytes) {
   if (!bytes) return TP_ERR_NULL;
   size_t b2 = 0, b1 = 0;

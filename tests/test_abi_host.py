@@ -143,6 +143,27 @@ def test_gemm_plan_query(lib):
     assert lib.tp_gemm_plan(0, 5, 5, 0, None, None, None) == -2
 
 
+def test_linear_bwd_plan(lib):
+    """The pairing query: shape-only, agreeing with the workspace query."""
+    # the MLP layers of the GPT-2-small shard (T=4096, h=768, F=1536) and of
+    # the 175B-class shard (T=2048, h=12288, F=6144)
+    assert L.tp_linear_bwd_plan(4096, 768, 1536) == (1, 1)    # fc1: 128x128 both
+    assert L.tp_linear_bwd_plan(4096, 1536, 768) == (2, 1)    # fc2: 128x128 + 128x192
+    assert L.tp_linear_bwd_plan(2048, 12288, 6144)[0] == 3
+    assert L.tp_linear_bwd_plan(2048, 6144, 12288)[0] == 3
+    # no pipelined tile fits a ragged layer
+    assert L.tp_linear_bwd_plan(300, 129, 200) == (0, 1)
+    assert L.tp_linear_bwd_plan(4096, 768, 1000) == (0, 1)
+    for T, k, n in [(4096, 768, 1536), (4096, 256, 256), (8192, 256, 256), (2048, 12288, 6144)]:
+        pr, sk = L.tp_linear_bwd_plan(T, k, n)
+        assert pr in (0, 1, 2, 3) and 1 <= sk <= 16
+        if pr and sk > 1:   # split partials live in the workspace
+            assert L.tp_linear_bwd_workspace_size(T, k, n, L.TP_BF16) >= sk * k * n * 4
+    assert lib.tp_linear_bwd_plan(0, 8, 8, None, None) == -2
+    assert lib.tp_linear_bwd_plan(8, 8, -1, None, None) == -2
+    assert lib.tp_linear_bwd_plan(64, 128, 128, None, None) == 0
+
+
 def test_linear_bwd_validation(lib):
     """tp_linear_bwd runs every check of both gradients before any launch."""
     f = lib.tp_linear_bwd
