@@ -269,6 +269,27 @@ struct OperandF8 {
 // ---------------------------------------------------------------------------
 // The kernel
 // ---------------------------------------------------------------------------
+// Rows of a tile group when each XCD takes c consecutive tiles of the grouped
+// column-major order. A run of c tiles is a g x (c/g) rectangle when g divides
+// c and tiles_m and c divides g * tiles_n; the rectangle reads g*BM + (c/g)*BN
+// operand rows per K step into the XCD's L2. The default of 8 rows is kept
+// unless a rectangle reads at most 4/5 of what 8 rows (and ceil(c/8) columns)
+// read: that happens for small grids, such as 9 weight-gradient tiles per XCD
+// (3 x 3 instead of a column of 8 and one more tile).
+__device__ __forceinline__ int xcd_group_rows(int c, int tiles_m, int tiles_n, int BM, int BN) {
+  const int base = 8 * BM + ((c + 7) / 8) * BN;
+  int best = 8, cost = base;
+  for (int g = 8; g >= 1; --g) {
+    if (c % g != 0 || tiles_m % g != 0 || (g * tiles_n) % c != 0) continue;
+    const int w = g * BM + (c / g) * BN;
+    if (w < cost) {
+      cost = w;
+      best = g;
+    }
+  }
+  return 5 * cost <= 4 * base ? best : 8;
+}
+
 // F8 = 0: bf16 operands; F8 = 1 + fmt_a + 2 * fmt_b: FP8 codes (both operands
 // K-contiguous, BK = 128 codes), fmt 0 = E4M3, 1 = E5M2.
 // One block of a product: output tile (or column-sum unit) number `block` of
@@ -296,7 +317,8 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---- output tile (same XCD-aware order as the general kernel)
+  // ---- output tile: blocks go round-robin over the 8 XCDs, so each XCD
+  // takes a run of consecutive tiles of a grouped column-major order
   const int tiles_m = static_cast<int>(p.M / BM);
   const int tiles_n = static_cast<int>(p.N / BN);
   const int ntiles = tiles_m * tiles_n;
@@ -313,8 +335,11 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
     }
   }
   int bid = block - z * ntiles;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-  constexpr int G = 8;
+  int G = 8;
+  if ((ntiles & 7) == 0) {
+    bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+    G = xcd_group_rows(ntiles >> 3, tiles_m, tiles_n, BM, BN);
+  }
   const int group = bid / (G * tiles_n);
   const int first_m = group * G;
   const int gs = min(tiles_m - first_m, G);
