@@ -293,7 +293,8 @@ int tp_reduce_partials(const float* const* partials, int p, const void* bias, vo
 /*
  * Standalone bias + activation pass: Y = act(U + bias), elementwise.
  * The fused epilogue of tp_column_linear_fwd does the same work inside the
- * GEMM; this call exists to measure the pass on its own (it is HBM-bound).
+ * GEMM. On its own the pass is HBM-bound. With bias NULL it rebuilds
+ * Y = GeLU(U) from a stored U for activation recompute.
  *
  * U    [T, n], ld_u, dtype in_dt
  * bias [n], dtype in_dt, or NULL

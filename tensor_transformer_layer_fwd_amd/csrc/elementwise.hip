@@ -184,8 +184,9 @@ __global__ __launch_bounds__(256) void bias_act_kernel(BiasActParams p) {
   }
 }
 
-// Vector path of bias_act: fp32 U, bf16 Y, eight columns per thread (two
-// 16-byte loads, one 16-byte store), 32-bit index arithmetic.
+// Vector path of bias_act: fp32 or bf16 U, bf16 Y, eight columns per thread
+// (two 16-byte loads of fp32 U or one of bf16 U, one 16-byte store), 32-bit
+// index arithmetic.
 __global__ __launch_bounds__(256) void bias_act_vec8_kernel(BiasActParams p) {
   const uint32_t no = static_cast<uint32_t>(p.N >> 3);
   const uint32_t total = static_cast<uint32_t>(p.T) * no;
@@ -193,7 +194,8 @@ __global__ __launch_bounds__(256) void bias_act_vec8_kernel(BiasActParams p) {
   for (uint32_t e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += stride) {
     const uint32_t t = e / no, c = (e - t * no) << 3;
     float u[8];
-    load8_f32(p.u, static_cast<int64_t>(t) * p.ldu + c, u);
+    if (p.u_f32) load8_f32(p.u, static_cast<int64_t>(t) * p.ldu + c, u);
+    else load8_bf16(p.u, static_cast<int64_t>(t) * p.ldu + c, u);
     if (p.bias) {
       float b[8];
       if (p.in_bf16) load8_bf16(p.bias, c, b);
@@ -323,8 +325,10 @@ hipError_t launch_reduce(const ReduceParams& p, hipStream_t s) {
 
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s) {
   auto a16 = [](const void* q) { return reinterpret_cast<uintptr_t>(q) % 16 == 0; };
-  if (p.u_f32 && p.out_bf16 && p.N % 8 == 0 && p.ldu % 4 == 0 && p.ldy % 8 == 0 && a16(p.u) &&
-      a16(p.y) && (!p.bias || a16(p.bias)) && p.T * (p.N / 8) < (int64_t(1) << 31)) {
+  // rows of U start 16-byte aligned: 4 fp32 or 8 bf16 elements
+  if ((p.u_f32 || p.in_bf16) && p.out_bf16 && p.N % 8 == 0 && p.ldu % (p.u_f32 ? 4 : 8) == 0 &&
+      p.ldy % 8 == 0 && a16(p.u) && a16(p.y) && (!p.bias || a16(p.bias)) &&
+      p.T * (p.N / 8) < (int64_t(1) << 31)) {
     hipLaunchKernelGGL(bias_act_vec8_kernel, dim3(grid_for(p.T * (p.N / 8), 256)), dim3(256), 0,
                        s, p);
     return hipGetLastError();

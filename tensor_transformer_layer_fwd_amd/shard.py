@@ -15,8 +15,11 @@ tp_linear_bwd_dgrad or tp_linear_bwd_wgrad call of its own.
 With recompute=True the step keeps only U_i of the fc1 output across the
 step (the activation recomputation of the "Megatron" page's training
 optimisations): Y_i lives in one transient buffer that fc2's forward reads, and
-the backward recomputes it from U_i in the fc2 dgrad epilogue
-(tp_linear_bwd_dgrad_recompute) just before fc2's weight gradient reads it.
+the backward recomputes it from U_i. With the fused backward, on shapes where
+fc2's gradients pair (tp_linear_bwd_plan), that is one elementwise pass
+(tp_bias_act) before the shard's tp_mlp_bwd call, so both layers still pair.
+Otherwise it is the fc2 dgrad epilogue (tp_linear_bwd_dgrad_recompute), just
+before fc2's weight gradient reads it.
 
 With fp8=True every MLP product runs on the FP8 matrix cores: each operand
 is quantised (tp_fp8_quantize, per-tensor current scaling) from its stored
@@ -66,6 +69,11 @@ class ShardStep:
         self.device = torch.device(device)
         self.dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
         self.tp_dt = L.TP_BF16 if cfg.dtype == "bf16" else L.TP_F32
+        # recompute with the fused backward: where fc2's gradients pair, Y_i is
+        # rebuilt by an elementwise pass so that the pair can read it;
+        # elsewhere the fc2 dgrad epilogue recomputes it
+        self.rebuild_y = (self.recompute and self.fused_bwd and cfg.dtype == "bf16" and
+                          L.tp_linear_bwd_plan(cfg.T, cfg.F, cfg.h)[0] != 0)
         self.inp = {k: to_device(v, self.device) for k, v in inputs.items()}
         self.out = {}
         self._graph = None
@@ -220,12 +228,17 @@ class ShardStep:
         for n, i in enumerate(cfg.shards):
             B_i, A_i = self._row("B", i, F), self._col("A", i, F)
             db = o["db"] if (cfg.has_bias and n == 0) else None
-            if self.fused_bwd and not self.recompute:
+            if self.fused_bwd and (self.rebuild_y or not self.recompute):
+                if self.rebuild_y:
+                    # Y_i again from the stored U_i, into the transient buffer:
+                    # one elementwise pass, so both layers can still pair
+                    L.tp_bias_act(o[f"U_{i}"], None, o["Yt"], act="gelu")
                 # both layers in one call: fc2's fix-up rides in fc1's launch
                 L.tp_mlp_bwd(inp["dZ"], inp["X"], A_i, B_i, o[f"U_{i}"], self._y(i), o[f"dU_{i}"],
                              o[f"dB_{i}"], db, o[f"dXp_{i}"], o[f"dA_{i}"], o.get(f"da_{i}"),
                              workspace=self.workspace)
-            elif self.recompute:
+                continue
+            if self.recompute:
                 # the weight gradient reads the Y_i the dgrad epilogue recomputes
                 L.tp_linear_bwd_dgrad_recompute(inp["dZ"], B_i, o[f"U_{i}"], o[f"dU_{i}"],
                                                 o["Yt"])
@@ -234,9 +247,8 @@ class ShardStep:
             else:
                 self._bwd(inp["dZ"], B_i, o[f"U_{i}"], self._y(i), o[f"dU_{i}"], o[f"dB_{i}"],
                           db, "gelu")
-            if not self.fused_bwd or self.recompute:
-                self._bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"], o[f"dA_{i}"],
-                          o.get(f"da_{i}"), "none")
+            self._bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"], o[f"dA_{i}"],
+                      o.get(f"da_{i}"), "none")
         if "dX" in o:
             L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])
 

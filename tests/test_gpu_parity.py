@@ -274,7 +274,7 @@ def test_reduce_partials_order_and_rounding(dev):
 @pytest.mark.parametrize("pad,with_bias", [(3, True), (8, True), (8, False)])
 def test_bias_act(dev, in_dt, out_dt, T, n, pad, with_bias):
     """Output row stride n + pad: pad 8 keeps 16-byte aligned rows (the
-    eight-column path for fp32 U and bf16 Y where n is a multiple of 8)."""
+    eight-column path for fp32 or bf16 U and bf16 Y where n is a multiple of 8)."""
     import tensor_transformer_layer_fwd_amd as tp
     rng = np.random.default_rng(T * n)
     U, Ur = rand(rng, (T, n), 2.0, in_dt)
@@ -850,16 +850,22 @@ def test_attention_bwd_deterministic(dev):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-@pytest.mark.parametrize("name,mb,seq", [("tiny", 8, 64), ("gpt2s", 1, 680), ("gpt350m", 1, 520)])
-def test_workload_recompute(dev, name, mb, seq):
+@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("name,mb,seq", [("tiny", 8, 64), ("gpt2s", 1, 680), ("gpt2s", 1, 1024),
+                                         ("gpt350m", 1, 520)])
+def test_workload_recompute(dev, name, mb, seq, fused):
     """The step with activation recompute: every output the oracle defines
     except the Y_i it no longer keeps, and the recomputed Y of the last shard
-    (left in the transient buffer) against the oracle's Y."""
+    (left in the transient buffer) against the oracle's Y. fused, where fc2
+    pairs: Y_i rebuilt by an elementwise pass before the paired backward;
+    otherwise in the fc2 dgrad epilogue."""
     from tensor_transformer_layer_fwd_amd.shard import ShardStep
     cfg = dataclasses.replace(get_config(name), micro_batch=mb, seq=seq)
-    _say(f"workload {name} with recompute T={cfg.T}")
+    _say(f"workload {name} with recompute T={cfg.T} fused={fused}")
     inputs = make_inputs(cfg)
-    step = ShardStep(cfg, inputs, dev, recompute=True)
+    step = ShardStep(cfg, inputs, dev, recompute=True, fused_bwd=fused)
+    # the aligned GPT-2-small shard pairs fc2's gradients: Y_i is rebuilt by a pass
+    assert step.rebuild_y == (fused and name == "gpt2s" and seq == 1024)
     step.run_eager()
     got = step.results()
     ref = oracle.run_config(cfg, inputs)
