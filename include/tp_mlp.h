@@ -403,6 +403,28 @@ int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x
                          hipStream_t stream);
 
 /*
+ * tp_fp8_quantize_both for n tensors (1 <= n <= 6) in two launches in all
+ * instead of 2n: one for every tensor's per-block maxima, one for every
+ * tensor's codes. Tensor i has its own scale and takes its arguments from
+ * entry i of each array. The arrays are HOST arrays of n entries; the pointers
+ * they hold are DEVICE pointers. Codes and scales are bitwise equal to n
+ * tp_fp8_quantize_both calls. No output may overlap another tensor's input or
+ * output. workspace: at least tp_fp8_quantize_multi_workspace_size(n) bytes
+ * (tensor i's maxima in its i-th slice), 4-byte aligned, contents on entry
+ * ignored. Every tensor is checked as tp_fp8_quantize_both checks it before
+ * the first launch, and the first failing check's status is returned.
+ * TP_ERR_SHAPE for n outside 1..6.
+ */
+int tp_fp8_quantize_both_multi(int n, const void* const* X, const int64_t* rows,
+                               const int64_t* cols, const int64_t* ld_x, const int* dt,
+                               const int* fmt, void* const* Q, const int64_t* ld_q,
+                               void* const* Qt, const int64_t* ld_qt, float* const* scale_inv,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace tp_fp8_quantize_both_multi needs for n tensors (n * 4 KiB). */
+int tp_fp8_quantize_multi_workspace_size(int n, size_t* bytes);
+
+/*
  * FP8 column-parallel forward: Y_i = act(X A_i + a_i) with U_i saved, as
  * tp_column_linear_fwd, from Xq = codes of X [T, h] (E4M3) and Atq = codes of
  * A_i^T [n, h] (E4M3, quantised with transpose). Y_i, U_i and bias_i bf16.

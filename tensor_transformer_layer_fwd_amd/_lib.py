@@ -60,6 +60,17 @@ SIGNATURES = {
                                ctypes.c_size_t, _vp]),
     "tp_fp8_quantize_both": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp, _i64,
                                     _vp, _vp, ctypes.c_size_t, _vp]),
+    "tp_fp8_quantize_both_multi": (_int, [_int, ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                          ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_void_p),
+                                          ctypes.POINTER(ctypes.c_int64),
+                                          ctypes.POINTER(ctypes.c_void_p), _vp, _sz, _vp]),
+    "tp_fp8_quantize_multi_workspace_size": (_int, [_int, ctypes.POINTER(ctypes.c_size_t)]),
     "tp_fp8_column_linear_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                         _i64, _i64, _i64, _int, _vp]),
     "tp_fp8_row_linear_fwd_partial": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -330,6 +341,36 @@ def tp_fp8_quantize_both(X, Q, Qt, scale_inv, workspace, fmt="e4m3", stream=None
         _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), _ptr(Q), _ld(Q), _ptr(Qt), _ld(Qt),
         _ptr(scale_inv), _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream(stream)))
+
+
+def tp_fp8_quantize_multi_workspace_size(n: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_fp8_quantize_multi_workspace_size",
+           lib().tp_fp8_quantize_multi_workspace_size(n, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_fp8_quantize_both_multi(items, workspace, stream=None):
+    """tp_fp8_quantize_both for each (X, Q, Qt, scale_inv, fmt) of `items` (at
+    most 6) in two launches in all."""
+    n = len(items)
+    vp = ctypes.c_void_p * n
+    i64 = ctypes.c_int64 * n
+    i32 = ctypes.c_int * n
+    X = vp(*[x.data_ptr() for x, *_ in items])
+    rows = i64(*[x.shape[0] for x, *_ in items])
+    cols = i64(*[x.shape[1] for x, *_ in items])
+    ld_x = i64(*[_ld(x) for x, *_ in items])
+    dt = i32(*[_dt(x) for x, *_ in items])
+    fmt = i32(*[_fmt(f) for *_, f in items])
+    Q = vp(*[q.data_ptr() for _, q, *_ in items])
+    ld_q = i64(*[_ld(q) for _, q, *_ in items])
+    Qt = vp(*[qt.data_ptr() for _, _, qt, *_ in items])
+    ld_qt = i64(*[_ld(qt) for _, _, qt, *_ in items])
+    si = vp(*[s.data_ptr() for _, _, _, s, _ in items])
+    _check("tp_fp8_quantize_both_multi", lib().tp_fp8_quantize_both_multi(
+        n, X, rows, cols, ld_x, dt, fmt, Q, ld_q, Qt, ld_qt, si, _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
 def tp_fp8_column_linear_fwd(Xq, Atq, x_si, a_si, bias, Y, U, act="gelu", stream=None):

@@ -46,12 +46,13 @@ __device__ __forceinline__ float block_max(float m, float* red) {
   return m;
 }
 
-__global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantParams p) {
+// Per-block maxima of |x|: block `block` of the tensor's `nblocks`.
+__device__ __forceinline__ void fp8_amax_block(const Fp8QuantParams& p, int block, int nblocks) {
   __shared__ float red[kThreads / 64];
   const int64_t ucols = (p.cols + 7) / 8, units = p.rows * ucols;
   float m = 0.0f;
-  for (int64_t u = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; u < units;
-       u += static_cast<int64_t>(gridDim.x) * kThreads) {
+  for (int64_t u = static_cast<int64_t>(block) * kThreads + threadIdx.x; u < units;
+       u += static_cast<int64_t>(nblocks) * kThreads) {
     const int64_t row = u / ucols, c0 = (u - row * ucols) * 8;
     float v[8];
     load8_any(p, row, c0, v);
@@ -59,7 +60,11 @@ __global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantParams p) {
     for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
   }
   m = block_max(m, red);
-  if (threadIdx.x == 0) p.partial[blockIdx.x] = m;
+  if (threadIdx.x == 0) p.partial[block] = m;
+}
+
+__global__ __launch_bounds__(kThreads) void fp8_amax_kernel(Fp8QuantParams p) {
+  fp8_amax_block(p, blockIdx.x, gridDim.x);
 }
 
 // Four codes of v[0..3] packed little-endian (v[0] in the low byte).
@@ -79,18 +84,18 @@ __device__ __forceinline__ uint32_t cvt4(const float* v, float s, float fmax, in
 }
 
 // amax from the per-block maxima, the scale, and (block 0) 1/s to memory
-__device__ __forceinline__ float fp8_scale(const Fp8QuantParams& p, float* red) {
+__device__ __forceinline__ float fp8_scale(const Fp8QuantParams& p, float* red, int block) {
   float m = 0.0f;
   for (int i = threadIdx.x; i < p.nblk; i += kThreads) m = fmaxf(m, p.partial[i]);
   m = block_max(m, red);
   const float s = m > 0.0f ? fp8_fmax(p.fmt) / m : 1.0f;
-  if (blockIdx.x == 0 && threadIdx.x == 0) p.scale_inv[0] = 1.0f / s;
+  if (block == 0 && threadIdx.x == 0) p.scale_inv[0] = 1.0f / s;
   return s;
 }
 
 __global__ __launch_bounds__(kThreads) void fp8_cast_kernel(Fp8QuantParams p) {
   __shared__ float red[kThreads / 64];
-  const float s = fp8_scale(p, red), fmax = fp8_fmax(p.fmt);
+  const float s = fp8_scale(p, red, blockIdx.x), fmax = fp8_fmax(p.fmt);
   const int64_t ucols = (p.cols + 7) / 8, units = p.rows * ucols;
   for (int64_t u = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; u < units;
        u += static_cast<int64_t>(gridDim.x) * kThreads) {
@@ -115,13 +120,14 @@ __global__ __launch_bounds__(kThreads) void fp8_cast_kernel(Fp8QuantParams p) {
 constexpr int kTT = 64;
 constexpr int kTStride = 80;  // bytes per LDS row: 16-byte aligned, rows spread over banks
 
-__global__ __launch_bounds__(kThreads) void fp8_cast_t_kernel(Fp8QuantParams p) {
+// Block `block` of the tensor's `nblocks`.
+__device__ __forceinline__ void fp8_cast_t_block(const Fp8QuantParams& p, int block, int nblocks) {
   __shared__ float red[kThreads / 64];
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTT * kTStride];
-  const float s = fp8_scale(p, red), fmax = fp8_fmax(p.fmt);
+  const float s = fp8_scale(p, red, block), fmax = fp8_fmax(p.fmt);
   const int64_t tr = (p.rows + kTT - 1) / kTT, tc = (p.cols + kTT - 1) / kTT;
   const int t = threadIdx.x, lr = t / 4, lc = 16 * (t % 4);
-  for (int64_t b = blockIdx.x; b < tr * tc; b += gridDim.x) {
+  for (int64_t b = block; b < tr * tc; b += nblocks) {
     const int64_t r0 = (b / tc) * kTT, c0 = (b % tc) * kTT;
     const int64_t row = r0 + lr;
     float v[16];
@@ -173,6 +179,29 @@ __global__ __launch_bounds__(kThreads) void fp8_cast_t_kernel(Fp8QuantParams p) 
   }
 }
 
+__global__ __launch_bounds__(kThreads) void fp8_cast_t_kernel(Fp8QuantParams p) {
+  fp8_cast_t_block(p, blockIdx.x, gridDim.x);
+}
+
+// Several tensors in one launch: tensor i owns blocks first[i] .. first[i+1]-1.
+__device__ __forceinline__ int fp8_multi_tensor(const Fp8MultiParams& m) {
+  int i = 0;
+  while (i + 1 < m.n && static_cast<int>(blockIdx.x) >= m.first[i + 1]) ++i;
+  return i;
+}
+
+__global__ __launch_bounds__(kThreads) void fp8_amax_multi_kernel(Fp8MultiParams m) {
+  const int i = fp8_multi_tensor(m);
+  const Fp8QuantParams p = m.t[i];
+  fp8_amax_block(p, blockIdx.x - m.first[i], m.first[i + 1] - m.first[i]);
+}
+
+__global__ __launch_bounds__(kThreads) void fp8_cast_t_multi_kernel(Fp8MultiParams m) {
+  const int i = fp8_multi_tensor(m);
+  const Fp8QuantParams p = m.t[i];
+  fp8_cast_t_block(p, blockIdx.x - m.first[i], m.first[i + 1] - m.first[i]);
+}
+
 }  // namespace
 
 int fp8_amax_blocks(int64_t rows, int64_t cols) {
@@ -181,21 +210,44 @@ int fp8_amax_blocks(int64_t rows, int64_t cols) {
   return static_cast<int>(b < kFp8AmaxBlocks ? b : kFp8AmaxBlocks);
 }
 
+namespace {
+unsigned cast_t_blocks(const Fp8QuantParams& p) {
+  const int64_t tiles = ((p.rows + kTT - 1) / kTT) * ((p.cols + kTT - 1) / kTT);
+  return static_cast<unsigned>(tiles < 4096 ? tiles : 4096);
+}
+}  // namespace
+
 hipError_t launch_fp8_quantize(Fp8QuantParams p, hipStream_t s) {
   p.nblk = fp8_amax_blocks(p.rows, p.cols);
   hipLaunchKernelGGL(fp8_amax_kernel, dim3(p.nblk), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.transpose) {
-    const int64_t tiles = ((p.rows + kTT - 1) / kTT) * ((p.cols + kTT - 1) / kTT);
-    const unsigned g = static_cast<unsigned>(tiles < 4096 ? tiles : 4096);
-    hipLaunchKernelGGL(fp8_cast_t_kernel, dim3(g), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(fp8_cast_t_kernel, dim3(cast_t_blocks(p)), dim3(kThreads), 0, s, p);
   } else {
     const int64_t units = p.rows * ((p.cols + 7) / 8);
     const int64_t b = (units + kThreads - 1) / kThreads;
     const unsigned g = static_cast<unsigned>(b < 8192 ? b : 8192);
     hipLaunchKernelGGL(fp8_cast_kernel, dim3(g), dim3(kThreads), 0, s, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_quantize_multi(const Fp8QuantParams* ps, int n, hipStream_t s) {
+  if (n < 1 || n > kFp8MaxMulti) return hipErrorInvalidValue;
+  Fp8MultiParams m{};
+  m.n = n;
+  for (int i = 0; i < n; ++i) {
+    m.t[i] = ps[i];
+    if (!m.t[i].transpose) return hipErrorInvalidValue;
+    m.t[i].nblk = fp8_amax_blocks(m.t[i].rows, m.t[i].cols);
+    m.first[i + 1] = m.first[i] + m.t[i].nblk;
+  }
+  hipLaunchKernelGGL(fp8_amax_multi_kernel, dim3(m.first[n]), dim3(kThreads), 0, s, m);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < n; ++i) m.first[i + 1] = m.first[i] + static_cast<int>(cast_t_blocks(m.t[i]));
+  hipLaunchKernelGGL(fp8_cast_t_multi_kernel, dim3(m.first[n]), dim3(kThreads), 0, s, m);
   return hipGetLastError();
 }
 

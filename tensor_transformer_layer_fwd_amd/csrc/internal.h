@@ -92,6 +92,15 @@ struct Fp8QuantParams {
 };
 int fp8_amax_blocks(int64_t rows, int64_t cols);
 hipError_t launch_fp8_quantize(Fp8QuantParams p, hipStream_t s);
+// Up to kFp8MaxMulti tensors, each quantised with transpose (and optionally its
+// own layout), in two launches; each tensor has its own partial array.
+constexpr int kFp8MaxMulti = 6;
+struct Fp8MultiParams {
+  Fp8QuantParams t[kFp8MaxMulti];
+  int first[kFp8MaxMulti + 1];  // first block of each tensor in the launch
+  int n;
+};
+hipError_t launch_fp8_quantize_multi(const Fp8QuantParams* ps, int n, hipStream_t s);
 
 // Attention core of one shard (forward): QKV [batch*seq, 3*heads*64] bf16 as
 // [Q | K | V], C [batch*seq, heads*64] bf16, lse [batch, heads, seq] (or null).

@@ -265,6 +265,38 @@ PairSetup setup_pair(const void* dOut, const void* W, const void* U, int act, co
 
 // What a paired weight gradient still needs after its launch: the split-K
 // fix-up, and pass 2 of its carried column sums.
+// Checks and parameters of one tensor quantised into both layouts.
+int fp8_both_params(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt, int fmt,
+                    void* Q, int64_t ld_q, void* Qt, int64_t ld_qt, float* scale_inv,
+                    void* workspace, size_t workspace_bytes, Fp8QuantParams* out) {
+  if (!X || !Q || !Qt || !scale_inv) return TP_ERR_NULL;
+  if (!dtype_ok(dt) || !fmt_ok(fmt)) return TP_ERR_DTYPE;
+  if (!dim_ok(rows) || !dim_ok(cols) || rows * cols > (int64_t(1) << 40)) return TP_ERR_SHAPE;
+  if (ld_x < cols || ld_q < cols || ld_qt < rows) return TP_ERR_SHAPE;
+  if (!aligned(scale_inv, 4) || !aligned(X, dt == TP_BF16 ? 2 : 4)) return TP_ERR_SHAPE;
+  if (!workspace || workspace_bytes < kFp8AmaxBlocks * sizeof(float) || !aligned(workspace, 4))
+    return TP_ERR_WORKSPACE;
+  Fp8QuantParams q{};
+  q.x = X;
+  q.rows = rows;
+  q.cols = cols;
+  q.ld_x = ld_x;
+  q.x_bf16 = dt == TP_BF16;
+  q.fmt = fmt;
+  q.transpose = 1;
+  q.q = static_cast<uint8_t*>(Qt);
+  q.ld_q = ld_qt;
+  q.q_rows = static_cast<uint8_t*>(Q);
+  q.ld_q_rows = ld_q;
+  q.scale_inv = scale_inv;
+  q.partial = static_cast<float*>(workspace);
+  q.vec_in = aligned(X, 16) && ld_x % (dt == TP_BF16 ? 8 : 4) == 0;
+  q.vec_out = aligned(Qt, 16) && ld_qt % 16 == 0;
+  q.vec_rows = aligned(Q, 16) && ld_q % 16 == 0;
+  *out = q;
+  return TP_OK;
+}
+
 bool pair_needs_finish(const PairSetup& q) {
   return q.plan.splitk > 1 || (q.carry && q.pw.cs_nchunks > 1);
 }
@@ -691,31 +723,41 @@ int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x
                          int fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
                          float* scale_inv, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
-  if (!X || !Q || !Qt || !scale_inv) return TP_ERR_NULL;
-  if (!dtype_ok(dt) || !fmt_ok(fmt)) return TP_ERR_DTYPE;
-  if (!dim_ok(rows) || !dim_ok(cols) || rows * cols > (int64_t(1) << 40)) return TP_ERR_SHAPE;
-  if (ld_x < cols || ld_q < cols || ld_qt < rows) return TP_ERR_SHAPE;
-  if (!aligned(scale_inv, 4) || !aligned(X, dt == TP_BF16 ? 2 : 4)) return TP_ERR_SHAPE;
-  if (!workspace || workspace_bytes < kFp8AmaxBlocks * sizeof(float) || !aligned(workspace, 4))
-    return TP_ERR_WORKSPACE;
   Fp8QuantParams q{};
-  q.x = X;
-  q.rows = rows;
-  q.cols = cols;
-  q.ld_x = ld_x;
-  q.x_bf16 = dt == TP_BF16;
-  q.fmt = fmt;
-  q.transpose = 1;
-  q.q = static_cast<uint8_t*>(Qt);
-  q.ld_q = ld_qt;
-  q.q_rows = static_cast<uint8_t*>(Q);
-  q.ld_q_rows = ld_q;
-  q.scale_inv = scale_inv;
-  q.partial = static_cast<float*>(workspace);
-  q.vec_in = aligned(X, 16) && ld_x % (dt == TP_BF16 ? 8 : 4) == 0;
-  q.vec_out = aligned(Qt, 16) && ld_qt % 16 == 0;
-  q.vec_rows = aligned(Q, 16) && ld_q % 16 == 0;
+  const int st = fp8_both_params(X, rows, cols, ld_x, dt, fmt, Q, ld_q, Qt, ld_qt, scale_inv,
+                                 workspace, workspace_bytes, &q);
+  if (st != TP_OK) return st;
   return hip_status(launch_fp8_quantize(q, stream));
+}
+
+int tp_fp8_quantize_multi_workspace_size(int n, size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (n < 1 || n > kFp8MaxMulti) return TP_ERR_SHAPE;
+  *bytes = static_cast<size_t>(n) * kFp8AmaxBlocks * sizeof(float);
+  return TP_OK;
+}
+
+int tp_fp8_quantize_both_multi(int n, const void* const* X, const int64_t* rows,
+                               const int64_t* cols, const int64_t* ld_x, const int* dt,
+                               const int* fmt, void* const* Q, const int64_t* ld_q,
+                               void* const* Qt, const int64_t* ld_qt, float* const* scale_inv,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !rows || !cols || !ld_x || !dt || !fmt || !Q || !ld_q || !Qt || !ld_qt ||
+      !scale_inv)
+    return TP_ERR_NULL;
+  if (n < 1 || n > kFp8MaxMulti) return TP_ERR_SHAPE;
+  if (!workspace || workspace_bytes < static_cast<size_t>(n) * kFp8AmaxBlocks * sizeof(float))
+    return TP_ERR_WORKSPACE;
+  Fp8QuantParams ps[kFp8MaxMulti];
+  for (int i = 0; i < n; ++i) {
+    // tensor i's per-block maxima in its own slice of the workspace
+    void* wi = static_cast<char*>(workspace) + static_cast<size_t>(i) * kFp8AmaxBlocks * sizeof(float);
+    const int st = fp8_both_params(X[i], rows[i], cols[i], ld_x[i], dt[i], fmt[i], Q[i], ld_q[i],
+                                   Qt[i], ld_qt[i], scale_inv[i], wi,
+                                   kFp8AmaxBlocks * sizeof(float), &ps[i]);
+    if (st != TP_OK) return st;
+  }
+  return hip_status(launch_fp8_quantize_multi(ps, n, stream));
 }
 
 int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,

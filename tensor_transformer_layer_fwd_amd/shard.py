@@ -138,7 +138,7 @@ class ShardStep:
                            f"Y{i}": (T, F), f"Yt{i}": (F, T)})
         self.q = {k: torch.empty(*v, **u8) for k, v in shapes.items()}
         self.qs = {k: torch.empty(1, device=self.device) for k in shapes}
-        self.qws = torch.empty(L.tp_fp8_quantize_workspace_size(T, h), **u8)
+        self.qws = torch.empty(L.tp_fp8_quantize_multi_workspace_size(6), **u8)
         return max(L.tp_fp8_linear_bwd_wgrad_workspace_size(T, F, h),
                    L.tp_fp8_linear_bwd_wgrad_workspace_size(T, h, F))
 
@@ -148,17 +148,28 @@ class ShardStep:
                                fmt=fmt)
         self.qs[tname] = self.qs[name]
 
+    def _quant_many(self, items):
+        """_quant2 of each (src, name, tname) in E4M3, six tensors per pair of
+        launches."""
+        for k in range(0, len(items), 6):
+            chunk = items[k:k + 6]
+            L.tp_fp8_quantize_both_multi(
+                [(src, self.q[n], self.q[t], self.qs[n], "e4m3") for src, n, t in chunk], self.qws)
+            for _, n, t in chunk:
+                self.qs[t] = self.qs[n]
+
     def mlp_forward_fp8(self):
         cfg, o, inp, q, qs = self.cfg, self.out, self.inp, self.q, self.qs
         F = cfg.F
-        self._quant2(inp["X"], "X", "Xt")
+        # X and every shard's weights are ready at the start: quantised together
+        self._quant_many([(inp["X"], "X", "Xt")] +
+                         [(self._col("A", i, F), f"A{i}", f"At{i}") for i in cfg.shards] +
+                         [(self._row("B", i, F), f"B{i}", f"Bt{i}") for i in cfg.shards])
         for i in cfg.shards:
             a_i = self._col("a", i, F) if cfg.has_bias else None
-            self._quant2(self._col("A", i, F), f"A{i}", f"At{i}")
             L.tp_fp8_column_linear_fwd(q["X"], q[f"At{i}"], qs["X"], qs[f"At{i}"], a_i,
                                        o[f"Y_{i}"], o[f"U_{i}"])
             self._quant2(o[f"Y_{i}"], f"Y{i}", f"Yt{i}")
-            self._quant2(self._row("B", i, F), f"B{i}", f"Bt{i}")
             L.tp_fp8_row_linear_fwd_partial(q[f"Y{i}"], q[f"Bt{i}"], qs[f"Y{i}"], qs[f"Bt{i}"],
                                             o[f"Zp_{i}"])
         if "Z" in o:

@@ -295,6 +295,34 @@ def test_dgrad_recompute_validation(lib):
     assert call(k=0) == -2
 
 
+def test_fp8_quantize_multi_validation(lib):
+    """The multi-tensor quantiser checks n, its arrays, the workspace and every
+    tensor on the host before any launch."""
+    import ctypes
+    buf = ctypes.create_string_buffer(2 * 4096 + 256)
+    p = (ctypes.addressof(buf) + 255) // 256 * 256
+    ws = ctypes.c_size_t(0)
+    assert lib.tp_fp8_quantize_multi_workspace_size(3, ctypes.byref(ws)) == 0
+    assert ws.value == 3 * 4096
+    assert lib.tp_fp8_quantize_multi_workspace_size(0, ctypes.byref(ws)) == -2
+    assert lib.tp_fp8_quantize_multi_workspace_size(7, ctypes.byref(ws)) == -2
+    assert lib.tp_fp8_quantize_multi_workspace_size(2, None) == -1
+    vp, i64, i32 = ctypes.c_void_p * 2, ctypes.c_int64 * 2, ctypes.c_int * 2
+
+    def call(n=2, Xs=(p, p), ld_x=(8, 8), fmt=(0, 1), ld_qt=(4, 4), wsb=2 * 4096, rows=True):
+        return lib.tp_fp8_quantize_both_multi(
+            n, vp(*Xs), i64(4, 4) if rows else None, i64(8, 8), i64(*ld_x),
+            i32(L.TP_BF16, L.TP_BF16), i32(*fmt), vp(p, p), i64(8, 8), vp(p, p), i64(*ld_qt),
+            vp(p, p), ctypes.c_void_p(p), wsb, None)
+    assert call(n=0) == -2 and call(n=7) == -2
+    assert call(rows=False) == -1
+    assert call(Xs=(p, None)) == -1            # the second tensor's input
+    assert call(ld_x=(8, 7)) == -2
+    assert call(ld_qt=(4, 3)) == -2            # X^T rows are 4 codes
+    assert call(fmt=(0, 2)) == -3
+    assert call(wsb=2 * 4096 - 4) == -5        # 4 KiB of maxima per tensor
+
+
 def test_fp8_validation(lib):
     """The FP8 entry points reject bad arguments on the host, before any launch."""
     import ctypes

@@ -343,3 +343,34 @@ def test_quantize_both_equals_two_calls(dev, fmt, rows, cols):
     q_ref, _, sinv = F.quantize(Xf, FMT[fmt])
     assert np.array_equal(Q.value(), q_ref) and np.array_equal(Qt.value(), q_ref.T)
     assert si.item() == float(sinv)
+
+
+@pytest.mark.parametrize("n", [1, 3, 6])
+def test_quantize_both_multi(dev, n):
+    """Several tensors in two launches: each tensor's codes in both layouts and
+    its scale equal the oracle's, and nothing lands outside any output."""
+    import tensor_transformer_layer_fwd_amd as tp
+    shapes = [(37, 53, "bf16", "e4m3"), (300, 1000, "f32", "e5m2"), (768, 4096, "bf16", "e4m3"),
+              (1, 1, "bf16", "e5m2"), (256, 384, "f32", "e4m3"), (64, 1536, "bf16", "e5m2")][:n]
+    _say(f"fp8 quantize_both_multi n={n}")
+    rng = np.random.default_rng(100 + n)
+    items, refs = [], []
+    for k, (rows, cols, dt, fmt) in enumerate(shapes):
+        scale = 0.5 * (k + 1)   # a different maximum, so a mixed-up scale shows
+        if dt == "bf16":
+            Xf, bits = rand_bf16(rng, (rows, cols), scale)
+            X = to_dev_bf16(bits, dev, pad=8)
+        else:
+            Xf = (rng.standard_normal((rows, cols)) * scale).astype(np.float32).astype(np.float64)
+            X = torch.from_numpy(Xf.astype(np.float32)).to(dev)
+        Q, Qt = Codes(rows, cols, dev, pad=16), Codes(cols, rows, dev, pad=16)
+        si = torch.full((1,), float("nan"), device=dev)
+        items.append((X, Q.view, Qt.view, si, fmt))
+        refs.append((Xf, fmt, Q, Qt, si))
+    ws = torch.empty(tp.tp_fp8_quantize_multi_workspace_size(n), dtype=torch.uint8, device=dev)
+    tp.tp_fp8_quantize_both_multi(items, ws)
+    torch.cuda.synchronize()
+    for Xf, fmt, Q, Qt, si in refs:
+        q_ref, _, sinv = F.quantize(Xf, FMT[fmt])
+        assert np.array_equal(Q.value(), q_ref) and np.array_equal(Qt.value(), q_ref.T)
+        assert si.item() == float(sinv)
