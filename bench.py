@@ -103,10 +103,12 @@ def layer_bwd_calls(step, i=0):
 
 
 def pair_calls(step, i=0):
-    """The layers of shard i whose fused backward is one paired kernel launch
-    (pairing query: paired, weight gradient not split), each timed without
-    its bias gradient, which the step adds as column partials and a short
-    second pass: (name, thunk, gemm flops, (T, k, n, pairing, splitk))."""
+    """The layers of shard i whose fused backward is a paired kernel launch,
+    each called without its bias gradient, which the step adds as column
+    partials and a short second pass: (name, thunk, gemm flops, (T, k, n,
+    pairing, splitk)). With splitk > 1 the call adds a fix-up launch (in the
+    step it rides in the next paired launch), so only splitk == 1 calls time
+    the paired kernel alone."""
     from tensor_transformer_layer_fwd_amd import _lib as L
     cfg, o, inp = step.cfg, step.out, step.inp
     if not (cfg.mlp and step.fused_bwd and cfg.dtype == "bf16"):
@@ -123,7 +125,7 @@ def pair_calls(step, i=0):
              lambda: L.tp_linear_bwd(o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"],
                                      o[f"dA_{i}"], None, act="none", workspace=step.workspace))):
         pr, sk = L.tp_linear_bwd_plan(T, k, n)
-        if pr and sk == 1:
+        if pr:
             out.append((name, fn, f, (T, k, n, pr, sk)))
     return out
 
@@ -339,20 +341,27 @@ def main():
     for name, fn, f in layer_bwd_calls(step):
         ms = time_call(fn, args.kernel_reps)
         layer_bwd[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
-    # dominant kernel: the slowest single-kernel launch the step makes. A layer
-    # whose fused backward is one paired launch contributes that kernel; any
-    # other layer runs its data gradient as a kernel of its own (its weight
-    # gradient call also launches a split-K fix-up and the bias column sums)
+    # dominant kernel: the slowest single-kernel launch the step makes that a
+    # call can time alone. A layer whose fused backward is a paired launch
+    # contributes that kernel when its weight gradient is not split (a split
+    # adds a fix-up launch to the call; in the step the fix-up rides in the
+    # next paired launch). A layer that does not pair runs its data gradient
+    # as a kernel of its own (its weight gradient call also launches a
+    # split-K fix-up and the bias column sums)
     flops_of = {name: f for name, _, f in shard_calls(step)}
     pair_geom = {}
     for name, fn, f, geom in pair_calls(step):
         ms = time_call(fn, args.kernel_reps)
-        kernels[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1)}
+        kernels[name] = {"us": round(ms * 1e3, 2), "tflops": round(f / (ms * 1e-3) / 1e12, 1),
+                         "pairing": geom[3], "splitk": geom[4]}
         flops_of[name], pair_geom[name] = f, geom
     single = ["fc1_fwd", "fc2_fwd"]
     for layer in ("fc2", "fc1"):
-        single.append(f"{layer}_bwd_pair" if f"{layer}_bwd_pair" in pair_geom
-                      else f"{layer}_dgrad")
+        geom = pair_geom.get(f"{layer}_bwd_pair")
+        if geom is None:
+            single.append(f"{layer}_dgrad")
+        elif geom[4] == 1:
+            single.append(f"{layer}_bwd_pair")
     dom = max(single, key=lambda k: kernels[k]["us"])
     dom_flops = flops_of[dom]
     dom_bytes = gemm_call_bytes(cfg, dom)

@@ -117,6 +117,38 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
 
 }  // namespace
 
+namespace {
+
+// Simulated time of one paired launch: the weight gradient on tile w in `sp`
+// K slices, the data gradient on tile d; one block per CU (the pair's stages
+// fill most of the LDS), blocks go to the CU that frees first, the weight
+// gradient's slices first. A split adds its fix-up.
+double pair_cost(const PipeTile* w, const PipeTile* d, int64_t T, int64_t k, int64_t n, int sp) {
+  const double kw = 2.0 * w->bm * w->bn * 64.0 / w->flop_per_sec_per_cu;
+  const double kd = 2.0 * d->bm * d->bn * 64.0 / d->flop_per_sec_per_cu;
+  const int64_t tiles_w = (k / w->bm) * (n / w->bn), tiles_d = (T / d->bm) * (k / d->bn);
+  std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
+  for (int c = 0; c < kCUs; ++c) cu.push(0.0);
+  auto run = [&](int64_t blocks, double sec) {
+    for (int64_t b = 0; b < blocks; ++b) {
+      const double f = cu.top();
+      cu.pop();
+      cu.push(f + kRoundOverheadSec + sec);
+    }
+  };
+  run(tiles_w * sp, static_cast<double>(T / sp / 64) * kw);
+  run(tiles_d, static_cast<double>(n / 64) * kd);
+  double c = 0.0;
+  while (!cu.empty()) {
+    c = cu.top();
+    cu.pop();
+  }
+  if (sp > 1) c += (2.0 * sp + 1.0) * k * n * 4.0 / kHbmBytesPerSec + kLaunchSec;
+  return c;
+}
+
+}  // namespace
+
 SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
   const SplitPlan none{kPairNone, 1, T};
   // the data gradient keeps its own tile; the weight gradient takes 128x128
@@ -134,35 +166,32 @@ SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
   if (T % 64 || k % w->bm || n % w->bn) return none;
   if (g_force_tile != 0 && g_force_split > 1 && T % (64 * g_force_split) == 0)
     return SplitPlan{kind, g_force_split, T / g_force_split};
-  // one block per CU (the pair's stages fill most of the LDS); blocks go to the
-  // CU that frees first, the weight gradient's slices first
-  const double kw = 2.0 * w->bm * w->bn * 64.0 / w->flop_per_sec_per_cu;
-  const double kd = 2.0 * d->bm * d->bn * 64.0 / d->flop_per_sec_per_cu;
-  const int64_t tiles_w = (k / w->bm) * (n / w->bn), tiles_d = (T / d->bm) * (k / d->bn);
+  auto split_ok = [&](int sp) { return sp == 1 || (T % (64 * sp) == 0 && T / sp >= 256); };
   int best = 0;
   double best_c = 1e30;
   for (int sp : {1, 2, 4, 8}) {
-    if (sp > 1 && (T % (64 * sp) || T / sp < 256)) continue;
-    std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-    for (int c = 0; c < kCUs; ++c) cu.push(0.0);
-    auto run = [&](int64_t blocks, double sec) {
-      for (int64_t b = 0; b < blocks; ++b) {
-        const double f = cu.top();
-        cu.pop();
-        cu.push(f + kRoundOverheadSec + sec);
-      }
-    };
-    run(tiles_w * sp, static_cast<double>(T / sp / 64) * kw);
-    run(tiles_d, static_cast<double>(n / 64) * kd);
-    double c = 0.0;
-    while (!cu.empty()) {
-      c = cu.top();
-      cu.pop();
-    }
-    if (sp > 1) c += (2.0 * sp + 1.0) * k * n * 4.0 / kHbmBytesPerSec + kLaunchSec;
+    if (!split_ok(sp)) continue;
+    const double c = pair_cost(w, d, T, k, n, sp);
     if (c < best_c) {
       best_c = c;
       best = sp;
+    }
+  }
+  // Both products on 256x192 as well, where both tile exactly and no tile is
+  // forced: fewer, larger blocks can fit the launch into one round of the
+  // CUs where the 128-row tiles need two (GPT-2 small's fc2 backward: 224
+  // blocks against 328).
+  const PipeTile* big = find_tile(kPipe256x192);
+  if (kind != kPairSame256x192 && g_force_tile == 0 && T % big->bm == 0 && k % big->bn == 0 &&
+      k % big->bm == 0 && n % big->bn == 0) {
+    for (int sp : {1, 2, 4, 8}) {
+      if (!split_ok(sp)) continue;
+      const double c = pair_cost(big, big, T, k, n, sp);
+      if (c < best_c) {
+        best_c = c;
+        best = sp;
+        kind = kPairSame256x192;
+      }
     }
   }
   return SplitPlan{kind, best, T / best};
