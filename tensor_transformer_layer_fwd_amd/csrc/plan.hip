@@ -169,30 +169,38 @@ SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
   auto split_ok = [&](int sp) { return sp == 1 || (T % (64 * sp) == 0 && T / sp >= 256); };
   int best = 0;
   double best_c = 1e30;
-  for (int sp : {1, 2, 4, 8}) {
-    if (!split_ok(sp)) continue;
-    const double c = pair_cost(w, d, T, k, n, sp);
-    if (c < best_c) {
-      best_c = c;
-      best = sp;
-    }
-  }
-  // Both products on 256x192 as well, where both tile exactly and no tile is
-  // forced: fewer, larger blocks can fit the launch into one round of the
-  // CUs where the 128-row tiles need two (GPT-2 small's fc2 backward: 224
-  // blocks against 328).
-  const PipeTile* big = find_tile(kPipe256x192);
-  if (kind != kPairSame256x192 && g_force_tile == 0 && T % big->bm == 0 && k % big->bn == 0 &&
-      k % big->bm == 0 && n % big->bn == 0) {
+  int64_t best_blocks = 0;
+  // a candidate wins on lower simulated time, or on equal time with fewer
+  // blocks (the model's ties come from a long weight gradient hiding the data
+  // gradient's rounds, which fewer blocks still shorten)
+  auto consider = [&](const PipeTile* tw_, const PipeTile* td_, int kind_) {
     for (int sp : {1, 2, 4, 8}) {
       if (!split_ok(sp)) continue;
-      const double c = pair_cost(big, big, T, k, n, sp);
-      if (c < best_c) {
+      const double c = pair_cost(tw_, td_, T, k, n, sp);
+      const int64_t blocks = (k / tw_->bm) * (n / tw_->bn) * sp + (T / td_->bm) * (k / td_->bn);
+      if (c < best_c - 1e-9 || (c < best_c + 1e-9 && blocks < best_blocks)) {
         best_c = c;
         best = sp;
-        kind = kPairSame256x192;
+        best_blocks = blocks;
+        kind = kind_;
       }
     }
+  };
+  consider(w, d, kind);
+  if (g_force_tile == 0) {
+    // Both products on 256x192 as well, where both tile exactly: fewer,
+    // larger blocks can fit the launch into one round of the CUs where the
+    // 128-row tiles need two (GPT-2 small's fc2 backward: 224 blocks
+    // against 328).
+    const PipeTile* big = find_tile(kPipe256x192);
+    if (kind != kPairSame256x192 && T % big->bm == 0 && k % big->bn == 0 && k % big->bm == 0 &&
+        n % big->bn == 0)
+      consider(big, big, kPairSame256x192);
+    // A 128x128 data gradient also as 128x192 where k allows (GPT-2 small's
+    // fc1 backward: 200 blocks against 264).
+    const PipeTile* wide = find_tile(kPipe128x192);
+    if (pd.tile == kPipe128x128 && k % wide->bn == 0)
+      consider(w, wide, kPairW128x128D128x192);
   }
   return SplitPlan{kind, best, T / best};
 }
