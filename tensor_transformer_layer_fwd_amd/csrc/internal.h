@@ -221,6 +221,8 @@ enum PairKind : int {
 // cannot pair), plan.splitk / k_chunk the weight gradient's K slices. Shapes
 // only, so the workspace query and the call agree.
 SplitPlan plan_pair(int64_t T, int64_t k, int64_t n);
+// CUs a paired launch of plan `pl` leaves without a tile in its first round.
+int pair_free_cus(const SplitPlan& pl, int64_t T, int64_t k, int64_t n);
 hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int kind, int ekd,
                                 const PairRider& rider, hipStream_t s);
 bool splitk_fixup_vec_ok(const GemmParams& p);

@@ -205,6 +205,17 @@ SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
   return SplitPlan{kind, best, T / best};
 }
 
+int pair_free_cus(const SplitPlan& pl, int64_t T, int64_t k, int64_t n) {
+  TileId tw = kPipe128x128, td = kPipe128x128;
+  if (pl.tile == kPairW128x128D128x192) td = kPipe128x192;
+  else if (pl.tile == kPairSame256x192) tw = td = kPipe256x192;
+  else if (pl.tile != kPairSame128x128) return 0;
+  const PipeTile* w = find_tile(tw);
+  const PipeTile* d = find_tile(td);
+  const int64_t blocks = (k / w->bm) * (n / w->bn) * pl.splitk + (T / d->bm) * (k / d->bn);
+  return blocks < kCUs ? static_cast<int>(kCUs - blocks) : 0;
+}
+
 namespace {
 const TileId kF8Tiles[] = {kPipe256x192, kPipe128x256, kPipe128x192, kPipe128x128};
 }  // namespace

@@ -257,7 +257,12 @@ PairSetup setup_pair(const void* dOut, const void* W, const void* U, int act, co
     q.pw.cs = c;
     q.pw.cs_nchunks = static_cast<int>(nchunks);
     q.pw.cs_units = static_cast<int>(units);
-    q.pw.cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
+    // on the CUs the tiles leave free in the first round, where there are at
+    // least 16, so the column sums do not push tiles into a second round
+    int64_t blocks = units < kColsumBlocks ? units : kColsumBlocks;
+    const int free_cus = pair_free_cus(q.plan, T, k, n);
+    if (free_cus >= 16 && free_cus < blocks) blocks = free_cus;
+    q.pw.cs_blocks = static_cast<int>(blocks);
     q.carry = true;
   }
   return q;
