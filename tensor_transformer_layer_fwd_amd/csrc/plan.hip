@@ -149,6 +149,33 @@ double pair_cost(const PipeTile* w, const PipeTile* d, int64_t T, int64_t k, int
 
 }  // namespace
 
+// A data gradient whose own tile has no paired kernel (128x256, 256x128,
+// 256x256): pair both products on 128x128 where they tile exactly and the
+// model puts the pair below the two calls (data gradient on its own tile,
+// weight gradient with its own plan, one more launch).
+SplitPlan plan_pair_other_tile(int64_t T, int64_t k, int64_t n, const SplitPlan& pd) {
+  const SplitPlan none{kPairNone, 1, T};
+  const PipeTile* t = find_tile(kPipe128x128);
+  if (g_force_tile != 0 || pd.tile == 0 || T % t->bm || k % t->bn || n % t->bn) return none;
+  const SplitPlan pw = plan_gemm_bf16(k, n, T, true);
+  const PipeTile* td = find_tile(pd.tile);
+  const PipeTile* tw = find_tile(pw.tile);
+  if (!td || !tw) return none;
+  const double two_calls = cost(T, k, n, *td, 1) + cost(k, n, T, *tw, pw.splitk) + kLaunchSec;
+  int best = 0;
+  double best_c = 1e30;
+  for (int sp : {1, 2, 4, 8}) {
+    if (sp > 1 && (T % (64 * sp) || T / sp < 256)) continue;
+    const double c = pair_cost(t, t, T, k, n, sp);
+    if (c < best_c) {
+      best_c = c;
+      best = sp;
+    }
+  }
+  if (best == 0 || best_c >= two_calls) return none;
+  return SplitPlan{kPairSame128x128, best, T / best};
+}
+
 SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
   const SplitPlan none{kPairNone, 1, T};
   // the data gradient keeps its own tile; the weight gradient takes 128x128
@@ -160,7 +187,7 @@ SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
   if (pd.tile == kPipe128x192) kind = kPairW128x128D128x192;
   else if (pd.tile == kPipe128x128) kind = kPairSame128x128;
   else if (pd.tile == kPipe256x192) kind = kPairSame256x192, tw = kPipe256x192;
-  if (kind == kPairNone) return none;
+  if (kind == kPairNone) return plan_pair_other_tile(T, k, n, pd);
   const PipeTile* w = find_tile(tw);
   const PipeTile* d = find_tile(pd.tile);
   if (T % 64 || k % w->bm || n % w->bn) return none;
