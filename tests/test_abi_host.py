@@ -155,6 +155,12 @@ def test_linear_bwd_plan(lib):
     assert L.tp_linear_bwd_plan(4096, 1536, 768) == (3, 4)
     assert L.tp_linear_bwd_plan(2048, 12288, 6144)[0] == 3
     assert L.tp_linear_bwd_plan(2048, 6144, 12288)[0] == 3
+    # the ~350M shard (T=6144, h=F=1024, QKV width 768): the data gradient's
+    # own 128x256 tile has no paired kernel, and both on 128x128 in 2 slices
+    # beats the two calls
+    assert L.tp_gemm_plan(6144, 1024, 1024)[0] == 12
+    assert L.tp_linear_bwd_plan(6144, 1024, 1024) == (1, 2)
+    assert L.tp_linear_bwd_plan(6144, 1024, 768) == (1, 2)
     # no pipelined tile fits a ragged layer
     assert L.tp_linear_bwd_plan(300, 129, 200) == (0, 1)
     assert L.tp_linear_bwd_plan(4096, 768, 1000) == (0, 1)
