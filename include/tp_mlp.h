@@ -41,7 +41,12 @@
  *     aligned pointers with ld a multiple of 8 take the vector-load path.
  *   - Results are deterministic: the same call on the same inputs gives the same
  *     bits (fixed summation orders, no floating-point atomics).
- *   - Calls are reentrant and hold no state beyond the loaded code object.
+ *   - Calls are reentrant. The library's only mutable state is per thread:
+ *     the last HIP error (tp_last_hip_error) and the tile override of
+ *     tp_set_gemm_override (a tuning and test hook), plus a per-device cache
+ *     of the device's CU and XCD counts, filled on first use. Tile and split
+ *     choices depend on the shapes and on those counts, so a workspace query
+ *     and the call it sizes agree when made on the same device and thread.
  */
 #ifndef TP_MLP_H
 #define TP_MLP_H
@@ -91,7 +96,7 @@ typedef enum { TP_FP8_E4M3 = 0, TP_FP8_E5M2 = 1 } tp_fp8_format;
  */
 int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, void* Y_i,
                          void* U_i, int64_t T, int64_t h, int64_t n, int64_t ld_x,
-                         int64_t ld_a, int64_t ld_y, int dt, int act, hipStream_t stream);
+                         int64_t ld_a, int64_t ld_y, tp_dtype dt, tp_act act, hipStream_t stream);
 
 /*
  * Row-parallel forward partial of shard i ("Megatron" page, "Tensor
@@ -108,7 +113,7 @@ int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, voi
  */
 int tp_row_linear_fwd_partial(const void* Y_i, const void* B_i, float* Zp_i, int64_t T,
                               int64_t k, int64_t h, int64_t ld_y, int64_t ld_b,
-                              int64_t ld_z, int dt, hipStream_t stream);
+                              int64_t ld_z, tp_dtype dt, hipStream_t stream);
 
 /*
  * Input gradient (dgrad) of Out = act(In W) for a weight stored [k, n]
@@ -126,9 +131,9 @@ int tp_row_linear_fwd_partial(const void* Y_i, const void* B_i, float* Zp_i, int
  * U    [T, k], ld_u, dtype dt (required when act != NONE)
  * dIn  [T, k], ld_din, dtype out_dt (TP_F32, or dt)
  */
-int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act, void* dIn,
+int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, tp_act act, void* dIn,
                         int64_t T, int64_t k, int64_t n, int64_t ld_dout, int64_t ld_w,
-                        int64_t ld_u, int64_t ld_din, int dt, int out_dt,
+                        int64_t ld_u, int64_t ld_din, tp_dtype dt, tp_dtype out_dt,
                         hipStream_t stream);
 
 /*
@@ -149,10 +154,10 @@ int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act,
  * values: TP_ERR_ACT) and out_dt = dt
  * Y    [T, k], ld_y, dtype dt; must not overlap U or dIn
  */
-int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U, int act,
+int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U, tp_act act,
                                   void* dIn, void* Y, int64_t T, int64_t k, int64_t n,
                                   int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_din,
-                                  int64_t ld_y, int dt, hipStream_t stream);
+                                  int64_t ld_y, tp_dtype dt, hipStream_t stream);
 
 /*
  * Weight and bias gradients (wgrad) of Out = In W + c for a weight stored
@@ -174,11 +179,11 @@ int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U
  */
 int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbias, int64_t T,
                         int64_t k, int64_t n, int64_t ld_in, int64_t ld_dout, int64_t ld_dw,
-                        int accumulate, int dt, void* workspace, size_t workspace_bytes,
+                        int accumulate, tp_dtype dt, void* workspace, size_t workspace_bytes,
                         hipStream_t stream);
 
 /* Scratch bytes tp_linear_bwd_wgrad needs for (T, k, n, dt); pure host function. */
-int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
+int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, tp_dtype dt,
                                        size_t* bytes);
 
 /*
@@ -206,14 +211,14 @@ int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
  * entry ignored; not shared by calls that may run at the same time. Errors as
  * the two calls; every check of both runs before the first launch.
  */
-int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const void* In,
+int tp_linear_bwd(const void* dOut, const void* W, const void* U, tp_act act, const void* In,
                   void* dIn, float* dW, float* dbias, int64_t T, int64_t k, int64_t n,
                   int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_in, int64_t ld_din,
-                  int64_t ld_dw, int accumulate, int dt, int out_dt, void* workspace,
+                  int64_t ld_dw, int accumulate, tp_dtype dt, tp_dtype out_dt, void* workspace,
                   size_t workspace_bytes, hipStream_t stream);
 
 /* Scratch bytes tp_linear_bwd needs for (T, k, n, dt); pure host function. */
-int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t* bytes);
+int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, tp_dtype dt, size_t* bytes);
 
 /*
  * How tp_linear_bwd runs a bf16 layer of this shape (pure host function, for
@@ -263,11 +268,11 @@ int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, 
                const void* Y_i, void* dU_i, float* dB_i, float* db, float* dXp_i, float* dA_i,
                float* da_i, int64_t T, int64_t h, int64_t F, int64_t ld_dz, int64_t ld_x,
                int64_t ld_a, int64_t ld_b, int64_t ld_u, int64_t ld_y, int64_t ld_du,
-               int64_t ld_dxp, int64_t ld_db, int64_t ld_da, int accumulate, int dt,
+               int64_t ld_dxp, int64_t ld_db, int64_t ld_da, int accumulate, tp_dtype dt,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Scratch bytes tp_mlp_bwd needs for (T, h, F, dt); pure host function. */
-int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, int dt, size_t* bytes);
+int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, tp_dtype dt, size_t* bytes);
 
 /*
  * Sum over shards, the one-GPU stand-in for the All-Reduce ("Megatron" page,
@@ -287,7 +292,7 @@ int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, int dt, size_t* b
  *           out_dt == TP_F32 and ld_out == ld_p
  */
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
-                       int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, int out_dt,
+                       int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, tp_dtype out_dt,
                        hipStream_t stream);
 
 /*
@@ -302,7 +307,7 @@ int tp_reduce_partials(const float* const* partials, int p, const void* bias, vo
  * act  TP_ACT_GELU_TANH or TP_ACT_NONE (then Y = U + bias)
  */
 int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, int64_t ld_u,
-                int64_t ld_y, int in_dt, int out_dt, int act, hipStream_t stream);
+                int64_t ld_y, tp_dtype in_dt, tp_dtype out_dt, tp_act act, hipStream_t stream);
 
 /*
  * Attention core of one shard, forward. The "Megatron" page ("Transformer-
@@ -327,7 +332,7 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
  */
 int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
                      int64_t heads, int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int causal,
-                     int dt, hipStream_t stream);
+                     tp_dtype dt, hipStream_t stream);
 
 /*
  * Attention core of one shard, backward: the gradient of the forward above
@@ -355,7 +360,7 @@ int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_
 int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float* lse,
                      float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
                      int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
-                     int64_t ld_dqkv, int causal, int dt, hipStream_t stream);
+                     int64_t ld_dqkv, int causal, tp_dtype dt, hipStream_t stream);
 
 /*
  * FP8 variant of the shard GEMMs. The "Megatron" page ("mixed-precision
@@ -387,7 +392,7 @@ int tp_fp8_quantize_workspace_size(int64_t rows, int64_t cols, size_t* bytes);
  * of X^T ([cols, rows], ld_q >= rows). The maximum is order-independent, so
  * the result is reproducible. X must hold finite values. Two launches.
  */
-int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt, int fmt,
+int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, tp_dtype dt, tp_fp8_format fmt,
                     int transpose, void* Q, int64_t ld_q, float* scale_inv, void* workspace,
                     size_t workspace_bytes, hipStream_t stream);
 
@@ -397,8 +402,8 @@ int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int
  * of X (two launches in all). The codes equal those of two tp_fp8_quantize
  * calls.
  */
-int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt,
-                         int fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
+int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x, tp_dtype dt,
+                         tp_fp8_format fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
                          float* scale_inv, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
@@ -433,7 +438,7 @@ int tp_fp8_quantize_multi_workspace_size(int n, size_t* bytes);
 int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
                              const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
                              int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
-                             int64_t ld_y, int act, hipStream_t stream);
+                             int64_t ld_y, tp_act act, hipStream_t stream);
 
 /*
  * FP8 row-parallel forward partial: Zp_i = Y_i B_i (fp32 [T, h]) from
@@ -451,9 +456,9 @@ int tp_fp8_row_linear_fwd_partial(const void* Yq, const void* Btq, const float* 
  * out_dt TP_BF16; act NONE writes dIn in out_dt (TP_F32 for a dX partial).
  */
 int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
-                            const float* w_scale_inv, int dout_fmt, const void* U, int act,
+                            const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U, tp_act act,
                             void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
-                            int64_t ld_w, int64_t ld_u, int64_t ld_din, int out_dt,
+                            int64_t ld_w, int64_t ld_u, int64_t ld_din, tp_dtype out_dt,
                             hipStream_t stream);
 
 /* Workspace bytes of tp_fp8_linear_bwd_wgrad (split-K partials and bias sums). */
@@ -467,7 +472,7 @@ int tp_fp8_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, size
  * of the unquantised dOut (bf16 [T, n], ld_dout), as tp_linear_bwd_wgrad.
  */
 int tp_fp8_linear_bwd_wgrad(const void* Intq, const void* dOuttq, const float* in_scale_inv,
-                            const float* dout_scale_inv, int dout_fmt, float* dW,
+                            const float* dout_scale_inv, tp_fp8_format dout_fmt, float* dW,
                             const void* dOut, float* dbias, int64_t T, int64_t k, int64_t n,
                             int64_t ld_int, int64_t ld_doutt, int64_t ld_dw, int64_t ld_dout,
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -490,9 +495,10 @@ int tp_gemm_plan(int64_t M, int64_t N, int64_t K, int allow_split, int* tile, in
  * tile `tile` (10..15, as for tp_gemm_plan) supports uses that tile, and a
  * weight-gradient product (the only kind that may split K) uses `splitk` K
  * slices when K is a multiple of 64 * splitk. tile = 0 restores the library's
- * own choice. Process-wide, and not synchronised with calls running on other
- * threads: set it only while no other thread calls the library. Returns
- * TP_ERR_SHAPE for an unknown tile id or a splitk outside 1..16.
+ * own choice. The override belongs to the calling thread: it changes the plans
+ * (and so the workspace queries) of calls made by that thread only, and other
+ * threads keep the library's choice. Returns TP_ERR_SHAPE for an unknown tile
+ * id or a splitk outside 1..16.
  */
 int tp_set_gemm_override(int tile, int splitk);
 

@@ -162,9 +162,87 @@ def _act(act) -> int:
     raise ValueError(f"unknown activation {act!r}")
 
 
+def _torch_dtypes(*names):
+    import torch
+    m = {"bf16": torch.bfloat16, "f32": torch.float32, "u8": torch.uint8}
+    return tuple(m[n] for n in names)
+
+
+class _Operands:
+    """The checks every wrapper runs on its operands before the library sees a
+    pointer: the C interface cannot see buffer sizes, so a tensor of the wrong
+    shape, dtype or layout would make the kernels read or write out of bounds.
+    Shapes and dtypes are checked first (ValueError / TypeError), then that
+    every operand is a GPU tensor on one device, the device of the stream."""
+
+    def __init__(self, fn: str):
+        self.fn = fn
+        self.seen = []
+
+    def __call__(self, name, t, shape, dtypes, optional=False):
+        import torch
+        if t is None:
+            if optional:
+                return self
+            raise ValueError(f"{self.fn}: {name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{self.fn}: {name} must be a torch.Tensor, not {type(t).__name__}")
+        if tuple(t.shape) != tuple(int(d) for d in shape):
+            raise ValueError(f"{self.fn}: {name} has shape {tuple(t.shape)}, "
+                             f"expected {tuple(int(d) for d in shape)}")
+        if dtypes is not None and t.dtype not in dtypes:
+            raise TypeError(f"{self.fn}: {name} has dtype {t.dtype}, expected one of "
+                            f"{[str(d) for d in dtypes]}")
+        if t.dim() == 2:
+            if t.stride(1) != 1 and t.shape[1] > 1:
+                raise ValueError(f"{self.fn}: {name} needs unit stride along its rows")
+        elif t.dim() == 1:
+            if t.stride(0) != 1 and t.shape[0] > 1:
+                raise ValueError(f"{self.fn}: {name} must be contiguous")
+        self.seen.append((name, t))
+        return self
+
+    def done(self, stream=None):
+        import torch
+        devs = set()
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{self.fn}: {name} is on {t.device}; every operand must be a "
+                                 "GPU tensor")
+            devs.add(t.device)
+        if len(devs) > 1:
+            raise ValueError(f"{self.fn}: operands on more than one device: {sorted(map(str, devs))}")
+        if devs:
+            (dev,) = devs
+            sdev = (torch.cuda.current_stream() if stream is None else stream).device
+            if sdev != dev:
+                raise ValueError(f"{self.fn}: operands on {dev}, stream on {sdev}")
+
+
+def _ws_bytes(workspace) -> int:
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def _check_ws(chk, workspace):
+    """A workspace is any contiguous GPU tensor; the library checks its size."""
+    if workspace is not None:
+        chk("workspace", workspace, (workspace.numel(),) if workspace.dim() == 1 else workspace.shape,
+            None)
+        if not workspace.is_contiguous():
+            raise ValueError(f"{chk.fn}: workspace must be contiguous")
+
+
 def tp_column_linear_fwd(X, A_i, bias_i, Y_i, U_i=None, act="gelu", stream=None):
+    chk = _Operands("tp_column_linear_fwd")
+    chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
     T, h = X.shape
+    dts = (X.dtype,)
+    chk("A_i", A_i, (h, _shape2(A_i)[1]), dts)
     n = A_i.shape[1]
+    chk("bias_i", bias_i, (n,), dts, optional=True)
+    chk("Y_i", Y_i, (T, n), dts)
+    chk("U_i", U_i, (T, n), dts, optional=_act(act) == TP_ACT_NONE)
+    chk.done(stream)
     if U_i is not None and _ld(U_i) != _ld(Y_i):
         raise ValueError("U_i and Y_i must share a row stride")
     _check("tp_column_linear_fwd", lib().tp_column_linear_fwd(
@@ -172,17 +250,37 @@ def tp_column_linear_fwd(X, A_i, bias_i, Y_i, U_i=None, act="gelu", stream=None)
         _ld(Y_i), _dt(X), _act(act), _stream(stream)))
 
 
+def _shape2(t):
+    """(rows, cols) of a 2-D tensor, or (-1, -1) so that the shape check fails."""
+    return tuple(t.shape) if t is not None and hasattr(t, "dim") and t.dim() == 2 else (-1, -1)
+
+
 def tp_row_linear_fwd_partial(Y_i, B_i, Zp_i, stream=None):
+    chk = _Operands("tp_row_linear_fwd_partial")
+    chk("Y_i", Y_i, _shape2(Y_i), _torch_dtypes("bf16", "f32"))
     T, k = Y_i.shape
+    chk("B_i", B_i, (k, _shape2(B_i)[1]), (Y_i.dtype,))
     h = B_i.shape[1]
+    chk("Zp_i", Zp_i, (T, h), _torch_dtypes("f32")).done(stream)
     _check("tp_row_linear_fwd_partial", lib().tp_row_linear_fwd_partial(
         _ptr(Y_i), _ptr(B_i), _ptr(Zp_i), T, k, h, _ld(Y_i), _ld(B_i), _ld(Zp_i), _dt(Y_i),
         _stream(stream)))
 
 
+def _out_dtypes(dt):
+    """Output dtypes a product of operand dtype dt may write: its own, or fp32."""
+    import torch
+    return (dt, torch.float32)
+
+
 def tp_linear_bwd_dgrad(dOut, W, U, dIn, act="none", stream=None):
+    chk = _Operands("tp_linear_bwd_dgrad")
+    chk("dOut", dOut, _shape2(dOut), _torch_dtypes("bf16", "f32"))
     T, n = dOut.shape
+    chk("W", W, (_shape2(W)[0], n), (dOut.dtype,))
     k = W.shape[0]
+    chk("U", U, (T, k), (dOut.dtype,), optional=_act(act) == TP_ACT_NONE)
+    chk("dIn", dIn, (T, k), _out_dtypes(dOut.dtype)).done(stream)
     ld_u = _ld(U) if U is not None else k
     _check("tp_linear_bwd_dgrad", lib().tp_linear_bwd_dgrad(
         _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(dIn), T, k, n, _ld(dOut), _ld(W), ld_u,
@@ -191,8 +289,13 @@ def tp_linear_bwd_dgrad(dOut, W, U, dIn, act="none", stream=None):
 
 def tp_linear_bwd_dgrad_recompute(dOut, W, U, dIn, Y, act="gelu", stream=None):
     """dIn = (dOut W^T) * act'(U) and Y = act(U) recomputed from the saved U."""
+    chk = _Operands("tp_linear_bwd_dgrad_recompute")
+    chk("dOut", dOut, _shape2(dOut), _torch_dtypes("bf16", "f32"))
     T, n = dOut.shape
+    dts = (dOut.dtype,)
+    chk("W", W, (_shape2(W)[0], n), dts)
     k = W.shape[0]
+    chk("U", U, (T, k), dts)("dIn", dIn, (T, k), dts)("Y", Y, (T, k), dts).done(stream)
     _check("tp_linear_bwd_dgrad_recompute", lib().tp_linear_bwd_dgrad_recompute(
         _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(dIn), _ptr(Y), T, k, n, _ld(dOut), _ld(W),
         _ld(U), _ld(dIn), _ld(Y), _dt(dOut), _stream(stream)))
@@ -207,12 +310,18 @@ def tp_linear_bwd_wgrad_workspace_size(T: int, k: int, n: int, dt: int) -> int:
 
 def tp_linear_bwd_wgrad(In, dOut, dW, dbias=None, accumulate=False, workspace=None,
                         stream=None):
+    chk = _Operands("tp_linear_bwd_wgrad")
+    chk("In", In, _shape2(In), _torch_dtypes("bf16", "f32"))
     T, k = In.shape
+    chk("dOut", dOut, (T, _shape2(dOut)[1]), (In.dtype,))
     n = dOut.shape[1]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    f32 = _torch_dtypes("f32")
+    chk("dW", dW, (k, n), f32)("dbias", dbias, (n,), f32, optional=True)
+    _check_ws(chk, workspace)
+    chk.done(stream)
     _check("tp_linear_bwd_wgrad", lib().tp_linear_bwd_wgrad(
         _ptr(In), _ptr(dOut), _ptr(dW), _ptr(dbias), T, k, n, _ld(In), _ld(dOut), _ld(dW),
-        int(bool(accumulate)), _dt(In), _ptr(workspace), ws_bytes, _stream(stream)))
+        int(bool(accumulate)), _dt(In), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_linear_bwd_workspace_size(T: int, k: int, n: int, dt: int) -> int:
@@ -235,14 +344,23 @@ def tp_linear_bwd(dOut, W, U, In, dIn, dW, dbias=None, act="none", accumulate=Fa
                   workspace=None, stream=None):
     """Both gradients of one linear layer: dIn = (dOut W^T) [* act'(U)] and
     dW (+)= In^T dOut, dbias (+)= column sums of dOut."""
+    chk = _Operands("tp_linear_bwd")
+    chk("dOut", dOut, _shape2(dOut), _torch_dtypes("bf16", "f32"))
     T, n = dOut.shape
+    dts = (dOut.dtype,)
+    chk("W", W, (_shape2(W)[0], n), dts)
     k = W.shape[0]
+    f32 = _torch_dtypes("f32")
+    chk("U", U, (T, k), dts, optional=_act(act) == TP_ACT_NONE)
+    chk("In", In, (T, k), dts)("dIn", dIn, (T, k), _out_dtypes(dOut.dtype))
+    chk("dW", dW, (k, n), f32)("dbias", dbias, (n,), f32, optional=True)
+    _check_ws(chk, workspace)
+    chk.done(stream)
     ld_u = _ld(U) if U is not None else k
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("tp_linear_bwd", lib().tp_linear_bwd(
         _ptr(dOut), _ptr(W), _ptr(U), _act(act), _ptr(In), _ptr(dIn), _ptr(dW), _ptr(dbias),
         T, k, n, _ld(dOut), _ld(W), ld_u, _ld(In), _ld(dIn), _ld(dW), int(bool(accumulate)),
-        _dt(dOut), _dt(dIn), _ptr(workspace), ws_bytes, _stream(stream)))
+        _dt(dOut), _dt(dIn), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_mlp_bwd_workspace_size(T: int, h: int, F: int, dt: int) -> int:
@@ -256,30 +374,50 @@ def tp_mlp_bwd(dZ, X, A_i, B_i, U_i, Y_i, dU_i, dB_i, db, dXp_i, dA_i, da_i, acc
                workspace=None, stream=None):
     """The backward of one shard's MLP block: fc2's gradients with the GeLU
     derivative, then fc1's, dXp_i the shard's fp32 dX partial."""
+    chk = _Operands("tp_mlp_bwd")
+    chk("dZ", dZ, _shape2(dZ), _torch_dtypes("bf16", "f32"))
     T, h = dZ.shape
+    dts, f32 = (dZ.dtype,), _torch_dtypes("f32")
+    chk("B_i", B_i, (_shape2(B_i)[0], h), dts)
     F = B_i.shape[0]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk("X", X, (T, h), dts)("A_i", A_i, (h, F), dts)("U_i", U_i, (T, F), dts)
+    chk("Y_i", Y_i, (T, F), dts)("dU_i", dU_i, (T, F), dts)("dB_i", dB_i, (F, h), f32)
+    chk("db", db, (h,), f32, optional=True)("dXp_i", dXp_i, (T, h), f32)
+    chk("dA_i", dA_i, (h, F), f32)("da_i", da_i, (F,), f32, optional=True)
+    _check_ws(chk, workspace)
+    chk.done(stream)
     _check("tp_mlp_bwd", lib().tp_mlp_bwd(
         _ptr(dZ), _ptr(X), _ptr(A_i), _ptr(B_i), _ptr(U_i), _ptr(Y_i), _ptr(dU_i), _ptr(dB_i),
         _ptr(db), _ptr(dXp_i), _ptr(dA_i), _ptr(da_i), T, h, F, _ld(dZ), _ld(X), _ld(A_i),
         _ld(B_i), _ld(U_i), _ld(Y_i), _ld(dU_i), _ld(dXp_i), _ld(dB_i), _ld(dA_i),
-        int(bool(accumulate)), _dt(dZ), _ptr(workspace), ws_bytes, _stream(stream)))
+        int(bool(accumulate)), _dt(dZ), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_reduce_partials(partials, bias, out, stream=None):
+    chk = _Operands("tp_reduce_partials")
+    if not partials:
+        raise ValueError("tp_reduce_partials: no partials")
     p = len(partials)
+    chk("partials[0]", partials[0], _shape2(partials[0]), _torch_dtypes("f32"))
     T, h = partials[0].shape
     ld_p = _ld(partials[0])
-    for P in partials:
-        if tuple(P.shape) != (T, h) or _ld(P) != ld_p:
+    for i, P in enumerate(partials[1:], 1):
+        chk(f"partials[{i}]", P, (T, h), _torch_dtypes("f32"))
+        if _ld(P) != ld_p:
             raise ValueError("partials must share shape and row stride")
+    chk("out", out, (T, h), _torch_dtypes("bf16", "f32"))
+    chk("bias", bias, (h,), (out.dtype,), optional=True).done(stream)
     arr = (ctypes.c_void_p * p)(*[P.data_ptr() for P in partials])
     _check("tp_reduce_partials", lib().tp_reduce_partials(
         arr, p, _ptr(bias), _ptr(out), T, h, ld_p, _ld(out), _dt(out), _stream(stream)))
 
 
 def tp_bias_act(U, bias, Y, act="gelu", stream=None):
+    chk = _Operands("tp_bias_act")
+    chk("U", U, _shape2(U), _torch_dtypes("bf16", "f32"))
     T, n = U.shape
+    chk("bias", bias, (n,), (U.dtype,), optional=True)
+    chk("Y", Y, (T, n), _torch_dtypes("bf16", "f32")).done(stream)
     _check("tp_bias_act", lib().tp_bias_act(
         _ptr(U), _ptr(bias), _ptr(Y), T, n, _ld(U), _ld(Y), _dt(U), _dt(Y), _act(act),
         _stream(stream)))
@@ -297,6 +435,15 @@ def tp_attention_fwd(QKV, C, lse, batch: int, seq: int, heads: int, causal: bool
                      stream=None):
     """Attention core of one shard: QKV [batch*seq, 3*heads*64] bf16 -> C
     [batch*seq, heads*64] bf16 and lse [batch, heads, seq] fp32 (or None)."""
+    chk = _Operands("tp_attention_fwd")
+    T, hd, bf = batch * seq, heads * 64, _torch_dtypes("bf16")
+    chk("QKV", QKV, (T, 3 * hd), bf)("C", C, (T, hd), bf)
+    if lse is not None:
+        chk("lse", lse, (batch * heads * seq,) if lse.dim() == 1 else (batch, heads, seq),
+            _torch_dtypes("f32"))
+        if not lse.is_contiguous():
+            raise ValueError("tp_attention_fwd: lse must be contiguous")
+    chk.done(stream)
     _check("tp_attention_fwd", lib().tp_attention_fwd(
         _ptr(QKV), _ptr(C), _ptr(lse), batch, seq, heads, 64, _ld(QKV), _ld(C), int(bool(causal)),
         _dt(QKV), _stream(stream)))
@@ -306,6 +453,16 @@ def tp_attention_bwd(QKV, C, dC, lse, delta, dQKV, batch: int, seq: int, heads: 
                      causal: bool = True, stream=None):
     """Backward of tp_attention_fwd: dQKV (laid out like QKV) from dC, the
     forward's C and lse; delta [batch, heads, seq] fp32 is a workspace."""
+    chk = _Operands("tp_attention_bwd")
+    T, hd, bf, f32 = batch * seq, heads * 64, _torch_dtypes("bf16"), _torch_dtypes("f32")
+    chk("QKV", QKV, (T, 3 * hd), bf)("C", C, (T, hd), bf)("dC", dC, (T, hd), bf)
+    chk("dQKV", dQKV, (T, 3 * hd), bf)
+    for name, t in (("lse", lse), ("delta", delta)):
+        chk(name, t, (batch * heads * seq,) if t is not None and t.dim() == 1
+            else (batch, heads, seq), f32)
+        if not t.is_contiguous():
+            raise ValueError(f"tp_attention_bwd: {name} must be contiguous")
+    chk.done(stream)
     _check("tp_attention_bwd", lib().tp_attention_bwd(
         _ptr(QKV), _ptr(C), _ptr(dC), _ptr(lse), _ptr(delta), _ptr(dQKV), batch, seq, heads, 64,
         _ld(QKV), _ld(C), _ld(dC), _ld(dQKV), int(bool(causal)), _dt(QKV), _stream(stream)))
@@ -327,20 +484,35 @@ def tp_fp8_quantize_workspace_size(rows: int, cols: int) -> int:
 
 def tp_fp8_quantize(X, Q, scale_inv, workspace, fmt="e4m3", transpose=False, stream=None):
     """Codes of X (or X^T) into the uint8 tensor Q; scale_inv (fp32 [1]) = 1/s."""
+    chk = _Operands("tp_fp8_quantize")
+    chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
     rows, cols = X.shape
+    chk("Q", Q, (cols, rows) if transpose else (rows, cols), _torch_dtypes("u8"))
+    chk("scale_inv", scale_inv, (1,), _torch_dtypes("f32"))
+    if workspace is None:
+        raise ValueError("tp_fp8_quantize: workspace is required")
+    _check_ws(chk, workspace)
+    chk.done(stream)
     _check("tp_fp8_quantize", lib().tp_fp8_quantize(
         _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), int(bool(transpose)), _ptr(Q), _ld(Q),
-        _ptr(scale_inv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _ptr(scale_inv), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_fp8_quantize_both(X, Q, Qt, scale_inv, workspace, fmt="e4m3", stream=None):
     """Codes of X into Q and of X^T into Qt from one read; scale_inv = 1/s."""
+    chk = _Operands("tp_fp8_quantize_both")
+    chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
     rows, cols = X.shape
+    u8 = _torch_dtypes("u8")
+    chk("Q", Q, (rows, cols), u8)("Qt", Qt, (cols, rows), u8)
+    chk("scale_inv", scale_inv, (1,), _torch_dtypes("f32"))
+    if workspace is None:
+        raise ValueError("tp_fp8_quantize_both: workspace is required")
+    _check_ws(chk, workspace)
+    chk.done(stream)
     _check("tp_fp8_quantize_both", lib().tp_fp8_quantize_both(
         _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), _ptr(Q), _ld(Q), _ptr(Qt), _ld(Qt),
-        _ptr(scale_inv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-        _stream(stream)))
+        _ptr(scale_inv), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_fp8_quantize_multi_workspace_size(n: int) -> int:
@@ -353,7 +525,17 @@ def tp_fp8_quantize_multi_workspace_size(n: int) -> int:
 def tp_fp8_quantize_both_multi(items, workspace, stream=None):
     """tp_fp8_quantize_both for each (X, Q, Qt, scale_inv, fmt) of `items` (at
     most 6) in two launches in all."""
+    chk = _Operands("tp_fp8_quantize_both_multi")
     n = len(items)
+    u8 = _torch_dtypes("u8")
+    for j, (x, q, qt, si, _) in enumerate(items):
+        chk(f"X[{j}]", x, _shape2(x), _torch_dtypes("bf16", "f32"))
+        chk(f"Q[{j}]", q, tuple(x.shape), u8)(f"Qt[{j}]", qt, tuple(x.shape)[::-1], u8)
+        chk(f"scale_inv[{j}]", si, (1,), _torch_dtypes("f32"))
+    if workspace is None:
+        raise ValueError("tp_fp8_quantize_both_multi: workspace is required")
+    _check_ws(chk, workspace)
+    chk.done(stream)
     vp = ctypes.c_void_p * n
     i64 = ctypes.c_int64 * n
     i32 = ctypes.c_int * n
@@ -370,20 +552,34 @@ def tp_fp8_quantize_both_multi(items, workspace, stream=None):
     si = vp(*[s.data_ptr() for _, _, _, s, _ in items])
     _check("tp_fp8_quantize_both_multi", lib().tp_fp8_quantize_both_multi(
         n, X, rows, cols, ld_x, dt, fmt, Q, ld_q, Qt, ld_qt, si, _ptr(workspace),
-        workspace.numel() * workspace.element_size(), _stream(stream)))
+        _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_fp8_column_linear_fwd(Xq, Atq, x_si, a_si, bias, Y, U, act="gelu", stream=None):
+    chk = _Operands("tp_fp8_column_linear_fwd")
+    u8, f32, bf = _torch_dtypes("u8"), _torch_dtypes("f32"), _torch_dtypes("bf16")
+    chk("Xq", Xq, _shape2(Xq), u8)
     T, h = Xq.shape
+    chk("Atq", Atq, (_shape2(Atq)[0], h), u8)
     n = Atq.shape[0]
+    chk("x_scale_inv", x_si, (1,), f32)("a_scale_inv", a_si, (1,), f32)
+    none = _act(act) == TP_ACT_NONE
+    chk("bias", bias, (n,), bf, optional=True)("Y", Y, (T, n), bf)
+    chk("U", U, (T, n), bf, optional=none).done(stream)
     _check("tp_fp8_column_linear_fwd", lib().tp_fp8_column_linear_fwd(
         _ptr(Xq), _ptr(Atq), _ptr(x_si), _ptr(a_si), _ptr(bias), _ptr(Y), _ptr(U), T, h, n,
         _ld(Xq), _ld(Atq), _ld(Y), _act(act), _stream(stream)))
 
 
 def tp_fp8_row_linear_fwd_partial(Yq, Btq, y_si, b_si, Zp, stream=None):
+    chk = _Operands("tp_fp8_row_linear_fwd_partial")
+    u8, f32 = _torch_dtypes("u8"), _torch_dtypes("f32")
+    chk("Yq", Yq, _shape2(Yq), u8)
     T, k = Yq.shape
+    chk("Btq", Btq, (_shape2(Btq)[0], k), u8)
     h = Btq.shape[0]
+    chk("y_scale_inv", y_si, (1,), f32)("b_scale_inv", b_si, (1,), f32)
+    chk("Zp", Zp, (T, h), f32).done(stream)
     _check("tp_fp8_row_linear_fwd_partial", lib().tp_fp8_row_linear_fwd_partial(
         _ptr(Yq), _ptr(Btq), _ptr(y_si), _ptr(b_si), _ptr(Zp), T, k, h, _ld(Yq), _ld(Btq),
         _ld(Zp), _stream(stream)))
@@ -391,8 +587,15 @@ def tp_fp8_row_linear_fwd_partial(Yq, Btq, y_si, b_si, Zp, stream=None):
 
 def tp_fp8_linear_bwd_dgrad(dOutq, Wq, d_si, w_si, dIn, U=None, act="none", dout_fmt="e5m2",
                             stream=None):
+    chk = _Operands("tp_fp8_linear_bwd_dgrad")
+    u8, f32, bf = _torch_dtypes("u8"), _torch_dtypes("f32"), _torch_dtypes("bf16")
+    chk("dOutq", dOutq, _shape2(dOutq), u8)
     T, n = dOutq.shape
+    chk("Wq", Wq, (_shape2(Wq)[0], n), u8)
     k = Wq.shape[0]
+    chk("dout_scale_inv", d_si, (1,), f32)("w_scale_inv", w_si, (1,), f32)
+    chk("U", U, (T, k), bf, optional=_act(act) == TP_ACT_NONE)
+    chk("dIn", dIn, (T, k), _torch_dtypes("bf16", "f32")).done(stream)
     ld_u = _ld(U) if U is not None else k
     _check("tp_fp8_linear_bwd_dgrad", lib().tp_fp8_linear_bwd_dgrad(
         _ptr(dOutq), _ptr(Wq), _ptr(d_si), _ptr(w_si), _fmt(dout_fmt), _ptr(U), _act(act),
@@ -408,13 +611,22 @@ def tp_fp8_linear_bwd_wgrad_workspace_size(T: int, k: int, n: int) -> int:
 
 def tp_fp8_linear_bwd_wgrad(Intq, dOuttq, in_si, d_si, dW, dOut=None, dbias=None,
                             dout_fmt="e5m2", workspace=None, stream=None):
+    chk = _Operands("tp_fp8_linear_bwd_wgrad")
+    u8, f32 = _torch_dtypes("u8"), _torch_dtypes("f32")
+    chk("Intq", Intq, _shape2(Intq), u8)
     k, T = Intq.shape
+    chk("dOuttq", dOuttq, (_shape2(dOuttq)[0], T), u8)
     n = dOuttq.shape[0]
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    chk("in_scale_inv", in_si, (1,), f32)("dout_scale_inv", d_si, (1,), f32)
+    chk("dW", dW, (k, n), f32)("dbias", dbias, (n,), f32, optional=True)
+    chk("dOut", dOut, (T, n), _torch_dtypes("bf16"), optional=dbias is None)
+    _check_ws(chk, workspace)
+    chk.done(stream)
     _check("tp_fp8_linear_bwd_wgrad", lib().tp_fp8_linear_bwd_wgrad(
         _ptr(Intq), _ptr(dOuttq), _ptr(in_si), _ptr(d_si), _fmt(dout_fmt), _ptr(dW), _ptr(dOut),
         _ptr(dbias), T, k, n, _ld(Intq), _ld(dOuttq), _ld(dW),
-        _ld(dOut) if dOut is not None else n, _ptr(workspace), ws_bytes, _stream(stream)))
+        _ld(dOut) if dOut is not None else n, _ptr(workspace), _ws_bytes(workspace),
+        _stream(stream)))
 
 
 def tp_set_gemm_override(tile: int = 0, splitk: int = 1) -> None:

@@ -202,7 +202,8 @@ __global__ __launch_bounds__(WM* WN * 64) void gemm_bf16_kernel(GemmParams p) {
   const int tiles_n = static_cast<int>((p.N + BN - 1) / BN);
   const int ntiles = tiles_m * tiles_n;
   int bid = blockIdx.x;
-  if ((ntiles & 7) == 0) bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
+  const int X = p.xcds;  // blocks go round-robin over the XCDs
+  if (X > 1 && ntiles % X == 0) bid = (bid % X) * (ntiles / X) + bid / X;
   constexpr int G = 8;
   const int group = bid / (G * tiles_n);
   const int first_m = group * G;

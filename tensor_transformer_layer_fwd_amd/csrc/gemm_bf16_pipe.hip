@@ -317,7 +317,7 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
   const int wm = wave / WN, wn = wave % WN;
 
-  // ---- output tile: blocks go round-robin over the 8 XCDs, so each XCD
+  // ---- output tile: blocks go round-robin over the XCDs, so each XCD
   // takes a run of consecutive tiles of a grouped column-major order
   const int tiles_m = static_cast<int>(p.M / BM);
   const int tiles_n = static_cast<int>(p.N / BN);
@@ -336,9 +336,10 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   }
   int bid = block - z * ntiles;
   int G = 8;
-  if ((ntiles & 7) == 0) {
-    bid = (bid & 7) * (ntiles >> 3) + (bid >> 3);
-    G = xcd_group_rows(ntiles >> 3, tiles_m, tiles_n, BM, BN);
+  const int X = p.xcds;
+  if (X > 1 && ntiles % X == 0) {
+    bid = (bid % X) * (ntiles / X) + bid / X;
+    G = xcd_group_rows(ntiles / X, tiles_m, tiles_n, BM, BN);
   }
   const int group = bid / (G * tiles_n);
   const int first_m = group * G;
@@ -938,8 +939,10 @@ hipError_t launch_pair256(const GemmParams& pw, const GemmParams& pd, int ekd, c
 
 }  // namespace
 
-hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int kind, int ekd,
+hipError_t launch_gemm_bwd_pair(const GemmParams& pw0, const GemmParams& pd0, int kind, int ekd,
                                 const PairRider& rider, hipStream_t s) {
+  GemmParams pw = pw0, pd = pd0;
+  pw.xcds = pd.xcds = device_shape().xcds;
   switch (kind) {
     case kPairSame128x128:
       return launch_pair_cfg<128, 128, 64, 3, 128, 128, 64, 3>(pw, pd, ekd, rider, s);
@@ -952,7 +955,9 @@ hipError_t launch_gemm_bwd_pair(const GemmParams& pw, const GemmParams& pd, int 
   }
 }
 
-hipError_t launch_gemm_fp8(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+hipError_t launch_gemm_fp8(const GemmParams& p0, const SplitPlan& plan, hipStream_t s) {
+  GemmParams p = p0;
+  p.xcds = device_shape().xcds;
   const int ek = fp8_epilogue_kind(p);
   if (ek == kEpiNone) return hipErrorInvalidValue;
   switch (p.f8) {

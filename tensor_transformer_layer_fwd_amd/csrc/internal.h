@@ -66,7 +66,18 @@ struct GemmParams {
   int f8;
   const float* sa_inv;
   const float* sb_inv;
+  // XCDs the blocks go round-robin over (device_shape().xcds; set by the
+  // launchers): each takes a run of consecutive tiles
+  int xcds;
 };
+
+// Compute units and XCDs of the current device, queried once per device
+// (hipDeviceAttributeMultiprocessorCount, hipDeviceAttributeNumberOfXccs).
+// Without a device (a host-only process) the MI355X figures, 256 and 8.
+struct DeviceShape {
+  int cus, xcds;
+};
+DeviceShape device_shape();
 
 
 // FP8 quantisation of X [rows, cols] (ld_x, bf16 or fp32) into codes Q

@@ -1,6 +1,6 @@
 // Host-side choice of GEMM tile and split-K, and the launch dispatch.
 //
-// The cost model counts rounds of tiles over the 256 CUs; a round costs a
+// The cost model counts rounds of tiles over the device's CUs (256 on MI355X); a round costs a
 // fixed overhead (prologue, epilogue, launch) plus the tile's matrix work at a
 // per-CU rate measured for each tile configuration on MI355X (the clock runs
 // at 1.8-2.2 GHz under matrix load, below the 2.4 GHz peak). A split K adds the
@@ -8,6 +8,7 @@
 // fix-up launch.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <functional>
 #include <queue>
 #include <vector>
@@ -15,12 +16,40 @@
 #include "internal.h"
 
 namespace tpmlp {
+
+DeviceShape device_shape() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];  // cus << 8 | xcds, 0 = not queried
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return DeviceShape{256, 8};
+  }
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    int cus = 0, xcds = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    if (hipDeviceGetAttribute(&xcds, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+        xcds < 1 || xcds > 255)
+      xcds = cus % 8 == 0 ? 8 : 1;
+    (void)hipGetLastError();
+    v = cus << 8 | xcds;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return DeviceShape{v >> 8, v & 255};
+}
+
 namespace {
 
-constexpr int kCUs = 256;
+int cus() { return device_shape().cus; }
 constexpr double kRoundOverheadSec = 3.0e-6;
 constexpr double kHbmBytesPerSec = 5.0e12;  // sustained, for partial traffic
 constexpr double kLaunchSec = 2.0e-6;       // one extra kernel
+// time of a paired launch over its simulated time (measured on the
+// 175B-class shard's 256x192 pairs: 1.09 and 1.14)
+constexpr double kPairSlowdown = 1.12;
 
 struct PipeTile {
   TileId id;
@@ -41,7 +70,7 @@ constexpr PipeTile kPipeTiles[] = {
 
 double cost(int64_t M, int64_t N, int64_t K, const PipeTile& t, int split) {
   const int64_t tiles = (M / t.bm) * (N / t.bn) * split;
-  const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+  const int64_t rounds = (tiles + cus() - 1) / cus();
   const double flops = 2.0 * t.bm * t.bn * static_cast<double>(K / split);
   double c = static_cast<double>(rounds) * (kRoundOverheadSec + flops / t.flop_per_sec_per_cu);
   // the slices write their partials and the fix-up reads them back
@@ -49,8 +78,8 @@ double cost(int64_t M, int64_t N, int64_t K, const PipeTile& t, int split) {
   return c;
 }
 
-int g_force_tile = 0;
-int g_force_split = 1;
+thread_local int g_force_tile = 0;
+thread_local int g_force_split = 1;
 
 const PipeTile* find_tile(int id) {
   for (const PipeTile& t : kPipeTiles)
@@ -101,8 +130,8 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split) {
   if (best_t < 1e30) return best;
   // General kernel (ragged shapes): split K when the grid is small.
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  if (allow_split && tiles < kCUs) {
-    const int64_t want = (kCUs + tiles - 1) / tiles;
+  if (allow_split && tiles < cus()) {
+    const int64_t want = (cus() + tiles - 1) / tiles;
     const int64_t max_split = K / 256;
     const int64_t s = want < max_split ? want : max_split;
     if (s > 1) {
@@ -128,7 +157,7 @@ double pair_cost(const PipeTile* w, const PipeTile* d, int64_t T, int64_t k, int
   const double kd = 2.0 * d->bm * d->bn * 64.0 / d->flop_per_sec_per_cu;
   const int64_t tiles_w = (k / w->bm) * (n / w->bn), tiles_d = (T / d->bm) * (k / d->bn);
   std::priority_queue<double, std::vector<double>, std::greater<double>> cu;
-  for (int c = 0; c < kCUs; ++c) cu.push(0.0);
+  for (int c = 0, n = cus(); c < n; ++c) cu.push(0.0);
   auto run = [&](int64_t blocks, double sec) {
     for (int64_t b = 0; b < blocks; ++b) {
       const double f = cu.top();
@@ -229,6 +258,23 @@ SplitPlan plan_pair(int64_t T, int64_t k, int64_t n) {
     if (pd.tile == kPipe128x128 && k % wide->bn == 0)
       consider(w, wide, kPairW128x128D128x192);
   }
+  if (g_force_tile == 0) {
+    // Pair only where the model puts the pair clearly below the two calls
+    // (the data gradient on its own tile, the weight gradient with its own
+    // plan, one more launch). A paired block runs slower than the same tile
+    // in a launch of its own (one kernel holds both bodies, and the LDS pool
+    // and register budget are the larger product's): on the 175B-class shard
+    // the 256x192 pairs took 652 and 668 us against 572 and 613 us for the
+    // two calls, where the model has both at the same number of rounds.
+    const SplitPlan pw1 = plan_gemm_bf16(k, n, T, true);
+    const PipeTile* tw1 = find_tile(pw1.tile);
+    const PipeTile* td1 = find_tile(pd.tile);
+    if (tw1 && td1) {
+      const double two_calls =
+          cost(T, k, n, *td1, 1) + cost(k, n, T, *tw1, pw1.splitk) + kLaunchSec;
+      if (best_c * kPairSlowdown >= two_calls) return none;
+    }
+  }
   return SplitPlan{kind, best, T / best};
 }
 
@@ -240,7 +286,7 @@ int pair_free_cus(const SplitPlan& pl, int64_t T, int64_t k, int64_t n) {
   const PipeTile* w = find_tile(tw);
   const PipeTile* d = find_tile(td);
   const int64_t blocks = (k / w->bm) * (n / w->bn) * pl.splitk + (T / d->bm) * (k / d->bn);
-  return blocks < kCUs ? static_cast<int>(kCUs - blocks) : 0;
+  return blocks < cus() ? static_cast<int>(cus() - blocks) : 0;
 }
 
 namespace {
@@ -283,7 +329,9 @@ int gemm_pipe_epilogue(const GemmParams& p, const SplitPlan& plan) {
   return pipe_epilogue_kind(p);
 }
 
-hipError_t launch_gemm_bf16(const GemmParams& p, const SplitPlan& plan, hipStream_t s) {
+hipError_t launch_gemm_bf16(const GemmParams& p0, const SplitPlan& plan, hipStream_t s) {
+  GemmParams p = p0;
+  p.xcds = device_shape().xcds;
   const int ek = gemm_pipe_epilogue(p, plan);
   if (ek != kEpiNone) return launch_gemm_bf16_pipe(p, plan, ek, s);
   return launch_gemm_bf16_general(p, plan, s);

@@ -329,7 +329,7 @@ extern "C" {
 
 int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, void* Y_i,
                          void* U_i, int64_t T, int64_t h, int64_t n, int64_t ld_x,
-                         int64_t ld_a, int64_t ld_y, int dt, int act, hipStream_t stream) {
+                         int64_t ld_a, int64_t ld_y, tp_dtype dt, tp_act act, hipStream_t stream) {
   if (!X || !A_i || !Y_i) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (!act_ok(act)) return TP_ERR_ACT;
@@ -359,7 +359,7 @@ int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, voi
 
 int tp_row_linear_fwd_partial(const void* Y_i, const void* B_i, float* Zp_i, int64_t T,
                               int64_t k, int64_t h, int64_t ld_y, int64_t ld_b,
-                              int64_t ld_z, int dt, hipStream_t stream) {
+                              int64_t ld_z, tp_dtype dt, hipStream_t stream) {
   if (!Y_i || !B_i || !Zp_i) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (!dim_ok(T) || !dim_ok(k) || !dim_ok(h)) return TP_ERR_SHAPE;
@@ -381,9 +381,9 @@ int tp_row_linear_fwd_partial(const void* Y_i, const void* B_i, float* Zp_i, int
   return run_gemm(p, dt, false, 0, stream);
 }
 
-int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act, void* dIn,
+int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, tp_act act, void* dIn,
                         int64_t T, int64_t k, int64_t n, int64_t ld_dout, int64_t ld_w,
-                        int64_t ld_u, int64_t ld_din, int dt, int out_dt,
+                        int64_t ld_u, int64_t ld_din, tp_dtype dt, tp_dtype out_dt,
                         hipStream_t stream) {
   if (!dOut || !W || !dIn) return TP_ERR_NULL;
   if (!dtype_ok(dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
@@ -397,10 +397,10 @@ int tp_linear_bwd_dgrad(const void* dOut, const void* W, const void* U, int act,
   return run_gemm(p, dt, false, 0, stream);
 }
 
-int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U, int act,
+int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U, tp_act act,
                                   void* dIn, void* Y, int64_t T, int64_t k, int64_t n,
                                   int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_din,
-                                  int64_t ld_y, int dt, hipStream_t stream) {
+                                  int64_t ld_y, tp_dtype dt, hipStream_t stream) {
   if (!dOut || !W || !U || !dIn || !Y) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (act != TP_ACT_GELU_TANH) return TP_ERR_ACT;
@@ -428,7 +428,7 @@ int tp_linear_bwd_dgrad_recompute(const void* dOut, const void* W, const void* U
   return run_gemm(p, dt, false, 0, stream);
 }
 
-int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
+int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, tp_dtype dt,
                                        size_t* bytes) {
   if (!bytes) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
@@ -439,7 +439,7 @@ int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, int dt,
 
 int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbias, int64_t T,
                         int64_t k, int64_t n, int64_t ld_in, int64_t ld_dout, int64_t ld_dw,
-                        int accumulate, int dt, void* workspace, size_t workspace_bytes,
+                        int accumulate, tp_dtype dt, void* workspace, size_t workspace_bytes,
                         hipStream_t stream) {
   if (!In || !dOut || !dW) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
@@ -456,7 +456,7 @@ int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbia
   return run_gemm(p, dt, true, split_bytes, stream, dbias ? &c : nullptr);
 }
 
-int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, int dt, size_t* bytes) {
+int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, tp_dtype dt, size_t* bytes) {
   if (!bytes) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
@@ -474,7 +474,7 @@ int tp_linear_bwd_plan(int64_t T, int64_t k, int64_t n, int* pairing, int* split
   return TP_OK;
 }
 
-int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, int dt, size_t* bytes) {
+int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, tp_dtype dt, size_t* bytes) {
   if (!bytes) return TP_ERR_NULL;
   size_t b2 = 0, b1 = 0;
   int st = tp_linear_bwd_workspace_size(T, F, h, dt, &b2);
@@ -493,7 +493,7 @@ int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, 
                const void* Y_i, void* dU_i, float* dB_i, float* db, float* dXp_i, float* dA_i,
                float* da_i, int64_t T, int64_t h, int64_t F, int64_t ld_dz, int64_t ld_x,
                int64_t ld_a, int64_t ld_b, int64_t ld_u, int64_t ld_y, int64_t ld_du,
-               int64_t ld_dxp, int64_t ld_db, int64_t ld_da, int accumulate, int dt,
+               int64_t ld_dxp, int64_t ld_db, int64_t ld_da, int accumulate, tp_dtype dt,
                void* workspace, size_t workspace_bytes, hipStream_t stream) {
   // fc2 (row-parallel, GeLU before it): dOut dZ [T,h], W = B_i [F,h], In = Y_i
   // fc1 (column-parallel): dOut dU_i [T,F], W = A_i [h,F], In = X, fp32 dX partial
@@ -555,10 +555,10 @@ int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, 
                        stream);
 }
 
-int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const void* In,
+int tp_linear_bwd(const void* dOut, const void* W, const void* U, tp_act act, const void* In,
                   void* dIn, float* dW, float* dbias, int64_t T, int64_t k, int64_t n,
                   int64_t ld_dout, int64_t ld_w, int64_t ld_u, int64_t ld_in, int64_t ld_din,
-                  int64_t ld_dw, int accumulate, int dt, int out_dt, void* workspace,
+                  int64_t ld_dw, int accumulate, tp_dtype dt, tp_dtype out_dt, void* workspace,
                   size_t workspace_bytes, hipStream_t stream) {
   // every check of both products first
   const int st = check_linear_bwd(dOut, W, U, act, In, dIn, dW, T, k, n, ld_dout, ld_w, ld_u,
@@ -588,7 +588,7 @@ int tp_linear_bwd(const void* dOut, const void* W, const void* U, int act, const
 }
 
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
-                       int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, int out_dt,
+                       int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, tp_dtype out_dt,
                        hipStream_t stream) {
   if (!partials || !out) return TP_ERR_NULL;
   if (p < 1 || p > kMaxPartials) return TP_ERR_SHAPE;
@@ -611,7 +611,7 @@ int tp_reduce_partials(const float* const* partials, int p, const void* bias, vo
 }
 
 int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, int64_t ld_u,
-                int64_t ld_y, int in_dt, int out_dt, int act, hipStream_t stream) {
+                int64_t ld_y, tp_dtype in_dt, tp_dtype out_dt, tp_act act, hipStream_t stream) {
   if (!U || !Y) return TP_ERR_NULL;
   if (!dtype_ok(in_dt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
   if (!act_ok(act)) return TP_ERR_ACT;
@@ -634,7 +634,7 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
 
 int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
                      int64_t heads, int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int causal,
-                     int dt, hipStream_t stream) {
+                     tp_dtype dt, hipStream_t stream) {
   if (!QKV || !C) return TP_ERR_NULL;
   if (dt != TP_BF16) return TP_ERR_DTYPE;
   if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || head_dim != 64) return TP_ERR_SHAPE;
@@ -660,7 +660,7 @@ int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_
 int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float* lse,
                      float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
                      int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
-                     int64_t ld_dqkv, int causal, int dt, hipStream_t stream) {
+                     int64_t ld_dqkv, int causal, tp_dtype dt, hipStream_t stream) {
   if (!QKV || !C || !dC || !lse || !delta || !dQKV) return TP_ERR_NULL;
   if (dt != TP_BF16) return TP_ERR_DTYPE;
   if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || head_dim != 64) return TP_ERR_SHAPE;
@@ -697,7 +697,7 @@ int tp_fp8_quantize_workspace_size(int64_t rows, int64_t cols, size_t* bytes) {
   return TP_OK;
 }
 
-int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt, int fmt,
+int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, tp_dtype dt, tp_fp8_format fmt,
                     int transpose, void* Q, int64_t ld_q, float* scale_inv, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   if (!X || !Q || !scale_inv) return TP_ERR_NULL;
@@ -724,8 +724,8 @@ int tp_fp8_quantize(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int
   return hip_status(launch_fp8_quantize(q, stream));
 }
 
-int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int dt,
-                         int fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
+int tp_fp8_quantize_both(const void* X, int64_t rows, int64_t cols, int64_t ld_x, tp_dtype dt,
+                         tp_fp8_format fmt, void* Q, int64_t ld_q, void* Qt, int64_t ld_qt,
                          float* scale_inv, void* workspace, size_t workspace_bytes,
                          hipStream_t stream) {
   Fp8QuantParams q{};
@@ -768,7 +768,7 @@ int tp_fp8_quantize_both_multi(int n, const void* const* X, const int64_t* rows,
 int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
                              const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
                              int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
-                             int64_t ld_y, int act, hipStream_t stream) {
+                             int64_t ld_y, tp_act act, hipStream_t stream) {
   if (!Xq || !Atq || !x_scale_inv || !a_scale_inv || !Y_i) return TP_ERR_NULL;
   if (!act_ok(act)) return TP_ERR_ACT;
   if (act != TP_ACT_NONE && !U_i) return TP_ERR_NULL;
@@ -825,9 +825,9 @@ int tp_fp8_row_linear_fwd_partial(const void* Yq, const void* Btq, const float* 
 }
 
 int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
-                            const float* w_scale_inv, int dout_fmt, const void* U, int act,
+                            const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U, tp_act act,
                             void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
-                            int64_t ld_w, int64_t ld_u, int64_t ld_din, int out_dt,
+                            int64_t ld_w, int64_t ld_u, int64_t ld_din, tp_dtype out_dt,
                             hipStream_t stream) {
   if (!dOutq || !Wq || !dout_scale_inv || !w_scale_inv || !dIn) return TP_ERR_NULL;
   if (!fmt_ok(dout_fmt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
@@ -867,7 +867,7 @@ int tp_fp8_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, size
 }
 
 int tp_fp8_linear_bwd_wgrad(const void* Intq, const void* dOuttq, const float* in_scale_inv,
-                            const float* dout_scale_inv, int dout_fmt, float* dW,
+                            const float* dout_scale_inv, tp_fp8_format dout_fmt, float* dW,
                             const void* dOut, float* dbias, int64_t T, int64_t k, int64_t n,
                             int64_t ld_int, int64_t ld_doutt, int64_t ld_dw, int64_t ld_dout,
                             void* workspace, size_t workspace_bytes, hipStream_t stream) {

@@ -153,8 +153,11 @@ def test_linear_bwd_plan(lib):
     # fc2: both on 256x192 with the weight gradient in 4 K slices, 224 blocks
     # (one round of the CUs) where 128x128 + 128x192 would need 328
     assert L.tp_linear_bwd_plan(4096, 1536, 768) == (3, 4)
-    assert L.tp_linear_bwd_plan(2048, 12288, 6144)[0] == 3
-    assert L.tp_linear_bwd_plan(2048, 6144, 12288)[0] == 3
+    # the 175B-class shard: both products already fill the CUs for several
+    # rounds each, so pairing saves no round and the paired kernel's slower
+    # blocks lose (652 and 668 us against 572 and 613 us for the two calls)
+    assert L.tp_linear_bwd_plan(2048, 12288, 6144) == (0, 1)
+    assert L.tp_linear_bwd_plan(2048, 6144, 12288) == (0, 1)
     # the ~350M shard (T=6144, h=F=1024, QKV width 768): the data gradient's
     # own 128x256 tile has no paired kernel, and both on 128x128 in 2 slices
     # beats the two calls
@@ -411,3 +414,85 @@ def test_valid_call_without_a_device_reports_hip_error(lib):
     assert lib.tp_bias_act(x, None, x, 8, 8, 8, 8, 1, 1, 1, None) == -6
     assert L.tp_last_hip_error() != 0
     assert "TP_ERR_HIP" in L.tp_status_string(-6)
+
+
+def test_gemm_override_is_per_thread(lib):
+    """The tuning hook changes the plans of the thread that set it only."""
+    import threading
+    own = L.tp_gemm_plan(4096, 1536, 768)
+    seen = {}
+    try:
+        L.tp_set_gemm_override(13, 1)
+        assert L.tp_gemm_plan(4096, 1536, 768)[0] == 13
+        t = threading.Thread(target=lambda: seen.update(plan=L.tp_gemm_plan(4096, 1536, 768)))
+        t.start()
+        t.join()
+    finally:
+        L.tp_set_gemm_override(0)
+    assert seen["plan"] == own != (13, 1, 768)
+    assert L.tp_gemm_plan(4096, 1536, 768) == own
+
+
+def test_enum_typed_arguments_in_header():
+    """dtype, activation and FP8 format arguments carry the header's enum types."""
+    src = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    assert not re.search(r"\bint (dt|out_dt|in_dt|act|fmt|dout_fmt)\b", src)
+    assert "tp_dtype dt" in src and "tp_act act" in src and "tp_fp8_format fmt" in src
+
+
+def test_binding_rejects_mismatched_operands():
+    """The torch wrappers check every operand's shape, dtype, layout and device
+    before calling the library (which cannot see buffer sizes); nothing is
+    launched. CPU tensors of the right shape fail the device check last."""
+    import torch
+    bf, f32, u8 = torch.bfloat16, torch.float32, torch.uint8
+    T, h, F = 64, 32, 48
+
+    def z(*shape, dtype=bf):
+        return torch.zeros(*shape, dtype=dtype)
+
+    X, A, a, Y, U = z(T, h), z(h, F), z(F), z(T, F), z(T, F)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        L.tp_column_linear_fwd(X, A, a, Y, U)
+    with pytest.raises(ValueError, match="A_i has shape"):
+        L.tp_column_linear_fwd(X, z(F, h), a, Y, U)          # transposed weight
+    with pytest.raises(ValueError, match="bias_i has shape"):
+        L.tp_column_linear_fwd(X, A, z(h), Y, U)
+    with pytest.raises(TypeError, match="Y_i has dtype"):
+        L.tp_column_linear_fwd(X, A, a, z(T, F, dtype=f32), U)
+    with pytest.raises(ValueError, match="U_i is required"):
+        L.tp_column_linear_fwd(X, A, a, Y, None, act="gelu")
+    with pytest.raises(ValueError, match="unit stride"):
+        L.tp_column_linear_fwd(X, A, a, z(F, T).t(), U)      # column-major view
+    B, Zp = z(F, h), z(T, h, dtype=f32)
+    with pytest.raises(TypeError, match="Zp_i has dtype"):
+        L.tp_row_linear_fwd_partial(Y, B, z(T, h))           # bf16 partial
+    with pytest.raises(ValueError, match="B_i has shape"):
+        L.tp_row_linear_fwd_partial(Y, z(h, F), Zp)
+    with pytest.raises(ValueError, match="dIn has shape"):
+        L.tp_linear_bwd_dgrad(z(T, h), B, U, z(T, h), act="gelu")
+    with pytest.raises(ValueError, match="dW has shape"):
+        L.tp_linear_bwd_wgrad(Y, z(T, h), z(h, F, dtype=f32))
+    with pytest.raises(TypeError, match="dW has dtype"):
+        L.tp_linear_bwd(z(T, h), B, U, Y, U, z(F, h), act="gelu")
+    with pytest.raises(ValueError, match="dXp_i has shape"):
+        L.tp_mlp_bwd(z(T, h), X, A, B, U, Y, z(T, F), z(F, h, dtype=f32), None,
+                     z(T, F, dtype=f32), z(h, F, dtype=f32), None)
+    with pytest.raises(ValueError, match="partials\\[1\\] has shape"):
+        L.tp_reduce_partials([Zp, z(T, h + 1, dtype=f32)], None, z(T, h))
+    with pytest.raises(TypeError, match="bias has dtype"):
+        L.tp_reduce_partials([Zp, Zp], z(h, dtype=f32), z(T, h))
+    with pytest.raises(ValueError, match="C has shape"):
+        L.tp_attention_fwd(z(128, 3 * 128), z(128, 64), None, 2, 64, 2)
+    with pytest.raises(ValueError, match="delta has shape"):
+        L.tp_attention_bwd(z(128, 384), z(128, 128), z(128, 128), z(256, dtype=f32),
+                           z(255, dtype=f32), z(128, 384), 2, 64, 2)
+    with pytest.raises(ValueError, match="Qt has shape"):
+        L.tp_fp8_quantize_both(X, z(T, h, dtype=u8), z(T, h, dtype=u8), z(1, dtype=f32),
+                               z(4096, dtype=u8))
+    with pytest.raises(ValueError, match="Atq has shape"):
+        L.tp_fp8_column_linear_fwd(z(T, h, dtype=u8), z(h, F, dtype=u8), z(1, dtype=f32),
+                                   z(1, dtype=f32), None, Y, U)
+    with pytest.raises(ValueError, match="dOut is required"):
+        L.tp_fp8_linear_bwd_wgrad(z(F, T, dtype=u8), z(h, T, dtype=u8), z(1, dtype=f32),
+                                  z(1, dtype=f32), z(F, h, dtype=f32), dbias=z(h, dtype=f32))
