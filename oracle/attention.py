@@ -77,3 +77,48 @@ def attention_core_bwd(QKV, dC, batch: int, seq: int, heads: int, d: int, causal
     dq = np.einsum("bhqk,bkhd->bqhd", ds, k) / math.sqrt(d)
     dk = np.einsum("bhqk,bqhd->bkhd", ds, q) / math.sqrt(d)
     return np.stack([dq, dk, dv], axis=2).reshape(batch * seq, 3 * heads * d)
+
+
+def tp_attn_block(X, W, Ow, dZa, p: int, batch: int, seq: int, heads: int, shards=None,
+                  d: int = 64, causal: bool = True):
+    """The attention block of a Transformer layer over p tensor-parallel
+    shards, forward then backward, with the attention core between the
+    projections ("Megatron" page, "Transformer-layer tensor parallelism": the
+    QKV projection split by output columns, the output projection by input
+    rows, each shard running the attention of its own heads).
+
+    Per shard i, with W_i = W[:, i*Q:(i+1)*Q] (Q = 3*heads*d/p, read as
+    [Q | K | V] of the shard's heads/p heads) and Ow_i = Ow[i*O:(i+1)*O, :]
+    (O = heads*d/p):
+        QKV_i = X W_i;  C_i, lse_i = attention core of QKV_i;  Zpa_i = C_i Ow_i
+        dC_i = dZa Ow_i^T;  dOw_i = C_i^T dZa;  dQKV_i = core backward of dC_i
+        dW_i = X^T dQKV_i;  dXqp_i = dQKV_i W_i^T
+    and the sums over shards Za = sum_i Zpa_i, dXq = sum_i dXqp_i (every shard ran).
+    """
+    from .oracle import (column_linear_fwd, linear_bwd_dgrad, linear_bwd_wgrad,
+                         reduce_partials, row_linear_fwd_partial, shard_columns, shard_rows)
+    if heads % p:
+        raise ValueError("the heads must split evenly over the shards")
+    shards = tuple(range(p)) if shards is None else tuple(shards)
+    H = heads // p
+    out = {}
+    Zp, dXp = [], []
+    for i in shards:
+        W_i, Ow_i = shard_columns(W, p, i), shard_rows(Ow, p, i)
+        QKV_i, _ = column_linear_fwd(X, W_i, None, "none")
+        C_i, lse_i = attention_core_fwd(QKV_i, batch, seq, H, d, causal)
+        Zpa_i = row_linear_fwd_partial(C_i, Ow_i)
+        dC_i = linear_bwd_dgrad(dZa, Ow_i, None, "none")
+        dOw_i, _ = linear_bwd_wgrad(C_i, dZa)
+        dQKV_i = attention_core_bwd(QKV_i, dC_i, batch, seq, H, d, causal)
+        dW_i, _ = linear_bwd_wgrad(X, dQKV_i)
+        dXq_i = linear_bwd_dgrad(dQKV_i, W_i, None, "none")
+        out.update({f"QKV_{i}": QKV_i, f"C_{i}": C_i, f"lse_{i}": lse_i, f"Zpa_{i}": Zpa_i,
+                    f"dC_{i}": dC_i, f"dOw_{i}": dOw_i, f"dQKV_{i}": dQKV_i, f"dW_{i}": dW_i,
+                    f"dXqp_{i}": dXq_i})
+        Zp.append(Zpa_i)
+        dXp.append(dXq_i)
+    if len(shards) == p:
+        out["Za"] = reduce_partials(Zp, None)
+        out["dXq"] = reduce_partials(dXp, None)
+    return out

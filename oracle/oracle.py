@@ -217,15 +217,22 @@ def mlp_unsharded(X, A, a, B, b, dZ):
             "da": da, "dX": dX}
 
 
-def run_config(cfg, inputs) -> dict:
+def run_config(cfg, inputs, attn_core: bool = False) -> dict:
     """All outputs of one fwd+bwd step of a workload (names as in tp_mlp /
-    tp_attn_proj), from the HostTensors of tp_inputs.make_inputs."""
+    tp_attn_proj), from the HostTensors of tp_inputs.make_inputs. With
+    attn_core the attention workloads run the whole attention block
+    (oracle.attention.tp_attn_block: the core between the projections, C_i
+    and dQKV_i computed rather than drawn)."""
     g = {k: v.f64() for k, v in inputs.items()}
     out = {}
     if cfg.mlp:
         out.update(tp_mlp(g["X"], g["A"], g.get("a"), g["B"], g.get("b"), g["dZ"],
                           cfg.p, cfg.shards, weights_are_shards=not cfg.full_weights))
-    if cfg.attn:
+    if cfg.attn and attn_core:
+        from .attention import tp_attn_block
+        out.update(tp_attn_block(g["X"], g["W"], g["Ow"], g["dZa"], cfg.p, cfg.micro_batch,
+                                 cfg.seq, cfg.heads, cfg.shards))
+    elif cfg.attn:
         out.update(tp_attn_proj(g["X"], g["W"], g["C"], g["Ow"], g["dQKV"], g["dZa"],
                                 cfg.p, cfg.shards))
     return out

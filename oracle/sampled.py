@@ -95,6 +95,20 @@ def attn_sampled(X, W, C, Ow, dQKV, dZa, p, rows, cols_q, cols_o, shards=None):
     return out
 
 
+def attn_block_sampled(X, W, Ow, dZa, p, batch, seq, heads, seqs, shards=None):
+    """Token-row outputs of the attention block (oracle.attention.tp_attn_block)
+    for the whole sequences `seqs`: attention stays inside a sequence, so the
+    block on those sequences' rows gives exactly those rows of QKV_i, C_i,
+    Zpa_i, dC_i, dQKV_i, dXqp_i, Za and dXq, and lse_i of those sequences. The
+    weight gradients sum over every token and are not returned."""
+    from .attention import tp_attn_block
+    seqs = np.asarray(seqs)
+    rows = (seqs[:, None] * seq + np.arange(seq)[None, :]).reshape(-1)
+    g = tp_attn_block(np.asarray(X)[rows], W, Ow, np.asarray(dZa)[rows], p, len(seqs), seq,
+                      heads, shards)
+    return {k: v for k, v in g.items() if not k.startswith(("dW_", "dOw_"))}
+
+
 # which axis of each device output the sample indexes
 ROW_SAMPLED = ("U", "Y", "Zp", "dU", "dXp", "Z", "dX", "QKV", "Zpa", "dC", "dXqp", "Za", "dXq")
 
@@ -130,5 +144,5 @@ def run_config_sampled(cfg, inputs, rows, cols_f=None, cols_q=None, cols_o=None)
     return out
 
 
-__all__ = ["mlp_sampled", "attn_sampled", "run_config_sampled", "sample_device_output",
-           "gelu_tanh"]
+__all__ = ["mlp_sampled", "attn_sampled", "attn_block_sampled", "run_config_sampled",
+           "sample_device_output", "gelu_tanh"]

@@ -193,3 +193,128 @@ def test_backward_special_cases():
     QKV2 = rng.standard_normal((seq, 3 * d))
     dQKV2 = attention_core_bwd(QKV2, G, batch, seq, heads, d, True)
     np.testing.assert_allclose(dQKV2[:, d:2 * d].sum(axis=0), 0.0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- #
+# the attention block: projections with the core between them                  #
+# --------------------------------------------------------------------------- #
+from oracle.attention import tp_attn_block  # noqa: E402
+
+
+def _block_inputs(rng, batch, seq, heads, d, h):
+    T = batch * seq
+    X = rng.standard_normal((T, h))
+    W = rng.standard_normal((h, 3 * heads * d)) * 0.3
+    Ow = rng.standard_normal((heads * d, h)) * 0.3
+    dZa = rng.standard_normal((T, h))
+    return X, W, Ow, dZa
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_block_finite_differences(causal):
+    """L = <dZa, Za(X, W, Ow)>: central differences along random directions
+    in X, W and Ow equal <dXq, E>, <[dW_0 .. dW_p-1], E> and <[dOw_0; ..], E>."""
+    rng = np.random.default_rng(21)
+    batch, seq, heads, d, h, p = 2, 5, 4, 3, 7, 2
+    X, W, Ow, dZa = _block_inputs(rng, batch, seq, heads, d, h)
+    g = tp_attn_block(X, W, Ow, dZa, p, batch, seq, heads, d=d, causal=causal)
+    dW = np.concatenate([g[f"dW_{i}"] for i in range(p)], axis=1)
+    dOw = np.concatenate([g[f"dOw_{i}"] for i in range(p)], axis=0)
+
+    def loss(X_, W_, Ow_):
+        return np.sum(dZa * tp_attn_block(X_, W_, Ow_, dZa, p, batch, seq, heads, d=d,
+                                          causal=causal)["Za"])
+
+    eps = 1e-5
+    for grad, which in ((g["dXq"], 0), (dW, 1), (dOw, 2)):
+        for _ in range(3):
+            args = [X, W, Ow]
+            E = rng.standard_normal(args[which].shape)
+            plus = list(args)
+            minus = list(args)
+            plus[which] = args[which] + eps * E
+            minus[which] = args[which] - eps * E
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            an = np.sum(grad * E)
+            assert abs(fd - an) <= 1e-7 * (1 + abs(an)), (which, fd, an)
+
+
+def test_block_is_independent_of_the_tp_degree():
+    """Heads do not interact, so the block over p = 1, 2, 4 shards gives the
+    same sums when W's columns are laid out per shard as [Q | K | V] of that
+    shard's heads (and Ow's rows as its heads' rows): this pins the head and
+    shard indexing of the column and row splits."""
+    rng = np.random.default_rng(22)
+    batch, seq, heads, d, h = 2, 4, 4, 2, 5
+    X, W1, Ow, dZa = _block_inputs(rng, batch, seq, heads, d, h)
+    ref = tp_attn_block(X, W1, Ow, dZa, 1, batch, seq, heads, d=d)
+    for p in (2, 4):
+        H = heads // p
+        # p = 1 layout: [Q heads 0..3 | K heads 0..3 | V heads 0..3]
+        cols = []
+        for i in range(p):
+            for part in range(3):
+                for j in range(i * H, (i + 1) * H):
+                    cols.extend(range(part * heads * d + j * d, part * heads * d + (j + 1) * d))
+        Wp = W1[:, cols]
+        got = tp_attn_block(X, Wp, Ow, dZa, p, batch, seq, heads, d=d)
+        np.testing.assert_allclose(got["Za"], ref["Za"], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["dXq"], ref["dXq"], rtol=1e-12, atol=1e-12)
+        dWp = np.concatenate([got[f"dW_{i}"] for i in range(p)], axis=1)
+        np.testing.assert_allclose(dWp, ref["dW_0"][:, cols], rtol=1e-12, atol=1e-12)
+        dOwp = np.concatenate([got[f"dOw_{i}"] for i in range(p)], axis=0)
+        np.testing.assert_allclose(dOwp, ref["dOw_0"], rtol=1e-12, atol=1e-12)
+
+
+def test_block_with_zero_queries_and_identity_values():
+    """W with a zero Q block and a V block that copies the first d features of
+    X per head: causal attention is then the running mean of those features,
+    so Za = prefix-mean(X[:, :d] per head) Ow, written out directly."""
+    rng = np.random.default_rng(23)
+    batch, seq, heads, d, h, p = 2, 6, 2, 3, 4, 2
+    X, W, Ow, dZa = _block_inputs(rng, batch, seq, heads, d, h)
+    H = heads // p
+    Q = 3 * H * d
+    for i in range(p):
+        blk = W[:, i * Q:(i + 1) * Q]
+        blk[:, :H * d] = 0.0                       # Q of the shard's heads
+        blk[:, 2 * H * d:] = 0.0                   # V of the shard's heads
+        for j in range(H):
+            for c in range(d):
+                blk[c, 2 * H * d + j * d + c] = 1.0
+    got = tp_attn_block(X, W, Ow, dZa, p, batch, seq, heads, d=d)
+    xs = X[:, :d].reshape(batch, seq, d)
+    mean = np.cumsum(xs, axis=1) / np.arange(1, seq + 1)[None, :, None]
+    C = np.tile(mean.reshape(batch * seq, d), (1, heads))    # every head sees the same values
+    np.testing.assert_allclose(got["Za"], C @ Ow, rtol=1e-12, atol=1e-12)
+
+
+def test_block_equals_projections_around_the_core():
+    """With C_i and dQKV_i taken from the core, the projection oracle
+    (tp_attn_proj, which takes them as inputs) gives the block's outputs."""
+    import oracle
+    rng = np.random.default_rng(24)
+    batch, seq, heads, d, h, p = 2, 5, 4, 2, 6, 2
+    X, W, Ow, dZa = _block_inputs(rng, batch, seq, heads, d, h)
+    g = tp_attn_block(X, W, Ow, dZa, p, batch, seq, heads, d=d)
+    C = np.concatenate([g[f"C_{i}"] for i in range(p)], axis=1)
+    dQKV = np.concatenate([g[f"dQKV_{i}"] for i in range(p)], axis=1)
+    r = oracle.tp_attn_proj(X, W, C, Ow, dQKV, dZa, p)
+    for k in r:
+        np.testing.assert_allclose(g[k], r[k], rtol=1e-12, atol=1e-12)
+
+
+def test_block_sampled_sequences_match_the_full_block():
+    """The whole-sequence sample of the block equals those rows of the full block."""
+    from oracle.sampled import attn_block_sampled
+    rng = np.random.default_rng(25)
+    batch, seq, heads, d, h, p = 4, 5, 2, 64, 8, 2
+    X, W, Ow, dZa = _block_inputs(rng, batch, seq, heads, d, h)
+    full = tp_attn_block(X, W, Ow, dZa, p, batch, seq, heads)
+    seqs = [3, 1]
+    rows = np.concatenate([np.arange(s * seq, (s + 1) * seq) for s in seqs])
+    got = attn_block_sampled(X, W, Ow, dZa, p, batch, seq, heads, seqs)
+    for k, v in got.items():
+        ref = full[k][seqs] if k.startswith("lse_") else full[k][rows]
+        np.testing.assert_allclose(v, ref, rtol=1e-12, atol=1e-13, err_msg=k)
+    assert not any(k.startswith(("dW_", "dOw_")) for k in got)
