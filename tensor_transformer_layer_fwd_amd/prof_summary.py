@@ -4,15 +4,29 @@
         --cmd "the profiled command" [--out profiles/NAME.txt]
     python -m tensor_transformer_layer_fwd_amd.prof_summary traffic \
         --fetch FETCH_COUNTER_CSV --write WRITE_COUNTER_CSV --kernel SUBSTRING \
-        --grid GRID_SIZE --copy-mib MIB --cmd-fetch "..." --cmd-write "..." \
-        [--out profiles/traffic.json]
-    python -m tensor_transformer_layer_fwd_amd.prof_summary mfma COUNTER_CSV --cmd "..."
+        --workload NAME --call NAME [--grid GRID_SIZE] --copy-mib MIB \
+        --cmd-fetch "..." --cmd-write "..." [--out profiles/traffic.json]
+    python -m tensor_transformer_layer_fwd_amd.prof_summary mfma COUNTER_CSV --cmd "..." \
+        [--sclk-mhz MHZ] [--out profiles/NAME.txt]
 
 `traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel into
 HBM bytes per launch, scaled by what the same counters read for a plain device
 copy of known size run in the same process (bench.py --calibrate-copy), and
-records a hash of the pipelined GEMM sources so that bench.py reports the figure only
-while the kernels are unchanged.
+records it under "workload:call" in profiles/traffic.json with a hash of the
+pipelined GEMM sources, so that bench.py reports the figure only while the
+kernels are unchanged.
+
+`mfma` turns SQ_VALU_MFMA_BUSY_CYCLES into the fraction of the matrix cores'
+cycles a dispatch kept busy. The counter adds, over every SIMD, the cycles each
+MFMA instruction occupies its unit (32 per v_mfma_f32_32x32x16_bf16: 32768
+flops at 1024 flops per clock per SIMD). The cycles the units had are SIMDs x
+the dispatch's duration (its own start and end timestamps in the counter run)
+x the engine clock: at the 2.4 GHz spec clock the fraction equals achieved
+flops over the spec peak; at the measured engine clock (--sclk-mhz) it is the
+utilisation of the clock the part held, never below the former.
+GRBM_GUI_ACTIVE is not used: summed over the XCDs and divided by their number
+it gave 2.69 GHz over a 35.7 us dispatch, above the part's highest clock, so its
+window is wider than the dispatch.
 """
 from __future__ import annotations
 
@@ -98,34 +112,78 @@ def cmd_traffic(a):
     f_scale = copy_bytes / (fc * 1024) if fc else 1.0
     w_scale = copy_bytes / (wc * 1024) if wc else 1.0
     rec = {
-        "call": a.call, "kernel": a.kernel, "grid": a.grid,
+        "workload": a.workload, "call": a.call, "kernel": a.kernel, "grid": a.grid,
         "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk, "dispatches": [nf, nw],
         "copy_calibration": {"bytes_each_way": copy_bytes, "fetch_kib": fc, "write_kib": wc,
                              "fetch_scale": f_scale, "write_scale": w_scale},
+        "fetch_bytes_per_launch": fk * 1024 * f_scale,
+        "write_bytes_per_launch": wk * 1024 * w_scale,
         "traffic_bytes_per_launch": fk * 1024 * f_scale + wk * 1024 * w_scale,
         "source_sha256": source_hash(),
         "commands": {"fetch": a.cmd_fetch, "write": a.cmd_write},
     }
-    text = json.dumps(rec, indent=1)
+    out = {"records": {}}
+    if a.out and os.path.exists(a.out):
+        try:
+            out = json.load(open(a.out))
+            out.setdefault("records", {})
+        except ValueError:
+            out = {"records": {}}
+    out["records"][f"{a.workload}:{a.call}"] = rec
+    text = json.dumps(out, indent=1)
     if a.out:
         open(a.out, "w").write(text + "\n")
-    print(text)
+    print(json.dumps(rec, indent=1))
+
+
+SIMDS = 1024  # 256 CUs x 4 SIMDs on MI355X
+SPEC_MHZ = 2400.0
+
+
+def mfma_rows(path, sclk_mhz=None):
+    """(kernel, grid, dispatches, median duration us, median busy cycles,
+    busy at the spec clock, busy at sclk_mhz or None) per kernel and grid."""
+    dur = collections.defaultdict(list)
+    cyc = collections.defaultdict(list)
+    seen = set()
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != "SQ_VALU_MFMA_BUSY_CYCLES":
+            continue
+        key = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        did = int(r["Dispatch_Id"])
+        if (did, key) in seen:
+            continue
+        seen.add((did, key))
+        dur[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        cyc[key].append(float(r["Counter_Value"]))
+    rows = []
+    for key in dur:
+        d, c = statistics.median(dur[key]), statistics.median(cyc[key])
+        if d <= 0:
+            continue
+        spec = c / (SIMDS * d * 1e-6 * SPEC_MHZ * 1e6)
+        at = c / (SIMDS * d * 1e-6 * sclk_mhz * 1e6) if sclk_mhz else None
+        rows.append((key[0], key[1], len(dur[key]), d, c, spec, at))
+    rows.sort(key=lambda r: -r[4] * 1.0)
+    return rows
 
 
 def cmd_mfma(a):
-    d = _per_dispatch(a.csv)
-    lines = [f"# rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_BUSY_CU_CYCLES",
+    rows = mfma_rows(a.csv, a.sclk_mhz)
+    lines = ["# rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES",
              f"# command: {a.cmd}",
-             "# MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCD x 1024 SIMDs)", "",
-             f"{'dispatches':>10} {'mfma_busy':>9}  kernel (grid)"]
-    agg = collections.defaultdict(list)
-    for (did, name, g), c in d.items():
-        if "GRBM_GUI_ACTIVE" not in c or c["GRBM_GUI_ACTIVE"] == 0:
+             "# busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x dispatch duration x clock);",
+             f"# busy_spec at the {SPEC_MHZ:.0f} MHz spec clock (= achieved flops / spec peak)",
+             (f"# busy_sclk at the measured engine clock ({a.sclk_mhz:.0f} MHz)" if a.sclk_mhz
+              else "# busy_sclk: no measured clock given"),
+             "",
+             f"{'dispatches':>10} {'dur_us':>9} {'busy_cycles':>13} {'busy_spec':>9} "
+             f"{'busy_sclk':>9}  kernel (grid)"]
+    for name, g, n, d, c, spec, at in rows:
+        if c == 0:
             continue
-        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / 8 * 1024)
-        agg[(_short(name), g)].append(busy)
-    for (name, g), v in sorted(agg.items(), key=lambda kv: -statistics.median(kv[1])):
-        lines.append(f"{len(v):10d} {100 * statistics.median(v):8.1f}%  {name} ({g})")
+        ats = f"{100 * at:8.1f}%" if at is not None else f"{'-':>9}"
+        lines.append(f"{n:10d} {d:9.2f} {c:13.0f} {100 * spec:8.1f}% {ats}  {name} ({g})")
     text = "\n".join(lines) + "\n"
     if a.out:
         open(a.out, "w").write(text)
@@ -144,6 +202,7 @@ def main():
     t.add_argument("--write", required=True)
     t.add_argument("--kernel", required=True)
     t.add_argument("--call", required=True, help="the bench.py call the kernel belongs to")
+    t.add_argument("--workload", required=True, help="the bench.py workload of the call")
     t.add_argument("--grid", type=int, default=None)
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--cmd-fetch", required=True)
@@ -152,6 +211,7 @@ def main():
     m = sub.add_parser("mfma")
     m.add_argument("csv")
     m.add_argument("--cmd", required=True)
+    m.add_argument("--sclk-mhz", type=float, default=None)
     m.add_argument("--out")
     a = ap.parse_args()
     {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)

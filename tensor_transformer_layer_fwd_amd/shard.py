@@ -21,6 +21,12 @@ fc2's gradients pair (tp_linear_bwd_plan), that is one elementwise pass
 Otherwise it is the fc2 dgrad epilogue (tp_linear_bwd_dgrad_recompute), just
 before fc2's weight gradient reads it.
 
+With attn_core=True the attention workloads run the whole attention block:
+the shard's attention core (tp_attention_fwd, causal, heads of 64) turns
+QKV_i into C_i between the two projections, and its backward
+(tp_attention_bwd) turns the output projection's dC_i into dQKV_i for the QKV
+projection's gradients, instead of taking C_i and dQKV_i as drawn inputs.
+
 With fp8=True every MLP product runs on the FP8 matrix cores: each operand
 is quantised (tp_fp8_quantize, per-tensor current scaling) from its stored
 value into the K-contiguous layout its product reads; weights and activations
@@ -58,8 +64,12 @@ class ShardStep:
     """Device buffers of one workload and the calls of one fwd+bwd step."""
 
     def __init__(self, cfg, inputs: dict, device="cuda", recompute=False, fp8=False,
-                 fused_bwd=True):
+                 fused_bwd=True, attn_core=False):
         self.cfg = cfg
+        self.attn_core = bool(attn_core and cfg.attn)
+        if self.attn_core and (cfg.dtype != "bf16" or cfg.heads % cfg.p or
+                               cfg.Q != 3 * 64 * (cfg.heads // cfg.p)):
+            raise ValueError("the attention core runs bf16 heads of 64, whole heads per shard")
         # both gradients of a layer in one call (tp_linear_bwd) or as two calls
         self.fused_bwd = bool(fused_bwd)
         self.recompute = bool(recompute and cfg.mlp)
@@ -113,6 +123,13 @@ class ShardStep:
                 self.out[f"dOw_{i}"] = torch.empty(O, h, **f32)
                 self.out[f"dW_{i}"] = torch.empty(h, Q, **f32)
                 self.out[f"dXqp_{i}"] = torch.empty(T, h, **f32)
+            if self.attn_core:
+                b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
+                for i in shards:
+                    self.out[f"C_{i}"] = torch.empty(T, O, **act)
+                    self.out[f"lse_{i}"] = torch.empty(b, H, Ls, **f32)
+                    self.out[f"dQKV_{i}"] = torch.empty(T, Q, **act)
+                self.delta = torch.empty(b, H, Ls, **f32)
             if len(shards) == cfg.p:
                 self.out["Za"] = torch.empty(T, h, **act)
                 self.out["dXq"] = torch.empty(T, h, **act)
@@ -264,24 +281,37 @@ class ShardStep:
         if "dX" in o:
             L.tp_reduce_partials([o[f"dXp_{i}"] for i in cfg.shards], None, o["dX"])
 
+    def _c(self, i):
+        """C_i: the core's output, or the drawn input of the projection-only step."""
+        return self.out[f"C_{i}"] if self.attn_core else self._col("C", i, self.cfg.O)
+
     def attn_forward(self):
         cfg, o, inp = self.cfg, self.out, self.inp
         Q, O = cfg.Q, cfg.O
+        b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
         for i in cfg.shards:
             L.tp_column_linear_fwd(inp["X"], self._col("W", i, Q), None, o[f"QKV_{i}"], None,
                                    act="none")
-            L.tp_row_linear_fwd_partial(self._col("C", i, O), self._row("Ow", i, O),
-                                        o[f"Zpa_{i}"])
+            if self.attn_core:
+                L.tp_attention_fwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"lse_{i}"], b, Ls, H)
+            L.tp_row_linear_fwd_partial(self._c(i), self._row("Ow", i, O), o[f"Zpa_{i}"])
         if "Za" in o:
             L.tp_reduce_partials([o[f"Zpa_{i}"] for i in cfg.shards], None, o["Za"])
 
     def attn_backward(self):
         cfg, o, inp = self.cfg, self.out, self.inp
         Q, O = cfg.Q, cfg.O
+        b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
         for i in cfg.shards:
             Ow_i, W_i = self._row("Ow", i, O), self._col("W", i, Q)
-            C_i, dQKV_i = self._col("C", i, O), self._col("dQKV", i, Q)
-            self._bwd(inp["dZa"], Ow_i, None, C_i, o[f"dC_{i}"], o[f"dOw_{i}"], None, "none")
+            self._bwd(inp["dZa"], Ow_i, None, self._c(i), o[f"dC_{i}"], o[f"dOw_{i}"], None,
+                      "none")
+            if self.attn_core:
+                L.tp_attention_bwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"dC_{i}"], o[f"lse_{i}"],
+                                   self.delta, o[f"dQKV_{i}"], b, Ls, H)
+                dQKV_i = o[f"dQKV_{i}"]
+            else:
+                dQKV_i = self._col("dQKV", i, Q)
             self._bwd(dQKV_i, W_i, None, inp["X"], o[f"dXqp_{i}"], o[f"dW_{i}"], None, "none")
         if "dXq" in o:
             L.tp_reduce_partials([o[f"dXqp_{i}"] for i in cfg.shards], None, o["dXq"])
