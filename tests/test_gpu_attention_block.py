@@ -3,8 +3,13 @@ shard's attention core and the row-split output projection, forward and
 backward, through the C ABI, against oracle.attention.tp_attn_block.
 
 Tolerance 5e-3 relative Frobenius error per output tensor, as for every bf16
-output; lse (fp32, a natural-log normaliser of order log(seq)) to 1e-3
-absolute, the bf16 rounding of QKV_i moving a score by a few 1e-3 at most.
+output. lse (fp32, the natural log of each query's softmax normaliser) is
+held to a bound derived from the arithmetic: the device's scores come from
+QKV_i rounded to bf16, so each product q_d k_d carries a relative error of at
+most (1 + 2^-8)^2 - 1, a score s_qk = sum_d q_d k_d / 8 an absolute error of at
+most that times sum_d |q_d k_d| / 8, and lse (a softmax-weighted mean of the
+scores to first order) at most the largest of those over the keys the query
+sees, plus 1e-5 for the fp32 sums.
 """
 import dataclasses
 import sys
@@ -35,14 +40,29 @@ def dev():
     return torch.device("cuda:0")
 
 
-def _check(got, ref, keys=None):
+def _lse_bound(QKV, batch, seq, heads, causal=True):
+    """Per-query bound [batch, heads, seq] on |lse_device - lse_exact| from the
+    bf16 rounding of Q and K (module docstring)."""
+    x = np.abs(np.asarray(QKV, np.float64)).reshape(batch, seq, 3, heads, 64)
+    q, k = x[:, :, 0], x[:, :, 1]
+    m = np.einsum("bqhd,bkhd->bhqk", q, k, optimize=True) / 8.0
+    if causal:
+        m = np.where(np.tril(np.ones((seq, seq), dtype=bool)), m, 0.0)
+    rel = (1.0 + 2.0 ** -8) ** 2 - 1.0
+    return rel * m.max(axis=-1) + 1e-5
+
+
+def _check(got, ref, keys=None, cfg=None):
     worst = (0.0, None)
     for k in (keys or ref):
         r = ref[k]
         g = got[k].reshape(r.shape)
         if k.startswith("lse_"):
-            d = float(np.max(np.abs(g - r)))
-            assert d <= 1e-3, (k, d)
+            i = k.split("_")[1]
+            H = cfg.heads // cfg.p
+            bound = _lse_bound(ref[f"QKV_{i}"], r.shape[0], cfg.seq, H)
+            d = np.abs(g - r)
+            assert np.all(d <= bound), (k, float(d.max()), float(bound.min()))
             continue
         e = oracle.rel_fro(g, r)
         worst = max(worst, (e, k))
@@ -63,7 +83,7 @@ def test_attention_block_reduced(dev, name, mb):
     got = step.results()
     ref = oracle.run_config(cfg, inputs, attn_core=True)
     assert set(ref) <= set(got), set(ref) - set(got)
-    worst = _check(got, ref)
+    worst = _check(got, ref, cfg=cfg)
     _say(f"  worst rel err {worst[0]:.3e} ({worst[1]})")
 
 
@@ -93,14 +113,14 @@ def test_attention_block_full_size(dev, name):
     for k in ref:
         v = got[k]
         got_s[k] = v[seqs] if k.startswith("lse_") else v[rows]
-    worst = _check(got_s, ref)
+    worst = _check(got_s, ref, cfg=cfg)
     _say(f"  sampled sequences: worst rel err {worst[0]:.3e} ({worst[1]})")
     if name == "attn":
         from oracle.attention import tp_attn_block
         full = tp_attn_block(g["X"], g["W"], g["Ow"], g["dZa"], cfg.p, cfg.micro_batch, cfg.seq,
                              cfg.heads)
         keys = [k for k in full if k.startswith(("dW_", "dOw_"))]
-        worst = _check(got, full, keys)
+        worst = _check(got, full, keys, cfg=cfg)
         _say(f"  weight gradients: worst rel err {worst[0]:.3e} ({worst[1]})")
 
 
