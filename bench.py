@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--only-call", default=None,
                     help="profiling aid: comma-separated calls of shard 0 of --workload, each "
                          "launched --steps times")
+    ap.add_argument("--per-product", action="store_true",
+                    help="profiling aid (with --only-call): the MLP as one call per product "
+                         "instead of tp_mlp_step")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="profiling aid (with --only-call): also copy MIB MiB device-to-device "
                          "three times, to scale HBM byte counters")
@@ -137,7 +140,22 @@ def shard_calls(step, i=0):
                               2 * T * k * n, T * k * e + T * n * e + k * n * 4, wt[1] == 1,
                               {"M": k, "N": n, "K": T, "tile": wt[0], "splitk": wt[1]}))
 
-    if cfg.mlp:
+    if cfg.mlp and step.step_call:
+        # the MLP of every shard in two launches: forward, sums and data
+        # gradients (four products per shard); weight gradients (two)
+        F, p = cfg.F, cfg.p
+        fused = L.tp_mlp_step_plan(T, h, F, p, step.tp_dt)
+        fr = p * 4 * 2 * T * h * F
+        br = (T * h * e + h * p * F * e + p * F * h * e + T * h * e  # X, A, B, dZ
+              + 3 * T * p * F * e + 2 * p * T * h * 4 + 2 * T * h * e  # U, Y, dU; Zp, dXp; Z, dX
+              + 3 * T * p * F * e + 2 * p * T * h * 4)  # re-read: Y, U, dU; Zp, dXp
+        fw = p * 2 * 2 * T * h * F
+        bw = 2 * T * p * F * e + 2 * T * h * e + 2 * p * F * h * 4  # Y, dU; dZ, X; dB, dA
+        geom = {"T": T, "h": h, "F": F, "p": p, "fused": fused}
+        calls.append(Call("mlp_step_rows", lambda: step.mlp_step("rows"), fr, br, fused, geom))
+        calls.append(Call("mlp_step_wgrad", lambda: step.mlp_step("wgrad"), fw, bw, fused, geom))
+        calls.append(Call("mlp_step", lambda: step.mlp_step(), fr + fw, br + bw, False, geom))
+    elif cfg.mlp:
         F = cfg.F
         A_i, B_i = step._col("A", i, F), step._row("B", i, F)
         a_i = step._col("a", i, F) if cfg.has_bias else None
@@ -313,6 +331,23 @@ def sample_sclk(busy_fn, seconds=0.6):
             "how": "amdsmi GFX clock every 20 ms while headline step replays run back to back"}
 
 
+def step_sclk(step):
+    """Engine clock of the step's first persistent launch: block 0's shader
+    clock (s_memtime) over the 100 MHz real-time clock (s_memrealtime), both
+    read at its start and end and left in the workspace; None without it."""
+    if not getattr(step, "step_call", False):
+        return None
+    import torch
+    torch.cuda.synchronize()
+    c = step.step_ws[64:96].view(torch.int64).cpu().tolist()
+    cyc, wall = c[2] - c[0], (c[3] - c[1]) / 100e6
+    if cyc <= 0 or wall <= 0:
+        return None
+    return {"mhz": round(cyc / wall / 1e6, 1), "spec_mhz": SPEC_SCLK_MHZ,
+            "window_us": round(wall * 1e6, 2),
+            "how": "s_memtime over s_memrealtime across block 0 of the last step's first launch"}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -447,7 +482,7 @@ def measure(name, args, inputs=None, attn_core=False, with_roofline=True, cpu_se
     return cfg, inputs, step, rec
 
 
-def hbm_passes(cfg, step, reps):
+def hbm_passes(cfg, inputs, step, reps):
     """The HBM-bound passes of the headline: the sum over shards (fp32
     partials -> bf16 + bias), the standalone bias + GeLU pass (fp32 U -> bf16 Y,
     an ablation of the epilogue fused into fc1) and, from the counter record,
@@ -472,8 +507,12 @@ def hbm_passes(cfg, step, reps):
            "bias_gelu_standalone": {"GB/s": round(gelu_bytes / (gelu_ms * 1e-3) / 1e9, 1),
                                     "bytes": gelu_bytes, "us": round(gelu_ms * 1e3, 2)},
            "peak_GB/s": PEAK_HBM_GBS}
-    fc1 = next(c for c in shard_calls(step) if c.name == "fc1_fwd")
+    # fc1 as its own product (tp_column_linear_fwd), as the counter record has it
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    own = ShardStep(cfg, inputs, "cuda:0", step_call=False)
+    fc1 = next(c for c in shard_calls(own) if c.name == "fc1_fwd")
     fc1_ms = time_call(fc1.fn, reps)
+    del own
     tr = traffic_record(cfg.name, "fc1_fwd")
     algo_w = 2 * cfg.T * cfg.F * 2
     out["fc1_fused_epilogue"] = {
@@ -520,7 +559,8 @@ def only_calls(args):
     from tensor_transformer_layer_fwd_amd.shard import ShardStep
     from tp_inputs import get_config, make_inputs
     cfg = get_config(args.workload)
-    step = ShardStep(cfg, make_inputs(cfg), "cuda:0", attn_core=cfg.attn)
+    step = ShardStep(cfg, make_inputs(cfg), "cuda:0", attn_core=cfg.attn,
+                     step_call=not args.per_product)
     step.run_eager()
     calls = {c.name: c for c in shard_calls(step)}
     for name in args.only_call.split(","):
@@ -557,9 +597,10 @@ def main():
 
     cfg, inputs, step, head = measure(args.workload, args, cpu_seconds=0)
     wall_ms = head["ms_per_step"]
-    sclk = sample_sclk(step.run)
+    step.run()
+    sclk = {"in_kernel": step_sclk(step), "amdsmi": sample_sclk(step.run)}
     log(f"[bench] engine clock under the step: {json.dumps(sclk)}")
-    hbm = hbm_passes(cfg, step, args.kernel_reps) if cfg.mlp and "Z" in step.out else None
+    hbm = hbm_passes(cfg, inputs, step, args.kernel_reps) if cfg.mlp and "Z" in step.out else None
     log(f"[bench] HBM passes: {json.dumps(hbm)}")
     recompute = fp8 = None
     if not args.no_variants and cfg.mlp:

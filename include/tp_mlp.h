@@ -275,6 +275,90 @@ int tp_mlp_bwd(const void* dZ, const void* X, const void* A_i, const void* B_i, 
 int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, tp_dtype dt, size_t* bytes);
 
 /*
+ * The whole MLP step of all p shards of a layer on this device: every
+ * shard's column-parallel fc1 (bias + GeLU) and row-parallel fc2 partial, the
+ * sum Z = Y_1 B_1 + .. + Y_p B_p + b that stands in for the All-Reduce
+ * ("Megatron" page, "Tensor Parallelism / mathematical principles"), then every
+ * shard's backward (as tp_mlp_bwd) and the sum of the dX partials. The
+ * results are those of the per-product calls above, shard by shard.
+ *
+ * Layouts (bf16 = dt, fp32 as noted; shard i is a column or row block):
+ *   X   [T, h], ld_x            A  [h, p*F], ld_a (A_i: columns i*F ..)
+ *   a   [p*F] or NULL           B  [p*F, h], ld_b (B_i: rows i*F ..)
+ *   b   [h] or NULL             dZ [T, h], ld_dz
+ *   U, Y, dU  [T, p*F], ld_u    (U_i, Y_i, dU_i: columns i*F ..)
+ *   Zp, dXp   fp32 [p, T, h]    compact (shard i at i*T*h, row stride h)
+ *   Z, dX     [T, h], ld_z / ld_dx
+ *   dB  fp32 [p*F, h], ld_db (dB_i: rows i*F ..)   db fp32 [h] or NULL
+ *   dA  fp32 [h, p*F], ld_da (dA_i: columns i*F ..) da fp32 [p*F] or NULL
+ * Weight and bias gradients are overwritten. db = column sums of dZ and
+ * da_i = column sums of dU_i are computed only where their pointer is set.
+ *
+ * bf16, with the shapes tp_mlp_step_plan reports as fused (T a multiple of
+ * 128 x the device's XCD count, h and F of 128, 16-byte aligned operands and
+ * row strides), runs in two persistent launches: one over each XCD's own
+ * token rows (forward, sums, data gradients), one for the weight gradients.
+ * Any other shape or dtype runs the same step as the per-product calls.
+ *
+ * workspace: at least tp_mlp_step_workspace_size bytes, 256-byte aligned,
+ * ZEROED BEFORE ITS FIRST USE (it holds the queues' counters, which every
+ * call leaves zeroed again). It belongs to tp_mlp_step calls alone: no other
+ * call may use it as scratch between them (that would leave the counters
+ * nonzero), and tp_mlp_step calls that share it must not overlap (enqueue them
+ * on one stream). Its first 32-bit word is nonzero after a call
+ * in which a dependency wait gave up (tp_set_wait_limit); that call's results
+ * are then invalid, and the word stays set until the caller clears it.
+ * Bytes 64..95 hold four 64-bit counters of the first launch's block 0: the
+ * shader clock and the 100 MHz real-time clock at its start, then at its end.
+ */
+int tp_mlp_step(const void* X, const void* A, const void* a, const void* B, const void* b,
+                const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The two halves of tp_mlp_step, same arguments: tp_mlp_step_rows computes
+ * the forward, both sums and the data gradients (U, Y, Zp, Z, dU, dXp, dX;
+ * the first launch), tp_mlp_step_wgrad the weight and bias gradients (dB, db,
+ * dA, da; the second launch) from the U, Y and dU the first left. Calling
+ * rows then wgrad on one stream is tp_mlp_step.
+ */
+int tp_mlp_step_rows(const void* X, const void* A, const void* a, const void* B, const void* b,
+                     const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                     float* db, float* dA, float* da, float* dXp, void* dX, int64_t T,
+                     int64_t h, int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b,
+                     int64_t ld_dz, int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db,
+                     int64_t ld_da, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+int tp_mlp_step_wgrad(const void* X, const void* A, const void* a, const void* B, const void* b,
+                      const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                      float* db, float* dA, float* da, float* dXp, void* dX, int64_t T,
+                      int64_t h, int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b,
+                      int64_t ld_dz, int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db,
+                      int64_t ld_da, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Workspace bytes of tp_mlp_step for these shapes (the larger of the fused
+ * path's and the per-product path's needs); pure host function. */
+int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt,
+                               size_t* bytes);
+
+/* Whether tp_mlp_step runs these shapes in the two persistent launches
+ * (*fused = 1, given aligned operands) or as per-product calls (0). */
+int tp_mlp_step_plan(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt, int* fused);
+
+/*
+ * Test hook: the number of polls after which a dependency wait of
+ * tp_mlp_step's persistent launches gives up (setting the workspace's error
+ * word), for calls made by the calling thread. 0 restores the default (about
+ * a quarter of a second); a negative value gives up at the first check that
+ * finds the dependency unmet. Every block still runs to its end.
+ */
+int tp_set_wait_limit(int64_t polls);
+
+/*
  * Sum over shards, the one-GPU stand-in for the All-Reduce ("Megatron" page,
  * "Tensor Parallelism / mathematical principles": the row-split partials Y_i B_i
  * are summed across GPUs; "Transformer-layer tensor parallelism": one such sum

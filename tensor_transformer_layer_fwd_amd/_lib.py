@@ -46,6 +46,16 @@ SIGNATURES = {
                           _int, _vp, _sz, _vp]),
     "tp_mlp_bwd_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_mlp_step": (_int, [_vp] * 17 + [_i64, _i64, _i64, _int] + [_i64] * 9 +
+                    [_int, _vp, _sz, _vp]),
+    "tp_mlp_step_rows": (_int, [_vp] * 17 + [_i64, _i64, _i64, _int] + [_i64] * 9 +
+                         [_int, _vp, _sz, _vp]),
+    "tp_mlp_step_wgrad": (_int, [_vp] * 17 + [_i64, _i64, _i64, _int] + [_i64] * 9 +
+                          [_int, _vp, _sz, _vp]),
+    "tp_mlp_step_workspace_size": (_int, [_i64, _i64, _i64, _int, _int,
+                                          ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_mlp_step_plan": (_int, [_i64, _i64, _i64, _int, _int, ctypes.POINTER(ctypes.c_int)]),
+    "tp_set_wait_limit": (_int, [_i64]),
     "tp_reduce_partials": (_int, [ctypes.POINTER(ctypes.c_void_p), _int, _vp, _vp, _i64, _i64, _i64,
                                   _i64, _int, _vp]),
     "tp_bias_act": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _int, _int, _int, _vp]),
@@ -391,6 +401,64 @@ def tp_mlp_bwd(dZ, X, A_i, B_i, U_i, Y_i, dU_i, dB_i, db, dXp_i, dA_i, da_i, acc
         _ptr(db), _ptr(dXp_i), _ptr(dA_i), _ptr(da_i), T, h, F, _ld(dZ), _ld(X), _ld(A_i),
         _ld(B_i), _ld(U_i), _ld(Y_i), _ld(dU_i), _ld(dXp_i), _ld(dB_i), _ld(dA_i),
         int(bool(accumulate)), _dt(dZ), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
+
+
+def tp_mlp_step_workspace_size(T: int, h: int, F: int, p: int, dt: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_mlp_step_workspace_size",
+           lib().tp_mlp_step_workspace_size(T, h, F, p, dt, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_mlp_step_plan(T: int, h: int, F: int, p: int, dt: int) -> bool:
+    """Whether tp_mlp_step runs these shapes in its two persistent launches."""
+    f = ctypes.c_int(0)
+    _check("tp_mlp_step_plan", lib().tp_mlp_step_plan(T, h, F, p, dt, ctypes.byref(f)))
+    return bool(f.value)
+
+
+def tp_set_wait_limit(polls: int = 0) -> None:
+    """Test hook: polls before a dependency wait of tp_mlp_step gives up (0:
+    the default; negative: at the first unmet check), for this thread."""
+    _check("tp_set_wait_limit", lib().tp_set_wait_limit(int(polls)))
+
+
+def tp_mlp_step(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, workspace,
+                stream=None, part="step"):
+    """The MLP step of all p shards (layouts in include/tp_mlp.h): U, Y, dU
+    [T, p*F]; Zp, dXp fp32 [p, T, h]; dB fp32 [p*F, h]; dA fp32 [h, p*F].
+    part "rows" or "wgrad" runs tp_mlp_step_rows / tp_mlp_step_wgrad."""
+    fn = {"step": "tp_mlp_step", "rows": "tp_mlp_step_rows", "wgrad": "tp_mlp_step_wgrad"}[part]
+    chk = _Operands(fn)
+    chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
+    T, h = X.shape
+    dts, f32 = (X.dtype,), _torch_dtypes("f32")
+    if Zp is None or Zp.dim() != 3:
+        raise ValueError("tp_mlp_step: Zp must be a [p, T, h] tensor")
+    p = Zp.shape[0]
+    chk("A", A, (h, _shape2(A)[1]), dts)
+    pF = A.shape[1]
+    if pF % p:
+        raise ValueError(f"tp_mlp_step: A's {pF} columns do not split into {p} shards")
+    F = pF // p
+    chk("a", a, (pF,), dts, optional=True)("B", B, (pF, h), dts)("b", b, (h,), dts, optional=True)
+    chk("dZ", dZ, (T, h), dts)("U", U, (T, pF), dts)("Y", Y, (T, pF), dts)
+    chk("dU", dU, (T, pF), dts)("Z", Z, (T, h), dts)("dX", dX, (T, h), dts)
+    for name, t in (("Zp", Zp), ("dXp", dXp)):
+        chk(name, t, (p, T, h), f32)
+        if not t.is_contiguous():
+            raise ValueError(f"tp_mlp_step: {name} must be contiguous [p, T, h]")
+    chk("dB", dB, (pF, h), f32)("db", db, (h,), f32, optional=True)
+    chk("dA", dA, (h, pF), f32)("da", da, (pF,), f32, optional=True)
+    _check_ws(chk, workspace)
+    chk.done(stream)
+    if _ld(U) != _ld(Y) or _ld(U) != _ld(dU):
+        raise ValueError("tp_mlp_step: U, Y and dU must share a row stride")
+    _check(fn, getattr(lib(), fn)(
+        _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(b), _ptr(dZ), _ptr(U), _ptr(Y), _ptr(Zp),
+        _ptr(Z), _ptr(dU), _ptr(dB), _ptr(db), _ptr(dA), _ptr(da), _ptr(dXp), _ptr(dX),
+        T, h, F, p, _ld(X), _ld(A), _ld(B), _ld(dZ), _ld(U), _ld(Z), _ld(dX), _ld(dB), _ld(dA),
+        _dt(X), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_reduce_partials(partials, bias, out, stream=None):

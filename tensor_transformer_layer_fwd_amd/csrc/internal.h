@@ -139,6 +139,62 @@ struct AttnBwdParams {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
+// The MLP step of p shards in two persistent launches (mlp_step.hip).
+// Launch A runs, per XCD, a queue over the XCD's own token rows: every
+// shard's fc1 forward (bias + GeLU) and fc2 forward partial, the sum over
+// shards, every shard's fc2 dgrad (GeLU derivative, column partials of dU_i)
+// and fc1 dgrad partial, the sum of the dX partials and the first pass of db.
+// Launch B runs every shard's two weight gradients as stream-K units inside
+// each XCD, then the second pass of the bias gradients.
+struct StepParams {
+  // operands, row strides in elements (bf16 unless noted)
+  const void* x;       // X [T, h], ld_x
+  const void* a;       // A [h, p*F], ld_a (shard i: columns i*F ..)
+  const void* bias_a;  // [p*F] or null
+  const void* b;       // B [p*F, h], ld_b (shard i: rows i*F ..)
+  const void* bias_b;  // [h] or null
+  const void* dz;      // dZ [T, h], ld_dz
+  void* u;             // U, Y, dU [T, p*F], ld_u (shard i: columns i*F ..)
+  void* y;
+  void* du;
+  float* zp;           // Zp, dXp fp32 [p, T, h], compact
+  float* dxp;
+  void* z;             // Z [T, h], ld_z
+  void* dx;            // dX [T, h], ld_dx
+  float* dbw;          // dB fp32 [p*F, h], ld_dbw (shard i: rows i*F ..)
+  float* dbias_b;      // db fp32 [h], or null
+  float* daw;          // dA fp32 [h, p*F], ld_daw (shard i: columns i*F ..)
+  float* dbias_a;      // da fp32 [p*F], or null
+  int64_t T, h, F;
+  int p;
+  int64_t ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_dbw, ld_daw;
+  // workspace
+  unsigned* err;       // nonzero after a dependency wait gave up
+  unsigned long long* clk;  // block 0 of launch A: s_memtime and s_memrealtime, start and end
+  unsigned* ctr;       // counters (mlp_step.hip)
+  float* cs_da;        // p x [T/128, F] column partials of dU_i
+  float* cs_db;        // [T/64, h] column partials of dZ
+  float* parts;        // xcds x units_b partial tiles of 128 x 128 floats
+  int xcds, rb, rbx;   // XCDs; token rows of a launch-A unit; its row blocks per XCD
+  int units_a;         // queue length of launch A per XCD
+  int tiles_b, len_b, units_b;  // per XCD: weight-gradient tiles, K-tiles per unit, units
+  int pass2_b;         // bias-gradient second-pass units per XCD
+  long long spin;      // polls before a dependency wait gives up
+};
+// Whether launch_mlp_step supports these shapes (the bf16 tiles, one row slab
+// per XCD); and the workspace it needs (0 when unsupported).
+bool mlp_step_supported(int64_t T, int64_t h, int64_t F, int p);
+size_t mlp_step_workspace_bytes(int64_t T, int64_t h, int64_t F, int p);
+// Fills the shapes, queue lengths and workspace pointers of s (operands set by
+// the caller) and enqueues both launches.
+// phases: bit 0 launch A (forward, sums, data gradients), bit 1 launch B
+// (weight and bias gradients).
+hipError_t launch_mlp_step(StepParams s, void* workspace, int phases, hipStream_t stream);
+// Polls before a dependency wait of launch_mlp_step gives up, for the calling
+// thread: 0 restores the default (about 0.25 s), a negative value gives up at
+// the first unsatisfied check.
+void set_step_wait_limit(long long polls);
+
 // Reduction over shards.
 constexpr int kMaxPartials = 16;
 struct ReduceParams {
@@ -187,6 +243,7 @@ hipError_t launch_gemm_fp8(const GemmParams& p, const SplitPlan& plan, hipStream
 int fp8_pipe_epilogue(const GemmParams& p);  // kEpiNone: not supported
 // Forced tile / split for later plans (tile 0: none); false for invalid values.
 bool set_gemm_override(int tile, int splitk);
+int forced_tile();  // the calling thread's forced tile (0: none)
 size_t colsum_workspace_bytes(int64_t T, int64_t N);
 
 // Launch per plan: the planned pipelined tile when the operands allow it,
@@ -199,7 +256,11 @@ hipError_t launch_gemm_bf16_general(const GemmParams& p, const SplitPlan& plan, 
 // fp32 store (or split-K partial), bf16 store, bias + GeLU saving the
 // pre-activation, and GeLU derivative from the saved pre-activation. All
 // outputs 16-byte aligned with row strides a multiple of 8.
-enum EpiKind : int { kEpiNone = -1, kEpiF32 = 0, kEpiBF16 = 1, kEpiBiasGelu = 2, kEpiDGelu = 3 };
+enum EpiKind : int { kEpiNone = -1, kEpiF32 = 0, kEpiBF16 = 1, kEpiBiasGelu = 2, kEpiDGelu = 3,
+                     // fp32 partial tile for a later block of the same tile
+                     kEpiF32Part = 4,
+                     // fp32 store of the earlier partial tiles plus this block's sums
+                     kEpiF32Fix = 5 };
 int pipe_epilogue_kind(const GemmParams& p);  // kEpiNone: use the general kernel
 hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int ek,
                                  hipStream_t s);

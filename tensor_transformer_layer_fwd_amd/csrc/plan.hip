@@ -91,6 +91,8 @@ SplitPlan plan_model(int64_t M, int64_t N, int64_t K, bool allow_split);
 
 }  // namespace
 
+int forced_tile() { return g_force_tile; }
+
 bool set_gemm_override(int tile, int splitk) {
   if ((tile != 0 && !find_tile(tile)) || splitk < 1 || splitk > 16) return false;
   g_force_tile = tile;

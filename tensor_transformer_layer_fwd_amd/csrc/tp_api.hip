@@ -587,6 +587,189 @@ int tp_linear_bwd(const void* dOut, const void* W, const void* U, tp_act act, co
                              workspace, workspace_bytes, stream);
 }
 
+int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt,
+                               size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(F) || p < 1 || p > kMaxPartials) return TP_ERR_SHAPE;
+  size_t fb = 0, w2 = 0, w1 = 0;
+  int st = tp_mlp_bwd_workspace_size(T, h, F, dt, &fb);
+  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, F, h, dt, &w2);
+  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, h, F, dt, &w1);
+  if (st != TP_OK) return st;
+  fb = fb > w2 ? fb : w2;
+  fb = fb > w1 ? fb : w1;
+  const size_t fused = dt == TP_BF16 ? mlp_step_workspace_bytes(T, h, F, p) : 0;
+  *bytes = fused > fb ? fused : fb;
+  return TP_OK;
+}
+
+int tp_mlp_step_plan(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt, int* fused) {
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(F) || p < 1 || p > kMaxPartials) return TP_ERR_SHAPE;
+  if (fused) *fused = dt == TP_BF16 && mlp_step_supported(T, h, F, p);
+  return TP_OK;
+}
+
+int tp_set_wait_limit(int64_t polls) {
+  set_step_wait_limit(polls);
+  return TP_OK;
+}
+
+static int mlp_step_impl(const void* X, const void* A, const void* a, const void* B, const void* b,
+                const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                int phases) {
+  if (!X || !A || !B || !dZ || !U || !Y || !Zp || !Z || !dU || !dB || !dA || !dXp || !dX)
+    return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(F) || p < 1 || p > kMaxPartials) return TP_ERR_SHAPE;
+  const int64_t pF = static_cast<int64_t>(p) * F;
+  if (!dim_ok(pF) || T * h > kMaxDim * 4 || ld_x < h || ld_a < pF || ld_b < h || ld_dz < h ||
+      ld_u < pF || ld_z < h || ld_dx < h || ld_db < h || ld_da < pF)
+    return TP_ERR_SHAPE;
+  size_t need = 0;
+  int st = tp_mlp_step_workspace_size(T, h, F, p, dt, &need);
+  if (st != TP_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return TP_ERR_WORKSPACE;
+  const size_t es = dt == TP_BF16 ? 2 : 4;
+  auto row_ok = [](const void* q, int64_t ld, size_t e) {
+    return aligned(q, 16) && (ld * static_cast<int64_t>(e)) % 16 == 0;
+  };
+  const bool fused = dt == TP_BF16 && mlp_step_supported(T, h, F, p) &&
+                     row_ok(X, ld_x, es) && row_ok(A, ld_a, es) && row_ok(B, ld_b, es) &&
+                     row_ok(dZ, ld_dz, es) && row_ok(U, ld_u, es) && row_ok(Y, ld_u, es) &&
+                     row_ok(dU, ld_u, es) && row_ok(Z, ld_z, es) && row_ok(dX, ld_dx, es) &&
+                     row_ok(Zp, h, 4) && row_ok(dXp, h, 4) && row_ok(dB, ld_db, 4) &&
+                     row_ok(dA, ld_da, 4) && (!a || aligned(a, 16)) && (!b || aligned(b, 16)) &&
+                     aligned(workspace, 256);
+  if (fused) {
+    StepParams s{};
+    s.x = X;
+    s.a = A;
+    s.bias_a = a;
+    s.b = B;
+    s.bias_b = b;
+    s.dz = dZ;
+    s.u = U;
+    s.y = Y;
+    s.du = dU;
+    s.zp = Zp;
+    s.dxp = dXp;
+    s.z = Z;
+    s.dx = dX;
+    s.dbw = dB;
+    s.dbias_b = db;
+    s.daw = dA;
+    s.dbias_a = da;
+    s.T = T;
+    s.h = h;
+    s.F = F;
+    s.p = p;
+    s.ld_x = ld_x;
+    s.ld_a = ld_a;
+    s.ld_b = ld_b;
+    s.ld_dz = ld_dz;
+    s.ld_u = ld_u;
+    s.ld_z = ld_z;
+    s.ld_dx = ld_dx;
+    s.ld_dbw = ld_db;
+    s.ld_daw = ld_da;
+    return hip_status(launch_mlp_step(s, workspace, phases, stream));
+  }
+  // the same step as one call per product. Both phases: every shard's
+  // forward, the sum, every shard's backward (tp_mlp_bwd, both layers' two
+  // gradients), the sum of the dX partials. Phase 1 alone: the forward, the
+  // sum and the data gradients; phase 2 alone: the weight and bias gradients.
+  const float* zparts[kMaxPartials];
+  const float* dparts[kMaxPartials];
+  auto Ai = [&](int i) { return static_cast<const char*>(A) + i * F * es; };
+  auto Bi = [&](int i) { return static_cast<const char*>(B) + i * F * ld_b * es; };
+  auto Ui = [&](int i) { return static_cast<char*>(U) + i * F * es; };
+  auto Yi = [&](int i) { return static_cast<char*>(Y) + i * F * es; };
+  auto dUi = [&](int i) { return static_cast<char*>(dU) + i * F * es; };
+  for (int i = 0; i < p; ++i) {
+    zparts[i] = Zp + i * T * h;
+    dparts[i] = dXp + i * T * h;
+  }
+  if (phases & 1) {
+    for (int i = 0; i < p; ++i) {
+      const void* ai = a ? static_cast<const char*>(a) + i * F * es : nullptr;
+      st = tp_column_linear_fwd(X, Ai(i), ai, Yi(i), Ui(i), T, h, F, ld_x, ld_a, ld_u, dt,
+                                TP_ACT_GELU_TANH, stream);
+      if (st != TP_OK) return st;
+      st = tp_row_linear_fwd_partial(Yi(i), Bi(i), Zp + i * T * h, T, F, h, ld_u, ld_b, h, dt,
+                                     stream);
+      if (st != TP_OK) return st;
+    }
+    st = tp_reduce_partials(zparts, p, b, Z, T, h, h, ld_z, dt, stream);
+    if (st != TP_OK) return st;
+  }
+  if (phases == 3) {
+    for (int i = 0; i < p; ++i) {
+      st = tp_mlp_bwd(dZ, X, Ai(i), Bi(i), Ui(i), Yi(i), dUi(i), dB + i * F * ld_db,
+                      i == 0 ? db : nullptr, dXp + i * T * h, dA + i * F, da ? da + i * F : nullptr,
+                      T, h, F, ld_dz, ld_x, ld_a, ld_b, ld_u, ld_u, ld_u, h, ld_db, ld_da, 0, dt,
+                      workspace, workspace_bytes, stream);
+      if (st != TP_OK) return st;
+    }
+    return tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
+  }
+  if (phases & 1) {
+    for (int i = 0; i < p; ++i) {
+      st = tp_linear_bwd_dgrad(dZ, Bi(i), Ui(i), TP_ACT_GELU_TANH, dUi(i), T, F, h, ld_dz, ld_b,
+                               ld_u, ld_u, dt, dt, stream);
+      if (st != TP_OK) return st;
+      st = tp_linear_bwd_dgrad(dUi(i), Ai(i), nullptr, TP_ACT_NONE, dXp + i * T * h, T, h, F,
+                               ld_u, ld_a, h, h, dt, TP_F32, stream);
+      if (st != TP_OK) return st;
+    }
+    st = tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
+    if (st != TP_OK) return st;
+  }
+  if (phases & 2) {
+    for (int i = 0; i < p; ++i) {
+      st = tp_linear_bwd_wgrad(Yi(i), dZ, dB + i * F * ld_db, i == 0 ? db : nullptr, T, F, h,
+                               ld_u, ld_dz, ld_db, 0, dt, workspace, workspace_bytes, stream);
+      if (st != TP_OK) return st;
+      st = tp_linear_bwd_wgrad(X, dUi(i), dA + i * F, da ? da + i * F : nullptr, T, h, F, ld_x,
+                               ld_u, ld_da, 0, dt, workspace, workspace_bytes, stream);
+      if (st != TP_OK) return st;
+    }
+  }
+  return TP_OK;
+}
+
+int tp_mlp_step(const void* X, const void* A, const void* a, const void* B, const void* b,
+                const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, 3);
+}
+
+int tp_mlp_step_rows(const void* X, const void* A, const void* a, const void* B, const void* b,
+                const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, 1);
+}
+
+int tp_mlp_step_wgrad(const void* X, const void* A, const void* a, const void* B, const void* b,
+                const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, 2);
+}
+
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
                        int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, tp_dtype out_dt,
                        hipStream_t stream) {

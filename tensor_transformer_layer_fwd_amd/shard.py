@@ -64,7 +64,7 @@ class ShardStep:
     """Device buffers of one workload and the calls of one fwd+bwd step."""
 
     def __init__(self, cfg, inputs: dict, device="cuda", recompute=False, fp8=False,
-                 fused_bwd=True, attn_core=False):
+                 fused_bwd=True, attn_core=False, step_call=True):
         self.cfg = cfg
         self.attn_core = bool(attn_core and cfg.attn)
         if self.attn_core and (cfg.dtype != "bf16" or cfg.heads % cfg.p or
@@ -92,19 +92,46 @@ class ShardStep:
         act = dict(device=self.device, dtype=self.dt)
         shards = cfg.shards
         ws = 0
+        # the whole MLP step of every shard in one tp_mlp_step call
+        self.step_call = bool(step_call and cfg.mlp and len(shards) == cfg.p and self.fused_bwd
+                              and not self.recompute and not self.fp8)
         if cfg.mlp:
             F = cfg.F
-            for i in shards:
-                self.out[f"U_{i}"] = torch.empty(T, F, **act)
-                if not self.recompute:
-                    self.out[f"Y_{i}"] = torch.empty(T, F, **act)
-                self.out[f"Zp_{i}"] = torch.empty(T, h, **f32)
-                self.out[f"dU_{i}"] = torch.empty(T, F, **act)
-                self.out[f"dB_{i}"] = torch.empty(F, h, **f32)
-                self.out[f"dA_{i}"] = torch.empty(h, F, **f32)
-                self.out[f"dXp_{i}"] = torch.empty(T, h, **f32)
+            if len(shards) == cfg.p and not self.recompute:
+                # every shard's tensors as blocks of one buffer each, in the
+                # layouts of tp_mlp_step (U_i = U[:, iF:(i+1)F], Zp_i = Zp[i], ...);
+                # the recompute step keeps a compact transient Y, so its U_i
+                # (which shares Y's row stride) stays a tensor of its own
+                p = cfg.p
+                self.mlp = {"U": torch.empty(T, p * F, **act), "dU": torch.empty(T, p * F, **act),
+                            "Zp": torch.empty(p, T, h, **f32), "dXp": torch.empty(p, T, h, **f32),
+                            "dB": torch.empty(p * F, h, **f32), "dA": torch.empty(h, p * F, **f32),
+                            "Y": torch.empty(T, p * F, **act)}
                 if cfg.has_bias:
-                    self.out[f"da_{i}"] = torch.empty(F, **f32)
+                    self.mlp["da"] = torch.empty(p * F, **f32)
+                for i in shards:
+                    cols = slice(i * F, (i + 1) * F)
+                    self.out[f"U_{i}"] = self.mlp["U"][:, cols]
+                    self.out[f"Y_{i}"] = self.mlp["Y"][:, cols]
+                    self.out[f"Zp_{i}"] = self.mlp["Zp"][i]
+                    self.out[f"dU_{i}"] = self.mlp["dU"][:, cols]
+                    self.out[f"dB_{i}"] = self.mlp["dB"][cols]
+                    self.out[f"dA_{i}"] = self.mlp["dA"][:, cols]
+                    self.out[f"dXp_{i}"] = self.mlp["dXp"][i]
+                    if cfg.has_bias:
+                        self.out[f"da_{i}"] = self.mlp["da"][cols]
+            else:
+                for i in shards:
+                    self.out[f"U_{i}"] = torch.empty(T, F, **act)
+                    if not self.recompute:
+                        self.out[f"Y_{i}"] = torch.empty(T, F, **act)
+                    self.out[f"Zp_{i}"] = torch.empty(T, h, **f32)
+                    self.out[f"dU_{i}"] = torch.empty(T, F, **act)
+                    self.out[f"dB_{i}"] = torch.empty(F, h, **f32)
+                    self.out[f"dA_{i}"] = torch.empty(h, F, **f32)
+                    self.out[f"dXp_{i}"] = torch.empty(T, h, **f32)
+                    if cfg.has_bias:
+                        self.out[f"da_{i}"] = torch.empty(F, **f32)
             if self.recompute:
                 # the forward's Y_i, then the backward's recomputed Y_i, shard by shard
                 self.out["Yt"] = torch.empty(T, F, **act)
@@ -114,6 +141,12 @@ class ShardStep:
                 self.out["Z"] = torch.empty(T, h, **act)
                 self.out["dX"] = torch.empty(T, h, **act)
             ws = max(ws, L.tp_mlp_bwd_workspace_size(T, h, F, self.tp_dt))
+            if self.step_call:
+                # tp_mlp_step's own workspace: its queue counters must stay
+                # zero between calls, so no other call may use it as scratch
+                self.step_ws = torch.zeros(
+                    max(L.tp_mlp_step_workspace_size(T, h, F, cfg.p, self.tp_dt), 256),
+                    dtype=torch.uint8, device=self.device)
         if cfg.attn:
             Q, O = cfg.Q, cfg.O
             for i in shards:
@@ -137,7 +170,8 @@ class ShardStep:
                      L.tp_linear_bwd_workspace_size(T, h, Q, self.tp_dt))
         if self.fp8:
             ws = max(ws, self._fp8_buffers())
-        # one scratch buffer, shared by the wgrad calls (they run in order on one stream)
+        # one scratch buffer, shared by the per-product calls (they run in
+        # order on one stream)
         self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=self.device)
 
     def _fp8_buffers(self):
@@ -316,15 +350,24 @@ class ShardStep:
         if "dXq" in o:
             L.tp_reduce_partials([o[f"dXqp_{i}"] for i in cfg.shards], None, o["dXq"])
 
+    def mlp_step(self, part="step"):
+        """Every shard's MLP forward and backward and both sums in one call."""
+        cfg, o, inp, m = self.cfg, self.out, self.inp, self.mlp
+        L.tp_mlp_step(inp["X"], inp["A"], inp.get("a"), inp["B"], inp.get("b"), inp["dZ"],
+                      m["U"], m["Y"], m["Zp"], o["Z"], m["dU"], m["dB"], o.get("db"), m["dA"],
+                      m.get("da"), m["dXp"], o["dX"], self.step_ws, part=part)
+
     def run_eager(self):
         """Enqueue one fwd+bwd step on the current stream."""
         if self.cfg.attn:
             self.attn_forward()
-        if self.cfg.mlp:
+        if self.step_call:
+            self.mlp_step()
+        elif self.cfg.mlp:
             self.mlp_forward_fp8() if self.fp8 else self.mlp_forward()
         if self.cfg.attn:
             self.attn_backward()
-        if self.cfg.mlp:
+        if self.cfg.mlp and not self.step_call:
             self.mlp_backward_fp8() if self.fp8 else self.mlp_backward()
 
     def capture(self):

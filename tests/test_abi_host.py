@@ -496,3 +496,47 @@ def test_binding_rejects_mismatched_operands():
     with pytest.raises(ValueError, match="dOut is required"):
         L.tp_fp8_linear_bwd_wgrad(z(F, T, dtype=u8), z(h, T, dtype=u8), z(1, dtype=f32),
                                   z(1, dtype=f32), z(F, h, dtype=f32), dbias=z(h, dtype=f32))
+
+
+def test_mlp_step_queries(lib):
+    """tp_mlp_step's fused-path and workspace queries (shape-only, host)."""
+    bf = L.TP_BF16
+    assert L.tp_mlp_step_plan(4096, 768, 1536, 2, bf)           # GPT-2-small, p = 2
+    assert L.tp_mlp_step_plan(6144, 1024, 1024, 4, bf)          # the ~350M layer's MLP
+    assert not L.tp_mlp_step_plan(680, 768, 1536, 2, bf)        # T not a multiple of 1024
+    assert not L.tp_mlp_step_plan(2048, 12288, 6144, 1, bf)     # 175B-class: products too big
+    assert not L.tp_mlp_step_plan(4096, 768, 1536, 2, L.TP_F32)
+    fused = L.tp_mlp_step_workspace_size(4096, 768, 1536, 2, bf)
+    per_product = L.tp_mlp_bwd_workspace_size(4096, 768, 1536, bf)
+    assert fused >= per_product and fused % 256 == 0
+    # column partials of dU_i and dZ and the stream-K partial tiles are part of it
+    assert fused >= 2 * 32 * 1536 * 4 + 64 * 768 * 4
+    assert L.tp_mlp_step_workspace_size(680, 768, 1536, 2, bf) >= \
+        L.tp_mlp_bwd_workspace_size(680, 768, 1536, bf)
+    out = ctypes.c_size_t(0)
+    assert lib.tp_mlp_step_workspace_size(4096, 768, 1536, 0, bf, ctypes.byref(out)) == -2
+    assert lib.tp_mlp_step_workspace_size(4096, 768, 1536, 17, bf, ctypes.byref(out)) == -2
+    assert lib.tp_mlp_step_workspace_size(4096, 768, 1536, 2, 5, ctypes.byref(out)) == -3
+    assert lib.tp_mlp_step_workspace_size(4096, 768, 1536, 2, bf, None) == -1
+    assert lib.tp_set_wait_limit(0) == 0
+
+
+def test_mlp_step_validation(lib):
+    """tp_mlp_step and its halves reject bad arguments before any launch."""
+    F_ = FAKE
+    for fn in (lib.tp_mlp_step, lib.tp_mlp_step_rows, lib.tp_mlp_step_wgrad):
+        def call(*, X=F_, dX=F_, T=4096, h=768, F=1536, p=2, ld_a=3072, ld_u=3072, dt=1,
+                 ws=F_, wsb=1 << 30):
+            return fn(X, F_, None, F_, None, F_, F_, F_, F_, F_, F_, F_, None, F_, None, F_, dX,
+                      T, h, F, p, 768, ld_a, 768, 768, ld_u, 768, 768, 768, 3072, dt, ws, wsb,
+                      None)
+        assert call(X=None) == -1
+        assert call(dX=None) == -1
+        assert call(T=0) == -2
+        assert call(p=0) == -2
+        assert call(p=17) == -2
+        assert call(ld_a=3071) == -2      # below p * F
+        assert call(ld_u=1536) == -2
+        assert call(dt=4) == -3
+        assert call(ws=None, wsb=0) == -5
+        assert call(wsb=1024) == -5
