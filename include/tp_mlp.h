@@ -67,7 +67,9 @@ typedef enum {
   TP_ERR_DTYPE = -3,     /* unknown dtype or unsupported dtype combination */
   TP_ERR_ACT = -4,       /* unknown activation */
   TP_ERR_WORKSPACE = -5, /* workspace smaller than tp_linear_bwd_wgrad_workspace_size */
-  TP_ERR_HIP = -6        /* a HIP launch failed; see tp_last_hip_error() */
+  TP_ERR_HIP = -6,       /* a HIP launch failed; see tp_last_hip_error() */
+  TP_ERR_SCRATCH = -7    /* tp_linear_bwd_wgrad_noalloc: the shape needs more than
+                            TP_NOALLOC_SCRATCH_BYTES of scratch */
 } tp_status;
 
 typedef enum { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
@@ -185,6 +187,33 @@ int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbia
 /* Scratch bytes tp_linear_bwd_wgrad needs for (T, k, n, dt); pure host function. */
 int tp_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, tp_dtype dt,
                                        size_t* bytes);
+
+/* Bytes of the library's own device scratch array behind
+ * tp_linear_bwd_wgrad_noalloc (one such array per GPU). */
+#define TP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * tp_linear_bwd_wgrad for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. Same arguments, layouts, results and kernels as
+ * tp_linear_bwd_wgrad, less the workspace: the split-K partials and the
+ * column-sum partials live in a scratch array of TP_NOALLOC_SCRATCH_BYTES
+ * that the library holds in static device memory on every GPU it is loaded
+ * on, until the process ends. Nothing is allocated or freed by this call.
+ *
+ * The array used is the one of the current device (hipGetDevice); stream must
+ * belong to that device. The first call on a device looks up that device's
+ * address of the array once. No byte of the array needs to hold any value on
+ * entry: every byte the kernels read was written earlier by the same call.
+ *
+ * Calls that may overlap on one GPU race on its array: serialise them (one
+ * stream, or events). Returns TP_ERR_SCRATCH, launching nothing, when
+ * tp_linear_bwd_wgrad_workspace_size(T, k, n, dt) exceeds
+ * TP_NOALLOC_SCRATCH_BYTES, and the errors of tp_linear_bwd_wgrad otherwise.
+ */
+int tp_linear_bwd_wgrad_noalloc(const void* In, const void* dOut, float* dW, float* dbias,
+                                int64_t T, int64_t k, int64_t n, int64_t ld_in, int64_t ld_dout,
+                                int64_t ld_dw, int accumulate, tp_dtype dt, hipStream_t stream);
 
 /*
  * The whole backward of one linear layer of the shard, the data gradient and

@@ -20,7 +20,9 @@ TP_OK = 0
 TP_F32, TP_BF16 = 0, 1
 TP_ACT_NONE, TP_ACT_GELU_TANH = 0, 1
 STATUS = {0: "TP_OK", -1: "TP_ERR_NULL", -2: "TP_ERR_SHAPE", -3: "TP_ERR_DTYPE",
-          -4: "TP_ERR_ACT", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP"}
+          -4: "TP_ERR_ACT", -5: "TP_ERR_WORKSPACE", -6: "TP_ERR_HIP",
+          -7: "TP_ERR_SCRATCH"}
+TP_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every function declared in include/tp_mlp.h, with its ctypes signature.
 _vp, _i64, _int, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
@@ -33,6 +35,8 @@ SIGNATURES = {
                                    _i64, _int, _int, _vp]),
     "tp_linear_bwd_wgrad": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _int,
                                    _int, _vp, _sz, _vp]),
+    "tp_linear_bwd_wgrad_noalloc": (_int, [_vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                           _i64, _int, _int, _vp]),
     "tp_linear_bwd_wgrad_workspace_size": (_int, [_i64, _i64, _i64, _int,
                                                   ctypes.POINTER(ctypes.c_size_t)]),
     "tp_linear_bwd": (_int, [_vp, _vp, _vp, _int, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
@@ -332,6 +336,23 @@ def tp_linear_bwd_wgrad(In, dOut, dW, dbias=None, accumulate=False, workspace=No
     _check("tp_linear_bwd_wgrad", lib().tp_linear_bwd_wgrad(
         _ptr(In), _ptr(dOut), _ptr(dW), _ptr(dbias), T, k, n, _ld(In), _ld(dOut), _ld(dW),
         int(bool(accumulate)), _dt(In), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
+
+
+def tp_linear_bwd_wgrad_noalloc(In, dOut, dW, dbias=None, accumulate=False, stream=None):
+    """tp_linear_bwd_wgrad on the library's static per-GPU scratch array: no
+    workspace argument, nothing allocated. Calls that may overlap on one GPU
+    race on that array."""
+    chk = _Operands("tp_linear_bwd_wgrad_noalloc")
+    chk("In", In, _shape2(In), _torch_dtypes("bf16", "f32"))
+    T, k = In.shape
+    chk("dOut", dOut, (T, _shape2(dOut)[1]), (In.dtype,))
+    n = dOut.shape[1]
+    f32 = _torch_dtypes("f32")
+    chk("dW", dW, (k, n), f32)("dbias", dbias, (n,), f32, optional=True)
+    chk.done(stream)
+    _check("tp_linear_bwd_wgrad_noalloc", lib().tp_linear_bwd_wgrad_noalloc(
+        _ptr(In), _ptr(dOut), _ptr(dW), _ptr(dbias), T, k, n, _ld(In), _ld(dOut), _ld(dW),
+        int(bool(accumulate)), _dt(In), _stream(stream)))
 
 
 def tp_linear_bwd_workspace_size(T: int, k: int, n: int, dt: int) -> int:

@@ -2,6 +2,9 @@
 // runs before the first HIP call, so a rejected call launches nothing.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tp_mlp.h"
 #include "internal.h"
 
@@ -325,6 +328,41 @@ bool rider_for(const PairSetup& q, PairRider* r) {
 
 }  // namespace
 
+// Scratch of tp_linear_bwd_wgrad_noalloc: one array per GPU, created with the
+// code object. In host code `scratch` only names the symbol; kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[TP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 256;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+int current_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxScratchDevices) return hip_status(hipErrorInvalidDevice);
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return hip_status(e);
+      if (!ptr) return hip_status(hipErrorInvalidSymbol);
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return TP_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int tp_column_linear_fwd(const void* X, const void* A_i, const void* bias_i, void* Y_i,
@@ -454,6 +492,24 @@ int tp_linear_bwd_wgrad(const void* In, const void* dOut, float* dW, float* dbia
       dOut, dbias, T, n, ld_dout, dt, accumulate,
       dbias ? reinterpret_cast<float*>(static_cast<char*>(workspace) + split_bytes) : nullptr);
   return run_gemm(p, dt, true, split_bytes, stream, dbias ? &c : nullptr);
+}
+
+int tp_linear_bwd_wgrad_noalloc(const void* In, const void* dOut, float* dW, float* dbias,
+                                int64_t T, int64_t k, int64_t n, int64_t ld_in, int64_t ld_dout,
+                                int64_t ld_dw, int accumulate, tp_dtype dt, hipStream_t stream) {
+  if (!In || !dOut || !dW) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(k) || !dim_ok(n)) return TP_ERR_SHAPE;
+  if (ld_in < k || ld_dout < n || ld_dw < n) return TP_ERR_SHAPE;
+  size_t need = 0;
+  int st = tp_linear_bwd_wgrad_workspace_size(T, k, n, dt, &need);
+  if (st != TP_OK) return st;
+  if (need > TP_NOALLOC_SCRATCH_BYTES) return TP_ERR_SCRATCH;
+  void* ws = nullptr;
+  st = current_scratch(&ws);
+  if (st != TP_OK) return st;
+  return tp_linear_bwd_wgrad(In, dOut, dW, dbias, T, k, n, ld_in, ld_dout, ld_dw, accumulate, dt,
+                             ws, TP_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int tp_linear_bwd_workspace_size(int64_t T, int64_t k, int64_t n, tp_dtype dt, size_t* bytes) {
@@ -1120,6 +1176,8 @@ const char* tp_status_string(int status) {
       return "TP_ERR_ACT: unknown activation";
     case TP_ERR_WORKSPACE:
       return "TP_ERR_WORKSPACE: workspace missing or too small";
+    case TP_ERR_SCRATCH:
+      return "TP_ERR_SCRATCH: shape needs more than the library's static scratch";
     case TP_ERR_HIP:
       return "TP_ERR_HIP: a HIP launch failed";
     default:

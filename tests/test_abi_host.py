@@ -540,3 +540,24 @@ def test_mlp_step_validation(lib):
         assert call(dt=4) == -3
         assert call(ws=None, wsb=0) == -5
         assert call(wsb=1024) == -5
+
+
+def test_noalloc_wgrad_rejects_shape_beyond_scratch(lib):
+    # the size check runs before any HIP call, so this needs no GPU; the
+    # pointers are never dereferenced
+    T, k, n = 1 << 20, 256, 1024
+    assert L.tp_linear_bwd_wgrad_workspace_size(T, k, n, L.TP_BF16) > L.TP_NOALLOC_SCRATCH_BYTES
+    fake = 1 << 20
+    st = lib.tp_linear_bwd_wgrad_noalloc(fake, fake, fake, None, T, k, n, k, n, n, 0,
+                                         L.TP_BF16, None)
+    assert L.STATUS[st] == "TP_ERR_SCRATCH"
+    assert L.tp_status_string(st).startswith("TP_ERR_SCRATCH")
+    assert lib.tp_linear_bwd_wgrad_noalloc(None, fake, fake, None, 5, 5, 5, 5, 5, 5, 0,
+                                           L.TP_BF16, None) == -1
+    assert lib.tp_linear_bwd_wgrad_noalloc(fake, fake, fake, None, 5, 5, 5, 4, 5, 5, 0,
+                                           L.TP_BF16, None) == -2
+    assert lib.tp_linear_bwd_wgrad_noalloc(fake, fake, fake, None, 5, 5, 5, 5, 5, 5, 0,
+                                           9, None) == -3
+    with open(HEADER) as f:
+        assert "#define TP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in f.read()
+    assert L.TP_NOALLOC_SCRATCH_BYTES == 32 << 20
