@@ -325,20 +325,23 @@ int tp_mlp_bwd_workspace_size(int64_t T, int64_t h, int64_t F, tp_dtype dt, size
  *
  * bf16, with the shapes tp_mlp_step_plan reports as fused (T a multiple of
  * 128 x the device's XCD count, h and F of 128, 16-byte aligned operands and
- * row strides), runs in two persistent launches: one over each XCD's own
- * token rows (forward, sums, data gradients), one for the weight gradients.
- * Any other shape or dtype runs the same step as the per-product calls.
+ * row strides), runs the forward, both sums and the data gradients in one
+ * persistent launch over each XCD's own token rows, then the weight and bias
+ * gradients of all shards as two products over the stacked shards
+ * (dB = Y^T dZ, dA = X^T dU, as tp_linear_bwd_wgrad). Any other shape or
+ * dtype runs the same step as the per-product calls.
  *
  * workspace: at least tp_mlp_step_workspace_size bytes, 256-byte aligned,
- * ZEROED BEFORE ITS FIRST USE (it holds the queues' counters, which every
- * call leaves zeroed again). It belongs to tp_mlp_step calls alone: no other
+ * ZEROED BEFORE ITS FIRST USE (it holds the queue's counters, which every
+ * call leaves zeroed again, ahead of the weight gradients' scratch). It belongs to tp_mlp_step calls alone: no other
  * call may use it as scratch between them (that would leave the counters
  * nonzero), and tp_mlp_step calls that share it must not overlap (enqueue them
  * on one stream). Its first 32-bit word is nonzero after a call
  * in which a dependency wait gave up (tp_set_wait_limit); that call's results
  * are then invalid, and the word stays set until the caller clears it.
- * Bytes 64..95 hold four 64-bit counters of the first launch's block 0: the
- * shader clock and the 100 MHz real-time clock at its start, then at its end.
+ * Bytes 64..95 hold four 64-bit counters of the persistent launch's block 0:
+ * the shader clock and the 100 MHz real-time clock at its start, then at its
+ * end.
  */
 int tp_mlp_step(const void* X, const void* A, const void* a, const void* B, const void* b,
                 const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
@@ -350,9 +353,9 @@ int tp_mlp_step(const void* X, const void* A, const void* a, const void* B, cons
 /*
  * The two halves of tp_mlp_step, same arguments: tp_mlp_step_rows computes
  * the forward, both sums and the data gradients (U, Y, Zp, Z, dU, dXp, dX;
- * the first launch), tp_mlp_step_wgrad the weight and bias gradients (dB, db,
- * dA, da; the second launch) from the U, Y and dU the first left. Calling
- * rows then wgrad on one stream is tp_mlp_step.
+ * the persistent launch), tp_mlp_step_wgrad the weight and bias gradients
+ * (dB, db, dA, da; the two products) from the Y and dU the first left.
+ * Calling rows then wgrad on one stream is tp_mlp_step.
  */
 int tp_mlp_step_rows(const void* X, const void* A, const void* a, const void* B, const void* b,
                      const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
@@ -374,13 +377,14 @@ int tp_mlp_step_wgrad(const void* X, const void* A, const void* a, const void* B
 int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt,
                                size_t* bytes);
 
-/* Whether tp_mlp_step runs these shapes in the two persistent launches
- * (*fused = 1, given aligned operands) or as per-product calls (0). */
+/* Whether tp_mlp_step runs these shapes in the persistent launch and the two
+ * stacked weight-gradient products (*fused = 1, given aligned operands) or as
+ * per-product calls (0). */
 int tp_mlp_step_plan(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt, int* fused);
 
 /*
  * Test hook: the number of polls after which a dependency wait of
- * tp_mlp_step's persistent launches gives up (setting the workspace's error
+ * tp_mlp_step's persistent launch gives up (setting the workspace's error
  * word), for calls made by the calling thread. 0 restores the default (about
  * a quarter of a second); a negative value gives up at the first check that
  * finds the dependency unmet. Every block still runs to its end.

@@ -432,7 +432,8 @@ def tp_mlp_step_workspace_size(T: int, h: int, F: int, p: int, dt: int) -> int:
 
 
 def tp_mlp_step_plan(T: int, h: int, F: int, p: int, dt: int) -> bool:
-    """Whether tp_mlp_step runs these shapes in its two persistent launches."""
+    """Whether tp_mlp_step runs these shapes fused: the persistent launch, then
+    the two stacked weight-gradient products."""
     f = ctypes.c_int(0)
     _check("tp_mlp_step_plan", lib().tp_mlp_step_plan(T, h, F, p, dt, ctypes.byref(f)))
     return bool(f.value)

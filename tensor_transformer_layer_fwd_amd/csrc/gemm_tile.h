@@ -292,12 +292,6 @@ __device__ __forceinline__ int xcd_group_rows(int c, int tiles_m, int tiles_n, i
   return 5 * cost <= 4 * base ? best : 8;
 }
 
-// Hook run by every thread of the block between a tile's K loop and its
-// epilogue (all copies done, the block synchronised): nothing by default.
-struct NoPre {
-  __device__ __forceinline__ void operator()() const {}
-};
-
 // F8 = 0: bf16 operands; F8 = 1 + fmt_a + 2 * fmt_b: FP8 codes (both operands
 // K-contiguous, BK = 128 codes), fmt 0 = E4M3, 1 = E5M2.
 // One output tile of a product: rows m0 .. m0+BM-1, columns n0 .. n0+BN-1,
@@ -306,10 +300,10 @@ struct NoPre {
 // only after its epilogue's last LDS access, so a caller that reuses the pool
 // synchronises first.
 template <int BM, int BN, int WM, int WN, int BK, int S, bool AK, bool BKC, int EK, int F8 = 0,
-          int POOL = 0, class Pre = NoPre>
+          int POOL = 0>
 __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_t m0,
                                                const int64_t n0, const int z, const int64_t kbeg,
-                                               const int nk, const Pre& pre = Pre{}) {
+                                               const int nk) {
   constexpr int NW = WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int FM = WTM / 32, FN = WTN / 32;
@@ -483,7 +477,6 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
   }
   wait_vmcnt<0>();
   block_sync();
-  pre();
   if constexpr (F8 > 0) {  // dequantisation: 1/sa * 1/sb
     const float sc = p.sa_inv[0] * p.sb_inv[0];
 #pragma unroll
@@ -519,17 +512,12 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
   const int64_t rowt = m0 + wm * WTM;
   // chunk C = P / 4 of pass P: width, lanes per row, rows per pass, lane offsets
   auto chunk_w = [](int C) { return WTN - 64 * C < 64 ? WTN - 64 * C : 64; };
-  // fp32 output: C, or this K slice's partial sums (row stride N) when split;
-  // a stream-K partial tile (kEpiF32Part) goes to p.ws as a BM x BN block
-  // addressed from the tile origin
-  constexpr bool F32OUT = EK == kEpiF32 || EK == kEpiF32Part || EK == kEpiF32Fix;
-  float* const cf = EK == kEpiF32Part ? p.ws
-                    : EK == kEpiF32 ? (p.splitk > 1 ? p.ws + static_cast<int64_t>(z) * p.M * p.N
-                                                    : static_cast<float*>(p.c))
-                    : EK == kEpiF32Fix ? static_cast<float*>(p.c)
-                                       : nullptr;
-  const int64_t ldc = EK == kEpiF32Part ? BN : (EK == kEpiF32 && p.splitk > 1) ? p.N : p.ldc;
-  const int64_t r_org = EK == kEpiF32Part ? m0 : 0, c_org = EK == kEpiF32Part ? n0 : 0;
+  // fp32 output: C, or this K slice's partial sums (row stride N) when split
+  constexpr bool F32OUT = EK == kEpiF32;
+  float* const cf = EK == kEpiF32 ? (p.splitk > 1 ? p.ws + static_cast<int64_t>(z) * p.M * p.N
+                                                  : static_cast<float*>(p.c))
+                                  : nullptr;
+  const int64_t ldc = (EK == kEpiF32 && p.splitk > 1) ? p.N : p.ldc;
 
   float bias8[NCH][8];
 #pragma unroll
@@ -593,22 +581,7 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
       const int64_t row = rowt + i * 32 + lr;
       const int64_t col = col0 + ec;
       if constexpr (F32OUT) {
-        if constexpr (EK == kEpiF32Fix) {
-          // the earlier K ranges' partial tiles (p.splitk of them, BM x BN
-          // each, consecutive at p.ws) in order, then this block's own sums
-          const float* w = p.ws + (row - m0) * BN + (col - n0);
-          f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(w);
-          f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(w + 4);
-          for (int q = 1; q < p.splitk; ++q) {
-            s0 += *reinterpret_cast<const f32x4_t*>(w + q * BM * BN);
-            s1 += *reinterpret_cast<const f32x4_t*>(w + q * BM * BN + 4);
-          }
-          if (p.splitk > 0) {
-            lo = s0 + lo;
-            hi = s1 + hi;
-          }
-        }
-        float* d = cf + (row - r_org) * ldc + (col - c_org);
+        float* d = cf + row * ldc + col;
         *reinterpret_cast<f32x4_t*>(d) = lo;
         *reinterpret_cast<f32x4_t*>(d + 4) = hi;
       } else {

@@ -139,13 +139,12 @@ struct AttnBwdParams {
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
 
-// The MLP step of p shards in two persistent launches (mlp_step.hip).
-// Launch A runs, per XCD, a queue over the XCD's own token rows: every
+// The row work of the MLP step of p shards in one persistent launch
+// (mlp_step.hip): per XCD, a queue over the XCD's own token rows of every
 // shard's fc1 forward (bias + GeLU) and fc2 forward partial, the sum over
-// shards, every shard's fc2 dgrad (GeLU derivative, column partials of dU_i)
-// and fc1 dgrad partial, the sum of the dX partials and the first pass of db.
-// Launch B runs every shard's two weight gradients as stream-K units inside
-// each XCD, then the second pass of the bias gradients.
+// shards, every shard's fc2 dgrad (GeLU derivative) and fc1 dgrad partial, and
+// the sum of the dX partials. The weight and bias gradients, which read every
+// token row, are products of their own (tp_api.hip).
 struct StepParams {
   // operands, row strides in elements (bf16 unless noted)
   const void* x;       // X [T, h], ld_x
@@ -161,36 +160,25 @@ struct StepParams {
   float* dxp;
   void* z;             // Z [T, h], ld_z
   void* dx;            // dX [T, h], ld_dx
-  float* dbw;          // dB fp32 [p*F, h], ld_dbw (shard i: rows i*F ..)
-  float* dbias_b;      // db fp32 [h], or null
-  float* daw;          // dA fp32 [h, p*F], ld_daw (shard i: columns i*F ..)
-  float* dbias_a;      // da fp32 [p*F], or null
   int64_t T, h, F;
   int p;
-  int64_t ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_dbw, ld_daw;
+  int64_t ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx;
   // workspace
   unsigned* err;       // nonzero after a dependency wait gave up
-  unsigned long long* clk;  // block 0 of launch A: s_memtime and s_memrealtime, start and end
+  unsigned long long* clk;  // block 0: s_memtime and s_memrealtime, start and end
   unsigned* ctr;       // counters (mlp_step.hip)
-  float* cs_da;        // p x [T/128, F] column partials of dU_i
-  float* cs_db;        // [T/64, h] column partials of dZ
-  float* parts;        // xcds x units_b partial tiles of 128 x 128 floats
-  int xcds, rb, rbx;   // XCDs; token rows of a launch-A unit; its row blocks per XCD
-  int units_a;         // queue length of launch A per XCD
-  int tiles_b, len_b, units_b;  // per XCD: weight-gradient tiles, K-tiles per unit, units
-  int pass2_b;         // bias-gradient second-pass units per XCD
+  int xcds, rb, rbx;   // XCDs; token rows of a unit; its row blocks per XCD
+  int units_a;         // queue length per XCD
   long long spin;      // polls before a dependency wait gives up
 };
-// Whether launch_mlp_step supports these shapes (the bf16 tiles, one row slab
+// Whether launch_mlp_rows supports these shapes (the bf16 tiles, one row slab
 // per XCD); and the workspace it needs (0 when unsupported).
 bool mlp_step_supported(int64_t T, int64_t h, int64_t F, int p);
 size_t mlp_step_workspace_bytes(int64_t T, int64_t h, int64_t F, int p);
-// Fills the shapes, queue lengths and workspace pointers of s (operands set by
-// the caller) and enqueues both launches.
-// phases: bit 0 launch A (forward, sums, data gradients), bit 1 launch B
-// (weight and bias gradients).
-hipError_t launch_mlp_step(StepParams s, void* workspace, int phases, hipStream_t stream);
-// Polls before a dependency wait of launch_mlp_step gives up, for the calling
+// Fills the shapes, queue length and workspace pointers of s (operands set by
+// the caller) and enqueues the launch.
+hipError_t launch_mlp_rows(StepParams s, void* workspace, hipStream_t stream);
+// Polls before a dependency wait of launch_mlp_rows gives up, for the calling
 // thread: 0 restores the default (about 0.25 s), a negative value gives up at
 // the first unsatisfied check.
 void set_step_wait_limit(long long polls);
@@ -256,11 +244,7 @@ hipError_t launch_gemm_bf16_general(const GemmParams& p, const SplitPlan& plan, 
 // fp32 store (or split-K partial), bf16 store, bias + GeLU saving the
 // pre-activation, and GeLU derivative from the saved pre-activation. All
 // outputs 16-byte aligned with row strides a multiple of 8.
-enum EpiKind : int { kEpiNone = -1, kEpiF32 = 0, kEpiBF16 = 1, kEpiBiasGelu = 2, kEpiDGelu = 3,
-                     // fp32 partial tile for a later block of the same tile
-                     kEpiF32Part = 4,
-                     // fp32 store of the earlier partial tiles plus this block's sums
-                     kEpiF32Fix = 5 };
+enum EpiKind : int { kEpiNone = -1, kEpiF32 = 0, kEpiBF16 = 1, kEpiBiasGelu = 2, kEpiDGelu = 3 };
 int pipe_epilogue_kind(const GemmParams& p);  // kEpiNone: use the general kernel
 hipError_t launch_gemm_bf16_pipe(const GemmParams& p, const SplitPlan& plan, int ek,
                                  hipStream_t s);

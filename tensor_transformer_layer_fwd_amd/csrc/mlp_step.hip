@@ -1,65 +1,52 @@
-// The MLP step of p tensor-parallel shards on one device ("Megatron" page,
-// "Tensor Parallelism / mathematical principles": U_i = X A_i + a_i,
-// Y_i = GeLU(U_i), Z = sum_i Y_i B_i + b; the backward is the derivative of
-// the same definitions) in two persistent launches of two blocks per CU.
+// The row work of the MLP step of p tensor-parallel shards on one device
+// ("Megatron" page, "Tensor Parallelism / mathematical principles":
+// U_i = X A_i + a_i, Y_i = GeLU(U_i), Z = sum_i Y_i B_i + b; the backward is
+// the derivative of the same definitions) in one persistent launch.
 //
-// Launch A: each XCD owns a slab of T / XCDs token rows and drains its own
-// ticket queue of units over those rows, in this order:
+// Each XCD owns a slab of T / XCDs token rows and drains its own ticket queue
+// of units over those rows, in this order:
 //   for each shard i: fc1 forward tiles (bias + GeLU, U_i and Y_i saved),
 //                     fc2 forward partial tiles (Zp_i, fp32);
 //   the sum over shards Z = sum_i Zp_i + b, in units of 16 rows;
-//   for each shard i: fc2 data-gradient tiles (dU_i = dZ B_i^T * GeLU'(U_i),
-//                     with the column partials of dU_i for da_i),
+//   for each shard i: fc2 data-gradient tiles (dU_i = dZ B_i^T * GeLU'(U_i)),
 //                     fc1 data-gradient partial tiles (dXp_i, fp32);
-//   the sum dX = sum_i dXp_i; the first pass of db = column sums of dZ.
-// A unit waits only for units of the same 128-row block that come earlier in
-// the same queue (fc2 forward for fc1's row block, the sums for every shard's
-// row block, fc2's data gradient for fc1's forward tile, fc1's data gradient
-// for fc2's). Producer and consumer therefore run on the same XCD and meet in
-// its L2: the producer's stores are complete (vmcnt 0) before it counts
-// itself done with an agent-scope atomic, and the consumer's loads come after
-// it sees the count. A consumer never touches those rows before their count
-// is complete, and the launch's start invalidated every CU's L1, so it cannot
+//   the sum dX = sum_i dXp_i.
+// A unit waits only for units of the same row block that come earlier in the
+// same queue (fc2 forward for fc1's row block, the sums for every shard's row
+// block, fc2's data gradient for fc1's forward tile, fc1's data gradient for
+// fc2's). Producer and consumer therefore run on the same XCD and meet in its
+// L2: the producer's stores are complete (vmcnt 0) before it counts itself
+// done with an agent-scope atomic, and the consumer's loads come after it sees
+// the count. A consumer never touches those rows before their count is
+// complete, and the launch's start invalidated every CU's L1, so it cannot
 // hold a stale copy. Tickets are taken in queue order and a unit only waits
 // for earlier tickets, which running blocks hold: the queue drains however
 // many blocks are resident.
 //
-// Launch B: the weight gradients dB_i = Y_i^T dZ and dA_i = X^T dU_i read
-// every token row, written by every XCD in launch A; the kernel boundary
-// makes them visible. Each XCD takes a contiguous share of all shards' 128 x
-// 128 weight-gradient tiles and cuts the K (token) range of its share into
-// equal units (stream-K), so every block does the same amount of work. A unit
-// that does not end its tile stores a partial tile; the unit that ends it
-// adds the earlier partials in K order, then its own sums, and stores dW.
-// The units of one tile are consecutive tickets of the same XCD. Then the
-// second passes of the bias gradients.
+// The weight gradients dB_i = Y_i^T dZ and dA_i = X^T dU_i read every token
+// row, which every XCD writes here; they run after this launch as products of
+// their own.
 //
-// Each launch's last block to finish (agent-scope done count) sets its
-// counters back to zero, so consecutive calls on one stream need no reset.
-// A dependency wait polls a bounded number of times; if it gives up it sets
-// the workspace's error word and carries on, so every block still exits.
+// The launch's last block to finish (agent-scope done count) sets the counters
+// back to zero, so consecutive calls on one stream need no reset. A dependency
+// wait polls a bounded number of times; if it gives up it sets the
+// workspace's error word and carries on, so every block still exits.
 #include <hip/hip_runtime.h>
 
-#include "colsum_device.h"
+#include "colsum_device.h"  // load8_f32, load8_bf16, store8
 #include "gemm_tile.h"
 
 namespace tpmlp {
 namespace {
 
-constexpr int kPoolA = 80 * 1024;  // two blocks per CU in 160 KiB of LDS
-constexpr int kPoolB = 64 * 1024;
-constexpr int kRows = 128;         // token rows of the smaller launch-A unit
-constexpr int kTileW = 128;        // weight-gradient tile
-constexpr int kBKW = 32;           // its K-tile
-constexpr int kPartFloats = kTileW * kTileW;
+constexpr int kRows = 128;  // token rows of the smaller unit
 
-// Counter layout (unsigned words from s.ctr): launch A's tickets (xcds), its
-// done count, the per-row-block counts cF1 [p][nrb], cF2 [nrb], cD2 [p][nrb],
-// cD1 [nrb]; then launch B's tickets (xcds), done count and partial flags
-// [xcds][units_b].
+// Counter layout (unsigned words from s.ctr): the tickets (xcds), the done
+// count, the per-row-block counts cF1 [p][nrb], cF2 [nrb], cD2 [p][nrb],
+// cD1 [nrb].
 struct Layout {
   int64_t nrb;
-  int64_t ta, da, f1, f2, d2, d1, a_end, tb, db, fl, b_end;
+  int64_t ta, da, f1, f2, d2, d1, end;
   __host__ __device__ explicit Layout(const StepParams& s) {
     nrb = s.T / s.rb;
     ta = 0;
@@ -68,11 +55,7 @@ struct Layout {
     f2 = f1 + s.p * nrb;
     d2 = f2 + nrb;
     d1 = d2 + s.p * nrb;
-    a_end = d1 + nrb;
-    tb = a_end;
-    db = tb + s.xcds;
-    fl = db + 1;
-    b_end = fl + static_cast<int64_t>(s.xcds) * s.units_b;
+    end = d1 + nrb;
   }
 };
 
@@ -185,9 +168,6 @@ __device__ __forceinline__ const uint16_t* bf(const void* q) {
 }
 __device__ __forceinline__ uint16_t* bfw(void* q) { return static_cast<uint16_t*>(q); }
 
-// ---------------------------------------------------------------------------
-// Launch A
-// ---------------------------------------------------------------------------
 // Tile configuration: RB token rows per unit (the row block), TN output
 // columns, WM x WN waves; K-tile and stages of the products with an
 // N-contiguous weight (NN: the forwards) and with two K-contiguous operands
@@ -202,19 +182,17 @@ struct RowsCfg {
 // 128 x 128 tiles, four waves, two blocks per CU
 using RowsSmall = RowsCfg<128, 128, 2, 2, 32, 4, 64, 2, 80 * 1024, 2>;
 // 256 x 128 tiles, eight waves of 64 x 64, one block per CU: two thirds of
-// the operand bytes per flop of the 128 x 128 tile
-using RowsLarge = RowsCfg<256, 128, 4, 2, 64, 2, 64, 2, 96 * 1024, 1>;
-// 256 x 192 tiles, eight waves of 64 x 96, 64-wide K-tiles double-buffered,
-// one block per CU: fewer accumulators per wave than 256 x 256
-using RowsMid = RowsCfg<256, 192, 4, 2, 64, 2, 64, 2, 112 * 1024, 1>;
+// the operand bytes per flop of the 128 x 128 tile; three 64-wide K-tiles in
+// flight (144 KiB of LDS)
+using RowsLarge = RowsCfg<256, 128, 4, 2, 64, 3, 64, 3, 144 * 1024, 1>;
 
-// Phases of a launch-A queue, in order. A unit only waits for units of
-// earlier phases: fc1 forward (F1), db's first pass (DB, no wait), fc2
-// forward (F2, after F1 of its row block and shard), fc2's data gradient (D2,
-// after F1), the forward sum (S1, after every shard's F2), fc1's data
-// gradient (D1, after D2) and the dX sum (S2, after every shard's D1). Within
-// a product the shards come in order.
-enum RowsKind : int { kF1 = 0, kF2 = 1, kS1 = 2, kD2 = 3, kD1 = 4, kS2 = 5, kDB = 6 };
+// Phases of a queue, in order. A unit only waits for units of earlier
+// phases: fc1 forward (F1), fc2 forward (F2, after F1 of its row block and
+// shard), fc2's data gradient (D2, after F1), the forward sum (S1, after every
+// shard's F2), fc1's data gradient (D1, after D2) and the dX sum (S2, after
+// every shard's D1). Within a product the shards come in order.
+enum RowsKind : int { kF1 = 0, kF2 = 1, kS1 = 2, kD2 = 3, kD1 = 4, kS2 = 5 };
+constexpr int kPhases = 6;
 
 // One GEMM tile of a unit. (Inlined: as a function of its own every call
 // saved and restored most of a wave's registers through scratch memory.)
@@ -238,18 +216,16 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
   const int64_t T = s.T, h = s.h, F = s.F;
   const int R = s.rbx;
   const int n1 = static_cast<int>(F / TN), n2 = static_cast<int>(h / TN);
-  const int ncb = static_cast<int>((h + 255) / 256);
-  const int ndb = R * (RB / kColsumRows) * ncb;
   // phase sizes, in queue order
-  const int counts[7] = {s.p * R * n1, ndb, s.p * R * n2, s.p * R * n1, R * SS, s.p * R * n2,
-                         R * SS};
-  const int kinds[7] = {kF1, kDB, kF2, kD2, kS1, kD1, kS2};
+  const int counts[kPhases] = {s.p * R * n1, s.p * R * n2, s.p * R * n1, R * SS, s.p * R * n2,
+                               R * SS};
+  const int kinds[kPhases] = {kF1, kF2, kD2, kS1, kD1, kS2};
   unsigned* ctr = s.ctr;
   for (;;) {
     const unsigned tk = next_ticket(ctr + L.ta + x, pool);
     if (tk >= static_cast<unsigned>(s.units_a)) break;
     int t = static_cast<int>(tk), ph = 0;
-    while (ph < 6 && t >= counts[ph]) t -= counts[ph++];
+    while (ph < kPhases - 1 && t >= counts[ph]) t -= counts[ph++];
     const int kind = kinds[ph];
     // t within the phase: (shard i,) row block j, column tile (or sum slice) n
     int i = 0, j = 0, n = 0;
@@ -261,11 +237,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
       i = t / (R * n2);
       j = (t % (R * n2)) / n2;
       n = t % n2;
-    } else if (kind == kS1 || kind == kS2) {
+    } else {  // the sums
       j = t / SS;
       n = t % SS;
-    } else {
-      j = t;
     }
     const int64_t rg = static_cast<int64_t>(x) * R + j;  // global row block
     const int64_t m0 = rg * RB;
@@ -316,7 +290,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
         g.ldc = s.ld_u;
         g.u = bf(s.u) + i * F;
         g.ldu = s.ld_u;
-        g.cs_part = s.dbias_a ? s.cs_da + i * L.nrb * F : nullptr;
         g.M = T, g.N = F, g.K = h, g.k_chunk = h;
         unit_tile<RB, TN, C::WM, C::WN, C::BKT, C::ST, true, true, kEpiDGelu, C::POOL>(
             g, m0, static_cast<int64_t>(n) * TN, static_cast<int>(h / C::BKT));
@@ -337,181 +310,24 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
         signal_count(ctr + L.d1 + rg);
         break;
       }
-      case kS2:  // dX = sum_i dXp_i
+      default:  // kS2: dX = sum_i dXp_i
         wait_count(ctr + L.d1 + rg, static_cast<unsigned>(s.p * n2), s);
         rows_sum_unit(s.dxp, T * h, s.p, h, nullptr, s.dx, s.ld_dx, m0 + n * kSumRows, h);
         break;
-      default: {  // db, first pass: column sums of this XCD's 64-row chunks of dZ
-        if (!s.dbias_b) break;
-        ColsumParams c{};
-        c.src = s.dz;
-        c.T = T;
-        c.N = h;
-        c.ld = s.ld_dz;
-        c.src_bf16 = 1;
-        c.dbias = s.dbias_b;
-        c.ws = s.cs_db;
-        const int chunk = x * R * (RB / kColsumRows) + j / ncb;
-        colsum_vec_unit(c, j % ncb, chunk, static_cast<int>(T / kColsumRows),
-                        reinterpret_cast<float(*)[256]>(pool));
-        break;
-      }
     }
   }
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     s.clk[2] = clock64();
     s.clk[3] = wall_clock64();
   }
-  finish_launch(ctr, L.da, L.ta, L.a_end);
+  finish_launch(ctr, L.da, L.ta, L.end);
 }
 
-// ---------------------------------------------------------------------------
-// Launch B
-// ---------------------------------------------------------------------------
-// Waits for the partial tiles of units [first, first + n) of this XCD.
-struct WaitParts {
-  const unsigned* flags;
-  int n;
-  const StepParams* s;
-  __device__ __forceinline__ void operator()() const {
-    if (threadIdx.x == 0) {
-      for (int q = 0; q < n; ++q) {
-        unsigned v = load_count(flags + q);
-        for (long long k = s->spin; v == 0 && k > 0; --k) {
-          __builtin_amdgcn_s_sleep(2);
-          v = load_count(flags + q);
-        }
-        if (v == 0)
-          __hip_atomic_fetch_or(s->err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    __syncthreads();
-  }
-};
-
-// Weight-gradient tile g (over all shards: for each shard dB_i's tiles, then
-// dA_i's, each row-major) as a TN product.
-__device__ __forceinline__ GemmParams wgrad_tile(const StepParams& s, int64_t gt, int64_t* m0,
-                                                 int64_t* n0) {
-  const int64_t tf = s.F / kTileW, th = s.h / kTileW;
-  const int64_t per = 2 * tf * th;
-  const int64_t i = gt / per;
-  int64_t r = gt % per;
-  GemmParams g{};
-  g.splitk = 1;
-  g.K = s.T;
-  g.k_chunk = s.T;
-  g.xcds = s.xcds;
-  if (r < tf * th) {  // dB_i [F, h] = Y_i^T dZ
-    g.a = bf(s.y) + i * s.F;
-    g.lda = s.ld_u;
-    g.b = s.dz;
-    g.ldb = s.ld_dz;
-    g.c = s.dbw + i * s.F * s.ld_dbw;
-    g.ldc = s.ld_dbw;
-    g.M = s.F, g.N = s.h;
-    *m0 = (r / th) * kTileW;
-    *n0 = (r % th) * kTileW;
-  } else {  // dA_i [h, F] = X^T dU_i
-    r -= tf * th;
-    g.a = s.x;
-    g.lda = s.ld_x;
-    g.b = bf(s.du) + i * s.F;
-    g.ldb = s.ld_u;
-    g.c = s.daw + i * s.F;
-    g.ldc = s.ld_daw;
-    g.M = s.h, g.N = s.F;
-    *m0 = (r / tf) * kTileW;
-    *n0 = (r % tf) * kTileW;
-  }
-  return g;
-}
-
-__global__ __launch_bounds__(256, 2) void mlp_wgrad_kernel(StepParams s) {
-  uint8_t* pool = pool_buf<kPoolB>();
-  const Layout L(s);
-  const int x = xcc_id() % s.xcds;
-  unsigned* ctr = s.ctr;
-  unsigned* flags = ctr + L.fl + static_cast<int64_t>(x) * s.units_b;
-  float* parts = s.parts + static_cast<int64_t>(x) * s.units_b * kPartFloats;
-  const int kt = static_cast<int>(s.T / kBKW);  // K-tiles of a tile
-  const int64_t total = static_cast<int64_t>(s.tiles_b) * kt;
-  const int nda = s.dbias_a ? s.p * static_cast<int>(s.F / 64) : 0;
-  const int ndb = s.dbias_b ? static_cast<int>(s.h / 64) : 0;
-  for (;;) {
-    const unsigned tk = next_ticket(ctr + L.tb + x, pool);
-    if (tk >= static_cast<unsigned>(s.units_b + s.pass2_b)) break;
-    const int u = static_cast<int>(tk);
-    if (u < s.units_b) {
-      // The unit's K range covers the end of one tile, any whole tiles, and
-      // the start of the next tile. The start, whose partial a later unit
-      // adds, runs first, so a unit never waits on a partial that its
-      // predecessor computes last: the waits do not chain along the queue.
-      const int64_t kb = static_cast<int64_t>(u) * s.len_b;
-      const int64_t kend = min(kb + s.len_b, total);
-      const int64_t last_start = max(kb, ((kend - 1) / kt) * kt);  // start of kend's tile
-      const bool tail_partial = kend % kt != 0;
-      for (int pass = 0; pass < 2; ++pass) {
-        // pass 0: the trailing partial segment (if any); pass 1: the others
-        int64_t k0 = pass == 0 ? (tail_partial ? last_start : kend) : kb;
-        const int64_t k1 = pass == 0 ? kend : (tail_partial ? last_start : kend);
-        while (k0 < k1) {
-          const int64_t jt = k0 / kt, tile_end = (jt + 1) * kt;
-          const int64_t seg_end = min(k1, tile_end);
-          int64_t m0, n0;
-          GemmParams g = wgrad_tile(s, static_cast<int64_t>(x) * s.tiles_b + jt, &m0, &n0);
-          const int64_t kbeg = (k0 - jt * kt) * kBKW;
-          const int nk = static_cast<int>(seg_end - k0);
-          __syncthreads();  // the previous segment's epilogue is done with the pool
-          if (seg_end == tile_end) {
-            // ends the tile: the earlier units of this tile left partial tiles
-            const int first = static_cast<int>((jt * kt) / s.len_b);
-            g.splitk = u - first;
-            g.ws = parts + static_cast<int64_t>(first) * kPartFloats;
-            gemm_pipe_tile<kTileW, kTileW, 2, 2, kBKW, 4, false, false, kEpiF32Fix, 0, kPoolB,
-                           WaitParts>(g, m0, n0, 0, kbeg, nk,
-                                      WaitParts{flags + first, u - first, &s});
-          } else {
-            g.ws = parts + static_cast<int64_t>(u) * kPartFloats;
-            gemm_pipe_tile<kTileW, kTileW, 2, 2, kBKW, 4, false, false, kEpiF32Part, 0, kPoolB>(
-                g, m0, n0, 0, kbeg, nk);
-            signal_count(flags + u);
-          }
-          k0 = seg_end;
-        }
-      }
-    } else {
-      // second passes of the bias gradients: unit q over 64 columns
-      const int q = (u - s.units_b) * s.xcds + x;
-      ColsumParams c{};
-      c.accumulate = 0;
-      int nchunks = 0, bx = 0;
-      if (q < nda) {
-        const int per = static_cast<int>(s.F / 64), i = q / per;
-        c.N = s.F;
-        c.dbias = s.dbias_a + i * s.F;
-        c.ws = s.cs_da + i * (s.T / s.rb) * s.F;
-        nchunks = static_cast<int>(s.T / s.rb);
-        bx = q % per;
-      } else if (q < nda + ndb) {
-        c.N = s.h;
-        c.dbias = s.dbias_b;
-        c.ws = s.cs_db;
-        nchunks = static_cast<int>(s.T / kColsumRows);
-        bx = q - nda;
-      }
-      if (nchunks > 0) colsum_pass2_unit(c, bx, nchunks, reinterpret_cast<float(*)[64]>(pool));
-    }
-  }
-  finish_launch(ctr, L.db, L.tb, L.b_end);
-}
-
-// Queue lengths and workspace layout of a step (shapes and device only).
+// Queue length and workspace layout of a step (shapes and device only).
 struct Plan {
-  int cfg;  // launch A's tiles: 0 RowsSmall (128 x 128), 1 RowsMid (256 x 192), 2 RowsLarge
-            // (256 x 128)
-  int xcds, rb, rbx, units_a, tiles_b, len_b, units_b, pass2_b;
-  size_t off_ctr, off_da, off_db, off_parts, bytes;
+  bool large;  // 256 x 128 tiles (RowsLarge), else 128 x 128 (RowsSmall)
+  int xcds, rb, rbx, units_a;
+  size_t off_ctr, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
@@ -520,9 +336,8 @@ template <class C>
 int rows_units(int64_t T, int64_t h, int64_t F, int p, int X) {
   const int R = static_cast<int>(T / C::RB / X);
   const int n1 = static_cast<int>(F / C::TN), n2 = static_cast<int>(h / C::TN);
-  const int ndb = R * (C::RB / kColsumRows) * static_cast<int>((h + 255) / 256);
   const int ss = C::RB / kSumRows;
-  return 2 * p * R * n1 + 2 * p * R * n2 + 2 * R * ss + ndb;
+  return 2 * p * R * n1 + 2 * p * R * n2 + 2 * R * ss;
 }
 
 bool plan_step(int64_t T, int64_t h, int64_t F, int p, Plan* pl) {
@@ -530,50 +345,25 @@ bool plan_step(int64_t T, int64_t h, int64_t F, int p, Plan* pl) {
   const int X = d.xcds;
   if (p < 1 || p > kMaxPartials || T < 1 || h < 1 || F < 1) return false;
   if (T % (static_cast<int64_t>(kRows) * X) || h % 128 || F % 128) return false;
-  const int64_t tiles = 2 * p * (F / kTileW) * (h / kTileW);
-  if (tiles % X) return false;
-  // the fused step is for products too small to fill the device on their
+  // the fused launch is for products too small to fill the device on their
   // own; above ~20 GFLOP a product keeps the one-product-per-launch path
   if (2.0 * T * h * F > 2.0e10) return false;
   Plan q{};
   q.xcds = X;
-  // launch A's tiles: 256 x 192 where the shapes divide, else 256 x 128, else
-  // 128 x 128; a tile forced with tp_set_gemm_override where it divides
-  auto fits = [&](int rb, int tn) {
-    return T % (static_cast<int64_t>(rb) * X) == 0 && h % tn == 0 && F % tn == 0;
-  };
-  const bool mid = fits(RowsMid::RB, RowsMid::TN), large = fits(RowsLarge::RB, RowsLarge::TN);
-  q.cfg = mid ? 1 : large ? 2 : 0;
-  const int ft = forced_tile();
-  if (ft == kPipe128x128) q.cfg = 0;
-  if (ft == kPipe256x192 && mid) q.cfg = 1;
-  if (ft == kPipe256x128 && large) q.cfg = 2;
-  q.rb = q.cfg == 0 ? RowsSmall::RB : RowsMid::RB;
+  // 256 x 128 tiles where the rows divide, else 128 x 128; 128 x 128 when
+  // tp_set_gemm_override forces that tile
+  q.large = T % (static_cast<int64_t>(RowsLarge::RB) * X) == 0 && forced_tile() != kPipe128x128;
+  q.rb = q.large ? RowsLarge::RB : RowsSmall::RB;
   q.rbx = static_cast<int>(T / q.rb / X);
-  q.units_a = q.cfg == 0   ? rows_units<RowsSmall>(T, h, F, p, X)
-              : q.cfg == 1 ? rows_units<RowsMid>(T, h, F, p, X)
-                           : rows_units<RowsLarge>(T, h, F, p, X);
-  q.tiles_b = static_cast<int>(tiles / X);
-  const int64_t kt = T / kBKW, total = q.tiles_b * kt;
-  const int want = 2 * (d.cus / X > 0 ? d.cus / X : 1);  // two units per CU
-  q.len_b = static_cast<int>((total + want - 1) / want);
-  if (q.len_b < 8) q.len_b = 8;
-  q.units_b = static_cast<int>((total + q.len_b - 1) / q.len_b);
-  const int npass2 = p * static_cast<int>(F / 64) + static_cast<int>(h / 64);
-  q.pass2_b = (npass2 + X - 1) / X;
+  q.units_a = q.large ? rows_units<RowsLarge>(T, h, F, p, X) : rows_units<RowsSmall>(T, h, F, p, X);
   StepParams tmp{};
   tmp.T = T;
   tmp.p = p;
   tmp.xcds = X;
   tmp.rb = q.rb;
-  tmp.units_b = q.units_b;
   const Layout lay(tmp);
   q.off_ctr = 128;
-  q.off_da = align256(q.off_ctr + lay.b_end * sizeof(unsigned));
-  q.off_db = align256(q.off_da + static_cast<size_t>(p) * (T / kRows) * F * sizeof(float));
-  q.off_parts = align256(q.off_db + static_cast<size_t>(T / kColsumRows) * h * sizeof(float));
-  q.bytes = align256(q.off_parts +
-                     static_cast<size_t>(X) * q.units_b * kPartFloats * sizeof(float));
+  q.bytes = align256(q.off_ctr + lay.end * sizeof(unsigned));
   *pl = q;
   return true;
 }
@@ -594,45 +384,27 @@ size_t mlp_step_workspace_bytes(int64_t T, int64_t h, int64_t F, int p) {
 
 void set_step_wait_limit(long long polls) { g_wait_limit = polls; }
 
-hipError_t launch_mlp_step(StepParams s, void* workspace, int phases, hipStream_t stream) {
+hipError_t launch_mlp_rows(StepParams s, void* workspace, hipStream_t stream) {
   Plan q;
   if (!plan_step(s.T, s.h, s.F, s.p, &q)) return hipErrorInvalidValue;
   char* w = static_cast<char*>(workspace);
   s.err = reinterpret_cast<unsigned*>(w);
   s.clk = reinterpret_cast<unsigned long long*>(w + 64);
   s.ctr = reinterpret_cast<unsigned*>(w + q.off_ctr);
-  s.cs_da = reinterpret_cast<float*>(w + q.off_da);
-  s.cs_db = reinterpret_cast<float*>(w + q.off_db);
-  s.parts = reinterpret_cast<float*>(w + q.off_parts);
   s.xcds = q.xcds;
   s.rb = q.rb;
   s.rbx = q.rbx;
   s.units_a = q.units_a;
-  s.tiles_b = q.tiles_b;
-  s.len_b = q.len_b;
-  s.units_b = q.units_b;
-  s.pass2_b = q.pass2_b;
   // about 0.25 s of polling at the default
   s.spin = g_wait_limit > 0 ? g_wait_limit : (g_wait_limit < 0 ? 0 : (1ll << 22));
   const int cus = device_shape().cus;
-  if (phases & 1) {
-    if (q.cfg == 1)
-      hipLaunchKernelGGL(mlp_rows_kernel<RowsMid>, dim3(cus * RowsMid::MINB),
-                         dim3(RowsMid::THREADS), 0, stream, s);
-    else if (q.cfg == 2)
-      hipLaunchKernelGGL(mlp_rows_kernel<RowsLarge>, dim3(cus * RowsLarge::MINB),
-                         dim3(RowsLarge::THREADS), 0, stream, s);
-    else
-      hipLaunchKernelGGL(mlp_rows_kernel<RowsSmall>, dim3(cus * RowsSmall::MINB),
-                         dim3(RowsSmall::THREADS), 0, stream, s);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (phases & 2) {
-    hipLaunchKernelGGL(mlp_wgrad_kernel, dim3(2 * cus), dim3(256), 0, stream, s);
-    return hipGetLastError();
-  }
-  return hipSuccess;
+  if (q.large)
+    hipLaunchKernelGGL(mlp_rows_kernel<RowsLarge>, dim3(cus * RowsLarge::MINB),
+                       dim3(RowsLarge::THREADS), 0, stream, s);
+  else
+    hipLaunchKernelGGL(mlp_rows_kernel<RowsSmall>, dim3(cus * RowsSmall::MINB),
+                       dim3(RowsSmall::THREADS), 0, stream, s);
+  return hipGetLastError();
 }
 
 }  // namespace tpmlp

@@ -648,15 +648,20 @@ int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype 
   if (!bytes) return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
   if (!dim_ok(T) || !dim_ok(h) || !dim_ok(F) || p < 1 || p > kMaxPartials) return TP_ERR_SHAPE;
+  const int64_t pF = static_cast<int64_t>(p) * F;
+  if (!dim_ok(pF)) return TP_ERR_SHAPE;
   size_t fb = 0, w2 = 0, w1 = 0;
   int st = tp_mlp_bwd_workspace_size(T, h, F, dt, &fb);
-  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, F, h, dt, &w2);
-  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, h, F, dt, &w1);
+  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, pF, h, dt, &w2);
+  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, h, pF, dt, &w1);
   if (st != TP_OK) return st;
-  fb = fb > w2 ? fb : w2;
-  fb = fb > w1 ? fb : w1;
-  const size_t fused = dt == TP_BF16 ? mlp_step_workspace_bytes(T, h, F, p) : 0;
-  *bytes = fused > fb ? fused : fb;
+  // the row launch's counters, then the stacked weight gradients' scratch;
+  // the per-product path uses the workspace from its start
+  const size_t rows = dt == TP_BF16 ? mlp_step_workspace_bytes(T, h, F, p) : 0;
+  const size_t wg = w1 > w2 ? w1 : w2;
+  const size_t fused = rows + wg;
+  const size_t each = fb > wg ? fb : wg;
+  *bytes = fused > each ? fused : each;
   return TP_OK;
 }
 
@@ -702,39 +707,52 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
                      row_ok(Zp, h, 4) && row_ok(dXp, h, 4) && row_ok(dB, ld_db, 4) &&
                      row_ok(dA, ld_da, 4) && (!a || aligned(a, 16)) && (!b || aligned(b, 16)) &&
                      aligned(workspace, 256);
+  const int64_t ld_y = ld_u;
+  // Weight and bias gradients of every shard as two products over the stacked
+  // shards: dB = Y^T dZ ([p*F, h]) with db = column sums of dZ, and
+  // dA = X^T dU ([h, p*F]) with da = column sums of dU.
+  auto wgrads = [&](void* ws, size_t ws_bytes) {
+    int r = tp_linear_bwd_wgrad(Y, dZ, dB, db, T, pF, h, ld_y, ld_dz, ld_db, 0, dt, ws, ws_bytes,
+                                stream);
+    if (r != TP_OK) return r;
+    return tp_linear_bwd_wgrad(X, dU, dA, da, T, h, pF, ld_x, ld_u, ld_da, 0, dt, ws, ws_bytes,
+                               stream);
+  };
   if (fused) {
-    StepParams s{};
-    s.x = X;
-    s.a = A;
-    s.bias_a = a;
-    s.b = B;
-    s.bias_b = b;
-    s.dz = dZ;
-    s.u = U;
-    s.y = Y;
-    s.du = dU;
-    s.zp = Zp;
-    s.dxp = dXp;
-    s.z = Z;
-    s.dx = dX;
-    s.dbw = dB;
-    s.dbias_b = db;
-    s.daw = dA;
-    s.dbias_a = da;
-    s.T = T;
-    s.h = h;
-    s.F = F;
-    s.p = p;
-    s.ld_x = ld_x;
-    s.ld_a = ld_a;
-    s.ld_b = ld_b;
-    s.ld_dz = ld_dz;
-    s.ld_u = ld_u;
-    s.ld_z = ld_z;
-    s.ld_dx = ld_dx;
-    s.ld_dbw = ld_db;
-    s.ld_daw = ld_da;
-    return hip_status(launch_mlp_step(s, workspace, phases, stream));
+    if (phases & 1) {
+      StepParams s{};
+      s.x = X;
+      s.a = A;
+      s.bias_a = a;
+      s.b = B;
+      s.bias_b = b;
+      s.dz = dZ;
+      s.u = U;
+      s.y = Y;
+      s.du = dU;
+      s.zp = Zp;
+      s.dxp = dXp;
+      s.z = Z;
+      s.dx = dX;
+      s.T = T;
+      s.h = h;
+      s.F = F;
+      s.p = p;
+      s.ld_x = ld_x;
+      s.ld_a = ld_a;
+      s.ld_b = ld_b;
+      s.ld_dz = ld_dz;
+      s.ld_u = ld_u;
+      s.ld_z = ld_z;
+      s.ld_dx = ld_dx;
+      st = hip_status(launch_mlp_rows(s, workspace, stream));
+      if (st != TP_OK) return st;
+    }
+    if (phases & 2) {
+      const size_t rows = mlp_step_workspace_bytes(T, h, F, p);
+      return wgrads(static_cast<char*>(workspace) + rows, workspace_bytes - rows);
+    }
+    return TP_OK;
   }
   // the same step as one call per product. Both phases: every shard's
   // forward, the sum, every shard's backward (tp_mlp_bwd, both layers' two
@@ -786,16 +804,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     st = tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
     if (st != TP_OK) return st;
   }
-  if (phases & 2) {
-    for (int i = 0; i < p; ++i) {
-      st = tp_linear_bwd_wgrad(Yi(i), dZ, dB + i * F * ld_db, i == 0 ? db : nullptr, T, F, h,
-                               ld_u, ld_dz, ld_db, 0, dt, workspace, workspace_bytes, stream);
-      if (st != TP_OK) return st;
-      st = tp_linear_bwd_wgrad(X, dUi(i), dA + i * F, da ? da + i * F : nullptr, T, h, F, ld_x,
-                               ld_u, ld_da, 0, dt, workspace, workspace_bytes, stream);
-      if (st != TP_OK) return st;
-    }
-  }
+  if (phases & 2) return wgrads(workspace, workspace_bytes);
   return TP_OK;
 }
 

@@ -1,13 +1,15 @@
-"""GPU parity of tp_mlp_step, the whole MLP step of every shard in two
-persistent launches, against the float64 oracle and against the per-product
-calls, plus its queue bookkeeping: consecutive calls, graph replay, the two
-halves called separately, and a dependency wait forced to give up.
+"""GPU parity of tp_mlp_step, the whole MLP step of every shard (one
+persistent launch for the forward, the sums and the data gradients, then the
+weight gradients as two products over the stacked shards), against the
+float64 oracle and against the per-product calls, plus its queue bookkeeping:
+consecutive calls, graph replay, the two halves called separately, and a
+dependency wait forced to give up.
 
 Tolerance: 5e-3 relative Frobenius error per output against the oracle (bf16
 storage). Against the per-product calls, which run the same K order per
 output element in every fused tile, the forward outputs and data gradients
-agree bitwise; the weight gradients' K ranges are summed in another order
-(stream-K partial tiles), so within 1e-5 relative.
+agree bitwise; the stacked weight-gradient products may split K otherwise
+than the per-shard calls, so the weight gradients agree within 1e-5 relative.
 """
 import dataclasses
 import sys
@@ -167,5 +169,5 @@ def test_mlp_step_clock_counters(dev):
     torch.cuda.synchronize()
     c = step.step_ws[64:96].view(torch.int64).cpu().tolist()
     mhz = (c[2] - c[0]) / ((c[3] - c[1]) / 100e6) / 1e6
-    _say(f"  engine clock over launch A: {mhz:.0f} MHz")
+    _say(f"  engine clock over the persistent launch: {mhz:.0f} MHz")
     assert 500 <= mhz <= 2600
