@@ -8,6 +8,8 @@
         --cmd-fetch "..." --cmd-write "..." [--out profiles/traffic.json]
     python -m tensor_transformer_layer_fwd_amd.prof_summary mfma COUNTER_CSV --cmd "..." \
         [--sclk-mhz MHZ] [--out profiles/NAME.txt]
+    python -m tensor_transformer_layer_fwd_amd.prof_summary stalls COUNTER_CSV ... \
+        --cmd "..." ... [--kernel SUBSTRING] [--sclk-mhz MHZ] [--out profiles/NAME.txt]
 
 `traffic` converts FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel into
 HBM bytes per launch, scaled by what the same counters read for a plain device
@@ -27,6 +29,16 @@ utilisation of the clock the part held, never below the former.
 GRBM_GUI_ACTIVE is not used: summed over the XCDs and divided by their number
 it gave 2.69 GHz over a 35.7 us dispatch, above the part's highest clock, so its
 window is wider than the dispatch.
+
+`stalls` merges counter passes of one command (each pass a run of its own) per
+kernel and grid and reports medians over dispatches: MFMA busy as above; the
+wave-cycle fractions spent waiting for anything (SQ_WAIT_ANY), for an
+instruction's operands or issue (SQ_WAIT_INST_ANY) and for LDS issue
+(SQ_WAIT_INST_LDS), all over SQ_WAVE_CYCLES (same quad-cycle units); LDS bank
+conflict cycles over LDS-active cycles; the derived VmemLatency and LdsLatency
+(cycles from issue to completion, averaged over instructions); the L2 hit rate
+TCC_HIT / (TCC_HIT + TCC_MISS); and the average latency of L2 misses
+(TCC_EA0_RDREQ_LEVEL / TCC_EA0_RDREQ, cycles).
 """
 from __future__ import annotations
 
@@ -190,6 +202,79 @@ def cmd_mfma(a):
     print(text)
 
 
+def _dispatches(path):
+    """{(kernel, grid, dispatch): {counter: value, "dur_us": duration}}."""
+    d = collections.defaultdict(dict)
+    for r in csv.DictReader(open(path)):
+        name = r["Kernel_Name"].replace("tpmlp::(anonymous namespace)::", "")
+        name = name.replace("(tpmlp::GemmParams)", "")
+        key = (name, int(r["Grid_Size"]), int(r["Dispatch_Id"]))
+        d[key][r["Counter_Name"]] = float(r["Counter_Value"])
+        d[key]["dur_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+    return d
+
+
+def cmd_stalls(a):
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in a.csv:
+        for (name, grid, _), vals in _dispatches(path).items():
+            if a.kernel and a.kernel not in name:
+                continue
+            for c, v in vals.items():
+                per[(name, grid)][c].append(v)
+
+    def med(vals, c):
+        return statistics.median(vals[c]) if vals.get(c) else None
+
+    def ratio(vals, num, den):
+        n, d = med(vals, num), med(vals, den)
+        return n / d if n is not None and d else None
+
+    lines = ["# rocprofv3 --pmc passes of one command (one pass per run), medians over dispatches",
+             *[f"# command: {c}" for c in a.cmd],
+             f"# mfma: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x dispatch duration x "
+             f"{a.sclk_mhz or SPEC_MHZ:.0f} MHz)",
+             "# wait_any, wait_inst, wait_lds: SQ_WAIT_ANY, SQ_WAIT_INST_ANY, SQ_WAIT_INST_LDS "
+             "over SQ_WAVE_CYCLES",
+             "# bank: SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS; vmem_lat, lds_lat: VmemLatency, "
+             "LdsLatency (cycles)",
+             "# l2_hit: TCC_HIT / (TCC_HIT + TCC_MISS); miss_lat: TCC_EA0_RDREQ_LEVEL / "
+             "TCC_EA0_RDREQ (cycles)",
+             ""]
+    hdr = ["dur_us", "mfma", "wait_any", "wait_inst", "wait_lds", "bank", "vmem_lat", "lds_lat",
+           "l2_hit", "miss_lat"]
+    lines.append(" ".join(f"{h:>9}" for h in hdr) + "  kernel (grid)")
+    clk = (a.sclk_mhz or SPEC_MHZ) * 1e6
+    rows = []
+    for (name, grid), vals in per.items():
+        dur = med(vals, "dur_us")
+        busy = None
+        if vals.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+            busy = statistics.median(
+                c / (SIMDS * t * 1e-6 * clk)
+                for c, t in zip(vals["SQ_VALU_MFMA_BUSY_CYCLES"], vals["dur_us"]) if t > 0)
+        hit, miss = med(vals, "TCC_HIT_sum"), med(vals, "TCC_MISS_sum")
+        cols = [dur, busy, ratio(vals, "SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+                ratio(vals, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+                ratio(vals, "SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"),
+                ratio(vals, "SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS"),
+                med(vals, "VmemLatency"), med(vals, "LdsLatency"),
+                hit / (hit + miss) if hit is not None and miss is not None and hit + miss else None,
+                ratio(vals, "TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum")]
+        rows.append((dur or 0.0, name, grid, cols))
+    rows.sort(key=lambda r: -r[0])
+    fmt = ["{:9.1f}", "{:9.3f}", "{:9.3f}", "{:9.3f}", "{:9.3f}", "{:9.3f}", "{:9.0f}",
+           "{:9.0f}", "{:9.3f}", "{:9.0f}"]
+    for _, name, grid, cols in rows[:a.top]:
+        cells = [f"{'-':>9}" if v is None else f.format(v) for f, v in zip(fmt, cols)]
+        short = name if len(name) <= 110 else name[:107] + "..."
+        lines.append(" ".join(cells) + f"  {short} ({grid})")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        open(a.out, "w").write(text)
+    print(text)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -213,8 +298,15 @@ def main():
     m.add_argument("--cmd", required=True)
     m.add_argument("--sclk-mhz", type=float, default=None)
     m.add_argument("--out")
+    st = sub.add_parser("stalls")
+    st.add_argument("csv", nargs="+")
+    st.add_argument("--cmd", action="append", required=True, help="one per pass, in order")
+    st.add_argument("--kernel", default=None)
+    st.add_argument("--sclk-mhz", type=float, default=None)
+    st.add_argument("--top", type=int, default=12)
+    st.add_argument("--out")
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.what](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma, "stalls": cmd_stalls}[a.what](a)
 
 
 if __name__ == "__main__":
