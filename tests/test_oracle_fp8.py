@@ -1,8 +1,11 @@
 """Pins of the FP8 oracle (oracle/fp8.py) against things other than itself:
 PyTorch's CPU float8 types (decode of every code, encode of random values and
 of every midpoint), a brute-force nearest search with ties to the even code,
-exact integer arithmetic for the GEMM, and closed forms of the scaling."""
+exact integer arithmetic for the GEMM, closed forms of the scaling, and the
+closed-form error of rounding to 3 or 2 significand bits."""
 import numpy as np
+
+import oracle
 import pytest
 import torch
 
@@ -143,25 +146,92 @@ def test_round_bf16_matches_torch():
     assert np.array_equal(F.round_bf16(x), ref)
 
 
+def rne_rel_rms(m):
+    """RMS relative error of rounding to nearest with m stored significand
+    bits, for values spread log-uniformly within a binade (as a Gaussian's
+    are, over the few binades that hold most of its mass): the error is
+    uniform on +-2^-m / 2 of the binade, so its RMS is 2^-m / sqrt(12) of it,
+    and the value's significand 1 + f has density 1 / ((1 + f) ln 2), giving
+    E[(1 + f)^-2] = (1/2 - 1/8) / ln 2."""
+    return 2.0 ** -m / np.sqrt(12.0) * np.sqrt((0.5 - 0.125) / np.log(2.0))
+
+
+@pytest.mark.parametrize("fmt,m", [(F.E4M3, 3), (F.E5M2, 2)])
+def test_quantised_gemm_error_matches_the_rounding_closed_form(fmt, m):
+    """Per-tensor current scaling then rounding to 3 (E4M3) or 2 (E5M2)
+    significand bits: each element's relative error has the closed-form RMS
+    above, and a product of two independently quantised Gaussian operands
+    over a long K sums those errors in quadrature, sqrt(2) times it."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((256, 2048))
+    w = rng.standard_normal((384, 2048))
+    qx, _, ix = F.quantize(x, fmt)
+    qw, _, iw = F.quantize(w, fmt)
+    eps = rne_rel_rms(m)
+    e_elem = oracle.rel_fro(F.fp8_decode(qx, fmt) * float(ix), x)
+    assert 0.95 < e_elem / eps < 1.05, e_elem / eps
+    e_gemm = oracle.rel_fro(F.fp8_gemm(qx, qw, fmt, fmt, ix, iw), x @ w.T)
+    assert 0.95 < e_gemm / (np.sqrt(2.0) * eps) < 1.05, e_gemm / (np.sqrt(2.0) * eps)
+
+
 @pytest.mark.parametrize("grad_fmt", [F.E4M3, F.E5M2])
 def test_fp8_step_within_quantisation_error_of_exact_step(grad_fmt):
-    """The FP8 step approximates the exact step: every output within the error
-    that 3-bit (2-bit) significands allow (about 2^-4 (2^-3) per element,
-    averaging down in the products), and visibly different from it (so the
-    quantisation really took place). A transposed operand, a wrong shard or a
-    misapplied scale gives errors of order one."""
+    """The FP8 step against the exact step, output by output, at the error
+    the recipe predicts: activations and weights in E4M3 (eps4 per element),
+    the gradients dZ and dU in grad_fmt (eps_g), errors of independent
+    roundings adding in quadrature and carried forward by the products:
+
+      U, Y   sqrt(2) eps4                        (X, A quantised)
+      Zp, Z  sqrt(e_Y^2 + 2 eps4^2)              (Y's own error, Y and B quantised)
+      dU, da sqrt(eps_g^2 + eps4^2)              (dZ and B quantised)
+      dB     sqrt(e_Y^2 + eps4^2 + eps_g^2)      (Y carried and quantised, dZ quantised)
+      dXp, dX, dA  sqrt(e_dU^2 + eps4^2 + eps_g^2)
+
+    Each error must lie within [0.85, 1.2] of its prediction. E5M2 where the
+    recipe has E4M3 doubles eps, and E4M3 where it has E5M2 halves eps_g, so
+    either swap moves some output's error out of its band (by factors 0.65 to
+    2); a transposed operand, a wrong shard or a misapplied scale gives errors
+    of order one. db comes from the unquantised dZ and is exact."""
+    exact, got = _fp8_step(grad_fmt)
+    assert set(got) == set(exact)
+    assert np.array_equal(got["db"], exact["db"])   # from the unquantised dZ
+    assert _out_of_band(exact, got, grad_fmt) == []
+
+
+def test_fp8_step_band_rejects_the_other_gradient_format():
+    """The step run with one gradient format, held to the other format's
+    prediction, leaves the band."""
+    for run, claimed in ((F.E4M3, F.E5M2), (F.E5M2, F.E4M3)):
+        exact, got = _fp8_step(run)
+        assert len(_out_of_band(exact, got, claimed)) >= 5
+
+
+def _fp8_step(grad_fmt):
     import dataclasses
-    import oracle
     from tp_inputs import get_config, make_inputs
     cfg = dataclasses.replace(get_config("gpt2s"), micro_batch=1, seq=256, h=256)
     inputs = make_inputs(cfg)
-    exact = oracle.run_config(cfg, inputs)
-    got = F.run_config_fp8(cfg, inputs, grad_fmt)
-    assert set(got) == set(exact)
-    bound = 0.12 if grad_fmt == F.E5M2 else 0.08
+    return oracle.run_config(cfg, inputs), F.run_config_fp8(cfg, inputs, grad_fmt)
+
+
+def _out_of_band(exact, got, grad_fmt):
+    """Outputs (other than db) whose error is outside [0.85, 1.2] x the
+    prediction for this gradient format."""
+    e4 = rne_rel_rms(3)
+    eg = rne_rel_rms(3 if grad_fmt == F.E4M3 else 2)
+    e_y = np.sqrt(2.0) * e4
+    e_du = np.sqrt(eg ** 2 + e4 ** 2)
+    pred = {"U": e_y, "Y": e_y, "Zp": np.sqrt(e_y ** 2 + 2 * e4 ** 2),
+            "Z": np.sqrt(e_y ** 2 + 2 * e4 ** 2), "dU": e_du, "da": e_du,
+            "dB": np.sqrt(e_y ** 2 + e4 ** 2 + eg ** 2),
+            "dXp": np.sqrt(e_du ** 2 + e4 ** 2 + eg ** 2),
+            "dX": np.sqrt(e_du ** 2 + e4 ** 2 + eg ** 2),
+            "dA": np.sqrt(e_du ** 2 + e4 ** 2 + eg ** 2)}
+    bad = []
     for k in exact:
         if k == "db":
-            assert np.array_equal(got[k], exact[k])   # from the unquantised dZ
             continue
-        e = oracle.rel_fro(got[k], exact[k])
-        assert 1e-3 < e < bound, (k, e)
+        r = oracle.rel_fro(got[k], exact[k]) / pred[k.split("_")[0]]
+        if not 0.85 < r < 1.2:
+            bad.append((k, round(r, 3)))
+    return bad
