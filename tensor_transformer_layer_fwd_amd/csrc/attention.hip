@@ -13,8 +13,11 @@
 // and 12-15), which two transposed LDS reads of the V tile produce at rows
 // base + 4*(lane/32) and base + 8 + 4*(lane/32).
 //
-// Per block: 128 queries of one (sequence, head), 4 waves of 32 queries. K and
-// V tiles of 64 keys go HBM -> LDS with direct copies through 3 stages.
+// Per block: 128 queries of one (sequence, head), 4 waves of 32 queries (and
+// up to two key groups). K and V tiles of 64 keys go HBM -> LDS with direct
+// copies through 3 stages. The running maximum of a row moves only when the
+// row's maximum grows by more than 2^8, so the outputs are rescaled rarely
+// and the exponents stay <= 8 (exact in the final division by the sum).
 #include <hip/hip_runtime.h>
 
 #include "device_common.h"
@@ -29,6 +32,8 @@ constexpr int kKB = 64;       // keys per tile
 constexpr int kStages = 3;
 constexpr int kTileBytes = kKB * kD * 2;  // one K or V tile
 constexpr int kStageBytes = 2 * kTileBytes;
+// growth of a row's running maximum (log2 units) before the forward rescales
+constexpr float kRegrow = 8.0f;
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
@@ -64,23 +69,28 @@ __device__ __forceinline__ void attn_sync() {
   asm volatile("" ::: "memory");
 }
 
-// KG key groups: with KG = 2 a block has 8 waves; waves w and w + 4 take the
-// same 32 queries and alternate key tiles (group g the tiles KG*i + g, through
-// a 3-stage ring of its own), and merge their running statistics and outputs
-// through LDS at the end. That halves the serial chain of a long causal row
-// and puts two waves on each SIMD when a shard has only one wave per SIMD's
-// worth of queries, so one wave's softmax runs beside the other's MFMAs.
-template <int KG>
-__global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
-  // one 3-stage ring of (K, V) tile pairs per key group, so that every stage
-  // offset a fragment read adds fits the instruction's 16-bit immediate
-  constexpr int NS = kStages;
+// A block takes QW * 32 queries of one (sequence, head) in QW query groups of
+// one wave each, and KG key groups: waves w and w + QW take the same 32
+// queries and alternate key tiles (group g the tiles KG*i + g, through an
+// NS-stage ring of its own), and merge their running statistics and outputs
+// through LDS at the end. Key groups shorten the serial chain of a long causal
+// row and put several waves on each SIMD when a shard has few queries, so one
+// wave's softmax runs beside another's MFMAs.
+template <int QW, int KG, int NS>
+__global__ __launch_bounds__(64 * QW * KG) void attn_fwd_kernel(AttnParams p) {
+  constexpr int QB = 32 * QW;  // queries per block
+  constexpr int WPW = 16 / QW;  // 1 KiB copy windows per wave and stage
+  static_assert(QW == 2 || QW == 4, "query groups");
+  static_assert(NS >= 2 && NS <= 4, "stages");
+  // one ring of (K, V) tile pairs per key group, so that every stage offset a
+  // fragment read adds fits the instruction's 16-bit immediate
   constexpr int kRing = NS * kStageBytes;
   constexpr int kLds = KG * kRing;
+  static_assert((KG - 1) * QW * 34 * 64 * 4 <= kLds, "LDS for the key-group merge");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int qw = wave & 3, grp = wave >> 2;  // query sub-block, key group
-  const int nqb = static_cast<int>((p.seq + kQB - 1) / kQB);
+  const int qw = wave % QW, grp = wave / QW;  // query group, key group
+  const int nqb = static_cast<int>((p.seq + QB - 1) / QB);
   // the longest causal rows first: query blocks in decreasing order
   const int qb = nqb - 1 - static_cast<int>(blockIdx.x % nqb);
   const int bh = static_cast<int>(blockIdx.x / nqb);
@@ -93,25 +103,23 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept for the whole pass
   const int ql = lane & 31, half = lane >> 5;
-  const int q = qb * kQB + qw * 32 + ql;
+  const int q = qb * QB + qw * 32 + ql;
   const int64_t qrow = row0 + (q < seq ? q : seq - 1);
   bf16x8_t qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
     qf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + qrow * p.ld_qkv + h * kD + 16 * ks + 8 * half);
-  // land them before any tile copy, so the copy waits below count copies only
-  attn_wait_vmcnt<0>();
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) asm volatile("" : "+v"(qf[ks]));
+  // (issued before the first tile copies and so, loads returning in order,
+  // landed whenever those copies have)
 
   // ---- tile copies: 16 windows of 1 KiB per (K, V) pair (8 of K, 8 of V),
-  // KG pairs per stage, four windows per wave; window w goes to group w/16's
+  // KG pairs per stage, WPW windows per wave; window w goes to group w/16's
   // ring, tile (w/8)%2 (K or V), rows 8*(w%8) .. +7; lane L copies row
   // 8*(w%8) + L/8, physical chunk L%8.
-  const uint16_t* src[4];
+  const uint16_t* src[WPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int w = wave * 4 + i, t = (w / 8) % 2, r = 8 * (w % 8) + lane / 8, pc = lane % 8;
+  for (int i = 0; i < WPW; ++i) {
+    const int w = wave * WPW + i, t = (w / 8) % 2, r = 8 * (w % 8) + lane / 8, pc = lane % 8;
     const int c = pc ^ (t == 0 ? kswz(r) : vswz(r));
     src[i] = qkv + (row0 + r) * p.ld_qkv + (1 + t) * hd + h * kD + c * 8;
   }
@@ -121,8 +129,8 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
   auto issue = [&](auto stage_c, int kp) {
     uint8_t* st = attn_lds<kLds>() + decltype(stage_c)::value * kStageBytes;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int w = wave * 4 + i, r = 8 * (w % 8) + lane / 8;
+    for (int i = 0; i < WPW; ++i) {
+      const int w = wave * WPW + i, r = 8 * (w % 8) + lane / 8;
       const int64_t kb = static_cast<int64_t>(kp) * KG + w / 16;
       // keys past the sequence read its last row (they are masked)
       const int64_t over = kb * kKB + r - (seq - 1);
@@ -136,15 +144,15 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
 
   // key tiles this block needs: all tiles up to its last query's
   const int nkb_seq = static_cast<int>((seq + kKB - 1) / kKB);
-  const int qlast = min(static_cast<int>(seq) - 1, qb * kQB + kQB - 1);
+  const int qlast = min(static_cast<int>(seq) - 1, qb * QB + QB - 1);
   const int nkb = p.causal ? min(nkb_seq, qlast / kKB + 1) : nkb_seq;
-  const int wq_last = qb * kQB + qw * 32 + 31;  // this wave's last query
+  const int wq_last = qb * QB + qw * 32 + 31;  // this wave's last query
 
   const float scale = p.scale_log2;  // log2(e) / sqrt(64)
   float m_run = -INFINITY, l_run = 0.0f;
   f32x16_t o[2] = {f32x16_t{}, f32x16_t{}};
 
-  const int wq_first = qb * kQB + qw * 32;     // this wave's first query
+  const int wq_first = qb * QB + qw * 32;     // this wave's first query
 
   // per-lane LDS byte addresses of the fragment reads within stage 0 (this
   // key group's tile pair)
@@ -206,40 +214,53 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
                      : "=v"(hi) : "v"(va[st][db]), "i"(SOFF + 8 * 128));  // key row + 8
         vf[st][db] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-    // scale and mask (register r of half m: key k0 + 32m + 8*(r/4) + 4*half + r%4);
-    // tiles wholly below the diagonal and inside the sequence need no mask
+    // mask (register r of half m: key k0 + 32m + 8*(r/4) + 4*half + r%4, seen
+    // when 32m + 8*(r/4) + r%4 <= lim); tiles wholly below the diagonal and
+    // inside the sequence need no mask. The maximum is taken on the raw scores
+    // (the scale is positive).
     const bool interior = (!p.causal || k0 + kKB - 1 <= wq_first) && k0 + kKB <= seq;
     float mx = -INFINITY;
+    if (interior) {
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[m][r] * scale;
-        if (!interior) {
-          const int key = k0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
-          if (key >= seq || (p.causal && key > q)) v = -INFINITY;
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[m][r], s[m][r + 1]));
+    } else {
+      const int lim = min(p.causal ? q : 0x7fffffff, static_cast<int>(seq) - 1) - k0 - 4 * half;
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = 32 * m + 8 * (r / 4) + (r % 4) <= lim ? s[m][r] : -INFINITY;
+          s[m][r] = v;
+          mx = fmaxf(mx, v);
         }
-        s[m][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;  // a row with no visible key yet
-    const float corr = __builtin_amdgcn_exp2f(m_run - m_use);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale;
+    // Lazy rescaling: the running maximum moves only when a row's maximum
+    // grows by more than kRegrow (log2 units), so exponents stay <= kRegrow
+    // and most tiles skip rescaling the outputs. The lanes of a query (lane,
+    // lane + 32) hold the same mx and m_run.
+    const bool grow = mx > m_run + kRegrow;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float corr = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.0f;  // 0 from -inf
+      m_run = grow ? mx : m_run;
+      l_run *= corr;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) o[db] *= corr;
+    }
+    const float m_use = m_run == -INFINITY ? 0.0f : m_run;  // a row with no visible key yet
     float sum = 0.0f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(s[m][r] - m_use);  // argument <= 0
+        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[m][r], scale, -m_use));
         s[m][r] = e;
         sum += e;
       }
     sum += __shfl_xor(sum, 32);
-    l_run = l_run * corr + sum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 2; ++db) o[db] *= corr;
+    l_run += sum;
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int st = 0; st < 4; ++st)
@@ -269,24 +290,25 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
       constexpr int J = decltype(jc)::value;
       const int kp = kp0 + J;
       if (kp < nkp) {
-        if constexpr (NS == 3) {
-          if (kp + 1 < nkp) attn_wait_vmcnt<4>();  // stage kp+1's copies may still fly
-          else attn_wait_vmcnt<0>();
-        } else {
-          attn_wait_vmcnt<0>();
-        }
+        // the copies of the stages after kp (up to NS - 2 of them) may still fly
+        const int later = min(NS - 2, nkp - 1 - kp);
+        if (NS >= 4 && later >= 2) attn_wait_vmcnt<(NS >= 4 ? 2 : 0) * WPW>();
+        else if (NS >= 3 && later >= 1) attn_wait_vmcnt<(NS >= 3 ? 1 : 0) * WPW>();
+        else attn_wait_vmcnt<0>();
         attn_sync();  // stage kp landed for every wave; stage (kp+NS-1)%NS is free
         if (kp + NS - 1 < nkp) issue(std::integral_constant<int, (J + NS - 1) % NS>{}, kp + NS - 1);
         compute(jc, kp * KG + grp);
       }
     });
   }
-  if constexpr (KG == 2) {
-    // merge the key groups: group 1 leaves (m, l, O^T) in LDS, group 0 folds
-    // them into its own; lane data at float index (wave%4 * 34 + j) * 64 + lane
+  if constexpr (KG > 1) {
+    // merge the key groups in group order: groups 1 .. KG-1 leave (m, l, O^T)
+    // in LDS, group 0 folds them into its own; lane data of group g, query
+    // group qw at float index (((g - 1) * QW + qw) * 34 + j) * 64 + lane
     attn_sync();  // every wave is done with the stages
-    float* x = reinterpret_cast<float*>(attn_lds<kLds>()) + qw * 34 * 64 + lane;
-    if (grp == 1) {
+    float* base = reinterpret_cast<float*>(attn_lds<kLds>()) + lane;
+    if (grp > 0) {
+      float* x = base + ((grp - 1) * QW + qw) * 34 * 64;
       x[0] = m_run;
       x[64] = l_run;
 #pragma unroll
@@ -295,17 +317,21 @@ __global__ __launch_bounds__(256 * KG) void attn_fwd_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r) x[(2 + 16 * db + r) * 64] = o[db][r];
     }
     attn_sync();
-    if (grp == 1) return;
-    const float m1 = x[0], l1 = x[64];
-    const float m_new = fmaxf(m_run, m1);
-    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
-    const float c0 = __builtin_amdgcn_exp2f(m_run - m_use), c1 = __builtin_amdgcn_exp2f(m1 - m_use);
-    l_run = l_run * c0 + l1 * c1;
-    m_run = m_new;
+    if (grp > 0) return;
 #pragma unroll
-    for (int db = 0; db < 2; ++db)
+    for (int g = 1; g < KG; ++g) {
+      const float* x = base + ((g - 1) * QW + qw) * 34 * 64;
+      const float m1 = x[0], l1 = x[64];
+      const float m_new = fmaxf(m_run, m1);
+      const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+      const float c0 = __builtin_amdgcn_exp2f(m_run - m_use), c1 = __builtin_amdgcn_exp2f(m1 - m_use);
+      l_run = l_run * c0 + l1 * c1;
+      m_run = m_new;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * c0 + x[(2 + 16 * db + r) * 64] * c1;
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] = o[db][r] * c0 + x[(2 + 16 * db + r) * 64] * c1;
+    }
   }
 
   // ---- output: lane holds query q and d = 32*db + 8*(r/4) + 4*half + r%4
@@ -901,13 +927,16 @@ hipError_t launch_attention_bwd(const AttnBwdParams& p, hipStream_t s) {
 }
 
 hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s) {
-  const int64_t blocks = p.batch * p.heads * ((p.seq + kQB - 1) / kQB);
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  // two key groups per block while the grid leaves SIMDs with one wave
-  if (blocks < 2 * 256)
-    hipLaunchKernelGGL(attn_fwd_kernel<2>, dim3(static_cast<unsigned>(blocks)), dim3(512), 0, s, p);
+  const int64_t bh = p.batch * p.heads;
+  const int64_t blocks128 = bh * ((p.seq + 127) / 128);
+  if (blocks128 > 0x3fffffff) return hipErrorInvalidConfiguration;
+  const int cus = device_shape().cus;
+  if (blocks128 < 2 * cus)  // two key groups while the grid leaves SIMDs with one wave
+    hipLaunchKernelGGL((attn_fwd_kernel<4, 2, 3>), dim3(static_cast<unsigned>(blocks128)),
+                       dim3(512), 0, s, p);
   else
-    hipLaunchKernelGGL(attn_fwd_kernel<1>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<4, 1, 3>), dim3(static_cast<unsigned>(blocks128)),
+                       dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -212,13 +212,14 @@ class ShardStep:
     def mlp_forward_fp8(self):
         cfg, o, inp, q, qs = self.cfg, self.out, self.inp, self.q, self.qs
         F = cfg.F
+        # X and every shard's weights, up to six tensors per pair of launches:
+        # the tensors the tensor-parallel group holds at the start
+        self._quant_many([(inp["X"], "X", "Xt")] +
+                         [t for i in cfg.shards
+                          for t in ((self._col("A", i, F), f"A{i}", f"At{i}"),
+                                    (self._row("B", i, F), f"B{i}", f"Bt{i}"))])
         for n, i in enumerate(cfg.shards):
             a_i = self._col("a", i, F) if cfg.has_bias else None
-            # the shard's weights (and X, once) in one pair of launches: the
-            # tensors one GPU of the tensor-parallel group holds at the start
-            first = [(inp["X"], "X", "Xt")] if n == 0 else []
-            self._quant_many(first + [(self._col("A", i, F), f"A{i}", f"At{i}"),
-                                      (self._row("B", i, F), f"B{i}", f"Bt{i}")])
             L.tp_fp8_column_linear_fwd(q["X"], q[f"At{i}"], qs["X"], qs[f"At{i}"], a_i,
                                        o[f"Y_{i}"], o[f"U_{i}"])
             self._quant2(o[f"Y_{i}"], f"Y{i}", f"Yt{i}")
