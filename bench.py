@@ -98,10 +98,13 @@ def attention_core_flops(cfg):
 
 
 class Call:
-    def __init__(self, name, fn, flops, nbytes, single, geom=None):
+    def __init__(self, name, fn, flops, nbytes, single, geom=None, post=None):
         self.name, self.fn, self.flops, self.bytes = name, fn, flops, nbytes
         self.single = single  # one kernel launch: its duration is that kernel's
         self.geom = geom or {}
+        # the rest of the step, run after the call when it is timed where the
+        # step runs it (time_in_step)
+        self.post = post
 
 
 def shard_calls(step, i=0):
@@ -152,7 +155,8 @@ def shard_calls(step, i=0):
         fw = p * 2 * 2 * T * h * F
         bw = 2 * T * p * F * e + 2 * T * h * e + 2 * p * F * h * 4  # Y, dU; dZ, X; dB, dA
         geom = {"T": T, "h": h, "F": F, "p": p, "fused": fused}
-        calls.append(Call("mlp_step_rows", lambda: step.mlp_step("rows"), fr, br, fused, geom))
+        calls.append(Call("mlp_step_rows", lambda: step.mlp_step("rows"), fr, br, fused, geom,
+                          post=lambda: step.mlp_step("wgrad")))
         calls.append(Call("mlp_step_wgrad", lambda: step.mlp_step("wgrad"), fw, bw, fused, geom))
         calls.append(Call("mlp_step", lambda: step.mlp_step(), fr + fw, br + bw, False, geom))
     elif cfg.mlp:
@@ -227,6 +231,38 @@ def time_call(fn, reps):
     e1.record(s)
     e1.synchronize()
     return e0.elapsed_time(e1) / reps
+
+
+def time_in_step(fn, post, reps):
+    """Average device duration (ms) of fn where the step runs it: HIP events
+    on its stream just before and after it, the rest of the step (post)
+    between repetitions. Both parts replay as captured graphs, so the host
+    enqueues the next call while the device still runs the previous post."""
+    import torch
+    graphs = []
+    for part in (fn, post):
+        for _ in range(2):
+            part()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            part()
+        graphs.append(g)
+    g_fn, g_post = graphs
+    for _ in range(3):
+        g_fn.replay()
+        g_post.replay()
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(s)
+        g_fn.replay()
+        e1.record(s)
+        g_post.replay()
+    torch.cuda.synchronize()
+    return sum(e0.elapsed_time(e1) for e0, e1 in ev) / reps
 
 
 def time_steps(step, steps, warmup):
@@ -432,6 +468,11 @@ def roofline(cfg, step, reps):
         if c.single and (best is None or ms > best[1]):
             best = (c, ms)
     c, ms = best
+    how = "back-to-back launches in one graph"
+    if c.post is not None:
+        ms = time_in_step(c.fn, c.post, reps)
+        per_call[c.name]["us_in_step"] = round(ms * 1e3, 2)
+        how = "HIP events around the launch inside the step, the rest of the step between"
     s = ms * 1e-3
     tf, gbs = c.flops / s / 1e12, c.bytes / s / 1e9
     hbm = c.bytes / (PEAK_HBM_GBS * 1e9) > c.flops / (PEAK_BF16_TFLOPS * 1e12)
@@ -444,7 +485,7 @@ def roofline(cfg, step, reps):
            "traffic": round(tr["traffic_bytes_per_launch"]) if tr else None,
            "algorithmic_bytes": c.bytes, "gemm_flops": c.flops, "tflops": round(tf, 1),
            "GB/s": round(gbs, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
-           "us_per_launch": round(ms * 1e3, 2), **c.geom}
+           "us_per_launch": round(ms * 1e3, 2), "timing": how, **c.geom}
     return rec, per_call
 
 
