@@ -47,6 +47,26 @@ __global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmP
   }
 }
 
+// Two weight gradients in one launch (TN, fp32, unsplit, 128 x 128 tiles
+// with 32-wide K-tiles in four stages): product 0's tiles, product 1's
+// tiles, then each product's column-sum pass-1 units (gemm_pipe_block runs
+// those for block indices past its tiles). Where each product alone fills
+// only part of the CUs, one launch puts both products' tiles on them at once.
+__global__ __launch_bounds__(256) void gemm_wgrad2_kernel(GemmParams p0, GemmParams p1, int nt0,
+                                                          int nt1) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < nt0) {
+    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, b);
+  } else if (b < nt0 + nt1) {
+    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p1, b - nt0);
+  } else if (b < nt0 + nt1 + p0.cs_blocks) {
+    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, nt0 + (b - nt0 - nt1));
+  } else {
+    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(
+        p1, nt1 + (b - nt0 - nt1 - p0.cs_blocks));
+  }
+}
+
 // The same for the 8-wave 256x192 tile in both products (64-wide K-tiles, two
 // stages), which share their stage arrays.
 template <int EKD>
@@ -266,6 +286,19 @@ hipError_t launch_pair256(const GemmParams& pw, const GemmParams& pd, int ekd, c
 }
 
 }  // namespace
+
+hipError_t launch_gemm_wgrad2(const GemmParams& a, const GemmParams& b, hipStream_t s) {
+  GemmParams p0 = a, p1 = b;
+  p0.xcds = p1.xcds = device_shape().xcds;
+  for (const GemmParams* q : {&p0, &p1})
+    if (q->splitk != 1 || q->M % 128 || q->N % 128 || q->K % 32) return hipErrorInvalidValue;
+  const int64_t nt0 = (p0.M / 128) * (p0.N / 128), nt1 = (p1.M / 128) * (p1.N / 128);
+  const int64_t grid = nt0 + nt1 + p0.cs_blocks + p1.cs_blocks;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(gemm_wgrad2_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p0, p1,
+                     static_cast<int>(nt0), static_cast<int>(nt1));
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bwd_pair(const GemmParams& pw0, const GemmParams& pd0, int kind, int ekd,
                                 const PairRider& rider, hipStream_t s) {

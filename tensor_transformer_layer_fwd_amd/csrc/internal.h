@@ -289,6 +289,13 @@ hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);
 int64_t colsum_chunks(const ColsumParams& p);
 bool colsum_vec_ok(const ColsumParams& p);
 hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s);
+// Pass 2 of two column sums (a's units, then b's) in one launch.
+hipError_t launch_colsum_pass2_two(const ColsumParams& a, int na, const ColsumParams& b, int nb,
+                                   hipStream_t s);
+// Two unsplit weight gradients (TN, fp32) on the 128 x 128 tile in one launch,
+// each with its carried column-sum pass-1 units (cs_blocks) after both
+// products' tiles.
+hipError_t launch_gemm_wgrad2(const GemmParams& p0, const GemmParams& p1, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s);
 hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s);

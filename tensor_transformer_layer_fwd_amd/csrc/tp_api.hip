@@ -183,6 +183,70 @@ ColsumParams bias_grad_params(const void* dOut, float* dbias, int64_t T, int64_t
   return c;
 }
 
+// Carried column sums of a weight gradient running on the pipelined kernel.
+void carry_colsums(GemmParams* p, const ColsumParams& cs) {
+  const int64_t nchunks = colsum_chunks(cs);
+  const int64_t units = (cs.N + 255) / 256 * nchunks;
+  p->cs = cs;
+  p->cs_nchunks = static_cast<int>(nchunks);
+  p->cs_units = static_cast<int>(units);
+  p->cs_blocks = static_cast<int>(units < kColsumBlocks ? units : kColsumBlocks);
+}
+
+size_t two_wgrads_cs_offset(int64_t T, int64_t n0, bool bias0) {
+  return bias0 ? (colsum_workspace_bytes(T, n0) + 255) / 256 * 256 : 0;
+}
+
+// Two weight gradients with their bias gradients, overwritten:
+// dW0 = In0^T dOut0 (k0 x n0), db0 = column sums of dOut0, and the same for 1.
+// Where both products run unsplit on the 128 x 128 tile with their column
+// sums carried, one launch runs both products and one launch both column-sum
+// second passes; otherwise they are two tp_linear_bwd_wgrad calls. ws holds
+// both products' column-sum partials (two_wgrads_cs_offset, then product 1's)
+// or either call's workspace.
+int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64_t k0, int64_t n0,
+               int64_t ld_in0, int64_t ld_dout0, int64_t ld_dw0, const void* In1,
+               const void* dOut1, float* dW1, float* db1, int64_t k1, int64_t n1, int64_t ld_in1,
+               int64_t ld_dout1, int64_t ld_dw1, int64_t T, int dt, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  if (dt == TP_BF16) {
+    const SplitPlan pl0 = plan_gemm_bf16(k0, n0, T, true), pl1 = plan_gemm_bf16(k1, n1, T, true);
+    const size_t off1 = two_wgrads_cs_offset(T, n0, db0 != nullptr);
+    const size_t need = off1 + (db1 ? colsum_workspace_bytes(T, n1) : 0);
+    if (pl0.tile == kPipe128x128 && pl1.tile == kPipe128x128 && pl0.splitk == 1 &&
+        pl1.splitk == 1 && (need == 0 || (ws && ws_bytes >= need))) {
+      char* w = static_cast<char*>(ws);
+      GemmParams p0 = wgrad_params(In0, dOut0, dW0, T, k0, n0, ld_in0, ld_dout0, ld_dw0, 0, ws);
+      GemmParams p1 = wgrad_params(In1, dOut1, dW1, T, k1, n1, ld_in1, ld_dout1, ld_dw1, 0, ws);
+      p0.splitk = p1.splitk = 1;
+      p0.k_chunk = p1.k_chunk = T;
+      const ColsumParams c0 = bias_grad_params(dOut0, db0, T, n0, ld_dout0, dt, 0,
+                                               reinterpret_cast<float*>(w));
+      const ColsumParams c1 = bias_grad_params(dOut1, db1, T, n1, ld_dout1, dt, 0,
+                                               reinterpret_cast<float*>(w + off1));
+      if (gemm_pipe_epilogue(p0, pl0) == kEpiF32 && gemm_pipe_epilogue(p1, pl1) == kEpiF32 &&
+          (!db0 || colsum_vec_ok(c0)) && (!db1 || colsum_vec_ok(c1))) {
+        if (db0) carry_colsums(&p0, c0);
+        if (db1) carry_colsums(&p1, c1);
+        hipError_t e = launch_gemm_wgrad2(p0, p1, stream);
+        const bool two0 = db0 && p0.cs_nchunks > 1, two1 = db1 && p1.cs_nchunks > 1;
+        if (e == hipSuccess && two0 && two1)
+          e = launch_colsum_pass2_two(p0.cs, p0.cs_nchunks, p1.cs, p1.cs_nchunks, stream);
+        else if (e == hipSuccess && two0)
+          e = launch_colsum_pass2(p0.cs, p0.cs_nchunks, stream);
+        else if (e == hipSuccess && two1)
+          e = launch_colsum_pass2(p1.cs, p1.cs_nchunks, stream);
+        return hip_status(e);
+      }
+    }
+  }
+  int st = tp_linear_bwd_wgrad(In0, dOut0, dW0, db0, T, k0, n0, ld_in0, ld_dout0, ld_dw0, 0,
+                               static_cast<tp_dtype>(dt), ws, ws_bytes, stream);
+  if (st != TP_OK) return st;
+  return tp_linear_bwd_wgrad(In1, dOut1, dW1, db1, T, k1, n1, ld_in1, ld_dout1, ld_dw1, 0,
+                             static_cast<tp_dtype>(dt), ws, ws_bytes, stream);
+}
+
 // Pair kind and K slices of the paired backward launch of a bf16 linear layer
 // (kPairNone: the layer's products cannot pair). Operand alignment is checked
 // at the call.
@@ -658,7 +722,10 @@ int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype 
   // the row launch's counters, then the stacked weight gradients' scratch;
   // the per-product path uses the workspace from its start
   const size_t rows = dt == TP_BF16 ? mlp_step_workspace_bytes(T, h, F, p) : 0;
-  const size_t wg = w1 > w2 ? w1 : w2;
+  // either weight gradient's own call, or both products' column-sum partials
+  const size_t both = two_wgrads_cs_offset(T, h, true) + colsum_workspace_bytes(T, pF);
+  size_t wg = w1 > w2 ? w1 : w2;
+  wg = wg > both ? wg : both;
   const size_t fused = rows + wg;
   const size_t each = fb > wg ? fb : wg;
   *bytes = fused > each ? fused : each;
@@ -712,11 +779,8 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
   // shards: dB = Y^T dZ ([p*F, h]) with db = column sums of dZ, and
   // dA = X^T dU ([h, p*F]) with da = column sums of dU.
   auto wgrads = [&](void* ws, size_t ws_bytes) {
-    int r = tp_linear_bwd_wgrad(Y, dZ, dB, db, T, pF, h, ld_y, ld_dz, ld_db, 0, dt, ws, ws_bytes,
-                                stream);
-    if (r != TP_OK) return r;
-    return tp_linear_bwd_wgrad(X, dU, dA, da, T, h, pF, ld_x, ld_u, ld_da, 0, dt, ws, ws_bytes,
-                               stream);
+    return two_wgrads(Y, dZ, dB, db, pF, h, ld_y, ld_dz, ld_db, X, dU, dA, da, h, pF, ld_x, ld_u,
+                      ld_da, T, dt, ws, ws_bytes, stream);
   };
   if (fused) {
     if (phases & 1) {
