@@ -597,25 +597,32 @@ __device__ __forceinline__ void attn_bwd_kv_block(const AttnBwdParams& p, const 
         sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[ks], kf[ks], sv, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], vf[ks], dp, 0, 0, 0);
       }
-      // P and dS (masked entries 0)
+      // P and dS (masked entries 0): register r = 4j + e holds query
+      // q0 + 4*half + off, off = 32m + 8j + e, seen when lo <= off <= hi. The
+      // mask is taken on one wave-uniform branch, not per element.
+      auto p_ds = [&](auto masked_c) {
+        constexpr bool kMasked = decltype(masked_c)::value;
+        const int base = q0 + 4 * half;
+        const int lo = p.causal ? key - base : -0x7fffffff;
+        const int hi = static_cast<int>(seq) - 1 - base;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int qi = 32 * m + 8 * j + 4 * half;
-        const float4 l4 = *reinterpret_cast<const float4*>(stats + qi);
-        const float4 d4 = *reinterpret_cast<const float4*>(stats + 64 + qi);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
+        for (int j = 0; j < 4; ++j) {
+          const int qi = 32 * m + 8 * j + 4 * half;
+          const float4 l4 = *reinterpret_cast<const float4*>(stats + qi);
+          const float4 d4 = *reinterpret_cast<const float4*>(stats + 64 + qi);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * j + e;
-          float pr = __builtin_amdgcn_exp2f(sv[r] * scale - lv[e] * 1.4426950408889634f);
-          if (!interior) {
-            const int qq = q0 + qi + e;
-            if (qq >= seq || (p.causal && key > qq)) pr = 0.0f;
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * j + e, off = 32 * m + 8 * j + e;
+            float pr = __builtin_amdgcn_exp2f(sv[r] * scale - lv[e] * 1.4426950408889634f);
+            if constexpr (kMasked) pr = (off >= lo && off <= hi) ? pr : 0.0f;
+            sv[r] = pr;
+            dp[r] = pr * (dp[r] - dl[e]);
           }
-          sv[r] = pr;
-          dp[r] = pr * (dp[r] - dl[e]);
         }
-      }
+      };
+      if (interior) p_ds(std::false_type{});
+      else p_ds(std::true_type{});
       // dV^T += dC^T P and dK^T += Q^T dS over the half's two 16-query steps
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -790,15 +797,22 @@ __device__ __forceinline__ void attn_bwd_q_block(const AttnBwdParams& p, const i
         sv = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qf[ks], sv, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[ks], df[ks], dp, 0, 0, 0);
       }
+      // dS (masked entries 0): register r holds key k0 + 4*half + off,
+      // off = 32m + 8*(r/4) + r%4, seen when off <= lim; one wave-uniform
+      // branch, not per element
+      auto ds = [&](auto masked_c) {
+        constexpr bool kMasked = decltype(masked_c)::value;
+        const int lim =
+            min(p.causal ? q : 0x7fffffff, static_cast<int>(seq) - 1) - k0 - 4 * half - 32 * m;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = __builtin_amdgcn_exp2f(sv[r] * scale - lq);
-        if (!interior) {
-          const int key = k0 + 32 * m + 8 * (r / 4) + 4 * half + (r % 4);
-          if (key >= seq || (p.causal && key > q)) pr = 0.0f;
+        for (int r = 0; r < 16; ++r) {
+          float pr = __builtin_amdgcn_exp2f(sv[r] * scale - lq);
+          if constexpr (kMasked) pr = 8 * (r / 4) + (r % 4) <= lim ? pr : 0.0f;
+          dp[r] = pr * (dp[r] - dl);
         }
-        dp[r] = pr * (dp[r] - dl);
-      }
+      };
+      if (interior) ds(std::false_type{});
+      else ds(std::true_type{});
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
         const int st = 2 * m + hh;
