@@ -558,6 +558,39 @@ int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_sca
                              int64_t ld_y, tp_act act, hipStream_t stream);
 
 /*
+ * tp_fp8_column_linear_fwd with act TP_ACT_GELU_TANH that also leaves the
+ * maxima of |Y_i| the quantisation of Y_i needs ("Megatron" page, mixed-precision
+ * training: FP8 with per-tensor current scaling): each wave of the epilogue
+ * stores the largest |stored bf16 value| of its part of an output tile into
+ * one float of y_amax, tp_fp8_amax_slots(T, n, h) of them in all (every slot is
+ * written; nothing needs clearing). tp_fp8_quantize_both_from_amax then
+ * quantises Y_i in one launch with the same codes and scale as
+ * tp_fp8_quantize_both. TP_ERR_SHAPE where no FP8 tile fits the shape.
+ */
+int tp_fp8_column_linear_fwd_amax(const void* Xq, const void* Atq, const float* x_scale_inv,
+                                  const float* a_scale_inv, const void* bias_i, void* Y_i,
+                                  void* U_i, int64_t T, int64_t h, int64_t n, int64_t ld_x,
+                                  int64_t ld_at, int64_t ld_y, float* y_amax,
+                                  hipStream_t stream);
+
+/*
+ * Slots of the maxima the _amax products write for an M x N output of
+ * K-long products (one per wave of each output tile of the planned FP8 tile);
+ * pure host function. TP_ERR_SHAPE where no FP8 tile fits.
+ */
+int tp_fp8_amax_slots(int64_t M, int64_t N, int64_t K, int64_t* slots);
+
+/*
+ * tp_fp8_quantize_both with the maxima of |X| already given (the amax slots
+ * of the product that wrote X, n_amax of them): the codes of X and X^T and
+ * 1/s in one launch, equal to tp_fp8_quantize_both's when the slots cover X.
+ */
+int tp_fp8_quantize_both_from_amax(const void* X, int64_t rows, int64_t cols, int64_t ld_x,
+                                   tp_dtype dt, tp_fp8_format fmt, void* Q, int64_t ld_q, void* Qt,
+                                   int64_t ld_qt, float* scale_inv, const float* amax,
+                                   int64_t n_amax, hipStream_t stream);
+
+/*
  * FP8 row-parallel forward partial: Zp_i = Y_i B_i (fp32 [T, h]) from
  * Yq = codes of Y_i [T, k] (E4M3) and Btq = codes of B_i^T [h, k] (E4M3).
  */
@@ -577,6 +610,17 @@ int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout
                             void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
                             int64_t ld_w, int64_t ld_u, int64_t ld_din, tp_dtype out_dt,
                             hipStream_t stream);
+
+/*
+ * tp_fp8_linear_bwd_dgrad with act TP_ACT_GELU_TANH and a bf16 dIn, that also
+ * leaves the maxima of |dIn| in din_amax (tp_fp8_amax_slots(T, k, n) floats),
+ * as tp_fp8_column_linear_fwd_amax does for Y_i.
+ */
+int tp_fp8_linear_bwd_dgrad_amax(const void* dOutq, const void* Wq, const float* dout_scale_inv,
+                                 const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U,
+                                 void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
+                                 int64_t ld_w, int64_t ld_u, int64_t ld_din, float* din_amax,
+                                 hipStream_t stream);
 
 /* Workspace bytes of tp_fp8_linear_bwd_wgrad (split-K partials and bias sums). */
 int tp_fp8_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, size_t* bytes);

@@ -87,6 +87,13 @@ SIGNATURES = {
     "tp_fp8_quantize_multi_workspace_size": (_int, [_int, ctypes.POINTER(ctypes.c_size_t)]),
     "tp_fp8_column_linear_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                         _i64, _i64, _i64, _int, _vp]),
+    "tp_fp8_column_linear_fwd_amax": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                             _i64, _i64, _i64, _i64, _vp, _vp]),
+    "tp_fp8_amax_slots": (_int, [_i64, _i64, _i64, ctypes.POINTER(ctypes.c_int64)]),
+    "tp_fp8_quantize_both_from_amax": (_int, [_vp, _i64, _i64, _i64, _int, _int, _vp, _i64, _vp,
+                                              _i64, _vp, _vp, _i64, _vp]),
+    "tp_fp8_linear_bwd_dgrad_amax": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _vp, _i64, _i64, _i64,
+                                            _i64, _i64, _i64, _i64, _vp, _vp]),
     "tp_fp8_row_linear_fwd_partial": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64,
                                              _i64, _i64, _vp]),
     "tp_fp8_linear_bwd_dgrad": (_int, [_vp, _vp, _vp, _vp, _int, _vp, _int, _vp, _i64, _i64,
@@ -645,7 +652,33 @@ def tp_fp8_quantize_both_multi(items, workspace, stream=None):
         _ws_bytes(workspace), _stream(stream)))
 
 
-def tp_fp8_column_linear_fwd(Xq, Atq, x_si, a_si, bias, Y, U, act="gelu", stream=None):
+def tp_fp8_amax_slots(M: int, N: int, K: int) -> int:
+    """Floats of amax slots the _amax FP8 products write for an M x N output."""
+    out = ctypes.c_int64(0)
+    _check("tp_fp8_amax_slots", lib().tp_fp8_amax_slots(M, N, K, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_fp8_quantize_both_from_amax(X, Q, Qt, scale_inv, amax, n_amax, fmt="e4m3", stream=None):
+    """tp_fp8_quantize_both with the maxima of |X| given (n_amax amax slots of
+    the product that wrote X): one launch."""
+    chk = _Operands("tp_fp8_quantize_both_from_amax")
+    chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
+    rows, cols = X.shape
+    u8, f32 = _torch_dtypes("u8"), _torch_dtypes("f32")
+    chk("Q", Q, (rows, cols), u8)("Qt", Qt, (cols, rows), u8)
+    chk("scale_inv", scale_inv, (1,), f32)
+    if amax is None or amax.dim() != 1 or amax.numel() < n_amax:
+        raise ValueError(f"tp_fp8_quantize_both_from_amax: amax must hold {n_amax} floats")
+    chk("amax", amax, (amax.numel(),), f32).done(stream)
+    _check("tp_fp8_quantize_both_from_amax", lib().tp_fp8_quantize_both_from_amax(
+        _ptr(X), rows, cols, _ld(X), _dt(X), _fmt(fmt), _ptr(Q), _ld(Q), _ptr(Qt), _ld(Qt),
+        _ptr(scale_inv), _ptr(amax), int(n_amax), _stream(stream)))
+
+
+def tp_fp8_column_linear_fwd(Xq, Atq, x_si, a_si, bias, Y, U, act="gelu", amax=None,
+                             stream=None):
+    """With amax (act "gelu" only): also the amax slots of |Y| (tp_fp8_amax_slots floats)."""
     chk = _Operands("tp_fp8_column_linear_fwd")
     u8, f32, bf = _torch_dtypes("u8"), _torch_dtypes("f32"), _torch_dtypes("bf16")
     chk("Xq", Xq, _shape2(Xq), u8)
@@ -655,7 +688,16 @@ def tp_fp8_column_linear_fwd(Xq, Atq, x_si, a_si, bias, Y, U, act="gelu", stream
     chk("x_scale_inv", x_si, (1,), f32)("a_scale_inv", a_si, (1,), f32)
     none = _act(act) == TP_ACT_NONE
     chk("bias", bias, (n,), bf, optional=True)("Y", Y, (T, n), bf)
-    chk("U", U, (T, n), bf, optional=none).done(stream)
+    chk("U", U, (T, n), bf, optional=none)
+    if amax is not None:
+        if none:
+            raise ValueError("tp_fp8_column_linear_fwd: amax needs act 'gelu'")
+        chk("amax", amax, (tp_fp8_amax_slots(T, n, h),), f32).done(stream)
+        _check("tp_fp8_column_linear_fwd_amax", lib().tp_fp8_column_linear_fwd_amax(
+            _ptr(Xq), _ptr(Atq), _ptr(x_si), _ptr(a_si), _ptr(bias), _ptr(Y), _ptr(U), T, h, n,
+            _ld(Xq), _ld(Atq), _ld(Y), _ptr(amax), _stream(stream)))
+        return
+    chk.done(stream)
     _check("tp_fp8_column_linear_fwd", lib().tp_fp8_column_linear_fwd(
         _ptr(Xq), _ptr(Atq), _ptr(x_si), _ptr(a_si), _ptr(bias), _ptr(Y), _ptr(U), T, h, n,
         _ld(Xq), _ld(Atq), _ld(Y), _act(act), _stream(stream)))
@@ -676,7 +718,8 @@ def tp_fp8_row_linear_fwd_partial(Yq, Btq, y_si, b_si, Zp, stream=None):
 
 
 def tp_fp8_linear_bwd_dgrad(dOutq, Wq, d_si, w_si, dIn, U=None, act="none", dout_fmt="e5m2",
-                            stream=None):
+                            amax=None, stream=None):
+    """With amax (act "gelu", bf16 dIn only): also the amax slots of |dIn|."""
     chk = _Operands("tp_fp8_linear_bwd_dgrad")
     u8, f32, bf = _torch_dtypes("u8"), _torch_dtypes("f32"), _torch_dtypes("bf16")
     chk("dOutq", dOutq, _shape2(dOutq), u8)
@@ -685,8 +728,17 @@ def tp_fp8_linear_bwd_dgrad(dOutq, Wq, d_si, w_si, dIn, U=None, act="none", dout
     k = Wq.shape[0]
     chk("dout_scale_inv", d_si, (1,), f32)("w_scale_inv", w_si, (1,), f32)
     chk("U", U, (T, k), bf, optional=_act(act) == TP_ACT_NONE)
-    chk("dIn", dIn, (T, k), _torch_dtypes("bf16", "f32")).done(stream)
+    chk("dIn", dIn, (T, k), _torch_dtypes("bf16", "f32"))
     ld_u = _ld(U) if U is not None else k
+    if amax is not None:
+        if _act(act) != TP_ACT_GELU_TANH or dIn.dtype != _torch_dtypes("bf16")[0]:
+            raise ValueError("tp_fp8_linear_bwd_dgrad: amax needs act 'gelu' and a bf16 dIn")
+        chk("amax", amax, (tp_fp8_amax_slots(T, k, n),), f32).done(stream)
+        _check("tp_fp8_linear_bwd_dgrad_amax", lib().tp_fp8_linear_bwd_dgrad_amax(
+            _ptr(dOutq), _ptr(Wq), _ptr(d_si), _ptr(w_si), _fmt(dout_fmt), _ptr(U), _ptr(dIn), T,
+            k, n, _ld(dOutq), _ld(Wq), ld_u, _ld(dIn), _ptr(amax), _stream(stream)))
+        return
+    chk.done(stream)
     _check("tp_fp8_linear_bwd_dgrad", lib().tp_fp8_linear_bwd_dgrad(
         _ptr(dOutq), _ptr(Wq), _ptr(d_si), _ptr(w_si), _fmt(dout_fmt), _ptr(U), _act(act),
         _ptr(dIn), T, k, n, _ld(dOutq), _ld(Wq), ld_u, _ld(dIn), _dt(dIn), _stream(stream)))

@@ -222,6 +222,10 @@ hipError_t launch_fp8_quantize(Fp8QuantParams p, hipStream_t s) {
   hipLaunchKernelGGL(fp8_amax_kernel, dim3(p.nblk), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_fp8_cast(p, s);
+}
+
+hipError_t launch_fp8_cast(Fp8QuantParams p, hipStream_t s) {
   if (p.transpose) {
     hipLaunchKernelGGL(fp8_cast_t_kernel, dim3(cast_t_blocks(p)), dim3(kThreads), 0, s, p);
   } else {

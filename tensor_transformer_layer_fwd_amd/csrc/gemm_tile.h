@@ -519,6 +519,7 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
                                   : nullptr;
   const int64_t ldc = (EK == kEpiF32 && p.splitk > 1) ? p.N : p.ldc;
 
+  float amax_run = 0.0f;  // largest |stored value| of this lane (amax epilogues)
   float bias8[NCH][8];
 #pragma unroll
   for (int C = 0; C < NCH; ++C) {
@@ -597,7 +598,10 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
           for (int q = 0; q < 8; ++q) v[q] += bias8[C][q];
           store8(p.c2, row * p.ldc2 + col, v, 1);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] = gelu_tanh(v[q]);
+          for (int q = 0; q < 8; ++q) {
+            v[q] = gelu_tanh(v[q]);
+            amax_run = fmaxf(amax_run, fabsf(v[q]));
+          }
         } else if constexpr (EK == kEpiDGelu) {
           const u32x4_t w = upre[i & 1][P];
           float u[8];
@@ -613,7 +617,10 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
             store8(p.c2, row * p.ldc2 + col, y, 1);
           }
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] *= gelu_tanh_grad(u[q]);
+          for (int q = 0; q < 8; ++q) {
+            v[q] *= gelu_tanh_grad(u[q]);
+            amax_run = fmaxf(amax_run, fabsf(v[q]));
+          }
           const u32x4_t wv{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                            pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
           *reinterpret_cast<u32x4_t*>(static_cast<uint16_t*>(p.c) + o) = wv;
@@ -629,6 +636,19 @@ __device__ __forceinline__ void gemm_pipe_tile(const GemmParams& p, const int64_
       }
     }
   });
+  if constexpr (EK == kEpiBiasGelu || EK == kEpiDGelu) {
+    if (p.amax) {
+      // the wave's largest |value| as stored: rounding to bf16 is monotonic
+      // and symmetric, so that is the bf16 rounding of the largest |v|
+      float m = amax_run;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      if (lane == 0) {
+        const int64_t tile = (m0 / BM) * (p.N / BN) + n0 / BN;
+        p.amax[tile * NW + wave] = __uint_as_float((pack_bf16x2(m, 0.0f) & 0xffffu) << 16);
+      }
+    }
+  }
   if constexpr (CSUM) {
     if (p.cs_part) {
       // row lanes of each wave row's sums in LDS: [WM][16][BN] floats

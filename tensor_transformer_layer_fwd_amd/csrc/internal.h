@@ -66,6 +66,11 @@ struct GemmParams {
   int f8;
   const float* sa_inv;
   const float* sb_inv;
+  // bias + GeLU and GeLU' epilogues of the pipelined kernel: when set, each
+  // wave stores the largest |stored bf16 value| of its part of the output
+  // tile at amax[tile * waves + wave] (tile = tile row * tile columns + tile
+  // column), for a quantiser that then needs no pass of its own over them
+  float* amax;
   // XCDs the blocks go round-robin over (device_shape().xcds; set by the
   // launchers): each takes a run of consecutive tiles
   int xcds;
@@ -103,6 +108,9 @@ struct Fp8QuantParams {
 };
 int fp8_amax_blocks(int64_t rows, int64_t cols);
 hipError_t launch_fp8_quantize(Fp8QuantParams p, hipStream_t s);
+// The cast launch alone, with p.partial / p.nblk holding maxima the caller
+// already has (amax slots of the producing GEMM's epilogue).
+hipError_t launch_fp8_cast(Fp8QuantParams p, hipStream_t s);
 // Up to kFp8MaxMulti tensors, each quantised with transpose (and optionally its
 // own layout), in two launches; each tensor has its own partial array.
 constexpr int kFp8MaxMulti = 6;

@@ -369,6 +369,27 @@ int fp8_both_params(const void* X, int64_t rows, int64_t cols, int64_t ld_x, int
   return TP_OK;
 }
 
+// Output tile and waves of an FP8 tile (as launched by the FP8 GEMM), or
+// false for a tile it does not use.
+bool fp8_tile_shape(int tile, int* bm, int* bn, int* waves) {
+  switch (tile) {
+    case kPipe128x256: *bm = 128, *bn = 256, *waves = 8; return true;
+    case kPipe128x128: *bm = 128, *bn = 128, *waves = 4; return true;
+    case kPipe256x192: *bm = 256, *bn = 192, *waves = 8; return true;
+    case kPipe128x192: *bm = 128, *bn = 192, *waves = 4; return true;
+    default: return false;
+  }
+}
+
+// Amax slots the FP8 epilogue of an unsplit M x N x K product writes: one
+// per wave of every output tile of the planned tile; 0 when no FP8 tile fits.
+int64_t fp8_amax_slot_count(int64_t M, int64_t N, int64_t K) {
+  const SplitPlan pl = plan_gemm_fp8(M, N, K, false);
+  int bm = 0, bn = 0, w = 0;
+  if (!fp8_tile_shape(pl.tile, &bm, &bn, &w) || M % bm || N % bn) return 0;
+  return (M / bm) * (N / bn) * w;
+}
+
 bool pair_needs_finish(const PairSetup& q) {
   return q.plan.splitk > 1 || (q.carry && q.pw.cs_nchunks > 1);
 }
@@ -1077,10 +1098,10 @@ int tp_fp8_quantize_both_multi(int n, const void* const* X, const int64_t* rows,
   return hip_status(launch_fp8_quantize_multi(ps, n, stream));
 }
 
-int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
-                             const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
-                             int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
-                             int64_t ld_y, tp_act act, hipStream_t stream) {
+static int fp8_column_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
+                          const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
+                          int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
+                          int64_t ld_y, tp_act act, float* amax, hipStream_t stream) {
   if (!Xq || !Atq || !x_scale_inv || !a_scale_inv || !Y_i) return TP_ERR_NULL;
   if (!act_ok(act)) return TP_ERR_ACT;
   if (act != TP_ACT_NONE && !U_i) return TP_ERR_NULL;
@@ -1107,7 +1128,27 @@ int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_sca
   p.f8 = 1;  // E4M3 x E4M3
   p.sa_inv = x_scale_inv;
   p.sb_inv = a_scale_inv;
+  p.amax = amax;
   return run_gemm_fp8(p, false, 0, stream);
+}
+
+int tp_fp8_column_linear_fwd(const void* Xq, const void* Atq, const float* x_scale_inv,
+                             const float* a_scale_inv, const void* bias_i, void* Y_i, void* U_i,
+                             int64_t T, int64_t h, int64_t n, int64_t ld_x, int64_t ld_at,
+                             int64_t ld_y, tp_act act, hipStream_t stream) {
+  return fp8_column_fwd(Xq, Atq, x_scale_inv, a_scale_inv, bias_i, Y_i, U_i, T, h, n, ld_x, ld_at,
+                        ld_y, act, nullptr, stream);
+}
+
+int tp_fp8_column_linear_fwd_amax(const void* Xq, const void* Atq, const float* x_scale_inv,
+                                  const float* a_scale_inv, const void* bias_i, void* Y_i,
+                                  void* U_i, int64_t T, int64_t h, int64_t n, int64_t ld_x,
+                                  int64_t ld_at, int64_t ld_y, float* y_amax,
+                                  hipStream_t stream) {
+  if (!y_amax) return TP_ERR_NULL;
+  if (fp8_amax_slot_count(T, n, h) == 0) return TP_ERR_SHAPE;
+  return fp8_column_fwd(Xq, Atq, x_scale_inv, a_scale_inv, bias_i, Y_i, U_i, T, h, n, ld_x, ld_at,
+                        ld_y, TP_ACT_GELU_TANH, y_amax, stream);
 }
 
 int tp_fp8_row_linear_fwd_partial(const void* Yq, const void* Btq, const float* y_scale_inv,
@@ -1136,11 +1177,11 @@ int tp_fp8_row_linear_fwd_partial(const void* Yq, const void* Btq, const float* 
   return run_gemm_fp8(p, false, 0, stream);
 }
 
-int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
-                            const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U, tp_act act,
-                            void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
-                            int64_t ld_w, int64_t ld_u, int64_t ld_din, tp_dtype out_dt,
-                            hipStream_t stream) {
+static int fp8_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
+                     const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U, tp_act act,
+                     void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout, int64_t ld_w,
+                     int64_t ld_u, int64_t ld_din, tp_dtype out_dt, float* amax,
+                     hipStream_t stream) {
   if (!dOutq || !Wq || !dout_scale_inv || !w_scale_inv || !dIn) return TP_ERR_NULL;
   if (!fmt_ok(dout_fmt) || !dtype_ok(out_dt)) return TP_ERR_DTYPE;
   if (!act_ok(act)) return TP_ERR_ACT;
@@ -1168,7 +1209,50 @@ int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout
   p.f8 = 1 + dout_fmt;  // dOut in dout_fmt, W in E4M3
   p.sa_inv = dout_scale_inv;
   p.sb_inv = w_scale_inv;
+  p.amax = amax;
   return run_gemm_fp8(p, false, 0, stream);
+}
+
+int tp_fp8_linear_bwd_dgrad(const void* dOutq, const void* Wq, const float* dout_scale_inv,
+                            const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U, tp_act act,
+                            void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
+                            int64_t ld_w, int64_t ld_u, int64_t ld_din, tp_dtype out_dt,
+                            hipStream_t stream) {
+  return fp8_dgrad(dOutq, Wq, dout_scale_inv, w_scale_inv, dout_fmt, U, act, dIn, T, k, n,
+                   ld_dout, ld_w, ld_u, ld_din, out_dt, nullptr, stream);
+}
+
+int tp_fp8_linear_bwd_dgrad_amax(const void* dOutq, const void* Wq, const float* dout_scale_inv,
+                                 const float* w_scale_inv, tp_fp8_format dout_fmt, const void* U,
+                                 void* dIn, int64_t T, int64_t k, int64_t n, int64_t ld_dout,
+                                 int64_t ld_w, int64_t ld_u, int64_t ld_din, float* din_amax,
+                                 hipStream_t stream) {
+  if (!din_amax) return TP_ERR_NULL;
+  if (fp8_amax_slot_count(T, k, n) == 0) return TP_ERR_SHAPE;
+  return fp8_dgrad(dOutq, Wq, dout_scale_inv, w_scale_inv, dout_fmt, U, TP_ACT_GELU_TANH, dIn, T,
+                   k, n, ld_dout, ld_w, ld_u, ld_din, TP_BF16, din_amax, stream);
+}
+
+int tp_fp8_amax_slots(int64_t M, int64_t N, int64_t K, int64_t* slots) {
+  if (!slots) return TP_ERR_NULL;
+  if (!dim_ok(M) || !dim_ok(N) || !dim_ok(K)) return TP_ERR_SHAPE;
+  *slots = fp8_amax_slot_count(M, N, K);
+  return *slots > 0 ? TP_OK : TP_ERR_SHAPE;
+}
+
+int tp_fp8_quantize_both_from_amax(const void* X, int64_t rows, int64_t cols, int64_t ld_x,
+                                   tp_dtype dt, tp_fp8_format fmt, void* Q, int64_t ld_q, void* Qt,
+                                   int64_t ld_qt, float* scale_inv, const float* amax,
+                                   int64_t n_amax, hipStream_t stream) {
+  if (!amax) return TP_ERR_NULL;
+  if (n_amax < 1 || n_amax > 0x7fffffff || !aligned(amax, 4)) return TP_ERR_SHAPE;
+  Fp8QuantParams q{};
+  // the maxima are given: the parameter check's workspace is the amax array
+  const int st = fp8_both_params(X, rows, cols, ld_x, dt, fmt, Q, ld_q, Qt, ld_qt, scale_inv,
+                                 const_cast<float*>(amax), kFp8AmaxBlocks * sizeof(float), &q);
+  if (st != TP_OK) return st;
+  q.nblk = static_cast<int>(n_amax);
+  return hip_status(launch_fp8_cast(q, stream));
 }
 
 int tp_fp8_linear_bwd_wgrad_workspace_size(int64_t T, int64_t k, int64_t n, size_t* bytes) {

@@ -190,6 +190,17 @@ class ShardStep:
         self.q = {k: torch.empty(*v, **u8) for k, v in shapes.items()}
         self.qs = {k: torch.empty(1, device=self.device) for k in shapes}
         self.qws = torch.empty(L.tp_fp8_quantize_multi_workspace_size(6), **u8)
+        # amax slots of Y_i (fc1's epilogue) and dU_i (fc2 dgrad's epilogue):
+        # their quantisation then runs as one launch; shapes no FP8 tile fits
+        # keep the two-pass quantiser
+        try:
+            self.amax_n = L.tp_fp8_amax_slots(T, F, h)
+        except L.TPError:
+            self.amax_n = 0
+        if self.amax_n:
+            f32 = dict(device=self.device, dtype=torch.float32)
+            self.amax_y = {i: torch.empty(self.amax_n, **f32) for i in self.cfg.shards}
+            self.amax_du = torch.empty(self.amax_n, **f32)
         return max(L.tp_fp8_linear_bwd_wgrad_workspace_size(T, F, h),
                    L.tp_fp8_linear_bwd_wgrad_workspace_size(T, h, F))
 
@@ -220,9 +231,16 @@ class ShardStep:
                                     (self._row("B", i, F), f"B{i}", f"Bt{i}"))])
         for n, i in enumerate(cfg.shards):
             a_i = self._col("a", i, F) if cfg.has_bias else None
-            L.tp_fp8_column_linear_fwd(q["X"], q[f"At{i}"], qs["X"], qs[f"At{i}"], a_i,
-                                       o[f"Y_{i}"], o[f"U_{i}"])
-            self._quant2(o[f"Y_{i}"], f"Y{i}", f"Yt{i}")
+            if self.amax_n:
+                L.tp_fp8_column_linear_fwd(q["X"], q[f"At{i}"], qs["X"], qs[f"At{i}"], a_i,
+                                           o[f"Y_{i}"], o[f"U_{i}"], amax=self.amax_y[i])
+                L.tp_fp8_quantize_both_from_amax(o[f"Y_{i}"], q[f"Y{i}"], q[f"Yt{i}"],
+                                                 qs[f"Y{i}"], self.amax_y[i], self.amax_n)
+                qs[f"Yt{i}"] = qs[f"Y{i}"]
+            else:
+                L.tp_fp8_column_linear_fwd(q["X"], q[f"At{i}"], qs["X"], qs[f"At{i}"], a_i,
+                                           o[f"Y_{i}"], o[f"U_{i}"])
+                self._quant2(o[f"Y_{i}"], f"Y{i}", f"Yt{i}")
             L.tp_fp8_row_linear_fwd_partial(q[f"Y{i}"], q[f"Bt{i}"], qs[f"Y{i}"], qs[f"Bt{i}"],
                                             o[f"Zp_{i}"])
         if "Z" in o:
@@ -235,12 +253,18 @@ class ShardStep:
         self._quant2(inp["dZ"], "dZ", "dZt", g)
         for n, i in enumerate(cfg.shards):
             L.tp_fp8_linear_bwd_dgrad(q["dZ"], q[f"B{i}"], qs["dZ"], qs[f"B{i}"], o[f"dU_{i}"],
-                                      U=o[f"U_{i}"], act="gelu", dout_fmt=g)
+                                      U=o[f"U_{i}"], act="gelu", dout_fmt=g,
+                                      amax=self.amax_du if self.amax_n else None)
             L.tp_fp8_linear_bwd_wgrad(q[f"Yt{i}"], q["dZt"], qs[f"Yt{i}"], qs["dZt"],
                                       o[f"dB_{i}"], dOut=inp["dZ"],
                                       dbias=o["db"] if (cfg.has_bias and n == 0) else None,
                                       dout_fmt=g, workspace=self.workspace)
-            self._quant2(o[f"dU_{i}"], "dU", "dUt", g)
+            if self.amax_n:
+                L.tp_fp8_quantize_both_from_amax(o[f"dU_{i}"], q["dU"], q["dUt"], qs["dU"],
+                                                 self.amax_du, self.amax_n, fmt=g)
+                qs["dUt"] = qs["dU"]
+            else:
+                self._quant2(o[f"dU_{i}"], "dU", "dUt", g)
             L.tp_fp8_linear_bwd_dgrad(q["dU"], q[f"A{i}"], qs["dU"], qs[f"A{i}"], o[f"dXp_{i}"],
                                       act="none", dout_fmt=g)
             L.tp_fp8_linear_bwd_wgrad(q["Xt"], q["dUt"], qs["Xt"], qs["dUt"], o[f"dA_{i}"],

@@ -562,3 +562,22 @@ def test_noalloc_wgrad_rejects_shape_beyond_scratch(lib):
     with open(HEADER) as f:
         assert "#define TP_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)" in f.read()
     assert L.TP_NOALLOC_SCRATCH_BYTES == 32 << 20
+
+
+def test_fp8_amax_entry_points_reject_bad_arguments(lib):
+    fake = 1 << 20
+    out = ctypes.c_int64(0)
+    assert lib.tp_fp8_amax_slots(4096, 1536, 768, ctypes.byref(out)) == 0 and out.value > 0
+    assert out.value % 4 == 0
+    assert lib.tp_fp8_amax_slots(100, 1536, 768, ctypes.byref(out)) == -2   # no FP8 tile fits
+    assert lib.tp_fp8_amax_slots(4096, 1536, 768, None) == -1
+    args = (fake, fake, fake, fake, None, fake, fake, 4096, 768, 1536, 768, 768, 1536)
+    assert lib.tp_fp8_column_linear_fwd_amax(*args, None, None) == -1
+    assert lib.tp_fp8_column_linear_fwd_amax(fake, fake, fake, fake, None, fake, fake, 100, 768,
+                                             1536, 768, 768, 1536, fake, None) == -2
+    assert lib.tp_fp8_linear_bwd_dgrad_amax(fake, fake, fake, fake, 1, fake, fake, 4096, 1536,
+                                            768, 768, 768, 1536, 1536, None, None) == -1
+    assert lib.tp_fp8_quantize_both_from_amax(fake, 64, 64, 64, L.TP_BF16, 0, fake, 64, fake, 64,
+                                              fake, None, 16, None) == -1
+    assert lib.tp_fp8_quantize_both_from_amax(fake, 64, 64, 64, L.TP_BF16, 0, fake, 64, fake, 64,
+                                              fake, fake, 0, None) == -2

@@ -374,3 +374,63 @@ def test_quantize_both_multi(dev, n):
         q_ref, _, sinv = F.quantize(Xf, FMT[fmt])
         assert np.array_equal(Q.value(), q_ref) and np.array_equal(Qt.value(), q_ref.T)
         assert si.item() == float(sinv)
+
+
+@pytest.mark.parametrize("tile", [0, 12, 13, 14, 15])
+def test_fp8_amax_epilogues_give_the_two_pass_codes(dev, tile):
+    """fc1's bias + GeLU epilogue and fc2 dgrad's GeLU' epilogue leave the
+    largest |stored value| per (tile, wave) slot; the one-launch quantiser on
+    those slots gives exactly the codes and 1/s of the two-pass quantiser on
+    the same output, and of the oracle's quantiser (every FP8 tile forced)."""
+    import tensor_transformer_layer_fwd_amd as tp
+    _say(f"fp8 amax epilogues tile {tile}")
+    rng = np.random.default_rng(70 + tile)
+    T, h, n = 1536, 768, 768
+    Xf, Xb = rand_bf16(rng, (T, h), 1.0)
+    Atf, Atb = rand_bf16(rng, (n, h), 0.05)
+    af, ab = rand_bf16(rng, (1, n), 0.1)
+    dZf, dZb = rand_bf16(rng, (T, h), 1.0)
+    Bf, Bb = rand_bf16(rng, (n, h), 0.05)     # B_i [F, h] as stored
+    try:
+        tp.tp_set_gemm_override(tile)
+        Xq, xsi, _, _ = _quant_both(tp, Xf, Xb, "e4m3", False, dev)
+        Aq, asi, _, _ = _quant_both(tp, Atf, Atb, "e4m3", False, dev)
+        dq, dsi, _, _ = _quant_both(tp, dZf, dZb, "e5m2", False, dev)
+        Bq, bsi, _, _ = _quant_both(tp, Bf, Bb, "e4m3", False, dev)
+        slots = tp.tp_fp8_amax_slots(T, n, h)
+        outs = []
+        for what in ("fwd", "dgrad"):
+            Y = torch.empty(T, n, dtype=torch.bfloat16, device=dev)
+            U = torch.empty(T, n, dtype=torch.bfloat16, device=dev)
+            amax = torch.full((slots,), float("nan"), device=dev)
+            fmt = "e4m3" if what == "fwd" else "e5m2"
+            if what == "fwd":
+                tp.tp_fp8_column_linear_fwd(Xq.view, Aq.view, xsi, asi, to_dev_bf16(ab, dev)[0],
+                                            Y, U, amax=amax)
+            else:
+                Ud = to_dev_bf16(f32_to_bf16_bits((rng.standard_normal((T, n)) * 1.5)
+                                                  .astype(np.float32)), dev)
+                tp.tp_fp8_linear_bwd_dgrad(dq.view, Bq.view, dsi, bsi, Y, U=Ud, act="gelu",
+                                           dout_fmt="e5m2", amax=amax)
+            Q1, Qt1 = Codes(T, n, dev), Codes(n, T, dev)
+            s1 = torch.full((1,), float("nan"), device=dev)
+            tp.tp_fp8_quantize_both_from_amax(Y, Q1.view, Qt1.view, s1, amax, slots, fmt=fmt)
+            Q2, Qt2 = Codes(T, n, dev), Codes(n, T, dev)
+            s2 = torch.full((1,), float("nan"), device=dev)
+            ws = torch.empty(tp.tp_fp8_quantize_workspace_size(T, n), dtype=torch.uint8,
+                             device=dev)
+            tp.tp_fp8_quantize_both(Y, Q2.view, Qt2.view, s2, ws, fmt=fmt)
+            torch.cuda.synchronize()
+            outs.append((what, Y, amax, (Q1, Qt1, s1), (Q2, Qt2, s2), fmt))
+    finally:
+        tp.tp_set_gemm_override(0)
+    for what, Y, amax, (Q1, Qt1, s1), (Q2, Qt2, s2), fmt in outs:
+        y = Y.double().cpu().numpy()
+        a = amax.cpu().numpy()
+        assert not np.isnan(a).any(), f"{what}: a slot was not written"
+        assert a.max() == np.abs(y).max(), (what, a.max(), np.abs(y).max())
+        assert np.array_equal(Q1.value(), Q2.value()) and np.array_equal(Qt1.value(), Qt2.value())
+        assert s1.item() == s2.item()
+        q_ref, _, sinv = F.quantize(y, FMT[fmt])
+        assert np.array_equal(Q1.value(), q_ref) and np.array_equal(Qt1.value(), q_ref.T)
+        assert s1.item() == np.float32(sinv)
