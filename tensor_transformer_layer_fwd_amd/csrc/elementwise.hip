@@ -78,15 +78,6 @@ __global__ __launch_bounds__(256) void colsum_pass2_kernel(ColsumParams p, int n
   colsum_pass2_unit(p, blockIdx.x, nchunks, part);
 }
 
-// Pass 2 of two column sums in one launch: a's 64-column units, then b's.
-__global__ __launch_bounds__(256) void colsum_pass2_two_kernel(ColsumParams a, int na,
-                                                               ColsumParams b, int nb) {
-  __shared__ float part[4][64];
-  const int ua = static_cast<int>((a.N + 63) / 64);
-  if (static_cast<int>(blockIdx.x) < ua) colsum_pass2_unit(a, blockIdx.x, na, part);
-  else colsum_pass2_unit(b, blockIdx.x - ua, nb, part);
-}
-
 // Split-K fix-up (vector path) and column-sum pass 2 in one launch: blocks
 // below nfix run the fix-up, the rest one pass-2 unit each.
 __global__ __launch_bounds__(256) void splitk_fixup_colsum_kernel(GemmParams p, int nfix,
@@ -291,14 +282,6 @@ bool colsum_vec_ok(const ColsumParams& p) {
 hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s) {
   hipLaunchKernelGGL(colsum_pass2_kernel, dim3(static_cast<unsigned>((p.N + 63) / 64)), dim3(256),
                      0, s, p, nchunks);
-  return hipGetLastError();
-}
-
-hipError_t launch_colsum_pass2_two(const ColsumParams& a, int na, const ColsumParams& b, int nb,
-                                   hipStream_t s) {
-  const int64_t units = (a.N + 63) / 64 + (b.N + 63) / 64;
-  hipLaunchKernelGGL(colsum_pass2_two_kernel, dim3(static_cast<unsigned>(units)), dim3(256), 0, s,
-                     a, na, b, nb);
   return hipGetLastError();
 }
 

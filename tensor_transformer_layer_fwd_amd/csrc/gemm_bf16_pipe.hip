@@ -47,24 +47,87 @@ __global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmP
   }
 }
 
-// Two weight gradients in one launch (TN, fp32, unsplit, 128 x 128 tiles
-// with 32-wide K-tiles in four stages): product 0's tiles, product 1's
-// tiles, then each product's column-sum pass-1 units (gemm_pipe_block runs
-// those for block indices past its tiles). Where each product alone fills
-// only part of the CUs, one launch puts both products' tiles on them at once.
+// Two weight gradients in one launch (TN, fp32, 128 x 128 tiles with 32-wide
+// K-tiles in four stages): the tiles run over all of K (product 0's, then
+// product 1's), then each product's column-sum pass-1 units (gemm_pipe_block
+// runs those for block indices past its tiles), then the K slices of the
+// split tiles. Where each product alone fills only part of the CUs, one launch
+// puts both products' tiles on them at once; where the tiles leave a
+// remainder over the CUs, slicing the remaining tiles along K spreads them
+// over every CU instead of doubling the work of a few.
+constexpr int kWg = 128;  // tile rows and columns
+
+// K slice c of the split tiles: tile whole + c / sk, slice c % sk, into its
+// compact partial. The operands start at the tile's origin, so the tile body
+// runs at (0, 0) and its split-K epilogue stores rows of 128.
+__device__ __forceinline__ void wgrad_slice(const GemmParams& p0, const GemmParams& p1, int nt0,
+                                            const WgradSplit& sp, int c) {
+  const int t = sp.whole + c / sp.sk, kz = c % sp.sk;
+  const GemmParams& p = t < nt0 ? p0 : p1;
+  int64_t m0, n0;
+  tile_origin<kWg, kWg>(p, t < nt0 ? t : t - nt0, &m0, &n0);
+  GemmParams q = p;
+  q.a = static_cast<const uint16_t*>(p.a) + m0;  // In [T, k]: its columns m0 ..
+  q.b = static_cast<const uint16_t*>(p.b) + n0;  // dOut [T, n]: its columns n0 ..
+  q.M = q.N = kWg;
+  q.splitk = sp.sk;
+  q.ws = sp.part + static_cast<int64_t>(c) * kWg * kWg;
+  const int64_t kc = p.K / sp.sk;
+  gemm_pipe_tile<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(q, 0, 0, 0, kz * kc,
+                                                              static_cast<int>(kc / 32));
+}
+
 __global__ __launch_bounds__(256) void gemm_wgrad2_kernel(GemmParams p0, GemmParams p1, int nt0,
-                                                          int nt1) {
+                                                          int nt1, WgradSplit sp) {
   const int b = static_cast<int>(blockIdx.x);
-  if (b < nt0) {
-    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, b);
-  } else if (b < nt0 + nt1) {
-    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p1, b - nt0);
-  } else if (b < nt0 + nt1 + p0.cs_blocks) {
-    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, nt0 + (b - nt0 - nt1));
+  const int ncs = p0.cs_blocks + p1.cs_blocks;
+  if (b < sp.whole) {
+    if (b < nt0) gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, b);
+    else gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p1, b - nt0);
+  } else if (b < sp.whole + ncs) {
+    const int r = b - sp.whole;
+    if (r < p0.cs_blocks) gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, nt0 + r);
+    else gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p1, nt1 + r - p0.cs_blocks);
   } else {
-    gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(
-        p1, nt1 + (b - nt0 - nt1 - p0.cs_blocks));
+    wgrad_slice(p0, p1, nt0, sp, b - sp.whole - ncs);
   }
+}
+
+// After the weight gradients: blocks below nfix add the K slices of 8 rows of
+// a split tile, in slice order, into the tile's output (one float4 per thread,
+// every slice's load issued before the adds); the others run pass 2 of the
+// column sums, product 0's 64-column units (u0 of them), then product 1's.
+constexpr int kFinRows = 8;   // rows of a split tile per fix-up block
+constexpr int kMaxSlices = 16;
+__global__ __launch_bounds__(256) void wgrad2_finish_kernel(GemmParams p0, GemmParams p1, int nt0,
+                                                            WgradSplit sp, int nfix, int u0,
+                                                            int n0, int n1) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b >= nfix) {
+    __shared__ float part[4][64];
+    if (b - nfix < u0) colsum_pass2_unit(p0.cs, b - nfix, n0, part);
+    else colsum_pass2_unit(p1.cs, b - nfix - u0, n1, part);
+    return;
+  }
+  constexpr int C = kWg, PER = kWg / kFinRows;  // row groups of a tile
+  static_assert(kFinRows * C == 4 * 256, "one float4 per thread");
+  const int e = b / PER, grp = b % PER;
+  const int t = sp.whole + e;
+  const GemmParams& p = t < nt0 ? p0 : p1;
+  int64_t m0, n0t;
+  tile_origin<kWg, kWg>(p, t < nt0 ? t : t - nt0, &m0, &n0t);
+  const int idx = grp * kFinRows * C + static_cast<int>(threadIdx.x) * 4;  // within the tile
+  const float* src = sp.part + static_cast<int64_t>(e) * sp.sk * C * C + idx;
+  f32x4_t v[kMaxSlices];
+#pragma unroll
+  for (int z = 0; z < kMaxSlices; ++z)
+    if (z < sp.sk) v[z] = *reinterpret_cast<const f32x4_t*>(src + static_cast<int64_t>(z) * C * C);
+  f32x4_t acc = v[0];
+#pragma unroll
+  for (int z = 1; z < kMaxSlices; ++z)
+    if (z < sp.sk) acc += v[z];
+  float* dst = static_cast<float*>(p.c) + (m0 + idx / C) * p.ldc + n0t + idx % C;
+  *reinterpret_cast<f32x4_t*>(dst) = acc;
 }
 
 // The same for the 8-wave 256x192 tile in both products (64-wide K-tiles, two
@@ -287,16 +350,38 @@ hipError_t launch_pair256(const GemmParams& pw, const GemmParams& pd, int ekd, c
 
 }  // namespace
 
-hipError_t launch_gemm_wgrad2(const GemmParams& a, const GemmParams& b, hipStream_t s) {
+hipError_t launch_gemm_wgrad2(const GemmParams& a, const GemmParams& b, const WgradSplit& sp,
+                              hipStream_t s) {
   GemmParams p0 = a, p1 = b;
   p0.xcds = p1.xcds = device_shape().xcds;
   for (const GemmParams* q : {&p0, &p1})
     if (q->splitk != 1 || q->M % 128 || q->N % 128 || q->K % 32) return hipErrorInvalidValue;
   const int64_t nt0 = (p0.M / 128) * (p0.N / 128), nt1 = (p1.M / 128) * (p1.N / 128);
-  const int64_t grid = nt0 + nt1 + p0.cs_blocks + p1.cs_blocks;
+  if (sp.sk < 0 || sp.sk > kMaxSlices || sp.whole < 0 || sp.whole > nt0 + nt1 || (sp.sk == 0 && sp.whole != nt0 + nt1) ||
+      (sp.sk > 0 && (!sp.part || p0.K != p1.K || p0.K % (32LL * sp.sk))))
+    return hipErrorInvalidValue;
+  const int64_t nsl = sp.sk > 0 ? (nt0 + nt1 - sp.whole) * sp.sk : 0;
+  const int64_t grid = sp.whole + nsl + p0.cs_blocks + p1.cs_blocks;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(gemm_wgrad2_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p0, p1,
-                     static_cast<int>(nt0), static_cast<int>(nt1));
+                     static_cast<int>(nt0), static_cast<int>(nt1), sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad2_finish(const GemmParams& a, const GemmParams& b, const WgradSplit& sp,
+                                int n0, int n1, hipStream_t s) {
+  GemmParams p0 = a, p1 = b;
+  p0.xcds = p1.xcds = device_shape().xcds;
+  const int64_t nt0 = (p0.M / 128) * (p0.N / 128), nt1 = (p1.M / 128) * (p1.N / 128);
+  if (sp.sk > kMaxSlices) return hipErrorInvalidValue;
+  const int64_t nfix = sp.sk > 0 ? (kWg / kFinRows) * (nt0 + nt1 - sp.whole) : 0;
+  const int64_t u0 = n0 > 1 ? (p0.cs.N + 63) / 64 : 0, u1 = n1 > 1 ? (p1.cs.N + 63) / 64 : 0;
+  const int64_t grid = nfix + u0 + u1;
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(wgrad2_finish_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p0,
+                     p1, static_cast<int>(nt0), sp, static_cast<int>(nfix), static_cast<int>(u0),
+                     n0, n1);
   return hipGetLastError();
 }
 

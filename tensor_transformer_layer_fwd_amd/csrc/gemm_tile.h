@@ -292,6 +292,29 @@ __device__ __forceinline__ int xcd_group_rows(int c, int tiles_m, int tiles_n, i
   return 5 * cost <= 4 * base ? best : 8;
 }
 
+// Origin (m0, n0) of output tile `bid` of a product's grid of BM x BN tiles.
+// Blocks go round-robin over the XCDs, so each XCD takes a run of consecutive
+// tiles of a grouped column-major order (groups of xcd_group_rows rows).
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(const GemmParams& p, int bid, int64_t* m0,
+                                            int64_t* n0) {
+  const int tiles_m = static_cast<int>(p.M / BM);
+  const int tiles_n = static_cast<int>(p.N / BN);
+  const int ntiles = tiles_m * tiles_n;
+  int G = 8;
+  const int X = p.xcds;
+  if (X > 1 && ntiles % X == 0) {
+    bid = (bid % X) * (ntiles / X) + bid / X;
+    G = xcd_group_rows(ntiles / X, tiles_m, tiles_n, BM, BN);
+  }
+  const int group = bid / (G * tiles_n);
+  const int first_m = group * G;
+  const int gs = min(tiles_m - first_m, G);
+  const int in_group = bid - group * G * tiles_n;
+  *m0 = static_cast<int64_t>(first_m + in_group % gs) * BM;
+  *n0 = static_cast<int64_t>(in_group / gs) * BN;
+}
+
 // F8 = 0: bf16 operands; F8 = 1 + fmt_a + 2 * fmt_b: FP8 codes (both operands
 // K-contiguous, BK = 128 codes), fmt 0 = E4M3, 1 = E5M2.
 // One output tile of a product: rows m0 .. m0+BM-1, columns n0 .. n0+BN-1,
@@ -684,8 +707,7 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
   using OA = std::conditional_t<(F8 > 0), OperandF8<BM, NW>, Operand<AK, BM, BK, NW>>;
   using OB = std::conditional_t<(F8 > 0), OperandF8<BN, NW>, Operand<BKC, BN, BK, NW>>;
   constexpr int SB = OA::BYTES + OB::BYTES;
-  // ---- output tile: blocks go round-robin over the XCDs, so each XCD
-  // takes a run of consecutive tiles of a grouped column-major order
+  // ---- output tile
   const int tiles_m = static_cast<int>(p.M / BM);
   const int tiles_n = static_cast<int>(p.N / BN);
   const int ntiles = tiles_m * tiles_n;
@@ -701,19 +723,8 @@ __device__ __forceinline__ void gemm_pipe_block(const GemmParams& p, const int b
       return;
     }
   }
-  int bid = block - z * ntiles;
-  int G = 8;
-  const int X = p.xcds;
-  if (X > 1 && ntiles % X == 0) {
-    bid = (bid % X) * (ntiles / X) + bid / X;
-    G = xcd_group_rows(ntiles / X, tiles_m, tiles_n, BM, BN);
-  }
-  const int group = bid / (G * tiles_n);
-  const int first_m = group * G;
-  const int gs = min(tiles_m - first_m, G);
-  const int in_group = bid - group * G * tiles_n;
-  const int64_t m0 = static_cast<int64_t>(first_m + in_group % gs) * BM;
-  const int64_t n0 = static_cast<int64_t>(in_group / gs) * BN;
+  int64_t m0, n0;
+  tile_origin<BM, BN>(p, block - z * ntiles, &m0, &n0);
 
   const int64_t kbeg = static_cast<int64_t>(z) * p.k_chunk;
   const int nk = static_cast<int>((min(p.K, kbeg + p.k_chunk) - kbeg) / BK);

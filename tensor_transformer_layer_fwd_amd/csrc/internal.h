@@ -297,13 +297,25 @@ hipError_t launch_colsum(const ColsumParams& p, hipStream_t s);
 int64_t colsum_chunks(const ColsumParams& p);
 bool colsum_vec_ok(const ColsumParams& p);
 hipError_t launch_colsum_pass2(const ColsumParams& p, int nchunks, hipStream_t s);
-// Pass 2 of two column sums (a's units, then b's) in one launch.
-hipError_t launch_colsum_pass2_two(const ColsumParams& a, int na, const ColsumParams& b, int nb,
-                                   hipStream_t s);
-// Two unsplit weight gradients (TN, fp32) on the 128 x 128 tile in one launch,
-// each with its carried column-sum pass-1 units (cs_blocks) after both
-// products' tiles.
-hipError_t launch_gemm_wgrad2(const GemmParams& p0, const GemmParams& p1, hipStream_t s);
+// Two weight gradients (TN, fp32) on the 128 x 128 tile in one launch, each
+// with its carried column-sum pass-1 units (cs_blocks) after both products'
+// tiles. Tiles of the combined list (product 0's, then product 1's) below
+// `whole` run over all of K; the others (a remainder over the CUs) run after
+// the column-sum units as sk blocks each, over K slices of K / sk rows, and
+// store fp32 partials ([tile - whole][slice][128 x 128], compact), which
+// launch_wgrad2_finish adds.
+struct WgradSplit {
+  float* part;
+  int whole;  // tiles run over all of K (the combined tile count when sk = 0)
+  int sk;     // K slices of each remaining tile; 0: none
+};
+hipError_t launch_gemm_wgrad2(const GemmParams& p0, const GemmParams& p1, const WgradSplit& sp,
+                              hipStream_t s);
+// After launch_gemm_wgrad2: the sums of the split tiles' K-slice partials
+// into their outputs (slices in K order), and the column sums' pass 2 of the
+// products with more than one row chunk (n0, n1 chunks; 1 or less: none).
+hipError_t launch_wgrad2_finish(const GemmParams& p0, const GemmParams& p1, const WgradSplit& sp,
+                                int n0, int n1, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, hipStream_t s);
 hipError_t launch_bias_act(const BiasActParams& p, hipStream_t s);
 hipError_t launch_attention_fwd(const AttnParams& p, hipStream_t s);

@@ -197,13 +197,34 @@ size_t two_wgrads_cs_offset(int64_t T, int64_t n0, bool bias0) {
   return bias0 ? (colsum_workspace_bytes(T, n0) + 255) / 256 * 256 : 0;
 }
 
+// K slices of the remaining tiles when 128 x 128 tiles leave a remainder over
+// the CUs: as many as fit one slice per CU, at most 16, with K a multiple of
+// 32 per slice; 0 when no remainder or fewer than 2 slices fit.
+int two_wgrads_slices(int64_t tiles, int64_t T, int cus) {
+  const int64_t rem = tiles % cus;
+  if (rem == 0) return 0;
+  for (int64_t sk = std::min<int64_t>(16, cus / rem); sk >= 2; --sk)
+    if (T % (32 * sk) == 0) return static_cast<int>(sk);
+  return 0;
+}
+
+// Scratch of the stacked weight gradients: both products' column-sum
+// partials, then the K-slice partials of the split tiles (at most one
+// 128 x 128 fp32 tile per CU).
+size_t two_wgrads_bytes(int64_t T, int64_t n0, int64_t n1) {
+  const size_t cs = two_wgrads_cs_offset(T, n0, true) + colsum_workspace_bytes(T, n1);
+  return (cs + 255) / 256 * 256 + static_cast<size_t>(device_shape().cus) * 128 * 128 * 4;
+}
+
 // Two weight gradients with their bias gradients, overwritten:
 // dW0 = In0^T dOut0 (k0 x n0), db0 = column sums of dOut0, and the same for 1.
 // Where both products run unsplit on the 128 x 128 tile with their column
-// sums carried, one launch runs both products and one launch both column-sum
-// second passes; otherwise they are two tp_linear_bwd_wgrad calls. ws holds
-// both products' column-sum partials (two_wgrads_cs_offset, then product 1's)
-// or either call's workspace.
+// sums carried, one launch runs both products (the tiles past the last whole
+// multiple of the CU count as K slices, when that fits) and one launch adds
+// the slices and runs both column-sum second passes; otherwise they are two
+// tp_linear_bwd_wgrad calls. ws holds both products' column-sum partials
+// (two_wgrads_cs_offset, then product 1's), then the slices' partials
+// (two_wgrads_bytes in all), or either call's workspace.
 int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64_t k0, int64_t n0,
                int64_t ld_in0, int64_t ld_dout0, int64_t ld_dw0, const void* In1,
                const void* dOut1, float* dW1, float* db1, int64_t k1, int64_t n1, int64_t ld_in1,
@@ -228,14 +249,20 @@ int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64
           (!db0 || colsum_vec_ok(c0)) && (!db1 || colsum_vec_ok(c1))) {
         if (db0) carry_colsums(&p0, c0);
         if (db1) carry_colsums(&p1, c1);
-        hipError_t e = launch_gemm_wgrad2(p0, p1, stream);
-        const bool two0 = db0 && p0.cs_nchunks > 1, two1 = db1 && p1.cs_nchunks > 1;
-        if (e == hipSuccess && two0 && two1)
-          e = launch_colsum_pass2_two(p0.cs, p0.cs_nchunks, p1.cs, p1.cs_nchunks, stream);
-        else if (e == hipSuccess && two0)
-          e = launch_colsum_pass2(p0.cs, p0.cs_nchunks, stream);
-        else if (e == hipSuccess && two1)
-          e = launch_colsum_pass2(p1.cs, p1.cs_nchunks, stream);
+        const int64_t tiles = (k0 / 128) * (n0 / 128) + (k1 / 128) * (n1 / 128);
+        WgradSplit sp{nullptr, static_cast<int>(tiles), 0};
+        const int sk = two_wgrads_slices(tiles, T, device_shape().cus);
+        const size_t off_part = (need + 255) / 256 * 256;
+        const int64_t rest = sk > 0 ? tiles % device_shape().cus : 0;
+        if (sk > 0 && ws && ws_bytes >= off_part + static_cast<size_t>(rest * sk) * 128 * 128 * 4) {
+          sp.part = reinterpret_cast<float*>(w + off_part);
+          sp.whole = static_cast<int>(tiles - rest);
+          sp.sk = sk;
+        }
+        hipError_t e = launch_gemm_wgrad2(p0, p1, sp, stream);
+        if (e == hipSuccess)
+          e = launch_wgrad2_finish(p0, p1, sp, db0 ? p0.cs_nchunks : 0, db1 ? p1.cs_nchunks : 0,
+                                   stream);
         return hip_status(e);
       }
     }
@@ -743,8 +770,8 @@ int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype 
   // the row launch's counters, then the stacked weight gradients' scratch;
   // the per-product path uses the workspace from its start
   const size_t rows = dt == TP_BF16 ? mlp_step_workspace_bytes(T, h, F, p) : 0;
-  // either weight gradient's own call, or both products' column-sum partials
-  const size_t both = two_wgrads_cs_offset(T, h, true) + colsum_workspace_bytes(T, pF);
+  // either weight gradient's own call, or the stacked products' scratch
+  const size_t both = two_wgrads_bytes(T, h, pF);
   size_t wg = w1 > w2 ? w1 : w2;
   wg = wg > both ? wg : both;
   const size_t fused = rows + wg;

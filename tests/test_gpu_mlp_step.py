@@ -6,7 +6,10 @@ consecutive calls, graph replay, the two halves called separately, and a
 dependency wait forced to give up.
 
 Tolerance: 5e-3 relative Frobenius error per output against the oracle (bf16
-storage). Against the per-product calls, which run the same K order per
+storage). The weight-gradient launch runs the tiles past the last whole
+multiple of the CU count as K slices added by a second launch (288 tiles at
+h = 768 leave 32, each in 8 slices on a 256-CU device); the h = 384 cases have
+fewer tiles than CUs, so every tile is sliced. Against the per-product calls, which run the same K order per
 output element in every fused tile, the forward outputs and data gradients
 agree bitwise; the stacked weight-gradient products may split K otherwise
 than the per-shard calls, so the weight gradients agree within 1e-5 relative.
@@ -49,6 +52,10 @@ CASES = [
     ("gpt350m", dict(micro_batch=1, seq=2048)),                 # p = 4, F = h = 1024, no bias
     ("gpt2s", dict(micro_batch=1, seq=1024, p=1)),              # one shard, F = 3072
     ("gpt2s", dict(micro_batch=1, seq=1024, h=256, p=8)),       # F = 128, p = 8
+    # 72 weight-gradient tiles, fewer than the CUs: every tile as K slices,
+    # two of 512 rows (T = 1024) or three of 1024 rows (T = 3072)
+    ("gpt2s", dict(micro_batch=1, seq=1024, h=384)),
+    ("gpt2s", dict(micro_batch=3, seq=1024, h=384)),
 ]
 
 
