@@ -592,9 +592,19 @@ def variants(cfg, inputs, args, wall_ms):
     r_ms, _ = time_steps(rs, args.steps, args.warmup)
     recompute = {"ms_per_step": round(r_ms, 5), "tflops": round(flops / (r_ms * 1e-3) / 1e12, 1),
                  "vs_stored": round(wall_ms / r_ms, 4),
-                 "activation_bytes_saved_per_shard": cfg.T * cfg.F * 2}
-    log(f"[bench] {cfg.name} with recompute: {json.dumps(recompute)}")
+                 "activation_bytes_saved_per_shard": cfg.T * cfg.F * 2,
+                 "split": rs.split_step}
     del rs
+    if recompute["split"]:
+        # recompute runs the step as its forward and backward calls: the
+        # stored step split the same way is the like-for-like reference
+        ss = ShardStep(cfg, inputs, "cuda:0", split_step=True)
+        ss.capture()
+        s_ms, _ = time_steps(ss, args.steps, args.warmup)
+        recompute["split_stored_ms_per_step"] = round(s_ms, 5)
+        recompute["vs_split_stored"] = round(s_ms / r_ms, 4)
+        del ss
+    log(f"[bench] {cfg.name} with recompute: {json.dumps(recompute)}")
     fp8 = {}
     for name in (cfg.name, "gpt175b"):
         c8 = get_config(name)

@@ -372,6 +372,36 @@ int tp_mlp_step_wgrad(const void* X, const void* A, const void* a, const void* B
                       int64_t ld_da, tp_dtype dt, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/*
+ * The forward and the backward of tp_mlp_step as two calls, same arguments,
+ * for a caller that runs other layers between them (the "Megatron" page,
+ * "Tensor Parallelism / mathematical principles", for the step; its training
+ * optimisations, activation recomputation, for `recompute`).
+ * tp_mlp_step_fwd computes U, Y, Zp and Z (the forward units of the
+ * persistent launch); tp_mlp_step_bwd computes dU, dXp, dX and the weight and
+ * bias gradients from the saved X, U, dZ and the weights (the backward units,
+ * then the two products). With recompute = 0 tp_mlp_step_bwd reads the Y the
+ * forward left; with recompute nonzero Y is only transient between the calls
+ * (its memory may be reused) and tp_mlp_step_bwd rebuilds Y_i = GeLU(U_i)
+ * from the saved bf16 U_i in fc2's data-gradient epilogue (as
+ * tp_linear_bwd_dgrad_recompute) before dB reads it. Forward then backward
+ * with recompute = 0 on one stream give tp_mlp_step's results bit for bit.
+ * The workspace rules are tp_mlp_step's (both calls share one workspace).
+ */
+int tp_mlp_step_fwd(const void* X, const void* A, const void* a, const void* B, const void* b,
+                    const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                    float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                    int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                    int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                    tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream);
+int tp_mlp_step_bwd(const void* X, const void* A, const void* a, const void* B, const void* b,
+                    const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                    float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                    int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                    int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                    int recompute, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
 /* Workspace bytes of tp_mlp_step for these shapes (the larger of the fused
  * path's and the per-product path's needs); pure host function. */
 int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt,

@@ -56,6 +56,10 @@ SIGNATURES = {
                          [_int, _vp, _sz, _vp]),
     "tp_mlp_step_wgrad": (_int, [_vp] * 17 + [_i64, _i64, _i64, _int] + [_i64] * 9 +
                           [_int, _vp, _sz, _vp]),
+    "tp_mlp_step_fwd": (_int, [_vp] * 17 + [_i64, _i64, _i64, _int] + [_i64] * 9 +
+                        [_int, _vp, _sz, _vp]),
+    "tp_mlp_step_bwd": (_int, [_vp] * 17 + [_i64, _i64, _i64, _int] + [_i64] * 9 +
+                        [_int, _int, _vp, _sz, _vp]),
     "tp_mlp_step_workspace_size": (_int, [_i64, _i64, _i64, _int, _int,
                                           ctypes.POINTER(ctypes.c_size_t)]),
     "tp_mlp_step_plan": (_int, [_i64, _i64, _i64, _int, _int, ctypes.POINTER(ctypes.c_int)]),
@@ -453,11 +457,16 @@ def tp_set_wait_limit(polls: int = 0) -> None:
 
 
 def tp_mlp_step(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, workspace,
-                stream=None, part="step"):
+                stream=None, part="step", recompute=False):
     """The MLP step of all p shards (layouts in include/tp_mlp.h): U, Y, dU
     [T, p*F]; Zp, dXp fp32 [p, T, h]; dB fp32 [p*F, h]; dA fp32 [h, p*F].
-    part "rows" or "wgrad" runs tp_mlp_step_rows / tp_mlp_step_wgrad."""
-    fn = {"step": "tp_mlp_step", "rows": "tp_mlp_step_rows", "wgrad": "tp_mlp_step_wgrad"}[part]
+    part "rows" or "wgrad" runs tp_mlp_step_rows / tp_mlp_step_wgrad, "fwd" or
+    "bwd" tp_mlp_step_fwd / tp_mlp_step_bwd (recompute: the backward rebuilds
+    Y from U)."""
+    fn = {"step": "tp_mlp_step", "rows": "tp_mlp_step_rows", "wgrad": "tp_mlp_step_wgrad",
+          "fwd": "tp_mlp_step_fwd", "bwd": "tp_mlp_step_bwd"}[part]
+    if recompute and part != "bwd":
+        raise ValueError("tp_mlp_step: recompute applies to part 'bwd'")
     chk = _Operands(fn)
     chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
     T, h = X.shape
@@ -487,6 +496,7 @@ def tp_mlp_step(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, wor
         _ptr(X), _ptr(A), _ptr(a), _ptr(B), _ptr(b), _ptr(dZ), _ptr(U), _ptr(Y), _ptr(Zp),
         _ptr(Z), _ptr(dU), _ptr(dB), _ptr(db), _ptr(dA), _ptr(da), _ptr(dXp), _ptr(dX),
         T, h, F, p, _ld(X), _ld(A), _ld(B), _ld(dZ), _ld(U), _ld(Z), _ld(dX), _ld(dB), _ld(dA),
+        *([int(bool(recompute))] if part == "bwd" else []),
         _dt(X), _ptr(workspace), _ws_bytes(workspace), _stream(stream)))
 
 

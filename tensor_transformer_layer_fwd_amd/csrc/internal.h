@@ -178,13 +178,15 @@ struct StepParams {
   int xcds, rb, rbx;   // XCDs; token rows of a unit; its row blocks per XCD
   int units_a;         // queue length per XCD
   long long spin;      // polls before a dependency wait gives up
+  int phases;          // 1: the forward units, 2: the backward units, 3: both
+  int recompute;       // backward: fc2's data-gradient epilogue rebuilds Y = GeLU(U)
 };
 // Whether launch_mlp_rows supports these shapes (the bf16 tiles, one row slab
 // per XCD); and the workspace it needs (0 when unsupported).
 bool mlp_step_supported(int64_t T, int64_t h, int64_t F, int p);
 size_t mlp_step_workspace_bytes(int64_t T, int64_t h, int64_t F, int p);
-// Fills the shapes, queue length and workspace pointers of s (operands set by
-// the caller) and enqueues the launch.
+// Fills the shapes, queue length and workspace pointers of s (operands,
+// phases and recompute set by the caller) and enqueues the launch.
 hipError_t launch_mlp_rows(StepParams s, void* workspace, hipStream_t stream);
 // Polls before a dependency wait of launch_mlp_rows gives up, for the calling
 // thread: 0 restores the default (about 0.25 s), a negative value gives up at

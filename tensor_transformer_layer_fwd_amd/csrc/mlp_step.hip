@@ -11,6 +11,12 @@
 //   for each shard i: fc2 data-gradient tiles (dU_i = dZ B_i^T * GeLU'(U_i)),
 //                     fc1 data-gradient partial tiles (dXp_i, fp32);
 //   the sum dX = sum_i dXp_i.
+// A launch runs the whole queue, or only its forward units (F1, F2, S1) or
+// only its backward units (D2, D1, S2), in the same order, for callers that
+// run the two halves as separate calls. In a backward-only launch fc2's data
+// gradient does not wait for fc1's forward tiles (an earlier launch wrote
+// U_i), and with recompute its epilogue also rebuilds Y_i = GeLU(U_i) from the
+// saved U_i for the weight gradient that follows.
 // A unit waits only for units of the same row block that come earlier in the
 // same queue (fc2 forward for fc1's row block, the sums for every shard's row
 // block, fc2's data gradient for fc1's forward tile, fc1's data gradient for
@@ -216,16 +222,29 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
   const int64_t T = s.T, h = s.h, F = s.F;
   const int R = s.rbx;
   const int n1 = static_cast<int>(F / TN), n2 = static_cast<int>(h / TN);
-  // phase sizes, in queue order
-  const int counts[kPhases] = {s.p * R * n1, s.p * R * n2, s.p * R * n1, R * SS, s.p * R * n2,
-                               R * SS};
-  const int kinds[kPhases] = {kF1, kF2, kD2, kS1, kD1, kS2};
+  // the queue's phases and their sizes, in queue order: all six, the forward
+  // three or the backward three
+  const int nf1 = s.p * R * n1, nf2 = s.p * R * n2, nsum = R * SS;
+  int counts[kPhases], kinds[kPhases], nph = 0;
+  auto add = [&](int kind, int n) {
+    kinds[nph] = kind;
+    counts[nph++] = n;
+  };
+  if (s.phases == 3) {
+    add(kF1, nf1), add(kF2, nf2), add(kD2, nf1), add(kS1, nsum), add(kD1, nf2), add(kS2, nsum);
+  } else if (s.phases == 1) {
+    add(kF1, nf1), add(kF2, nf2), add(kS1, nsum);
+  } else {
+    add(kD2, nf1), add(kD1, nf2), add(kS2, nsum);
+  }
+  // fc2's data gradient waits for fc1's forward tiles only in the same launch
+  const bool d2_waits = (s.phases & 1) != 0;
   unsigned* ctr = s.ctr;
   for (;;) {
     const unsigned tk = next_ticket(ctr + L.ta + x, pool);
     if (tk >= static_cast<unsigned>(s.units_a)) break;
     int t = static_cast<int>(tk), ph = 0;
-    while (ph < kPhases - 1 && t >= counts[ph]) t -= counts[ph++];
+    while (ph < nph - 1 && t >= counts[ph]) t -= counts[ph++];
     const int kind = kinds[ph];
     // t within the phase: (shard i,) row block j, column tile (or sum slice) n
     int i = 0, j = 0, n = 0;
@@ -281,7 +300,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
         rows_sum_unit(s.zp, T * h, s.p, h, s.bias_b, s.z, s.ld_z, m0 + n * kSumRows, h);
         break;
       case kD2: {  // fc2 data gradient: dU_i = (dZ B_i^T) * GeLU'(U_i)
-        wait_count(ctr + L.f1 + i * L.nrb + rg, n1, s);
+        if (d2_waits) wait_count(ctr + L.f1 + i * L.nrb + rg, n1, s);
         g.a = s.dz;
         g.lda = s.ld_dz;
         g.b = bf(s.b) + i * F * s.ld_b;
@@ -290,6 +309,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
         g.ldc = s.ld_u;
         g.u = bf(s.u) + i * F;
         g.ldu = s.ld_u;
+        if (s.recompute) {  // Y_i = GeLU(U_i) from the saved U_i
+          g.c2 = bfw(s.y) + i * F;
+          g.ldc2 = s.ld_u;
+        }
         g.M = T, g.N = F, g.K = h, g.k_chunk = h;
         unit_tile<RB, TN, C::WM, C::WN, C::BKT, C::ST, true, true, kEpiDGelu, C::POOL>(
             g, m0, static_cast<int64_t>(n) * TN, static_cast<int>(h / C::BKT));
@@ -326,18 +349,19 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
 // Queue length and workspace layout of a step (shapes and device only).
 struct Plan {
   bool large;  // 256 x 128 tiles (RowsLarge), else 128 x 128 (RowsSmall)
-  int xcds, rb, rbx, units_a;
+  int xcds, rb, rbx, units_a;  // units_a: of one half (forward or backward)
   size_t off_ctr, bytes;
 };
 
 size_t align256(size_t b) { return (b + 255) / 256 * 256; }
 
+// Units of the forward (or of the backward) half of a queue.
 template <class C>
-int rows_units(int64_t T, int64_t h, int64_t F, int p, int X) {
+int rows_units_half(int64_t T, int64_t h, int64_t F, int p, int X) {
   const int R = static_cast<int>(T / C::RB / X);
   const int n1 = static_cast<int>(F / C::TN), n2 = static_cast<int>(h / C::TN);
   const int ss = C::RB / kSumRows;
-  return 2 * p * R * n1 + 2 * p * R * n2 + 2 * R * ss;
+  return p * R * n1 + p * R * n2 + R * ss;
 }
 
 bool plan_step(int64_t T, int64_t h, int64_t F, int p, Plan* pl) {
@@ -355,7 +379,8 @@ bool plan_step(int64_t T, int64_t h, int64_t F, int p, Plan* pl) {
   q.large = T % (static_cast<int64_t>(RowsLarge::RB) * X) == 0 && forced_tile() != kPipe128x128;
   q.rb = q.large ? RowsLarge::RB : RowsSmall::RB;
   q.rbx = static_cast<int>(T / q.rb / X);
-  q.units_a = q.large ? rows_units<RowsLarge>(T, h, F, p, X) : rows_units<RowsSmall>(T, h, F, p, X);
+  q.units_a = q.large ? rows_units_half<RowsLarge>(T, h, F, p, X)
+                      : rows_units_half<RowsSmall>(T, h, F, p, X);
   StepParams tmp{};
   tmp.T = T;
   tmp.p = p;
@@ -394,7 +419,8 @@ hipError_t launch_mlp_rows(StepParams s, void* workspace, hipStream_t stream) {
   s.xcds = q.xcds;
   s.rb = q.rb;
   s.rbx = q.rbx;
-  s.units_a = q.units_a;
+  if (s.phases < 1 || s.phases > 3) return hipErrorInvalidValue;
+  s.units_a = s.phases == 3 ? 2 * q.units_a : q.units_a;
   // about 0.25 s of polling at the default
   s.spin = g_wait_limit > 0 ? g_wait_limit : (g_wait_limit < 0 ? 0 : (1ll << 22));
   const int cus = device_shape().cus;

@@ -792,13 +792,17 @@ int tp_set_wait_limit(int64_t polls) {
   return TP_OK;
 }
 
+// Phases of mlp_step_impl: the forward and the Z sum, the data gradients and
+// the dX sum, the weight and bias gradients.
+constexpr int kPhFwd = 1, kPhWgrad = 2, kPhBwd = 4;
+
 static int mlp_step_impl(const void* X, const void* A, const void* a, const void* B, const void* b,
                 const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
                 float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
                 int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
                 int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
                 tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                int phases) {
+                int phases, int recompute) {
   if (!X || !A || !B || !dZ || !U || !Y || !Zp || !Z || !dU || !dB || !dA || !dXp || !dX)
     return TP_ERR_NULL;
   if (!dtype_ok(dt)) return TP_ERR_DTYPE;
@@ -831,7 +835,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
                       ld_da, T, dt, ws, ws_bytes, stream);
   };
   if (fused) {
-    if (phases & 1) {
+    if (phases & (kPhFwd | kPhBwd)) {
       StepParams s{};
       s.x = X;
       s.a = A;
@@ -857,19 +861,22 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
       s.ld_u = ld_u;
       s.ld_z = ld_z;
       s.ld_dx = ld_dx;
+      s.phases = ((phases & kPhFwd) ? 1 : 0) | ((phases & kPhBwd) ? 2 : 0);
+      s.recompute = recompute != 0;
       st = hip_status(launch_mlp_rows(s, workspace, stream));
       if (st != TP_OK) return st;
     }
-    if (phases & 2) {
+    if (phases & kPhWgrad) {
       const size_t rows = mlp_step_workspace_bytes(T, h, F, p);
       return wgrads(static_cast<char*>(workspace) + rows, workspace_bytes - rows);
     }
     return TP_OK;
   }
-  // the same step as one call per product. Both phases: every shard's
+  // the same step as one call per product. The whole step: every shard's
   // forward, the sum, every shard's backward (tp_mlp_bwd, both layers' two
-  // gradients), the sum of the dX partials. Phase 1 alone: the forward, the
-  // sum and the data gradients; phase 2 alone: the weight and bias gradients.
+  // gradients), the sum of the dX partials. Otherwise the forward and the sum;
+  // the data gradients (with Y_i rebuilt from U_i when recomputing) and their
+  // sum; the weight and bias gradients: whichever phases are asked for.
   const float* zparts[kMaxPartials];
   const float* dparts[kMaxPartials];
   auto Ai = [&](int i) { return static_cast<const char*>(A) + i * F * es; };
@@ -881,7 +888,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     zparts[i] = Zp + i * T * h;
     dparts[i] = dXp + i * T * h;
   }
-  if (phases & 1) {
+  if (phases & kPhFwd) {
     for (int i = 0; i < p; ++i) {
       const void* ai = a ? static_cast<const char*>(a) + i * F * es : nullptr;
       st = tp_column_linear_fwd(X, Ai(i), ai, Yi(i), Ui(i), T, h, F, ld_x, ld_a, ld_u, dt,
@@ -894,7 +901,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     st = tp_reduce_partials(zparts, p, b, Z, T, h, h, ld_z, dt, stream);
     if (st != TP_OK) return st;
   }
-  if (phases == 3) {
+  if ((phases & (kPhBwd | kPhWgrad)) == (kPhBwd | kPhWgrad) && !recompute) {
     for (int i = 0; i < p; ++i) {
       st = tp_mlp_bwd(dZ, X, Ai(i), Bi(i), Ui(i), Yi(i), dUi(i), dB + i * F * ld_db,
                       i == 0 ? db : nullptr, dXp + i * T * h, dA + i * F, da ? da + i * F : nullptr,
@@ -904,10 +911,13 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     }
     return tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
   }
-  if (phases & 1) {
+  if (phases & kPhBwd) {
     for (int i = 0; i < p; ++i) {
-      st = tp_linear_bwd_dgrad(dZ, Bi(i), Ui(i), TP_ACT_GELU_TANH, dUi(i), T, F, h, ld_dz, ld_b,
-                               ld_u, ld_u, dt, dt, stream);
+      st = recompute ? tp_linear_bwd_dgrad_recompute(dZ, Bi(i), Ui(i), TP_ACT_GELU_TANH, dUi(i),
+                                                     Yi(i), T, F, h, ld_dz, ld_b, ld_u, ld_u,
+                                                     ld_u, dt, stream)
+                     : tp_linear_bwd_dgrad(dZ, Bi(i), Ui(i), TP_ACT_GELU_TANH, dUi(i), T, F, h,
+                                           ld_dz, ld_b, ld_u, ld_u, dt, dt, stream);
       if (st != TP_OK) return st;
       st = tp_linear_bwd_dgrad(dUi(i), Ai(i), nullptr, TP_ACT_NONE, dXp + i * T * h, T, h, F,
                                ld_u, ld_a, h, h, dt, TP_F32, stream);
@@ -916,7 +926,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     st = tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
     if (st != TP_OK) return st;
   }
-  if (phases & 2) return wgrads(workspace, workspace_bytes);
+  if (phases & kPhWgrad) return wgrads(workspace, workspace_bytes);
   return TP_OK;
 }
 
@@ -926,7 +936,7 @@ int tp_mlp_step(const void* X, const void* A, const void* a, const void* B, cons
                 int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
                 int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
                 tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, 3);
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, kPhFwd | kPhBwd | kPhWgrad, 0);
 }
 
 int tp_mlp_step_rows(const void* X, const void* A, const void* a, const void* B, const void* b,
@@ -935,7 +945,7 @@ int tp_mlp_step_rows(const void* X, const void* A, const void* a, const void* B,
                 int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
                 int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
                 tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, 1);
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, kPhFwd | kPhBwd, 0);
 }
 
 int tp_mlp_step_wgrad(const void* X, const void* A, const void* a, const void* B, const void* b,
@@ -944,7 +954,30 @@ int tp_mlp_step_wgrad(const void* X, const void* A, const void* a, const void* B
                 int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
                 int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
                 tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, 2);
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p, ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace, workspace_bytes, stream, kPhWgrad, 0);
+}
+
+int tp_mlp_step_fwd(const void* X, const void* A, const void* a, const void* B, const void* b,
+                    const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                    float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                    int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                    int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                    tp_dtype dt, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p,
+                       ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace,
+                       workspace_bytes, stream, kPhFwd, 0);
+}
+
+int tp_mlp_step_bwd(const void* X, const void* A, const void* a, const void* B, const void* b,
+                    const void* dZ, void* U, void* Y, float* Zp, void* Z, void* dU, float* dB,
+                    float* db, float* dA, float* da, float* dXp, void* dX, int64_t T, int64_t h,
+                    int64_t F, int p, int64_t ld_x, int64_t ld_a, int64_t ld_b, int64_t ld_dz,
+                    int64_t ld_u, int64_t ld_z, int64_t ld_dx, int64_t ld_db, int64_t ld_da,
+                    int recompute, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return mlp_step_impl(X, A, a, B, b, dZ, U, Y, Zp, Z, dU, dB, db, dA, da, dXp, dX, T, h, F, p,
+                       ld_x, ld_a, ld_b, ld_dz, ld_u, ld_z, ld_dx, ld_db, ld_da, dt, workspace,
+                       workspace_bytes, stream, kPhBwd | kPhWgrad, recompute != 0);
 }
 
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,

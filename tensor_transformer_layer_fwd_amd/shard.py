@@ -64,7 +64,7 @@ class ShardStep:
     """Device buffers of one workload and the calls of one fwd+bwd step."""
 
     def __init__(self, cfg, inputs: dict, device="cuda", recompute=False, fp8=False,
-                 fused_bwd=True, attn_core=False, step_call=True):
+                 fused_bwd=True, attn_core=False, step_call=True, split_step=False):
         self.cfg = cfg
         self.attn_core = bool(attn_core and cfg.attn)
         if self.attn_core and (cfg.dtype != "bf16" or cfg.heads % cfg.p or
@@ -82,8 +82,17 @@ class ShardStep:
         # recompute with the fused backward: where fc2's gradients pair, Y_i is
         # rebuilt by an elementwise pass so that the pair can read it;
         # elsewhere the fc2 dgrad epilogue recomputes it
-        self.rebuild_y = (self.recompute and self.fused_bwd and cfg.dtype == "bf16" and
-                          L.tp_linear_bwd_plan(cfg.T, cfg.F, cfg.h)[0] != 0)
+        # the whole MLP step of every shard in tp_mlp_step calls: one call, or
+        # with recompute the forward and the backward (which rebuilds Y from U)
+        self.step_call = bool(step_call and cfg.mlp and len(cfg.shards) == cfg.p and
+                              self.fused_bwd and not self.fp8 and
+                              (not self.recompute or
+                               (cfg.dtype == "bf16" and
+                                L.tp_mlp_step_plan(cfg.T, cfg.h, cfg.F, cfg.p, L.TP_BF16))))
+        # the fused step as its forward and backward calls: always with recompute
+        self.split_step = self.step_call and (bool(split_step) or self.recompute)
+        self.rebuild_y = (self.recompute and self.fused_bwd and not self.step_call and
+                          cfg.dtype == "bf16" and L.tp_linear_bwd_plan(cfg.T, cfg.F, cfg.h)[0] != 0)
         self.inp = {k: to_device(v, self.device) for k, v in inputs.items()}
         self.out = {}
         self._graph = None
@@ -92,12 +101,9 @@ class ShardStep:
         act = dict(device=self.device, dtype=self.dt)
         shards = cfg.shards
         ws = 0
-        # the whole MLP step of every shard in one tp_mlp_step call
-        self.step_call = bool(step_call and cfg.mlp and len(shards) == cfg.p and self.fused_bwd
-                              and not self.recompute and not self.fp8)
         if cfg.mlp:
             F = cfg.F
-            if len(shards) == cfg.p and not self.recompute:
+            if len(shards) == cfg.p and (not self.recompute or self.step_call):
                 # every shard's tensors as blocks of one buffer each, in the
                 # layouts of tp_mlp_step (U_i = U[:, iF:(i+1)F], Zp_i = Zp[i], ...);
                 # the recompute step keeps a compact transient Y, so its U_i
@@ -112,7 +118,8 @@ class ShardStep:
                 for i in shards:
                     cols = slice(i * F, (i + 1) * F)
                     self.out[f"U_{i}"] = self.mlp["U"][:, cols]
-                    self.out[f"Y_{i}"] = self.mlp["Y"][:, cols]
+                    if not self.recompute:  # with recompute Y is transient
+                        self.out[f"Y_{i}"] = self.mlp["Y"][:, cols]
                     self.out[f"Zp_{i}"] = self.mlp["Zp"][i]
                     self.out[f"dU_{i}"] = self.mlp["dU"][:, cols]
                     self.out[f"dB_{i}"] = self.mlp["dB"][cols]
@@ -132,7 +139,12 @@ class ShardStep:
                     self.out[f"dXp_{i}"] = torch.empty(T, h, **f32)
                     if cfg.has_bias:
                         self.out[f"da_{i}"] = torch.empty(F, **f32)
-            if self.recompute:
+            if self.recompute and self.step_call:
+                # every shard's Y in one transient buffer: the forward's, then the
+                # backward's rebuilt from U (the last shard's block reported)
+                last = shards[-1]
+                self.out["Yt"] = self.mlp["Y"][:, last * F:(last + 1) * F]
+            elif self.recompute:
                 # the forward's Y_i, then the backward's recomputed Y_i, shard by shard
                 self.out["Yt"] = torch.empty(T, F, **act)
             if cfg.has_bias:
@@ -376,11 +388,18 @@ class ShardStep:
             L.tp_reduce_partials([o[f"dXqp_{i}"] for i in cfg.shards], None, o["dXq"])
 
     def mlp_step(self, part="step"):
-        """Every shard's MLP forward and backward and both sums in one call."""
+        """Every shard's MLP forward and backward and both sums in one call
+        (part "step"), or the call named by part; split (always with
+        recompute) the step is the forward call, then the backward call (which
+        with recompute rebuilds Y from U)."""
         cfg, o, inp, m = self.cfg, self.out, self.inp, self.mlp
-        L.tp_mlp_step(inp["X"], inp["A"], inp.get("a"), inp["B"], inp.get("b"), inp["dZ"],
-                      m["U"], m["Y"], m["Zp"], o["Z"], m["dU"], m["dB"], o.get("db"), m["dA"],
-                      m.get("da"), m["dXp"], o["dX"], self.step_ws, part=part)
+        parts = [("fwd", False), ("bwd", self.recompute)] if (self.split_step and part == "step") \
+            else [(part, self.recompute and part == "bwd")]
+        for pt, rc in parts:
+            L.tp_mlp_step(inp["X"], inp["A"], inp.get("a"), inp["B"], inp.get("b"), inp["dZ"],
+                          m["U"], m["Y"], m["Zp"], o["Z"], m["dU"], m["dB"], o.get("db"),
+                          m["dA"], m.get("da"), m["dXp"], o["dX"], self.step_ws, part=pt,
+                          recompute=rc)
 
     def run_eager(self):
         """Enqueue one fwd+bwd step on the current stream."""

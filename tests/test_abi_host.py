@@ -523,14 +523,17 @@ def test_mlp_step_queries(lib):
 
 
 def test_mlp_step_validation(lib):
-    """tp_mlp_step and its halves reject bad arguments before any launch."""
+    """tp_mlp_step, its halves and its forward / backward calls reject bad
+    arguments before any launch."""
     F_ = FAKE
-    for fn in (lib.tp_mlp_step, lib.tp_mlp_step_rows, lib.tp_mlp_step_wgrad):
+    for fn, extra in ((lib.tp_mlp_step, ()), (lib.tp_mlp_step_rows, ()),
+                      (lib.tp_mlp_step_wgrad, ()), (lib.tp_mlp_step_fwd, ()),
+                      (lib.tp_mlp_step_bwd, (0,)), (lib.tp_mlp_step_bwd, (1,))):
         def call(*, X=F_, dX=F_, T=4096, h=768, F=1536, p=2, ld_a=3072, ld_u=3072, dt=1,
                  ws=F_, wsb=1 << 30):
             return fn(X, F_, None, F_, None, F_, F_, F_, F_, F_, F_, F_, None, F_, None, F_, dX,
-                      T, h, F, p, 768, ld_a, 768, 768, ld_u, 768, 768, 768, 3072, dt, ws, wsb,
-                      None)
+                      T, h, F, p, 768, ld_a, 768, 768, ld_u, 768, 768, 768, 3072, *extra, dt, ws,
+                      wsb, None)
         assert call(X=None) == -1
         assert call(dX=None) == -1
         assert call(T=0) == -2

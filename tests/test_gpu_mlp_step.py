@@ -2,8 +2,9 @@
 persistent launch for the forward, the sums and the data gradients, then the
 weight gradients as two products over the stacked shards), against the
 float64 oracle and against the per-product calls, plus its queue bookkeeping:
-consecutive calls, graph replay, the two halves called separately, and a
-dependency wait forced to give up.
+consecutive calls, graph replay, the two halves called separately, the
+forward and backward calls (with and without recompute), and a dependency wait
+forced to give up.
 
 Tolerance: 5e-3 relative Frobenius error per output against the oracle (bf16
 storage). The weight-gradient launch runs the tiles past the last whole
@@ -101,6 +102,104 @@ def test_mlp_step_against_per_product_calls(dev, name):
             assert oracle.rel_fro(got[k], want[k]) <= 1e-5, k
         else:
             np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+
+
+def _mlp_buffers(cfg, dev):
+    """Fresh stacked buffers of tp_mlp_step for cfg (outputs filled with a
+    value no step leaves, so that anything not written shows)."""
+    T, h, F, p = cfg.T, cfg.h, cfg.F, cfg.p
+    bf = dict(device=dev, dtype=torch.bfloat16)
+    f32 = dict(device=dev, dtype=torch.float32)
+    m = {"U": torch.empty(T, p * F, **bf), "Y": torch.empty(T, p * F, **bf),
+         "dU": torch.empty(T, p * F, **bf), "Zp": torch.empty(p, T, h, **f32),
+         "dXp": torch.empty(p, T, h, **f32), "Z": torch.empty(T, h, **bf),
+         "dX": torch.empty(T, h, **bf), "dB": torch.empty(p * F, h, **f32),
+         "dA": torch.empty(h, p * F, **f32), "db": torch.empty(h, **f32),
+         "da": torch.empty(p * F, **f32)}
+    for t in m.values():
+        t.fill_(-7.0)
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    m["ws"] = torch.zeros(L.tp_mlp_step_workspace_size(T, h, F, p, L.TP_BF16), dtype=torch.uint8,
+                          device=dev)
+    return m
+
+
+def _mlp_call(inp, m, part, recompute=False):
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    L.tp_mlp_step(inp["X"], inp["A"], inp.get("a"), inp["B"], inp.get("b"), inp["dZ"], m["U"],
+                  m["Y"], m["Zp"], m["Z"], m["dU"], m["dB"], m["db"] if "b" in inp else None,
+                  m["dA"], m["da"] if "a" in inp else None, m["dXp"], m["dX"], m["ws"], part=part,
+                  recompute=recompute)
+
+
+SPLIT_CASES = [("gpt2s", dict(micro_batch=1, seq=1024)), ("gpt350m", dict(micro_batch=1, seq=2048)),
+               ("gpt2s", dict(micro_batch=1, seq=1024, h=384))]
+
+
+@pytest.mark.parametrize("name,kw", SPLIT_CASES)
+def test_mlp_step_forward_then_backward_is_the_step(dev, name, kw):
+    """tp_mlp_step_fwd then tp_mlp_step_bwd (recompute off) leave every
+    output of tp_mlp_step bit for bit; the forward alone writes the forward's
+    outputs and no gradient."""
+    from tensor_transformer_layer_fwd_amd.shard import to_device
+    cfg = _mlp_cfg(name, **kw)
+    _say(f"mlp step fwd + bwd {name} T={cfg.T} h={cfg.h} p={cfg.p}")
+    inp = {k: to_device(v, dev) for k, v in make_inputs(cfg).items()}
+    one = _mlp_buffers(cfg, dev)
+    _mlp_call(inp, one, "step")
+    two = _mlp_buffers(cfg, dev)
+    _mlp_call(inp, two, "fwd")
+    torch.cuda.synchronize()
+    for k in ("dU", "dXp", "dX", "dB", "dA"):
+        assert bool((two[k] == -7.0).all()), f"the forward wrote {k}"
+    for k in ("U", "Y", "Zp", "Z"):
+        assert torch.equal(one[k], two[k]), k
+    _mlp_call(inp, two, "bwd")
+    torch.cuda.synchronize()
+    for k in one:
+        if k == "ws" or (k == "db" and "b" not in inp) or (k == "da" and "a" not in inp):
+            continue
+        assert torch.equal(one[k], two[k]), k
+    assert int(two["ws"][:4].view(torch.int32).item()) == 0, "a dependency wait gave up"
+
+
+@pytest.mark.parametrize("name,kw", SPLIT_CASES)
+def test_mlp_step_backward_rebuilds_y(dev, name, kw):
+    """With recompute the backward rebuilds Y from U after the forward's Y
+    was overwritten: Y equals what tp_linear_bwd_dgrad_recompute rebuilds for
+    each shard, bit for bit; every output that does not read Y equals the
+    stored step's bit for bit, and dB (which reads the rebuilt Y) is within
+    the step tolerance of the oracle."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    from tensor_transformer_layer_fwd_amd.shard import to_device
+    cfg = _mlp_cfg(name, **kw)
+    _say(f"mlp step bwd recompute {name} T={cfg.T} h={cfg.h} p={cfg.p}")
+    inputs = make_inputs(cfg)
+    inp = {k: to_device(v, dev) for k, v in inputs.items()}
+    ref = _mlp_buffers(cfg, dev)
+    _mlp_call(inp, ref, "step")
+    m = _mlp_buffers(cfg, dev)
+    _mlp_call(inp, m, "fwd")
+    m["Y"].fill_(3.0)  # Y is transient between the calls
+    _mlp_call(inp, m, "bwd", recompute=True)
+    torch.cuda.synchronize()
+    F = cfg.F
+    for i in range(cfg.p):
+        cols = slice(i * F, (i + 1) * F)
+        y = torch.empty(cfg.T, F, device=dev, dtype=torch.bfloat16)
+        du = torch.empty_like(y)
+        L.tp_linear_bwd_dgrad_recompute(inp["dZ"], inp["B"][cols], m["U"][:, cols], du, y)
+        torch.cuda.synchronize()
+        assert torch.equal(m["Y"][:, cols], y), f"Y_{i}"
+        assert torch.equal(m["dU"][:, cols], du), f"dU_{i}"
+    for k in ("U", "Zp", "Z", "dU", "dXp", "dX", "dA") + (("da",) if "a" in inp else ()) + \
+            (("db",) if "b" in inp else ()):
+        assert torch.equal(ref[k], m[k]), k
+    want = oracle.run_config(cfg, inputs)
+    for i in range(cfg.p):
+        e = oracle.rel_fro(m["dB"][i * F:(i + 1) * F].double().cpu().numpy(), want[f"dB_{i}"])
+        assert e <= 5e-3, (i, e)
+    assert int(m["ws"][:4].view(torch.int32).item()) == 0, "a dependency wait gave up"
 
 
 def test_mlp_step_repeats_replays_and_halves(dev):

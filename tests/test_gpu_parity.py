@@ -850,22 +850,28 @@ def test_attention_bwd_deterministic(dev):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
-@pytest.mark.parametrize("fused", [True, False])
+@pytest.mark.parametrize("mode", ["step", "pair", "products"])
 @pytest.mark.parametrize("name,mb,seq", [("tiny", 8, 64), ("gpt2s", 1, 680), ("gpt2s", 1, 1024),
                                          ("gpt350m", 1, 520)])
-def test_workload_recompute(dev, name, mb, seq, fused):
+def test_workload_recompute(dev, name, mb, seq, mode):
     """The step with activation recompute: every output the oracle defines
     except the Y_i it no longer keeps, and the recomputed Y of the last shard
-    (left in the transient buffer) against the oracle's Y. fused, where fc2
-    pairs: Y_i rebuilt by an elementwise pass before the paired backward;
-    otherwise in the fc2 dgrad epilogue."""
+    (left in the transient buffer) against the oracle's Y. mode "step": the
+    fused forward and backward calls where the shapes take them (the backward
+    rebuilds every Y_i in fc2's data-gradient epilogue); "pair": the paired
+    backward, Y_i rebuilt by an elementwise pass where fc2 pairs; "products":
+    one call per product, Y_i rebuilt in the fc2 dgrad epilogue."""
     from tensor_transformer_layer_fwd_amd.shard import ShardStep
     cfg = dataclasses.replace(get_config(name), micro_batch=mb, seq=seq)
-    _say(f"workload {name} with recompute T={cfg.T} fused={fused}")
+    _say(f"workload {name} with recompute T={cfg.T} mode={mode}")
     inputs = make_inputs(cfg)
-    step = ShardStep(cfg, inputs, dev, recompute=True, fused_bwd=fused)
-    # the aligned GPT-2-small shard pairs fc2's gradients: Y_i is rebuilt by a pass
-    assert step.rebuild_y == (fused and name == "gpt2s" and seq == 1024)
+    step = ShardStep(cfg, inputs, dev, recompute=True, fused_bwd=mode != "products",
+                     step_call=mode == "step")
+    aligned = name == "gpt2s" and seq == 1024
+    # the aligned GPT-2-small shard runs the fused calls; with them off it
+    # pairs fc2's gradients, and Y_i is rebuilt by a pass
+    assert step.step_call == (mode == "step" and aligned)
+    assert step.rebuild_y == (mode == "pair" and aligned)
     step.run_eager()
     got = step.results()
     ref = oracle.run_config(cfg, inputs)

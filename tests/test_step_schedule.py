@@ -23,12 +23,16 @@ import random
 import pytest
 
 PHASES = ("F1", "F2", "D2", "S1", "D1", "S2")
+# A launch runs the whole queue, or only its forward or its backward units (in
+# the same order); in a backward-only launch fc2's data gradient (D2) waits for
+# nothing, fc1's forward having run in an earlier launch.
+QUEUES = {"step": PHASES, "fwd": ("F1", "F2", "S1"), "bwd": ("D2", "D1", "S2")}
 
 
-def queue(p, R, n1, n2, SS):
+def queue(p, R, n1, n2, SS, phases=PHASES):
     """Units of one XCD in ticket order: (kind, shard, row block, column)."""
     units = []
-    for kind in PHASES:
+    for kind in phases:
         if kind in ("F1", "D2"):
             units += [(kind, i, j, n) for i in range(p) for j in range(R) for n in range(n1)]
         elif kind in ("F2", "D1"):
@@ -38,9 +42,11 @@ def queue(p, R, n1, n2, SS):
     return units
 
 
-def producers(unit, p, n1, n2):
+def producers(unit, p, n1, n2, d2_waits=True):
     """The counter a unit waits for: (kind produced, shards, row block), needed count."""
     kind, i, j, _ = unit
+    if kind == "D2" and not d2_waits:
+        return None, 0
     if kind in ("F2", "D2"):
         return ("F1", (i,), j), n1
     if kind == "S1":
@@ -62,13 +68,15 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("which", sorted(QUEUES))
 @pytest.mark.parametrize("p,R,n1,n2,SS", SHAPES)
-def test_every_dependency_has_an_earlier_ticket(p, R, n1, n2, SS):
-    units = queue(p, R, n1, n2, SS)
+def test_every_dependency_has_an_earlier_ticket(p, R, n1, n2, SS, which):
+    units = queue(p, R, n1, n2, SS, QUEUES[which])
     tickets = {u: t for t, u in enumerate(units)}
-    assert len(tickets) == len(units) == 2 * p * R * (n1 + n2) + 2 * R * SS
+    halves = 1 if which == "step" else 0.5
+    assert len(tickets) == len(units) == int(halves * (2 * p * R * (n1 + n2) + 2 * R * SS))
     for t, u in enumerate(units):
-        (src, need) = producers(u, p, n1, n2)
+        (src, need) = producers(u, p, n1, n2, d2_waits=which != "bwd")
         if src is None:
             continue
         kind, shards, j = src
@@ -77,7 +85,7 @@ def test_every_dependency_has_an_earlier_ticket(p, R, n1, n2, SS):
         assert max(tickets[v] for v in deps) < t, u
 
 
-def drain(units, p, n1, n2, blocks, rng):
+def drain(units, p, n1, n2, blocks, rng, d2_waits=True):
     """Event simulation: `blocks` blocks take tickets in order, wait for their
     unit's count, run it for a random time, count it done. Returns the number
     of completed units (all of them unless the queue deadlocks)."""
@@ -90,7 +98,7 @@ def drain(units, p, n1, n2, blocks, rng):
     finished = 0
 
     def ready(u):
-        src, need = producers(u, p, n1, n2)
+        src, need = producers(u, p, n1, n2, d2_waits)
         if src is None:
             return True
         kind, shards, j = src
@@ -123,12 +131,13 @@ def drain(units, p, n1, n2, blocks, rng):
         free += 1
 
 
+@pytest.mark.parametrize("which", sorted(QUEUES))
 @pytest.mark.parametrize("p,R,n1,n2,SS", SHAPES)
 @pytest.mark.parametrize("blocks", [1, 2, 3, 7, 32, 64])
-def test_queue_drains_with_any_number_of_blocks(p, R, n1, n2, SS, blocks):
-    units = queue(p, R, n1, n2, SS)
+def test_queue_drains_with_any_number_of_blocks(p, R, n1, n2, SS, blocks, which):
+    units = queue(p, R, n1, n2, SS, QUEUES[which])
     rng = random.Random(1000 * blocks + p * 97 + R)
-    assert drain(units, p, n1, n2, blocks, rng) == len(units)
+    assert drain(units, p, n1, n2, blocks, rng, d2_waits=which != "bwd") == len(units)
 
 
 def test_model_detects_a_queue_that_could_deadlock():
