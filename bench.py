@@ -177,7 +177,59 @@ def shard_calls(step, i=0):
         layer("fc2", inp["dZ"], B_i, o[f"U_{i}"], Y_i, o[f"dU_{i}"], o[f"dB_{i}"], F, h, "gelu", e)
         layer("fc1", o[f"dU_{i}"], A_i, None, inp["X"], o[f"dXp_{i}"], o[f"dA_{i}"], h, F, "none",
               4)
-    if cfg.attn:
+    if cfg.attn and step.proj_call:
+        # every shard's attention projections: one persistent launch (QKV,
+        # the output projection and its sum, dC, the dXq partials and their
+        # sum), then the weight gradients (two products). With the core the
+        # QKV forward runs per product, the core in between, and the
+        # persistent launch twice (output projection with dC; dXq)
+        Q, O, p = cfg.Q, cfg.O, cfg.p
+        fused = L.tp_attn_proj_step_plan(T, h, Q, O, p, step.tp_dt)
+        geom = {"T": T, "h": h, "Q": Q, "O": O, "p": p, "fused": fused}
+        f_q, f_o, f_c, f_x = (p * 2 * T * h * Q, p * 2 * T * O * h, p * 2 * T * h * O,
+                              p * 2 * T * Q * h)
+        fw = p * 2 * T * O * h + p * 2 * T * h * Q
+        bw = (T * p * O * e + T * h * e + T * h * e + T * p * Q * e  # C, dZa, X, dQKV
+              + p * O * h * 4 + h * p * Q * 4)  # dO, dW
+        if not step.attn_core:
+            fr = f_q + f_o + f_c + f_x
+            br = (T * h * e + h * p * Q * e + p * O * h * e + T * p * O * e + T * h * e
+                  + T * p * Q * e  # X, W, Ow, C, dZa, dQKV
+                  + T * p * Q * e + T * p * O * e  # QKV, dC
+                  + 2 * 2 * p * T * h * 4 + 2 * T * h * e)  # Zpa, dXqp written and read; Za, dXq
+            calls.append(Call("attn_proj_rows", lambda: step.proj_step(15), fr, br, fused, geom,
+                              post=lambda: step.proj_step(16)))
+            calls.append(Call("attn_proj_wgrad", lambda: step.proj_step(16), fw, bw, fused, geom))
+            calls.append(Call("attn_proj_step", lambda: step.proj_step(31), fr + fw, br + bw,
+                              False, geom))
+        else:
+            b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
+            W_i = step._col("W", i, Q)
+            calls.append(Call("qkv_fwd",
+                              lambda: L.tp_column_linear_fwd(inp["X"], W_i, None, o[f"QKV_{i}"],
+                                                             None, act="none"),
+                              2 * T * h * Q, T * h * e + h * Q * e + T * Q * e, True,
+                              {"M": T, "N": Q, "K": h}))
+            br6 = (T * p * O * e + p * O * h * e + T * h * e  # C, Ow, dZa
+                   + T * p * O * e + 2 * p * T * h * 4 + T * h * e)  # dC; Zpa written, read; Za
+            calls.append(Call("attn_proj_out_dc", lambda: step.proj_step(6), f_o + f_c, br6, fused,
+                              geom))
+            br8 = T * p * Q * e + h * p * Q * e + 2 * p * T * h * 4 + T * h * e
+            calls.append(Call("attn_proj_dx_wgrad", lambda: step.proj_step(24), f_x + fw, br8 + bw,
+                              False, geom))
+            ff, fb = attention_core_flops(cfg)
+            hd = H * 64
+            calls.append(Call("attn_fwd",
+                              lambda: L.tp_attention_fwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"lse_{i}"],
+                                                         b, Ls, H),
+                              ff, T * 3 * hd * 2 + T * hd * 2 + b * H * Ls * 4, True))
+            calls.append(Call("attn_bwd",
+                              lambda: L.tp_attention_bwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"dC_{i}"],
+                                                         o[f"lse_{i}"], step.delta,
+                                                         o[f"dQKV_{i}"], b, Ls, H),
+                              fb, T * 3 * hd * 2 * 2 + 2 * T * hd * 2 + b * H * Ls * 4 * 3,
+                              False))
+    elif cfg.attn:
         Q, O = cfg.Q, cfg.O
         W_i, Ow_i = step._col("W", i, Q), step._row("Ow", i, O)
         C_i = step._c(i)

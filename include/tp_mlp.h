@@ -402,6 +402,65 @@ int tp_mlp_step_bwd(const void* X, const void* A, const void* a, const void* B, 
                     int recompute, tp_dtype dt, void* workspace, size_t workspace_bytes,
                     hipStream_t stream);
 
+/*
+ * The attention projections of all p shards of a layer on this device
+ * ("Megatron" page, "Transformer-layer tensor parallelism": the QKV
+ * projection is column-parallel and the output projection row-parallel, the
+ * sum over shards standing in for the All-Reduce; the backward is the
+ * derivative of the same definitions):
+ *   QKV_i = X W_i                      (stage 1)
+ *   Zpa_i = C_i O_i, Za = sum_i Zpa_i   (stage 2)
+ *   dC_i  = dZa O_i^T                  (stage 4)
+ *   dXqp_i = dQKV_i W_i^T, dXq = sum_i dXqp_i   (stage 8)
+ *   dO_i = C_i^T dZa, dW_i = X^T dQKV_i (stage 16, fp32, overwritten)
+ * `stages` is any nonempty sum of those bits; the stages run in that order.
+ * C_i and dQKV_i are inputs: the attention core's output and input gradient
+ * (tp_attention_fwd / tp_attention_bwd), so a caller with the core runs stage
+ * 1, the core, stage 2; then stage 4, the core's backward, stages 8 + 16.
+ * Without it all five stages are one call.
+ *
+ * Layouts (bf16 = dt, fp32 as noted; shard i is a column or row block):
+ *   X [T, h], ld_x            W [h, p*Q], ld_w (W_i: columns i*Q ..)
+ *   Ow [p*O, h], ld_ow (O_i: rows i*O ..)
+ *   C [T, p*O], ld_c          dZa [T, h], ld_dz      dQKV [T, p*Q], ld_dqkv
+ *   QKV [T, p*Q], ld_qkv      dC [T, p*O], ld_dc
+ *   Zpa, dXqp fp32 [p, T, h] compact (shard i at i*T*h, row stride h)
+ *   Za [T, h], ld_za          dXq [T, h], ld_dxq
+ *   dOw fp32 [p*O, h], ld_dow (dO_i: rows i*O ..)
+ *   dW  fp32 [h, p*Q], ld_dw  (dW_i: columns i*Q ..)
+ * Pointers a stage does not touch may be NULL.
+ *
+ * bf16 with the shapes tp_attn_proj_step_plan reports as fused (T a multiple
+ * of 128 x the device's XCD count; h, Q, O of 128; 16-byte aligned operands
+ * and row strides) runs stages 1, 2, 4 and 8 in one persistent launch over
+ * each XCD's own token rows (the MLP step's queue, with no dependency between
+ * the products and the sums waiting for every shard's partials), and stage 16
+ * as two products over the stacked shards (as tp_mlp_step's weight
+ * gradients). Any other shape or dtype runs the same stages as the
+ * per-product calls. The results are those of the per-product calls.
+ *
+ * workspace: at least tp_attn_proj_step_workspace_size bytes, 256-byte
+ * aligned, zeroed before its first use, with the same rules as tp_mlp_step's
+ * (its counters are left zeroed by every call; calls sharing it do not
+ * overlap; its first 32-bit word is nonzero after a call in which a sum's
+ * wait gave up).
+ */
+int tp_attn_proj_step(const void* X, const void* W, const void* Ow, const void* C,
+                      const void* dZa, const void* dQKV, void* QKV, float* Zpa, void* Za,
+                      void* dC, float* dOw, float* dW, float* dXqp, void* dXq, int64_t T,
+                      int64_t h, int64_t Q, int64_t O, int p, int64_t ld_x, int64_t ld_w,
+                      int64_t ld_ow, int64_t ld_c, int64_t ld_dz, int64_t ld_dqkv, int64_t ld_qkv,
+                      int64_t ld_dc, int64_t ld_za, int64_t ld_dxq, int64_t ld_dow, int64_t ld_dw,
+                      int stages, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+/* Workspace bytes of tp_attn_proj_step (pure host function). */
+int tp_attn_proj_step_workspace_size(int64_t T, int64_t h, int64_t Q, int64_t O, int p,
+                                     tp_dtype dt, size_t* bytes);
+/* *fused = 1 where tp_attn_proj_step runs the persistent launch for these
+ * shapes (alignment aside), else 0. */
+int tp_attn_proj_step_plan(int64_t T, int64_t h, int64_t Q, int64_t O, int p, tp_dtype dt,
+                           int* fused);
+
 /* Workspace bytes of tp_mlp_step for these shapes (the larger of the fused
  * path's and the per-product path's needs); pure host function. */
 int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype dt,

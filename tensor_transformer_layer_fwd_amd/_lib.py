@@ -63,6 +63,12 @@ SIGNATURES = {
     "tp_mlp_step_workspace_size": (_int, [_i64, _i64, _i64, _int, _int,
                                           ctypes.POINTER(ctypes.c_size_t)]),
     "tp_mlp_step_plan": (_int, [_i64, _i64, _i64, _int, _int, ctypes.POINTER(ctypes.c_int)]),
+    "tp_attn_proj_step": (_int, [_vp] * 14 + [_i64, _i64, _i64, _i64, _int] + [_i64] * 12 +
+                          [_int, _int, _vp, _sz, _vp]),
+    "tp_attn_proj_step_workspace_size": (_int, [_i64, _i64, _i64, _i64, _int, _int,
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "tp_attn_proj_step_plan": (_int, [_i64, _i64, _i64, _i64, _int, _int,
+                                      ctypes.POINTER(ctypes.c_int)]),
     "tp_set_wait_limit": (_int, [_i64]),
     "tp_reduce_partials": (_int, [ctypes.POINTER(ctypes.c_void_p), _int, _vp, _vp, _i64, _i64, _i64,
                                   _i64, _int, _vp]),
@@ -448,6 +454,73 @@ def tp_mlp_step_plan(T: int, h: int, F: int, p: int, dt: int) -> bool:
     f = ctypes.c_int(0)
     _check("tp_mlp_step_plan", lib().tp_mlp_step_plan(T, h, F, p, dt, ctypes.byref(f)))
     return bool(f.value)
+
+
+def tp_attn_proj_step_workspace_size(T: int, h: int, Q: int, O: int, p: int, dt: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("tp_attn_proj_step_workspace_size",
+           lib().tp_attn_proj_step_workspace_size(T, h, Q, O, p, dt, ctypes.byref(out)))
+    return int(out.value)
+
+
+def tp_attn_proj_step_plan(T: int, h: int, Q: int, O: int, p: int, dt: int) -> bool:
+    """Whether tp_attn_proj_step runs these shapes fused: the persistent launch,
+    then the two stacked weight-gradient products."""
+    f = ctypes.c_int(0)
+    _check("tp_attn_proj_step_plan",
+           lib().tp_attn_proj_step_plan(T, h, Q, O, p, dt, ctypes.byref(f)))
+    return bool(f.value)
+
+
+ATTN_PROJ_STAGES = {"qkv": 1, "out": 2, "dc": 4, "dx": 8, "wgrad": 16}
+
+
+def tp_attn_proj_step(X, W, Ow, C, dZa, dQKV, QKV, Zpa, Za, dC, dOw, dW, dXqp, dXq, workspace,
+                      stages=31, stream=None):
+    """The attention projections of all p shards (layouts in include/tp_mlp.h):
+    W [h, p*Q], Ow [p*O, h]; C, dC [T, p*O]; QKV, dQKV [T, p*Q]; Zpa, dXqp fp32
+    [p, T, h]; dOw fp32 [p*O, h]; dW fp32 [h, p*Q]. stages: a sum of
+    ATTN_PROJ_STAGES (an int, or an iterable of their names); the tensors a
+    stage does not touch may be None."""
+    if not isinstance(stages, int):
+        stages = sum(ATTN_PROJ_STAGES[n] for n in stages)
+    chk = _Operands("tp_attn_proj_step")
+    chk("X", X, _shape2(X), _torch_dtypes("bf16", "f32"))
+    T, h = X.shape
+    dts, f32 = (X.dtype,), _torch_dtypes("f32")
+    if Zpa is not None and Zpa.dim() == 3:
+        p = Zpa.shape[0]
+    elif dXqp is not None and dXqp.dim() == 3:
+        p = dXqp.shape[0]
+    else:
+        raise ValueError("tp_attn_proj_step: Zpa or dXqp must be a [p, T, h] tensor")
+    chk("W", W, (h, _shape2(W)[1]), dts)("Ow", Ow, (_shape2(Ow)[0], h), dts)
+    pQ, pO = W.shape[1], Ow.shape[0]
+    if pQ % p or pO % p:
+        raise ValueError(f"tp_attn_proj_step: W's {pQ} columns or Ow's {pO} rows do not split "
+                         f"into {p} shards")
+    Q, O = pQ // p, pO // p
+    opt = True
+    chk("C", C, (T, pO), dts, optional=opt)("dZa", dZa, (T, h), dts, optional=opt)
+    chk("dQKV", dQKV, (T, pQ), dts, optional=opt)("QKV", QKV, (T, pQ), dts, optional=opt)
+    chk("Za", Za, (T, h), dts, optional=opt)("dC", dC, (T, pO), dts, optional=opt)
+    chk("dXq", dXq, (T, h), dts, optional=opt)
+    for name, t in (("Zpa", Zpa), ("dXqp", dXqp)):
+        chk(name, t, (p, T, h), f32, optional=opt)
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"tp_attn_proj_step: {name} must be contiguous [p, T, h]")
+    chk("dOw", dOw, (pO, h), f32, optional=opt)("dW", dW, (h, pQ), f32, optional=opt)
+    _check_ws(chk, workspace)
+    chk.done(stream)
+
+    def ld(t, w):
+        return _ld(t) if t is not None else w
+    _check("tp_attn_proj_step", lib().tp_attn_proj_step(
+        _ptr(X), _ptr(W), _ptr(Ow), _ptr(C), _ptr(dZa), _ptr(dQKV), _ptr(QKV), _ptr(Zpa),
+        _ptr(Za), _ptr(dC), _ptr(dOw), _ptr(dW), _ptr(dXqp), _ptr(dXq), T, h, Q, O, p, _ld(X),
+        _ld(W), _ld(Ow), ld(C, pO), ld(dZa, h), ld(dQKV, pQ), ld(QKV, pQ), ld(dC, pO), ld(Za, h),
+        ld(dXq, h), ld(dOw, h), ld(dW, pQ), int(stages), _dt(X), _ptr(workspace),
+        _ws_bytes(workspace), _stream(stream)))
 
 
 def tp_set_wait_limit(polls: int = 0) -> None:

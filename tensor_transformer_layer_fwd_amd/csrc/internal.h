@@ -188,10 +188,48 @@ size_t mlp_step_workspace_bytes(int64_t T, int64_t h, int64_t F, int p);
 // Fills the shapes, queue length and workspace pointers of s (operands,
 // phases and recompute set by the caller) and enqueues the launch.
 hipError_t launch_mlp_rows(StepParams s, void* workspace, hipStream_t stream);
+// The attention projections of p shards in one persistent launch over each
+// XCD's own token rows (proj_step.hip): QKV_i = X W_i, the output projection's
+// partial Zpa_i = C_i O_i and their sum Za, dC_i = dZa O_i^T, and the partial
+// dXqp_i = dQKV_i W_i^T with its sum dXq. Layouts as tp_attn_proj_step's.
+struct ProjParams {
+  const void* x;     // X [T, h], ld_x
+  const void* w;     // W [h, p*Q], ld_w (W_i: columns i*Q ..)
+  const void* ow;    // Ow [p*O, h], ld_ow (O_i: rows i*O ..)
+  const void* c;     // C [T, p*O], ld_c (C_i: columns i*O ..)
+  const void* dz;    // dZa [T, h], ld_dz
+  const void* dqkv;  // dQKV [T, p*Q], ld_dqkv
+  void* qkv;         // QKV [T, p*Q], ld_qkv
+  void* dc;          // dC [T, p*O], ld_dc
+  float* zp;         // Zpa, dXqp fp32 [p, T, h], compact
+  float* dxp;
+  void* z;           // Za [T, h], ld_z
+  void* dx;          // dXq [T, h], ld_dx
+  int64_t T, h, Q, O;
+  int p;
+  int64_t ld_x, ld_w, ld_ow, ld_c, ld_dz, ld_dqkv, ld_qkv, ld_dc, ld_z, ld_dx;
+  // the units the launch runs: kProjQkv (QKV_i), kProjOut (Zpa_i and Za),
+  // kProjDc (dC_i), kProjDx (dXqp_i and dXq)
+  int phases;
+  // workspace (launch_proj_rows)
+  unsigned* err;
+  unsigned long long* clk;
+  unsigned* ctr;
+  int xcds, rb, rbx, units_a;
+  long long spin;
+};
+constexpr int kProjQkv = 1, kProjOut = 2, kProjDc = 4, kProjDx = 8;
+bool proj_step_supported(int64_t T, int64_t h, int64_t Q, int64_t O, int p);
+size_t proj_step_workspace_bytes(int64_t T, int64_t h, int64_t Q, int64_t O, int p);
+hipError_t launch_proj_rows(ProjParams s, void* workspace, hipStream_t stream);
+
 // Polls before a dependency wait of launch_mlp_rows gives up, for the calling
 // thread: 0 restores the default (about 0.25 s), a negative value gives up at
 // the first unsatisfied check.
 void set_step_wait_limit(long long polls);
+// The polls a dependency wait of the persistent launches takes before giving
+// up (set_step_wait_limit's value for the calling thread, or the default).
+long long step_wait_polls();
 
 // Reduction over shards.
 constexpr int kMaxPartials = 16;

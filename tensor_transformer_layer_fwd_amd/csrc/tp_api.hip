@@ -980,6 +980,162 @@ int tp_mlp_step_bwd(const void* X, const void* A, const void* a, const void* B, 
                        workspace_bytes, stream, kPhBwd | kPhWgrad, recompute != 0);
 }
 
+// ---------------------------------------------------------------------------
+// The attention projections of all shards (tp_attn_proj_step)
+// ---------------------------------------------------------------------------
+int tp_attn_proj_step_workspace_size(int64_t T, int64_t h, int64_t Q, int64_t O, int p,
+                                     tp_dtype dt, size_t* bytes) {
+  if (!bytes) return TP_ERR_NULL;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(Q) || !dim_ok(O) || p < 1 || p > kMaxPartials)
+    return TP_ERR_SHAPE;
+  const int64_t pQ = static_cast<int64_t>(p) * Q, pO = static_cast<int64_t>(p) * O;
+  if (!dim_ok(pQ) || !dim_ok(pO)) return TP_ERR_SHAPE;
+  size_t w1 = 0, w2 = 0;
+  int st = tp_linear_bwd_wgrad_workspace_size(T, pO, h, dt, &w1);
+  if (st == TP_OK) st = tp_linear_bwd_wgrad_workspace_size(T, h, pQ, dt, &w2);
+  if (st != TP_OK) return st;
+  // the row launch's counters, then the stacked weight gradients' scratch
+  const size_t rows = dt == TP_BF16 ? proj_step_workspace_bytes(T, h, Q, O, p) : 0;
+  size_t wg = w1 > w2 ? w1 : w2;
+  const size_t both = two_wgrads_bytes(T, h, pQ);
+  wg = wg > both ? wg : both;
+  *bytes = rows + wg;
+  return TP_OK;
+}
+
+int tp_attn_proj_step_plan(int64_t T, int64_t h, int64_t Q, int64_t O, int p, tp_dtype dt,
+                           int* fused) {
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(Q) || !dim_ok(O) || p < 1 || p > kMaxPartials)
+    return TP_ERR_SHAPE;
+  if (fused) *fused = dt == TP_BF16 && proj_step_supported(T, h, Q, O, p);
+  return TP_OK;
+}
+
+int tp_attn_proj_step(const void* X, const void* W, const void* Ow, const void* C,
+                      const void* dZa, const void* dQKV, void* QKV, float* Zpa, void* Za,
+                      void* dC, float* dOw, float* dW, float* dXqp, void* dXq, int64_t T,
+                      int64_t h, int64_t Q, int64_t O, int p, int64_t ld_x, int64_t ld_w,
+                      int64_t ld_ow, int64_t ld_c, int64_t ld_dz, int64_t ld_dqkv, int64_t ld_qkv,
+                      int64_t ld_dc, int64_t ld_za, int64_t ld_dxq, int64_t ld_dow, int64_t ld_dw,
+                      int stages, tp_dtype dt, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  if (stages < 1 || stages > 31) return TP_ERR_SHAPE;
+  if (!dtype_ok(dt)) return TP_ERR_DTYPE;
+  if (!dim_ok(T) || !dim_ok(h) || !dim_ok(Q) || !dim_ok(O) || p < 1 || p > kMaxPartials)
+    return TP_ERR_SHAPE;
+  const int64_t pQ = static_cast<int64_t>(p) * Q, pO = static_cast<int64_t>(p) * O;
+  if (!dim_ok(pQ) || !dim_ok(pO) || ld_x < h || ld_w < pQ || ld_ow < h || ld_c < pO ||
+      ld_dz < h || ld_dqkv < pQ || ld_qkv < pQ || ld_dc < pO || ld_za < h || ld_dxq < h ||
+      ld_dow < h || ld_dw < pQ)
+    return TP_ERR_SHAPE;
+  // the operands each stage reads and writes
+  const bool sq = stages & 1, so = stages & 2, sc = stages & 4, sx = stages & 8, sw = stages & 16;
+  if ((sq && (!X || !W || !QKV)) || (so && (!C || !Ow || !Zpa || !Za)) ||
+      (sc && (!dZa || !Ow || !dC)) || (sx && (!dQKV || !W || !dXqp || !dXq)) ||
+      (sw && (!C || !dZa || !dOw || !X || !dQKV || !dW)))
+    return TP_ERR_NULL;
+  size_t need = 0;
+  int st = tp_attn_proj_step_workspace_size(T, h, Q, O, p, dt, &need);
+  if (st != TP_OK) return st;
+  if (!workspace || workspace_bytes < need) return TP_ERR_WORKSPACE;
+  const size_t es = dt == TP_BF16 ? 2 : 4;
+  auto row_ok = [](const void* q, int64_t ld, size_t e) {
+    return !q || (aligned(q, 16) && (ld * static_cast<int64_t>(e)) % 16 == 0);
+  };
+  const bool fused = dt == TP_BF16 && proj_step_supported(T, h, Q, O, p) &&
+                     row_ok(X, ld_x, es) && row_ok(W, ld_w, es) && row_ok(Ow, ld_ow, es) &&
+                     row_ok(C, ld_c, es) && row_ok(dZa, ld_dz, es) &&
+                     row_ok(dQKV, ld_dqkv, es) && row_ok(QKV, ld_qkv, es) &&
+                     row_ok(dC, ld_dc, es) && row_ok(Za, ld_za, es) && row_ok(dXq, ld_dxq, es) &&
+                     row_ok(Zpa, h, 4) && row_ok(dXqp, h, 4) && aligned(workspace, 256);
+  const size_t rows = dt == TP_BF16 ? proj_step_workspace_bytes(T, h, Q, O, p) : 0;
+  if (fused && (stages & 15)) {
+    ProjParams s{};
+    s.x = X;
+    s.w = W;
+    s.ow = Ow;
+    s.c = C;
+    s.dz = dZa;
+    s.dqkv = dQKV;
+    s.qkv = QKV;
+    s.dc = dC;
+    s.zp = Zpa;
+    s.dxp = dXqp;
+    s.z = Za;
+    s.dx = dXq;
+    s.T = T;
+    s.h = h;
+    s.Q = Q;
+    s.O = O;
+    s.p = p;
+    s.ld_x = ld_x;
+    s.ld_w = ld_w;
+    s.ld_ow = ld_ow;
+    s.ld_c = ld_c;
+    s.ld_dz = ld_dz;
+    s.ld_dqkv = ld_dqkv;
+    s.ld_qkv = ld_qkv;
+    s.ld_dc = ld_dc;
+    s.ld_z = ld_za;
+    s.ld_dx = ld_dxq;
+    s.phases = stages & 15;
+    st = hip_status(launch_proj_rows(s, workspace, stream));
+    if (st != TP_OK) return st;
+  } else if (stages & 15) {
+    // one call per product, shard by shard, then the sums
+    const float* zparts[kMaxPartials];
+    const float* dparts[kMaxPartials];
+    for (int i = 0; i < p; ++i) {
+      zparts[i] = Zpa + i * T * h;
+      dparts[i] = dXqp + i * T * h;
+    }
+    auto col = [&](const void* q, int64_t off) { return static_cast<const char*>(q) + off * es; };
+    for (int i = 0; i < p; ++i) {
+      const void* Wi = col(W, i * Q);
+      const void* Oi = col(Ow, i * O * ld_ow);
+      if (sq) {
+        st = tp_column_linear_fwd(X, Wi, nullptr, static_cast<char*>(QKV) + i * Q * es, nullptr,
+                                  T, h, Q, ld_x, ld_w, ld_qkv, dt, TP_ACT_NONE, stream);
+        if (st != TP_OK) return st;
+      }
+      if (so) {
+        st = tp_row_linear_fwd_partial(col(C, i * O), Oi, Zpa + i * T * h, T, O, h, ld_c, ld_ow,
+                                       h, dt, stream);
+        if (st != TP_OK) return st;
+      }
+      if (sc) {
+        st = tp_linear_bwd_dgrad(dZa, Oi, nullptr, TP_ACT_NONE,
+                                 static_cast<char*>(dC) + i * O * es, T, O, h, ld_dz, ld_ow, ld_dc,
+                                 ld_dc, dt, dt, stream);
+        if (st != TP_OK) return st;
+      }
+      if (sx) {
+        st = tp_linear_bwd_dgrad(col(dQKV, i * Q), Wi, nullptr, TP_ACT_NONE, dXqp + i * T * h, T,
+                                 h, Q, ld_dqkv, ld_w, h, h, dt, TP_F32, stream);
+        if (st != TP_OK) return st;
+      }
+    }
+    if (so) {
+      st = tp_reduce_partials(zparts, p, nullptr, Za, T, h, h, ld_za, dt, stream);
+      if (st != TP_OK) return st;
+    }
+    if (sx) {
+      st = tp_reduce_partials(dparts, p, nullptr, dXq, T, h, h, ld_dxq, dt, stream);
+      if (st != TP_OK) return st;
+    }
+  }
+  if (sw) {
+    // dO = C^T dZa ([p*O, h]) and dW = X^T dQKV ([h, p*Q]) over the stacked shards
+    char* w = static_cast<char*>(workspace) + (fused ? rows : 0);
+    return two_wgrads(C, dZa, dOw, nullptr, pO, h, ld_c, ld_dz, ld_dow, X, dQKV, dW, nullptr, h,
+                      pQ, ld_x, ld_dqkv, ld_dw, T, dt, w, workspace_bytes - (fused ? rows : 0),
+                      stream);
+  }
+  return TP_OK;
+}
+
 int tp_reduce_partials(const float* const* partials, int p, const void* bias, void* out,
                        int64_t T, int64_t h, int64_t ld_p, int64_t ld_out, tp_dtype out_dt,
                        hipStream_t stream) {

@@ -56,8 +56,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # Sources of the pipelined bf16 GEMM kernels, of the fused step's persistent
 # launch and of their tile choice: the kernels whose HBM traffic
 # profiles/traffic.json records.
-GEMM_SOURCES = ("gemm_bf16_pipe.hip", "gemm_tile.h", "mlp_step.hip", "device_common.h",
-                "internal.h", "colsum_device.h", "plan.hip")
+GEMM_SOURCES = ("gemm_bf16_pipe.hip", "gemm_tile.h", "mlp_step.hip", "proj_step.hip",
+                "step_queue.h", "device_common.h", "internal.h", "colsum_device.h", "plan.hip")
 
 
 def source_hash() -> str:

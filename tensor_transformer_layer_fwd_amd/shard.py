@@ -89,6 +89,9 @@ class ShardStep:
                               (not self.recompute or
                                (cfg.dtype == "bf16" and
                                 L.tp_mlp_step_plan(cfg.T, cfg.h, cfg.F, cfg.p, L.TP_BF16))))
+        # every shard's attention projections in tp_attn_proj_step calls
+        self.proj_call = bool(step_call and cfg.attn and len(cfg.shards) == cfg.p and
+                              self.fused_bwd and cfg.full_weights)
         # the fused step as its forward and backward calls: always with recompute
         self.split_step = self.step_call and (bool(split_step) or self.recompute)
         self.rebuild_y = (self.recompute and self.fused_bwd and not self.step_call and
@@ -161,19 +164,46 @@ class ShardStep:
                     dtype=torch.uint8, device=self.device)
         if cfg.attn:
             Q, O = cfg.Q, cfg.O
-            for i in shards:
-                self.out[f"QKV_{i}"] = torch.empty(T, Q, **act)
-                self.out[f"Zpa_{i}"] = torch.empty(T, h, **f32)
-                self.out[f"dC_{i}"] = torch.empty(T, O, **act)
-                self.out[f"dOw_{i}"] = torch.empty(O, h, **f32)
-                self.out[f"dW_{i}"] = torch.empty(h, Q, **f32)
-                self.out[f"dXqp_{i}"] = torch.empty(T, h, **f32)
+            if self.proj_call:
+                # every shard's tensors as blocks of one buffer each, in the
+                # layouts of tp_attn_proj_step (QKV_i = QKV[:, iQ:(i+1)Q], ...)
+                p = cfg.p
+                self.attn = {"QKV": torch.empty(T, p * Q, **act), "Zpa": torch.empty(p, T, h, **f32),
+                             "dC": torch.empty(T, p * O, **act), "dOw": torch.empty(p * O, h, **f32),
+                             "dW": torch.empty(h, p * Q, **f32), "dXqp": torch.empty(p, T, h, **f32)}
+                if self.attn_core:
+                    self.attn["C"] = torch.empty(T, p * O, **act)
+                    self.attn["dQKV"] = torch.empty(T, p * Q, **act)
+                a = self.attn
+                for i in shards:
+                    qc, oc = slice(i * Q, (i + 1) * Q), slice(i * O, (i + 1) * O)
+                    self.out[f"QKV_{i}"] = a["QKV"][:, qc]
+                    self.out[f"Zpa_{i}"] = a["Zpa"][i]
+                    self.out[f"dC_{i}"] = a["dC"][:, oc]
+                    self.out[f"dOw_{i}"] = a["dOw"][oc]
+                    self.out[f"dW_{i}"] = a["dW"][:, qc]
+                    self.out[f"dXqp_{i}"] = a["dXqp"][i]
+                    if self.attn_core:
+                        self.out[f"C_{i}"] = a["C"][:, oc]
+                        self.out[f"dQKV_{i}"] = a["dQKV"][:, qc]
+                self.proj_ws = torch.zeros(
+                    max(L.tp_attn_proj_step_workspace_size(T, h, Q, O, p, self.tp_dt), 256),
+                    dtype=torch.uint8, device=self.device)
+            else:
+                for i in shards:
+                    self.out[f"QKV_{i}"] = torch.empty(T, Q, **act)
+                    self.out[f"Zpa_{i}"] = torch.empty(T, h, **f32)
+                    self.out[f"dC_{i}"] = torch.empty(T, O, **act)
+                    self.out[f"dOw_{i}"] = torch.empty(O, h, **f32)
+                    self.out[f"dW_{i}"] = torch.empty(h, Q, **f32)
+                    self.out[f"dXqp_{i}"] = torch.empty(T, h, **f32)
             if self.attn_core:
                 b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
                 for i in shards:
-                    self.out[f"C_{i}"] = torch.empty(T, O, **act)
+                    if not self.proj_call:
+                        self.out[f"C_{i}"] = torch.empty(T, O, **act)
+                        self.out[f"dQKV_{i}"] = torch.empty(T, Q, **act)
                     self.out[f"lse_{i}"] = torch.empty(b, H, Ls, **f32)
-                    self.out[f"dQKV_{i}"] = torch.empty(T, Q, **act)
                 self.delta = torch.empty(b, H, Ls, **f32)
             if len(shards) == cfg.p:
                 self.out["Za"] = torch.empty(T, h, **act)
@@ -356,10 +386,36 @@ class ShardStep:
         """C_i: the core's output, or the drawn input of the projection-only step."""
         return self.out[f"C_{i}"] if self.attn_core else self._col("C", i, self.cfg.O)
 
+    def proj_step(self, stages):
+        """Stages of every shard's attention projections in one
+        tp_attn_proj_step call."""
+        inp, a, o = self.inp, self.attn, self.out
+        C = a["C"] if self.attn_core else inp["C"]
+        dQKV = a["dQKV"] if self.attn_core else inp["dQKV"]
+        L.tp_attn_proj_step(inp["X"], inp["W"], inp["Ow"], C, inp["dZa"], dQKV, a["QKV"],
+                            a["Zpa"], o["Za"], a["dC"], a["dOw"], a["dW"], a["dXqp"], o["dXq"],
+                            self.proj_ws, stages=stages)
+
     def attn_forward(self):
         cfg, o, inp = self.cfg, self.out, self.inp
         Q, O = cfg.Q, cfg.O
         b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
+        if self.proj_call:
+            if not self.attn_core:  # every stage reads only inputs: one call
+                self.proj_step(("qkv", "out", "dc", "dx", "wgrad"))
+                return
+            # QKV alone is a single product per shard, which the per-product
+            # tiles balance better than a launch of that stage alone
+            for i in cfg.shards:
+                L.tp_column_linear_fwd(inp["X"], self._col("W", i, Q), None, o[f"QKV_{i}"], None,
+                                       act="none")
+            for i in cfg.shards:
+                L.tp_attention_fwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"lse_{i}"], b, Ls, H)
+            # the output projection's forward and its data gradient read the
+            # same C_i, O_i and dZa: one launch, as the MLP step runs a layer's
+            # forward and backward in one
+            self.proj_step(("out", "dc"))
+            return
         for i in cfg.shards:
             L.tp_column_linear_fwd(inp["X"], self._col("W", i, Q), None, o[f"QKV_{i}"], None,
                                    act="none")
@@ -373,6 +429,13 @@ class ShardStep:
         cfg, o, inp = self.cfg, self.out, self.inp
         Q, O = cfg.Q, cfg.O
         b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
+        if self.proj_call:
+            if self.attn_core:  # without the core the forward call did it all
+                for i in cfg.shards:
+                    L.tp_attention_bwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"dC_{i}"], o[f"lse_{i}"],
+                                       self.delta, o[f"dQKV_{i}"], b, Ls, H)
+                self.proj_step(("dx", "wgrad"))
+            return
         for i in cfg.shards:
             Ow_i, W_i = self._row("Ow", i, O), self._col("W", i, Q)
             self._bwd(inp["dZa"], Ow_i, None, self._c(i), o[f"dC_{i}"], o[f"dOw_{i}"], None,

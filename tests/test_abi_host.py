@@ -546,6 +546,45 @@ def test_mlp_step_validation(lib):
         assert call(wsb=1024) == -5
 
 
+def test_attn_proj_step_queries_and_validation(lib):
+    """tp_attn_proj_step's queries and its argument checks, before any launch."""
+    bf = L.TP_BF16
+    assert L.tp_attn_proj_step_plan(4096, 1024, 1536, 512, 2, bf)    # attention projections
+    assert L.tp_attn_proj_step_plan(6144, 1024, 768, 256, 4, bf)     # the ~350M layer's
+    assert not L.tp_attn_proj_step_plan(680, 1024, 1536, 512, 2, bf)  # T not a multiple of 1024
+    assert not L.tp_attn_proj_step_plan(4096, 1024, 1536, 500, 2, bf)
+    assert not L.tp_attn_proj_step_plan(4096, 1024, 1536, 512, 2, L.TP_F32)
+    ws = L.tp_attn_proj_step_workspace_size(4096, 1024, 1536, 512, 2, bf)
+    assert ws % 256 == 0 and ws >= L.tp_linear_bwd_wgrad_workspace_size(4096, 1024, 3072, bf)
+    out = ctypes.c_size_t(0)
+    assert lib.tp_attn_proj_step_workspace_size(4096, 1024, 1536, 512, 0, bf,
+                                                ctypes.byref(out)) == -2
+    assert lib.tp_attn_proj_step_workspace_size(4096, 1024, 1536, 512, 2, 9,
+                                                ctypes.byref(out)) == -3
+    assert lib.tp_attn_proj_step_workspace_size(4096, 1024, 1536, 512, 2, bf, None) == -1
+    F_ = FAKE
+
+    def call(*, stages=31, X=F_, C=F_, dQKV=F_, T=4096, p=2, ld_w=3072, dt=1, ws=F_,
+             wsb=1 << 30):
+        return lib.tp_attn_proj_step(X, F_, F_, C, F_, dQKV, F_, F_, F_, F_, F_, F_, F_, F_, T,
+                                     1024, 1536, 512, p, 1024, ld_w, 1024, 1024, 1024, 3072, 3072,
+                                     1024, 1024, 1024, 1024, 3072, stages, dt, ws, wsb, None)
+    assert call(stages=0) == -2
+    assert call(stages=32) == -2
+    assert call(X=None) == -1                 # stage 1 reads X
+    # dC alone does not read X: that call passes the pointer checks and stops
+    # at the (too small) workspace, so nothing is launched
+    assert call(stages=4, X=None, wsb=1024) == -5
+    assert call(stages=2, C=None) == -1
+    assert call(stages=8, dQKV=None) == -1
+    assert call(T=0) == -2
+    assert call(p=17) == -2
+    assert call(ld_w=3071) == -2
+    assert call(dt=4) == -3
+    assert call(ws=None, wsb=0) == -5
+    assert call(wsb=1024) == -5
+
+
 def test_noalloc_wgrad_rejects_shape_beyond_scratch(lib):
     # the size check runs before any HIP call, so this needs no GPU; the
     # pointers are never dereferenced
