@@ -217,17 +217,18 @@ def shard_calls(step, i=0):
             br8 = T * p * Q * e + h * p * Q * e + 2 * p * T * h * 4 + T * h * e
             calls.append(Call("attn_proj_dx_wgrad", lambda: step.proj_step(24), f_x + fw, br8 + bw,
                               False, geom))
+            # the core of every shard's heads in one launch per direction
             ff, fb = attention_core_flops(cfg)
-            hd = H * 64
-            calls.append(Call("attn_fwd",
-                              lambda: L.tp_attention_fwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"lse_{i}"],
-                                                         b, Ls, H),
-                              ff, T * 3 * hd * 2 + T * hd * 2 + b * H * Ls * 4, True))
-            calls.append(Call("attn_bwd",
-                              lambda: L.tp_attention_bwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"dC_{i}"],
-                                                         o[f"lse_{i}"], step.delta,
-                                                         o[f"dQKV_{i}"], b, Ls, H),
-                              fb, T * 3 * hd * 2 * 2 + 2 * T * hd * 2 + b * H * Ls * 4 * 3,
+            hd, a = p * H * 64, step.attn
+            calls.append(Call("attn_fwd_shards",
+                              lambda: L.tp_attention_fwd(a["QKV"], a["C"], a["lse"], b, Ls, H,
+                                                         shards=p),
+                              p * ff, T * 3 * hd * 2 + T * hd * 2 + b * p * H * Ls * 4, True))
+            calls.append(Call("attn_bwd_shards",
+                              lambda: L.tp_attention_bwd(a["QKV"], a["C"], a["dC"], a["lse"],
+                                                         step.delta, a["dQKV"], b, Ls, H,
+                                                         shards=p),
+                              p * fb, T * 3 * hd * 2 * 2 + 2 * T * hd * 2 + b * p * H * Ls * 4 * 3,
                               False))
     elif cfg.attn:
         Q, O = cfg.Q, cfg.O

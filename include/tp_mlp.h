@@ -569,6 +569,29 @@ int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float
                      int64_t ld_dqkv, int causal, tp_dtype dt, hipStream_t stream);
 
 /*
+ * The attention core of `shards` shards in one launch, forward and backward:
+ * every shard as tp_attention_fwd / tp_attention_bwd with `heads` heads, the
+ * shards side by side in the layouts tp_attn_proj_step stacks them in:
+ *   QKV, dQKV [batch*seq, shards*3*heads*head_dim]: shard s's [Q | K | V]
+ *             block is columns s*3*heads*head_dim ..
+ *   C, dC     [batch*seq, shards*heads*head_dim]: shard s's heads are
+ *             columns s*heads*head_dim ..
+ *   lse, delta [batch, shards*heads, seq] fp32
+ * The results equal the per-shard calls bit for bit (each shard's heads run
+ * the same kernels in the same order); one launch fills the device where one
+ * shard's heads would not. Arguments and errors as the single-shard calls,
+ * with shards in 1 .. 16 (TP_ERR_SHAPE otherwise).
+ */
+int tp_attention_fwd_shards(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
+                            int64_t heads, int64_t shards, int64_t head_dim, int64_t ld_qkv,
+                            int64_t ld_c, int causal, tp_dtype dt, hipStream_t stream);
+int tp_attention_bwd_shards(const void* QKV, const void* C, const void* dC, const float* lse,
+                            float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
+                            int64_t shards, int64_t head_dim, int64_t ld_qkv, int64_t ld_c,
+                            int64_t ld_dc, int64_t ld_dqkv, int causal, tp_dtype dt,
+                            hipStream_t stream);
+
+/*
  * FP8 variant of the shard GEMMs. The "Megatron" page ("mixed-precision
  * training") trains in FP8 besides FP16/BF16, and the "Megatron-LM
  * quick-start" page ("performance optimisation") recommends it; neither fixes

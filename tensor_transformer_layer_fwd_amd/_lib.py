@@ -114,6 +114,10 @@ SIGNATURES = {
                                        _i64, _i64, _i64, _i64, _i64, _vp, ctypes.c_size_t, _vp]),
     "tp_attention_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                 _i64, _i64, _int, _int, _vp]),
+    "tp_attention_fwd_shards": (_int, [_vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                       _int, _int, _vp]),
+    "tp_attention_bwd_shards": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i64,
+                                       _i64, _i64, _i64, _i64, _int, _int, _vp]),
     "tp_set_gemm_override": (_int, [_int, _int]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_hip_error": (_int, []),
@@ -612,40 +616,51 @@ def tp_gemm_plan(M: int, N: int, K: int, allow_split: bool = False):
 
 
 def tp_attention_fwd(QKV, C, lse, batch: int, seq: int, heads: int, causal: bool = True,
-                     stream=None):
+                     stream=None, shards: int = 1):
     """Attention core of one shard: QKV [batch*seq, 3*heads*64] bf16 -> C
-    [batch*seq, heads*64] bf16 and lse [batch, heads, seq] fp32 (or None)."""
-    chk = _Operands("tp_attention_fwd")
-    T, hd, bf = batch * seq, heads * 64, _torch_dtypes("bf16")
+    [batch*seq, heads*64] bf16 and lse [batch, heads, seq] fp32 (or None).
+    shards > 1: that many shards of `heads` heads side by side in one launch
+    (tp_attention_fwd_shards): QKV [.., shards*3*heads*64], C [.., shards*heads*64],
+    lse [batch, shards*heads, seq]."""
+    fn = "tp_attention_fwd" if shards == 1 else "tp_attention_fwd_shards"
+    chk = _Operands(fn)
+    H = heads * shards
+    T, hd, bf = batch * seq, H * 64, _torch_dtypes("bf16")
     chk("QKV", QKV, (T, 3 * hd), bf)("C", C, (T, hd), bf)
     if lse is not None:
-        chk("lse", lse, (batch * heads * seq,) if lse.dim() == 1 else (batch, heads, seq),
+        chk("lse", lse, (batch * H * seq,) if lse.dim() == 1 else (batch, H, seq),
             _torch_dtypes("f32"))
         if not lse.is_contiguous():
-            raise ValueError("tp_attention_fwd: lse must be contiguous")
+            raise ValueError(f"{fn}: lse must be contiguous")
     chk.done(stream)
-    _check("tp_attention_fwd", lib().tp_attention_fwd(
-        _ptr(QKV), _ptr(C), _ptr(lse), batch, seq, heads, 64, _ld(QKV), _ld(C), int(bool(causal)),
-        _dt(QKV), _stream(stream)))
+    extra = [] if shards == 1 else [shards]
+    _check(fn, getattr(lib(), fn)(
+        _ptr(QKV), _ptr(C), _ptr(lse), batch, seq, heads, *extra, 64, _ld(QKV), _ld(C),
+        int(bool(causal)), _dt(QKV), _stream(stream)))
 
 
 def tp_attention_bwd(QKV, C, dC, lse, delta, dQKV, batch: int, seq: int, heads: int,
-                     causal: bool = True, stream=None):
+                     causal: bool = True, stream=None, shards: int = 1):
     """Backward of tp_attention_fwd: dQKV (laid out like QKV) from dC, the
-    forward's C and lse; delta [batch, heads, seq] fp32 is a workspace."""
-    chk = _Operands("tp_attention_bwd")
-    T, hd, bf, f32 = batch * seq, heads * 64, _torch_dtypes("bf16"), _torch_dtypes("f32")
+    forward's C and lse; delta [batch, heads, seq] fp32 is a workspace.
+    shards as tp_attention_fwd (delta [batch, shards*heads, seq])."""
+    fn = "tp_attention_bwd" if shards == 1 else "tp_attention_bwd_shards"
+    chk = _Operands(fn)
+    H = heads * shards
+    T, hd, bf, f32 = batch * seq, H * 64, _torch_dtypes("bf16"), _torch_dtypes("f32")
     chk("QKV", QKV, (T, 3 * hd), bf)("C", C, (T, hd), bf)("dC", dC, (T, hd), bf)
     chk("dQKV", dQKV, (T, 3 * hd), bf)
     for name, t in (("lse", lse), ("delta", delta)):
-        chk(name, t, (batch * heads * seq,) if t is not None and t.dim() == 1
-            else (batch, heads, seq), f32)
+        chk(name, t, (batch * H * seq,) if t is not None and t.dim() == 1
+            else (batch, H, seq), f32)
         if not t.is_contiguous():
-            raise ValueError(f"tp_attention_bwd: {name} must be contiguous")
+            raise ValueError(f"{fn}: {name} must be contiguous")
     chk.done(stream)
-    _check("tp_attention_bwd", lib().tp_attention_bwd(
-        _ptr(QKV), _ptr(C), _ptr(dC), _ptr(lse), _ptr(delta), _ptr(dQKV), batch, seq, heads, 64,
-        _ld(QKV), _ld(C), _ld(dC), _ld(dQKV), int(bool(causal)), _dt(QKV), _stream(stream)))
+    extra = [] if shards == 1 else [shards]
+    _check(fn, getattr(lib(), fn)(
+        _ptr(QKV), _ptr(C), _ptr(dC), _ptr(lse), _ptr(delta), _ptr(dQKV), batch, seq, heads,
+        *extra, 64, _ld(QKV), _ld(C), _ld(dC), _ld(dQKV), int(bool(causal)), _dt(QKV),
+        _stream(stream)))
 
 
 TP_FP8_E4M3, TP_FP8_E5M2 = 0, 1

@@ -99,7 +99,8 @@ __global__ __launch_bounds__(64 * QW * KG) void attn_fwd_kernel(AttnParams p) {
   const int64_t seq = p.seq;
   const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
   const int64_t row0 = b * seq;  // first token of the sequence
-  const int64_t hd = p.heads * kD;
+  const int64_t hd = p.group * kD;  // Q to K, K to V
+  const int64_t qcol = (h / p.group) * 3 * hd + (h % p.group) * kD;  // this head's Q
 
   // ---- Q fragments (B operand of S^T = K Q^T), kept for the whole pass
   const int ql = lane & 31, half = lane >> 5;
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(64 * QW * KG) void attn_fwd_kernel(AttnParams p) {
   bf16x8_t qf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
-    qf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + qrow * p.ld_qkv + h * kD + 16 * ks + 8 * half);
+    qf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + qrow * p.ld_qkv + qcol + 16 * ks + 8 * half);
   // (issued before the first tile copies and so, loads returning in order,
   // landed whenever those copies have)
 
@@ -121,7 +122,7 @@ __global__ __launch_bounds__(64 * QW * KG) void attn_fwd_kernel(AttnParams p) {
   for (int i = 0; i < WPW; ++i) {
     const int w = wave * WPW + i, t = (w / 8) % 2, r = 8 * (w % 8) + lane / 8, pc = lane % 8;
     const int c = pc ^ (t == 0 ? kswz(r) : vswz(r));
-    src[i] = qkv + (row0 + r) * p.ld_qkv + (1 + t) * hd + h * kD + c * 8;
+    src[i] = qkv + (row0 + r) * p.ld_qkv + qcol + (1 + t) * hd + c * 8;
   }
   // stage of key tiles KG*kp .. KG*kp + KG-1; a tile past the last one is
   // still copied (its rows clamp to the sequence's last) so that every wave
@@ -523,7 +524,8 @@ __device__ __forceinline__ void attn_bwd_kv_block(const AttnBwdParams& p, const 
   const int bh = block / nkb;
   const int h = bh % static_cast<int>(p.heads);
   const int64_t b = bh / p.heads;
-  const int64_t row0 = b * seq, hd = p.heads * kD;
+  const int64_t row0 = b * seq, hd = p.group * kD;
+  const int64_t qcol = (h / p.group) * 3 * hd + (h % p.group) * kD;
   const int64_t lbase = (b * p.heads + h) * seq;
   const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
   const uint16_t* dcp = static_cast<const uint16_t*>(p.dc);
@@ -535,8 +537,8 @@ __device__ __forceinline__ void attn_bwd_kv_block(const AttnBwdParams& p, const 
   bf16x8_t kf[4], vf[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    kf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + krow * p.ld_qkv + hd + h * kD + 16 * ks + 8 * half);
-    vf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + krow * p.ld_qkv + 2 * hd + h * kD + 16 * ks + 8 * half);
+    kf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + krow * p.ld_qkv + qcol + hd + 16 * ks + 8 * half);
+    vf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + krow * p.ld_qkv + qcol + 2 * hd + 16 * ks + 8 * half);
   }
   attn_wait_vmcnt<0>();
   lds_tie(kf);
@@ -548,7 +550,7 @@ __device__ __forceinline__ void attn_bwd_kv_block(const AttnBwdParams& p, const 
   const int qt0 = p.causal ? kb * 2 : 0;
   const int nst = (nqt - qt0 + QG - 1) / QG;
   TileCopy cq, cd;
-  cq.init(qkv, p.ld_qkv, row0, h * kD, 2 * kw, lane);  // Q tile: windows 2kw, 2kw+1
+  cq.init(qkv, p.ld_qkv, row0, qcol, 2 * kw, lane);  // Q tile: windows 2kw, 2kw+1
   cd.init(dcp, p.ld_dc, row0, h * kD, 2 * kw, lane);   // dC tile
   static_assert(POOL == 0 || POOL >= kLds, "LDS pool");
   uint8_t* const lds = attn_bwd_lds<POOL ? POOL : kLds>();
@@ -692,7 +694,7 @@ __device__ __forceinline__ void attn_bwd_kv_block(const AttnBwdParams& p, const 
 
   // dK = dK^T^T / 8, dV = dV^T^T: lane holds key `key`, d = 32db + 8*(r/4) + 4*half + r%4
   if (key < seq) {
-    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + (row0 + key) * p.ld_dqkv + h * kD;
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + (row0 + key) * p.ld_dqkv + qcol;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll
@@ -733,7 +735,8 @@ __device__ __forceinline__ void attn_bwd_q_block(const AttnBwdParams& p, const i
   const int bh = BYLEN ? block % nbh : block / nqb;
   const int h = bh % static_cast<int>(p.heads);
   const int64_t b = bh / p.heads;
-  const int64_t row0 = b * seq, hd = p.heads * kD;
+  const int64_t row0 = b * seq, hd = p.group * kD;
+  const int64_t qcol = (h / p.group) * 3 * hd + (h % p.group) * kD;
   const int64_t lbase = (b * p.heads + h) * seq;
   const uint16_t* qkv = static_cast<const uint16_t*>(p.qkv);
   const uint16_t* dcp = static_cast<const uint16_t*>(p.dc);
@@ -743,7 +746,7 @@ __device__ __forceinline__ void attn_bwd_q_block(const AttnBwdParams& p, const i
   bf16x8_t qf[4], df[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    qf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + qrow * p.ld_qkv + h * kD + 16 * ks + 8 * half);
+    qf[ks] = *reinterpret_cast<const bf16x8_t*>(qkv + qrow * p.ld_qkv + qcol + 16 * ks + 8 * half);
     df[ks] = *reinterpret_cast<const bf16x8_t*>(dcp + qrow * p.ld_dc + h * kD + 16 * ks + 8 * half);
   }
   const float lq = p.lse[lbase + (q < seq ? q : seq - 1)] * 1.4426950408889634f;
@@ -758,8 +761,8 @@ __device__ __forceinline__ void attn_bwd_q_block(const AttnBwdParams& p, const i
   const int nst = (nkt + KG - 1) / KG;
   const int wq_first = qb * kQB + qw * 32, wq_last = wq_first + 31;
   TileCopy ck, cv;
-  ck.init(qkv, p.ld_qkv, row0, hd + h * kD, 2 * qw, lane);
-  cv.init(qkv, p.ld_qkv, row0, 2 * hd + h * kD, 2 * qw, lane);
+  ck.init(qkv, p.ld_qkv, row0, qcol + hd, 2 * qw, lane);
+  cv.init(qkv, p.ld_qkv, row0, qcol + 2 * hd, 2 * qw, lane);
   static_assert(POOL == 0 || POOL >= kLds, "LDS pool");
   uint8_t* const lds = attn_bwd_lds<POOL ? POOL : kLds>();
   FragAddr fa;
@@ -867,7 +870,7 @@ __device__ __forceinline__ void attn_bwd_q_block(const AttnBwdParams& p, const i
   }
 
   if (q < seq) {
-    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + (row0 + q) * p.ld_dqkv + h * kD;
+    uint16_t* out = static_cast<uint16_t*>(p.dqkv) + (row0 + q) * p.ld_dqkv + qcol;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
 #pragma unroll

@@ -128,6 +128,11 @@ struct AttnParams {
   void* c;
   float* lse;
   int64_t batch, seq, heads, ld_qkv, ld_c;
+  // heads per block of QKV columns: head h's Q, K and V are at columns
+  // (h / group) * 3 * group * 64 + (h % group) * 64, + group * 64 and
+  // + 2 * group * 64 (group = heads: one [Q | K | V] block; one block per
+  // shard when several shards' heads run in one launch)
+  int64_t group;
   int causal;
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };
@@ -143,6 +148,7 @@ struct AttnBwdParams {
   float* delta;
   void* dqkv;
   int64_t batch, seq, heads, ld_qkv, ld_c, ld_dc, ld_dqkv;
+  int64_t group;  // heads per block of QKV (and dQKV) columns, as AttnParams
   int causal;
   float scale_log2;  // log2(e) / sqrt(head_dim)
 };

@@ -1181,13 +1181,20 @@ int tp_bias_act(const void* U, const void* bias, void* Y, int64_t T, int64_t n, 
   return hip_status(launch_bias_act(b, stream));
 }
 
-int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
-                     int64_t heads, int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int causal,
-                     tp_dtype dt, hipStream_t stream) {
+// Attention core of `shards` shards of `heads` heads each in one launch: shard
+// s's [Q | K | V] block is columns s*3*heads*64 .. of QKV (as tp_attn_proj_step
+// stacks it), its heads are C's columns s*heads*64 .., and lse and delta are
+// [batch, shards*heads, seq].
+static int attention_fwd_impl(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
+                              int64_t heads, int64_t shards, int64_t head_dim, int64_t ld_qkv,
+                              int64_t ld_c, int causal, tp_dtype dt, hipStream_t stream) {
   if (!QKV || !C) return TP_ERR_NULL;
   if (dt != TP_BF16) return TP_ERR_DTYPE;
-  if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || head_dim != 64) return TP_ERR_SHAPE;
-  if (ld_qkv < 3 * heads * head_dim || ld_c < heads * head_dim) return TP_ERR_SHAPE;
+  if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || shards < 1 || shards > kMaxPartials ||
+      head_dim != 64)
+    return TP_ERR_SHAPE;
+  const int64_t all = heads * shards;
+  if (ld_qkv < 3 * all * head_dim || ld_c < all * head_dim) return TP_ERR_SHAPE;
   if ((reinterpret_cast<uintptr_t>(QKV) & 15) || (ld_qkv & 7) ||
       (reinterpret_cast<uintptr_t>(C) & 7) || (ld_c & 3))
     return TP_ERR_SHAPE;
@@ -1198,7 +1205,8 @@ int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_
   a.lse = lse;
   a.batch = batch;
   a.seq = seq;
-  a.heads = heads;
+  a.heads = all;
+  a.group = heads;
   a.ld_qkv = ld_qkv;
   a.ld_c = ld_c;
   a.causal = causal != 0;
@@ -1206,14 +1214,17 @@ int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_
   return hip_status(launch_attention_fwd(a, stream));
 }
 
-int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float* lse,
-                     float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
-                     int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
-                     int64_t ld_dqkv, int causal, tp_dtype dt, hipStream_t stream) {
+static int attention_bwd_impl(const void* QKV, const void* C, const void* dC, const float* lse,
+                              float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
+                              int64_t shards, int64_t head_dim, int64_t ld_qkv, int64_t ld_c,
+                              int64_t ld_dc, int64_t ld_dqkv, int causal, tp_dtype dt,
+                              hipStream_t stream) {
   if (!QKV || !C || !dC || !lse || !delta || !dQKV) return TP_ERR_NULL;
   if (dt != TP_BF16) return TP_ERR_DTYPE;
-  if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || head_dim != 64) return TP_ERR_SHAPE;
-  const int64_t hd = heads * head_dim;
+  if (!dim_ok(batch) || !dim_ok(seq) || !dim_ok(heads) || shards < 1 || shards > kMaxPartials ||
+      head_dim != 64)
+    return TP_ERR_SHAPE;
+  const int64_t all = heads * shards, hd = all * head_dim;
   if (ld_qkv < 3 * hd || ld_c < hd || ld_dc < hd || ld_dqkv < 3 * hd) return TP_ERR_SHAPE;
   auto al = [](const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; };
   if (!al(QKV, 16) || (ld_qkv & 7) || !al(C, 16) || (ld_c & 7) || !al(dC, 16) || (ld_dc & 7) ||
@@ -1229,7 +1240,8 @@ int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float
   a.dqkv = dQKV;
   a.batch = batch;
   a.seq = seq;
-  a.heads = heads;
+  a.heads = all;
+  a.group = heads;
   a.ld_qkv = ld_qkv;
   a.ld_c = ld_c;
   a.ld_dc = ld_dc;
@@ -1237,6 +1249,37 @@ int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float
   a.causal = causal != 0;
   a.scale_log2 = static_cast<float>(1.4426950408889634 / 8.0);  // log2(e) / sqrt(64)
   return hip_status(launch_attention_bwd(a, stream));
+}
+
+int tp_attention_fwd(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
+                     int64_t heads, int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int causal,
+                     tp_dtype dt, hipStream_t stream) {
+  return attention_fwd_impl(QKV, C, lse, batch, seq, heads, 1, head_dim, ld_qkv, ld_c, causal, dt,
+                            stream);
+}
+
+int tp_attention_bwd(const void* QKV, const void* C, const void* dC, const float* lse,
+                     float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
+                     int64_t head_dim, int64_t ld_qkv, int64_t ld_c, int64_t ld_dc,
+                     int64_t ld_dqkv, int causal, tp_dtype dt, hipStream_t stream) {
+  return attention_bwd_impl(QKV, C, dC, lse, delta, dQKV, batch, seq, heads, 1, head_dim, ld_qkv,
+                            ld_c, ld_dc, ld_dqkv, causal, dt, stream);
+}
+
+int tp_attention_fwd_shards(const void* QKV, void* C, float* lse, int64_t batch, int64_t seq,
+                            int64_t heads, int64_t shards, int64_t head_dim, int64_t ld_qkv,
+                            int64_t ld_c, int causal, tp_dtype dt, hipStream_t stream) {
+  return attention_fwd_impl(QKV, C, lse, batch, seq, heads, shards, head_dim, ld_qkv, ld_c,
+                            causal, dt, stream);
+}
+
+int tp_attention_bwd_shards(const void* QKV, const void* C, const void* dC, const float* lse,
+                            float* delta, void* dQKV, int64_t batch, int64_t seq, int64_t heads,
+                            int64_t shards, int64_t head_dim, int64_t ld_qkv, int64_t ld_c,
+                            int64_t ld_dc, int64_t ld_dqkv, int causal, tp_dtype dt,
+                            hipStream_t stream) {
+  return attention_bwd_impl(QKV, C, dC, lse, delta, dQKV, batch, seq, heads, shards, head_dim,
+                            ld_qkv, ld_c, ld_dc, ld_dqkv, causal, dt, stream);
 }
 
 int tp_fp8_quantize_workspace_size(int64_t rows, int64_t cols, size_t* bytes) {

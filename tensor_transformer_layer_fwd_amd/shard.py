@@ -199,12 +199,18 @@ class ShardStep:
                     self.out[f"dXqp_{i}"] = torch.empty(T, h, **f32)
             if self.attn_core:
                 b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
-                for i in shards:
-                    if not self.proj_call:
+                if self.proj_call:
+                    # every shard's heads side by side: one core launch per direction
+                    self.attn["lse"] = torch.empty(b, cfg.p * H, Ls, **f32)
+                    self.delta = torch.empty(b, cfg.p * H, Ls, **f32)
+                    for i in shards:
+                        self.out[f"lse_{i}"] = self.attn["lse"][:, i * H:(i + 1) * H]
+                else:
+                    for i in shards:
                         self.out[f"C_{i}"] = torch.empty(T, O, **act)
                         self.out[f"dQKV_{i}"] = torch.empty(T, Q, **act)
-                    self.out[f"lse_{i}"] = torch.empty(b, H, Ls, **f32)
-                self.delta = torch.empty(b, H, Ls, **f32)
+                        self.out[f"lse_{i}"] = torch.empty(b, H, Ls, **f32)
+                    self.delta = torch.empty(b, H, Ls, **f32)
             if len(shards) == cfg.p:
                 self.out["Za"] = torch.empty(T, h, **act)
                 self.out["dXq"] = torch.empty(T, h, **act)
@@ -409,8 +415,8 @@ class ShardStep:
             for i in cfg.shards:
                 L.tp_column_linear_fwd(inp["X"], self._col("W", i, Q), None, o[f"QKV_{i}"], None,
                                        act="none")
-            for i in cfg.shards:
-                L.tp_attention_fwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"lse_{i}"], b, Ls, H)
+            a = self.attn
+            L.tp_attention_fwd(a["QKV"], a["C"], a["lse"], b, Ls, H, shards=cfg.p)
             # the output projection's forward and its data gradient read the
             # same C_i, O_i and dZa: one launch, as the MLP step runs a layer's
             # forward and backward in one
@@ -431,9 +437,9 @@ class ShardStep:
         b, Ls, H = cfg.micro_batch, cfg.seq, cfg.heads // cfg.p
         if self.proj_call:
             if self.attn_core:  # without the core the forward call did it all
-                for i in cfg.shards:
-                    L.tp_attention_bwd(o[f"QKV_{i}"], o[f"C_{i}"], o[f"dC_{i}"], o[f"lse_{i}"],
-                                       self.delta, o[f"dQKV_{i}"], b, Ls, H)
+                a = self.attn
+                L.tp_attention_bwd(a["QKV"], a["C"], a["dC"], a["lse"], self.delta, a["dQKV"], b,
+                                   Ls, H, shards=cfg.p)
                 self.proj_step(("dx", "wgrad"))
             return
         for i in cfg.shards:

@@ -140,3 +140,37 @@ def test_attention_block_graph_replay_is_bitwise(dev):
         got = step.results()
         for k in want:
             np.testing.assert_array_equal(got[k], want[k], err_msg=k)
+
+
+@pytest.mark.parametrize("shards,batch,seq,heads", [(2, 2, 512, 8), (4, 1, 1024, 4), (3, 2, 200, 2)])
+def test_attention_core_of_several_shards_in_one_launch(dev, shards, batch, seq, heads):
+    """tp_attention_fwd_shards / tp_attention_bwd_shards over shards side by
+    side (each shard's [Q | K | V] block, its C heads, its lse rows) give the
+    per-shard calls' C, lse and dQKV bit for bit, including a ragged
+    sequence."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    _say(f"attention core, {shards} shards in one launch: {batch} x {seq}, {heads} heads")
+    g = torch.Generator(device=dev)
+    g.manual_seed(1000 * shards + seq)
+    T, hq, hc = batch * seq, 3 * heads * 64, heads * 64
+    bf = dict(device=dev, dtype=torch.bfloat16)
+    QKV = torch.randn(T, shards * hq, device=dev, generator=g).to(torch.bfloat16)
+    dC = torch.randn(T, shards * hc, device=dev, generator=g).to(torch.bfloat16)
+    C = torch.empty(T, shards * hc, **bf)
+    dQKV = torch.empty(T, shards * hq, **bf)
+    lse = torch.empty(batch, shards * heads, seq, device=dev)
+    delta = torch.empty_like(lse)
+    L.tp_attention_fwd(QKV, C, lse, batch, seq, heads, shards=shards)
+    L.tp_attention_bwd(QKV, C, dC, lse, delta, dQKV, batch, seq, heads, shards=shards)
+    for s in range(shards):
+        q, c = slice(s * hq, (s + 1) * hq), slice(s * hc, (s + 1) * hc)
+        Cs = torch.empty(T, hc, **bf)
+        ls = torch.empty(batch, heads, seq, device=dev)
+        dQs = torch.empty(T, hq, **bf)
+        L.tp_attention_fwd(QKV[:, q], Cs, ls, batch, seq, heads)
+        L.tp_attention_bwd(QKV[:, q], Cs, dC[:, c].contiguous(), ls, torch.empty_like(ls), dQs,
+                           batch, seq, heads)
+        torch.cuda.synchronize()
+        assert torch.equal(C[:, c], Cs), f"C of shard {s}"
+        assert torch.equal(lse[:, s * heads:(s + 1) * heads], ls), f"lse of shard {s}"
+        assert torch.equal(dQKV[:, q], dQs), f"dQKV of shard {s}"
