@@ -557,6 +557,26 @@ def roofline(cfg, step, reps):
     return rec, per_call
 
 
+def attention_core_record(step, reps):
+    """The attention core's launches in the step (the forward, and the
+    backward's delta pass with its dK/dV + dQ launch), each against its own
+    roofline: the larger of its flops at the bf16 peak (the causal half of the
+    scores) and its algorithmic bytes at HBM peak."""
+    out = {}
+    for c in shard_calls(step):
+        if not c.name.startswith(("attn_fwd", "attn_bwd")):
+            continue
+        ms = time_call(c.fn, reps)
+        t_mfma = c.flops / (PEAK_BF16_TFLOPS * 1e12)
+        t_hbm = c.bytes / (PEAK_HBM_GBS * 1e9)
+        out[c.name] = {"us": round(ms * 1e3, 2), "tflops": round(c.flops / (ms * 1e-3) / 1e12, 1),
+                       "algorithmic_bytes": c.bytes, "flops": c.flops,
+                       "bound": "hbm" if t_hbm > t_mfma else "mfma",
+                       "roofline_us": round(max(t_mfma, t_hbm) * 1e6, 2),
+                       "frac": round(max(t_mfma, t_hbm) / (ms * 1e-3), 4)}
+    return out
+
+
 def measure(name, args, inputs=None, attn_core=False, with_roofline=True, cpu_seconds=None):
     import torch
     from tensor_transformer_layer_fwd_amd.shard import ShardStep
@@ -584,6 +604,9 @@ def measure(name, args, inputs=None, attn_core=False, with_roofline=True, cpu_se
     if with_roofline:
         rec["roofline"], rec["per_call_shard0"] = roofline(cfg, step, args.kernel_reps)
         log(f"[bench] {name} roofline: {json.dumps(rec['roofline'])}")
+    if attn_core and cfg.attn:
+        rec["attention_core"] = attention_core_record(step, args.kernel_reps)
+        log(f"[bench] {name} attention core: {json.dumps(rec['attention_core'])}")
     secs = args.cpu_seconds if cpu_seconds is None else cpu_seconds
     if not args.no_cpu_baseline and secs > 0:
         log(f"[bench] {name}: timing the float64 oracle on the host for ~{secs:.0f} s")
