@@ -218,11 +218,11 @@ size_t two_wgrads_bytes(int64_t T, int64_t n0, int64_t n1) {
 
 // Two weight gradients with their bias gradients, overwritten:
 // dW0 = In0^T dOut0 (k0 x n0), db0 = column sums of dOut0, and the same for 1.
-// Where both products run unsplit on the 128 x 128 tile with their column
-// sums carried, one launch runs both products (the tiles past the last whole
-// multiple of the CU count as K slices, when that fits) and one launch adds
-// the slices and runs both column-sum second passes; otherwise they are two
-// tp_linear_bwd_wgrad calls. ws holds both products' column-sum partials
+// Where both products tile by 128 x 128 with their column sums carried, one
+// launch runs both products (the tiles past the last whole multiple of the CU
+// count as K slices, when that fits) and one launch adds the slices and runs
+// both column-sum second passes; otherwise they are two tp_linear_bwd_wgrad
+// calls. ws holds both products' column-sum partials
 // (two_wgrads_cs_offset, then product 1's), then the slices' partials
 // (two_wgrads_bytes in all), or either call's workspace.
 int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64_t k0, int64_t n0,
@@ -231,11 +231,14 @@ int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64
                int64_t ld_dout1, int64_t ld_dw1, int64_t T, int dt, void* ws, size_t ws_bytes,
                hipStream_t stream) {
   if (dt == TP_BF16) {
-    const SplitPlan pl0 = plan_gemm_bf16(k0, n0, T, true), pl1 = plan_gemm_bf16(k1, n1, T, true);
+    // the stacked launch takes both products on 128 x 128 tiles whatever
+    // each would plan alone: together they fill the CUs (the tiles past the
+    // last whole multiple of the CU count as K slices)
+    const SplitPlan pl0{kPipe128x128, 1, T}, pl1{kPipe128x128, 1, T};
     const size_t off1 = two_wgrads_cs_offset(T, n0, db0 != nullptr);
     const size_t need = off1 + (db1 ? colsum_workspace_bytes(T, n1) : 0);
-    if (pl0.tile == kPipe128x128 && pl1.tile == kPipe128x128 && pl0.splitk == 1 &&
-        pl1.splitk == 1 && (need == 0 || (ws && ws_bytes >= need))) {
+    if (k0 % 128 == 0 && n0 % 128 == 0 && k1 % 128 == 0 && n1 % 128 == 0 && T % 32 == 0 &&
+        (need == 0 || (ws && ws_bytes >= need))) {
       char* w = static_cast<char*>(ws);
       GemmParams p0 = wgrad_params(In0, dOut0, dW0, T, k0, n0, ld_in0, ld_dout0, ld_dw0, 0, ws);
       GemmParams p1 = wgrad_params(In1, dOut1, dW1, T, k1, n1, ld_in1, ld_dout1, ld_dw1, 0, ws);
