@@ -112,3 +112,27 @@ def test_attn_proj_step_stages_and_repeats(dev):
         for k in want:
             np.testing.assert_array_equal(got[k], want[k], err_msg=f"call {rep + 2}: {k}")
     assert int(step.proj_ws[:4].view(torch.int32).item()) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(micro_batch=1, seq=680),          # ragged T: per-product path
+                                dict(micro_batch=1, seq=512, dtype="f32")])  # fp32: per-product path
+def test_attn_proj_step_outside_the_fused_shapes(dev, kw):
+    """Shapes and dtypes the persistent launch does not take run the same
+    stages as per-product calls inside tp_attn_proj_step; against the oracle
+    (fp32: 1e-5)."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    cfg = _cfg("attn", **kw)
+    dt = L.TP_BF16 if cfg.dtype == "bf16" else L.TP_F32
+    assert not L.tp_attn_proj_step_plan(cfg.T, cfg.h, cfg.Q, cfg.O, cfg.p, dt)
+    _say(f"attn proj step outside the fused shapes T={cfg.T} dtype={cfg.dtype}")
+    inputs = make_inputs(cfg)
+    step = ShardStep(cfg, inputs, dev)
+    assert step.proj_call
+    step.run_eager()
+    got = step.results()
+    ref = oracle.run_config(cfg, inputs)
+    tol = 5e-3 if cfg.dtype == "bf16" else 1e-5
+    for k, r in ref.items():
+        e = oracle.rel_fro(got[k], r)
+        assert e <= tol, (k, e)
