@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gemm_tile.h"
+#include "step_queue.h"  // rows_sum_unit
 
 namespace tpmlp {
 namespace {
@@ -51,10 +52,13 @@ __global__ __launch_bounds__(256) void gemm_bwd_pair_kernel(GemmParams pw, GemmP
 // K-tiles in four stages): the tiles run over all of K (product 0's, then
 // product 1's), then each product's column-sum pass-1 units (gemm_pipe_block
 // runs those for block indices past its tiles), then the K slices of the
-// split tiles. Where each product alone fills only part of the CUs, one launch
-// puts both products' tiles on them at once; where the tiles leave a
-// remainder over the CUs, slicing the remaining tiles along K spreads them
-// over every CU instead of doubling the work of a few.
+// split tiles, then the units of an optional row sum. Where each product
+// alone fills only part of the CUs, one launch puts both products' tiles on
+// them at once; where the tiles leave a remainder over the CUs, slicing the
+// remaining tiles along K spreads them over every CU instead of doubling the
+// work of a few. The row-sum units read and write memory only: they take the
+// CUs' second block slots, which the slices leave early, while the tiles'
+// matrix work runs beside them.
 constexpr int kWg = 128;  // tile rows and columns
 
 // K slice c of the split tiles: tile whole + c / sk, slice c % sk, into its
@@ -78,7 +82,8 @@ __device__ __forceinline__ void wgrad_slice(const GemmParams& p0, const GemmPara
 }
 
 __global__ __launch_bounds__(256) void gemm_wgrad2_kernel(GemmParams p0, GemmParams p1, int nt0,
-                                                          int nt1, WgradSplit sp) {
+                                                          int nt1, WgradSplit sp, int nsl,
+                                                          RowSumParams rs) {
   const int b = static_cast<int>(blockIdx.x);
   const int ncs = p0.cs_blocks + p1.cs_blocks;
   if (b < sp.whole) {
@@ -88,8 +93,11 @@ __global__ __launch_bounds__(256) void gemm_wgrad2_kernel(GemmParams p0, GemmPar
     const int r = b - sp.whole;
     if (r < p0.cs_blocks) gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p0, nt0 + r);
     else gemm_pipe_block<128, 128, 2, 2, 32, 4, false, false, kEpiF32>(p1, nt1 + r - p0.cs_blocks);
-  } else {
+  } else if (b < sp.whole + ncs + nsl) {
     wgrad_slice(p0, p1, nt0, sp, b - sp.whole - ncs);
+  } else {
+    const int64_t row0 = static_cast<int64_t>(b - sp.whole - ncs - nsl) * kSumRows;
+    rows_sum_unit(rs.parts, rs.rows * rs.N, rs.p, rs.N, nullptr, rs.out, rs.ld_out, row0, rs.N);
   }
 }
 
@@ -351,7 +359,7 @@ hipError_t launch_pair256(const GemmParams& pw, const GemmParams& pd, int ekd, c
 }  // namespace
 
 hipError_t launch_gemm_wgrad2(const GemmParams& a, const GemmParams& b, const WgradSplit& sp,
-                              hipStream_t s) {
+                              const RowSumParams* rs, hipStream_t s) {
   GemmParams p0 = a, p1 = b;
   p0.xcds = p1.xcds = device_shape().xcds;
   for (const GemmParams* q : {&p0, &p1})
@@ -361,10 +369,19 @@ hipError_t launch_gemm_wgrad2(const GemmParams& a, const GemmParams& b, const Wg
       (sp.sk > 0 && (!sp.part || p0.K != p1.K || p0.K % (32LL * sp.sk))))
     return hipErrorInvalidValue;
   const int64_t nsl = sp.sk > 0 ? (nt0 + nt1 - sp.whole) * sp.sk : 0;
-  const int64_t grid = sp.whole + nsl + p0.cs_blocks + p1.cs_blocks;
+  RowSumParams r{};
+  if (rs) {
+    r = *rs;
+    auto a16 = [](const void* q) { return (reinterpret_cast<uintptr_t>(q) & 15) == 0; };
+    if (!r.parts || !r.out || !a16(r.parts) || !a16(r.out) || r.p < 1 || r.p > kMaxPartials || r.rows < 0 ||
+        r.rows % kSumRows || r.N < 8 || r.N % 8 || r.ld_out < r.N || r.ld_out % 8)
+      return hipErrorInvalidValue;
+  }
+  const int64_t nsum = r.rows / kSumRows;
+  const int64_t grid = sp.whole + nsl + p0.cs_blocks + p1.cs_blocks + nsum;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(gemm_wgrad2_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, p0, p1,
-                     static_cast<int>(nt0), static_cast<int>(nt1), sp);
+                     static_cast<int>(nt0), static_cast<int>(nt1), sp, static_cast<int>(nsl), r);
   return hipGetLastError();
 }
 

@@ -186,6 +186,7 @@ struct StepParams {
   long long spin;      // polls before a dependency wait gives up
   int phases;          // 1: the forward units, 2: the backward units, 3: both
   int recompute;       // backward: fc2's data-gradient epilogue rebuilds Y = GeLU(U)
+  int no_dx_sum;       // backward without the dX sum units (a later launch sums)
 };
 // Whether launch_mlp_rows supports these shapes (the bf16 tiles, one row slab
 // per XCD); and the workspace it needs (0 when unsupported).
@@ -355,8 +356,17 @@ struct WgradSplit {
   int whole;  // tiles run over all of K (the combined tile count when sk = 0)
   int sk;     // K slices of each remaining tile; 0: none
 };
+// A sum over row partials that the stacked weight-gradient launch runs in
+// blocks after its tiles: out = sum_i parts[i] (bf16 out, fp32 partials of
+// `rows` x N, compact, shard i at i * rows * N); rows a multiple of 16.
+struct RowSumParams {
+  const float* parts;
+  int p;
+  void* out;
+  int64_t rows, N, ld_out;
+};
 hipError_t launch_gemm_wgrad2(const GemmParams& p0, const GemmParams& p1, const WgradSplit& sp,
-                              hipStream_t s);
+                              const RowSumParams* rs, hipStream_t s);
 // After launch_gemm_wgrad2: the sums of the split tiles' K-slice partials
 // into their outputs (slices in K order), and the column sums' pass 2 of the
 // products with more than one row chunk (n0, n1 chunks; 1 or less: none).

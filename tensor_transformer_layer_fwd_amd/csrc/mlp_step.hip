@@ -16,7 +16,10 @@
 // run the two halves as separate calls. In a backward-only launch fc2's data
 // gradient does not wait for fc1's forward tiles (an earlier launch wrote
 // U_i), and with recompute its epilogue also rebuilds Y_i = GeLU(U_i) from the
-// saved U_i for the weight gradient that follows.
+// saved U_i for the weight gradient that follows. A launch can also leave
+// the dX sum out of its queue (no_dx_sum), for the weight-gradient launch
+// that follows it to run beside its tiles: the sum's units would otherwise
+// come last and run alone after the final fc1 data-gradient tiles.
 // A unit waits only for units of the same row block that come earlier in the
 // same queue (fc2 forward for fc1's row block, the sums for every shard's row
 // block, fc2's data gradient for fc1's forward tile, fc1's data gradient for
@@ -92,12 +95,15 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
     kinds[nph] = kind;
     counts[nph++] = n;
   };
+  // (with no_dx_sum the dX sum is a phase of no units, which keeps the
+  // phase tables' layout fixed: the compiler holds them in registers)
+  const int ns2 = s.no_dx_sum ? 0 : nsum;
   if (s.phases == 3) {
-    add(kF1, nf1), add(kF2, nf2), add(kD2, nf1), add(kS1, nsum), add(kD1, nf2), add(kS2, nsum);
+    add(kF1, nf1), add(kF2, nf2), add(kD2, nf1), add(kS1, nsum), add(kD1, nf2), add(kS2, ns2);
   } else if (s.phases == 1) {
     add(kF1, nf1), add(kF2, nf2), add(kS1, nsum);
   } else {
-    add(kD2, nf1), add(kD1, nf2), add(kS2, nsum);
+    add(kD2, nf1), add(kD1, nf2), add(kS2, ns2);
   }
   // fc2's data gradient waits for fc1's forward tiles only in the same launch
   const bool d2_waits = (s.phases & 1) != 0;
@@ -288,6 +294,11 @@ hipError_t launch_mlp_rows(StepParams s, void* workspace, hipStream_t stream) {
   s.rbx = q.rbx;
   if (s.phases < 1 || s.phases > 3) return hipErrorInvalidValue;
   s.units_a = s.phases == 3 ? 2 * q.units_a : q.units_a;
+  if (s.phases & 2) {
+    if (s.no_dx_sum) s.units_a -= q.rbx * (q.rb / kSumRows);  // the dX sum units
+  } else {
+    s.no_dx_sum = 0;
+  }
   s.spin = step_wait_polls();
   const int cus = device_shape().cus;
   if (q.large)

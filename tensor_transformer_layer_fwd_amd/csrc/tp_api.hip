@@ -208,6 +208,18 @@ int two_wgrads_slices(int64_t tiles, int64_t T, int cus) {
   return 0;
 }
 
+// Whether the stacked launch of these shapes leaves a block slot free on
+// every CU for most of its time: at most one whole tile per CU (the split
+// tiles' K slices take the other slots only briefly). A row sum riding in
+// the launch then runs beside the tiles; otherwise it would run after them.
+bool two_wgrads_slot_free(int64_t k0, int64_t n0, int64_t k1, int64_t n1, int64_t T) {
+  if (k0 % 128 || n0 % 128 || k1 % 128 || n1 % 128 || T % 32) return false;
+  const int cus = device_shape().cus;
+  const int64_t tiles = (k0 / 128) * (n0 / 128) + (k1 / 128) * (n1 / 128);
+  const int64_t whole = two_wgrads_slices(tiles, T, cus) > 0 ? tiles - tiles % cus : tiles;
+  return whole <= cus;
+}
+
 // Scratch of the stacked weight gradients: both products' column-sum
 // partials, then the K-slice partials of the split tiles (at most one
 // 128 x 128 fp32 tile per CU).
@@ -224,12 +236,14 @@ size_t two_wgrads_bytes(int64_t T, int64_t n0, int64_t n1) {
 // both column-sum second passes; otherwise they are two tp_linear_bwd_wgrad
 // calls. ws holds both products' column-sum partials
 // (two_wgrads_cs_offset, then product 1's), then the slices' partials
-// (two_wgrads_bytes in all), or either call's workspace.
+// (two_wgrads_bytes in all), or either call's workspace. With rs, the
+// launch also runs that row sum (in blocks after its tiles), or the two calls
+// are followed by the standalone sum.
 int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64_t k0, int64_t n0,
                int64_t ld_in0, int64_t ld_dout0, int64_t ld_dw0, const void* In1,
                const void* dOut1, float* dW1, float* db1, int64_t k1, int64_t n1, int64_t ld_in1,
                int64_t ld_dout1, int64_t ld_dw1, int64_t T, int dt, void* ws, size_t ws_bytes,
-               hipStream_t stream) {
+               hipStream_t stream, const RowSumParams* rs = nullptr) {
   if (dt == TP_BF16) {
     // the stacked launch takes both products on 128 x 128 tiles whatever
     // each would plan alone: together they fill the CUs (the tiles past the
@@ -262,7 +276,7 @@ int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64
           sp.whole = static_cast<int>(tiles - rest);
           sp.sk = sk;
         }
-        hipError_t e = launch_gemm_wgrad2(p0, p1, sp, stream);
+        hipError_t e = launch_gemm_wgrad2(p0, p1, sp, rs, stream);
         if (e == hipSuccess)
           e = launch_wgrad2_finish(p0, p1, sp, db0 ? p0.cs_nchunks : 0, db1 ? p1.cs_nchunks : 0,
                                    stream);
@@ -273,8 +287,19 @@ int two_wgrads(const void* In0, const void* dOut0, float* dW0, float* db0, int64
   int st = tp_linear_bwd_wgrad(In0, dOut0, dW0, db0, T, k0, n0, ld_in0, ld_dout0, ld_dw0, 0,
                                static_cast<tp_dtype>(dt), ws, ws_bytes, stream);
   if (st != TP_OK) return st;
-  return tp_linear_bwd_wgrad(In1, dOut1, dW1, db1, T, k1, n1, ld_in1, ld_dout1, ld_dw1, 0,
-                             static_cast<tp_dtype>(dt), ws, ws_bytes, stream);
+  st = tp_linear_bwd_wgrad(In1, dOut1, dW1, db1, T, k1, n1, ld_in1, ld_dout1, ld_dw1, 0,
+                           static_cast<tp_dtype>(dt), ws, ws_bytes, stream);
+  if (st != TP_OK || !rs) return st;
+  ReduceParams r{};
+  for (int i = 0; i < rs->p; ++i) r.parts[i] = rs->parts + i * rs->rows * rs->N;
+  r.p = rs->p;
+  r.out = rs->out;
+  r.T = rs->rows;
+  r.N = rs->N;
+  r.ldp = rs->N;
+  r.ldo = rs->ld_out;
+  r.out_bf16 = true;
+  return hip_status(launch_reduce(r, stream));
 }
 
 // Pair kind and K slices of the paired backward launch of a bf16 linear layer
@@ -833,9 +858,15 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
   // Weight and bias gradients of every shard as two products over the stacked
   // shards: dB = Y^T dZ ([p*F, h]) with db = column sums of dZ, and
   // dA = X^T dU ([h, p*F]) with da = column sums of dU.
+  // With the row launch's data gradients in the same call, the stacked launch
+  // also sums the dX partials (the row launch leaves that sum out) where it
+  // leaves block slots free beside its tiles.
+  const bool dx_in_wgrads = fused && (phases & kPhBwd) && (phases & kPhWgrad) &&
+                            two_wgrads_slot_free(pF, h, h, pF, T);
+  const RowSumParams dxsum{dXp, p, dX, T, h, ld_dx};
   auto wgrads = [&](void* ws, size_t ws_bytes) {
     return two_wgrads(Y, dZ, dB, db, pF, h, ld_y, ld_dz, ld_db, X, dU, dA, da, h, pF, ld_x, ld_u,
-                      ld_da, T, dt, ws, ws_bytes, stream);
+                      ld_da, T, dt, ws, ws_bytes, stream, dx_in_wgrads ? &dxsum : nullptr);
   };
   if (fused) {
     if (phases & (kPhFwd | kPhBwd)) {
@@ -866,6 +897,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
       s.ld_dx = ld_dx;
       s.phases = ((phases & kPhFwd) ? 1 : 0) | ((phases & kPhBwd) ? 2 : 0);
       s.recompute = recompute != 0;
+      s.no_dx_sum = dx_in_wgrads;
       st = hip_status(launch_mlp_rows(s, workspace, stream));
       if (st != TP_OK) return st;
     }

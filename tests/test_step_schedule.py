@@ -25,8 +25,11 @@ import pytest
 PHASES = ("F1", "F2", "D2", "S1", "D1", "S2")
 # A launch runs the whole queue, or only its forward or its backward units (in
 # the same order); in a backward-only launch fc2's data gradient (D2) waits for
-# nothing, fc1's forward having run in an earlier launch.
-QUEUES = {"step": PHASES, "fwd": ("F1", "F2", "S1"), "bwd": ("D2", "D1", "S2")}
+# nothing, fc1's forward having run in an earlier launch. When the weight
+# gradients follow in the same call, the launch leaves the dX sum (S2) to
+# their launch.
+QUEUES = {"step": PHASES, "fwd": ("F1", "F2", "S1"), "bwd": ("D2", "D1", "S2"),
+          "step_no_dx_sum": PHASES[:-1], "bwd_no_dx_sum": ("D2", "D1")}
 
 
 def queue(p, R, n1, n2, SS, phases=PHASES):
@@ -73,10 +76,11 @@ SHAPES = [
 def test_every_dependency_has_an_earlier_ticket(p, R, n1, n2, SS, which):
     units = queue(p, R, n1, n2, SS, QUEUES[which])
     tickets = {u: t for t, u in enumerate(units)}
-    halves = 1 if which == "step" else 0.5
-    assert len(tickets) == len(units) == int(halves * (2 * p * R * (n1 + n2) + 2 * R * SS))
+    size = {"F1": p * R * n1, "D2": p * R * n1, "F2": p * R * n2, "D1": p * R * n2,
+            "S1": R * SS, "S2": R * SS}
+    assert len(tickets) == len(units) == sum(size[k] for k in QUEUES[which])
     for t, u in enumerate(units):
-        (src, need) = producers(u, p, n1, n2, d2_waits=which != "bwd")
+        (src, need) = producers(u, p, n1, n2, d2_waits=not which.startswith("bwd"))
         if src is None:
             continue
         kind, shards, j = src
@@ -137,7 +141,7 @@ def drain(units, p, n1, n2, blocks, rng, d2_waits=True):
 def test_queue_drains_with_any_number_of_blocks(p, R, n1, n2, SS, blocks, which):
     units = queue(p, R, n1, n2, SS, QUEUES[which])
     rng = random.Random(1000 * blocks + p * 97 + R)
-    assert drain(units, p, n1, n2, blocks, rng, d2_waits=which != "bwd") == len(units)
+    assert drain(units, p, n1, n2, blocks, rng, d2_waits=not which.startswith("bwd")) == len(units)
 
 
 def test_model_detects_a_queue_that_could_deadlock():
