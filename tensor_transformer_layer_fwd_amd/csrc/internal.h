@@ -224,6 +224,7 @@ struct ProjParams {
   unsigned* ctr;
   int xcds, rb, rbx, units_a;
   long long spin;
+  int no_dx_sum;      // with kProjDx: no dXq sum units (a later launch sums)
 };
 constexpr int kProjQkv = 1, kProjOut = 2, kProjDc = 4, kProjDx = 8;
 bool proj_step_supported(int64_t T, int64_t h, int64_t Q, int64_t O, int p);

@@ -22,7 +22,8 @@
 // stage, the core, the output projection, then dC, the core's backward and
 // dXq. The weight gradients dO_i = C_i^T dZa and dW_i = X^T dQKV_i read every
 // token row; they run after this launch as two products over the stacked
-// shards.
+// shards. When they follow in the same call and their launch has room, it
+// also runs the dXq sum, and this launch leaves that sum out (no_dx_sum).
 #include "step_queue.h"
 
 namespace tpmlp {
@@ -202,7 +203,7 @@ int proj_units(const ProjParams& s, int R) {
   if (s.phases & kProjQkv) u += s.p * R * nq;
   if (s.phases & kProjOut) u += s.p * R * nh + R * ss;
   if (s.phases & kProjDc) u += s.p * R * no;
-  if (s.phases & kProjDx) u += s.p * R * nh + R * ss;
+  if (s.phases & kProjDx) u += s.p * R * nh + (s.no_dx_sum ? 0 : R * ss);
   return u;
 }
 

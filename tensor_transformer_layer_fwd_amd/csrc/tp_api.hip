@@ -1086,6 +1086,9 @@ int tp_attn_proj_step(const void* X, const void* W, const void* Ow, const void* 
                      row_ok(dC, ld_dc, es) && row_ok(Za, ld_za, es) && row_ok(dXq, ld_dxq, es) &&
                      row_ok(Zpa, h, 4) && row_ok(dXqp, h, 4) && aligned(workspace, 256);
   const size_t rows = dt == TP_BF16 ? proj_step_workspace_bytes(T, h, Q, O, p) : 0;
+  // the dXq sum rides in the stacked weight-gradient launch, as in the MLP step
+  const bool dx_in_wgrads = fused && sx && sw && two_wgrads_slot_free(pO, h, h, pQ, T);
+  const RowSumParams dxsum{dXqp, p, dXq, T, h, ld_dxq};
   if (fused && (stages & 15)) {
     ProjParams s{};
     s.x = X;
@@ -1116,6 +1119,7 @@ int tp_attn_proj_step(const void* X, const void* W, const void* Ow, const void* 
     s.ld_z = ld_za;
     s.ld_dx = ld_dxq;
     s.phases = stages & 15;
+    s.no_dx_sum = dx_in_wgrads;
     st = hip_status(launch_proj_rows(s, workspace, stream));
     if (st != TP_OK) return st;
   } else if (stages & 15) {
@@ -1166,7 +1170,7 @@ int tp_attn_proj_step(const void* X, const void* W, const void* Ow, const void* 
     char* w = static_cast<char*>(workspace) + (fused ? rows : 0);
     return two_wgrads(C, dZa, dOw, nullptr, pO, h, ld_c, ld_dz, ld_dow, X, dQKV, dW, nullptr, h,
                       pQ, ld_x, ld_dqkv, ld_dw, T, dt, w, workspace_bytes - (fused ? rows : 0),
-                      stream);
+                      stream, dx_in_wgrads ? &dxsum : nullptr);
   }
   return TP_OK;
 }
