@@ -198,9 +198,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void mlp_rows_kernel(StepParam
         g.M = T, g.N = h, g.K = F, g.k_chunk = F;
         unit_tile<RB, TN, C::WM, C::WN, C::BKT, C::ST, true, true, kEpiF32, C::POOL>(
             g, m0, static_cast<int64_t>(n) * TN, static_cast<int>(F / C::BKT));
-        // only the dX sum reads these partials: without it the stores drain
-        // behind the next unit's first copies
-        if (!s.no_dx_sum) signal_count(ctr + L.d1 + rg);
+        signal_count(ctr + L.d1 + rg);
         break;
       }
       default:  // kS2: dX = sum_i dXp_i

@@ -154,7 +154,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void proj_rows_kernel(ProjPara
         g.N = h, g.K = Q, g.k_chunk = Q;
         unit_tile<RB, TN, C::WM, C::WN, C::BKT, C::ST, true, true, kEpiF32, C::POOL>(
             g, m0, n0, static_cast<int>(Q / C::BKT));
-        if (!s.no_dx_sum) signal_count(ctr + L.px + rg);  // only the dXq sum reads them
+        signal_count(ctr + L.px + rg);
         break;
       default:  // kPS2: dXq = sum_i dXqp_i
         wait_count(ctr + L.px + rg, static_cast<unsigned>(s.p * nh), s.spin, s.err);
