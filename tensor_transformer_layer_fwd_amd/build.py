@@ -37,13 +37,23 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-file additions. The attention kernels apply the softmax to the MFMA
+# results with vector ALU instructions: left to its heuristics the compiler
+# keeps the score and output accumulators in AGPRs there and copies them to
+# and from VGPRs around every step (a quarter of the forward's vector
+# instructions); the VGPR form keeps them where the arithmetic reads them.
+FILE_FLAGS = {
+    "attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *DEVICE_FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *DEVICE_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
