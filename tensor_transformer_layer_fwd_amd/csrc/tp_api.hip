@@ -802,9 +802,10 @@ int tp_mlp_step_workspace_size(int64_t T, int64_t h, int64_t F, int p, tp_dtype 
   const size_t both = two_wgrads_bytes(T, h, pF);
   size_t wg = w1 > w2 ? w1 : w2;
   wg = wg > both ? wg : both;
-  const size_t fused = rows + wg;
+  // (the per-product path's scratch also starts past the row counters, so
+  // that calls of either path can share one workspace)
   const size_t each = fb > wg ? fb : wg;
-  *bytes = fused > each ? fused : each;
+  *bytes = rows + each;
   return TP_OK;
 }
 
@@ -907,6 +908,11 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     }
     return TP_OK;
   }
+  // the per-product path's scratch: past the row counters (where the shapes
+  // have them), which must stay zero for the fused calls
+  const size_t rows_off = dt == TP_BF16 ? mlp_step_workspace_bytes(T, h, F, p) : 0;
+  void* scratch = static_cast<char*>(workspace) + rows_off;
+  const size_t scratch_bytes = workspace_bytes - rows_off;
   // the same step as one call per product. The whole step: every shard's
   // forward, the sum, every shard's backward (tp_mlp_bwd, both layers' two
   // gradients), the sum of the dX partials. Otherwise the forward and the sum;
@@ -941,7 +947,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
       st = tp_mlp_bwd(dZ, X, Ai(i), Bi(i), Ui(i), Yi(i), dUi(i), dB + i * F * ld_db,
                       i == 0 ? db : nullptr, dXp + i * T * h, dA + i * F, da ? da + i * F : nullptr,
                       T, h, F, ld_dz, ld_x, ld_a, ld_b, ld_u, ld_u, ld_u, h, ld_db, ld_da, 0, dt,
-                      workspace, workspace_bytes, stream);
+                      scratch, scratch_bytes, stream);
       if (st != TP_OK) return st;
     }
     return tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
@@ -961,7 +967,7 @@ static int mlp_step_impl(const void* X, const void* A, const void* a, const void
     st = tp_reduce_partials(dparts, p, nullptr, dX, T, h, h, ld_dx, dt, stream);
     if (st != TP_OK) return st;
   }
-  if (phases & kPhWgrad) return wgrads(workspace, workspace_bytes);
+  if (phases & kPhWgrad) return wgrads(scratch, scratch_bytes);
   return TP_OK;
 }
 
@@ -1167,9 +1173,10 @@ int tp_attn_proj_step(const void* X, const void* W, const void* Ow, const void* 
   }
   if (sw) {
     // dO = C^T dZa ([p*O, h]) and dW = X^T dQKV ([h, p*Q]) over the stacked shards
-    char* w = static_cast<char*>(workspace) + (fused ? rows : 0);
+    // past the row counters in either path (they must stay zero)
+    char* w = static_cast<char*>(workspace) + rows;
     return two_wgrads(C, dZa, dOw, nullptr, pO, h, ld_c, ld_dz, ld_dow, X, dQKV, dW, nullptr, h,
-                      pQ, ld_x, ld_dqkv, ld_dw, T, dt, w, workspace_bytes - (fused ? rows : 0),
+                      pQ, ld_x, ld_dqkv, ld_dw, T, dt, w, workspace_bytes - rows,
                       stream, dx_in_wgrads ? &dxsum : nullptr);
   }
   return TP_OK;

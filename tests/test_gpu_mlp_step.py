@@ -236,6 +236,42 @@ def test_mlp_step_repeats_replays_and_halves(dev):
     assert int(step.step_ws[:4].view(torch.int32).item()) == 0
 
 
+def test_mlp_step_per_product_call_leaves_the_counters(dev):
+    """A call that runs the step as per-product calls (here: a bias that is
+    not 16-byte aligned) on the workspace of fused calls uses only the scratch
+    past the persistent launch's counters: the next fused call gives the
+    first one's bits, and the per-product call's outputs match the oracle."""
+    from tensor_transformer_layer_fwd_amd import _lib as L
+    from tensor_transformer_layer_fwd_amd.shard import ShardStep
+    cfg = _mlp_cfg("gpt2s", micro_batch=1, seq=1024)
+    _say(f"mlp step per-product call on a fused workspace T={cfg.T}")
+    inputs = make_inputs(cfg)
+    step = ShardStep(cfg, inputs, dev)
+    step.run_eager()
+    want = step.results()
+    inp, m, o = step.inp, step.mlp, step.out
+    pF = inp["a"].shape[0]
+    a_off = torch.empty(pF + 1, dtype=inp["a"].dtype, device=dev)[1:]  # 2 bytes off
+    a_off.copy_(inp["a"])
+    assert a_off.data_ptr() % 16 != 0
+    for v in o.values():
+        v.fill_(float("nan"))
+    L.tp_mlp_step(inp["X"], inp["A"], a_off, inp["B"], inp.get("b"), inp["dZ"], m["U"], m["Y"],
+                  m["Zp"], o["Z"], m["dU"], m["dB"], o.get("db"), m["dA"], m.get("da"), m["dXp"],
+                  o["dX"], step.step_ws)
+    torch.cuda.synchronize()
+    got = step.results()
+    ref = oracle.run_config(cfg, inputs)
+    for k, r in ref.items():
+        e = oracle.rel_fro(got[k], r)
+        assert e <= 5e-3, (k, e)
+    step.run_eager()
+    got = step.results()
+    for k in want:
+        np.testing.assert_array_equal(got[k], want[k], err_msg=f"fused call after: {k}")
+    assert int(step.step_ws[:4].view(torch.int32).item()) == 0
+
+
 def test_mlp_step_wait_that_gives_up_still_ends(dev):
     """With the wait limit forced to give up at the first unmet check, the
     call still runs to its end (every block exits) and the error word tells;
